@@ -1,0 +1,339 @@
+"""CPU oracle for the routed-MoE MLP forward (NumPy, float64).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import or call this package.  The HIP
+library never does, and this package imports nothing from it.
+
+What it computes, step by step, and where each step comes from:
+
+  S0 (ScMoE only) pre-norm of the routed input:
+     ms_t = sum_i x[t,i]^2 / H,  r_t = 1/sqrt(ms_t + eps),
+     xr[t,i] = bf16(x[t,i] * r_t * gamma_pre[i]).
+     Source: "core.models.hybrid.shortcut_block" (Megatron-Core API docs),
+     module doc and ShortcutMoEBlock._moe_router_preprocess: the shortcut
+     representation is normalised before routing and dispatch.  The norm
+     is an RMSNorm with eps 1e-6 (the ScMoE workload's definition).
+  S1 router GEMM: l = fp32( x @ W_r^T ), bf16 activations widened exactly,
+     fp32 weights.  Source: "bridge.models.beam.modeling_beam",
+     beam_router_gating_linear / _BeamRouterGatingLinear / BeamTopKRouter:
+     logits in the router dtype, both operands in fp32, fp32 weights.
+  S2 scores and top-k: s = sigmoid(l) (fp32), s' = s + b (fp32 add),
+     the k largest s' over all E experts (ties to the lower id), ids
+     emitted in ascending order, w = fp32(rsf * s[ids]) -- the bias
+     steers the choice only, the weight is the unbiased score, the
+     scaling factor multiplies routed weights only, k <= 16.
+     Source: "Module glm5next_mlp" (metrale_model_arch docs), section
+     "Numerics the kernels rely on"; Constants, KERNEL_MAX_TOP_K.
+  S3 permute: stable counting sort of the T*k (token, slot) pairs by
+     expert id -> offsets[E+1], sorted_token[T*k], inv_pos[T*k].
+     Source: "Module glm5next_mlp", Constants, MOE_MODULE (token sort /
+     permute / unpermute kernels).
+  S4/S5 grouped SwiGLU experts: per expert, g = A Wg^T, u = A Wu^T,
+     h = bf16( silu(min(g, L)) * clamp(u, -L, L) ), y = h Wd^T (not
+     rounded).  Gate rows first, then up rows, in the fused weight.
+     Source: "Module glm5next_mlp", "Numerics the kernels rely on" (the
+     clamp bounds gate from above only and up on both sides);
+     "mstar.model.components.distributed.mlp", ParallelGatedMLP (gate/up
+     fused into one projection, gate = shard 0, up = shard 1).
+  S6 shared expert: the same SwiGLU FFN with its own width, same clamp,
+     on all rows, added unscaled.  Source: "Module glm5next_mlp", Modules
+     (forward: the dense SwiGLU FFN also serves as the shared expert) and
+     "Numerics the kernels rely on"; shortcut_block._moe_shared_experts
+     (ScMoE: the shared expert sees the current layer's input).
+  S7 combine: z[t] = sum_j w[t,j] * y[inv_pos[t*k+j]] + ys[t];
+     out = bf16(z), or for ScMoE out = bf16(z * r_z * gamma_post) with
+     r_z = 1/sqrt(mean(z^2) + eps).  Source: "Module glm5next_mlp",
+     section "One all-reduce for both EP and TP" (shared output and routed
+     slots added in one combine); shortcut_block module doc and
+     ShortcutMoEBlock._postprocess (post-norm of the merged sum).
+
+Readings where the pages are silent (each also listed in the design
+notes): bias added to the sigmoid score, not to the logit; no
+renormalisation of the top-k weights; ties go to the lower expert id; ids
+ascending inside a token; NaN scores rank below every number; the clamp
+acts on the fp32 pre-activations; bf16 rounding happens only at h, at the
+ScMoE pre-norm output and at the final output; bf16(v) of a float64 value
+is round-to-nearest-even of its fp32 rounding; eps is the fp32 value the
+caller passes, widened.
+
+Precision: all sums in float64 (BLAS matmul as a step), single roundings
+at the points named above.  bf16 tensors are uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+KERNEL_MAX_TOP_K = 16
+
+
+# ---------------------------------------------------------------- bf16 ----
+
+def bf16_to_f64(u: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact)."""
+    u32 = np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def bf16_of_f32(f: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns, round to nearest, ties to even."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(f)
+    if nan.any():                         # keep sign and payload, force quiet
+        top = (f.view(np.uint32)[nan] >> np.uint32(16)).astype(np.uint16)
+        r[nan] = top | np.uint16(0x0040)
+    return r
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bit patterns via the fp32 value (the activation
+    precision of the layer), round to nearest even."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        return bf16_of_f32(np.asarray(v, dtype=np.float64).astype(np.float32))
+
+
+# -------------------------------------------------------------- S0 norm ---
+
+def rmsnorm_bf16(x_bits: np.ndarray, gamma: np.ndarray | None, eps: float) -> np.ndarray:
+    """S0: xr = bf16(x * r * gamma), r = 1/sqrt(sum(x^2)/H + eps), fp64.
+
+    `eps` is the fp32 value of the norm's epsilon, used widened to fp64.
+    The product is formed as (x * r) * gamma in fp64, rounded to fp32,
+    then to bf16 -- one fixed order so that an implementation doing the
+    same IEEE operations reproduces every bit.
+    """
+    x = bf16_to_f64(x_bits)
+    H = x.shape[-1]
+    ms = np.sum(x * x, axis=-1) / H
+    r = 1.0 / np.sqrt(ms + float(np.float32(eps)))
+    v = x * r[..., None]
+    if gamma is not None:
+        v = v * np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    return bf16_round(v)
+
+
+def rmsnorm_f64(z: np.ndarray, gamma: np.ndarray | None, eps: float) -> np.ndarray:
+    """RMSNorm of a float64 matrix (the ScMoE post-norm before rounding)."""
+    ms = np.mean(z * z, axis=-1)
+    r = 1.0 / np.sqrt(ms + float(np.float32(eps)))
+    v = z * r[..., None]
+    if gamma is not None:
+        v = v * np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    return v
+
+
+# ------------------------------------------------------------ S1 router ---
+
+def router_logits(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """S1: l = fp32(x @ W_r^T), x widened exactly from bf16, fp64 sums."""
+    x = bf16_to_f64(x_bits)
+    wr = np.asarray(w_router, dtype=np.float32).astype(np.float64)
+    return (x @ wr.T).astype(np.float32)
+
+
+def sigmoid_f32(l: np.ndarray) -> np.ndarray:
+    """S2: s = fp32(1 / (1 + exp(-l))) evaluated in fp64, rounded once."""
+    l64 = np.asarray(l, dtype=np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-l64))
+    return s.astype(np.float32)
+
+
+def selection_order(s_biased: np.ndarray) -> np.ndarray:
+    """Experts of each token ranked by (s' descending, id ascending); NaN
+    scores rank after every number (NaNs among themselves by id)."""
+    T, E = s_biased.shape
+    ids = np.broadcast_to(np.arange(E), (T, E))
+    neg = -s_biased.astype(np.float64)
+    # lexsort: last key is primary; NaN sorts to the end of an ascending key.
+    return np.lexsort((ids, neg), axis=-1)
+
+
+def topk_route(logits: np.ndarray, corr_bias: np.ndarray | None, k: int,
+               rsf: float) -> dict:
+    """S2: scores, biased selection, ascending ids, unbiased weights.
+
+    Returns dict(ids int32 [T,k], w fp32 [T,k], s fp32 [T,E], s_biased fp32
+    [T,E], gap float64 [T]) where gap is the k-th minus the (k+1)-th biased
+    score (inf when k == E) -- the tie margin of each token's selection.
+    """
+    T, E = logits.shape
+    if not (1 <= k <= min(E, KERNEL_MAX_TOP_K)):
+        raise ValueError(f"k={k} outside 1..min(E={E}, {KERNEL_MAX_TOP_K})")
+    s = sigmoid_f32(logits)
+    b = np.zeros(E, np.float32) if corr_bias is None else np.asarray(corr_bias, np.float32)
+    sb = (s + b[None, :]).astype(np.float32)          # fp32 add
+    order = selection_order(sb)
+    ids = np.sort(order[:, :k], axis=1).astype(np.int32)
+    w = (np.float32(rsf) * np.take_along_axis(s, ids, axis=1)).astype(np.float32)
+    ranked = np.take_along_axis(sb, order, axis=1).astype(np.float64)
+    if k < E:
+        gap = ranked[:, k - 1] - ranked[:, k]
+    else:
+        gap = np.full(T, np.inf)
+    return dict(ids=ids, w=w, s=s, s_biased=sb, gap=gap)
+
+
+# ----------------------------------------------------------- S3 permute ---
+
+def permute(ids: np.ndarray, E: int) -> dict:
+    """S3: stable counting sort of the flattened (t, j) pairs by expert id."""
+    T, k = ids.shape
+    flat = ids.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    np.cumsum(counts, out=offsets[1:])
+    order = np.argsort(flat, kind="stable")
+    inv_pos = np.empty(T * k, dtype=np.int64)
+    inv_pos[order] = np.arange(T * k)
+    return dict(offsets=offsets.astype(np.int32),
+                sorted_token=(order // k).astype(np.int32),
+                inv_pos=inv_pos.astype(np.int32),
+                counts=counts.astype(np.int64))
+
+
+# ---------------------------------------------------------- S4-S6 FFN ----
+
+def swiglu_ffn(a: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
+               limit: float, round_h: bool = True) -> tuple[np.ndarray, np.ndarray]:
+    """S4+S5 for one expert (or S6 for the shared one), fp64.
+
+    a          float64 [n, H] (the rows routed to this expert)
+    w_gate_up  bf16 [2I, H]: gate rows [0, I), up rows [I, 2I)
+    w_down     bf16 [H, I]
+    Returns (h float64 [n, I] -- the bf16 value when round_h, y float64
+    [n, H], unrounded).
+    """
+    I = w_gate_up.shape[0] // 2
+    wg = bf16_to_f64(w_gate_up[:I])
+    wu = bf16_to_f64(w_gate_up[I:])
+    g = a @ wg.T
+    u = a @ wu.T
+    L = float(np.float32(limit))
+    gc = np.minimum(g, L)                 # gate: bounded above only
+    uc = np.clip(u, -L, L)                # up: bounded on both sides
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = gc / (1.0 + np.exp(-gc)) * uc
+    if round_h:
+        h = bf16_to_f64(bf16_round(h))
+    y = h @ bf16_to_f64(w_down).T
+    return h, y
+
+
+def routed_experts(xr_bits: np.ndarray, perm: dict, w_gate_up: np.ndarray,
+                   w_down: np.ndarray, limit: float, round_h: bool = True,
+                   expert_range: tuple[int, int] | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """S4+S5 over all experts: rows of segment e of the permutation go
+    through expert e.  Returns (h_perm [T*k, I], y_perm [T*k, H]) float64
+    in permuted-row order; rows of experts outside `expert_range` stay 0."""
+    offsets = perm["offsets"]
+    st = perm["sorted_token"]
+    E = offsets.shape[0] - 1
+    I = w_gate_up.shape[1] // 2
+    H = w_down.shape[1]
+    M = st.shape[0]
+    h_perm = np.zeros((M, I))
+    y_perm = np.zeros((M, H))
+    lo, hi = (0, E) if expert_range is None else expert_range
+    for e in range(lo, hi):
+        a0, a1 = int(offsets[e]), int(offsets[e + 1])
+        if a1 == a0:
+            continue
+        a = bf16_to_f64(xr_bits[st[a0:a1]])
+        h, y = swiglu_ffn(a, w_gate_up[e], w_down[e], limit, round_h)
+        h_perm[a0:a1] = h
+        y_perm[a0:a1] = y
+    return h_perm, y_perm
+
+
+# ----------------------------------------------------------- S7 combine ---
+
+def combine(y_perm: np.ndarray, w: np.ndarray, inv_pos: np.ndarray,
+            ys: np.ndarray | None) -> np.ndarray:
+    """S7 (before rounding): z[t] = sum_j w[t,j] y[inv_pos[t*k+j]] + ys[t]."""
+    T, k = w.shape
+    H = y_perm.shape[1]
+    z = np.zeros((T, H)) if ys is None else np.array(ys, dtype=np.float64)
+    rows = inv_pos.reshape(T, k)
+    for j in range(k):
+        z += w[:, j].astype(np.float64)[:, None] * y_perm[rows[:, j]]
+    return z
+
+
+# ------------------------------------------------------------ the layer ---
+
+def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
+            eps: float = 1e-6, ids: np.ndarray | None = None,
+            round_h: bool = True, expert_range: tuple[int, int] | None = None,
+            include_shared: bool = True) -> dict:
+    """The whole layer (S0-S7) on one batch.
+
+    `inp` holds the arrays named in moe_inputs.generate (x, x_cur,
+    w_router, corr_bias, w_gate_up, w_down, ws_gate_up, ws_down,
+    gamma_pre, gamma_post).  When `ids` is given, routing uses those
+    expert ids instead of the oracle's own top-k (the weights are still the
+    oracle's unbiased scores for those ids); this re-derives the layer for
+    tokens whose selection is a near-tie.  `expert_range` keeps only the
+    routed slots of experts in [lo, hi) (one expert-parallel rank's share);
+    `include_shared` drops the shared expert.
+
+    Returns a dict with every intermediate: xr, logits, s, s_biased, gap,
+    ids, w, offsets, sorted_token, inv_pos, h_perm, y_perm, hs, ys, z, out
+    (bf16 bits) and out_f64 (the pre-rounding value).
+    """
+    x = inp["x"]
+    T, H = x.shape
+    wr = inp["w_router"]
+    E = wr.shape[0]
+    res: dict = {}
+    if scmoe:
+        xr = rmsnorm_bf16(x, inp.get("gamma_pre"), eps)
+        x_sh = inp["x_cur"]
+    else:
+        xr = np.asarray(x, dtype=np.uint16)
+        x_sh = x
+    res["xr"] = xr
+    logits = router_logits(xr, wr)
+    r = topk_route(logits, inp.get("corr_bias"), k, rsf)
+    res.update(logits=logits, s=r["s"], s_biased=r["s_biased"], gap=r["gap"])
+    if ids is None:
+        ids, w = r["ids"], r["w"]
+    else:
+        ids = np.asarray(ids, dtype=np.int32)
+        w = (np.float32(rsf) * np.take_along_axis(r["s"], ids.astype(np.int64), axis=1)).astype(np.float32)
+    res["ids"], res["w"] = ids, w
+    p = permute(ids, E)
+    res.update(offsets=p["offsets"], sorted_token=p["sorted_token"],
+               inv_pos=p["inv_pos"], counts=p["counts"])
+    h_perm, y_perm = routed_experts(xr, p, inp["w_gate_up"], inp["w_down"],
+                                    limit, round_h, expert_range)
+    res["h_perm"], res["y_perm"] = h_perm, y_perm
+    ys = None
+    if include_shared and inp.get("ws_gate_up") is not None and inp["ws_gate_up"].shape[0] > 0:
+        hs, ys = swiglu_ffn(bf16_to_f64(x_sh), inp["ws_gate_up"], inp["ws_down"],
+                            limit, round_h)
+        res["hs"] = hs
+    res["ys"] = ys
+    z = combine(y_perm, w, p["inv_pos"], ys)
+    res["z"] = z
+    if scmoe:
+        v = rmsnorm_f64(z, inp.get("gamma_post"), eps)
+    else:
+        v = z
+    res["out_f64"] = v
+    res["out"] = bf16_round(v)
+    return res
+
+
+def take_rows(inp: dict, rows: np.ndarray) -> dict:
+    """The same inputs restricted to a subset of tokens.  Every step of the
+    layer is row-independent (the router ranks each token on its own), so
+    forward(take_rows(inp, rows)) gives exactly those rows of the full
+    forward's ids, weights and outputs."""
+    out = dict(inp)
+    out["x"] = inp["x"][rows]
+    if "x_cur" in inp:
+        out["x_cur"] = inp["x_cur"][rows]
+    return out

@@ -1,0 +1,91 @@
+"""Planted mistakes (in the oracle, on the CPU): each plausible error in the
+layer's arithmetic must make at least one pin fail.  This shows the pins
+are sharp enough to trust the oracle."""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as mo
+from tests.helpers import load_hand_example
+
+
+def _hand_matches():
+    inp, p, exp = load_hand_example()
+    res = mo.forward(inp, k=p["k"], rsf=p["rsf"], limit=p["limit"])
+    ok = (np.array_equal(res["ids"], exp["ids"])
+          and np.allclose(res["w"], exp["w"], rtol=1e-8)
+          and np.allclose(res["z"], exp["z"], rtol=1e-8, atol=1e-9)
+          and np.array_equal(mo.bf16_to_f64(res["out"]), np.asarray(exp["out"], np.float64)))
+    return ok
+
+
+def test_unmutated_oracle_matches():
+    assert _hand_matches()
+
+
+def _symmetric_clamp(a, w_gate_up, w_down, limit, round_h=True):
+    I = w_gate_up.shape[0] // 2
+    g = a @ mo.bf16_to_f64(w_gate_up[:I]).T
+    u = a @ mo.bf16_to_f64(w_gate_up[I:]).T
+    gc = np.clip(g, -limit, limit)
+    h = gc / (1 + np.exp(-gc)) * np.clip(u, -limit, limit)
+    if round_h:
+        h = mo.bf16_to_f64(mo.bf16_round(h))
+    return h, h @ mo.bf16_to_f64(w_down).T
+
+
+def _swapped_gate_up(a, w_gate_up, w_down, limit, round_h=True):
+    I = w_gate_up.shape[0] // 2
+    sw = np.concatenate([w_gate_up[I:], w_gate_up[:I]])
+    return _real_ffn(a, sw, w_down, limit, round_h)
+
+
+_real_ffn = mo.swiglu_ffn
+_real_route = mo.topk_route
+_real_combine = mo.combine
+
+
+def _biased_weights(logits, corr_bias, k, rsf):
+    r = _real_route(logits, corr_bias, k, rsf)
+    r["w"] = (np.float32(rsf) * np.take_along_axis(r["s_biased"], r["ids"], 1)).astype(np.float32)
+    return r
+
+
+def _renormalised(logits, corr_bias, k, rsf):
+    r = _real_route(logits, corr_bias, k, rsf)
+    w = np.take_along_axis(r["s"], r["ids"], 1).astype(np.float64)
+    r["w"] = (rsf * w / w.sum(1, keepdims=True)).astype(np.float32)
+    return r
+
+
+def _bias_on_logit(logits, corr_bias, k, rsf):
+    shifted = (logits + corr_bias[None, :]).astype(np.float32)
+    r = _real_route(shifted, None, k, rsf)
+    r["w"] = (np.float32(rsf) * np.take_along_axis(mo.sigmoid_f32(logits), r["ids"], 1)).astype(np.float32)
+    return r
+
+
+def _ties_to_higher_id(logits, corr_bias, k, rsf):
+    E = logits.shape[1]
+    r = _real_route(logits[:, ::-1].copy(), corr_bias[::-1].copy(), k, rsf)
+    ids = np.sort(E - 1 - r["ids"], axis=1).astype(np.int32)
+    r["ids"] = ids
+    r["w"] = (np.float32(rsf) * np.take_along_axis(mo.sigmoid_f32(logits), ids, 1)).astype(np.float32)
+    return r
+
+
+def _shared_scaled(y_perm, w, inv_pos, ys):
+    return _real_combine(y_perm, w, inv_pos, None if ys is None else 2.5 * ys)
+
+
+@pytest.mark.parametrize("name,attr,fake", [
+    ("symmetric clamp", "swiglu_ffn", _symmetric_clamp),
+    ("gate/up swapped", "swiglu_ffn", _swapped_gate_up),
+    ("weights carry the bias", "topk_route", _biased_weights),
+    ("weights renormalised", "topk_route", _renormalised),
+    ("bias on the logit", "topk_route", _bias_on_logit),
+    ("ties to the higher id", "topk_route", _ties_to_higher_id),
+    ("shared expert scaled", "combine", _shared_scaled),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, attr, fake):
+    monkeypatch.setattr(mo, attr, fake)
+    assert not _hand_matches(), name
