@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-MoE MLP forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+One step = one moe_forward call (router, top-k, permute, grouped gate_up
+with the SwiGLU epilogue, grouped down, combine) over one batch of seeded
+synthetic input already resident in HBM.  W untimed steps, then K timed
+steps between two device synchronisations.  Prints one JSON line.
+
+The default workload is the decode-shaped layer (T=32, H=4096, E=64,
+top-8, I=1408, shared I_s=2816), which is bound by HBM bandwidth; the
+prefill, zipf and scmoe workloads (bound by the bf16 matrix cores) can be
+asked for with --workload.
+
+roofline: the dominant kernel is the grouped gate_up launch (routed and
+shared experts in one launch).  Its average duration is measured live with
+HIP events recorded by moe_forward itself on its stream at the boundaries
+of that step, over every timed step.  Algorithmic work per launch:
+  HBM-bound:  bytes = sum over touched experts of 2*I*H*2 (gate/up weights)
+              + 2*I_s*H*2 (shared) + T*H*2 (x) + (T*k*I + T*I_s)*2 (h out)
+  MFMA-bound: flops = 2*T*k*H*2I + 2*T*H*2I_s
+traffic: FETCH_SIZE + WRITE_SIZE per launch from the committed rocprofv3
+counter summary of that kernel, when it was taken on the current kernel
+source (else null).
+
+cpu_baseline: the CPU oracle (float64 NumPy, untuned) timed on this host on
+a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE fwd tokens/s; % bf16 MFMA peak (prefill), % HBM GB/s (decode)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["grouped_gemm.hip", "kernels.h", "common.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_steered_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload_label: str):
+    path = os.path.join(ROOT, "profiles", f"gate_up_{workload_label}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its own stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev: int) -> None:
+        self.hip.hipEventDestroy(ev)
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, inp, sample_tokens: int) -> dict:
+    """The oracle, as it stands, on the first `sample_tokens` tokens."""
+    from oracle import moe_oracle as mo
+    import numpy as np
+    rows = np.arange(min(sample_tokens, wl.T))
+    sub = mo.take_rows(inp, rows)
+    t0 = time.perf_counter()
+    mo.forward(sub, k=wl.k, rsf=wl.rsf, limit=wl.limit, scmoe=wl.scmoe, eps=wl.eps)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"first {len(rows)} of {wl.T} tokens of the same batch, one oracle forward "
+                      f"({dt:.2f} s, float64 NumPy)"}
+
+
+def calibrate_copy(nbytes: int, reps: int) -> None:
+    """A plain streaming kernel of known size (read nbytes, write nbytes), to
+    scale the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "neg_f32", "read_bytes": nbytes, "write_bytes": nbytes,
+                      "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "prefill", "zipf", "scmoe"])
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens the CPU oracle runs on (default: by workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a 1 GiB streaming copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this layer is built and measured at EP=TP=1 on a single MI355X)", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy(1 << 30, 5)
+        return 0
+
+    import numpy as np
+    import torch
+    import moe_inputs
+    import mixture_experts_layer_steered_amd as moe
+
+    wl = moe_inputs.WORKLOADS[args.workload]
+    steps = args.steps if args.steps is not None else (300 if wl.T <= 64 else 20)
+    warmup = args.warmup if args.warmup is not None else (30 if wl.T <= 64 else 3)
+    sample = args.cpu_sample if args.cpu_sample is not None else (wl.T if wl.T <= 64 else 8)
+
+    print(f"[bench] generating {wl.label()}", file=sys.stderr, flush=True)
+    inp = moe_inputs.generate(wl, seed=0)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
+
+    def dev_f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+    T, H, E, k, I, Is = wl.T, wl.H, wl.E, wl.k, wl.I, wl.I_s
+    params = moe.make_params(T, H, E, k, I, Is, wl.rsf, wl.limit, wl.scmoe, wl.eps)
+    x = dev_bf16(inp["x"])
+    x_cur = dev_bf16(inp["x_cur"]) if wl.scmoe else None
+    dev = dict(w_router=dev_f32(inp["w_router"]), corr_bias=dev_f32(inp["corr_bias"]),
+               w_gate_up=dev_bf16(inp["w_gate_up"]), w_down=dev_bf16(inp["w_down"]),
+               ws_gate_up=dev_bf16(inp["ws_gate_up"]) if Is else None,
+               ws_down=dev_bf16(inp["ws_down"]) if Is else None,
+               gamma_pre=dev_f32(inp["gamma_pre"]) if wl.scmoe else None,
+               gamma_post=dev_f32(inp["gamma_post"]) if wl.scmoe else None)
+    weights = moe.make_weights(**dev)
+    ws = torch.empty(moe.moe_workspace_size(params), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+
+    # one probed call to learn the routing (touched experts) for the byte count
+    moe.moe_forward(params, x, x_cur, weights, out, moe.make_probes(expert_offsets=offsets), ws)
+    torch.cuda.synchronize()
+    counts = np.diff(offsets.cpu().numpy())
+    touched = int(np.sum(counts > 0))
+
+    hip = HipEvents()
+    evs = [(hip.create(), hip.create()) for _ in range(steps)]
+    probes = [moe.make_probes(events={moe.MOE_EV_PERMUTE: a, moe.MOE_EV_GATE_UP: b}) for a, b in evs]
+
+    print(f"[bench] warmup {warmup}, steps {steps}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        moe.moe_forward(params, x, x_cur, weights, out, None, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_forward(params, x, x_cur, weights, out, probes[i], ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    gate_up_ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / steps
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    # algorithmic work of the dominant launch and of the whole layer
+    gu_weight_bytes = touched * 2 * I * H * 2 + 2 * Is * H * 2
+    gu_bytes = gu_weight_bytes + T * H * 2 + (T * k * I + T * Is) * 2
+    gu_flops = 2 * T * k * H * 2 * I + 2 * T * H * 2 * Is
+    layer_bytes = (touched * 3 * I * H * 2 + 3 * Is * H * 2 + E * H * 4 + E * 4 + T * H * 2
+                   * (2 if wl.scmoe else 1) + T * H * 2)
+    layer_flops = 2 * T * k * H * 3 * I + 2 * T * H * 3 * Is
+    router_flops = 2 * T * H * E
+    hbm_bound = wl.T * k <= 64 * E   # about a row tile per expert or less: weight streaming
+    traffic = committed_traffic(wl.label())
+    if hbm_bound:
+        achieved = gu_bytes / (gate_up_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "grouped gate_up + SwiGLU (routed + shared, one launch)",
+                    "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": round(gate_up_ms, 5)}
+    else:
+        achieved = gu_flops / (gate_up_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                    "traffic": traffic,
+                    "kernel": "grouped gate_up + SwiGLU (routed + shared, one launch)",
+                    "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(gate_up_ms, 5)}
+    s_step = ms_per_step * 1e-3
+    layer = {"tokens_per_s": round(T / s_step, 1),
+             "GB_per_s": round(layer_bytes / s_step / 1e9, 1),
+             "hbm_frac": round(layer_bytes / s_step / 1e9 / HBM_PEAK_GBS, 4),
+             "TFLOP_per_s": round((layer_flops + router_flops) / s_step / 1e12, 1),
+             "mfma_frac": round((layer_flops + router_flops) / s_step / 1e12 / BF16_PEAK_TFLOPS, 4),
+             "experts_touched": touched, "max_over_mean_count": round(float(counts.max() / counts.mean()), 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu oracle on {sample} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, inp, sample)
+
+    line = {
+        "metric": METRIC, "value": round(T / s_step, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.label(), "T": T, "H": H, "E": E, "k": k, "I": I, "I_shared": Is,
+                   "routed_scaling_factor": wl.rsf, "swiglu_limit": wl.limit,
+                   "scmoe": wl.scmoe, "seed": 0, "parallelism": "ep1_tp1"},
+        "roofline": roofline, "cpu_baseline": cpu, "layer": layer,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,245 @@
+/*
+ * moe.h -- C ABI of the routed mixture-of-experts MLP forward for MI355X
+ * (gfx950, CDNA4).  Plain pointers and sizes only; every buffer is device
+ * memory unless a comment says "host".
+ *
+ * The layer (one token t of T, hidden size H, E routed experts, top-k):
+ *   [ScMoE] xr = bf16(RMSNorm_pre(x_prev))            else xr = x
+ *   l  = fp32(xr @ W_r^T)                             router GEMM, fp32
+ *   s  = sigmoid(l);  s' = s + b                      b steers selection only
+ *   ids = the k largest s' over all E (ties -> lower id), ascending
+ *   w  = rsf * s[ids]                                 unbiased, scaled
+ *   permute the T*k (token, slot) pairs by expert id (stable)
+ *   per expert e: h = bf16(silu(min(g, L)) * clamp(u, -L, L)),
+ *                 [g, u] = x_row @ W_gu[e]^T,  y = h @ W_d[e]^T (fp32)
+ *   shared:       the same FFN on x (ScMoE: x_cur), width I_s, unscaled
+ *   z  = sum_j w[t,j] * y[t,j] + ys[t]                one combine, fp32
+ *   out = bf16(z)           [ScMoE] out = bf16(RMSNorm_post(z))
+ *
+ * Sources (web pages; cited by title and section):
+ *   "Module glm5next_mlp" (metrale_model_arch docs): section "Numerics the
+ *     kernels rely on" (asymmetric SwiGLU clamp with a required limit;
+ *     selection-only correction bias; routed_scaling_factor on routed
+ *     weights only; top-k over the full expert count), section "One
+ *     all-reduce for both EP and TP" (shared output and routed slots summed
+ *     in one combine), Modules forward / forward_prefill_gemm (dense SwiGLU
+ *     FFN reused as the shared expert; one grouped launch per projection),
+ *     Constants KERNEL_MAX_TOP_K (k <= 16) and MOE_MODULE (token sort /
+ *     permute / unpermute).
+ *   "bridge.models.beam.modeling_beam" (NeMo Megatron-Bridge API docs):
+ *     beam_router_gating_linear, _BeamRouterGatingLinear, BeamTopKRouter
+ *     (router logits inp @ weight^T in fp32 with fp32 router weights).
+ *   "mstar.model.components.distributed.mlp": ParallelGatedMLP (gate and up
+ *     fused in one weight, gate first).
+ *   "core.models.hybrid.shortcut_block" (Megatron-Core API docs): module
+ *     doc and ShortcutMoEBlock (ScMoE: the preceding layer's normalised
+ *     representation is routed, the shared expert runs on the current one,
+ *     the merged sum is normalised again).
+ *
+ * Conventions shared by every entry point:
+ *   - bf16 values are passed as uint16_t bit patterns (moe_bf16).
+ *   - Weights are [out, in] with the input dimension contiguous (the layout
+ *     of x @ W^T).  w_gate_up[e] holds the I gate rows, then the I up rows.
+ *   - Every call only enqueues work on `stream` and returns; it never
+ *     synchronises, allocates or frees device memory, and keeps no pointer
+ *     after it returns.  The caller owns all buffers and keeps them alive
+ *     until the stream has run the work.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is enqueued and no output is touched.  The detail of
+ *     the last error of the calling thread is in moe_last_error().
+ *   - Results are deterministic: identical inputs give identical bits (no
+ *     floating-point atomics anywhere).
+ *   - Device pointers must be 16-byte aligned; H, I and I_shared must be
+ *     multiples of 8.  T == 0 is a successful no-op.
+ *   - Functions are reentrant; the only library state is the per-thread
+ *     error text.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16;
+
+#define MOE_MAX_TOP_K 16      /* "Module glm5next_mlp", Constants, KERNEL_MAX_TOP_K */
+#define MOE_MAX_EXPERTS 1024  /* implementation bound of the top-k and permute kernels */
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* violates the layer's definition (k < 1, k > 16,
+                              k > E, E < 1, H or I < 1, I_shared < 0, T < 0,
+                              limit not finite or <= 0, rsf not finite,
+                              ScMoE with eps <= 0 or no x_shared, a NULL
+                              required pointer) */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside the kernels: H, I or I_shared
+                              not a multiple of 8, a pointer not 16-byte
+                              aligned, E > 1024, T*k >= 2^31, ScMoE with
+                              H > 8192 */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the size asked for */
+  MOE_ERR_DEVICE = 4       /* a launch failed (hipGetLastError); faults inside
+                              kernels surface at the caller's synchronisation */
+} moe_status;
+
+/* Shape and constants of one layer call. */
+typedef struct moe_params {
+  int64_t T;                   /* tokens (rows of x)                              */
+  int32_t H;                   /* hidden size                                     */
+  int32_t E;                   /* routed experts (the full count, never a share)  */
+  int32_t k;                   /* experts per token, 1 <= k <= min(E, 16)         */
+  int32_t I;                   /* routed expert intermediate width                */
+  int32_t I_shared;            /* shared expert width; 0 = no shared expert       */
+  float routed_scaling_factor; /* multiplies the routed weights only; finite      */
+  float swiglu_limit;          /* L: required, finite, > 0 (no default exists)    */
+  int32_t scmoe;               /* 1 = ScMoE pairing: RMSNorm before routing and   */
+                               /*     on the merged output; 0 = plain layer       */
+  float norm_eps;              /* RMSNorm epsilon (ScMoE), > 0                    */
+} moe_params;
+
+/* Device weights of one layer (all caller-owned, read-only). */
+typedef struct moe_weights {
+  const float* w_router;       /* [E, H] fp32                                     */
+  const float* corr_bias;      /* [E] fp32 selection-only bias; NULL = zeros      */
+  const moe_bf16* w_gate_up;   /* [E, 2I, H] bf16: gate rows [0,I), up [I,2I)     */
+  const moe_bf16* w_down;      /* [E, H, I] bf16                                  */
+  const moe_bf16* ws_gate_up;  /* [2I_s, H] bf16; unused when I_shared == 0       */
+  const moe_bf16* ws_down;     /* [H, I_s] bf16; unused when I_shared == 0        */
+  const float* gamma_pre;      /* [H] fp32 ScMoE pre-norm gain; NULL = ones       */
+  const float* gamma_post;     /* [H] fp32 ScMoE post-norm gain; NULL = ones      */
+} moe_weights;
+
+/* Step boundaries of moe_forward at which caller-created HIP events can be
+ * recorded on `stream` (for timing a step on the stream it runs on).
+ * events[MOE_EV_BEGIN] is recorded before the first kernel, events[s] right
+ * after step s; a step the layer does not run records at the same point as
+ * the one before it. */
+enum {
+  MOE_EV_BEGIN = 0,
+  MOE_EV_PRENORM = 1,  /* ScMoE pre-norm                                    */
+  MOE_EV_ROUTER = 2,   /* router logits + top-k                             */
+  MOE_EV_PERMUTE = 3,  /* permutation + grouped-GEMM tile schedule          */
+  MOE_EV_GATE_UP = 4,  /* grouped gate_up + SwiGLU (routed and shared)      */
+  MOE_EV_DOWN = 5,     /* grouped down projection (routed and shared)       */
+  MOE_EV_COMBINE = 6,  /* weighted combine (+ ScMoE post-norm)              */
+  MOE_EV_COUNT = 7
+};
+
+/* Optional observation points of moe_forward.  A non-NULL output pointer
+ * receives that step's result (and is used in place of the workspace
+ * slot); a non-NULL event is recorded at its step boundary; NULL members
+ * are skipped. */
+typedef struct moe_probes {
+  int32_t* topk_ids;           /* [T, k]                                          */
+  float* topk_w;               /* [T, k]                                          */
+  int32_t* expert_offsets;     /* [E + 1]                                         */
+  int32_t* sorted_token;       /* [T * k]                                         */
+  int32_t* inv_pos;            /* [T * k]                                         */
+  moe_bf16* xr;                /* [T, H] ScMoE routed input after the pre-norm    */
+  hipEvent_t events[MOE_EV_COUNT];
+} moe_probes;
+
+/* Bytes of workspace that moe_forward (and, for the same params, each of
+ * moe_router_topk and moe_permute) needs.  Host-only, pure function of
+ * *p; validates *p like moe_forward. */
+moe_status moe_workspace_size(const moe_params* p, size_t* bytes);
+
+/* Router: l = fp32(x @ W_r^T), s = sigmoid(l), s' = s + corr_bias, the k
+ * largest s' over all E experts (equal s' -> lower id first, NaN below every
+ * number), emitted in ascending id order with weight rsf * s (the bias never
+ * enters a weight).
+ *   x         [T, H] bf16 (for ScMoE: the already normalised routed input)
+ *   w_router  [E, H] fp32;  corr_bias [E] fp32 or NULL
+ *   topk_ids  [T, k] int32 out;  topk_w [T, k] fp32 out
+ *   ws        >= moe_workspace_size(p) bytes of scratch
+ * Uses p->T, H, E, k, routed_scaling_factor.
+ * Sources: "Module glm5next_mlp", "Numerics the kernels rely on" and
+ * KERNEL_MAX_TOP_K; "bridge.models.beam.modeling_beam",
+ * beam_router_gating_linear. */
+moe_status moe_router_topk(const moe_params* p, const moe_bf16* x, const float* w_router,
+                           const float* corr_bias, int32_t* topk_ids, float* topk_w,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Permute: stable counting sort of the T*k pairs (t, j), keyed by
+ * topk_ids[t, j] (each in [0, E)).
+ *   expert_offsets [E+1] out: offsets[0] = 0, offsets[E] = T*k, segment e is
+ *                  rows [offsets[e], offsets[e+1])
+ *   sorted_token   [T*k] out: token of each permuted row (ascending inside a
+ *                  segment)
+ *   inv_pos        [T*k] out: permuted row of pair t*k + j
+ * Bit-exact and deterministic.  Ids outside [0, E) are undefined behaviour
+ * (they are not checked on the device).
+ * Source: "Module glm5next_mlp", Constants, MOE_MODULE. */
+moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* inv_pos, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Bytes of workspace moe_grouped_swiglu_gemm needs (host-only, pure). */
+moe_status moe_grouped_gemm_workspace_size(int32_t n_groups, int64_t M_total, int32_t H,
+                                           int32_t I, size_t* bytes);
+
+/* Grouped SwiGLU FFN, one launch per projection for all groups.  For each
+ * group g and each row r in [group_offsets[g], group_offsets[g+1]):
+ *   a_r = a[row_index ? row_index[r] : r]                     (bf16, length H)
+ *   g_r = a_r @ W_gu[g][0:I]^T,  u_r = a_r @ W_gu[g][I:2I]^T   (fp32 accumulate)
+ *   h[r] = bf16(silu(min(g_r, L)) * clamp(u_r, -L, L))       [M_total, I] bf16
+ *   y[r] = h[r] @ W_d[g]^T                                    [M_total, H] fp32
+ *   n_groups       >= 1
+ *   M_total        rows; group_offsets[n_groups] must equal it (device data:
+ *                  group_offsets[0] = 0, non-decreasing)
+ *   a              [rows_a, H] bf16; row_index [M_total] int32 or NULL
+ *   group_offsets  [n_groups + 1] int32 (device)
+ *   w_gate_up      [n_groups, 2I, H] bf16;  w_down [n_groups, H, I] bf16
+ *   h, y           outputs as above
+ * Source: "Module glm5next_mlp", Modules forward_prefill_gemm (one grouped
+ * launch per projection) and "Numerics the kernels rely on" (the clamp);
+ * "mstar.model.components.distributed.mlp", ParallelGatedMLP (fused
+ * gate/up weight). */
+moe_status moe_grouped_swiglu_gemm(int32_t n_groups, int64_t M_total, int32_t H, int32_t I,
+                                   float swiglu_limit, const moe_bf16* a,
+                                   const int32_t* row_index, const int32_t* group_offsets,
+                                   const moe_bf16* w_gate_up, const moe_bf16* w_down,
+                                   moe_bf16* h, float* y, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* Combine: z[t] = sum_{j<k} topk_w[t,j] * y_perm[inv_pos[t*k+j]] + y_shared[t]
+ * (fp32, j ascending), then out = bf16(z), or with p->scmoe
+ * out = bf16(z * gamma_post / sqrt(mean(z^2) + eps)).
+ *   y_perm [T*k, H] fp32; topk_w [T, k] fp32; inv_pos [T*k] int32
+ *   y_shared [T, H] fp32 or NULL (no shared term);  gamma_post [H] or NULL
+ *   out [T, H] bf16
+ * Sources: "Module glm5next_mlp", "One all-reduce for both EP and TP";
+ * "core.models.hybrid.shortcut_block", ShortcutMoEBlock._postprocess. */
+moe_status moe_combine(const moe_params* p, const float* y_perm, const float* topk_w,
+                       const int32_t* inv_pos, const float* y_shared, const float* gamma_post,
+                       moe_bf16* out, hipStream_t stream);
+
+/* The whole layer.
+ *   x_routed  [T, H] bf16: the layer input (ScMoE: the preceding layer's
+ *             hidden, normalised here before routing and the experts)
+ *   x_shared  [T, H] bf16: the shared expert's input; NULL = x_routed in the
+ *             plain layer; required with ScMoE (the current layer's hidden)
+ *   w         weights;  out [T, H] bf16;  probes NULL or optional outputs
+ *   ws        >= moe_workspace_size(p) bytes
+ * Sources: all of the above; "Module glm5next_mlp", Modules forward. */
+moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
+                       const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Static text naming a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Detail of the last error returned to the calling thread ("" if none).
+ * The pointer stays valid until the thread's next library call. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

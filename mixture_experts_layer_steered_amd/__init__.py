@@ -1,0 +1,204 @@
+"""Routed mixture-of-experts MLP forward for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over libmoe.so (the C ABI in include/moe.h).  Every
+function has the C name, takes torch tensors (device memory) or None for a
+NULL pointer, marshals them to pointers, enqueues on the current (or given)
+HIP stream and raises MoeError on a non-OK status.  All arithmetic happens
+in the library's HIP kernels; there is no other implementation behind
+these names, and importing fails if the library has not been built
+(python -m mixture_experts_layer_steered_amd.build).
+
+bf16 tensors may be torch.bfloat16 or torch.int16/uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_DEVICE = 4
+MOE_MAX_TOP_K = 16
+MOE_MAX_EXPERTS = 1024
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+class moe_params(Structure):
+    _fields_ = [
+        ("T", c_int64), ("H", c_int32), ("E", c_int32), ("k", c_int32), ("I", c_int32),
+        ("I_shared", c_int32), ("routed_scaling_factor", c_float), ("swiglu_limit", c_float),
+        ("scmoe", c_int32), ("norm_eps", c_float),
+    ]
+
+
+class moe_weights(Structure):
+    _fields_ = [(n, c_void_p) for n in (
+        "w_router", "corr_bias", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
+        "gamma_pre", "gamma_post")]
+
+
+MOE_EV_BEGIN, MOE_EV_PRENORM, MOE_EV_ROUTER, MOE_EV_PERMUTE = 0, 1, 2, 3
+MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_COMBINE, MOE_EV_COUNT = 4, 5, 6, 7
+
+
+class moe_probes(Structure):
+    _fields_ = [(n, c_void_p) for n in (
+        "topk_ids", "topk_w", "expert_offsets", "sorted_token", "inv_pos", "xr")] + [
+        ("events", c_void_p * MOE_EV_COUNT)]
+
+
+def _load() -> ctypes.CDLL:
+    # torch first: its bundled HIP runtime then satisfies libmoe.so's
+    # libamdhip64.so.7 dependency, so one runtime serves both (streams and
+    # device pointers are shared objects of that runtime).
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m mixture_experts_layer_steered_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    st = c_int
+    P = POINTER(moe_params)
+    sig = {
+        "moe_workspace_size": (st, [P, POINTER(c_size_t)]),
+        "moe_router_topk": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_size_t, c_void_p]),
+        "moe_permute": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                             c_void_p]),
+        "moe_grouped_gemm_workspace_size": (st, [c_int32, c_int64, c_int32, c_int32,
+                                                 POINTER(c_size_t)]),
+        "moe_grouped_swiglu_gemm": (st, [c_int32, c_int64, c_int32, c_int32, c_float, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_size_t, c_void_p]),
+        "moe_combine": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                             c_void_p]),
+        "moe_forward": (st, [P, c_void_p, c_void_p, POINTER(moe_weights), c_void_p,
+                             POINTER(moe_probes), c_void_p, c_size_t, c_void_p]),
+        "moe_status_string": (c_char_p, [c_int]),
+        "moe_last_error": (c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
+            "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
+            "moe_forward", "moe_status_string", "moe_last_error")
+
+
+def _status_name(s: int) -> str:
+    return _lib.moe_status_string(s).decode()
+
+
+def _check(s: int) -> None:
+    if s != MOE_OK:
+        raise MoeError(s, _lib.moe_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    """Size of a workspace tensor; a raw integer pointer carries no size."""
+    if t is None or isinstance(t, int):
+        return 0
+    return t.numel() * t.element_size()
+
+
+def make_params(T, H, E, k, I, I_shared, routed_scaling_factor, swiglu_limit, scmoe=False,
+                norm_eps=1e-6) -> moe_params:
+    return moe_params(int(T), int(H), int(E), int(k), int(I), int(I_shared),
+                      float(routed_scaling_factor), float(swiglu_limit), int(bool(scmoe)),
+                      float(norm_eps))
+
+
+def moe_workspace_size(params: moe_params) -> int:
+    n = c_size_t(0)
+    _check(_lib.moe_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def moe_router_topk(params, x, w_router, corr_bias, topk_ids, topk_w, ws, stream=None):
+    _check(_lib.moe_router_topk(ctypes.byref(params), _ptr(x), _ptr(w_router), _ptr(corr_bias),
+                                _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws),
+                                _stream(stream)))
+
+
+def moe_permute(params, topk_ids, expert_offsets, sorted_token, inv_pos, ws, stream=None):
+    _check(_lib.moe_permute(ctypes.byref(params), _ptr(topk_ids), _ptr(expert_offsets),
+                            _ptr(sorted_token), _ptr(inv_pos), _ptr(ws), _nbytes(ws),
+                            _stream(stream)))
+
+
+def moe_grouped_gemm_workspace_size(n_groups, M_total, H, I) -> int:
+    n = c_size_t(0)
+    _check(_lib.moe_grouped_gemm_workspace_size(int(n_groups), int(M_total), int(H), int(I),
+                                                ctypes.byref(n)))
+    return n.value
+
+
+def moe_grouped_swiglu_gemm(n_groups, M_total, H, I, swiglu_limit, a, row_index, group_offsets,
+                            w_gate_up, w_down, h, y, ws, stream=None):
+    _check(_lib.moe_grouped_swiglu_gemm(int(n_groups), int(M_total), int(H), int(I),
+                                        float(swiglu_limit), _ptr(a), _ptr(row_index),
+                                        _ptr(group_offsets), _ptr(w_gate_up), _ptr(w_down),
+                                        _ptr(h), _ptr(y), _ptr(ws), _nbytes(ws),
+                                        _stream(stream)))
+
+
+def moe_combine(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, out, stream=None):
+    _check(_lib.moe_combine(ctypes.byref(params), _ptr(y_perm), _ptr(topk_w), _ptr(inv_pos),
+                            _ptr(y_shared), _ptr(gamma_post), _ptr(out), _stream(stream)))
+
+
+def make_weights(w_router, corr_bias, w_gate_up, w_down, ws_gate_up=None, ws_down=None,
+                 gamma_pre=None, gamma_post=None) -> moe_weights:
+    return moe_weights(*[_ptr(t) for t in (w_router, corr_bias, w_gate_up, w_down, ws_gate_up,
+                                           ws_down, gamma_pre, gamma_post)])
+
+
+def make_probes(topk_ids=None, topk_w=None, expert_offsets=None, sorted_token=None,
+                inv_pos=None, xr=None, events=None) -> moe_probes:
+    """`events`: dict {MOE_EV_*: raw hipEvent_t handle (int)}."""
+    pr = moe_probes(*[_ptr(t) for t in (topk_ids, topk_w, expert_offsets, sorted_token,
+                                        inv_pos, xr)])
+    for i, ev in (events or {}).items():
+        pr.events[i] = ev
+    return pr
+
+
+def moe_forward(params, x_routed, x_shared, weights: moe_weights, out, probes=None, ws=None,
+                stream=None):
+    pr = ctypes.byref(probes) if probes is not None else None
+    _check(_lib.moe_forward(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
+                            ctypes.byref(weights), _ptr(out), pr, _ptr(ws), _nbytes(ws),
+                            _stream(stream)))

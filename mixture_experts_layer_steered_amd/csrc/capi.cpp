@@ -1,0 +1,441 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace carving and launch sequencing.  Nothing here allocates device
+// memory or synchronises; every kernel goes onto the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(ptr)                                                           \
+  do {                                                                             \
+    if ((ptr) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #ptr);    \
+    if (!aligned16(ptr))                                                           \
+      return fail(MOE_ERR_UNSUPPORTED, "%s is not 16-byte aligned", #ptr);         \
+  } while (0)
+
+#define OPTIONAL_PTR(ptr)                                                          \
+  do {                                                                             \
+    if ((ptr) != nullptr && !aligned16(ptr))                                       \
+      return fail(MOE_ERR_UNSUPPORTED, "%s is not 16-byte aligned", #ptr);         \
+  } while (0)
+
+constexpr int64_t kMaxPairs = (int64_t)1 << 31;
+constexpr int kMaxNormH = 8192;  // ScMoE norms hold one row per workgroup in registers
+
+moe_status check_params(const moe_params* p) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "params is NULL");
+  if (p->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", (long long)p->T);
+  if (p->E < 1) return fail(MOE_ERR_INVALID_ARG, "E = %d < 1", p->E);
+  if (p->k < 1 || p->k > MOE_MAX_TOP_K)
+    return fail(MOE_ERR_INVALID_ARG, "k = %d outside 1..%d", p->k, MOE_MAX_TOP_K);
+  if (p->k > p->E) return fail(MOE_ERR_INVALID_ARG, "k = %d > E = %d", p->k, p->E);
+  if (p->H < 1) return fail(MOE_ERR_INVALID_ARG, "H = %d < 1", p->H);
+  if (p->I < 1) return fail(MOE_ERR_INVALID_ARG, "I = %d < 1", p->I);
+  if (p->I_shared < 0) return fail(MOE_ERR_INVALID_ARG, "I_shared = %d < 0", p->I_shared);
+  if (!std::isfinite(p->swiglu_limit) || !(p->swiglu_limit > 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be finite and > 0 (no default)");
+  if (!std::isfinite(p->routed_scaling_factor))
+    return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor is not finite");
+  if (p->scmoe != 0 && p->scmoe != 1)
+    return fail(MOE_ERR_INVALID_ARG, "scmoe = %d is not 0 or 1", p->scmoe);
+  if (p->scmoe && !(std::isfinite(p->norm_eps) && p->norm_eps > 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "norm_eps must be finite and > 0 with scmoe");
+  if (p->E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "E = %d > %d", p->E, MOE_MAX_EXPERTS);
+  if (p->H % 8 || p->I % 8 || p->I_shared % 8)
+    return fail(MOE_ERR_UNSUPPORTED, "H, I, I_shared must be multiples of 8 (%d, %d, %d)", p->H,
+                p->I, p->I_shared);
+  if (p->T * (int64_t)p->k >= kMaxPairs)
+    return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld >= 2^31", (long long)(p->T * p->k));
+  if (p->scmoe && p->H > kMaxNormH)
+    return fail(MOE_ERR_UNSUPPORTED, "scmoe with H = %d > %d", p->H, kMaxNormH);
+  return MOE_OK;
+}
+
+// Workspace carving: 256-byte aligned slots in a fixed order.
+struct Carver {
+  size_t off = 0;
+  char* base = nullptr;
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+GemmVariant pick_variant(int64_t rows, int64_t groups) {
+  // about one MFMA row tile or less per group: stream the weights with short
+  // tiles; otherwise the LDS-tiled prefill tiles
+  return (rows <= 64 * groups) ? GemmVariant::kStream : GemmVariant::kTiled;
+}
+
+struct Layout {
+  float* logits;
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* starts;
+  int32_t* offsets;
+  int32_t* sorted_token;
+  int32_t* inv_pos;
+  int32_t* mstart;
+  uint16_t* h;
+  float* y;
+  uint16_t* hs;
+  float* ys;
+  uint16_t* xr;
+  size_t bytes;
+};
+
+Layout carve(const moe_params& p, void* ws) {
+  Carver c;
+  c.base = static_cast<char*>(ws);
+  const int64_t T = p.T, N = p.T * p.k;
+  const int tiles = permute_tiles(N);
+  Layout L;
+  L.logits = c.take<float>(T * p.E);
+  L.ids = c.take<int32_t>(N);
+  L.w = c.take<float>(N);
+  L.counts = c.take<int32_t>((size_t)tiles * p.E);
+  L.starts = c.take<int32_t>((size_t)tiles * p.E);
+  L.offsets = c.take<int32_t>(p.E + 1);
+  L.sorted_token = c.take<int32_t>(N);
+  L.inv_pos = c.take<int32_t>(N);
+  L.mstart = c.take<int32_t>(p.E + 1);
+  L.h = c.take<uint16_t>((size_t)N * p.I);
+  L.y = c.take<float>((size_t)N * p.H);
+  L.hs = c.take<uint16_t>((size_t)T * p.I_shared);
+  L.ys = c.take<float>(p.I_shared ? (size_t)T * p.H : 0);
+  L.xr = c.take<uint16_t>(p.scmoe ? (size_t)T * p.H : 0);
+  L.bytes = (c.off + 255) & ~size_t(255);
+  return L;
+}
+
+// Router-only and permute-only entry points use the front of the workspace.
+size_t router_ws_bytes(const moe_params& p) { return (size_t)p.T * p.E * sizeof(float); }
+size_t permute_ws_bytes(const moe_params& p) {
+  Carver c;
+  const int tiles = permute_tiles(p.T * p.k);
+  c.take<int32_t>((size_t)tiles * p.E);
+  c.take<int32_t>((size_t)tiles * p.E);
+  return c.off;
+}
+
+moe_status device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int32_t* offsets,
+                         const int32_t* mstart, const uint16_t* W, int64_t w_stride, void* out,
+                         int64_t M, int G, int N, int K, GemmVariant v) {
+  GemmProblem P;
+  const int bm = gemm_tile_m(v), bn = gemm_tile_n(v);
+  P.A = A;
+  P.row_index = row_index;
+  P.group_offsets = offsets;
+  P.mtile_start = mstart;
+  P.W = W;
+  P.w_stride = w_stride;
+  P.out = out;
+  P.M = M;
+  P.G = G;
+  P.N = N;
+  P.K = K;
+  P.ntiles = (N + bn - 1) / bn;
+  P.max_mtiles = (int32_t)((M + bm - 1) / bm + (offsets ? G : 0));
+  return P;
+}
+
+bool tiles_fit(const GemmProblem& a, const GemmProblem* b) {
+  int64_t t = (int64_t)a.max_mtiles * a.ntiles + (b ? (int64_t)b->max_mtiles * b->ntiles : 0);
+  return t < ((int64_t)1 << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_workspace_size(const moe_params* p, size_t* bytes) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = carve(*p, nullptr).bytes;
+  return ok();
+}
+
+moe_status moe_router_topk(const moe_params* p, const moe_bf16* x, const float* w_router,
+                           const float* corr_bias, int32_t* topk_ids, float* topk_w, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  if (p->T == 0) return ok();
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_router);
+  OPTIONAL_PTR(corr_bias);
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(ws);
+  if (ws_bytes < router_ws_bytes(*p))
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, router_ws_bytes(*p));
+  float* logits = static_cast<float*>(ws);
+  if ((s = device_status(launch_router_logits(x, w_router, logits, p->T, p->H, p->E, stream),
+                         "router logits")) != MOE_OK)
+    return s;
+  if ((s = device_status(launch_router_topk(logits, corr_bias, topk_ids, topk_w, p->T, p->E, p->k,
+                                            p->routed_scaling_factor, stream),
+                         "router top-k")) != MOE_OK)
+    return s;
+  return ok();
+}
+
+moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* inv_pos, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(expert_offsets);
+  const int64_t N = p->T * p->k;
+  if (N > 0) {
+    REQUIRE_PTR(topk_ids);
+    REQUIRE_PTR(sorted_token);
+    REQUIRE_PTR(inv_pos);
+    REQUIRE_PTR(ws);
+    if (ws_bytes < permute_ws_bytes(*p))
+      return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, permute_ws_bytes(*p));
+  }
+  Carver c;
+  c.base = static_cast<char*>(ws);
+  const int tiles = permute_tiles(N);
+  int32_t* counts = c.take<int32_t>((size_t)tiles * p->E);
+  int32_t* starts = c.take<int32_t>((size_t)tiles * p->E);
+  if ((s = device_status(launch_permute(topk_ids, counts, starts, expert_offsets, sorted_token,
+                                        inv_pos, N, p->E, p->k, stream),
+                         "permute")) != MOE_OK)
+    return s;
+  return ok();
+}
+
+moe_status moe_grouped_gemm_workspace_size(int32_t n_groups, int64_t M_total, int32_t H,
+                                           int32_t I, size_t* bytes) {
+  if (n_groups < 1 || n_groups > MOE_MAX_EXPERTS)
+    return fail(n_groups < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED,
+                "n_groups = %d outside 1..%d", n_groups, MOE_MAX_EXPERTS);
+  if (M_total < 0 || H < 1 || I < 1) return fail(MOE_ERR_INVALID_ARG, "bad M_total/H/I");
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ((size_t)(n_groups + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+  return ok();
+}
+
+moe_status moe_grouped_swiglu_gemm(int32_t n_groups, int64_t M_total, int32_t H, int32_t I,
+                                   float swiglu_limit, const moe_bf16* a,
+                                   const int32_t* row_index, const int32_t* group_offsets,
+                                   const moe_bf16* w_gate_up, const moe_bf16* w_down, moe_bf16* h,
+                                   float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  size_t need = 0;
+  moe_status s = moe_grouped_gemm_workspace_size(n_groups, M_total, H, I, &need);
+  if (s != MOE_OK) return s;
+  if (!std::isfinite(swiglu_limit) || !(swiglu_limit > 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be finite and > 0 (no default)");
+  if (H % 8 || I % 8) return fail(MOE_ERR_UNSUPPORTED, "H, I must be multiples of 8");
+  if (M_total >= kMaxPairs) return fail(MOE_ERR_UNSUPPORTED, "M_total >= 2^31");
+  if (M_total == 0) return ok();
+  REQUIRE_PTR(a);
+  OPTIONAL_PTR(row_index);
+  REQUIRE_PTR(group_offsets);
+  REQUIRE_PTR(w_gate_up);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(ws);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const GemmVariant v = pick_variant(M_total, n_groups);
+  int32_t* mstart = static_cast<int32_t*>(ws);
+  GemmProblem gu = make_problem(a, row_index, group_offsets, mstart, w_gate_up,
+                                (int64_t)2 * I * H, h, M_total, n_groups, I, H, v);
+  GemmProblem dn = make_problem(h, nullptr, group_offsets, mstart, w_down, (int64_t)H * I, y,
+                                M_total, n_groups, H, I, v);
+  if (!tiles_fit(gu, nullptr) || !tiles_fit(dn, nullptr))
+    return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");
+  const int bm = gemm_tile_m(v);
+  if ((s = device_status(
+           launch_gemm_schedule(group_offsets, n_groups, bm, bm, mstart, nullptr, stream),
+           "gemm schedule")) != MOE_OK)
+    return s;
+  if ((s = device_status(launch_grouped_gemm(v, true, gu, nullptr, swiglu_limit, stream),
+                         "gate_up")) != MOE_OK)
+    return s;
+  if ((s = device_status(launch_grouped_gemm(v, false, dn, nullptr, swiglu_limit, stream),
+                         "down")) != MOE_OK)
+    return s;
+  return ok();
+}
+
+moe_status moe_combine(const moe_params* p, const float* y_perm, const float* topk_w,
+                       const int32_t* inv_pos, const float* y_shared, const float* gamma_post,
+                       moe_bf16* out, hipStream_t stream) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  if (p->T == 0) return ok();
+  REQUIRE_PTR(y_perm);
+  REQUIRE_PTR(topk_w);
+  REQUIRE_PTR(inv_pos);
+  OPTIONAL_PTR(y_shared);
+  OPTIONAL_PTR(gamma_post);
+  REQUIRE_PTR(out);
+  if ((s = device_status(launch_combine(y_perm, topk_w, inv_pos, y_shared, gamma_post, out, p->T,
+                                        p->H, p->k, p->scmoe, p->norm_eps, stream),
+                         "combine")) != MOE_OK)
+    return s;
+  return ok();
+}
+
+moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
+                       const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (p->T == 0) return ok();
+  REQUIRE_PTR(x_routed);
+  if (p->scmoe && !x_shared)
+    return fail(MOE_ERR_INVALID_ARG, "scmoe needs x_shared (the current layer's input)");
+  OPTIONAL_PTR(x_shared);
+  REQUIRE_PTR(w->w_router);
+  OPTIONAL_PTR(w->corr_bias);
+  REQUIRE_PTR(w->w_gate_up);
+  REQUIRE_PTR(w->w_down);
+  if (p->I_shared > 0) {
+    REQUIRE_PTR(w->ws_gate_up);
+    REQUIRE_PTR(w->ws_down);
+  }
+  OPTIONAL_PTR(w->gamma_pre);
+  OPTIONAL_PTR(w->gamma_post);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(ws);
+  if (probes) {
+    OPTIONAL_PTR(probes->topk_ids);
+    OPTIONAL_PTR(probes->topk_w);
+    OPTIONAL_PTR(probes->expert_offsets);
+    OPTIONAL_PTR(probes->sorted_token);
+    OPTIONAL_PTR(probes->inv_pos);
+    OPTIONAL_PTR(probes->xr);
+  }
+  Layout L = carve(*p, ws);
+  if (ws_bytes < L.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.bytes);
+  if (probes) {
+    if (probes->topk_ids) L.ids = probes->topk_ids;
+    if (probes->topk_w) L.w = probes->topk_w;
+    if (probes->expert_offsets) L.offsets = probes->expert_offsets;
+    if (probes->sorted_token) L.sorted_token = probes->sorted_token;
+    if (probes->inv_pos) L.inv_pos = probes->inv_pos;
+    if (probes->xr && p->scmoe) L.xr = probes->xr;
+  }
+  const int64_t T = p->T, N = T * p->k;
+  const GemmVariant v = pick_variant(N, p->E);
+  const uint16_t* xr = x_routed;
+  const uint16_t* xs = x_shared ? x_shared : x_routed;
+  const bool shared = p->I_shared > 0;
+
+  GemmProblem gu = make_problem(xr, L.sorted_token, L.offsets, L.mstart, w->w_gate_up,
+                                (int64_t)2 * p->I * p->H, L.h, N, p->E, p->I, p->H, v);
+  GemmProblem dn = make_problem(L.h, nullptr, L.offsets, L.mstart, w->w_down,
+                                (int64_t)p->H * p->I, L.y, N, p->E, p->H, p->I, v);
+  GemmProblem sgu = make_problem(xs, nullptr, nullptr, nullptr, w->ws_gate_up, 0, L.hs, T, 1,
+                                 p->I_shared, p->H, v);
+  GemmProblem sdn = make_problem(L.hs, nullptr, nullptr, nullptr, w->ws_down, 0, L.ys, T, 1, p->H,
+                                 p->I_shared, v);
+  if (p->scmoe) gu.A = L.xr;
+  if (!tiles_fit(gu, shared ? &sgu : nullptr) || !tiles_fit(dn, shared ? &sdn : nullptr))
+    return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");
+
+  auto mark = [&](int ev) -> moe_status {
+    if (probes && probes->events[ev])
+      return device_status(hipEventRecord(probes->events[ev], stream), "event record");
+    return MOE_OK;
+  };
+  if ((s = mark(MOE_EV_BEGIN)) != MOE_OK) return s;
+  if (p->scmoe) {
+    if ((s = device_status(launch_rmsnorm_bf16(x_routed, w->gamma_pre, L.xr, T, p->H, p->norm_eps,
+                                               stream),
+                           "pre-norm")) != MOE_OK)
+      return s;
+    xr = L.xr;
+  }
+  if ((s = mark(MOE_EV_PRENORM)) != MOE_OK) return s;
+  if ((s = device_status(launch_router_logits(xr, w->w_router, L.logits, T, p->H, p->E, stream),
+                         "router logits")) != MOE_OK)
+    return s;
+  if ((s = device_status(launch_router_topk(L.logits, w->corr_bias, L.ids, L.w, T, p->E, p->k,
+                                            p->routed_scaling_factor, stream),
+                         "router top-k")) != MOE_OK)
+    return s;
+  if ((s = mark(MOE_EV_ROUTER)) != MOE_OK) return s;
+  if ((s = device_status(launch_permute(L.ids, L.counts, L.starts, L.offsets, L.sorted_token,
+                                        L.inv_pos, N, p->E, p->k, stream),
+                         "permute")) != MOE_OK)
+    return s;
+  const int bm = gemm_tile_m(v);
+  if ((s = device_status(launch_gemm_schedule(L.offsets, p->E, bm, bm, L.mstart, nullptr, stream),
+                         "gemm schedule")) != MOE_OK)
+    return s;
+  if ((s = mark(MOE_EV_PERMUTE)) != MOE_OK) return s;
+  if ((s = device_status(launch_grouped_gemm(v, true, gu, shared ? &sgu : nullptr,
+                                             p->swiglu_limit, stream),
+                         "gate_up")) != MOE_OK)
+    return s;
+  if ((s = mark(MOE_EV_GATE_UP)) != MOE_OK) return s;
+  if ((s = device_status(launch_grouped_gemm(v, false, dn, shared ? &sdn : nullptr,
+                                             p->swiglu_limit, stream),
+                         "down")) != MOE_OK)
+    return s;
+  if ((s = mark(MOE_EV_DOWN)) != MOE_OK) return s;
+  if ((s = device_status(launch_combine(L.y, L.w, L.inv_pos, shared ? L.ys : nullptr,
+                                        w->gamma_post, out, T, p->H, p->k, p->scmoe, p->norm_eps,
+                                        stream),
+                         "combine")) != MOE_OK)
+    return s;
+  if ((s = mark(MOE_EV_COMBINE)) != MOE_OK) return s;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Device helpers shared by the gfx950 kernels of the MoE forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#define MOE_WAVE 64
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays a
+// quiet NaN with its sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Clamped SwiGLU on fp32 pre-activations: the gate is bounded from above
+// only, the up projection on both sides; silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float swiglu_clamped(float g, float u, float limit) {
+  g = fminf(g, limit);
+  u = fminf(fmaxf(u, -limit), limit);
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// Butterfly (xor) reductions: addition is commutative, so every lane ends
+// with the same bits, and the order is fixed, so runs repeat exactly.
+
+// 64-bit wave-wide max (every lane ends with the max).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, off, MOE_WAVE);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, MOE_WAVE);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);
+  return v;
+}

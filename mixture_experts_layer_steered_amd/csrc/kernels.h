@@ -1,0 +1,52 @@
+// Host-side launchers of the gfx950 kernels (one translation unit each).
+// Every launcher only enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_MAX_EXPERTS_DEV 1024
+#define MOE_MAX_TOP_K_DEV 16
+
+// One grouped GEMM problem: rows of A (optionally gathered through
+// row_index) grouped by device offsets, each group against its own weight.
+struct GemmProblem {
+  const uint16_t* A;              // [rows_a, K] bf16, K contiguous
+  const int32_t* row_index;       // [M] source row of each GEMM row, or nullptr
+  const int32_t* group_offsets;   // [G+1] device row offsets, or nullptr: one group of M rows
+  const int32_t* mtile_start;     // [G+1] device m-tile prefix (with group_offsets)
+  const uint16_t* W;              // [G, WR, K] bf16; gate_up: WR = 2N, down: WR = N
+  int64_t w_stride;               // elements between groups of W
+  void* out;                      // [M, N]: bf16 h (gate_up) or fp32 y (down)
+  int64_t M;                      // total rows
+  int32_t G;                      // groups
+  int32_t N;                      // output columns
+  int32_t K;                      // reduction length
+  int32_t ntiles;                 // ceil(N / BN)
+  int32_t max_mtiles;             // host bound: ceil(M / BM) + G (or ceil(M / BM) for one group)
+};
+
+enum class GemmVariant { kStream, kTiled };
+int gemm_tile_m(GemmVariant v);
+int gemm_tile_n(GemmVariant v);
+
+hipError_t launch_router_logits(const uint16_t* x, const float* w, float* logits, int64_t T,
+                                int H, int E, hipStream_t stream);
+hipError_t launch_router_topk(const float* logits, const float* bias, int32_t* ids, float* wts,
+                              int64_t T, int E, int k, float rsf, hipStream_t stream);
+
+int permute_tiles(int64_t N);
+hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* inv_pos, int64_t N, int E, int k,
+                          hipStream_t stream);
+
+hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
+                                int32_t* start0, int32_t* start1, hipStream_t stream);
+hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
+                               const GemmProblem* b, float limit, hipStream_t stream);
+
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, const float* gamma, uint16_t* out, int64_t T,
+                               int H, float eps, hipStream_t stream);
+hipError_t launch_combine(const float* y_perm, const float* w, const int32_t* inv_pos,
+                          const float* y_shared, const float* gamma_post, uint16_t* out,
+                          int64_t T, int H, int k, int post_norm, float eps, hipStream_t stream);

@@ -1,0 +1,194 @@
+// Router of the routed-MoE layer on gfx950: fp32 logits, sigmoid scores, a
+// selection-only correction bias, and a wavefront top-k.
+//
+// Logits.  The router runs in fp32 with fp32 weights against bf16
+// activations ("bridge.models.beam.modeling_beam", beam_router_gating_linear
+// and BeamTopKRouter).  A bf16 activation times an fp32 weight is computed
+// exactly on bf16 matrix cores by splitting each fp32 weight w into three
+// bf16 pieces w = hi + mid + lo (8 + 8 + 8 significant bits, each piece the
+// truncation of what is left, so the split is exact); each bf16 x bf16
+// product is exact in fp32 and the MFMA sums them with fp32 accumulation.
+// The logits therefore equal an fp32 GEMM up to summation order, at the
+// rate of three bf16 MFMAs instead of one fp32 MFMA of a quarter the K.
+//
+// Top-k.  s = sigmoid(l) (evaluated in fp64, rounded once to fp32),
+// s' = s + b in fp32, and the k largest s' over all E experts are chosen,
+// ties to the lower expert id, NaN below every number; the ids are written
+// in ascending order with weight rsf * s ("Module glm5next_mlp", section
+// "Numerics the kernels rely on"; Constants, KERNEL_MAX_TOP_K).  One
+// wavefront ranks one token: each lane holds up to 16 experts as 64-bit
+// keys (orderable score bits, inverted id) and k wave-wide arg-max rounds
+// pick the winners.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int RT_BT = 64;       // tokens per workgroup tile
+constexpr int RT_BE = 64;       // experts per workgroup tile
+constexpr int RT_BK = 32;       // K per LDS stage
+constexpr int RT_LD = RT_BK + 8;  // padded LDS row (bf16 elements): 80 bytes
+
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  uint32_t u = __float_as_uint(w);
+  uint32_t h = u & 0xffff0000u;
+  float r1 = w - __uint_as_float(h);          // exact: the 16 bits below hi
+  uint32_t m = __float_as_uint(r1) & 0xffff0000u;
+  float r2 = r1 - __uint_as_float(m);         // exact: at most 8 bits left
+  hi = h >> 16;
+  mid = m >> 16;
+  lo = __float_as_uint(r2) >> 16;             // exact in bf16
+}
+
+// logits[T, E] = fp32(x[T, H] @ w[E, H]^T).  Grid: (ceil(T/64), ceil(E/64)).
+__global__ __launch_bounds__(256) void router_logits_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
+    int64_t T, int H, int E) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[RT_BT * RT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t wsp[3][RT_BE * RT_LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t t0 = (int64_t)blockIdx.x * RT_BT;
+  const int e0 = blockIdx.y * RT_BE;
+
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+  // x tile: 64 rows x 32 k = 256 chunks of 8 bf16, one per thread
+  const int xr = tid >> 2, xc = (tid & 3) * 8;
+  // w tile: 64 rows x 32 k = 512 float4, two per thread
+  for (int k0 = 0; k0 < H; k0 += RT_BK) {
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (t0 + xr < T && k0 + xc < H)
+      xv = *reinterpret_cast<const uint4*>(x + (t0 + xr) * (int64_t)H + k0 + xc);
+    float4 wv[2];
+    int wr_[2], wc_[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int idx = tid + q * 256;
+      wr_[q] = idx >> 3;
+      wc_[q] = (idx & 7) * 4;
+      wv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e0 + wr_[q] < E && k0 + wc_[q] < H)
+        wv[q] = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + wr_[q]) * H + k0 + wc_[q]);
+    }
+    __syncthreads();
+    *reinterpret_cast<uint4*>(&xs[xr * RT_LD + xc]) = xv;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t h[4], m[4], l[4];
+      split3(wv[q].x, h[0], m[0], l[0]);
+      split3(wv[q].y, h[1], m[1], l[1]);
+      split3(wv[q].z, h[2], m[2], l[2]);
+      split3(wv[q].w, h[3], m[3], l[3]);
+      int o = wr_[q] * RT_LD + wc_[q];
+      *reinterpret_cast<uint2*>(&wsp[0][o]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      *reinterpret_cast<uint2*>(&wsp[1][o]) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
+      *reinterpret_cast<uint2*>(&wsp[2][o]) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < RT_BK / 16; ++ks) {
+      const int kk = ks * 16 + (lane >> 5) * 8;
+      bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&xs[(wm * 32 + (lane & 31)) * RT_LD + kk]);
+      const int bo = (wn * 32 + (lane & 31)) * RT_LD + kk;
+      bf16x8_t b2 = *reinterpret_cast<const bf16x8_t*>(&wsp[2][bo]);
+      bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&wsp[1][bo]);
+      bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&wsp[0][bo]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b2, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc, 0, 0, 0);
+    }
+  }
+  // 32x32 accumulator: lane holds column (lane & 31), rows 8*(r/4) + 4*(lane/32) + r%4
+  const int col = e0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    int64_t row = t0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (row < T && col < E) logits[row * E + col] = acc[r];
+  }
+}
+
+__device__ __forceinline__ float sigmoid_f32(float l) {
+  return (float)(1.0 / (1.0 + exp(-(double)l)));
+}
+
+// Total order key: larger = ranks first.  High word: the biased score's bits
+// made unsigned-orderable (NaN -> 0, below everything); low word: ~id, so on
+// equal scores the lower id wins.
+__device__ __forceinline__ uint64_t select_key(float sb, int e) {
+  uint32_t u;
+  if (sb != sb) {
+    u = 0u;
+  } else {
+    u = __float_as_uint(sb + 0.0f);  // -0 -> +0
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
+}
+
+constexpr int TK_PER_LANE = MOE_MAX_EXPERTS_DEV / 64;
+
+// One wavefront per token.  Grid: ceil(T/4) workgroups of 256.
+__global__ __launch_bounds__(256) void router_topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int64_t T, int E, int k, float rsf) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* lrow = logits + t * E;
+  uint64_t key[TK_PER_LANE];
+#pragma unroll
+  for (int i = 0; i < TK_PER_LANE; ++i) {
+    int e = lane + 64 * i;
+    key[i] = 0;
+    if (e < E) {
+      float s = sigmoid_f32(lrow[e]);
+      float b = bias ? bias[e] : 0.0f;
+      key[i] = select_key(s + b, e);
+    }
+  }
+  int mine = -1;  // lane j < k ends up holding the j-th pick
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < TK_PER_LANE; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(~(uint32_t)best);
+#pragma unroll
+    for (int i = 0; i < TK_PER_LANE; ++i)
+      if (key[i] == best) key[i] = 0;  // taken: 0 is below every real key
+    if (lane == j) mine = e;
+  }
+  // ascending order: rank of each pick among the k picks
+  int rank = 0;
+  for (int i = 0; i < k; ++i) {
+    int other = __shfl(mine, i, 64);
+    rank += (lane < k && other < mine) ? 1 : 0;
+  }
+  if (lane < k) {
+    ids[t * k + rank] = mine;
+    wts[t * k + rank] = rsf * sigmoid_f32(lrow[mine]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const float* w, float* logits, int64_t T,
+                                int H, int E, hipStream_t stream) {
+  dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((E + RT_BE - 1) / RT_BE));
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, w, logits, T, H, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const float* logits, const float* bias, int32_t* ids, float* wts,
+                              int64_t T, int E, int k, float rsf, hipStream_t stream) {
+  dim3 grid((unsigned)((T + 3) / 4));
+  hipLaunchKernelGGL(router_topk_kernel, grid, dim3(256), 0, stream, logits, bias, ids, wts, T,
+                     E, k, rsf);
+  return hipGetLastError();
+}

@@ -1,0 +1,169 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the library
+through its C ABI, and compare with the oracle.
+
+Parity bar (the layer's tolerances):
+  * expert ids bit-exact, except tokens whose k-th and (k+1)-th biased
+    scores (oracle) lie within 1e-5 of each other (count reported); for
+    such tokens the oracle re-derives the rest of the layer from the GPU's
+    ids, since either selection is correct;
+  * offsets, sorted_token and inv_pos bit-exact (against the oracle's
+    permutation of the GPU's ids);
+  * emitted weights within W_ULP units in the last place of the oracle's
+    fp32 weight for the same (token, expert);
+  * outputs |gpu - oracle| <= 2e-2 * max(1, |oracle|) elementwise.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from oracle import moe_oracle as mo
+
+NEAR_TIE = 1e-5
+OUT_TOL = 2e-2
+W_ULP = 4
+
+
+def torch_and_lib():
+    import torch
+    import mixture_experts_layer_steered_amd as moe
+    return torch, moe
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(torch, a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
+
+
+def dev_f32(torch, a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+
+def to_bits(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+class Device:
+    """Inputs of one workload resident on the GPU plus the output buffers."""
+
+    def __init__(self, wl, inp: dict):
+        torch, moe = torch_and_lib()
+        self.torch, self.moe, self.wl, self.inp = torch, moe, wl, inp
+        T, H, E, k = inp["x"].shape[0], wl.H, wl.E, wl.k
+        self.T = T
+        self.params = moe.make_params(T, H, E, k, wl.I, wl.I_s, wl.rsf, wl.limit, wl.scmoe, wl.eps)
+        self.x = dev_bf16(torch, inp["x"])
+        self.x_cur = dev_bf16(torch, inp["x_cur"]) if wl.scmoe else None
+        self.w_router = dev_f32(torch, inp["w_router"])
+        self.corr_bias = dev_f32(torch, inp["corr_bias"]) if inp.get("corr_bias") is not None else None
+        self.w_gate_up = dev_bf16(torch, inp["w_gate_up"])
+        self.w_down = dev_bf16(torch, inp["w_down"])
+        self.ws_gate_up = dev_bf16(torch, inp["ws_gate_up"]) if wl.I_s else None
+        self.ws_down = dev_bf16(torch, inp["ws_down"]) if wl.I_s else None
+        self.gamma_pre = dev_f32(torch, inp["gamma_pre"]) if inp.get("gamma_pre") is not None else None
+        self.gamma_post = dev_f32(torch, inp["gamma_post"]) if inp.get("gamma_post") is not None else None
+        self.weights = moe.make_weights(self.w_router, self.corr_bias, self.w_gate_up, self.w_down,
+                                        self.ws_gate_up, self.ws_down, self.gamma_pre,
+                                        self.gamma_post)
+        nbytes = moe.moe_workspace_size(self.params)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        N = T * k
+        self.ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        self.sorted_token = torch.empty(max(N, 1), dtype=torch.int32, device="cuda")
+        self.inv_pos = torch.empty(max(N, 1), dtype=torch.int32, device="cuda")
+        self.xr = torch.empty((T, H), dtype=torch.int16, device="cuda") if wl.scmoe else None
+        self.probes = moe.make_probes(self.ids, self.w, self.offsets, self.sorted_token,
+                                      self.inv_pos, self.xr)
+
+    def canary(self) -> None:
+        """Fill every output with NaN / out-of-range bits first, so that an
+        element the kernels never write shows up."""
+        self.out.fill_(0x7FC0)
+        self.ids.fill_(-7)
+        self.w.fill_(float("nan"))
+        self.offsets.fill_(-7)
+        self.sorted_token.fill_(-7)
+        self.inv_pos.fill_(-7)
+        if self.xr is not None:
+            self.xr.fill_(0x7FC0)
+
+    def run(self) -> None:
+        self.moe.moe_forward(self.params, self.x, self.x_cur, self.weights, self.out, self.probes,
+                             self.ws)
+
+    def result(self) -> dict:
+        self.torch.cuda.synchronize()
+        N = self.T * self.wl.k
+        r = dict(out=to_bits(self.out), ids=self.ids.cpu().numpy(), w=self.w.cpu().numpy(),
+                 offsets=self.offsets.cpu().numpy(),
+                 sorted_token=self.sorted_token.cpu().numpy()[:N],
+                 inv_pos=self.inv_pos.cpu().numpy()[:N])
+        if self.xr is not None:
+            r["xr"] = to_bits(self.xr)
+        return r
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    return np.abs(a.astype(np.float64) - b.astype(np.float64)) / np.spacing(np.abs(b)).astype(np.float64)
+
+
+def check_layer(wl, inp: dict, gpu: dict, rows: np.ndarray | None = None) -> dict:
+    """Compare one GPU forward with the oracle.  `rows` = token sample for
+    the output check (None = all tokens); routing and the permutation are
+    always checked on every token.  Returns a report; raises AssertionError
+    on any violation."""
+    kw = dict(k=wl.k, rsf=wl.rsf, limit=wl.limit, scmoe=wl.scmoe, eps=wl.eps)
+    T = inp["x"].shape[0]
+    rep: dict = {}
+    # --- routing on every token (the oracle's router only: cheap)
+    if wl.scmoe:
+        xr = mo.rmsnorm_bf16(inp["x"], inp.get("gamma_pre"), wl.eps)
+        rep["xr_mismatch"] = int(np.sum(xr != gpu["xr"]))
+        assert rep["xr_mismatch"] == 0, f"pre-norm output differs in {rep['xr_mismatch']} elements"
+    else:
+        xr = inp["x"]
+    logits = mo.router_logits(xr, inp["w_router"])
+    r = mo.topk_route(logits, inp.get("corr_bias"), wl.k, wl.rsf)
+    mism = np.any(gpu["ids"] != r["ids"], axis=1)
+    near = r["gap"] < NEAR_TIE
+    rep["near_tie_tokens"] = int(near.sum())
+    rep["id_mismatch_tokens"] = int(mism.sum())
+    bad = np.nonzero(mism & ~near)[0]
+    assert bad.size == 0, f"ids differ on non-near-tie tokens {bad[:10]} (gaps {r['gap'][bad[:10]]})"
+    ids_g = gpu["ids"]
+    assert np.all((ids_g >= 0) & (ids_g < wl.E)), "ids out of range"
+    assert np.all(np.diff(ids_g, axis=1) > 0), "ids not strictly ascending"
+    w_ref = (np.float32(wl.rsf) * np.take_along_axis(r["s"], ids_g.astype(np.int64), 1)).astype(np.float32)
+    ud = ulp_distance(gpu["w"], w_ref)
+    rep["w_max_ulp"] = float(ud.max()) if ud.size else 0.0
+    assert rep["w_max_ulp"] <= W_ULP, f"weights off by {rep['w_max_ulp']} ulp"
+    # --- permutation of the GPU's ids, bit-exact
+    p = mo.permute(ids_g, wl.E)
+    for key in ("offsets", "sorted_token", "inv_pos"):
+        assert np.array_equal(gpu[key], p[key]), f"{key} differs"
+    rep["experts_touched"] = int(np.sum(p["counts"] > 0))
+    rep["max_over_mean_count"] = float(p["counts"].max() / max(p["counts"].mean(), 1e-9))
+    # --- outputs
+    if rows is None:
+        rows = np.arange(T)
+    sub = mo.take_rows(inp, rows)
+    res = mo.forward(sub, ids=ids_g[rows], **kw)
+    o_ref = mo.bf16_to_f64(res["out"])
+    o_gpu = mo.bf16_to_f64(gpu["out"][rows])
+    assert np.all(np.isfinite(o_gpu)), "non-finite output (unwritten element?)"
+    d = np.abs(o_gpu - o_ref) / (OUT_TOL * np.maximum(1.0, np.abs(o_ref)))
+    rep["out_max_d_over_tol"] = float(d.max()) if d.size else 0.0
+    rep["out_exact_frac"] = float(np.mean(o_gpu == o_ref)) if d.size else 1.0
+    rep["rows_checked"] = int(len(rows))
+    assert rep["out_max_d_over_tol"] <= 1.0, f"output tolerance exceeded: {rep}"
+    return rep

@@ -1,0 +1,147 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, the Python structs match the C layout, and every
+host-side validation path returns its documented status (no kernel is
+launched on any of these paths)."""
+import ctypes
+import math
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("mixture_experts_layer_steered_amd")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe.EXPORTED)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_struct_layout_matches_header(tmp_path):
+    prog = tmp_path / "layout.c"
+    prog.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
+        "int main(void){\n"
+        'printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(moe_params), offsetof(moe_params, norm_eps),'
+        " offsetof(moe_params, scmoe), sizeof(moe_weights), sizeof(moe_probes),"
+        " offsetof(moe_probes, events));\n"
+        "return 0;}\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(prog), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("HIP headers unusable from gcc: " + r.stderr[:200])
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(moe.moe_params), moe.moe_params.norm_eps.offset,
+            moe.moe_params.scmoe.offset, ctypes.sizeof(moe.moe_weights),
+            ctypes.sizeof(moe.moe_probes), moe.moe_probes.events.offset]
+    assert got == want
+
+
+def P(**kw):
+    base = dict(T=64, H=128, E=8, k=2, I=256, I_shared=256, routed_scaling_factor=1.0,
+                swiglu_limit=7.0, scmoe=False, norm_eps=1e-6)
+    base.update(kw)
+    return moe.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=17, E=32), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=9, E=8), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(H=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(I=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(I_shared=-8), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(swiglu_limit=0.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(swiglu_limit=-1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(swiglu_limit=math.nan), moe.MOE_ERR_INVALID_ARG),
+    (dict(swiglu_limit=math.inf), moe.MOE_ERR_INVALID_ARG),
+    (dict(routed_scaling_factor=math.inf), moe.MOE_ERR_INVALID_ARG),
+    (dict(scmoe=True, norm_eps=0.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(H=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(I=260), moe.MOE_ERR_UNSUPPORTED),
+    (dict(I_shared=12), moe.MOE_ERR_UNSUPPORTED),
+    (dict(E=1025, k=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=2 ** 28, k=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(scmoe=True, H=8200), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_param_validation(kw, status):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(P(**kw))
+    assert ei.value.status == status
+    assert moe._lib.moe_last_error().decode() != ""
+
+
+def test_workspace_size_is_pure_and_grows():
+    a = moe.moe_workspace_size(P())
+    assert a == moe.moe_workspace_size(P()) and a > 0
+    assert moe.moe_workspace_size(P(T=128)) > a
+    assert moe.moe_workspace_size(P(T=0)) >= 0
+
+
+def test_entry_points_reject_before_launch():
+    """Null / misaligned pointers and short workspaces fail on the host."""
+    p = P()
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_router_topk(p, None, 16, None, 16, 16, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_router_topk(p, 18, 16, None, 16, 16, 16, stream=0)   # misaligned x
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    # workspace of 0 bytes (an int pointer carries no size)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_router_topk(p, 16, 16, None, 16, 16, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_grouped_swiglu_gemm(4, 100, 128, 256, float("nan"), 16, None, 16, 16, 16, 16, 16,
+                                    16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_grouped_swiglu_gemm(0, 100, 128, 256, 7.0, 16, None, 16, 16, 16, 16, 16, 16,
+                                    stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    w = moe.make_weights(16, None, 16, 16, 16, 16)
+    with pytest.raises(moe.MoeError) as ei:   # ScMoE without the shared input
+        moe.moe_forward(P(scmoe=True), 16, None, w, 16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:   # shared expert weights missing
+        moe.moe_forward(P(), 16, None, moe.make_weights(16, None, 16, 16), 16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:   # workspace too small
+        moe.moe_forward(P(), 16, None, w, 16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop_without_pointers():
+    p = P(T=0)
+    moe.moe_forward(p, None, None, moe.make_weights(None, None, None, None), None, None, None,
+                    stream=0)
+    moe.moe_router_topk(p, None, None, None, None, None, None, stream=0)
+    moe.moe_combine(p, None, None, None, None, None, None, stream=0)
+    moe.moe_grouped_swiglu_gemm(3, 0, 128, 256, 7.0, None, None, None, None, None, None, None,
+                                None, stream=0)
+
+
+def test_status_strings():
+    for s, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARG"), (2, "MOE_ERR_UNSUPPORTED"),
+                    (3, "MOE_ERR_WORKSPACE"), (4, "MOE_ERR_DEVICE")]:
+        assert moe._lib.moe_status_string(s).decode() == name

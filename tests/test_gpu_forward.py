@@ -1,0 +1,149 @@
+"""Whole-layer parity on the GPU (moe_forward through the C ABI) against
+the oracle: small and medium shapes compared on every element, the
+measured workloads at full size on every token's routing and permutation
+and on a sample of tokens' outputs (the layer is row-independent, so the
+oracle computes those rows alone), plus the layer's degenerate cases."""
+import numpy as np
+import pytest
+
+import moe_inputs
+from moe_inputs import Workload
+from oracle import moe_oracle as mo
+from tests import gpu_harness as gh
+from tests.helpers import load_hand_example
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    torch, _ = gh.torch_and_lib()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_and_check(wl, inp, rows=None):
+    gh.note(f"forward {wl.label()} T={inp['x'].shape[0]}")
+    d = gh.Device(wl, inp)
+    d.canary()
+    d.run()
+    gpu = d.result()
+    rep = gh.check_layer(wl, inp, gpu, rows)
+    gh.note(f"  {rep}")
+    return rep, gpu, d
+
+
+SMALL = {
+    "tiny": moe_inputs.WORKLOADS["tiny"],
+    # several m-tiles and n-tiles, K and N tails (H, I not multiples of 64/128)
+    "medium_ragged": Workload("medium_ragged", T=300, H=520, E=24, k=6, I=264, I_s=136, rsf=1.7),
+    # decode-like: few rows per expert (weight-streaming tiles)
+    "decode_small": Workload("decode_small", T=20, H=512, E=40, k=4, I=176, I_s=352),
+    # no shared expert
+    "no_shared": Workload("no_shared", T=150, H=256, E=16, k=3, I=128, I_s=0),
+    # clamp stress: large weights push |g|, |u| past the limit
+    "clamp_stress": Workload("clamp_stress", T=64, H=128, E=8, k=2, I=256, I_s=256,
+                             weight_std=0.3),
+    # ScMoE pairing with random RMSNorm gains
+    "scmoe_gamma": Workload("scmoe_gamma", T=200, H=384, E=32, k=4, I=192, I_s=256,
+                            scmoe=True, gamma_jitter=0.1),
+    # k at its bound, many experts
+    "k16": Workload("k16", T=96, H=256, E=300, k=16, I=64, I_s=64, rsf=2.5),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    wl = SMALL[name]
+    inp = moe_inputs.generate(wl, seed=0)
+    rep, _, _ = run_and_check(wl, inp)
+    assert rep["rows_checked"] == wl.T
+
+
+def test_forward_hand_example():
+    inp, p, exp = load_hand_example()
+    # the library needs H, I multiples of 8: embed the example in zeros
+    H8, I8 = 8, 8
+    T, E = p["T"], p["E"]
+    x = np.zeros((T, H8), np.uint16)
+    x[:, :2] = inp["x"]
+    wr = np.zeros((E, H8), np.float32)
+    wr[:, :2] = inp["w_router"]
+    wgu = np.zeros((E, 2 * I8, H8), np.uint16)
+    wgu[:, 0, :2] = inp["w_gate_up"][:, 0]
+    wgu[:, I8, :2] = inp["w_gate_up"][:, 1]
+    wd = np.zeros((E, H8, I8), np.uint16)
+    wd[:, :2, 0] = inp["w_down"][:, :, 0]
+    sgu = np.zeros((2 * I8, H8), np.uint16)
+    sgu[0, :2] = inp["ws_gate_up"][0]
+    sgu[I8, :2] = inp["ws_gate_up"][1]
+    sd = np.zeros((H8, I8), np.uint16)
+    sd[:2, 0] = inp["ws_down"][:, 0]
+    full = dict(x=x, w_router=wr, corr_bias=inp["corr_bias"], w_gate_up=wgu, w_down=wd,
+                ws_gate_up=sgu, ws_down=sd)
+    wl = Workload("hand", T=T, H=H8, E=E, k=p["k"], I=I8, I_s=I8, rsf=p["rsf"], limit=p["limit"])
+    rep, gpu, _ = run_and_check(wl, full)
+    np.testing.assert_array_equal(gpu["ids"], exp["ids"])
+    np.testing.assert_array_equal(gpu["offsets"], exp["offsets"])
+    np.testing.assert_array_equal(gpu["sorted_token"], exp["sorted_token"])
+    np.testing.assert_array_equal(gpu["inv_pos"], exp["inv_pos"])
+    np.testing.assert_allclose(gpu["w"], exp["w"], rtol=1e-7)
+    out = mo.bf16_to_f64(gpu["out"][:, :2])
+    np.testing.assert_array_equal(out, np.asarray(exp["out"], np.float64))
+    assert np.all(gpu["out"][:, 2:] == 0)
+
+
+def test_forward_single_expert_is_dense_ffn():
+    """E=1, k=1, zero router, rsf=2 -> weight exactly 1: the layer is the
+    dense clamped SwiGLU FFN plus the shared one."""
+    wl = Workload("e1", T=77, H=256, E=1, k=1, I=136, I_s=64, rsf=2.0, weight_std=0.2)
+    inp = moe_inputs.generate(wl, seed=3)
+    inp["w_router"][:] = 0
+    inp["corr_bias"][:] = 0
+    rep, gpu, _ = run_and_check(wl, inp)
+    assert np.all(gpu["w"] == 1.0)
+    assert np.all(gpu["ids"] == 0)
+
+
+def test_forward_single_token_and_empty_batch():
+    wl = Workload("t1", T=1, H=64, E=4, k=2, I=32, I_s=16)
+    run_and_check(wl, moe_inputs.generate(wl, seed=1))
+    # T = 0 is a no-op that succeeds
+    torch, moe = gh.torch_and_lib()
+    p = moe.make_params(0, 64, 4, 2, 32, 16, 1.0, 7.0)
+    w = moe.make_weights(None, None, None, None)
+    out = torch.empty(0, dtype=torch.int16, device="cuda")
+    moe.moe_forward(p, None, None, w, out, None, None)
+
+
+# ---------------------------------------------- measured workloads ----
+
+def _full(name, sample):
+    wl = moe_inputs.WORKLOADS[name]
+    gh.note(f"generating {wl.label()}")
+    inp = moe_inputs.generate(wl, seed=0)
+    rows = None
+    if sample is not None:
+        rows = np.sort(np.random.default_rng(7).choice(wl.T, size=sample, replace=False))
+    rep, _, dev = run_and_check(wl, inp, rows)
+    del dev
+    return rep
+
+
+def test_forward_decode_full():
+    rep = _full("decode", None)
+    assert rep["rows_checked"] == 32
+
+
+def test_forward_prefill_full_sampled():
+    _full("prefill", 96)
+
+
+def test_forward_scmoe_full_sampled():
+    _full("scmoe", 96)
+
+
+def test_forward_zipf_full_sampled():
+    rep = _full("zipf", 48)
+    # the Zipf-scaled router leaves the expert load strongly skewed
+    assert rep["max_over_mean_count"] > 4

@@ -1,0 +1,198 @@
+"""Per-entry-point parity on the GPU: router top-k, permute, grouped SwiGLU
+GEMM and combine, each called through the C ABI and compared with the
+oracle element by element on seeded inputs that span several tiles and a
+ragged tail."""
+import numpy as np
+import pytest
+
+import moe_inputs
+from oracle import moe_oracle as mo
+from tests import gpu_harness as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tl():
+    torch, moe = gh.torch_and_lib()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch, moe
+
+
+# ------------------------------------------------------------ router ----
+
+@pytest.mark.parametrize("T,H,E,k,rsf", [
+    (1, 8, 1, 1, 1.0),          # degenerate: one token, one expert
+    (100, 136, 8, 2, 1.0),      # ragged T, H not a multiple of the K step
+    (333, 512, 64, 8, 2.5),     # several token tiles, scaled weights
+    (70, 256, 200, 16, 1.0),    # k at its bound, E not a multiple of 64
+    (65, 128, 1024, 16, 1.0),   # E at its bound
+    (64, 64, 16, 16, 1.0),      # k == E
+])
+def test_router_topk_parity(tl, T, H, E, k, rsf):
+    torch, moe = tl
+    gh.note(f"router T={T} H={H} E={E} k={k}")
+    rng = np.random.default_rng(T + E)
+    x = moe_inputs.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    p = moe.make_params(T, H, E, k, 8, 0, rsf, 7.0)
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ids = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(p, gh.dev_bf16(torch, x), gh.dev_f32(torch, wr), gh.dev_f32(torch, b),
+                        ids, w, ws)
+    torch.cuda.synchronize()
+    ids_g, w_g = ids.cpu().numpy(), w.cpu().numpy()
+    r = mo.topk_route(mo.router_logits(x, wr), b, k, rsf)
+    mism = np.any(ids_g != r["ids"], axis=1)
+    assert not np.any(mism & (r["gap"] >= gh.NEAR_TIE)), np.nonzero(mism)[0][:8]
+    w_ref = (np.float32(rsf) * np.take_along_axis(r["s"], ids_g.astype(np.int64), 1)).astype(np.float32)
+    assert gh.ulp_distance(w_g, w_ref).max() <= gh.W_ULP
+
+
+def test_router_ties_nan_and_no_bias(tl):
+    """Exact ties (identical router rows) go to the lower id; a NaN logit
+    ranks last; NULL bias means zeros."""
+    torch, moe = tl
+    T, H, E, k = 40, 64, 12, 3
+    rng = np.random.default_rng(0)
+    x = moe_inputs.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    wr[5] = wr[2]
+    wr[9] = wr[2]           # experts 2, 5, 9 always tie
+    wr[7] = np.nan          # expert 7's logit is NaN for every token
+    p = moe.make_params(T, H, E, k, 8, 0, 1.0, 7.0)
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(p, gh.dev_bf16(torch, x), gh.dev_f32(torch, wr), None, ids, w, ws)
+    torch.cuda.synchronize()
+    r = mo.topk_route(mo.router_logits(x, wr), None, k, 1.0)
+    np.testing.assert_array_equal(ids.cpu().numpy(), r["ids"])
+    assert not np.any(ids.cpu().numpy() == 7)
+
+
+# ----------------------------------------------------------- permute ----
+
+@pytest.mark.parametrize("T,E,k,skew", [
+    (1, 1, 1, 0.0),
+    (37, 8, 2, 0.0),
+    (1500, 64, 8, 0.0),       # 12000 pairs: three permute tiles
+    (600, 1024, 16, 0.0),     # E and k at their bounds
+    (5000, 256, 8, 3.0),      # heavy skew: few experts take most pairs
+    (700, 100, 4, 50.0),      # extreme skew: most experts empty
+])
+def test_permute_parity(tl, T, E, k, skew):
+    torch, moe = tl
+    gh.note(f"permute T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 3 + E)
+    prob = np.exp(-skew * np.arange(E) / E)
+    prob /= prob.sum()
+    ids = np.stack([np.sort(rng.choice(E, size=k, replace=False, p=prob)) for _ in range(T)]).astype(np.int32)
+    p = moe.make_params(T, 8, E, k, 8, 0, 1.0, 7.0)
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    off = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
+    st = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+    inv = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
+    moe.moe_permute(p, torch.from_numpy(ids).cuda(), off, st, inv, ws)
+    torch.cuda.synchronize()
+    ref = mo.permute(ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(st.cpu().numpy(), ref["sorted_token"])
+    np.testing.assert_array_equal(inv.cpu().numpy(), ref["inv_pos"])
+
+
+# ------------------------------------------------------ grouped GEMM ----
+
+@pytest.mark.parametrize("counts,H,I,std", [
+    ([3], 64, 8, 0.05),                                  # one tiny group
+    ([0, 5, 0, 1, 130, 0, 7], 136, 264, 0.05),          # empty groups, ragged M/N/K
+    ([257, 128, 1, 300], 520, 136, 0.05),               # several m-tiles per group
+    ([40] * 12, 256, 384, 0.3),                          # clamp stress: |g|,|u| past L
+    ([2, 3, 4, 1] * 16, 512, 1408, 0.02),                # short groups (weight streaming tiles)
+])
+def test_grouped_swiglu_gemm_parity(tl, counts, H, I, std):
+    torch, moe = tl
+    gh.note(f"grouped gemm counts={counts[:8]} H={H} I={I}")
+    rng = np.random.default_rng(sum(counts) + H + I)
+    G = len(counts)
+    M = int(sum(counts))
+    rows_a = max(M // 2, 1) + 3
+    a = moe_inputs.f32_to_bf16_bits(rng.standard_normal((rows_a, H)).astype(np.float32))
+    row_index = rng.integers(0, rows_a, M).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    wgu = moe_inputs.f32_to_bf16_bits((rng.standard_normal((G, 2 * I, H)) * std).astype(np.float32))
+    wd = moe_inputs.f32_to_bf16_bits((rng.standard_normal((G, H, I)) * std).astype(np.float32))
+    L = 7.0
+    h = torch.full((M, I), 0x7FC0, dtype=torch.int16, device="cuda")
+    y = torch.full((M, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_grouped_gemm_workspace_size(G, M, H, I), dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_swiglu_gemm(G, M, H, I, L, gh.dev_bf16(torch, a), torch.from_numpy(row_index).cuda(),
+                                torch.from_numpy(offsets).cuda(), gh.dev_bf16(torch, wgu),
+                                gh.dev_bf16(torch, wd), h, y, ws)
+    torch.cuda.synchronize()
+    h_g = mo.bf16_to_f64(gh.to_bits(h))
+    y_g = y.cpu().numpy().astype(np.float64)
+    u32 = 2.0 ** -24
+    for g in range(G):
+        sl = slice(offsets[g], offsets[g + 1])
+        if offsets[g] == offsets[g + 1]:
+            continue
+        A = mo.bf16_to_f64(a[row_index[sl]])
+        Wg_, Wu_ = mo.bf16_to_f64(wgu[g][:I]), mo.bf16_to_f64(wgu[g][I:])
+        gg, uu = A @ Wg_.T, A @ Wu_.T
+        gc, uc = np.minimum(gg, L), np.clip(uu, -L, L)
+        h_ref = gc / (1 + np.exp(-gc)) * uc
+        # forward-error bound: fp32 sums of H products, |silu'| <= 1.1, then
+        # one bf16 rounding (half an ulp = 2^-9 relative)
+        eg = H * u32 * (np.abs(A) @ np.abs(Wg_).T)
+        eu = H * u32 * (np.abs(A) @ np.abs(Wu_).T)
+        bound = 1.1 * np.abs(uc) * eg + np.abs(gc / (1 + np.exp(-gc))) * eu
+        # (+ a few fp32 ulps for evaluating silu and the product)
+        bound = bound + 2.0 ** -9 * (np.abs(h_ref) + bound) + 1e-6 * np.abs(h_ref) + 1e-30
+        assert np.all(np.abs(h_g[sl] - h_ref) <= bound), f"group {g}: h"
+        # y from the GPU's own h: fp32 sums of I products
+        Wd_ = mo.bf16_to_f64(wd[g])
+        y_ref = h_g[sl] @ Wd_.T
+        ey = I * u32 * (np.abs(h_g[sl]) @ np.abs(Wd_).T) + 1e-30
+        assert np.all(np.abs(y_g[sl] - y_ref) <= ey), f"group {g}: y"
+    if std >= 0.3:   # the clamp stress case really hit both clamps
+        A = mo.bf16_to_f64(a[row_index])
+        gg = A[: offsets[1]] @ mo.bf16_to_f64(wgu[0][:I]).T
+        assert (gg > L).any() and (gg < -L).any()
+
+
+# ----------------------------------------------------------- combine ----
+
+@pytest.mark.parametrize("T,H,k,shared,post", [
+    (1, 8, 1, False, False),
+    (77, 136, 3, True, False),
+    (300, 1024, 8, True, False),
+    (50, 520, 4, True, True),        # ScMoE post-norm
+    (20, 8192, 16, False, True),     # post-norm at its H bound
+])
+def test_combine_parity(tl, T, H, k, shared, post):
+    torch, moe = tl
+    gh.note(f"combine T={T} H={H} k={k} shared={shared} post={post}")
+    rng = np.random.default_rng(T + H)
+    N = T * k
+    y = (rng.standard_normal((N, H)) * 3).astype(np.float32)
+    w = rng.uniform(0, 2.5, (T, k)).astype(np.float32)
+    inv = rng.permutation(N).astype(np.int32)
+    ys = (rng.standard_normal((T, H)) * 2).astype(np.float32) if shared else None
+    gamma = rng.uniform(0.9, 1.1, H).astype(np.float32) if post else None
+    p = moe.make_params(T, H, 16, k, 8, 8 if shared else 0, 1.0, 7.0, scmoe=post, norm_eps=1e-6)
+    out = torch.full((T, H), 0x7FC0, dtype=torch.int16, device="cuda")
+    moe.moe_combine(p, gh.dev_f32(torch, y), gh.dev_f32(torch, w), torch.from_numpy(inv).cuda(),
+                    None if ys is None else gh.dev_f32(torch, ys),
+                    None if gamma is None else gh.dev_f32(torch, gamma), out)
+    torch.cuda.synchronize()
+    z = mo.combine(y.astype(np.float64), w, inv, None if ys is None else ys.astype(np.float64))
+    ref = mo.bf16_to_f64(mo.bf16_round(mo.rmsnorm_f64(z, gamma, 1e-6) if post else z))
+    got = mo.bf16_to_f64(gh.to_bits(out))
+    d = np.abs(got - ref) / (gh.OUT_TOL * np.maximum(1, np.abs(ref)))
+    assert d.max() <= 1.0
+    # fp32 accumulation of at most 17 terms: almost every element rounds the same
+    assert np.mean(got == ref) > 0.99
