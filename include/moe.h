@@ -141,6 +141,7 @@ typedef struct moe_probes {
   int32_t* sorted_token;       /* [T * k]                                         */
   int32_t* inv_pos;            /* [T * k]                                         */
   moe_bf16* xr;                /* [T, H] ScMoE routed input after the pre-norm    */
+  float* logits;               /* [T, E] fp32 router logits                       */
   hipEvent_t events[MOE_EV_COUNT];
 } moe_probes;
 
@@ -156,7 +157,9 @@ moe_status moe_workspace_size(const moe_params* p, size_t* bytes);
  *   x         [T, H] bf16 (for ScMoE: the already normalised routed input)
  *   w_router  [E, H] fp32;  corr_bias [E] fp32 or NULL
  *   topk_ids  [T, k] int32 out;  topk_w [T, k] fp32 out
- *   ws        >= moe_workspace_size(p) bytes of scratch
+ *   ws        >= moe_workspace_size(p) bytes of scratch; on return its first
+ *             T*E floats hold the fp32 logits [T, E] (once the stream has
+ *             run the work)
  * Uses p->T, H, E, k, routed_scaling_factor.
  * Sources: "Module glm5next_mlp", "Numerics the kernels rely on" and
  * KERNEL_MAX_TOP_K; "bridge.models.beam.modeling_beam",

@@ -54,7 +54,7 @@ MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_COMBINE, MOE_EV_COUNT = 4, 5, 6, 7
 
 class moe_probes(Structure):
     _fields_ = [(n, c_void_p) for n in (
-        "topk_ids", "topk_w", "expert_offsets", "sorted_token", "inv_pos", "xr")] + [
+        "topk_ids", "topk_w", "expert_offsets", "sorted_token", "inv_pos", "xr", "logits")] + [
         ("events", c_void_p * MOE_EV_COUNT)]
 
 
@@ -187,10 +187,10 @@ def make_weights(w_router, corr_bias, w_gate_up, w_down, ws_gate_up=None, ws_dow
 
 
 def make_probes(topk_ids=None, topk_w=None, expert_offsets=None, sorted_token=None,
-                inv_pos=None, xr=None, events=None) -> moe_probes:
+                inv_pos=None, xr=None, logits=None, events=None) -> moe_probes:
     """`events`: dict {MOE_EV_*: raw hipEvent_t handle (int)}."""
     pr = moe_probes(*[_ptr(t) for t in (topk_ids, topk_w, expert_offsets, sorted_token,
-                                        inv_pos, xr)])
+                                        inv_pos, xr, logits)])
     for i, ev in (events or {}).items():
         pr.events[i] = ev
     return pr

@@ -359,6 +359,7 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
     OPTIONAL_PTR(probes->sorted_token);
     OPTIONAL_PTR(probes->inv_pos);
     OPTIONAL_PTR(probes->xr);
+    OPTIONAL_PTR(probes->logits);
   }
   Layout L = carve(*p, ws);
   if (ws_bytes < L.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.bytes);
@@ -369,6 +370,7 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
     if (probes->sorted_token) L.sorted_token = probes->sorted_token;
     if (probes->inv_pos) L.inv_pos = probes->inv_pos;
     if (probes->xr && p->scmoe) L.xr = probes->xr;
+    if (probes->logits) L.logits = probes->logits;
   }
   const int64_t T = p->T, N = T * p->k;
   const GemmVariant v = pick_variant(N, p->E);
