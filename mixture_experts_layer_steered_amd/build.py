@@ -39,9 +39,6 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
-    if src.endswith(".cpp"):
-        cmd = [hipcc(), "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-c",
-               os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

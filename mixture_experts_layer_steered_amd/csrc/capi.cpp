@@ -1,9 +1,12 @@
 // Host side of the C ABI declared in include/moe.h: argument validation,
 // workspace carving and launch sequencing.  Nothing here allocates device
 // memory or synchronises; every kernel goes onto the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "../../include/moe.h"
@@ -89,14 +92,43 @@ struct Carver {
   }
 };
 
-GemmVariant pick_variant(int64_t rows, int64_t groups) {
-  // about one MFMA row tile or less per group: stream the weights with short
-  // tiles; otherwise the LDS-tiled prefill tiles
-  return (rows <= 64 * groups) ? GemmVariant::kStream : GemmVariant::kTiled;
+// Tile variant by the mean rows per group: about one short row tile or less
+// (decode) -> 32-row tiles; several 256-row tiles -> the pipelined 256-row
+// tiles; in between the 128-row tiles.  MOE_GEMM_VARIANT=tile32 | tile128 |
+// pipe256 | stream forces one (a tuning lever; results are identical up to
+// fp32 summation order).
+GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
+  if (const char* env = std::getenv("MOE_GEMM_VARIANT")) {
+    if (!std::strcmp(env, "tile32")) return GemmVariant::kTile32;
+    if (!std::strcmp(env, "tile128")) return GemmVariant::kTile128;
+    if (!std::strcmp(env, "pipe256")) return GemmVariant::kPipe256;
+    if (!std::strcmp(env, "pipe256k64")) return GemmVariant::kPipe256K64;
+    if (!std::strcmp(env, "stream32")) return GemmVariant::kStream32;
+    if (!std::strcmp(env, "stream")) return GemmVariant::kStream;
+  }
+  if (rows <= 64 * groups) return GemmVariant::kTile32;
+  if (rows >= 512 * groups) return GemmVariant::kPipe256;
+  return GemmVariant::kTile128;
+}
+
+// The pipelined variant addresses A rows and one group's weights with 32-bit
+// element offsets and steps K in whole 32-wide stages; other operands fall
+// back to the 128-row tiles.
+GemmVariant pick_variant(int64_t rows, int64_t groups, int64_t a_elems, int64_t w_group_elems,
+                         bool k_multiple_of_32, bool k_multiple_of_64) {
+  GemmVariant v = pick_variant_raw(rows, groups);
+  const int64_t lim = (int64_t)1 << 31;
+  const bool pipe = v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64;
+  if (pipe && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32)) v = GemmVariant::kTile128;
+  if (v == GemmVariant::kPipe256K64 && !k_multiple_of_64) v = GemmVariant::kPipe256;
+  if (v == GemmVariant::kStream32 && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_64))
+    v = GemmVariant::kTile32;
+  return v;
 }
 
 struct Layout {
   float* logits;
+  float* partial;
   int32_t* ids;
   float* w;
   int32_t* counts;
@@ -119,7 +151,9 @@ Layout carve(const moe_params& p, void* ws) {
   const int64_t T = p.T, N = p.T * p.k;
   const int tiles = permute_tiles(N);
   Layout L;
+  const int splits = router_splits(T, p.H, p.E);
   L.logits = c.take<float>(T * p.E);
+  L.partial = c.take<float>(splits > 1 ? (size_t)splits * T * p.E : 0);
   L.ids = c.take<int32_t>(N);
   L.w = c.take<float>(N);
   L.counts = c.take<int32_t>((size_t)tiles * p.E);
@@ -137,8 +171,15 @@ Layout carve(const moe_params& p, void* ws) {
   return L;
 }
 
-// Router-only and permute-only entry points use the front of the workspace.
-size_t router_ws_bytes(const moe_params& p) { return (size_t)p.T * p.E * sizeof(float); }
+// Router-only and permute-only entry points use the front of the workspace
+// (router: the logits first, then the K-slice partials).
+size_t router_ws_bytes(const moe_params& p) {
+  Carver c;
+  const int splits = router_splits(p.T, p.H, p.E);
+  c.take<float>((size_t)p.T * p.E);
+  c.take<float>(splits > 1 ? (size_t)splits * p.T * p.E : 0);
+  return c.off;
+}
 size_t permute_ws_bytes(const moe_params& p) {
   Carver c;
   const int tiles = permute_tiles(p.T * p.k);
@@ -154,9 +195,9 @@ moe_status device_status(hipError_t e, const char* what) {
 
 GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int32_t* offsets,
                          const int32_t* mstart, const uint16_t* W, int64_t w_stride, void* out,
-                         int64_t M, int G, int N, int K, GemmVariant v) {
+                         int64_t M, int G, int N, int K, GemmVariant v, bool gateup) {
   GemmProblem P;
-  const int bm = gemm_tile_m(v), bn = gemm_tile_n(v);
+  const int bm = gemm_tile_m(v), bn = gemm_tile_n(v, gateup);
   P.A = A;
   P.row_index = row_index;
   P.group_offsets = offsets;
@@ -174,7 +215,9 @@ GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int3
 }
 
 bool tiles_fit(const GemmProblem& a, const GemmProblem* b) {
-  int64_t t = (int64_t)a.max_mtiles * a.ntiles + (b ? (int64_t)b->max_mtiles * b->ntiles : 0);
+  // n-tiles padded to blocks of 8 (the pipelined variant's tile order)
+  auto n = [](const GemmProblem& p) { return (int64_t)p.max_mtiles * ((p.ntiles + 7) / 8 * 8); };
+  const int64_t t = n(a) + (b ? n(*b) : 0);
   return t < ((int64_t)1 << 31);
 }
 
@@ -217,13 +260,14 @@ moe_status moe_router_topk(const moe_params* p, const moe_bf16* x, const float* 
   REQUIRE_PTR(ws);
   if (ws_bytes < router_ws_bytes(*p))
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, router_ws_bytes(*p));
-  float* logits = static_cast<float*>(ws);
-  if ((s = device_status(launch_router_logits(x, w_router, logits, p->T, p->H, p->E, stream),
-                         "router logits")) != MOE_OK)
-    return s;
-  if ((s = device_status(launch_router_topk(logits, corr_bias, topk_ids, topk_w, p->T, p->E, p->k,
-                                            p->routed_scaling_factor, stream),
-                         "router top-k")) != MOE_OK)
+  Carver c;
+  c.base = static_cast<char*>(ws);
+  const int splits = router_splits(p->T, p->H, p->E);
+  float* logits = c.take<float>((size_t)p->T * p->E);
+  float* partial = c.take<float>(splits > 1 ? (size_t)splits * p->T * p->E : 0);
+  if ((s = device_status(launch_router(x, w_router, corr_bias, logits, partial, topk_ids, topk_w,
+                                       p->T, p->H, p->E, p->k, p->routed_scaling_factor, stream),
+                         "router")) != MOE_OK)
     return s;
   return ok();
 }
@@ -288,12 +332,17 @@ moe_status moe_grouped_swiglu_gemm(int32_t n_groups, int64_t M_total, int32_t H,
   REQUIRE_PTR(y);
   REQUIRE_PTR(ws);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  const GemmVariant v = pick_variant(M_total, n_groups);
+  // A is addressed up to the largest row it can hold; the gate_up A is the
+  // caller's [rows_a, H] input (rows_a unknown here: bound it by M_total when
+  // gathered rows can repeat, the routed case), the down A is h [M_total, I].
+  const GemmVariant v =
+      pick_variant(M_total, n_groups, std::max<int64_t>(M_total, 1) * std::max(H, I),
+                   (int64_t)2 * I * H, H % 32 == 0 && I % 32 == 0, H % 64 == 0 && I % 64 == 0);
   int32_t* mstart = static_cast<int32_t*>(ws);
   GemmProblem gu = make_problem(a, row_index, group_offsets, mstart, w_gate_up,
-                                (int64_t)2 * I * H, h, M_total, n_groups, I, H, v);
+                                (int64_t)2 * I * H, h, M_total, n_groups, I, H, v, true);
   GemmProblem dn = make_problem(h, nullptr, group_offsets, mstart, w_down, (int64_t)H * I, y,
-                                M_total, n_groups, H, I, v);
+                                M_total, n_groups, H, I, v, false);
   if (!tiles_fit(gu, nullptr) || !tiles_fit(dn, nullptr))
     return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");
   const int bm = gemm_tile_m(v);
@@ -373,19 +422,23 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
     if (probes->logits) L.logits = probes->logits;
   }
   const int64_t T = p->T, N = T * p->k;
-  const GemmVariant v = pick_variant(N, p->E);
+  const GemmVariant v = pick_variant(
+      N, p->E, std::max<int64_t>(N, T) * std::max(p->H, std::max(p->I, p->I_shared)),
+      (int64_t)2 * std::max(p->I, p->I_shared) * p->H,
+      p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0,
+      p->H % 64 == 0 && p->I % 64 == 0 && p->I_shared % 64 == 0);
   const uint16_t* xr = x_routed;
   const uint16_t* xs = x_shared ? x_shared : x_routed;
   const bool shared = p->I_shared > 0;
 
   GemmProblem gu = make_problem(xr, L.sorted_token, L.offsets, L.mstart, w->w_gate_up,
-                                (int64_t)2 * p->I * p->H, L.h, N, p->E, p->I, p->H, v);
+                                (int64_t)2 * p->I * p->H, L.h, N, p->E, p->I, p->H, v, true);
   GemmProblem dn = make_problem(L.h, nullptr, L.offsets, L.mstart, w->w_down,
-                                (int64_t)p->H * p->I, L.y, N, p->E, p->H, p->I, v);
+                                (int64_t)p->H * p->I, L.y, N, p->E, p->H, p->I, v, false);
   GemmProblem sgu = make_problem(xs, nullptr, nullptr, nullptr, w->ws_gate_up, 0, L.hs, T, 1,
-                                 p->I_shared, p->H, v);
+                                 p->I_shared, p->H, v, true);
   GemmProblem sdn = make_problem(L.hs, nullptr, nullptr, nullptr, w->ws_down, 0, L.ys, T, 1, p->H,
-                                 p->I_shared, v);
+                                 p->I_shared, v, false);
   if (p->scmoe) gu.A = L.xr;
   if (!tiles_fit(gu, shared ? &sgu : nullptr) || !tiles_fit(dn, shared ? &sdn : nullptr))
     return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");
@@ -404,12 +457,9 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
     xr = L.xr;
   }
   if ((s = mark(MOE_EV_PRENORM)) != MOE_OK) return s;
-  if ((s = device_status(launch_router_logits(xr, w->w_router, L.logits, T, p->H, p->E, stream),
-                         "router logits")) != MOE_OK)
-    return s;
-  if ((s = device_status(launch_router_topk(L.logits, w->corr_bias, L.ids, L.w, T, p->E, p->k,
-                                            p->routed_scaling_factor, stream),
-                         "router top-k")) != MOE_OK)
+  if ((s = device_status(launch_router(xr, w->w_router, w->corr_bias, L.logits, L.partial, L.ids,
+                                       L.w, T, p->H, p->E, p->k, p->routed_scaling_factor, stream),
+                         "router")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_ROUTER)) != MOE_OK) return s;
   if ((s = device_status(launch_permute(L.ids, L.counts, L.starts, L.offsets, L.sorted_token,

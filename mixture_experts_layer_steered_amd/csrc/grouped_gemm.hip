@@ -28,6 +28,8 @@
 // exits when past the end.  Workgroup ids are remapped so each of the 8 XCDs
 // works a contiguous range of tiles, m-tiles fastest: consecutive tiles on an
 // XCD share one weight n-tile in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -206,6 +208,145 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tile, float 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming variant, for expert segments of about one row tile or less
+// (decode): the weights are read exactly once and nothing is reused, so
+// they bypass LDS.  A workgroup owns one m-tile of up to 32 rows and 64
+// weight rows (gate_up: 32 gate + the matching 32 up rows; down: 64 output
+// columns).  Its 4 wavefronts split K into 4 contiguous ranges; each lane
+// loads 64 contiguous bytes of its row per 64-wide K chunk, two chunks per
+// iteration, straight into MFMA operand registers (A rows and weight rows
+// use the same K assignment, so the MFMA pairs matching K indices).  The
+// four partial accumulators are summed through LDS in wave order (fixed,
+// so reruns repeat), then the epilogue writes h (clamped SwiGLU) or y.
+constexpr int ST_BM = 32;   // rows per tile
+constexpr int ST_WR = 64;   // weight rows per tile (two 32-wide MFMA column tiles)
+constexpr int ST_UNROLL = 2;
+
+template <bool GATEUP>
+__device__ __forceinline__ void stream_tile(const GemmProblem& P, int tile, float limit) {
+  __shared__ float red[4][2][16][64];  // [wave][col tile][acc reg][lane]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int mt_global = tile / P.ntiles;  // n-tiles fastest: one expert's tiles share its A rows
+  const int nt = tile % P.ntiles;
+
+  int g = 0;
+  int64_t row0, row_end;
+  if (P.group_offsets == nullptr) {
+    row0 = (int64_t)mt_global * ST_BM;
+    row_end = P.M;
+    if (row0 >= row_end) return;
+  } else {
+    if (mt_global >= P.mtile_start[P.G]) return;
+    int lo = 0, hi = P.G - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (P.mtile_start[mid] <= mt_global) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    row0 = P.group_offsets[g] + (int64_t)(mt_global - P.mtile_start[g]) * ST_BM;
+    row_end = P.group_offsets[g + 1];
+  }
+  const int K = P.K, N = P.N;
+  const int j = lane & 31, half = lane >> 5;
+  // this lane's A row and its two weight rows
+  const int64_t r = row0 + j;
+  const uint16_t* a_row = nullptr;
+  if (r < row_end) a_row = P.A + (P.row_index ? (int64_t)P.row_index[r] : r) * K;
+  const uint16_t* __restrict__ Wg = P.W + (int64_t)g * P.w_stride;
+  const uint16_t* b_row[2];
+  int n0;
+  if (GATEUP) {
+    n0 = nt * 32;
+    const int n = n0 + j;
+    b_row[0] = n < N ? Wg + (int64_t)n * K : nullptr;         // gate row
+    b_row[1] = n < N ? Wg + (int64_t)(N + n) * K : nullptr;   // matching up row
+  } else {
+    n0 = nt * 64;
+    b_row[0] = n0 + j < N ? Wg + (int64_t)(n0 + j) * K : nullptr;
+    b_row[1] = n0 + 32 + j < N ? Wg + (int64_t)(n0 + 32 + j) * K : nullptr;
+  }
+  // K chunks of 64, split into 4 contiguous ranges
+  const int chunks = (K + 63) >> 6;
+  const int c_begin = wave * chunks / 4, c_end = (wave + 1) * chunks / 4;
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[t][q] = 0.f;
+
+  for (int c = c_begin; c < c_end; c += ST_UNROLL) {
+    uint4 av[ST_UNROLL][4], bv[ST_UNROLL][2][4];
+#pragma unroll
+    for (int u = 0; u < ST_UNROLL; ++u) {
+      const int kc = (c + u) * 64 + half * 32;
+      const bool chunk_ok = c + u < c_end;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kq = kc + q * 8;
+        const bool in = chunk_ok && kq < K;
+        av[u][q] = (in && a_row) ? *reinterpret_cast<const uint4*>(a_row + kq) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          bv[u][t][q] = (in && b_row[t]) ? *reinterpret_cast<const uint4*>(b_row[t] + kq)
+                                         : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < ST_UNROLL; ++u) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av[u][q]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv[u][t][q]),
+                                                          acc[t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) red[wave][t][q][lane] = acc[t][q];
+  __syncthreads();
+
+  // element (reg q, lane l) of column tile t is row 8*(q/4) + 4*(l/32) + q%4,
+  // column (l & 31) of that tile
+  if (GATEUP) {
+    uint16_t* __restrict__ h = static_cast<uint16_t*>(P.out);
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int q = e >> 6, l = e & 63;
+      const float gsum = red[0][0][q][l] + red[1][0][q][l] + red[2][0][q][l] + red[3][0][q][l];
+      const float usum = red[0][1][q][l] + red[1][1][q][l] + red[2][1][q][l] + red[3][1][q][l];
+      const int64_t row = row0 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
+      const int col = n0 + (l & 31);
+      if (row < row_end && col < N)
+        h[row * N + col] = (uint16_t)f32_to_bf16_bits(swiglu_clamped(gsum, usum, limit));
+    }
+  } else {
+    float* __restrict__ y = static_cast<float*>(P.out);
+    for (int e = threadIdx.x; e < 2 * 16 * 64; e += 256) {
+      const int t = e >> 10, q = (e >> 6) & 15, l = e & 63;
+      const float v = red[0][t][q][l] + red[1][t][q][l] + red[2][t][q][l] + red[3][t][q][l];
+      const int64_t row = row0 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
+      const int col = n0 + t * 32 + (l & 31);
+      if (row < row_end && col < N) y[row * N + col] = v;
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void grouped_stream_kernel(GemmProblem p0, GemmProblem p1,
+                                                             int tiles0, float limit) {
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  if (tile < tiles0)
+    stream_tile<GATEUP>(p0, tile, limit);
+  else
+    stream_tile<GATEUP>(p1, tile - tiles0, limit);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void grouped_gemm_kernel(
     GemmProblem p0, GemmProblem p1, int tiles0, float limit) {
@@ -214,6 +355,378 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void grouped_gemm_kernel(
     gemm_tile<BM, BN, WAVES_M, WAVES_N, GATEUP>(p0, tile, limit);
   else
     gemm_tile<BM, BN, WAVES_M, WAVES_N, GATEUP>(p1, tile - tiles0, limit);
+}
+
+constexpr int PL_NBLK = 8;
+
+// ---------------------------------------------------------------------------
+// Pipelined LDS-tiled variant for long expert segments (prefill).
+//
+// Persistent: one workgroup per CU walks a dense list of output tiles.  The
+// real tile count is read on the device (m-tile prefix x n-tiles, routed
+// and shared problems back to back) and split into 8 equal contiguous
+// ranges, one per XCD (workgroup b runs on XCD b % 8), so every XCD gets the
+// same work and its 32 CUs work on neighbouring tiles that share A and B
+// rows in its L2.  Inside a problem tiles run n-block (8 n-tiles) major,
+// then m-tile, then n-tile.
+//
+// Workgroup tile: BM rows x BN output columns (gate_up: BN gate + BN up
+// weight rows), 4 wavefronts as 2 x 2, each owning (BM/2) x (BN/2) outputs
+// (x2 for gate/up) in 32x32 MFMA accumulators.  K advances KB at a time
+// through STAGES LDS slots filled by direct global->LDS 16-byte loads
+// (global_load_lds_dwordx4), STAGES-1 of them in flight.  A row of a stage
+// is KB*2 bytes; each load instruction writes 1 KB of LDS in lane order
+// (1024/(KB*2) whole rows), and the XOR swizzle of the 16-byte chunk slots
+// -- chosen so the 16 rows one ds_read_b128 pass touches fall in 16
+// different bank groups of the 64-bank LDS -- comes from which global chunk
+// each lane fetches.  Rows past a segment or past N fetch the tile's first
+// row (their products reach only outputs never stored).
+//
+// Per step: the MFMAs of K substep s run while the fragments of substep s+1
+// are read from LDS; the loads of the stage STAGES-1 ahead go out with the
+// first substep; before the last substep each wave waits for its own loads
+// of the next stage and its own LDS reads, then a fence-free barrier makes
+// the next stage visible (its substep-0 fragments are read during the last
+// substep's MFMAs).
+
+__device__ __forceinline__ void lds_direct_16(const void* g, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                   0, 0);
+}
+
+// s_waitcnt vmcnt(n) with lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] and [15:14],
+// expcnt[6:4], lgkmcnt[11:8]): this wave's loads up to the n newest and all of
+// its LDS reads and writes have completed.
+#define PL_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0070)
+#define PL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
+// Workgroup barrier without a memory fence.  __syncthreads() fences, which
+// makes every wave wait for all of its outstanding loads (including the
+// direct-to-LDS loads of later stages) and would drain the pipeline at each
+// step.  Here the waits are explicit (PL_WAIT_VM_LDS before the barrier) and
+// the empty asm statements only stop the compiler from moving memory
+// operations across the barrier.
+__device__ __forceinline__ void pl_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int KB>
+__device__ __forceinline__ int pl_swz(int row, int chunk) {
+  // 64-byte rows: 4 rows share a 256-byte bank cycle; 128-byte rows: 2 rows
+  return KB == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ ((row >> 1) & 7);
+}
+
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, bool DENSE>
+__device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, int tile,
+                                          float limit, uint16_t* smem) {
+  constexpr int NB = GATEUP ? 2 * BN : BN;   // weight rows per tile
+  constexpr int ROWS = BM + NB;              // LDS rows per stage
+  constexpr int CHUNKS = KB / 8;             // 16-byte chunks per row
+  constexpr int STAGE = ROWS * KB;           // bf16 elements per stage
+  constexpr int RPI = 64 / CHUNKS;           // rows per 1 KB load instruction
+  constexpr int INSTR = ROWS / RPI;          // load instructions per stage
+  constexpr int PER_WAVE = INSTR / 4;
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int NMAT = GATEUP ? 2 : 1;
+  constexpr int SUB = KB / 16;               // MFMA K substeps per stage
+  static_assert(INSTR % 4 == 0 && SUB % 2 == 0, "shape");
+  constexpr int A_INSTR = BM / (4 * RPI);    // instructions of each wave that fill A rows
+  static_assert(BM % (4 * RPI) == 0, "A rows fill whole instructions of every wave");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  int mt_global, nt;
+  if (DENSE) {
+    // tile -> (n-block, m-tile, n-tile); the last n-block may be narrower
+    const int full = mt_total * PL_NBLK;
+    const int nb = tile / full;
+    const int rem = tile - nb * full;
+    const int width = min(PL_NBLK, P.ntiles - nb * PL_NBLK);
+    mt_global = rem / width;
+    nt = nb * PL_NBLK + rem % width;
+  } else {
+    // padded tile space: n-tiles fastest (one expert's n-tiles share its A
+    // rows); m-tiles past the device-side count exit
+    mt_global = tile / P.ntiles;
+    nt = tile % P.ntiles;
+    if (mt_global >= mt_total) return;
+  }
+
+  int g = 0;
+  int64_t row0, row_end;
+  if (P.group_offsets == nullptr) {
+    row0 = (int64_t)mt_global * BM;
+    row_end = P.M;
+  } else {
+    int lo = 0, hi = P.G - 1;  // last g with mtile_start[g] <= mt_global
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (P.mtile_start[mid] <= mt_global) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    row0 = P.group_offsets[g] + (int64_t)(mt_global - P.mtile_start[g]) * BM;
+    row_end = P.group_offsets[g + 1];
+  }
+  const int n0 = nt * BN;
+  const int K = P.K, N = P.N;
+  const uint16_t* __restrict__ Wg = P.W + (int64_t)g * P.w_stride;
+  const uint16_t* __restrict__ Abase = P.A;
+
+  // Instruction i of this wave fills stage rows RPI*q .. RPI*q+RPI-1 with
+  // q = wave + 4*i; lane L writes row RPI*q + L/CHUNKS, slot L%CHUNKS, which
+  // holds logical chunk pl_swz(row, slot) (the swizzle is an involution).
+  // Each instruction keeps a 32-bit element offset from a uniform base (A,
+  // or this group's weights; both well below 2^31 elements, the host checks).
+  uint32_t off[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int row = RPI * (wave + 4 * i) + lane / CHUNKS;
+    const int chunk = pl_swz<KB>(row, lane % CHUNKS);
+    if (i < A_INSTR) {
+      const int64_t gr = row0 + row < row_end ? row0 + row : row0;
+      const int64_t a_row = P.row_index ? (int64_t)P.row_index[gr] : gr;
+      off[i] = (uint32_t)(a_row * K + chunk * 8);
+    } else {
+      const int r = row - BM;
+      int n = GATEUP ? n0 + (r < BN ? r : r - BN) : n0 + r;
+      const bool up = GATEUP && r >= BN;
+      if (n >= N) n = n0;
+      off[i] = (uint32_t)((int64_t)(up ? N + n : n) * K + chunk * 8);
+    }
+  }
+  // K is a multiple of KB here (the host only picks this variant then), so
+  // every stage is whole and the loads need no predicate.
+  auto issue = [&](int slot, int k0) __attribute__((always_inline)) {
+    uint16_t* base = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      lds_direct_16((i < A_INSTR ? Abase : Wg) + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+  };
+
+  f32x16_t acc[NMAT][TM][TN];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
+
+  // MFMA fragments of one 16-wide K substep, two groups (substeps alternate)
+  bf16x8_t af[2][TM], bfr[2][NMAT][TN];
+  auto read_frags = [&](int slot, int ks, auto grp_c) __attribute__((always_inline)) {
+    constexpr int grp = decltype(grp_c)::value;
+    const uint16_t* As = smem + slot * STAGE;
+    const uint16_t* Bs = As + BM * KB;
+    const int chunk = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WM + i * 32 + (lane & 31);
+      af[grp][i] = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + pl_swz<KB>(r, chunk) * 8]);
+    }
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = m * BN + wn * WN + j * 32 + (lane & 31);
+        bfr[grp][m][j] = *reinterpret_cast<const bf16x8_t*>(&Bs[r * KB + pl_swz<KB>(r, chunk) * 8]);
+      }
+  };
+  auto mfmas = [&](auto grp_c) __attribute__((always_inline)) {
+    constexpr int grp = decltype(grp_c)::value;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[grp][i], bfr[grp][m][j],
+                                                                acc[m][i][j], 0, 0, 0);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  constexpr int NREAD = TM + NMAT * TN;  // fragment reads per substep
+  constexpr int NMFMA = TM * NMAT * TN;  // MFMAs per substep
+  const int nk = K / KB;
+  // Every step issues exactly one stage of loads (stages past the end
+  // re-fetch the last K step into a free slot), so "stage kt+1 landed" is
+  // always "at most STAGES-2 newer stages of this wave's loads in flight".
+  auto stage_k = [&](int s) __attribute__((always_inline)) { return min(s, nk - 1) * KB; };
+
+  // previous tile's stores out of the vmcnt queue; every wave done with LDS
+  PL_WAIT_VM(0);
+  __syncthreads();
+#pragma unroll
+  for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(s0, stage_k(s0));
+  PL_WAIT_VM_LDS((STAGES - 2) * PER_WAVE);
+  pl_barrier();
+  read_frags(0, 0, C0{});
+
+  int slot = 0;                // LDS slot of stage kt
+  int slot_prev = STAGES - 1;  // slot of stage kt-1 (= stage kt+STAGES-1)
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot_next = slot + 1 == STAGES ? 0 : slot + 1;
+#pragma unroll
+    for (int ks = 0; ks < SUB; ++ks) {
+      const bool even = (ks & 1) == 0;
+      if (ks == SUB - 1) {
+        // own loads of stage kt+1 landed and own LDS reads of stage kt done:
+        // after the barrier stage kt+1 is complete everywhere, and nobody
+        // reads the slot the next step's loads overwrite
+        PL_WAIT_VM_LDS((STAGES - 2) * PER_WAVE);
+        pl_barrier();
+      }
+      // MFMAs of substep ks; read the fragments of the next substep
+      if (even) mfmas(C0{}); else mfmas(C1{});
+      if (ks + 1 < SUB) {
+        if (even) read_frags(slot, ks + 1, C1{}); else read_frags(slot, ks + 1, C0{});
+      } else {
+        read_frags(slot_next, 0, C0{});
+      }
+      if (ks == 0) issue(slot_prev, stage_k(kt + STAGES - 1));
+      // interleave: groups of up to 4 MFMAs, each followed by its share of
+      // the fragment reads (and, in substep 0, of the stage loads)
+      constexpr int MF = NMFMA >= 4 ? 4 : NMFMA;
+      constexpr int GROUPS = NMFMA / MF;
+      constexpr int RD = (NREAD + GROUPS - 1) / GROUPS;
+      constexpr int VM = (PER_WAVE + GROUPS - 1) / GROUPS;
+#pragma unroll
+      for (int q = 0; q < GROUPS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+        if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
+      }
+    }
+    slot_prev = slot;
+    slot = slot_next;
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WN + j * 32 + (lane & 31);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= row_end) continue;
+        if (GATEUP) {
+          const float hv = swiglu_clamped(acc[0][i][j][r], acc[NMAT - 1][i][j][r], limit);
+          static_cast<uint16_t*>(P.out)[row * N + col] = (uint16_t)f32_to_bf16_bits(hv);
+        } else {
+          static_cast<float*>(P.out)[row * N + col] = acc[0][i][j][r];
+        }
+      }
+    }
+  }
+}
+
+template <int BM>
+__device__ __forceinline__ int pipe_mtiles(const GemmProblem& P) {
+  return P.group_offsets ? P.mtile_start[P.G] : (int)((P.M + BM - 1) / BM);
+}
+
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M>
+__global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(GemmProblem p0, GemmProblem p1,
+                                                              int has_p1, float limit) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+  const int mt0 = pipe_mtiles<BM>(p0);
+  const int mt1 = has_p1 ? pipe_mtiles<BM>(p1) : 0;
+  const int tiles0 = mt0 * p0.ntiles;
+  const int total = tiles0 + mt1 * p1.ntiles;
+  // equal contiguous tile ranges per XCD; this XCD's workgroups stride it
+  const int nwg = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, lid = b >> 3;
+  const int nwg_x = (nwg - xcd + 7) >> 3;
+  const int t_begin = (int)((int64_t)total * xcd / 8);
+  const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  for (int t = t_begin + lid; t < t_end; t += nwg_x) {
+    if (t < tiles0)
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true>(p0, mt0, t, limit, smem_dyn);
+    else
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true>(p1, mt1, t - tiles0, limit, smem_dyn);
+  }
+}
+
+// Non-persistent launch of the same tile body over the padded tile space
+// (host bound on m-tiles x n-tiles per problem, XCD-remapped so each XCD
+// takes a contiguous range): for short expert segments, where a few hundred
+// tiles each stream their weights once and the hardware's dispatch of new
+// workgroups as CUs free up balances the load.
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M>
+__global__ __launch_bounds__(256, 1) void grouped_pipe_grid_kernel(GemmProblem p0, GemmProblem p1,
+                                                                   int tiles0, float limit) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  if (t < tiles0)
+    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false>(p0, pipe_mtiles<BM>(p0), t, limit,
+                                                         smem_dyn);
+  else
+    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false>(p1, pipe_mtiles<BM>(p1), t - tiles0,
+                                                         limit, smem_dyn);
+}
+
+int device_cu_count() {
+  static int cached = 0;  // per process: one device model in a run
+  if (cached == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cached = n;
+    else
+      cached = 256;
+  }
+  return cached;
+}
+
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M = 2>
+hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
+                       hipStream_t stream) {
+  constexpr int NB = GATEUP ? 2 * BN : BN;
+  const size_t lds = (size_t)STAGES * (BM + NB) * KB * sizeof(uint16_t);
+  static_assert((size_t)STAGES * (BM + NB) * KB * 2 <= 160 * 1024, "LDS");
+  auto kern = grouped_pipe_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M>;
+  static bool attr_set = false;  // raise the dynamic LDS limit once per process
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const GemmProblem pb = b ? *b : a;
+  const int grid = device_cu_count();  // one resident workgroup per CU
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a, pb, b ? 1 : 0, limit);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M>
+hipError_t launch_pipe_grid(const GemmProblem& a, const GemmProblem* b, float limit,
+                            hipStream_t stream) {
+  constexpr int NB = GATEUP ? 2 * BN : BN;
+  const size_t lds = (size_t)STAGES * (BM + NB) * KB * sizeof(uint16_t);
+  static_assert((size_t)STAGES * (BM + NB) * KB * 2 <= 160 * 1024, "LDS");
+  auto kern = grouped_pipe_grid_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles0 = a.max_mtiles * a.ntiles;
+  const int total = tiles0 + (b ? b->max_mtiles * b->ntiles : 0);
+  if (total == 0) return hipSuccess;
+  const GemmProblem pb = b ? *b : a;
+  hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, stream, a, pb, tiles0, limit);
+  return hipGetLastError();
 }
 
 // m-tile prefix of up to two tile heights over one set of group offsets.
@@ -268,8 +781,23 @@ hipError_t launch_pair(const GemmProblem& a, const GemmProblem* b, float limit, 
 
 }  // namespace
 
-int gemm_tile_m(GemmVariant v) { return v == GemmVariant::kStream ? 32 : 128; }
-int gemm_tile_n(GemmVariant) { return 128; }
+int gemm_tile_m(GemmVariant v) {
+  switch (v) {
+    case GemmVariant::kStream: return ST_BM;
+    case GemmVariant::kTile32: return 32;
+    case GemmVariant::kTile128: return 128;
+    case GemmVariant::kPipe256: return 256;
+    case GemmVariant::kPipe256K64: return 256;
+    case GemmVariant::kStream32: return 32;
+  }
+  return 128;
+}
+int gemm_tile_n(GemmVariant v, bool gateup) {
+  if (v == GemmVariant::kStream) return gateup ? ST_WR / 2 : ST_WR;
+  if (v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64 || v == GemmVariant::kStream32)
+    return gateup ? 128 : 256;
+  return 128;
+}
 
 hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
                                 int32_t* start0, int32_t* start1, hipStream_t stream) {
@@ -280,6 +808,31 @@ hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, in
 
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                const GemmProblem* b, float limit, hipStream_t stream) {
-  if (v == GemmVariant::kStream) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
+  if (v == GemmVariant::kStream) {
+    const int tiles0 = a.max_mtiles * a.ntiles;
+    const int total = tiles0 + (b ? b->max_mtiles * b->ntiles : 0);
+    if (total == 0) return hipSuccess;
+    const GemmProblem pb = b ? *b : a;
+    if (gateup)
+      hipLaunchKernelGGL(grouped_stream_kernel<true>, dim3(total), dim3(256), 0, stream, a, pb,
+                         tiles0, limit);
+    else
+      hipLaunchKernelGGL(grouped_stream_kernel<false>, dim3(total), dim3(256), 0, stream, a, pb,
+                         tiles0, limit);
+    return hipGetLastError();
+  }
+  if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
+  if (v == GemmVariant::kPipe256) {  // K steps of 32, five stages
+    if (gateup) return launch_pipe<256, 128, true, 32, 5>(a, b, limit, stream);
+    return launch_pipe<256, 256, false, 32, 5>(a, b, limit, stream);
+  }
+  if (v == GemmVariant::kStream32) {  // 32-row tiles, K steps of 64, three stages
+    if (gateup) return launch_pipe_grid<32, 128, true, 64, 3, 1>(a, b, limit, stream);
+    return launch_pipe_grid<32, 256, false, 64, 3, 1>(a, b, limit, stream);
+  }
+  if (v == GemmVariant::kPipe256K64) {  // K steps of 64 (128-byte rows), two stages
+    if (gateup) return launch_pipe<256, 128, true, 64, 2>(a, b, limit, stream);
+    return launch_pipe<256, 256, false, 64, 2>(a, b, limit, stream);
+  }
   return launch_pair<128, 128, 2, 2>(a, b, limit, gateup, stream);
 }

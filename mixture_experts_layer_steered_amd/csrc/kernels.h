@@ -22,18 +22,24 @@ struct GemmProblem {
   int32_t G;                      // groups
   int32_t N;                      // output columns
   int32_t K;                      // reduction length
-  int32_t ntiles;                 // ceil(N / BN)
+  int32_t ntiles;                 // ceil(N / BN) (BN of the variant and projection)
   int32_t max_mtiles;             // host bound: ceil(M / BM) + G (or ceil(M / BM) for one group)
 };
 
-enum class GemmVariant { kStream, kTiled };
+// Tile variants of the grouped GEMM: LDS-staged 32-row tiles (short expert
+// segments), LDS-staged 128-row tiles, pipelined 256-row tiles with direct
+// global->LDS loads (long segments), and split-K weight streaming through
+// registers (kept for comparison; slower on gfx950).
+enum class GemmVariant { kTile32, kTile128, kPipe256, kPipe256K64, kStream32, kStream };
 int gemm_tile_m(GemmVariant v);
-int gemm_tile_n(GemmVariant v);
+int gemm_tile_n(GemmVariant v, bool gateup);
 
-hipError_t launch_router_logits(const uint16_t* x, const float* w, float* logits, int64_t T,
-                                int H, int E, hipStream_t stream);
-hipError_t launch_router_topk(const float* logits, const float* bias, int32_t* ids, float* wts,
-                              int64_t T, int E, int k, float rsf, hipStream_t stream);
+// K-slices of the router GEMM (partials are summed in slice order by the
+// top-k kernel); `partial` needs splits*T*E floats when splits > 1.
+int router_splits(int64_t T, int H, int E);
+hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, float* logits,
+                         float* partial, int32_t* ids, float* wts, int64_t T, int H, int E, int k,
+                         float rsf, hipStream_t stream);
 
 int permute_tiles(int64_t N);
 hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, int32_t* offsets,

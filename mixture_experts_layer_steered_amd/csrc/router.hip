@@ -28,6 +28,7 @@ constexpr int RT_BT = 64;       // tokens per workgroup tile
 constexpr int RT_BE = 64;       // experts per workgroup tile
 constexpr int RT_BK = 32;       // K per LDS stage
 constexpr int RT_LD = RT_BK + 8;  // padded LDS row (bf16 elements): 80 bytes
+constexpr int RT_MAX_SPLITS = 16; // K slices of the router GEMM at most
 
 __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   uint32_t u = __float_as_uint(w);
@@ -40,10 +41,12 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
   lo = __float_as_uint(r2) >> 16;             // exact in bf16
 }
 
-// logits[T, E] = fp32(x[T, H] @ w[E, H]^T).  Grid: (ceil(T/64), ceil(E/64)).
+// partial[s][T, E] = fp32(x[T, K_s] @ w[E, K_s]^T) over the s-th K slice of
+// k_slice columns.  Grid: (ceil(T/64), ceil(E/64), splits).  With one split
+// the partial is the logit itself.
 __global__ __launch_bounds__(256) void router_logits_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
-    int64_t T, int H, int E) {
+    const uint16_t* __restrict__ x, const float* __restrict__ w, float* __restrict__ partial,
+    int64_t T, int H, int E, int k_slice) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[RT_BT * RT_LD];
   __shared__ __attribute__((aligned(16))) uint16_t wsp[3][RT_BE * RT_LD];
 
@@ -61,9 +64,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   // x tile: 64 rows x 32 k = 256 chunks of 8 bf16, one per thread
   const int xr = tid >> 2, xc = (tid & 3) * 8;
   // w tile: 64 rows x 32 k = 512 float4, two per thread
-  for (int k0 = 0; k0 < H; k0 += RT_BK) {
+  const int k_begin = blockIdx.z * k_slice;
+  const int k_end = min(H, k_begin + k_slice);
+  float* __restrict__ logits = partial + (int64_t)blockIdx.z * T * E;
+  for (int k0 = k_begin; k0 < k_end; k0 += RT_BK) {
     uint4 xv = make_uint4(0, 0, 0, 0);
-    if (t0 + xr < T && k0 + xc < H)
+    if (t0 + xr < T && k0 + xc < k_end)
       xv = *reinterpret_cast<const uint4*>(x + (t0 + xr) * (int64_t)H + k0 + xc);
     float4 wv[2];
     int wr_[2], wc_[2];
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
       wr_[q] = idx >> 3;
       wc_[q] = (idx & 7) * 4;
       wv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + wr_[q] < E && k0 + wc_[q] < H)
+      if (e0 + wr_[q] < E && k0 + wc_[q] < k_end)
         wv[q] = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + wr_[q]) * H + k0 + wc_[q]);
     }
     __syncthreads();
@@ -131,38 +137,68 @@ __device__ __forceinline__ uint64_t select_key(float sb, int e) {
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
 }
 
-constexpr int TK_PER_LANE = MOE_MAX_EXPERTS_DEV / 64;
-
-// One wavefront per token.  Grid: ceil(T/4) workgroups of 256.
+// One wavefront per token.  Grid: ceil(T/4) workgroups of 256.  With
+// splits > 1 the logit is the sum of the K-slice partials in slice order
+// (fixed, so reruns repeat), written to `logits` for the caller.
+// TK_PER_LANE = ceil(E/64) experts per lane (a template, so the key arrays
+// stay in registers and no loop runs over absent experts).
+template <int TK_PER_LANE>
 __global__ __launch_bounds__(256) void router_topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ bias, int32_t* __restrict__ ids,
-    float* __restrict__ wts, int64_t T, int E, int k, float rsf) {
+    const float* __restrict__ partial, int splits, float* __restrict__ logits,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wts,
+    int64_t T, int E, int k, float rsf) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* lrow = logits + t * E;
+  const int64_t TE = T * E;
   uint64_t key[TK_PER_LANE];
+  float lg[TK_PER_LANE];
 #pragma unroll
   for (int i = 0; i < TK_PER_LANE; ++i) {
-    int e = lane + 64 * i;
+    const int e = lane + 64 * i;
     key[i] = 0;
+    lg[i] = 0.f;
     if (e < E) {
-      float s = sigmoid_f32(lrow[e]);
-      float b = bias ? bias[e] : 0.0f;
+      // slices four at a time (independent loads in flight), summed in
+      // slice order
+      float l = partial[t * E + e];
+      for (int sp0 = 1; sp0 < splits; sp0 += 4) {
+        float pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          pv[u] = sp0 + u < splits ? partial[(sp0 + u) * TE + t * E + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (sp0 + u < splits) l += pv[u];
+      }
+      if (splits > 1) logits[t * E + e] = l;
+      lg[i] = l;
+      const float s = sigmoid_f32(l);
+      const float b = bias ? bias[e] : 0.0f;
       key[i] = select_key(s + b, e);
     }
   }
-  int mine = -1;  // lane j < k ends up holding the j-th pick
+  int mine = -1;       // lane j < k ends up holding the j-th pick
+  float mine_l = 0.f;  // and its logit
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < TK_PER_LANE; ++i) best = key[i] > best ? key[i] : best;
     best = wave_max_u64(best);
     const int e = (int)(~(uint32_t)best);
+    float le = 0.f;
 #pragma unroll
-    for (int i = 0; i < TK_PER_LANE; ++i)
-      if (key[i] == best) key[i] = 0;  // taken: 0 is below every real key
-    if (lane == j) mine = e;
+    for (int i = 0; i < TK_PER_LANE; ++i) {
+      if (key[i] == best) {
+        key[i] = 0;  // taken: 0 is below every real key
+        le = lg[i];
+      }
+    }
+    le = __shfl(le, e & 63, 64);  // the owner lane of expert e holds its logit
+    if (lane == j) {
+      mine = e;
+      mine_l = le;
+    }
   }
   // ascending order: rank of each pick among the k picks
   int rank = 0;
@@ -172,23 +208,44 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
   if (lane < k) {
     ids[t * k + rank] = mine;
-    wts[t * k + rank] = rsf * sigmoid_f32(lrow[mine]);
+    wts[t * k + rank] = rsf * sigmoid_f32(mine_l);
   }
 }
 
 }  // namespace
 
-hipError_t launch_router_logits(const uint16_t* x, const float* w, float* logits, int64_t T,
-                                int H, int E, hipStream_t stream) {
-  dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((E + RT_BE - 1) / RT_BE));
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, w, logits, T, H, E);
-  return hipGetLastError();
+int router_splits(int64_t T, int H, int E) {
+  // enough workgroups to cover the chip (about two per CU), each slice a
+  // multiple of the 32-wide K step and at least 64 wide
+  const int64_t tiles = ((T + RT_BT - 1) / RT_BT) * ((E + RT_BE - 1) / RT_BE);
+  if (tiles == 0) return 1;
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t max_s = (H + 63) / 64;
+  if (s > max_s) s = max_s;
+  if (s > RT_MAX_SPLITS) s = RT_MAX_SPLITS;
+  return s < 1 ? 1 : (int)s;
 }
 
-hipError_t launch_router_topk(const float* logits, const float* bias, int32_t* ids, float* wts,
-                              int64_t T, int E, int k, float rsf, hipStream_t stream) {
-  dim3 grid((unsigned)((T + 3) / 4));
-  hipLaunchKernelGGL(router_topk_kernel, grid, dim3(256), 0, stream, logits, bias, ids, wts, T,
-                     E, k, rsf);
+hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, float* logits,
+                         float* partial, int32_t* ids, float* wts, int64_t T, int H, int E, int k,
+                         float rsf, hipStream_t stream) {
+  const int splits = router_splits(T, H, E);
+  int k_slice = (H + splits - 1) / splits;
+  k_slice = (k_slice + RT_BK - 1) / RT_BK * RT_BK;
+  float* part = splits > 1 ? partial : logits;
+  dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((E + RT_BE - 1) / RT_BE), splits);
+  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, w, part, T, H, E,
+                     k_slice);
+  const dim3 g((unsigned)((T + 3) / 4)), b(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(router_topk_kernel<1>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
+  else if (E <= 128)
+    hipLaunchKernelGGL(router_topk_kernel<2>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
+  else if (E <= 256)
+    hipLaunchKernelGGL(router_topk_kernel<4>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
+  else if (E <= 512)
+    hipLaunchKernelGGL(router_topk_kernel<8>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<16>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
   return hipGetLastError();
 }

@@ -49,6 +49,11 @@ SMALL = {
                             scmoe=True, gamma_jitter=0.1),
     # k at its bound, many experts
     "k16": Workload("k16", T=96, H=256, E=300, k=16, I=64, I_s=64, rsf=2.5),
+    # long expert segments (LDS-tiled GEMM variant), several m-tiles per expert
+    "prefill_small": Workload("prefill_small", T=520, H=256, E=8, k=2, I=200, I_s=136),
+    # long segments with H, I multiples of 32 (the pipelined tiles apply):
+    # ragged last m-tile, an N tail in gate_up (I = 160 < 2 x 128)
+    "pipe_small": Workload("pipe_small", T=600, H=256, E=4, k=2, I=160, I_s=96, rsf=1.3),
 }
 
 
@@ -147,3 +152,18 @@ def test_forward_zipf_full_sampled():
     rep = _full("zipf", 48)
     # the Zipf-scaled router leaves the expert load strongly skewed
     assert rep["max_over_mean_count"] > 4
+
+
+@pytest.mark.parametrize("variant", ["tile32", "tile128", "pipe256", "pipe256k64", "stream32",
+                                     "stream"])
+@pytest.mark.parametrize("name", ["medium_ragged", "decode_small", "scmoe_gamma", "prefill_small",
+                                  "pipe_small"])
+def test_forward_every_tile_variant(monkeypatch, variant, name):
+    """Each grouped-GEMM tile variant (forced through MOE_GEMM_VARIANT) gives
+    a parity-green layer; the automatic choice is only a speed decision."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT", variant)
+    wl = SMALL[name]
+    step = {"pipe256": 32, "pipe256k64": 64, "stream32": 64}.get(variant)
+    if step and (wl.H % step or wl.I % step or wl.I_s % step):
+        pytest.skip(f"the pipelined tiles step K in whole {step}-wide stages")
+    run_and_check(wl, moe_inputs.generate(wl, seed=1))
