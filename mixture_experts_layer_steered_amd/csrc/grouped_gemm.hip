@@ -674,6 +674,340 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_grid_kernel(GemmProblem p
                                                          limit, smem_dyn);
 }
 
+// ---------------------------------------------------------------------------
+// Persistent weight-streaming variant for short expert segments (decode).
+//
+// With a few rows per expert every weight byte feeds a few MACs, so the
+// projection runs at the rate HBM delivers weights.  HBM3E here gives its
+// best rate when each weight row is read in long contiguous pieces (about
+// 6.2 TB/s for 512-byte pieces, 5.2 TB/s for the 128-byte pieces of a
+// 64-wide K step), so a workgroup owns only 64 weight rows (gate_up: 32 gate
+// rows and the matching 32 up rows; down: 64 output columns) and reads KB*2
+// contiguous bytes of each per stage, STAGES-1 stages in flight, through
+// direct global->LDS loads (1 KB per instruction: RPI whole row pieces).
+// A tile holds up to 32 rows of A as two 16-row MFMA halves; the second is
+// skipped when the segment ends within the first.
+//
+// The four wavefronts split the K range of each stage into 32-wide substeps
+// of v_mfma_f32_16x16x32_bf16 and each keeps partial sums of the whole tile.
+// At the end of a tile the partials are added through LDS, always as
+// (w0 + w2) + (w1 + w3), so reruns repeat bit for bit, and wavefront 0
+// stores h or y.
+//
+// One workgroup per CU walks a share of its XCD's contiguous range of the
+// dense tile list and keeps its loads running across tile boundaries: the
+// first stages of the next tile are in flight while the current one is
+// reduced and stored.  The per-tile lookups (segment offsets, m-tile prefix,
+// gathered row ids) are uniform and go through the scalar cache, so they
+// never wait behind the stage loads.  Inside an expert the m-tiles of one
+// weight tile are adjacent: when a segment spans several m-tiles, the
+// repeated weight reads are served by L2.
+constexpr int WS_BM = 32;  // A rows per tile
+constexpr int WS_NB = 64;  // weight rows per tile
+
+__device__ __forceinline__ int ws_swz(int row, int chunk) {
+  // rows are a multiple of 256 bytes long: the 16 rows one ds_read_b128 pass
+  // touches must sit in 16 different 16-byte bank groups
+  return chunk ^ (row & 15);
+}
+
+// Uniform load through the scalar data cache (waited on with lgkmcnt).
+__device__ __forceinline__ int32_t ws_sload(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// One problem's fields, selected between the two problems of the launch.
+struct WsProb {
+  const uint16_t* A;
+  const int32_t* row_index;
+  const int32_t* offs;
+  const int32_t* mstart;
+  const uint16_t* W;
+  int64_t w_stride;
+  void* out;
+  int64_t M;
+  int G, N, K, ntiles, mt_total;
+};
+
+__device__ __forceinline__ WsProb ws_pick(const GemmProblem& a, const GemmProblem& b, bool second,
+                                          int mt_a, int mt_b) {
+  WsProb q;
+  q.A = second ? b.A : a.A;
+  q.row_index = second ? b.row_index : a.row_index;
+  q.offs = second ? b.group_offsets : a.group_offsets;
+  q.mstart = second ? b.mtile_start : a.mtile_start;
+  q.W = second ? b.W : a.W;
+  q.w_stride = second ? b.w_stride : a.w_stride;
+  q.out = second ? b.out : a.out;
+  q.M = second ? b.M : a.M;
+  q.G = second ? b.G : a.G;
+  q.N = second ? b.N : a.N;
+  q.K = second ? b.K : a.K;
+  q.ntiles = second ? b.ntiles : a.ntiles;
+  q.mt_total = second ? mt_b : mt_a;
+  return q;
+}
+
+// Dense tile t of a problem -> rows [row0, row_end) of group g, columns from
+// n0.  Within a group the m-tiles of one n-tile are adjacent.
+template <int BN>
+__device__ __forceinline__ void ws_locate(const WsProb& P, int t, int64_t& row0, int64_t& row_end,
+                                          int& n0, int& g) {
+  if (P.offs == nullptr) {
+    const int nt = t / P.mt_total, mt = t - nt * P.mt_total;
+    g = 0;
+    row0 = (int64_t)mt * WS_BM;
+    row_end = P.M;
+    n0 = nt * BN;
+    return;
+  }
+  int lo = 0, hi = P.G - 1;  // last g with mstart[g] * ntiles <= t (its m-tile count is > 0)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ws_sload(P.mstart, mid) * P.ntiles <= t) lo = mid; else hi = mid - 1;
+  }
+  g = lo;
+  const int m_first = ws_sload(P.mstart, g);
+  const int mcount = ws_sload(P.mstart, g + 1) - m_first;
+  const int local = t - m_first * P.ntiles;
+  const int nt = local / mcount, mt = local - nt * mcount;
+  row0 = ws_sload(P.offs, g) + (int64_t)mt * WS_BM;
+  row_end = ws_sload(P.offs, g + 1);
+  n0 = nt * BN;
+}
+
+template <bool GATEUP, int KB, int STAGES>
+__global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0, GemmProblem p1,
+                                                                 int has_p1, float limit) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+  constexpr int BM = WS_BM, NB = WS_NB;
+  constexpr int BN = GATEUP ? NB / 2 : NB;  // output columns per tile
+  constexpr int ROWS = BM + NB;             // LDS rows per stage
+  constexpr int CHUNKS = KB / 8;            // 16-byte chunks per row piece
+  constexpr int STAGE = ROWS * KB;          // bf16 elements per stage
+  constexpr int RPI = 64 / CHUNKS;          // row pieces per 1 KB load instruction
+  constexpr int INSTR = ROWS / RPI;
+  constexpr int PER_WAVE = INSTR / 4;
+  constexpr int A_INSTR = BM / (4 * RPI);   // instructions of each wave that fill A rows
+  constexpr int SUB_W = KB / 128;           // 32-wide substeps per wave per stage
+  constexpr int NT = NB / 16;               // 16-column MFMA tiles
+  static_assert(INSTR % 4 == 0 && BM % (4 * RPI) == 0 && SUB_W >= 1, "shape");
+  static_assert((STAGES - 2) * PER_WAVE <= 63, "vmcnt range");
+  float* red = reinterpret_cast<float*>(smem_dyn + STAGES * STAGE);  // [2][2][NT][4][64]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int mt0 = pipe_mtiles<BM>(p0);
+  const int mt1 = has_p1 ? pipe_mtiles<BM>(p1) : 0;
+  const int tiles0 = mt0 * p0.ntiles;
+  const int total = tiles0 + mt1 * p1.ntiles;
+  const int nwg = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, lid = b >> 3;
+  const int nwg_x = (nwg - xcd + 7) >> 3;
+  const int t_begin = (int)((int64_t)total * xcd / 8);
+  const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  if (t_begin + lid >= t_end) return;
+
+  // ---- load cursor: tile t_ld, K stage kt_ld, LDS slot slot_ld
+  int t_ld = t_begin + lid, kt_ld = 0, slot_ld = 0, nk_ld = 1;
+  const uint16_t* ld_A = nullptr;
+  const uint16_t* ld_W = nullptr;
+  uint32_t off[PER_WAVE];
+  auto setup_ld = [&]() __attribute__((always_inline)) {
+    const bool sec = t_ld >= tiles0;
+    const WsProb P = ws_pick(p0, p1, sec, mt0, mt1);
+    int64_t row0, row_end;
+    int n0, g;
+    ws_locate<BN>(P, sec ? t_ld - tiles0 : t_ld, row0, row_end, n0, g);
+    ld_A = P.A;
+    ld_W = P.W + (int64_t)g * P.w_stride;
+    nk_ld = P.K / KB;
+    // instruction i of this wave fills stage rows RPI*q .. RPI*q+RPI-1,
+    // q = wave + 4i; lane L writes row RPI*q + L/CHUNKS, slot L%CHUNKS, which
+    // holds logical chunk ws_swz(row, slot); A rows past the segment and
+    // weight rows past N fetch the tile's first row (their products reach
+    // only outputs that are never stored)
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int chunk = ws_swz(RPI * (wave + 4 * i) + lane / CHUNKS, lane % CHUNKS);
+      if (i < A_INSTR) {
+        int64_t src[RPI];
+#pragma unroll
+        for (int j = 0; j < RPI; ++j) {
+          const int64_t gr = row0 + RPI * (wave + 4 * i) + j;
+          const int64_t r = gr < row_end ? gr : row0;
+          src[j] = P.row_index ? (int64_t)ws_sload(P.row_index, r) : r;
+        }
+        int64_t mine = src[0];
+#pragma unroll
+        for (int j = 1; j < RPI; ++j)
+          if (lane / CHUNKS == j) mine = src[j];
+        off[i] = (uint32_t)(mine * P.K + chunk * 8);
+      } else {
+        const int r = RPI * (wave + 4 * i) + lane / CHUNKS - BM;
+        int n = GATEUP ? n0 + (r < BN ? r : r - BN) : n0 + r;
+        const bool up = GATEUP && r >= BN;
+        if (n >= P.N) n = n0;
+        off[i] = (uint32_t)((int64_t)(up ? P.N + n : n) * P.K + chunk * 8);
+      }
+    }
+  };
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if (t_ld >= t_end) return;
+    uint16_t* base = smem_dyn + slot_ld * STAGE;
+    const int k0 = kt_ld * KB;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      lds_direct_16((i < A_INSTR ? ld_A : ld_W) + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+    slot_ld = slot_ld + 1 == STAGES ? 0 : slot_ld + 1;
+    if (++kt_ld == nk_ld) {
+      kt_ld = 0;
+      t_ld += nwg_x;
+      if (t_ld < t_end) setup_ld();
+    }
+  };
+
+  // ---- compute cursor
+  int t_cp = t_begin + lid, kt_cp = 0, slot_cp = 0, nk_cp = 1, N_cp = 0;
+  int64_t row0_cp = 0, row_end_cp = 0;
+  int n0_cp = 0;
+  void* out_cp = nullptr;
+  bool second = false;
+  auto setup_cp = [&]() __attribute__((always_inline)) {
+    const bool sec = t_cp >= tiles0;
+    const WsProb P = ws_pick(p0, p1, sec, mt0, mt1);
+    int g;
+    ws_locate<BN>(P, sec ? t_cp - tiles0 : t_cp, row0_cp, row_end_cp, n0_cp, g);
+    nk_cp = P.K / KB;
+    N_cp = P.N;
+    out_cp = P.out;
+    second = row_end_cp - row0_cp > 16;
+  };
+
+  f32x4_t acc[2][NT];
+  auto zero = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[h][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // partial sums of waves 2, 3 are added by waves 0, 1, then wave 1's by
+  // wave 0, which stores the tile
+  auto reduce_store = [&]() __attribute__((always_inline)) {
+    auto slot_of = [&](int w, int h, int t, int r) { return (((w * 2 + h) * NT + t) * 4 + r) * 64 + lane; };
+    const int halves = second ? 2 : 1;
+    if (wave >= 2) {
+      for (int h = 0; h < halves; ++h)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[slot_of(wave - 2, h, t, r)] = acc[h][t][r];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    pl_barrier();
+    if (wave < 2) {
+      for (int h = 0; h < halves; ++h)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[h][t][r] += red[slot_of(wave, h, t, r)];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    pl_barrier();
+    if (wave == 1) {
+      for (int h = 0; h < halves; ++h)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[slot_of(0, h, t, r)] = acc[h][t][r];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    pl_barrier();
+    if (wave == 0) {
+      // element (reg r, lane l) of MFMA tile (h, t): row 16h + 4(l/16) + r,
+      // weight row 16t + l%16
+      for (int h = 0; h < halves; ++h) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[h][t][r] += red[slot_of(0, h, t, r)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = row0_cp + 16 * h + 4 * (lane >> 4) + r;
+          if (row >= row_end_cp) continue;
+          if (GATEUP) {
+#pragma unroll
+            for (int t = 0; t < NT / 2; ++t) {
+              const int col = n0_cp + 16 * t + (lane & 15);
+              if (col < N_cp)
+                static_cast<uint16_t*>(out_cp)[row * N_cp + col] = (uint16_t)f32_to_bf16_bits(
+                    swiglu_clamped(acc[h][t][r], acc[h][t + NT / 2][r], limit));
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const int col = n0_cp + 16 * t + (lane & 15);
+              if (col < N_cp) static_cast<float*>(out_cp)[row * N_cp + col] = acc[h][t][r];
+            }
+          }
+        }
+      }
+    }
+  };
+
+  setup_ld();
+  setup_cp();
+  zero();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue_next();
+
+  while (true) {
+    // own loads of this stage landed (at most STAGES-2 newer stages in
+    // flight while the loader still has work), own LDS reads done; after
+    // the barrier the stage is complete everywhere and the slot the next
+    // loads overwrite (read in the previous step) is free
+    if (t_ld < t_end)
+      PL_WAIT_VM_LDS((STAGES - 2) * PER_WAVE);
+    else
+      PL_WAIT_VM_LDS(0);
+    pl_barrier();
+    issue_next();
+    const uint16_t* As = smem_dyn + slot_cp * STAGE;
+    const uint16_t* Bs = As + BM * KB;
+#pragma unroll
+    for (int sw = 0; sw < SUB_W; ++sw) {
+      const int chunk = (wave * SUB_W + sw) * 4 + (lane >> 4);
+      const int r = lane & 15;
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + ws_swz(r, chunk) * 8]);
+      bf16x8_t bf[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        bf[t] = *reinterpret_cast<const bf16x8_t*>(&Bs[(16 * t + r) * KB + ws_swz(BM + 16 * t + r, chunk) * 8]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bf[t], acc[0][t], 0, 0, 0);
+      if (second) {
+        const bf16x8_t a1 =
+            *reinterpret_cast<const bf16x8_t*>(&As[(16 + r) * KB + ws_swz(16 + r, chunk) * 8]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bf[t], acc[1][t], 0, 0, 0);
+      }
+    }
+    slot_cp = slot_cp + 1 == STAGES ? 0 : slot_cp + 1;
+    if (++kt_cp == nk_cp) {
+      reduce_store();
+      t_cp += nwg_x;
+      if (t_cp >= t_end) break;
+      kt_cp = 0;
+      setup_cp();
+      zero();
+    }
+  }
+}
+
 int device_cu_count() {
   static int cached = 0;  // per process: one device model in a run
   if (cached == 0) {
@@ -726,6 +1060,27 @@ hipError_t launch_pipe_grid(const GemmProblem& a, const GemmProblem* b, float li
   if (total == 0) return hipSuccess;
   const GemmProblem pb = b ? *b : a;
   hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, stream, a, pb, tiles0, limit);
+  return hipGetLastError();
+}
+
+template <bool GATEUP, int KB, int STAGES>
+hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limit,
+                          hipStream_t stream) {
+  const size_t lds = (size_t)STAGES * (WS_BM + WS_NB) * KB * sizeof(uint16_t) +
+                     (size_t)2 * 2 * (WS_NB / 16) * 4 * 64 * sizeof(float);
+  static_assert((size_t)STAGES * (WS_BM + WS_NB) * KB * 2 + 2 * 2 * (WS_NB / 16) * 4 * 64 * 4 <=
+                    160 * 1024, "LDS");
+  auto kern = grouped_wstream_kernel<GATEUP, KB, STAGES>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const GemmProblem pb = b ? *b : a;
+  hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3(256), lds, stream, a, pb, b ? 1 : 0,
+                     limit);
   return hipGetLastError();
 }
 
@@ -789,11 +1144,13 @@ int gemm_tile_m(GemmVariant v) {
     case GemmVariant::kPipe256: return 256;
     case GemmVariant::kPipe256K64: return 256;
     case GemmVariant::kStream32: return 32;
+    case GemmVariant::kWStream: return WS_BM;
   }
   return 128;
 }
 int gemm_tile_n(GemmVariant v, bool gateup) {
   if (v == GemmVariant::kStream) return gateup ? ST_WR / 2 : ST_WR;
+  if (v == GemmVariant::kWStream) return gateup ? WS_NB / 2 : WS_NB;
   if (v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64 || v == GemmVariant::kStream32)
     return gateup ? 128 : 256;
   return 128;
@@ -822,6 +1179,14 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
     return hipGetLastError();
   }
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
+  if (v == GemmVariant::kWStream) {  // 512-byte row pieces when every K allows, else 256
+    const bool k256 = a.K % 256 == 0 && (!b || b->K % 256 == 0);
+    if (gateup)
+      return k256 ? launch_wstream<true, 256, 3>(a, b, limit, stream)
+                  : launch_wstream<true, 128, 6>(a, b, limit, stream);
+    return k256 ? launch_wstream<false, 256, 3>(a, b, limit, stream)
+                : launch_wstream<false, 128, 6>(a, b, limit, stream);
+  }
   if (v == GemmVariant::kPipe256) {  // K steps of 32, five stages
     if (gateup) return launch_pipe<256, 128, true, 32, 5>(a, b, limit, stream);
     return launch_pipe<256, 256, false, 32, 5>(a, b, limit, stream);

@@ -26,11 +26,11 @@ struct GemmProblem {
   int32_t max_mtiles;             // host bound: ceil(M / BM) + G (or ceil(M / BM) for one group)
 };
 
-// Tile variants of the grouped GEMM: LDS-staged 32-row tiles (short expert
-// segments), LDS-staged 128-row tiles, pipelined 256-row tiles with direct
-// global->LDS loads (long segments), and split-K weight streaming through
-// registers (kept for comparison; slower on gfx950).
-enum class GemmVariant { kTile32, kTile128, kPipe256, kPipe256K64, kStream32, kStream };
+// Tile variants of the grouped GEMM: persistent weight streaming in long
+// row pieces (short expert segments; K a multiple of 128), LDS-staged 32-row
+// and 128-row tiles, pipelined 256-row tiles with direct global->LDS loads
+// (long segments), and two earlier streaming forms kept for comparison.
+enum class GemmVariant { kTile32, kTile128, kPipe256, kPipe256K64, kStream32, kStream, kWStream };
 int gemm_tile_m(GemmVariant v);
 int gemm_tile_n(GemmVariant v, bool gateup);
 
