@@ -114,13 +114,14 @@ GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
 }
 
 // The pipelined and streaming variants address A rows and one group's
-// weights with 32-bit element offsets and step K in whole stages (32, 64 or
-// 128 wide); other operands fall back to the LDS-staged tiles.
+// weights with 32-bit element offsets and step K in 32-wide units (the
+// pipelined ones in whole 32- or 64-wide stages); other operands fall back
+// to the LDS-staged tiles.
 GemmVariant pick_variant(int64_t rows, int64_t groups, int64_t a_elems, int64_t w_group_elems,
-                         bool k_multiple_of_32, bool k_multiple_of_64, bool k_multiple_of_128) {
+                         bool k_multiple_of_32, bool k_multiple_of_64) {
   GemmVariant v = pick_variant_raw(rows, groups);
   const int64_t lim = (int64_t)1 << 31;
-  if (v == GemmVariant::kWStream && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_128))
+  if (v == GemmVariant::kWStream && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32))
     v = GemmVariant::kTile32;
   const bool pipe = v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64;
   if (pipe && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32)) v = GemmVariant::kTile128;
@@ -341,8 +342,7 @@ moe_status moe_grouped_swiglu_gemm(int32_t n_groups, int64_t M_total, int32_t H,
   // gathered rows can repeat, the routed case), the down A is h [M_total, I].
   const GemmVariant v =
       pick_variant(M_total, n_groups, std::max<int64_t>(M_total, 1) * std::max(H, I),
-                   (int64_t)2 * I * H, H % 32 == 0 && I % 32 == 0, H % 64 == 0 && I % 64 == 0,
-                   H % 128 == 0 && I % 128 == 0);
+                   (int64_t)2 * I * H, H % 32 == 0 && I % 32 == 0, H % 64 == 0 && I % 64 == 0);
   int32_t* mstart = static_cast<int32_t*>(ws);
   GemmProblem gu = make_problem(a, row_index, group_offsets, mstart, w_gate_up,
                                 (int64_t)2 * I * H, h, M_total, n_groups, I, H, v, true);
@@ -431,8 +431,7 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
       N, p->E, std::max<int64_t>(N, T) * std::max(p->H, std::max(p->I, p->I_shared)),
       (int64_t)2 * std::max(p->I, p->I_shared) * p->H,
       p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0,
-      p->H % 64 == 0 && p->I % 64 == 0 && p->I_shared % 64 == 0,
-      p->H % 128 == 0 && p->I % 128 == 0 && p->I_shared % 128 == 0);
+      p->H % 64 == 0 && p->I % 64 == 0 && p->I_shared % 64 == 0);
   const uint16_t* xr = x_routed;
   const uint16_t* xs = x_shared ? x_shared : x_routed;
   const bool shared = p->I_shared > 0;

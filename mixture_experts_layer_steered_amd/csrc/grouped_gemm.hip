@@ -681,29 +681,29 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_grid_kernel(GemmProblem p
 // projection runs at the rate HBM delivers weights.  HBM3E here gives its
 // best rate when each weight row is read in long contiguous pieces (about
 // 6.2 TB/s for 512-byte pieces, 5.2 TB/s for the 128-byte pieces of a
-// 64-wide K step), so a workgroup owns only 64 weight rows (gate_up: 32 gate
-// rows and the matching 32 up rows; down: 64 output columns) and reads KB*2
-// contiguous bytes of each per stage, STAGES-1 stages in flight, through
-// direct global->LDS loads (1 KB per instruction: RPI whole row pieces).
-// A tile holds up to 32 rows of A as two 16-row MFMA halves; the second is
-// skipped when the segment ends within the first.
+// 64-wide K step), so a workgroup owns only 64 weight rows and reads KB*2
+// contiguous bytes of each per stage through direct global->LDS loads (1 KB
+// per instruction: RPI whole row pieces), STAGES-1 stages in flight.  K needs
+// only be a multiple of 32: in a last, partial stage the lanes past K fetch
+// the stage's last valid chunk again and the 32-wide substeps past K are
+// skipped.
 //
-// The four wavefronts split the K range of each stage into 32-wide substeps
-// of v_mfma_f32_16x16x32_bf16 and each keeps partial sums of the whole tile.
-// At the end of a tile the partials are added through LDS, always as
-// (w0 + w2) + (w1 + w3), so reruns repeat bit for bit, and wavefront 0
-// stores h or y.
+// A tile is 16 rows of A (one v_mfma_f32_16x16x32_bf16 row block) by the 64
+// weight rows; wavefront w owns weight rows 16w .. 16w+15 and runs every K
+// substep for them, so no partial sums cross wavefronts.  In gate_up those
+// 16 rows are 8 gate rows and the matching 8 up rows: MFMA columns j and
+// j+8 of a lane group hold g and u of one output column, which meet through
+// a lane shuffle for the clamped SwiGLU.  Down: 16 output columns per wave.
 //
 // One workgroup per CU walks a share of its XCD's contiguous range of the
 // dense tile list and keeps its loads running across tile boundaries: the
 // first stages of the next tile are in flight while the current one is
-// reduced and stored.  The per-tile lookups (segment offsets, m-tile prefix,
-// gathered row ids) are uniform and go through the scalar cache, so they
-// never wait behind the stage loads.  Inside an expert the m-tiles of one
-// weight tile are adjacent: when a segment spans several m-tiles, the
-// repeated weight reads are served by L2.
-constexpr int WS_BM = 32;  // A rows per tile
-constexpr int WS_NB = 64;  // weight rows per tile
+// stored.  Per-tile lookups (segment offsets, m-tile prefix, gathered row
+// ids) are uniform and go through the scalar cache.  Inside an expert the
+// m-tiles of one weight tile are adjacent, so when a segment spans several
+// m-tiles the repeated weight reads are served by L2.
+constexpr int WS_BM = 16;  // A rows per tile
+constexpr int WS_NB = 64;  // weight rows per tile (16 per wavefront)
 
 __device__ __forceinline__ int ws_swz(int row, int chunk) {
   // rows are a multiple of 256 bytes long: the 16 rows one ds_read_b128 pass
@@ -749,7 +749,10 @@ __device__ __forceinline__ WsProb ws_pick(const GemmProblem& a, const GemmProble
 }
 
 // Dense tile t of a problem -> rows [row0, row_end) of group g, columns from
-// n0.  Within a group the m-tiles of one n-tile are adjacent.
+// n0.  Within a group the m-tiles of one n-tile are adjacent.  g comes in as
+// the group of an earlier tile of the same problem (a workgroup's tiles only
+// move forward, usually within the same group: a short forward scan), or
+// negative (binary search).
 template <int BN>
 __device__ __forceinline__ void ws_locate(const WsProb& P, int t, int64_t& row0, int64_t& row_end,
                                           int& n0, int& g) {
@@ -761,12 +764,17 @@ __device__ __forceinline__ void ws_locate(const WsProb& P, int t, int64_t& row0,
     n0 = nt * BN;
     return;
   }
-  int lo = 0, hi = P.G - 1;  // last g with mstart[g] * ntiles <= t (its m-tile count is > 0)
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ws_sload(P.mstart, mid) * P.ntiles <= t) lo = mid; else hi = mid - 1;
+  // g = last group with mstart[g] * ntiles <= t (its m-tile count is > 0)
+  if (g < 0) {
+    int lo = 0, hi = P.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ws_sload(P.mstart, mid) * P.ntiles <= t) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+  } else {
+    while (g + 1 < P.G && ws_sload(P.mstart, g + 1) * P.ntiles <= t) ++g;
   }
-  g = lo;
   const int m_first = ws_sload(P.mstart, g);
   const int mcount = ws_sload(P.mstart, g + 1) - m_first;
   const int local = t - m_first * P.ntiles;
@@ -789,11 +797,9 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
   constexpr int INSTR = ROWS / RPI;
   constexpr int PER_WAVE = INSTR / 4;
   constexpr int A_INSTR = BM / (4 * RPI);   // instructions of each wave that fill A rows
-  constexpr int SUB_W = KB / 128;           // 32-wide substeps per wave per stage
-  constexpr int NT = NB / 16;               // 16-column MFMA tiles
-  static_assert(INSTR % 4 == 0 && BM % (4 * RPI) == 0 && SUB_W >= 1, "shape");
+  constexpr int SUB = KB / 32;              // 32-wide K substeps per stage
+  static_assert(INSTR % 4 == 0 && BM % (4 * RPI) == 0 && CHUNKS >= 16, "shape");
   static_assert((STAGES - 2) * PER_WAVE <= 63, "vmcnt range");
-  float* red = reinterpret_cast<float*>(smem_dyn + STAGES * STAGE);  // [2][2][NT][4][64]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -802,27 +808,40 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
   const int mt1 = has_p1 ? pipe_mtiles<BM>(p1) : 0;
   const int tiles0 = mt0 * p0.ntiles;
   const int total = tiles0 + mt1 * p1.ntiles;
+  // each XCD takes a contiguous tile range of equal cost (K stages: the two
+  // problems' K may differ), which its workgroups stride
+  const int nk0 = (p0.K + KB - 1) / KB, nk1 = (p1.K + KB - 1) / KB;
+  const int64_t c0 = (int64_t)tiles0 * nk0;
+  const int64_t ctot = c0 + (int64_t)(total - tiles0) * nk1;
+  auto first_tile_from = [&](int64_t c) {  // first tile starting at cost >= c
+    return c <= c0 ? (int)((c + nk0 - 1) / nk0) : tiles0 + (int)((c - c0 + nk1 - 1) / nk1);
+  };
   const int nwg = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, lid = b >> 3;
   const int nwg_x = (nwg - xcd + 7) >> 3;
-  const int t_begin = (int)((int64_t)total * xcd / 8);
-  const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  const int t_begin = first_tile_from(ctot * xcd / 8);
+  const int t_end = first_tile_from(ctot * (xcd + 1) / 8);
   if (t_begin + lid >= t_end) return;
 
   // ---- load cursor: tile t_ld, K stage kt_ld, LDS slot slot_ld
-  int t_ld = t_begin + lid, kt_ld = 0, slot_ld = 0, nk_ld = 1;
+  int t_ld = t_begin + lid, kt_ld = 0, slot_ld = 0, nk_ld = 1, K_ld = 0;
   const uint16_t* ld_A = nullptr;
   const uint16_t* ld_W = nullptr;
   uint32_t off[PER_WAVE];
+  int g_ld = -1;
+  bool sec_ld = false;
   auto setup_ld = [&]() __attribute__((always_inline)) {
     const bool sec = t_ld >= tiles0;
+    if (sec != sec_ld) g_ld = -1;
+    sec_ld = sec;
     const WsProb P = ws_pick(p0, p1, sec, mt0, mt1);
     int64_t row0, row_end;
-    int n0, g;
-    ws_locate<BN>(P, sec ? t_ld - tiles0 : t_ld, row0, row_end, n0, g);
+    int n0;
+    ws_locate<BN>(P, sec ? t_ld - tiles0 : t_ld, row0, row_end, n0, g_ld);
     ld_A = P.A;
-    ld_W = P.W + (int64_t)g * P.w_stride;
-    nk_ld = P.K / KB;
+    ld_W = P.W + (int64_t)g_ld * P.w_stride;
+    nk_ld = (P.K + KB - 1) / KB;
+    K_ld = P.K;
     // instruction i of this wave fills stage rows RPI*q .. RPI*q+RPI-1,
     // q = wave + 4i; lane L writes row RPI*q + L/CHUNKS, slot L%CHUNKS, which
     // holds logical chunk ws_swz(row, slot); A rows past the segment and
@@ -845,9 +864,11 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
           if (lane / CHUNKS == j) mine = src[j];
         off[i] = (uint32_t)(mine * P.K + chunk * 8);
       } else {
+        // weight row r of the tile: wave r/16's block; in gate_up its first 8
+        // rows are gate rows and the next 8 the matching up rows
         const int r = RPI * (wave + 4 * i) + lane / CHUNKS - BM;
-        int n = GATEUP ? n0 + (r < BN ? r : r - BN) : n0 + r;
-        const bool up = GATEUP && r >= BN;
+        int n = GATEUP ? n0 + 8 * (r >> 4) + (r & 7) : n0 + r;
+        const bool up = GATEUP && (r & 8);
         if (n >= P.N) n = n0;
         off[i] = (uint32_t)((int64_t)(up ? P.N + n : n) * P.K + chunk * 8);
       }
@@ -857,9 +878,21 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
     if (t_ld >= t_end) return;
     uint16_t* base = smem_dyn + slot_ld * STAGE;
     const int k0 = kt_ld * KB;
+    if (k0 + KB <= K_ld) {
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      lds_direct_16((i < A_INSTR ? ld_A : ld_W) + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+      for (int i = 0; i < PER_WAVE; ++i)
+        lds_direct_16((i < A_INSTR ? ld_A : ld_W) + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+    } else {
+      // partial stage: lanes past K fetch the stage's last valid chunk of
+      // their row again (same cache line as a valid lane; never read)
+      const int last = ((K_ld - k0) >> 3) - 1;
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int chunk = ws_swz(RPI * (wave + 4 * i) + lane / CHUNKS, lane % CHUNKS);
+        const uint32_t o = off[i] + k0 - (uint32_t)(chunk > last ? chunk - last : 0) * 8;
+        lds_direct_16((i < A_INSTR ? ld_A : ld_W) + o, base + (wave + 4 * i) * RPI * KB);
+      }
+    }
     slot_ld = slot_ld + 1 == STAGES ? 0 : slot_ld + 1;
     if (++kt_ld == nk_ld) {
       kt_ld = 0;
@@ -869,97 +902,54 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
   };
 
   // ---- compute cursor
-  int t_cp = t_begin + lid, kt_cp = 0, slot_cp = 0, nk_cp = 1, N_cp = 0;
+  int t_cp = t_begin + lid, kt_cp = 0, slot_cp = 0, nk_cp = 1, N_cp = 0, K_cp = 0;
   int64_t row0_cp = 0, row_end_cp = 0;
   int n0_cp = 0;
   void* out_cp = nullptr;
-  bool second = false;
+  int g_cp = -1;
+  bool sec_cp = false;
   auto setup_cp = [&]() __attribute__((always_inline)) {
     const bool sec = t_cp >= tiles0;
+    if (sec != sec_cp) g_cp = -1;
+    sec_cp = sec;
     const WsProb P = ws_pick(p0, p1, sec, mt0, mt1);
-    int g;
-    ws_locate<BN>(P, sec ? t_cp - tiles0 : t_cp, row0_cp, row_end_cp, n0_cp, g);
-    nk_cp = P.K / KB;
+    ws_locate<BN>(P, sec ? t_cp - tiles0 : t_cp, row0_cp, row_end_cp, n0_cp, g_cp);
+    nk_cp = (P.K + KB - 1) / KB;
+    K_cp = P.K;
     N_cp = P.N;
     out_cp = P.out;
-    second = row_end_cp - row0_cp > 16;
   };
 
-  f32x4_t acc[2][NT];
-  auto zero = [&]() __attribute__((always_inline)) {
+  // element (reg r, lane l) of the wave's accumulator: row 4(l/16) + r of
+  // the tile, weight row 16*wave + l%16
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15;       // fragment row (A) / weight row within the wave's block
+  auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[h][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
-
-  // partial sums of waves 2, 3 are added by waves 0, 1, then wave 1's by
-  // wave 0, which stores the tile
-  auto reduce_store = [&]() __attribute__((always_inline)) {
-    auto slot_of = [&](int w, int h, int t, int r) { return (((w * 2 + h) * NT + t) * 4 + r) * 64 + lane; };
-    const int halves = second ? 2 : 1;
-    if (wave >= 2) {
-      for (int h = 0; h < halves; ++h)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) red[slot_of(wave - 2, h, t, r)] = acc[h][t][r];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    pl_barrier();
-    if (wave < 2) {
-      for (int h = 0; h < halves; ++h)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[h][t][r] += red[slot_of(wave, h, t, r)];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    pl_barrier();
-    if (wave == 1) {
-      for (int h = 0; h < halves; ++h)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) red[slot_of(0, h, t, r)] = acc[h][t][r];
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    pl_barrier();
-    if (wave == 0) {
-      // element (reg r, lane l) of MFMA tile (h, t): row 16h + 4(l/16) + r,
-      // weight row 16t + l%16
-      for (int h = 0; h < halves; ++h) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[h][t][r] += red[slot_of(0, h, t, r)];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = row0_cp + 16 * h + 4 * (lane >> 4) + r;
-          if (row >= row_end_cp) continue;
-          if (GATEUP) {
-#pragma unroll
-            for (int t = 0; t < NT / 2; ++t) {
-              const int col = n0_cp + 16 * t + (lane & 15);
-              if (col < N_cp)
-                static_cast<uint16_t*>(out_cp)[row * N_cp + col] = (uint16_t)f32_to_bf16_bits(
-                    swiglu_clamped(acc[h][t][r], acc[h][t + NT / 2][r], limit));
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              const int col = n0_cp + 16 * t + (lane & 15);
-              if (col < N_cp) static_cast<float*>(out_cp)[row * N_cp + col] = acc[h][t][r];
-            }
-          }
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = row0_cp + 4 * (lane >> 4) + r;
+      if (GATEUP) {
+        const float u = __shfl_xor(acc[r], 8, 64);  // lanes j, j+8: g and u of one column
+        const int col = n0_cp + 8 * wave + (fr & 7);
+        if (fr < 8 && row < row_end_cp && col < N_cp)
+          static_cast<uint16_t*>(out_cp)[row * N_cp + col] =
+              (uint16_t)f32_to_bf16_bits(swiglu_clamped(acc[r], u, limit));
+      } else {
+        const int col = n0_cp + 16 * wave + fr;
+        if (row < row_end_cp && col < N_cp) static_cast<float*>(out_cp)[row * N_cp + col] = acc[r];
       }
     }
+  };
+  auto substep = [&](const uint16_t* As, const uint16_t* Bs, int ks) __attribute__((always_inline)) {
+    const int chunk = ks * 4 + (lane >> 4);
+    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&As[fr * KB + ws_swz(fr, chunk) * 8]);
+    const int br = 16 * wave + fr;
+    const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&Bs[br * KB + ws_swz(BM + br, chunk) * 8]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc, 0, 0, 0);
   };
 
   setup_ld();
   setup_cp();
-  zero();
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue_next();
 
@@ -976,34 +966,21 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
     issue_next();
     const uint16_t* As = smem_dyn + slot_cp * STAGE;
     const uint16_t* Bs = As + BM * KB;
+    const int sub_valid = (K_cp - kt_cp * KB) >> 5;  // 32-wide substeps left in K
+    if (sub_valid >= SUB) {
 #pragma unroll
-    for (int sw = 0; sw < SUB_W; ++sw) {
-      const int chunk = (wave * SUB_W + sw) * 4 + (lane >> 4);
-      const int r = lane & 15;
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + ws_swz(r, chunk) * 8]);
-      bf16x8_t bf[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        bf[t] = *reinterpret_cast<const bf16x8_t*>(&Bs[(16 * t + r) * KB + ws_swz(BM + 16 * t + r, chunk) * 8]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bf[t], acc[0][t], 0, 0, 0);
-      if (second) {
-        const bf16x8_t a1 =
-            *reinterpret_cast<const bf16x8_t*>(&As[(16 + r) * KB + ws_swz(16 + r, chunk) * 8]);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[1][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bf[t], acc[1][t], 0, 0, 0);
-      }
+      for (int ks = 0; ks < SUB; ++ks) substep(As, Bs, ks);
+    } else {
+      for (int ks = 0; ks < sub_valid; ++ks) substep(As, Bs, ks);
     }
     slot_cp = slot_cp + 1 == STAGES ? 0 : slot_cp + 1;
     if (++kt_cp == nk_cp) {
-      reduce_store();
+      store();
       t_cp += nwg_x;
       if (t_cp >= t_end) break;
       kt_cp = 0;
       setup_cp();
-      zero();
+      acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -1066,10 +1043,8 @@ hipError_t launch_pipe_grid(const GemmProblem& a, const GemmProblem* b, float li
 template <bool GATEUP, int KB, int STAGES>
 hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limit,
                           hipStream_t stream) {
-  const size_t lds = (size_t)STAGES * (WS_BM + WS_NB) * KB * sizeof(uint16_t) +
-                     (size_t)2 * 2 * (WS_NB / 16) * 4 * 64 * sizeof(float);
-  static_assert((size_t)STAGES * (WS_BM + WS_NB) * KB * 2 + 2 * 2 * (WS_NB / 16) * 4 * 64 * 4 <=
-                    160 * 1024, "LDS");
+  const size_t lds = (size_t)STAGES * (WS_BM + WS_NB) * KB * sizeof(uint16_t);
+  static_assert((size_t)STAGES * (WS_BM + WS_NB) * KB * 2 <= 160 * 1024, "LDS");
   auto kern = grouped_wstream_kernel<GATEUP, KB, STAGES>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -1179,13 +1154,9 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
     return hipGetLastError();
   }
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
-  if (v == GemmVariant::kWStream) {  // 512-byte row pieces when every K allows, else 256
-    const bool k256 = a.K % 256 == 0 && (!b || b->K % 256 == 0);
-    if (gateup)
-      return k256 ? launch_wstream<true, 256, 3>(a, b, limit, stream)
-                  : launch_wstream<true, 128, 6>(a, b, limit, stream);
-    return k256 ? launch_wstream<false, 256, 3>(a, b, limit, stream)
-                : launch_wstream<false, 128, 6>(a, b, limit, stream);
+  if (v == GemmVariant::kWStream) {  // 512-byte row pieces, four stages
+    if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream);
+    return launch_wstream<false, 256, 4>(a, b, limit, stream);
   }
   if (v == GemmVariant::kPipe256) {  // K steps of 32, five stages
     if (gateup) return launch_pipe<256, 128, true, 32, 5>(a, b, limit, stream);

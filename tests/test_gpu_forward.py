@@ -54,11 +54,12 @@ SMALL = {
     # long segments with H, I multiples of 32 (the pipelined tiles apply):
     # ragged last m-tile, an N tail in gate_up (I = 160 < 2 x 128)
     "pipe_small": Workload("pipe_small", T=600, H=256, E=4, k=2, I=160, I_s=96, rsf=1.3),
-    # decode-like with H, I multiples of 128 (the weight-streaming tiles apply):
-    # 512-byte row pieces in gate_up, 256-byte ones in down (I = 384)
+    # decode-like, weight-streaming tiles: whole 256-wide K stages in gate_up,
+    # a partial last stage in down (I = 384)
     "stream_small": Workload("stream_small", T=40, H=512, E=16, k=4, I=384, I_s=256),
     # weight streaming with segments of several 32-row m-tiles and both
-    # 16-row halves; 256-byte row pieces everywhere (H = 384)
+    # 16-row halves; partial K stages in gate_up (H = 384) and in the shared
+    # down projection (a single half stage, I_s = 128)
     "stream_multi": Workload("stream_multi", T=300, H=384, E=8, k=2, I=256, I_s=128, rsf=1.5),
 }
 
@@ -169,7 +170,7 @@ def test_forward_every_tile_variant(monkeypatch, variant, name):
     a parity-green layer; the automatic choice is only a speed decision."""
     monkeypatch.setenv("MOE_GEMM_VARIANT", variant)
     wl = SMALL[name]
-    step = {"pipe256": 32, "pipe256k64": 64, "stream32": 64, "wstream": 128}.get(variant)
+    step = {"pipe256": 32, "pipe256k64": 64, "stream32": 64, "wstream": 32}.get(variant)
     if step and (wl.H % step or wl.I % step or wl.I_s % step):
         pytest.skip(f"the pipelined tiles step K in whole {step}-wide stages")
     run_and_check(wl, moe_inputs.generate(wl, seed=1))
