@@ -132,6 +132,56 @@ def calibrate_copy(nbytes: int, reps: int) -> None:
                       "reps": reps}))
 
 
+def _is_gate_up(name: str) -> bool:
+    # grouped GEMM kernels carry the gate_up flag as a `true` template argument
+    return "grouped_" in name and ("<true" in name or ", true" in name)
+
+
+def _counter_means(csv_path: str, counter: str, select) -> tuple[float, int]:
+    """Mean of one rocprofv3 counter (CSV output) over the dispatches of the
+    kernels that `select` accepts by name."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and select(r["Kernel_Name"])]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for the selected kernels in {csv_path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: str,
+                  cal_write_csv: str, command: str) -> None:
+    """HBM traffic of the dominant launch from rocprofv3 counter runs:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the gate_up kernel, each
+    scaled by what the same counter reads for the calibration copy (a
+    torch.neg over 1 GiB: 1 GiB read, 1 GiB written).  Writes
+    profiles/gate_up_<workload>_traffic.json, stamped with the kernel
+    source hash so that bench.py drops it once the kernel changes."""
+    import moe_inputs
+    wl = moe_inputs.WORKLOADS[workload]
+    f_kib, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_gate_up)
+    w_kib, nw = _counter_means(write_csv, "WRITE_SIZE", _is_gate_up)
+    cf_kib, _ = _counter_means(cal_fetch_csv, "FETCH_SIZE", lambda n: "neg" in n)
+    cw_kib, _ = _counter_means(cal_write_csv, "WRITE_SIZE", lambda n: "neg" in n)
+    gib = float(1 << 30)
+    f_scale, w_scale = gib / (cf_kib * 1024.0), gib / (cw_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * f_scale
+    write_b = w_kib * 1024.0 * w_scale
+    out = {"workload": wl.label(), "kernel": "grouped gate_up + SwiGLU",
+           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "dispatches": [nf, nw],
+           "copy_calibration": {"kernel": "torch.neg fp32, 1 GiB in, 1 GiB out",
+                                "fetch_kib": round(cf_kib, 1), "write_kib": round(cw_kib, 1),
+                                "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+           "hbm_bytes_per_launch": round(fetch_b + write_b),
+           "hbm_fetch_bytes": round(fetch_b), "hbm_write_bytes": round(write_b),
+           "command": command, "kernel_source_sha256": kernel_source_sha()}
+    path = os.path.join(ROOT, "profiles", f"gate_up_{wl.label()}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,7 +194,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB streaming copy (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="summarise rocprofv3 counter runs into profiles/ (no GPU work)")
+    ap.add_argument("--traffic-command", default="",
+                    help="the command lines that produced the counter runs (recorded)")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic, args.traffic_command)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
