@@ -94,9 +94,9 @@ struct Carver {
 
 // Tile variant by the mean rows per group: about one short row tile or less
 // (decode) -> persistent weight streaming; several 256-row tiles -> the
-// pipelined 256-row tiles; in between the 128-row tiles.
-// MOE_GEMM_VARIANT=wstream | tile32 | tile128 | pipe256 | pipe256k64 |
-// stream32 | stream forces one (a tuning lever; results are identical up to
+// pipelined 256-row tiles (eight wavefronts); in between the 128-row tiles.
+// MOE_GEMM_VARIANT=wstream | tile32 | tile128 | pipe256 | pipe256w8 |
+// pipe256k64 | stream32 | stream forces one (a tuning lever; results are identical up to
 // fp32 summation order).
 GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
   if (const char* env = std::getenv("MOE_GEMM_VARIANT")) {
@@ -107,9 +107,10 @@ GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
     if (!std::strcmp(env, "stream32")) return GemmVariant::kStream32;
     if (!std::strcmp(env, "stream")) return GemmVariant::kStream;
     if (!std::strcmp(env, "wstream")) return GemmVariant::kWStream;
+    if (!std::strcmp(env, "pipe256w8")) return GemmVariant::kPipe256W8;
   }
   if (rows <= 64 * groups) return GemmVariant::kWStream;
-  if (rows >= 512 * groups) return GemmVariant::kPipe256;
+  if (rows >= 512 * groups) return GemmVariant::kPipe256W8;
   return GemmVariant::kTile128;
 }
 
@@ -123,7 +124,8 @@ GemmVariant pick_variant(int64_t rows, int64_t groups, int64_t a_elems, int64_t 
   const int64_t lim = (int64_t)1 << 31;
   if (v == GemmVariant::kWStream && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32))
     v = GemmVariant::kTile32;
-  const bool pipe = v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64;
+  const bool pipe = v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64 ||
+                    v == GemmVariant::kPipe256W8;
   if (pipe && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32)) v = GemmVariant::kTile128;
   if (v == GemmVariant::kPipe256K64 && !k_multiple_of_64) v = GemmVariant::kPipe256;
   if (v == GemmVariant::kStream32 && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_64))

@@ -418,7 +418,7 @@ __device__ __forceinline__ int pl_swz(int row, int chunk) {
   return KB == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ ((row >> 1) & 7);
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, bool DENSE>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, bool DENSE, int NW>
 __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, int tile,
                                           float limit, uint16_t* smem) {
   constexpr int NB = GATEUP ? 2 * BN : BN;   // weight rows per tile
@@ -427,15 +427,16 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   constexpr int STAGE = ROWS * KB;           // bf16 elements per stage
   constexpr int RPI = 64 / CHUNKS;           // rows per 1 KB load instruction
   constexpr int INSTR = ROWS / RPI;          // load instructions per stage
-  constexpr int PER_WAVE = INSTR / 4;
-  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int PER_WAVE = INSTR / NW;
+  constexpr int WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int NMAT = GATEUP ? 2 : 1;
   constexpr int SUB = KB / 16;               // MFMA K substeps per stage
-  static_assert(INSTR % 4 == 0 && SUB % 2 == 0, "shape");
-  constexpr int A_INSTR = BM / (4 * RPI);    // instructions of each wave that fill A rows
-  static_assert(BM % (4 * RPI) == 0, "A rows fill whole instructions of every wave");
+  static_assert(INSTR % NW == 0 && SUB % 2 == 0, "shape");
+  constexpr int A_INSTR = BM / (NW * RPI);   // instructions of each wave that fill A rows
+  static_assert(BM % (NW * RPI) == 0, "A rows fill whole instructions of every wave");
+  constexpr int VM_STAGE = PER_WAVE;         // vector memory instructions per stage per wave
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -486,7 +487,7 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   uint32_t off[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int row = RPI * (wave + 4 * i) + lane / CHUNKS;
+    const int row = RPI * (wave + NW * i) + lane / CHUNKS;
     const int chunk = pl_swz<KB>(row, lane % CHUNKS);
     if (i < A_INSTR) {
       const int64_t gr = row0 + row < row_end ? row0 + row : row0;
@@ -506,7 +507,7 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
     uint16_t* base = smem + slot * STAGE;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i)
-      lds_direct_16((i < A_INSTR ? Abase : Wg) + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+      lds_direct_16((i < A_INSTR ? Abase : Wg) + off[i] + k0, base + (wave + NW * i) * RPI * KB);
   };
 
   f32x16_t acc[NMAT][TM][TN];
@@ -560,12 +561,16 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   // always "at most STAGES-2 newer stages of this wave's loads in flight".
   auto stage_k = [&](int s) __attribute__((always_inline)) { return min(s, nk - 1) * KB; };
 
-  // previous tile's stores out of the vmcnt queue; every wave done with LDS
-  PL_WAIT_VM(0);
-  __syncthreads();
+  // every wave done reading LDS (the previous tile's last stage) before the
+  // slots are refilled.  No fence: the previous tile's loads all landed
+  // before its epilogue, and its epilogue stores drain while this tile's
+  // first stages load (they are only older entries of the vmcnt queue in the
+  // waits below)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  pl_barrier();
 #pragma unroll
   for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(s0, stage_k(s0));
-  PL_WAIT_VM_LDS((STAGES - 2) * PER_WAVE);
+  PL_WAIT_VM_LDS((STAGES - 2) * VM_STAGE);
   pl_barrier();
   read_frags(0, 0, C0{});
 
@@ -580,23 +585,27 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
         // own loads of stage kt+1 landed and own LDS reads of stage kt done:
         // after the barrier stage kt+1 is complete everywhere, and nobody
         // reads the slot the next step's loads overwrite
-        PL_WAIT_VM_LDS((STAGES - 2) * PER_WAVE);
+        PL_WAIT_VM_LDS((STAGES - 2) * VM_STAGE);
         pl_barrier();
       }
-      // MFMAs of substep ks; read the fragments of the next substep
-      if (even) mfmas(C0{}); else mfmas(C1{});
+      // read the fragments of the next substep, then the MFMAs of substep
+      // ks.  In this program order both fragment groups are live at once, so
+      // they keep separate registers and the reads overlap the MFMAs (reads
+      // placed after the MFMAs let the register allocator fold the groups
+      // into one, which serialises every substep on the LDS latency).
       if (ks + 1 < SUB) {
         if (even) read_frags(slot, ks + 1, C1{}); else read_frags(slot, ks + 1, C0{});
       } else {
         read_frags(slot_next, 0, C0{});
       }
+      if (even) mfmas(C0{}); else mfmas(C1{});
       if (ks == 0) issue(slot_prev, stage_k(kt + STAGES - 1));
       // interleave: groups of up to 4 MFMAs, each followed by its share of
       // the fragment reads (and, in substep 0, of the stage loads)
       constexpr int MF = NMFMA >= 4 ? 4 : NMFMA;
       constexpr int GROUPS = NMFMA / MF;
       constexpr int RD = (NREAD + GROUPS - 1) / GROUPS;
-      constexpr int VM = (PER_WAVE + GROUPS - 1) / GROUPS;
+      constexpr int VM = (VM_STAGE + GROUPS - 1) / GROUPS;
 #pragma unroll
       for (int q = 0; q < GROUPS; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
@@ -607,6 +616,9 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
     slot_prev = slot;
     slot = slot_next;
   }
+  // the re-fetches past the end of K landed: nothing of this tile is still
+  // in flight into LDS when the next tile refills the slots
+  PL_WAIT_VM(0);
 
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -634,8 +646,8 @@ __device__ __forceinline__ int pipe_mtiles(const GemmProblem& P) {
   return P.group_offsets ? P.mtile_start[P.G] : (int)((P.M + BM - 1) / BM);
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M>
-__global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(GemmProblem p0, GemmProblem p1,
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void grouped_pipe_kernel(GemmProblem p0, GemmProblem p1,
                                                               int has_p1, float limit) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
   const int mt0 = pipe_mtiles<BM>(p0);
@@ -650,9 +662,10 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(GemmProblem p0, Ge
   const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
   for (int t = t_begin + lid; t < t_end; t += nwg_x) {
     if (t < tiles0)
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true>(p0, mt0, t, limit, smem_dyn);
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true, NW>(p0, mt0, t, limit, smem_dyn);
     else
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true>(p1, mt1, t - tiles0, limit, smem_dyn);
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true, NW>(p1, mt1, t - tiles0, limit,
+                                                               smem_dyn);
   }
 }
 
@@ -661,17 +674,17 @@ __global__ __launch_bounds__(256, 1) void grouped_pipe_kernel(GemmProblem p0, Ge
 // takes a contiguous range): for short expert segments, where a few hundred
 // tiles each stream their weights once and the hardware's dispatch of new
 // workgroups as CUs free up balances the load.
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M>
-__global__ __launch_bounds__(256, 1) void grouped_pipe_grid_kernel(GemmProblem p0, GemmProblem p1,
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void grouped_pipe_grid_kernel(GemmProblem p0, GemmProblem p1,
                                                                    int tiles0, float limit) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   if (t < tiles0)
-    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false>(p0, pipe_mtiles<BM>(p0), t, limit,
-                                                         smem_dyn);
+    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false, NW>(p0, pipe_mtiles<BM>(p0), t, limit,
+                                                             smem_dyn);
   else
-    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false>(p1, pipe_mtiles<BM>(p1), t - tiles0,
-                                                         limit, smem_dyn);
+    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false, NW>(p1, pipe_mtiles<BM>(p1), t - tiles0,
+                                                             limit, smem_dyn);
 }
 
 // ---------------------------------------------------------------------------
@@ -998,13 +1011,13 @@ int device_cu_count() {
   return cached;
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M = 2>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M = 2, int NW = 4>
 hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
                        hipStream_t stream) {
   constexpr int NB = GATEUP ? 2 * BN : BN;
   const size_t lds = (size_t)STAGES * (BM + NB) * KB * sizeof(uint16_t);
   static_assert((size_t)STAGES * (BM + NB) * KB * 2 <= 160 * 1024, "LDS");
-  auto kern = grouped_pipe_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M>;
+  auto kern = grouped_pipe_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>;
   static bool attr_set = false;  // raise the dynamic LDS limit once per process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1014,17 +1027,17 @@ hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
   }
   const GemmProblem pb = b ? *b : a;
   const int grid = device_cu_count();  // one resident workgroup per CU
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a, pb, b ? 1 : 0, limit);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream, a, pb, b ? 1 : 0, limit);
   return hipGetLastError();
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW = 4>
 hipError_t launch_pipe_grid(const GemmProblem& a, const GemmProblem* b, float limit,
                             hipStream_t stream) {
   constexpr int NB = GATEUP ? 2 * BN : BN;
   const size_t lds = (size_t)STAGES * (BM + NB) * KB * sizeof(uint16_t);
   static_assert((size_t)STAGES * (BM + NB) * KB * 2 <= 160 * 1024, "LDS");
-  auto kern = grouped_pipe_grid_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M>;
+  auto kern = grouped_pipe_grid_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1036,7 +1049,7 @@ hipError_t launch_pipe_grid(const GemmProblem& a, const GemmProblem* b, float li
   const int total = tiles0 + (b ? b->max_mtiles * b->ntiles : 0);
   if (total == 0) return hipSuccess;
   const GemmProblem pb = b ? *b : a;
-  hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, stream, a, pb, tiles0, limit);
+  hipLaunchKernelGGL(kern, dim3(total), dim3(NW * 64), lds, stream, a, pb, tiles0, limit);
   return hipGetLastError();
 }
 
@@ -1118,6 +1131,7 @@ int gemm_tile_m(GemmVariant v) {
     case GemmVariant::kTile128: return 128;
     case GemmVariant::kPipe256: return 256;
     case GemmVariant::kPipe256K64: return 256;
+    case GemmVariant::kPipe256W8: return 256;
     case GemmVariant::kStream32: return 32;
     case GemmVariant::kWStream: return WS_BM;
   }
@@ -1126,7 +1140,8 @@ int gemm_tile_m(GemmVariant v) {
 int gemm_tile_n(GemmVariant v, bool gateup) {
   if (v == GemmVariant::kStream) return gateup ? ST_WR / 2 : ST_WR;
   if (v == GemmVariant::kWStream) return gateup ? WS_NB / 2 : WS_NB;
-  if (v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64 || v == GemmVariant::kStream32)
+  if (v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64 || v == GemmVariant::kStream32 ||
+      v == GemmVariant::kPipe256W8)
     return gateup ? 128 : 256;
   return 128;
 }
@@ -1165,6 +1180,10 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
   if (v == GemmVariant::kStream32) {  // 32-row tiles, K steps of 64, three stages
     if (gateup) return launch_pipe_grid<32, 128, true, 64, 3, 1>(a, b, limit, stream);
     return launch_pipe_grid<32, 256, false, 64, 3, 1>(a, b, limit, stream);
+  }
+  if (v == GemmVariant::kPipe256W8) {  // as kPipe256 with eight wavefronts (two per SIMD)
+    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8>(a, b, limit, stream);
+    return launch_pipe<256, 256, false, 32, 5, 2, 8>(a, b, limit, stream);
   }
   if (v == GemmVariant::kPipe256K64) {  // K steps of 64 (128-byte rows), two stages
     if (gateup) return launch_pipe<256, 128, true, 64, 2>(a, b, limit, stream);

@@ -30,7 +30,9 @@ struct GemmProblem {
 // row pieces (short expert segments; K a multiple of 32), LDS-staged 32-row
 // and 128-row tiles, pipelined 256-row tiles with direct global->LDS loads
 // (long segments), and two earlier streaming forms kept for comparison.
-enum class GemmVariant { kTile32, kTile128, kPipe256, kPipe256K64, kStream32, kStream, kWStream };
+enum class GemmVariant {
+  kTile32, kTile128, kPipe256, kPipe256K64, kStream32, kStream, kWStream, kPipe256W8
+};
 int gemm_tile_m(GemmVariant v);
 int gemm_tile_n(GemmVariant v, bool gateup);
 
