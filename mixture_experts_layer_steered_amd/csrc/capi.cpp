@@ -300,7 +300,7 @@ moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, int32_t* ex
   int32_t* counts = c.take<int32_t>((size_t)tiles * p->E);
   int32_t* starts = c.take<int32_t>((size_t)tiles * p->E);
   if ((s = device_status(launch_permute(topk_ids, counts, starts, expert_offsets, sorted_token,
-                                        inv_pos, N, p->E, p->k, stream),
+                                        inv_pos, N, p->E, p->k, 0, nullptr, stream),
                          "permute")) != MOE_OK)
     return s;
   return ok();
@@ -469,13 +469,12 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
                          "router")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_ROUTER)) != MOE_OK) return s;
+  // the permutation and the grouped GEMM's m-tile prefix (one launch for a
+  // decode-sized batch)
   if ((s = device_status(launch_permute(L.ids, L.counts, L.starts, L.offsets, L.sorted_token,
-                                        L.inv_pos, N, p->E, p->k, stream),
+                                        L.inv_pos, N, p->E, p->k, gemm_tile_m(v), L.mstart,
+                                        stream),
                          "permute")) != MOE_OK)
-    return s;
-  const int bm = gemm_tile_m(v);
-  if ((s = device_status(launch_gemm_schedule(L.offsets, p->E, bm, bm, L.mstart, nullptr, stream),
-                         "gemm schedule")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_PERMUTE)) != MOE_OK) return s;
   if ((s = device_status(launch_grouped_gemm(v, true, gu, shared ? &sgu : nullptr,

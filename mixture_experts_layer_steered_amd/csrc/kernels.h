@@ -44,9 +44,11 @@ hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, f
                          float rsf, hipStream_t stream);
 
 int permute_tiles(int64_t N);
+// mstart (optional): also write the grouped GEMM's m-tile prefix over the
+// expert counts for tiles of bm rows (as launch_gemm_schedule does).
 hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, int32_t* offsets,
                           int32_t* sorted_token, int32_t* inv_pos, int64_t N, int E, int k,
-                          hipStream_t stream);
+                          int bm, int32_t* mstart, hipStream_t stream);
 
 hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
                                 int32_t* start0, int32_t* start1, hipStream_t stream);

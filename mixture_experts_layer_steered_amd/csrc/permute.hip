@@ -13,6 +13,8 @@
 //                       LDS prefix over the waves, and ranks equal ids inside
 //                       a 64-pair step with ballot match masks, so every
 //                       expert's rows keep the pairs' order.
+// With a single tile (decode) one workgroup does all three, and the grouped
+// GEMM's m-tile prefix, in one launch.
 // The LDS atomics of steps 1 and 3 only count; the order of the increments
 // never shows in a result.
 #include "common.h"
@@ -132,14 +134,107 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(
   }
 }
 
+// All pairs in one tile (N <= 4096, decode-sized batches): the three passes
+// in one workgroup, plus the m-tile prefix of the grouped GEMM over the
+// expert counts (the schedule the GEMM launches read), in one launch.
+__global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_pos, int64_t N, int E, int k,
+    int bm, int32_t* __restrict__ mstart) {
+  __shared__ int32_t whist[PM_WAVES][MOE_MAX_EXPERTS_DEV];
+  __shared__ int32_t wsum[2][PM_WAVES];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) whist[i / E][i % E] = 0;
+  __syncthreads();
+  const int64_t wbase = (int64_t)wave * PM_PER_WAVE;
+  int my_e[PM_STEPS];
+#pragma unroll
+  for (int s = 0; s < PM_STEPS; ++s) {
+    const int64_t p = wbase + s * 64 + lane;
+    my_e[s] = (p < N) ? ids[p] : MOE_MAX_EXPERTS_DEV;  // sentinel: matches no expert
+    if (p < N) atomicAdd(&whist[wave][my_e[s]], 1);
+  }
+  __syncthreads();
+  // thread e: expert e's count, then exclusive scans over experts of the
+  // counts (offsets) and of the m-tiles ceil(count / bm) (GEMM schedule)
+  const int e = threadIdx.x;
+  int32_t cnt = 0;
+  if (e < E)
+    for (int w = 0; w < PM_WAVES; ++w) cnt += whist[w][e];
+  int32_t v[2] = {cnt, (cnt + bm - 1) / bm};
+  int32_t incl[2] = {v[0], v[1]};
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int32_t o = __shfl_up(incl[q], off, 64);
+      if (lane >= off) incl[q] += o;
+    }
+  }
+  if (lane == 63) {
+    wsum[0][wave] = incl[0];
+    wsum[1][wave] = incl[1];
+  }
+  __syncthreads();
+  int32_t before[2] = {0, 0};
+  for (int w = 0; w < wave; ++w) {
+    before[0] += wsum[0][w];
+    before[1] += wsum[1][w];
+  }
+  const int32_t start = before[0] + incl[0] - v[0];
+  if (e < E) {
+    offsets[e] = start;
+    if (mstart) mstart[e] = before[1] + incl[1] - v[1];
+    // each wave's run of expert e starts after the earlier waves' pairs
+    int32_t run = start;
+    for (int w = 0; w < PM_WAVES; ++w) {
+      const int32_t c = whist[w][e];
+      whist[w][e] = run;
+      run += c;
+    }
+  }
+  if (e == E - 1) {
+    offsets[E] = (int32_t)N;
+    if (mstart) mstart[E] = before[1] + incl[1];
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int s = 0; s < PM_STEPS; ++s) {
+    const int ee = my_e[s];
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+      const bool bit = (ee >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int n_same = __popcll(same);
+    if (ee < E) {
+      const int64_t p = wbase + s * 64 + lane;
+      const int32_t pos = whist[wave][ee] + rank;
+      sorted_token[pos] = (int32_t)(p / k);
+      inv_pos[p] = pos;
+      if (rank == 0) whist[wave][ee] += n_same;
+    }
+  }
+}
+
 }  // namespace
 
 int permute_tiles(int64_t N) { return (int)((N + PM_TILE - 1) / PM_TILE); }
 
 hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, int32_t* offsets,
                           int32_t* sorted_token, int32_t* inv_pos, int64_t N, int E, int k,
-                          hipStream_t stream) {
+                          int bm, int32_t* mstart, hipStream_t stream) {
   const int tiles = permute_tiles(N);
+  if (tiles == 1) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PM_THREADS), 0, stream, ids, offsets,
+                       sorted_token, inv_pos, N, E, k, bm > 0 ? bm : 1, mstart);
+    return hipGetLastError();
+  }
   if (tiles == 0) {
     // no pairs: offsets are all zero
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, stream, counts, starts,
@@ -152,5 +247,6 @@ hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, 
                      offsets, tiles, E, N);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(tiles), dim3(PM_THREADS), 0, stream, ids,
                      starts, sorted_token, inv_pos, N, E, k);
+  if (mstart) return launch_gemm_schedule(offsets, E, bm, bm, mstart, nullptr, stream);
   return hipGetLastError();
 }

@@ -19,6 +19,8 @@
 // wavefront ranks one token: each lane holds up to 16 experts as 64-bit
 // keys (orderable score bits, inverted id) and k wave-wide arg-max rounds
 // pick the winners.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,6 +31,7 @@ constexpr int RT_BE = 64;       // experts per workgroup tile
 constexpr int RT_BK = 32;       // K per LDS stage
 constexpr int RT_LD = RT_BK + 8;  // padded LDS row (bf16 elements): 80 bytes
 constexpr int RT_MAX_SPLITS = 16; // K slices of the router GEMM at most
+constexpr int RT_DEPTH = 4;       // K steps in flight per workgroup
 
 __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   uint32_t u = __float_as_uint(w);
@@ -64,39 +67,54 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   // x tile: 64 rows x 32 k = 256 chunks of 8 bf16, one per thread
   const int xr = tid >> 2, xc = (tid & 3) * 8;
   // w tile: 64 rows x 32 k = 512 float4, two per thread
+  int wr_[2], wc_[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + q * 256;
+    wr_[q] = idx >> 3;
+    wc_[q] = (idx & 7) * 4;
+  }
   const int k_begin = blockIdx.z * k_slice;
   const int k_end = min(H, k_begin + k_slice);
+  const int nit = k_end > k_begin ? (k_end - k_begin + RT_BK - 1) / RT_BK : 0;
   float* __restrict__ logits = partial + (int64_t)blockIdx.z * T * E;
-  for (int k0 = k_begin; k0 < k_end; k0 += RT_BK) {
-    uint4 xv = make_uint4(0, 0, 0, 0);
+
+  // K steps go through a ring of RT_DEPTH register buffers: the loads of
+  // step it + RT_DEPTH are issued as soon as step it is in LDS, so a slice
+  // pays about one memory round trip instead of one per step
+  uint4 xv[RT_DEPTH];
+  float4 wv[RT_DEPTH][2];
+  auto load = [&](int it, auto d_c) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_c)::value;
+    const int k0 = k_begin + it * RT_BK;
+    xv[d] = make_uint4(0, 0, 0, 0);
     if (t0 + xr < T && k0 + xc < k_end)
-      xv = *reinterpret_cast<const uint4*>(x + (t0 + xr) * (int64_t)H + k0 + xc);
-    float4 wv[2];
-    int wr_[2], wc_[2];
+      xv[d] = *reinterpret_cast<const uint4*>(x + (t0 + xr) * (int64_t)H + k0 + xc);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      int idx = tid + q * 256;
-      wr_[q] = idx >> 3;
-      wc_[q] = (idx & 7) * 4;
-      wv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      wv[d][q] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e0 + wr_[q] < E && k0 + wc_[q] < k_end)
-        wv[q] = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + wr_[q]) * H + k0 + wc_[q]);
+        wv[d][q] = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + wr_[q]) * H + k0 + wc_[q]);
     }
+  };
+  auto step = [&](int it, auto d_c) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_c)::value;
     __syncthreads();
-    *reinterpret_cast<uint4*>(&xs[xr * RT_LD + xc]) = xv;
+    *reinterpret_cast<uint4*>(&xs[xr * RT_LD + xc]) = xv[d];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       uint32_t h[4], m[4], l[4];
-      split3(wv[q].x, h[0], m[0], l[0]);
-      split3(wv[q].y, h[1], m[1], l[1]);
-      split3(wv[q].z, h[2], m[2], l[2]);
-      split3(wv[q].w, h[3], m[3], l[3]);
-      int o = wr_[q] * RT_LD + wc_[q];
+      split3(wv[d][q].x, h[0], m[0], l[0]);
+      split3(wv[d][q].y, h[1], m[1], l[1]);
+      split3(wv[d][q].z, h[2], m[2], l[2]);
+      split3(wv[d][q].w, h[3], m[3], l[3]);
+      const int o = wr_[q] * RT_LD + wc_[q];
       *reinterpret_cast<uint2*>(&wsp[0][o]) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       *reinterpret_cast<uint2*>(&wsp[1][o]) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
       *reinterpret_cast<uint2*>(&wsp[2][o]) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
     }
     __syncthreads();
+    if (it + RT_DEPTH < nit) load(it + RT_DEPTH, d_c);
 #pragma unroll
     for (int ks = 0; ks < RT_BK / 16; ++ks) {
       const int kk = ks * 16 + (lane >> 5) * 8;
@@ -109,6 +127,21 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc, 0, 0, 0);
     }
+  };
+  using D0 = std::integral_constant<int, 0>;
+  using D1 = std::integral_constant<int, 1>;
+  using D2 = std::integral_constant<int, 2>;
+  using D3 = std::integral_constant<int, 3>;
+  static_assert(RT_DEPTH == 4, "the ring below is unrolled for four buffers");
+  if (0 < nit) load(0, D0{});
+  if (1 < nit) load(1, D1{});
+  if (2 < nit) load(2, D2{});
+  if (3 < nit) load(3, D3{});
+  for (int it0 = 0; it0 < nit; it0 += RT_DEPTH) {
+    step(it0, D0{});
+    if (it0 + 1 < nit) step(it0 + 1, D1{});
+    if (it0 + 2 < nit) step(it0 + 2, D2{});
+    if (it0 + 3 < nit) step(it0 + 3, D3{});
   }
   // 32x32 accumulator: lane holds column (lane & 31), rows 8*(r/4) + 4*(lane/32) + r%4
   const int col = e0 + wn * 32 + (lane & 31);
@@ -159,17 +192,18 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     key[i] = 0;
     lg[i] = 0.f;
     if (e < E) {
-      // slices four at a time (independent loads in flight), summed in
-      // slice order
-      float l = partial[t * E + e];
-      for (int sp0 = 1; sp0 < splits; sp0 += 4) {
-        float pv[4];
+      // the K-slice partials, loaded TK_SLICES at a time (one round trip
+      // for the usual slice counts), summed in slice order
+      constexpr int TK_SLICES = TK_PER_LANE <= 4 ? 16 : 64 / TK_PER_LANE;
+      float l = 0.f;
+      for (int sp0 = 0; sp0 < splits; sp0 += TK_SLICES) {
+        float pv[TK_SLICES];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < TK_SLICES; ++u)
           pv[u] = sp0 + u < splits ? partial[(sp0 + u) * TE + t * E + e] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (sp0 + u < splits) l += pv[u];
+        for (int u = 0; u < TK_SLICES; ++u)
+          if (sp0 + u < splits) l = sp0 + u == 0 ? pv[u] : l + pv[u];
       }
       if (splits > 1) logits[t * E + e] = l;
       lg[i] = l;
