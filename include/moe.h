@@ -175,12 +175,18 @@ moe_status moe_router_topk(const moe_params* p, const moe_bf16* x, const float* 
  *   sorted_token   [T*k] out: token of each permuted row (ascending inside a
  *                  segment)
  *   inv_pos        [T*k] out: permuted row of pair t*k + j
+ *   x, x_perm      optional gather: with both non-NULL, x_perm[r] =
+ *                  x[sorted_token[r]] ([T, H] bf16 in, [T*k, H] bf16 out);
+ *                  with both NULL nothing is gathered (moe_forward never
+ *                  gathers: its gate_up GEMM reads x through sorted_token);
+ *                  x_perm without x is MOE_ERR_INVALID_ARG
  * Bit-exact and deterministic.  Ids outside [0, E) are undefined behaviour
  * (they are not checked on the device).
- * Source: "Module glm5next_mlp", Constants, MOE_MODULE. */
-moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, int32_t* expert_offsets,
-                       int32_t* sorted_token, int32_t* inv_pos, void* ws, size_t ws_bytes,
-                       hipStream_t stream);
+ * Source: "Module glm5next_mlp", Constants, MOE_MODULE (token sort / permute
+ * / unpermute). */
+moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, const moe_bf16* x,
+                       int32_t* expert_offsets, int32_t* sorted_token, int32_t* inv_pos,
+                       moe_bf16* x_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of workspace moe_grouped_swiglu_gemm needs (host-only, pure). */
 moe_status moe_grouped_gemm_workspace_size(int32_t n_groups, int64_t M_total, int32_t H,

@@ -74,8 +74,8 @@ def _load() -> ctypes.CDLL:
         "moe_workspace_size": (st, [P, POINTER(c_size_t)]),
         "moe_router_topk": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
-        "moe_permute": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
-                             c_void_p]),
+        "moe_permute": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                             c_void_p, c_size_t, c_void_p]),
         "moe_grouped_gemm_workspace_size": (st, [c_int32, c_int64, c_int32, c_int32,
                                                  POINTER(c_size_t)]),
         "moe_grouped_swiglu_gemm": (st, [c_int32, c_int64, c_int32, c_int32, c_float, c_void_p,
@@ -153,10 +153,11 @@ def moe_router_topk(params, x, w_router, corr_bias, topk_ids, topk_w, ws, stream
                                 _stream(stream)))
 
 
-def moe_permute(params, topk_ids, expert_offsets, sorted_token, inv_pos, ws, stream=None):
-    _check(_lib.moe_permute(ctypes.byref(params), _ptr(topk_ids), _ptr(expert_offsets),
-                            _ptr(sorted_token), _ptr(inv_pos), _ptr(ws), _nbytes(ws),
-                            _stream(stream)))
+def moe_permute(params, topk_ids, expert_offsets, sorted_token, inv_pos, ws, stream=None,
+                x=None, x_perm=None):
+    _check(_lib.moe_permute(ctypes.byref(params), _ptr(topk_ids), _ptr(x), _ptr(expert_offsets),
+                            _ptr(sorted_token), _ptr(inv_pos), _ptr(x_perm), _ptr(ws),
+                            _nbytes(ws), _stream(stream)))
 
 
 def moe_grouped_gemm_workspace_size(n_groups, M_total, H, I) -> int:

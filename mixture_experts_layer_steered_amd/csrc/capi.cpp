@@ -279,17 +279,20 @@ moe_status moe_router_topk(const moe_params* p, const moe_bf16* x, const float* 
   return ok();
 }
 
-moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, int32_t* expert_offsets,
-                       int32_t* sorted_token, int32_t* inv_pos, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, const moe_bf16* x,
+                       int32_t* expert_offsets, int32_t* sorted_token, int32_t* inv_pos,
+                       moe_bf16* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status s = check_params(p);
   if (s != MOE_OK) return s;
+  if (x_perm && !x) return fail(MOE_ERR_INVALID_ARG, "x_perm needs x (the rows to gather)");
   REQUIRE_PTR(expert_offsets);
   const int64_t N = p->T * p->k;
   if (N > 0) {
     REQUIRE_PTR(topk_ids);
     REQUIRE_PTR(sorted_token);
     REQUIRE_PTR(inv_pos);
+    OPTIONAL_PTR(x);
+    OPTIONAL_PTR(x_perm);
     REQUIRE_PTR(ws);
     if (ws_bytes < permute_ws_bytes(*p))
       return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, permute_ws_bytes(*p));
@@ -302,6 +305,10 @@ moe_status moe_permute(const moe_params* p, const int32_t* topk_ids, int32_t* ex
   if ((s = device_status(launch_permute(topk_ids, counts, starts, expert_offsets, sorted_token,
                                         inv_pos, N, p->E, p->k, 0, nullptr, stream),
                          "permute")) != MOE_OK)
+    return s;
+  if (x_perm && N > 0 &&
+      (s = device_status(launch_gather_rows(x, sorted_token, x_perm, N, p->H, stream),
+                         "gather")) != MOE_OK)
     return s;
   return ok();
 }

@@ -50,6 +50,10 @@ hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, 
                           int32_t* sorted_token, int32_t* inv_pos, int64_t N, int E, int k,
                           int bm, int32_t* mstart, hipStream_t stream);
 
+// x_perm[r] = x[sorted_token[r]] for r < N (rows of H bf16, H a multiple of 8).
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_token, uint16_t* x_perm,
+                              int64_t N, int H, hipStream_t stream);
+
 hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
                                 int32_t* start0, int32_t* start1, hipStream_t stream);
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,

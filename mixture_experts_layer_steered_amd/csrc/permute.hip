@@ -222,9 +222,38 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(
   }
 }
 
+// Optional materialised gather of the permuted activations: 16 bytes per
+// thread, consecutive threads along a row (coalesced reads of the source row
+// and writes of the destination row); grid-stride over (row, chunk).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ sorted_token,
+                                                          uint4* __restrict__ x_perm, int64_t N,
+                                                          int chunks) {
+  const int64_t total = N * chunks;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / chunks;
+    const int c = (int)(i - r * chunks);
+    x_perm[i] = x[(int64_t)sorted_token[r] * chunks + c];
+  }
+}
+
 }  // namespace
 
 int permute_tiles(int64_t N) { return (int)((N + PM_TILE - 1) / PM_TILE); }
+
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_token, uint16_t* x_perm,
+                              int64_t N, int H, hipStream_t stream) {
+  const int chunks = H / 8;
+  const int64_t total = N * chunks;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(x), sorted_token,
+                     reinterpret_cast<uint4*>(x_perm), N, chunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, int32_t* offsets,
                           int32_t* sorted_token, int32_t* inv_pos, int64_t N, int E, int k,

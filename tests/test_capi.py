@@ -111,6 +111,12 @@ def test_entry_points_reject_before_launch():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_router_topk(p, 16, 16, None, 16, 16, 16, stream=0)
     assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as ei:   # a gather target without rows to gather
+        moe.moe_permute(p, 16, 16, 16, 16, 16, x=None, x_perm=16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:   # misaligned gather source
+        moe.moe_permute(p, 16, 16, 16, 16, 16, x=18, x_perm=16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_grouped_swiglu_gemm(4, 100, 128, 256, float("nan"), 16, None, 16, 16, 16, 16, 16,
                                     16, stream=0)

@@ -93,17 +93,28 @@ def test_permute_parity(tl, T, E, k, skew):
     prob = np.exp(-skew * np.arange(E) / E)
     prob /= prob.sum()
     ids = np.stack([np.sort(rng.choice(E, size=k, replace=False, p=prob)) for _ in range(T)]).astype(np.int32)
-    p = moe.make_params(T, 8, E, k, 8, 0, 1.0, 7.0)
+    H = 24 if T > 1000 else 136   # the optional gather: ragged row widths (16-byte chunks)
+    p = moe.make_params(T, H, E, k, 8, 0, 1.0, 7.0)
     ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
     off = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
     st = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
     inv = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
-    moe.moe_permute(p, torch.from_numpy(ids).cuda(), off, st, inv, ws)
+    x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    xp = torch.full((T * k, H), -1, dtype=torch.int16, device="cuda")
+    moe.moe_permute(p, torch.from_numpy(ids).cuda(), off, st, inv, ws, x=gh.dev_bf16(torch, x),
+                    x_perm=xp)
     torch.cuda.synchronize()
     ref = mo.permute(ids, E)
     np.testing.assert_array_equal(off.cpu().numpy(), ref["offsets"])
     np.testing.assert_array_equal(st.cpu().numpy(), ref["sorted_token"])
     np.testing.assert_array_equal(inv.cpu().numpy(), ref["inv_pos"])
+    # gathered rows are byte copies of the oracle's permuted rows
+    np.testing.assert_array_equal(gh.to_bits(xp), x[ref["sorted_token"]])
+    # without x / x_perm nothing is gathered (and the sort is the same)
+    st.fill_(-1)
+    moe.moe_permute(p, torch.from_numpy(ids).cuda(), off, st, inv, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(st.cpu().numpy(), ref["sorted_token"])
 
 
 # ------------------------------------------------------ grouped GEMM ----
