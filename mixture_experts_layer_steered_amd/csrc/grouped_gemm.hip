@@ -399,6 +399,10 @@ __device__ __forceinline__ void lds_direct_16(const void* g, uint16_t* lds_wave_
 // its LDS reads and writes have completed.
 #define PL_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0070)
 #define PL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+// vmcnt(n) with lgkmcnt(m), m < 16: all but this wave's m newest LDS
+// operations have completed (they complete in order)
+#define PL_WAIT_VM_LDS_N(n, m) \
+  __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0070 | ((m) << 8))
 
 // Workgroup barrier without a memory fence.  __syncthreads() fences, which
 // makes every wave wait for all of its outstanding loads (including the
@@ -557,8 +561,17 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   constexpr int NMFMA = TM * NMAT * TN;  // MFMAs per substep
   const int nk = K / KB;
   // Every step issues exactly one stage of loads (stages past the end
-  // re-fetch the last K step into a free slot), so "stage kt+1 landed" is
-  // always "at most STAGES-2 newer stages of this wave's loads in flight".
+  // re-fetch the last K step into a free slot).  With four or more slots the
+  // loads of step kt refill the slot of stage kt-2 (LAG 2), else that of
+  // stage kt-1 (LAG 1); AHEAD = STAGES - LAG stages are issued ahead of the
+  // one being read, so "stage kt+1 landed" is "at most AHEAD-1 newer stages
+  // of this wave's loads in flight".  Before the barrier of step kt each wave
+  // also finishes its reads of the slot the next step refills: with LAG 2
+  // those are all but its newest NREAD reads (the fragments of the substep
+  // still to come), so the wait does not stall on reads just issued; with
+  // LAG 1 all of them.
+  constexpr int LAG = STAGES >= 4 ? 2 : 1;
+  constexpr int AHEAD = STAGES - LAG;
   auto stage_k = [&](int s) __attribute__((always_inline)) { return min(s, nk - 1) * KB; };
 
   // every wave done reading LDS (the previous tile's last stage) before the
@@ -569,52 +582,55 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   pl_barrier();
 #pragma unroll
-  for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(s0, stage_k(s0));
-  PL_WAIT_VM_LDS((STAGES - 2) * VM_STAGE);
+  for (int s0 = 0; s0 < AHEAD; ++s0) issue(s0, stage_k(s0));
+  PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
   pl_barrier();
   read_frags(0, 0, C0{});
 
-  int slot = 0;                // LDS slot of stage kt
-  int slot_prev = STAGES - 1;  // slot of stage kt-1 (= stage kt+STAGES-1)
+  int slot = 0;            // LDS slot of stage kt
+  int slot_issue = AHEAD;  // slot of stage kt + AHEAD
   for (int kt = 0; kt < nk; ++kt) {
     const int slot_next = slot + 1 == STAGES ? 0 : slot + 1;
 #pragma unroll
     for (int ks = 0; ks < SUB; ++ks) {
       const bool even = (ks & 1) == 0;
       if (ks == SUB - 1) {
-        // own loads of stage kt+1 landed and own LDS reads of stage kt done:
-        // after the barrier stage kt+1 is complete everywhere, and nobody
-        // reads the slot the next step's loads overwrite
-        PL_WAIT_VM_LDS((STAGES - 2) * VM_STAGE);
+        // own loads of stage kt+1 landed, own reads of the slot the next
+        // step refills done: after the barrier stage kt+1 is complete
+        // everywhere and nobody still reads that slot
+        if (LAG == 2)
+          PL_WAIT_VM_LDS_N((AHEAD - 1) * VM_STAGE, NREAD);
+        else
+          PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
         pl_barrier();
       }
       // read the fragments of the next substep, then the MFMAs of substep
       // ks.  In this program order both fragment groups are live at once, so
-      // they keep separate registers and the reads overlap the MFMAs (reads
-      // placed after the MFMAs let the register allocator fold the groups
-      // into one, which serialises every substep on the LDS latency).
+      // they keep separate registers (reads placed after the MFMAs let the
+      // register allocator fold the groups into one).
       if (ks + 1 < SUB) {
         if (even) read_frags(slot, ks + 1, C1{}); else read_frags(slot, ks + 1, C0{});
       } else {
         read_frags(slot_next, 0, C0{});
       }
       if (even) mfmas(C0{}); else mfmas(C1{});
-      if (ks == 0) issue(slot_prev, stage_k(kt + STAGES - 1));
-      // interleave: groups of up to 4 MFMAs, each followed by its share of
-      // the fragment reads (and, in substep 0, of the stage loads)
-      constexpr int MF = NMFMA >= 4 ? 4 : NMFMA;
-      constexpr int GROUPS = NMFMA / MF;
-      constexpr int RD = (NREAD + GROUPS - 1) / GROUPS;
-      constexpr int VM = (VM_STAGE + GROUPS - 1) / GROUPS;
+      if (ks == 0) issue(slot_issue, stage_k(kt + AHEAD));
+      // schedule: the first MFMA (its operands were read a substep ago, so
+      // its wait finds them done), then all fragment reads of the next
+      // substep, then the remaining MFMAs with the stage loads spread
+      // between them
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
 #pragma unroll
-      for (int q = 0; q < GROUPS; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-        if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
+      for (int q = 1; q < NMFMA; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ks == 0 && q <= VM_STAGE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
+      if (ks == 0 && NMFMA <= VM_STAGE)
+        __builtin_amdgcn_sched_group_barrier(0x020, VM_STAGE - NMFMA + 1, 0);
     }
-    slot_prev = slot;
     slot = slot_next;
+    slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
   }
   // the re-fetches past the end of K landed: nothing of this tile is still
   // in flight into LDS when the next tile refills the slots
