@@ -11,11 +11,11 @@
 // The logits therefore equal an fp32 GEMM up to summation order, at the
 // rate of three bf16 MFMAs instead of one fp32 MFMA of a quarter the K.
 //
-// Top-k.  s = sigmoid(l) (evaluated in fp64, rounded once to fp32),
-// s' = s + b in fp32, and the k largest s' over all E experts are chosen,
-// ties to the lower expert id, NaN below every number; the ids are written
-// in ascending order with weight rsf * s ("Module glm5next_mlp", section
-// "Numerics the kernels rely on"; Constants, KERNEL_MAX_TOP_K).  One
+// Top-k (topk.h).  s = sigmoid(l) (evaluated in fp64, rounded once to
+// fp32), s' = s + b in fp32, and the k largest s' over all E experts are
+// chosen, ties to the lower expert id, NaN below every number; the ids are
+// written in ascending order with weight rsf * s ("Module glm5next_mlp",
+// section "Numerics the kernels rely on"; Constants, KERNEL_MAX_TOP_K).  One
 // wavefront ranks one token: each lane holds up to 16 experts as 64-bit
 // keys (orderable score bits, inverted id) and k wave-wide arg-max rounds
 // pick the winners.
@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace {
 
@@ -152,29 +153,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
 }
 
-__device__ __forceinline__ float sigmoid_f32(float l) {
-  return (float)(1.0 / (1.0 + exp(-(double)l)));
-}
-
-// Total order key: larger = ranks first.  High word: the biased score's bits
-// made unsigned-orderable (NaN -> 0, below everything); low word: ~id, so on
-// equal scores the lower id wins.
-__device__ __forceinline__ uint64_t select_key(float sb, int e) {
-  uint32_t u;
-  if (sb != sb) {
-    u = 0u;
-  } else {
-    u = __float_as_uint(sb + 0.0f);  // -0 -> +0
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
-}
-
-// One wavefront per token.  Grid: ceil(T/4) workgroups of 256.  With
-// splits > 1 the logit is the sum of the K-slice partials in slice order
-// (fixed, so reruns repeat), written to `logits` for the caller.
-// TK_PER_LANE = ceil(E/64) experts per lane (a template, so the key arrays
-// stay in registers and no loop runs over absent experts).
+// One wavefront per token.  Grid: ceil(T/4) workgroups of 256.
 template <int TK_PER_LANE>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ partial, int splits, float* __restrict__ logits,
@@ -183,67 +162,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int64_t TE = T * E;
-  uint64_t key[TK_PER_LANE];
-  float lg[TK_PER_LANE];
-#pragma unroll
-  for (int i = 0; i < TK_PER_LANE; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = 0;
-    lg[i] = 0.f;
-    if (e < E) {
-      // the K-slice partials, loaded TK_SLICES at a time (one round trip
-      // for the usual slice counts), summed in slice order
-      constexpr int TK_SLICES = TK_PER_LANE <= 4 ? 16 : 64 / TK_PER_LANE;
-      float l = 0.f;
-      for (int sp0 = 0; sp0 < splits; sp0 += TK_SLICES) {
-        float pv[TK_SLICES];
-#pragma unroll
-        for (int u = 0; u < TK_SLICES; ++u)
-          pv[u] = sp0 + u < splits ? partial[(sp0 + u) * TE + t * E + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < TK_SLICES; ++u)
-          if (sp0 + u < splits) l = sp0 + u == 0 ? pv[u] : l + pv[u];
-      }
-      if (splits > 1) logits[t * E + e] = l;
-      lg[i] = l;
-      const float s = sigmoid_f32(l);
-      const float b = bias ? bias[e] : 0.0f;
-      key[i] = select_key(s + b, e);
-    }
-  }
-  int mine = -1;       // lane j < k ends up holding the j-th pick
-  float mine_l = 0.f;  // and its logit
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < TK_PER_LANE; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(~(uint32_t)best);
-    float le = 0.f;
-#pragma unroll
-    for (int i = 0; i < TK_PER_LANE; ++i) {
-      if (key[i] == best) {
-        key[i] = 0;  // taken: 0 is below every real key
-        le = lg[i];
-      }
-    }
-    le = __shfl(le, e & 63, 64);  // the owner lane of expert e holds its logit
-    if (lane == j) {
-      mine = e;
-      mine_l = le;
-    }
-  }
-  // ascending order: rank of each pick among the k picks
-  int rank = 0;
-  for (int i = 0; i < k; ++i) {
-    int other = __shfl(mine, i, 64);
-    rank += (lane < k && other < mine) ? 1 : 0;
-  }
-  if (lane < k) {
-    ids[t * k + rank] = mine;
-    wts[t * k + rank] = rsf * sigmoid_f32(mine_l);
-  }
+  int id, slot;
+  topk_token<TK_PER_LANE>(partial, splits, logits, bias, ids, wts, t, T, E, k, rsf, lane, id,
+                          slot);
 }
 
 }  // namespace
@@ -260,9 +181,9 @@ int router_splits(int64_t T, int H, int E) {
   return s < 1 ? 1 : (int)s;
 }
 
-hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, float* logits,
-                         float* partial, int32_t* ids, float* wts, int64_t T, int H, int E, int k,
-                         float rsf, hipStream_t stream) {
+static hipError_t launch_router_logits(const uint16_t* x, const float* w, float* logits,
+                                       float* partial, int64_t T, int H, int E,
+                                       hipStream_t stream) {
   const int splits = router_splits(T, H, E);
   int k_slice = (H + splits - 1) / splits;
   k_slice = (k_slice + RT_BK - 1) / RT_BK * RT_BK;
@@ -270,6 +191,16 @@ hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, f
   dim3 grid((unsigned)((T + RT_BT - 1) / RT_BT), (unsigned)((E + RT_BE - 1) / RT_BE), splits);
   hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, w, part, T, H, E,
                      k_slice);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, float* logits,
+                         float* partial, int32_t* ids, float* wts, int64_t T, int H, int E, int k,
+                         float rsf, hipStream_t stream) {
+  hipError_t e = launch_router_logits(x, w, logits, partial, T, H, E, stream);
+  if (e != hipSuccess) return e;
+  const int splits = router_splits(T, H, E);
+  float* part = splits > 1 ? partial : logits;
   const dim3 g((unsigned)((T + 3) / 4)), b(256);
   if (E <= 64)
     hipLaunchKernelGGL(router_topk_kernel<1>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
