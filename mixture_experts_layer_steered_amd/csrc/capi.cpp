@@ -95,17 +95,13 @@ struct Carver {
 // Tile variant by the mean rows per group: about one short row tile or less
 // (decode) -> persistent weight streaming; several 256-row tiles -> the
 // pipelined 256-row tiles (eight wavefronts); in between the 128-row tiles.
-// MOE_GEMM_VARIANT=wstream | tile32 | tile128 | pipe256 | pipe256w8 |
-// pipe256k64 | stream32 | stream forces one (a tuning lever; results are identical up to
-// fp32 summation order).
+// MOE_GEMM_VARIANT=wstream | tile32 | tile128 | pipe256 | pipe256w8 forces
+// one (a tuning lever; results are identical up to fp32 summation order).
 GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
   if (const char* env = std::getenv("MOE_GEMM_VARIANT")) {
     if (!std::strcmp(env, "tile32")) return GemmVariant::kTile32;
     if (!std::strcmp(env, "tile128")) return GemmVariant::kTile128;
     if (!std::strcmp(env, "pipe256")) return GemmVariant::kPipe256;
-    if (!std::strcmp(env, "pipe256k64")) return GemmVariant::kPipe256K64;
-    if (!std::strcmp(env, "stream32")) return GemmVariant::kStream32;
-    if (!std::strcmp(env, "stream")) return GemmVariant::kStream;
     if (!std::strcmp(env, "wstream")) return GemmVariant::kWStream;
     if (!std::strcmp(env, "pipe256w8")) return GemmVariant::kPipe256W8;
   }
@@ -115,21 +111,16 @@ GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
 }
 
 // The pipelined and streaming variants address A rows and one group's
-// weights with 32-bit element offsets and step K in 32-wide units (the
-// pipelined ones in whole 32- or 64-wide stages); other operands fall back
-// to the LDS-staged tiles.
+// weights with 32-bit element offsets and step K in 32-wide units; other
+// operands fall back to the LDS-staged tiles.
 GemmVariant pick_variant(int64_t rows, int64_t groups, int64_t a_elems, int64_t w_group_elems,
-                         bool k_multiple_of_32, bool k_multiple_of_64) {
+                         bool k_multiple_of_32) {
   GemmVariant v = pick_variant_raw(rows, groups);
   const int64_t lim = (int64_t)1 << 31;
   if (v == GemmVariant::kWStream && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32))
     v = GemmVariant::kTile32;
-  const bool pipe = v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64 ||
-                    v == GemmVariant::kPipe256W8;
+  const bool pipe = v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256W8;
   if (pipe && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32)) v = GemmVariant::kTile128;
-  if (v == GemmVariant::kPipe256K64 && !k_multiple_of_64) v = GemmVariant::kPipe256;
-  if (v == GemmVariant::kStream32 && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_64))
-    v = GemmVariant::kTile32;
   return v;
 }
 
@@ -351,7 +342,7 @@ moe_status moe_grouped_swiglu_gemm(int32_t n_groups, int64_t M_total, int32_t H,
   // gathered rows can repeat, the routed case), the down A is h [M_total, I].
   const GemmVariant v =
       pick_variant(M_total, n_groups, std::max<int64_t>(M_total, 1) * std::max(H, I),
-                   (int64_t)2 * I * H, H % 32 == 0 && I % 32 == 0, H % 64 == 0 && I % 64 == 0);
+                   (int64_t)2 * I * H, H % 32 == 0 && I % 32 == 0);
   int32_t* mstart = static_cast<int32_t*>(ws);
   GemmProblem gu = make_problem(a, row_index, group_offsets, mstart, w_gate_up,
                                 (int64_t)2 * I * H, h, M_total, n_groups, I, H, v, true);
@@ -439,8 +430,7 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
   const GemmVariant v = pick_variant(
       N, p->E, std::max<int64_t>(N, T) * std::max(p->H, std::max(p->I, p->I_shared)),
       (int64_t)2 * std::max(p->I, p->I_shared) * p->H,
-      p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0,
-      p->H % 64 == 0 && p->I % 64 == 0 && p->I_shared % 64 == 0);
+      p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0);
   const uint16_t* xr = x_routed;
   const uint16_t* xs = x_shared ? x_shared : x_routed;
   const bool shared = p->I_shared > 0;

@@ -208,145 +208,6 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tile, float 
   }
 }
 
-// ---------------------------------------------------------------------------
-// Weight-streaming variant, for expert segments of about one row tile or less
-// (decode): the weights are read exactly once and nothing is reused, so
-// they bypass LDS.  A workgroup owns one m-tile of up to 32 rows and 64
-// weight rows (gate_up: 32 gate + the matching 32 up rows; down: 64 output
-// columns).  Its 4 wavefronts split K into 4 contiguous ranges; each lane
-// loads 64 contiguous bytes of its row per 64-wide K chunk, two chunks per
-// iteration, straight into MFMA operand registers (A rows and weight rows
-// use the same K assignment, so the MFMA pairs matching K indices).  The
-// four partial accumulators are summed through LDS in wave order (fixed,
-// so reruns repeat), then the epilogue writes h (clamped SwiGLU) or y.
-constexpr int ST_BM = 32;   // rows per tile
-constexpr int ST_WR = 64;   // weight rows per tile (two 32-wide MFMA column tiles)
-constexpr int ST_UNROLL = 2;
-
-template <bool GATEUP>
-__device__ __forceinline__ void stream_tile(const GemmProblem& P, int tile, float limit) {
-  __shared__ float red[4][2][16][64];  // [wave][col tile][acc reg][lane]
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int mt_global = tile / P.ntiles;  // n-tiles fastest: one expert's tiles share its A rows
-  const int nt = tile % P.ntiles;
-
-  int g = 0;
-  int64_t row0, row_end;
-  if (P.group_offsets == nullptr) {
-    row0 = (int64_t)mt_global * ST_BM;
-    row_end = P.M;
-    if (row0 >= row_end) return;
-  } else {
-    if (mt_global >= P.mtile_start[P.G]) return;
-    int lo = 0, hi = P.G - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (P.mtile_start[mid] <= mt_global) lo = mid; else hi = mid - 1;
-    }
-    g = lo;
-    row0 = P.group_offsets[g] + (int64_t)(mt_global - P.mtile_start[g]) * ST_BM;
-    row_end = P.group_offsets[g + 1];
-  }
-  const int K = P.K, N = P.N;
-  const int j = lane & 31, half = lane >> 5;
-  // this lane's A row and its two weight rows
-  const int64_t r = row0 + j;
-  const uint16_t* a_row = nullptr;
-  if (r < row_end) a_row = P.A + (P.row_index ? (int64_t)P.row_index[r] : r) * K;
-  const uint16_t* __restrict__ Wg = P.W + (int64_t)g * P.w_stride;
-  const uint16_t* b_row[2];
-  int n0;
-  if (GATEUP) {
-    n0 = nt * 32;
-    const int n = n0 + j;
-    b_row[0] = n < N ? Wg + (int64_t)n * K : nullptr;         // gate row
-    b_row[1] = n < N ? Wg + (int64_t)(N + n) * K : nullptr;   // matching up row
-  } else {
-    n0 = nt * 64;
-    b_row[0] = n0 + j < N ? Wg + (int64_t)(n0 + j) * K : nullptr;
-    b_row[1] = n0 + 32 + j < N ? Wg + (int64_t)(n0 + 32 + j) * K : nullptr;
-  }
-  // K chunks of 64, split into 4 contiguous ranges
-  const int chunks = (K + 63) >> 6;
-  const int c_begin = wave * chunks / 4, c_end = (wave + 1) * chunks / 4;
-
-  f32x16_t acc[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) acc[t][q] = 0.f;
-
-  for (int c = c_begin; c < c_end; c += ST_UNROLL) {
-    uint4 av[ST_UNROLL][4], bv[ST_UNROLL][2][4];
-#pragma unroll
-    for (int u = 0; u < ST_UNROLL; ++u) {
-      const int kc = (c + u) * 64 + half * 32;
-      const bool chunk_ok = c + u < c_end;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kq = kc + q * 8;
-        const bool in = chunk_ok && kq < K;
-        av[u][q] = (in && a_row) ? *reinterpret_cast<const uint4*>(a_row + kq) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          bv[u][t][q] = (in && b_row[t]) ? *reinterpret_cast<const uint4*>(b_row[t] + kq)
-                                         : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < ST_UNROLL; ++u) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av[u][q]);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bv[u][t][q]),
-                                                          acc[t], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) red[wave][t][q][lane] = acc[t][q];
-  __syncthreads();
-
-  // element (reg q, lane l) of column tile t is row 8*(q/4) + 4*(l/32) + q%4,
-  // column (l & 31) of that tile
-  if (GATEUP) {
-    uint16_t* __restrict__ h = static_cast<uint16_t*>(P.out);
-    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-      const int q = e >> 6, l = e & 63;
-      const float gsum = red[0][0][q][l] + red[1][0][q][l] + red[2][0][q][l] + red[3][0][q][l];
-      const float usum = red[0][1][q][l] + red[1][1][q][l] + red[2][1][q][l] + red[3][1][q][l];
-      const int64_t row = row0 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
-      const int col = n0 + (l & 31);
-      if (row < row_end && col < N)
-        h[row * N + col] = (uint16_t)f32_to_bf16_bits(swiglu_clamped(gsum, usum, limit));
-    }
-  } else {
-    float* __restrict__ y = static_cast<float*>(P.out);
-    for (int e = threadIdx.x; e < 2 * 16 * 64; e += 256) {
-      const int t = e >> 10, q = (e >> 6) & 15, l = e & 63;
-      const float v = red[0][t][q][l] + red[1][t][q][l] + red[2][t][q][l] + red[3][t][q][l];
-      const int64_t row = row0 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
-      const int col = n0 + t * 32 + (l & 31);
-      if (row < row_end && col < N) y[row * N + col] = v;
-    }
-  }
-}
-
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void grouped_stream_kernel(GemmProblem p0, GemmProblem p1,
-                                                             int tiles0, float limit) {
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  if (tile < tiles0)
-    stream_tile<GATEUP>(p0, tile, limit);
-  else
-    stream_tile<GATEUP>(p1, tile - tiles0, limit);
-}
-
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void grouped_gemm_kernel(
     GemmProblem p0, GemmProblem p1, int tiles0, float limit) {
@@ -422,7 +283,7 @@ __device__ __forceinline__ int pl_swz(int row, int chunk) {
   return KB == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ ((row >> 1) & 7);
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, bool DENSE, int NW>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW>
 __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, int tile,
                                           float limit, uint16_t* smem) {
   constexpr int NB = GATEUP ? 2 * BN : BN;   // weight rows per tile
@@ -446,22 +307,13 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  int mt_global, nt;
-  if (DENSE) {
-    // tile -> (n-block, m-tile, n-tile); the last n-block may be narrower
-    const int full = mt_total * PL_NBLK;
-    const int nb = tile / full;
-    const int rem = tile - nb * full;
-    const int width = min(PL_NBLK, P.ntiles - nb * PL_NBLK);
-    mt_global = rem / width;
-    nt = nb * PL_NBLK + rem % width;
-  } else {
-    // padded tile space: n-tiles fastest (one expert's n-tiles share its A
-    // rows); m-tiles past the device-side count exit
-    mt_global = tile / P.ntiles;
-    nt = tile % P.ntiles;
-    if (mt_global >= mt_total) return;
-  }
+  // tile -> (n-block, m-tile, n-tile); the last n-block may be narrower
+  const int full = mt_total * PL_NBLK;
+  const int nb = tile / full;
+  const int rem = tile - nb * full;
+  const int width = min(PL_NBLK, P.ntiles - nb * PL_NBLK);
+  const int mt_global = rem / width;
+  const int nt = nb * PL_NBLK + rem % width;
 
   int g = 0;
   int64_t row0, row_end;
@@ -678,29 +530,11 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_pipe_kernel(GemmProblem p0
   const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
   for (int t = t_begin + lid; t < t_end; t += nwg_x) {
     if (t < tiles0)
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true, NW>(p0, mt0, t, limit, smem_dyn);
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>(p0, mt0, t, limit, smem_dyn);
     else
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, true, NW>(p1, mt1, t - tiles0, limit,
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>(p1, mt1, t - tiles0, limit,
                                                                smem_dyn);
   }
-}
-
-// Non-persistent launch of the same tile body over the padded tile space
-// (host bound on m-tiles x n-tiles per problem, XCD-remapped so each XCD
-// takes a contiguous range): for short expert segments, where a few hundred
-// tiles each stream their weights once and the hardware's dispatch of new
-// workgroups as CUs free up balances the load.
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void grouped_pipe_grid_kernel(GemmProblem p0, GemmProblem p1,
-                                                                   int tiles0, float limit) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  if (t < tiles0)
-    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false, NW>(p0, pipe_mtiles<BM>(p0), t, limit,
-                                                             smem_dyn);
-  else
-    pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, false, NW>(p1, pipe_mtiles<BM>(p1), t - tiles0,
-                                                             limit, smem_dyn);
 }
 
 // ---------------------------------------------------------------------------
@@ -1047,28 +881,6 @@ hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
   return hipGetLastError();
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW = 4>
-hipError_t launch_pipe_grid(const GemmProblem& a, const GemmProblem* b, float limit,
-                            hipStream_t stream) {
-  constexpr int NB = GATEUP ? 2 * BN : BN;
-  const size_t lds = (size_t)STAGES * (BM + NB) * KB * sizeof(uint16_t);
-  static_assert((size_t)STAGES * (BM + NB) * KB * 2 <= 160 * 1024, "LDS");
-  auto kern = grouped_pipe_grid_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int tiles0 = a.max_mtiles * a.ntiles;
-  const int total = tiles0 + (b ? b->max_mtiles * b->ntiles : 0);
-  if (total == 0) return hipSuccess;
-  const GemmProblem pb = b ? *b : a;
-  hipLaunchKernelGGL(kern, dim3(total), dim3(NW * 64), lds, stream, a, pb, tiles0, limit);
-  return hipGetLastError();
-}
-
 template <bool GATEUP, int KB, int STAGES>
 hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limit,
                           hipStream_t stream) {
@@ -1142,22 +954,17 @@ hipError_t launch_pair(const GemmProblem& a, const GemmProblem* b, float limit, 
 
 int gemm_tile_m(GemmVariant v) {
   switch (v) {
-    case GemmVariant::kStream: return ST_BM;
     case GemmVariant::kTile32: return 32;
     case GemmVariant::kTile128: return 128;
     case GemmVariant::kPipe256: return 256;
-    case GemmVariant::kPipe256K64: return 256;
     case GemmVariant::kPipe256W8: return 256;
-    case GemmVariant::kStream32: return 32;
     case GemmVariant::kWStream: return WS_BM;
   }
   return 128;
 }
 int gemm_tile_n(GemmVariant v, bool gateup) {
-  if (v == GemmVariant::kStream) return gateup ? ST_WR / 2 : ST_WR;
   if (v == GemmVariant::kWStream) return gateup ? WS_NB / 2 : WS_NB;
-  if (v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256K64 || v == GemmVariant::kStream32 ||
-      v == GemmVariant::kPipe256W8)
+  if (v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256W8)
     return gateup ? 128 : 256;
   return 128;
 }
@@ -1171,19 +978,6 @@ hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, in
 
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                const GemmProblem* b, float limit, hipStream_t stream) {
-  if (v == GemmVariant::kStream) {
-    const int tiles0 = a.max_mtiles * a.ntiles;
-    const int total = tiles0 + (b ? b->max_mtiles * b->ntiles : 0);
-    if (total == 0) return hipSuccess;
-    const GemmProblem pb = b ? *b : a;
-    if (gateup)
-      hipLaunchKernelGGL(grouped_stream_kernel<true>, dim3(total), dim3(256), 0, stream, a, pb,
-                         tiles0, limit);
-    else
-      hipLaunchKernelGGL(grouped_stream_kernel<false>, dim3(total), dim3(256), 0, stream, a, pb,
-                         tiles0, limit);
-    return hipGetLastError();
-  }
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
   if (v == GemmVariant::kWStream) {  // 512-byte row pieces, four stages
     if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream);
@@ -1193,17 +987,9 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
     if (gateup) return launch_pipe<256, 128, true, 32, 5>(a, b, limit, stream);
     return launch_pipe<256, 256, false, 32, 5>(a, b, limit, stream);
   }
-  if (v == GemmVariant::kStream32) {  // 32-row tiles, K steps of 64, three stages
-    if (gateup) return launch_pipe_grid<32, 128, true, 64, 3, 1>(a, b, limit, stream);
-    return launch_pipe_grid<32, 256, false, 64, 3, 1>(a, b, limit, stream);
-  }
   if (v == GemmVariant::kPipe256W8) {  // as kPipe256 with eight wavefronts (two per SIMD)
     if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8>(a, b, limit, stream);
     return launch_pipe<256, 256, false, 32, 5, 2, 8>(a, b, limit, stream);
-  }
-  if (v == GemmVariant::kPipe256K64) {  // K steps of 64 (128-byte rows), two stages
-    if (gateup) return launch_pipe<256, 128, true, 64, 2>(a, b, limit, stream);
-    return launch_pipe<256, 256, false, 64, 2>(a, b, limit, stream);
   }
   return launch_pair<128, 128, 2, 2>(a, b, limit, gateup, stream);
 }

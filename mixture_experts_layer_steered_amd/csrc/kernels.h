@@ -28,11 +28,9 @@ struct GemmProblem {
 
 // Tile variants of the grouped GEMM: persistent weight streaming in long
 // row pieces (short expert segments; K a multiple of 32), LDS-staged 32-row
-// and 128-row tiles, pipelined 256-row tiles with direct global->LDS loads
-// (long segments), and two earlier streaming forms kept for comparison.
-enum class GemmVariant {
-  kTile32, kTile128, kPipe256, kPipe256K64, kStream32, kStream, kWStream, kPipe256W8
-};
+// and 128-row tiles, and pipelined 256-row tiles with direct global->LDS
+// loads (long segments) in four- and eight-wavefront forms.
+enum class GemmVariant { kTile32, kTile128, kPipe256, kWStream, kPipe256W8 };
 int gemm_tile_m(GemmVariant v);
 int gemm_tile_n(GemmVariant v, bool gateup);
 
