@@ -95,18 +95,18 @@ struct Carver {
 // Tile variant by the mean rows per group: about one short row tile or less
 // (decode) -> persistent weight streaming; several 256-row tiles -> the
 // pipelined 256-row tiles (eight wavefronts); in between the 128-row tiles.
-// MOE_GEMM_VARIANT=wstream | tile32 | tile128 | pipe256 | pipe256w8 forces
+// MOE_GEMM_VARIANT=wstream | tile32 | tile128 | pipe256w8 | pingpong forces
 // one (a tuning lever; results are identical up to fp32 summation order).
 GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
   if (const char* env = std::getenv("MOE_GEMM_VARIANT")) {
     if (!std::strcmp(env, "tile32")) return GemmVariant::kTile32;
     if (!std::strcmp(env, "tile128")) return GemmVariant::kTile128;
-    if (!std::strcmp(env, "pipe256")) return GemmVariant::kPipe256;
     if (!std::strcmp(env, "wstream")) return GemmVariant::kWStream;
     if (!std::strcmp(env, "pipe256w8")) return GemmVariant::kPipe256W8;
+    if (!std::strcmp(env, "pingpong")) return GemmVariant::kPingPong;
   }
   if (rows <= 64 * groups) return GemmVariant::kWStream;
-  if (rows >= 512 * groups) return GemmVariant::kPipe256W8;
+  if (rows >= 512 * groups) return GemmVariant::kPingPong;
   return GemmVariant::kTile128;
 }
 
@@ -119,7 +119,7 @@ GemmVariant pick_variant(int64_t rows, int64_t groups, int64_t a_elems, int64_t 
   const int64_t lim = (int64_t)1 << 31;
   if (v == GemmVariant::kWStream && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32))
     v = GemmVariant::kTile32;
-  const bool pipe = v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256W8;
+  const bool pipe = v == GemmVariant::kPipe256W8 || v == GemmVariant::kPingPong;
   if (pipe && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32)) v = GemmVariant::kTile128;
   return v;
 }
@@ -213,7 +213,8 @@ GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int3
 }
 
 bool tiles_fit(const GemmProblem& a, const GemmProblem* b) {
-  // n-tiles padded to blocks of 8 (the pipelined variant's tile order)
+  // every variant's tile index (at most m-tiles x n-tiles, counted here with
+  // n-tiles rounded up to 8) stays a positive int
   auto n = [](const GemmProblem& p) { return (int64_t)p.max_mtiles * ((p.ntiles + 7) / 8 * 8); };
   const int64_t t = n(a) + (b ? n(*b) : 0);
   return t < ((int64_t)1 << 31);

@@ -7,6 +7,9 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
 #define MOE_WAVE 64
 
@@ -30,6 +33,15 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float limit) {
   g = fminf(g, limit);
   u = fminf(fmaxf(u, -limit), limit);
   return g / (1.0f + expf(-g)) * u;
+}
+
+// The same with the hardware exponential and reciprocal (about 1 ulp each):
+// e^-g = 2^(-g log2 e); a gate far below zero gives 2^+inf = inf, 1/inf = 0.
+__device__ __forceinline__ float swiglu_clamped_fast(float g, float u, float limit) {
+  g = fminf(g, limit);
+  u = fminf(fmaxf(u, -limit), limit);
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // Butterfly (xor) reductions: addition is commutative, so every lane ends

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void grouped_gemm_kernel(
     gemm_tile<BM, BN, WAVES_M, WAVES_N, GATEUP>(p1, tile - tiles0, limit);
 }
 
-constexpr int PL_NBLK = 8;
+constexpr int PL_MBLK = 8;
 
 // ---------------------------------------------------------------------------
 // Pipelined LDS-tiled variant for long expert segments (prefill).
@@ -228,31 +228,52 @@ constexpr int PL_NBLK = 8;
 // and shared problems back to back) and split into 8 equal contiguous
 // ranges, one per XCD (workgroup b runs on XCD b % 8), so every XCD gets the
 // same work and its 32 CUs work on neighbouring tiles that share A and B
-// rows in its L2.  Inside a problem tiles run n-block (8 n-tiles) major,
-// then m-tile, then n-tile.
+// rows in its L2.  Inside a problem tiles run group (expert) major, then in
+// blocks of up to 8 m-tiles, n-tile, m-tile: the m-tiles of an expert (a few
+// in prefill) that use one weight tile run side by side and read it from HBM
+// once, and an expert's weights go to one XCD.
 //
 // Workgroup tile: BM rows x BN output columns (gate_up: BN gate + BN up
-// weight rows), 4 wavefronts as 2 x 2, each owning (BM/2) x (BN/2) outputs
-// (x2 for gate/up) in 32x32 MFMA accumulators.  K advances KB at a time
-// through STAGES LDS slots filled by direct global->LDS 16-byte loads
-// (global_load_lds_dwordx4), STAGES-1 of them in flight.  A row of a stage
-// is KB*2 bytes; each load instruction writes 1 KB of LDS in lane order
-// (1024/(KB*2) whole rows), and the XOR swizzle of the 16-byte chunk slots
-// -- chosen so the 16 rows one ds_read_b128 pass touches fall in 16
-// different bank groups of the 64-bank LDS -- comes from which global chunk
-// each lane fetches.  Rows past a segment or past N fetch the tile's first
-// row (their products reach only outputs never stored).
+// weight rows), eight wavefronts as 2 x 4, each owning (BM/2) x (BN/4)
+// outputs (x2 for gate/up) in 32x32 MFMA accumulators (weight fragment as
+// the first operand, so a lane holds runs of four adjacent output columns
+// for one A row and the epilogue stores 8 or 16 bytes at a time).  K
+// advances KB at a time through STAGES LDS slots filled by direct
+// buffer->LDS 16-byte loads (buffer_load_dwordx4 ... lds), STAGES-1 of them
+// in flight.  A row of a stage is KB*2 bytes; each load instruction writes
+// 1 KB of LDS in lane order (1024/(KB*2) whole rows), and the XOR swizzle
+// of the 16-byte chunk slots -- chosen so the 16 rows one ds_read_b128 pass
+// touches fall in 16 different bank groups of the 64-bank LDS -- comes from
+// which global chunk each lane fetches.  Rows past a segment or past N
+// fetch the tile's first row (their products reach only outputs never
+// stored).
 //
-// Per step: the MFMAs of K substep s run while the fragments of substep s+1
-// are read from LDS; the loads of the stage STAGES-1 ahead go out with the
-// first substep; before the last substep each wave waits for its own loads
-// of the next stage and its own LDS reads, then a fence-free barrier makes
-// the next stage visible (its substep-0 fragments are read during the last
+// Two schedules of the same tile: interleaved (below, the else branch of
+// pipe_tile) and ping-pong (the PP branch).  Interleaved, per step: the
+// MFMAs of K substep s run while the fragments of substep s+1 are read from
+// LDS; the loads of the stage STAGES-1 ahead go out with the first substep;
+// before the last substep each wave waits for its own loads of the next
+// stage and its own LDS reads, then a fence-free barrier makes the next
+// stage visible (its substep-0 fragments are read during the last
 // substep's MFMAs).
 
 __device__ __forceinline__ void lds_direct_16(const void* g, uint16_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
                                    0, 0);
+}
+
+// Raw buffer resource over [base, base + 4 GiB): stride 0, the largest record
+// count, and the dword-3 word of CDNA's untyped buffer loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pl_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc at voff + soff bytes into LDS, lane L's bytes at
+// lds_wave_base + 16 L (buffer_load_dwordx4 ... lds)
+__device__ __forceinline__ void lds_buffer_16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                              uint32_t soff, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, soff, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) with lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] and [15:14],
@@ -283,7 +304,7 @@ __device__ __forceinline__ int pl_swz(int row, int chunk) {
   return KB == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ ((row >> 1) & 7);
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP>
 __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, int tile,
                                           float limit, uint16_t* smem) {
   constexpr int NB = GATEUP ? 2 * BN : BN;   // weight rows per tile
@@ -307,39 +328,38 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   const int wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-  // tile -> (n-block, m-tile, n-tile); the last n-block may be narrower
-  const int full = mt_total * PL_NBLK;
-  const int nb = tile / full;
-  const int rem = tile - nb * full;
-  const int width = min(PL_NBLK, P.ntiles - nb * PL_NBLK);
-  const int mt_global = rem / width;
-  const int nt = nb * PL_NBLK + rem % width;
-
-  int g = 0;
-  int64_t row0, row_end;
-  if (P.group_offsets == nullptr) {
-    row0 = (int64_t)mt_global * BM;
-    row_end = P.M;
-  } else {
-    int lo = 0, hi = P.G - 1;  // last g with mtile_start[g] <= mt_global
+  // tile -> (group, m-block, n-tile, m-tile): a group's tiles run in blocks
+  // of up to PL_MBLK m-tiles, all n-tiles of a block together, m-tiles
+  // fastest; the last block of a group may be narrower
+  int g = 0, ms = 0, mc = mt_total;
+  if (P.group_offsets != nullptr) {
+    int lo = 0, hi = P.G - 1;  // last g with mtile_start[g] * ntiles <= tile
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (P.mtile_start[mid] <= mt_global) lo = mid; else hi = mid - 1;
+      if (P.mtile_start[mid] * P.ntiles <= tile) lo = mid; else hi = mid - 1;
     }
     g = lo;
-    row0 = P.group_offsets[g] + (int64_t)(mt_global - P.mtile_start[g]) * BM;
-    row_end = P.group_offsets[g + 1];
+    ms = P.mtile_start[g];
+    mc = P.mtile_start[g + 1] - ms;
   }
+  const int local = tile - ms * P.ntiles;
+  const int blk = local / (PL_MBLK * P.ntiles);
+  const int rem = local - blk * PL_MBLK * P.ntiles;
+  const int width = min(PL_MBLK, mc - blk * PL_MBLK);
+  const int nt = rem / width;
+  const int ml = blk * PL_MBLK + rem % width;
+  const int64_t row0 = (P.group_offsets ? (int64_t)P.group_offsets[g] : 0) + (int64_t)ml * BM;
+  const int64_t row_end = P.group_offsets ? (int64_t)P.group_offsets[g + 1] : P.M;
   const int n0 = nt * BN;
   const int K = P.K, N = P.N;
-  const uint16_t* __restrict__ Wg = P.W + (int64_t)g * P.w_stride;
-  const uint16_t* __restrict__ Abase = P.A;
 
   // Instruction i of this wave fills stage rows RPI*q .. RPI*q+RPI-1 with
-  // q = wave + 4*i; lane L writes row RPI*q + L/CHUNKS, slot L%CHUNKS, which
+  // q = wave + NW*i; lane L writes row RPI*q + L/CHUNKS, slot L%CHUNKS, which
   // holds logical chunk pl_swz(row, slot) (the swizzle is an involution).
-  // Each instruction keeps a 32-bit element offset from a uniform base (A,
-  // or this group's weights; both well below 2^31 elements, the host checks).
+  // Each instruction keeps a 32-bit byte offset from a buffer resource over A
+  // or this group's weights (both below 2^31 elements, the host checks).
+  const __amdgpu_buffer_rsrc_t rs_a = pl_rsrc(P.A);
+  const __amdgpu_buffer_rsrc_t rs_w = pl_rsrc(P.W + (int64_t)g * P.w_stride);
   uint32_t off[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
@@ -348,13 +368,13 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
     if (i < A_INSTR) {
       const int64_t gr = row0 + row < row_end ? row0 + row : row0;
       const int64_t a_row = P.row_index ? (int64_t)P.row_index[gr] : gr;
-      off[i] = (uint32_t)(a_row * K + chunk * 8);
+      off[i] = (uint32_t)((a_row * K + chunk * 8) * 2);
     } else {
       const int r = row - BM;
       int n = GATEUP ? n0 + (r < BN ? r : r - BN) : n0 + r;
       const bool up = GATEUP && r >= BN;
       if (n >= N) n = n0;
-      off[i] = (uint32_t)((int64_t)(up ? N + n : n) * K + chunk * 8);
+      off[i] = (uint32_t)(((int64_t)(up ? N + n : n) * K + chunk * 8) * 2);
     }
   }
   // K is a multiple of KB here (the host only picks this variant then), so
@@ -363,7 +383,8 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
     uint16_t* base = smem + slot * STAGE;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i)
-      lds_direct_16((i < A_INSTR ? Abase : Wg) + off[i] + k0, base + (wave + NW * i) * RPI * KB);
+      lds_buffer_16(i < A_INSTR ? rs_a : rs_w, off[i], (uint32_t)k0 * 2,
+                    base + (wave + NW * i) * RPI * KB);
   };
 
   f32x16_t acc[NMAT][TM][TN];
@@ -404,107 +425,207 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[grp][i], bfr[grp][m][j],
+          acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[grp][m][j], af[grp][i],
                                                                 acc[m][i][j], 0, 0, 0);
   };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  constexpr int NREAD = TM + NMAT * TN;  // fragment reads per substep
-  constexpr int NMFMA = TM * NMAT * TN;  // MFMAs per substep
   const int nk = K / KB;
-  // Every step issues exactly one stage of loads (stages past the end
-  // re-fetch the last K step into a free slot).  With four or more slots the
-  // loads of step kt refill the slot of stage kt-2 (LAG 2), else that of
-  // stage kt-1 (LAG 1); AHEAD = STAGES - LAG stages are issued ahead of the
-  // one being read, so "stage kt+1 landed" is "at most AHEAD-1 newer stages
-  // of this wave's loads in flight".  Before the barrier of step kt each wave
-  // also finishes its reads of the slot the next step refills: with LAG 2
-  // those are all but its newest NREAD reads (the fragments of the substep
-  // still to come), so the wait does not stall on reads just issued; with
-  // LAG 1 all of them.
-  constexpr int LAG = STAGES >= 4 ? 2 : 1;
-  constexpr int AHEAD = STAGES - LAG;
   auto stage_k = [&](int s) __attribute__((always_inline)) { return min(s, nk - 1) * KB; };
+  // the wave's group (ping-pong), in a scalar register: barriers are only
+  // ever skipped by whole wavefronts
+  const int group = __builtin_amdgcn_readfirstlane(wave >> 2);
+  if constexpr (PP) {
+    // Ping-pong (eight wavefronts as two groups of four, wave w on SIMD
+    // w % 4, so each SIMD holds one wave of each group).  Group 0 owns the
+    // tile's first BM/2 rows, group 1 the rest.  A step of one group is a
+    // memory phase -- read the fragments of one K stage from LDS, issue this
+    // wave's share of the stage AHEAD = STAGES-1 ahead, wait for its own
+    // loads of the next stage -- then a barrier, then the compute phase (the
+    // stage's MFMAs from registers only), then a barrier.  Group 1 starts one
+    // barrier late, so on every SIMD one wave computes while the other reads
+    // and loads.  Stage kt+STAGES refills the slot of stage kt; its loads go
+    // out in the memory phases of step kt+1, after the barrier that ends
+    // group 1's memory phase of step kt.
+    static_assert(NW == 8 && WAVES_M == 2, "two row halves, one per group");
+    static_assert(KB == 32, "one 32-wide K stage per ping-pong step");
+    bf16x8_t fa[2][TM], fb[2][NMAT][TN];
+    auto read_stage = [&](int slot) __attribute__((always_inline)) {
+      const uint16_t* As = smem + slot * STAGE;
+      const uint16_t* Bs = As + BM * KB;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int chunk = s * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int r = wm * WM + i * 32 + (lane & 31);
+          fa[s][i] = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + pl_swz<KB>(r, chunk) * 8]);
+        }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int r = m * BN + wn * WN + j * 32 + (lane & 31);
+            fb[s][m][j] =
+                *reinterpret_cast<const bf16x8_t*>(&Bs[r * KB + pl_swz<KB>(r, chunk) * 8]);
+          }
+      }
+    };
+    // MFMA q of a stage: substep, then gate/up, then column block, then row block
+    constexpr int NQ = 2 * NMAT * TN * TM;
+    auto mfma_q = [&](int q) __attribute__((always_inline)) {
+      const int s = q / (NMAT * TN * TM), m = q / (TN * TM) % NMAT, j = q / TM % TN, i = q % TM;
+      acc[m][i][j] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][m][j], fa[s][i], acc[m][i][j], 0, 0, 0);
+    };
+    auto compute = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) mfma_q(q);
+    };
+    auto pp_barrier = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      pl_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  // every wave done reading LDS (the previous tile's last stage) before the
-  // slots are refilled.  No fence: the previous tile's loads all landed
-  // before its epilogue, and its epilogue stores drain while this tile's
-  // first stages load (they are only older entries of the vmcnt queue in the
-  // waits below)
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  pl_barrier();
+    constexpr int AHEAD = STAGES - 1;
 #pragma unroll
-  for (int s0 = 0; s0 < AHEAD; ++s0) issue(s0, stage_k(s0));
-  PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
-  pl_barrier();
-  read_frags(0, 0, C0{});
-
-  int slot = 0;            // LDS slot of stage kt
-  int slot_issue = AHEAD;  // slot of stage kt + AHEAD
-  for (int kt = 0; kt < nk; ++kt) {
-    const int slot_next = slot + 1 == STAGES ? 0 : slot + 1;
-#pragma unroll
-    for (int ks = 0; ks < SUB; ++ks) {
-      const bool even = (ks & 1) == 0;
-      if (ks == SUB - 1) {
-        // own loads of stage kt+1 landed, own reads of the slot the next
-        // step refills done: after the barrier stage kt+1 is complete
-        // everywhere and nobody still reads that slot
-        if (LAG == 2)
-          PL_WAIT_VM_LDS_N((AHEAD - 1) * VM_STAGE, NREAD);
-        else
-          PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
-        pl_barrier();
-      }
-      // read the fragments of the next substep, then the MFMAs of substep
-      // ks.  In this program order both fragment groups are live at once, so
-      // they keep separate registers (reads placed after the MFMAs let the
-      // register allocator fold the groups into one).
-      if (ks + 1 < SUB) {
-        if (even) read_frags(slot, ks + 1, C1{}); else read_frags(slot, ks + 1, C0{});
-      } else {
-        read_frags(slot_next, 0, C0{});
-      }
-      if (even) mfmas(C0{}); else mfmas(C1{});
-      if (ks == 0) issue(slot_issue, stage_k(kt + AHEAD));
-      // schedule: the first MFMA (its operands were read a substep ago, so
-      // its wait finds them done), then all fragment reads of the next
-      // substep, then the remaining MFMAs with the stage loads spread
-      // between them
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-#pragma unroll
-      for (int q = 1; q < NMFMA; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (ks == 0 && q <= VM_STAGE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      if (ks == 0 && NMFMA <= VM_STAGE)
-        __builtin_amdgcn_sched_group_barrier(0x020, VM_STAGE - NMFMA + 1, 0);
+    for (int s0 = 0; s0 < AHEAD; ++s0) issue(s0, stage_k(s0));
+    PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+    pp_barrier();  // stage 0 complete everywhere
+    if (group) pp_barrier();
+    int slot = 0, slot_issue = AHEAD;
+    for (int kt = 0; kt < nk; ++kt) {
+      read_stage(slot);
+      issue(slot_issue, stage_k(kt + AHEAD));
+      PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+      pp_barrier();
+      compute();
+      pp_barrier();
+      slot = slot + 1 == STAGES ? 0 : slot + 1;
+      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
     }
-    slot = slot_next;
-    slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
-  }
-  // the re-fetches past the end of K landed: nothing of this tile is still
-  // in flight into LDS when the next tile refills the slots
-  PL_WAIT_VM(0);
+    // Group 0 stores (below) while group 1 runs its last compute phase, then
+    // takes the barrier that pairs with group 1's last one, after which no
+    // wave reads LDS.  Re-fetches past the end of K may still be in flight:
+    // every LDS byte is written by the same wave and instruction slot in
+    // each tile, and a wave's loads complete in order, so the next tile's
+    // loads land later.
+  } else {
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    constexpr int NREAD = TM + NMAT * TN;  // fragment reads per substep
+    constexpr int NMFMA = TM * NMAT * TN;  // MFMAs per substep
+    // Every step issues exactly one stage of loads (stages past the end
+    // re-fetch the last K step into a free slot).  With four or more slots the
+    // loads of step kt refill the slot of stage kt-2 (LAG 2), else that of
+    // stage kt-1 (LAG 1); AHEAD = STAGES - LAG stages are issued ahead of the
+    // one being read, so "stage kt+1 landed" is "at most AHEAD-1 newer stages
+    // of this wave's loads in flight".  Before the barrier of step kt each wave
+    // also finishes its reads of the slot the next step refills: with LAG 2
+    // those are all but its newest NREAD reads (the fragments of the substep
+    // still to come), so the wait does not stall on reads just issued; with
+    // LAG 1 all of them.
+    constexpr int LAG = STAGES >= 4 ? 2 : 1;
+    constexpr int AHEAD = STAGES - LAG;
 
+    // every wave done reading LDS (the previous tile's last stage) before the
+    // slots are refilled.  No fence: the previous tile's loads all landed
+    // before its epilogue, and its epilogue stores drain while this tile's
+    // first stages load (they are only older entries of the vmcnt queue in the
+    // waits below)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    pl_barrier();
+  #pragma unroll
+    for (int s0 = 0; s0 < AHEAD; ++s0) issue(s0, stage_k(s0));
+    PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+    pl_barrier();
+    read_frags(0, 0, C0{});
+
+    int slot = 0;            // LDS slot of stage kt
+    int slot_issue = AHEAD;  // slot of stage kt + AHEAD
+    for (int kt = 0; kt < nk; ++kt) {
+      const int slot_next = slot + 1 == STAGES ? 0 : slot + 1;
+  #pragma unroll
+      for (int ks = 0; ks < SUB; ++ks) {
+        const bool even = (ks & 1) == 0;
+        if (ks == SUB - 1) {
+          // own loads of stage kt+1 landed, own reads of the slot the next
+          // step refills done: after the barrier stage kt+1 is complete
+          // everywhere and nobody still reads that slot
+          if (LAG == 2)
+            PL_WAIT_VM_LDS_N((AHEAD - 1) * VM_STAGE, NREAD);
+          else
+            PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+          pl_barrier();
+        }
+        // read the fragments of the next substep, then the MFMAs of substep
+        // ks.  In this program order both fragment groups are live at once, so
+        // they keep separate registers (reads placed after the MFMAs let the
+        // register allocator fold the groups into one).
+        if (ks + 1 < SUB) {
+          if (even) read_frags(slot, ks + 1, C1{}); else read_frags(slot, ks + 1, C0{});
+        } else {
+          read_frags(slot_next, 0, C0{});
+        }
+        if (even) mfmas(C0{}); else mfmas(C1{});
+        if (ks == 0) issue(slot_issue, stage_k(kt + AHEAD));
+        // schedule: the first MFMA (its operands were read a substep ago, so
+        // its wait finds them done), then all fragment reads of the next
+        // substep, then the remaining MFMAs with the stage loads spread
+        // between them
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
+  #pragma unroll
+        for (int q = 1; q < NMFMA; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ks == 0 && q <= VM_STAGE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        if (ks == 0 && NMFMA <= VM_STAGE)
+          __builtin_amdgcn_sched_group_barrier(0x020, VM_STAGE - NMFMA + 1, 0);
+      }
+      slot = slot_next;
+      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
+    }
+    // the re-fetches past the end of K landed: nothing of this tile is still
+    // in flight into LDS when the next tile refills the slots
+    PL_WAIT_VM(0);
+  }
+
+  // Epilogue.  The weight fragment is the MFMA's first operand, so an
+  // accumulator is a 32 (weight rows) x 32 (A rows) block: lane L holds A
+  // row L % 32 and weight rows 8*(r/4) + 4*(L/32) + r%4, i.e. four runs of
+  // four adjacent output columns -- 8-byte (h) or 16-byte (y) stores.  N is
+  // a multiple of 32 here, so a run is either wholly inside N or past it.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int64_t row = row0 + wm * WM + i * 32 + (lane & 31);
+    if (row >= row_end) continue;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + (lane & 31);
-      if (col >= N) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= row_end) continue;
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (col >= N) continue;
+        const f32x16_t& g = acc[0][i][j];
         if (GATEUP) {
-          const float hv = swiglu_clamped(acc[0][i][j][r], acc[NMAT - 1][i][j][r], limit);
-          static_cast<uint16_t*>(P.out)[row * N + col] = (uint16_t)f32_to_bf16_bits(hv);
+          const f32x16_t& u = acc[NMAT - 1][i][j];
+          float2_t h01 = {swiglu_clamped_fast(g[4 * q], u[4 * q], limit),
+                          swiglu_clamped_fast(g[4 * q + 1], u[4 * q + 1], limit)};
+          float2_t h23 = {swiglu_clamped_fast(g[4 * q + 2], u[4 * q + 2], limit),
+                          swiglu_clamped_fast(g[4 * q + 3], u[4 * q + 3], limit)};
+          uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
+                        __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
+          *reinterpret_cast<uint2_t*>(static_cast<uint16_t*>(P.out) + row * N + col) = pk;
         } else {
-          static_cast<float*>(P.out)[row * N + col] = acc[0][i][j][r];
+          f32x4_t v = {g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(P.out) + row * N + col) = v;
         }
       }
+    }
+  }
+  if constexpr (PP) {
+    if (group == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      pl_barrier();
     }
   }
 }
@@ -514,7 +635,7 @@ __device__ __forceinline__ int pipe_mtiles(const GemmProblem& P) {
   return P.group_offsets ? P.mtile_start[P.G] : (int)((P.M + BM - 1) / BM);
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP>
 __global__ __launch_bounds__(NW * 64, 1) void grouped_pipe_kernel(GemmProblem p0, GemmProblem p1,
                                                               int has_p1, float limit) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
@@ -530,10 +651,10 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_pipe_kernel(GemmProblem p0
   const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
   for (int t = t_begin + lid; t < t_end; t += nwg_x) {
     if (t < tiles0)
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>(p0, mt0, t, limit, smem_dyn);
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW, PP>(p0, mt0, t, limit, smem_dyn);
     else
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>(p1, mt1, t - tiles0, limit,
-                                                               smem_dyn);
+      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW, PP>(p1, mt1, t - tiles0, limit,
+                                                                   smem_dyn);
   }
 }
 
@@ -861,13 +982,13 @@ int device_cu_count() {
   return cached;
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M = 2, int NW = 4>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP>
 hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
                        hipStream_t stream) {
   constexpr int NB = GATEUP ? 2 * BN : BN;
   const size_t lds = (size_t)STAGES * (BM + NB) * KB * sizeof(uint16_t);
   static_assert((size_t)STAGES * (BM + NB) * KB * 2 <= 160 * 1024, "LDS");
-  auto kern = grouped_pipe_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW>;
+  auto kern = grouped_pipe_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW, PP>;
   static bool attr_set = false;  // raise the dynamic LDS limit once per process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -956,15 +1077,15 @@ int gemm_tile_m(GemmVariant v) {
   switch (v) {
     case GemmVariant::kTile32: return 32;
     case GemmVariant::kTile128: return 128;
-    case GemmVariant::kPipe256: return 256;
     case GemmVariant::kPipe256W8: return 256;
+    case GemmVariant::kPingPong: return 256;
     case GemmVariant::kWStream: return WS_BM;
   }
   return 128;
 }
 int gemm_tile_n(GemmVariant v, bool gateup) {
   if (v == GemmVariant::kWStream) return gateup ? WS_NB / 2 : WS_NB;
-  if (v == GemmVariant::kPipe256 || v == GemmVariant::kPipe256W8)
+  if (v == GemmVariant::kPipe256W8 || v == GemmVariant::kPingPong)
     return gateup ? 128 : 256;
   return 128;
 }
@@ -983,13 +1104,13 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
     if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream);
     return launch_wstream<false, 256, 4>(a, b, limit, stream);
   }
-  if (v == GemmVariant::kPipe256) {  // K steps of 32, five stages
-    if (gateup) return launch_pipe<256, 128, true, 32, 5>(a, b, limit, stream);
-    return launch_pipe<256, 256, false, 32, 5>(a, b, limit, stream);
+  if (v == GemmVariant::kPipe256W8) {  // eight wavefronts, two per SIMD, interleaved
+    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false>(a, b, limit, stream);
+    return launch_pipe<256, 256, false, 32, 5, 2, 8, false>(a, b, limit, stream);
   }
-  if (v == GemmVariant::kPipe256W8) {  // as kPipe256 with eight wavefronts (two per SIMD)
-    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8>(a, b, limit, stream);
-    return launch_pipe<256, 256, false, 32, 5, 2, 8>(a, b, limit, stream);
+  if (v == GemmVariant::kPingPong) {  // eight wavefronts taking turns on each SIMD
+    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, true>(a, b, limit, stream);
+    return launch_pipe<256, 256, false, 32, 5, 2, 8, true>(a, b, limit, stream);
   }
   return launch_pair<128, 128, 2, 2>(a, b, limit, gateup, stream);
 }

@@ -28,9 +28,10 @@ struct GemmProblem {
 
 // Tile variants of the grouped GEMM: persistent weight streaming in long
 // row pieces (short expert segments; K a multiple of 32), LDS-staged 32-row
-// and 128-row tiles, and pipelined 256-row tiles with direct global->LDS
-// loads (long segments) in four- and eight-wavefront forms.
-enum class GemmVariant { kTile32, kTile128, kPipe256, kWStream, kPipe256W8 };
+// and 128-row tiles, and pipelined 256-row tiles with direct buffer->LDS
+// loads (long segments), eight wavefronts either interleaved or taking turns
+// on each SIMD (ping-pong).
+enum class GemmVariant { kTile32, kTile128, kWStream, kPipe256W8, kPingPong };
 int gemm_tile_m(GemmVariant v);
 int gemm_tile_n(GemmVariant v, bool gateup);
 

@@ -161,7 +161,7 @@ def test_forward_zipf_full_sampled():
     assert rep["max_over_mean_count"] > 4
 
 
-@pytest.mark.parametrize("variant", ["wstream", "tile32", "tile128", "pipe256", "pipe256w8"])
+@pytest.mark.parametrize("variant", ["wstream", "tile32", "tile128", "pipe256w8", "pingpong"])
 @pytest.mark.parametrize("name", ["medium_ragged", "decode_small", "scmoe_gamma", "prefill_small",
                                   "pipe_small", "stream_small", "stream_multi"])
 def test_forward_every_tile_variant(monkeypatch, variant, name):
@@ -169,7 +169,7 @@ def test_forward_every_tile_variant(monkeypatch, variant, name):
     a parity-green layer; the automatic choice is only a speed decision."""
     monkeypatch.setenv("MOE_GEMM_VARIANT", variant)
     wl = SMALL[name]
-    step = {"pipe256": 32, "pipe256w8": 32, "wstream": 32}.get(variant)
+    step = {"pipe256w8": 32, "pingpong": 32, "wstream": 32}.get(variant)
     if step and (wl.H % step or wl.I % step or wl.I_s % step):
         pytest.skip(f"the pipelined tiles step K in whole {step}-wide stages")
     run_and_check(wl, moe_inputs.generate(wl, seed=1))
