@@ -304,33 +304,53 @@ __device__ __forceinline__ int pl_swz(int row, int chunk) {
   return KB == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ ((row >> 1) & 7);
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP>
-__device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, int tile,
-                                          float limit, uint16_t* smem) {
-  constexpr int NB = GATEUP ? 2 * BN : BN;   // weight rows per tile
-  constexpr int ROWS = BM + NB;              // LDS rows per stage
-  constexpr int CHUNKS = KB / 8;             // 16-byte chunks per row
-  constexpr int STAGE = ROWS * KB;           // bf16 elements per stage
-  constexpr int RPI = 64 / CHUNKS;           // rows per 1 KB load instruction
-  constexpr int INSTR = ROWS / RPI;          // load instructions per stage
-  constexpr int PER_WAVE = INSTR / NW;
-  constexpr int WAVES_N = NW / WAVES_M;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int NMAT = GATEUP ? 2 : 1;
-  constexpr int SUB = KB / 16;               // MFMA K substeps per stage
+// Compile-time shape of the pipelined tile.
+template <int BM_, int BN_, bool GATEUP_, int KB_, int NW_, int WAVES_M_>
+struct PipeShape {
+  static constexpr int BM = BM_, BN = BN_, KB = KB_, NW = NW_, WAVES_M = WAVES_M_;
+  static constexpr bool GATEUP = GATEUP_;
+  static constexpr int NB = GATEUP ? 2 * BN : BN;  // weight rows per tile
+  static constexpr int ROWS = BM + NB;             // LDS rows per stage
+  static constexpr int CHUNKS = KB / 8;            // 16-byte chunks per row
+  static constexpr int STAGE = ROWS * KB;          // bf16 elements per stage
+  static constexpr int RPI = 64 / CHUNKS;          // rows per 1 KB load instruction
+  static constexpr int INSTR = ROWS / RPI;         // load instructions per stage
+  static constexpr int PER_WAVE = INSTR / NW;      // of them per wavefront
+  static constexpr int WAVES_N = NW / WAVES_M;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int NMAT = GATEUP ? 2 : 1;
+  static constexpr int SUB = KB / 16;              // MFMA K substeps per stage
+  static constexpr int A_INSTR = BM / (NW * RPI);  // instructions of each wave that fill A rows
   static_assert(INSTR % NW == 0 && SUB % 2 == 0, "shape");
-  constexpr int A_INSTR = BM / (NW * RPI);   // instructions of each wave that fill A rows
   static_assert(BM % (NW * RPI) == 0, "A rows fill whole instructions of every wave");
-  constexpr int VM_STAGE = PER_WAVE;         // vector memory instructions per stage per wave
+};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+// One output tile as one wavefront sees it: rows [row0, row_end) of its
+// problem (one group's segment), output columns from n0, and the per-lane
+// byte offsets of this wave's load instructions from two buffer resources
+// (A, and this group's weights).
+template <class S>
+struct PipeTile {
+  int64_t row0, row_end;
+  int n0;
+  __amdgpu_buffer_rsrc_t rs_a, rs_w;
+  uint32_t off[S::PER_WAVE];
+};
 
-  // tile -> (group, m-block, n-tile, m-tile): a group's tiles run in blocks
-  // of up to PL_MBLK m-tiles, all n-tiles of a block together, m-tiles
-  // fastest; the last block of a group may be narrower
+// Tile t of a problem with mt_total m-tiles.  Tile order: group (expert)
+// major, then blocks of up to PL_MBLK m-tiles, n-tile, m-tile (the last
+// block of a group may be narrower).  Instruction i of wave w fills stage
+// rows RPI*q .. RPI*q+RPI-1 with q = w + NW*i; lane L writes row
+// RPI*q + L/CHUNKS, slot L%CHUNKS, which holds logical chunk pl_swz(row,
+// slot) (the swizzle is an involution).  Rows past the segment or past N
+// fetch the tile's first row (their products reach only outputs never
+// stored).  Offsets are 32-bit: A and one group's weights hold fewer than
+// 2^31 elements (the host checks).
+template <class S>
+__device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, int tile,
+                                            PipeTile<S>& T) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int g = 0, ms = 0, mc = mt_total;
   if (P.group_offsets != nullptr) {
     int lo = 0, hi = P.G - 1;  // last g with mtile_start[g] * ntiles <= tile
@@ -348,54 +368,119 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   const int width = min(PL_MBLK, mc - blk * PL_MBLK);
   const int nt = rem / width;
   const int ml = blk * PL_MBLK + rem % width;
-  const int64_t row0 = (P.group_offsets ? (int64_t)P.group_offsets[g] : 0) + (int64_t)ml * BM;
-  const int64_t row_end = P.group_offsets ? (int64_t)P.group_offsets[g + 1] : P.M;
-  const int n0 = nt * BN;
+  T.row0 = (P.group_offsets ? (int64_t)P.group_offsets[g] : 0) + (int64_t)ml * S::BM;
+  T.row_end = P.group_offsets ? (int64_t)P.group_offsets[g + 1] : P.M;
+  T.n0 = nt * S::BN;
+  T.rs_a = pl_rsrc(P.A);
+  T.rs_w = pl_rsrc(P.W + (int64_t)g * P.w_stride);
   const int K = P.K, N = P.N;
-
-  // Instruction i of this wave fills stage rows RPI*q .. RPI*q+RPI-1 with
-  // q = wave + NW*i; lane L writes row RPI*q + L/CHUNKS, slot L%CHUNKS, which
-  // holds logical chunk pl_swz(row, slot) (the swizzle is an involution).
-  // Each instruction keeps a 32-bit byte offset from a buffer resource over A
-  // or this group's weights (both below 2^31 elements, the host checks).
-  const __amdgpu_buffer_rsrc_t rs_a = pl_rsrc(P.A);
-  const __amdgpu_buffer_rsrc_t rs_w = pl_rsrc(P.W + (int64_t)g * P.w_stride);
-  uint32_t off[PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int row = RPI * (wave + NW * i) + lane / CHUNKS;
-    const int chunk = pl_swz<KB>(row, lane % CHUNKS);
-    if (i < A_INSTR) {
-      const int64_t gr = row0 + row < row_end ? row0 + row : row0;
+  for (int i = 0; i < S::PER_WAVE; ++i) {
+    const int row = S::RPI * (wave + S::NW * i) + lane / S::CHUNKS;
+    const int chunk = pl_swz<S::KB>(row, lane % S::CHUNKS);
+    if (i < S::A_INSTR) {
+      const int64_t gr = T.row0 + row < T.row_end ? T.row0 + row : T.row0;
       const int64_t a_row = P.row_index ? (int64_t)P.row_index[gr] : gr;
-      off[i] = (uint32_t)((a_row * K + chunk * 8) * 2);
+      T.off[i] = (uint32_t)((a_row * K + chunk * 8) * 2);
     } else {
-      const int r = row - BM;
-      int n = GATEUP ? n0 + (r < BN ? r : r - BN) : n0 + r;
-      const bool up = GATEUP && r >= BN;
-      if (n >= N) n = n0;
-      off[i] = (uint32_t)(((int64_t)(up ? N + n : n) * K + chunk * 8) * 2);
+      const int r = row - S::BM;
+      int n = S::GATEUP ? T.n0 + (r < S::BN ? r : r - S::BN) : T.n0 + r;
+      const bool up = S::GATEUP && r >= S::BN;
+      if (n >= N) n = T.n0;
+      T.off[i] = (uint32_t)(((int64_t)(up ? N + n : n) * K + chunk * 8) * 2);
     }
   }
-  // K is a multiple of KB here (the host only picks this variant then), so
-  // every stage is whole and the loads need no predicate.
-  auto issue = [&](int slot, int k0) __attribute__((always_inline)) {
-    uint16_t* base = smem + slot * STAGE;
+}
+
+// This wave's loads of the K columns [k0, k0 + KB) of tile T into LDS slot
+// `slot` (K is a multiple of KB here, so every stage is whole).
+template <class S>
+__device__ __forceinline__ void pipe_issue(const PipeTile<S>& T, uint16_t* smem, int slot,
+                                           int k0) {
+  const int wave = threadIdx.x >> 6;
+  uint16_t* base = smem + slot * S::STAGE;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      lds_buffer_16(i < A_INSTR ? rs_a : rs_w, off[i], (uint32_t)k0 * 2,
-                    base + (wave + NW * i) * RPI * KB);
+  for (int i = 0; i < S::PER_WAVE; ++i)
+    lds_buffer_16(i < S::A_INSTR ? T.rs_a : T.rs_w, T.off[i], (uint32_t)k0 * 2,
+                  base + (wave + S::NW * i) * S::RPI * S::KB);
+}
+
+// Epilogue.  The weight fragment is the MFMA's first operand, so an
+// accumulator is a 32 (weight rows) x 32 (A rows) block: lane L holds A row
+// L % 32 and weight rows 8*(r/4) + 4*(L/32) + r%4, i.e. four runs of four
+// adjacent output columns -- 8-byte (h) or 16-byte (y) stores.  N is a
+// multiple of 32 here, so a run is either wholly inside N or past it.
+template <class S>
+__device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<S>& T,
+                                           const f32x16_t (&acc)[S::NMAT][S::TM][S::TN],
+                                           float limit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
+  const int N = P.N;
+#pragma unroll
+  for (int i = 0; i < S::TM; ++i) {
+    const int64_t row = T.row0 + wm * S::WM + i * 32 + (lane & 31);
+    if (row >= T.row_end) continue;
+#pragma unroll
+    for (int j = 0; j < S::TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = T.n0 + wn * S::WN + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (col >= N) continue;
+        const f32x16_t& g = acc[0][i][j];
+        if (S::GATEUP) {
+          const f32x16_t& u = acc[S::NMAT - 1][i][j];
+          float2_t h01 = {swiglu_clamped_fast(g[4 * q], u[4 * q], limit),
+                          swiglu_clamped_fast(g[4 * q + 1], u[4 * q + 1], limit)};
+          float2_t h23 = {swiglu_clamped_fast(g[4 * q + 2], u[4 * q + 2], limit),
+                          swiglu_clamped_fast(g[4 * q + 3], u[4 * q + 3], limit)};
+          uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
+                        __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
+          *reinterpret_cast<uint2_t*>(static_cast<uint16_t*>(P.out) + row * N + col) = pk;
+        } else {
+          f32x4_t v = {g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(P.out) + row * N + col) = v;
+        }
+      }
+    }
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void pipe_zero(f32x16_t (&acc)[S::NMAT][S::TM][S::TN]) {
+#pragma unroll
+  for (int m = 0; m < S::NMAT; ++m)
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
+}
+
+// One tile, interleaved schedule (both wavefronts of a SIMD read fragments
+// and issue MFMAs; one barrier per stage).
+template <class S, int STAGES>
+__device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, int tile,
+                                          float limit, uint16_t* smem) {
+  constexpr int BM = S::BM, BN = S::BN, KB = S::KB;
+  constexpr int STAGE = S::STAGE, TM = S::TM, TN = S::TN, NMAT = S::NMAT, SUB = S::SUB;
+  constexpr int WM = S::WM, WN = S::WN;
+  constexpr int VM_STAGE = S::PER_WAVE;  // vector memory instructions per stage per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
+
+  PipeTile<S> T;
+  pipe_locate<S>(P, mt_total, tile, T);
+  const int nk = P.K / KB;
+  auto stage_k = [&](int s) __attribute__((always_inline)) { return min(s, nk - 1) * KB; };
+  auto issue = [&](int slot, int k0) __attribute__((always_inline)) {
+    pipe_issue<S>(T, smem, slot, k0);
   };
 
   f32x16_t acc[NMAT][TM][TN];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
+  pipe_zero<S>(acc);
 
   // MFMA fragments of one 16-wide K substep, two groups (substeps alternate)
   bf16x8_t af[2][TM], bfr[2][NMAT][TN];
@@ -428,206 +513,85 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
           acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[grp][m][j], af[grp][i],
                                                                 acc[m][i][j], 0, 0, 0);
   };
-  const int nk = K / KB;
-  auto stage_k = [&](int s) __attribute__((always_inline)) { return min(s, nk - 1) * KB; };
-  // the wave's group (ping-pong), in a scalar register: barriers are only
-  // ever skipped by whole wavefronts
-  const int group = __builtin_amdgcn_readfirstlane(wave >> 2);
-  if constexpr (PP) {
-    // Ping-pong (eight wavefronts as two groups of four, wave w on SIMD
-    // w % 4, so each SIMD holds one wave of each group).  Group 0 owns the
-    // tile's first BM/2 rows, group 1 the rest.  A step of one group is a
-    // memory phase -- read the fragments of one K stage from LDS, issue this
-    // wave's share of the stage AHEAD = STAGES-1 ahead, wait for its own
-    // loads of the next stage -- then a barrier, then the compute phase (the
-    // stage's MFMAs from registers only), then a barrier.  Group 1 starts one
-    // barrier late, so on every SIMD one wave computes while the other reads
-    // and loads.  Stage kt+STAGES refills the slot of stage kt; its loads go
-    // out in the memory phases of step kt+1, after the barrier that ends
-    // group 1's memory phase of step kt.
-    static_assert(NW == 8 && WAVES_M == 2, "two row halves, one per group");
-    static_assert(KB == 32, "one 32-wide K stage per ping-pong step");
-    bf16x8_t fa[2][TM], fb[2][NMAT][TN];
-    auto read_stage = [&](int slot) __attribute__((always_inline)) {
-      const uint16_t* As = smem + slot * STAGE;
-      const uint16_t* Bs = As + BM * KB;
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  constexpr int NREAD = TM + NMAT * TN;  // fragment reads per substep
+  constexpr int NMFMA = TM * NMAT * TN;  // MFMAs per substep
+  // Every step issues exactly one stage of loads (stages past the end
+  // re-fetch the last K step into a free slot).  With four or more slots the
+  // loads of step kt refill the slot of stage kt-2 (LAG 2), else that of
+  // stage kt-1 (LAG 1); AHEAD = STAGES - LAG stages are issued ahead of the
+  // one being read, so "stage kt+1 landed" is "at most AHEAD-1 newer stages
+  // of this wave's loads in flight".  Before the barrier of step kt each wave
+  // also finishes its reads of the slot the next step refills: with LAG 2
+  // those are all but its newest NREAD reads (the fragments of the substep
+  // still to come), so the wait does not stall on reads just issued; with
+  // LAG 1 all of them.
+  constexpr int LAG = STAGES >= 4 ? 2 : 1;
+  constexpr int AHEAD = STAGES - LAG;
+
+  // every wave done reading LDS (the previous tile's last stage) before the
+  // slots are refilled.  No fence: the previous tile's loads all landed
+  // before its epilogue, and its epilogue stores drain while this tile's
+  // first stages load (they are only older entries of the vmcnt queue in the
+  // waits below)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  pl_barrier();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int chunk = s * 2 + (lane >> 5);
+  for (int s0 = 0; s0 < AHEAD; ++s0) issue(s0, stage_k(s0));
+  PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+  pl_barrier();
+  read_frags(0, 0, C0{});
+
+  int slot = 0;            // LDS slot of stage kt
+  int slot_issue = AHEAD;  // slot of stage kt + AHEAD
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot_next = slot + 1 == STAGES ? 0 : slot + 1;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = wm * WM + i * 32 + (lane & 31);
-          fa[s][i] = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + pl_swz<KB>(r, chunk) * 8]);
-        }
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int r = m * BN + wn * WN + j * 32 + (lane & 31);
-            fb[s][m][j] =
-                *reinterpret_cast<const bf16x8_t*>(&Bs[r * KB + pl_swz<KB>(r, chunk) * 8]);
-          }
+    for (int ks = 0; ks < SUB; ++ks) {
+      const bool even = (ks & 1) == 0;
+      if (ks == SUB - 1) {
+        // own loads of stage kt+1 landed, own reads of the slot the next
+        // step refills done: after the barrier stage kt+1 is complete
+        // everywhere and nobody still reads that slot
+        if (LAG == 2)
+          PL_WAIT_VM_LDS_N((AHEAD - 1) * VM_STAGE, NREAD);
+        else
+          PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+        pl_barrier();
       }
-    };
-    // MFMA q of a stage: substep, then gate/up, then column block, then row block
-    constexpr int NQ = 2 * NMAT * TN * TM;
-    auto mfma_q = [&](int q) __attribute__((always_inline)) {
-      const int s = q / (NMAT * TN * TM), m = q / (TN * TM) % NMAT, j = q / TM % TN, i = q % TM;
-      acc[m][i][j] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][m][j], fa[s][i], acc[m][i][j], 0, 0, 0);
-    };
-    auto compute = [&]() __attribute__((always_inline)) {
+      // read the fragments of the next substep, then the MFMAs of substep
+      // ks.  In this program order both fragment groups are live at once, so
+      // they keep separate registers (reads placed after the MFMAs let the
+      // register allocator fold the groups into one).
+      if (ks + 1 < SUB) {
+        if (even) read_frags(slot, ks + 1, C1{}); else read_frags(slot, ks + 1, C0{});
+      } else {
+        read_frags(slot_next, 0, C0{});
+      }
+      if (even) mfmas(C0{}); else mfmas(C1{});
+      if (ks == 0) issue(slot_issue, stage_k(kt + AHEAD));
+      // schedule: the first MFMA (its operands were read a substep ago, so
+      // its wait finds them done), then all fragment reads of the next
+      // substep, then the remaining MFMAs with the stage loads spread
+      // between them
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) mfma_q(q);
-    };
-    auto pp_barrier = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-      pl_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
-    constexpr int AHEAD = STAGES - 1;
-#pragma unroll
-    for (int s0 = 0; s0 < AHEAD; ++s0) issue(s0, stage_k(s0));
-    PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
-    pp_barrier();  // stage 0 complete everywhere
-    if (group) pp_barrier();
-    int slot = 0, slot_issue = AHEAD;
-    for (int kt = 0; kt < nk; ++kt) {
-      read_stage(slot);
-      issue(slot_issue, stage_k(kt + AHEAD));
-      PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
-      pp_barrier();
-      compute();
-      pp_barrier();
-      slot = slot + 1 == STAGES ? 0 : slot + 1;
-      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
-    }
-    // Group 0 stores (below) while group 1 runs its last compute phase, then
-    // takes the barrier that pairs with group 1's last one, after which no
-    // wave reads LDS.  Re-fetches past the end of K may still be in flight:
-    // every LDS byte is written by the same wave and instruction slot in
-    // each tile, and a wave's loads complete in order, so the next tile's
-    // loads land later.
-  } else {
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    constexpr int NREAD = TM + NMAT * TN;  // fragment reads per substep
-    constexpr int NMFMA = TM * NMAT * TN;  // MFMAs per substep
-    // Every step issues exactly one stage of loads (stages past the end
-    // re-fetch the last K step into a free slot).  With four or more slots the
-    // loads of step kt refill the slot of stage kt-2 (LAG 2), else that of
-    // stage kt-1 (LAG 1); AHEAD = STAGES - LAG stages are issued ahead of the
-    // one being read, so "stage kt+1 landed" is "at most AHEAD-1 newer stages
-    // of this wave's loads in flight".  Before the barrier of step kt each wave
-    // also finishes its reads of the slot the next step refills: with LAG 2
-    // those are all but its newest NREAD reads (the fragments of the substep
-    // still to come), so the wait does not stall on reads just issued; with
-    // LAG 1 all of them.
-    constexpr int LAG = STAGES >= 4 ? 2 : 1;
-    constexpr int AHEAD = STAGES - LAG;
-
-    // every wave done reading LDS (the previous tile's last stage) before the
-    // slots are refilled.  No fence: the previous tile's loads all landed
-    // before its epilogue, and its epilogue stores drain while this tile's
-    // first stages load (they are only older entries of the vmcnt queue in the
-    // waits below)
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    pl_barrier();
-  #pragma unroll
-    for (int s0 = 0; s0 < AHEAD; ++s0) issue(s0, stage_k(s0));
-    PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
-    pl_barrier();
-    read_frags(0, 0, C0{});
-
-    int slot = 0;            // LDS slot of stage kt
-    int slot_issue = AHEAD;  // slot of stage kt + AHEAD
-    for (int kt = 0; kt < nk; ++kt) {
-      const int slot_next = slot + 1 == STAGES ? 0 : slot + 1;
-  #pragma unroll
-      for (int ks = 0; ks < SUB; ++ks) {
-        const bool even = (ks & 1) == 0;
-        if (ks == SUB - 1) {
-          // own loads of stage kt+1 landed, own reads of the slot the next
-          // step refills done: after the barrier stage kt+1 is complete
-          // everywhere and nobody still reads that slot
-          if (LAG == 2)
-            PL_WAIT_VM_LDS_N((AHEAD - 1) * VM_STAGE, NREAD);
-          else
-            PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
-          pl_barrier();
-        }
-        // read the fragments of the next substep, then the MFMAs of substep
-        // ks.  In this program order both fragment groups are live at once, so
-        // they keep separate registers (reads placed after the MFMAs let the
-        // register allocator fold the groups into one).
-        if (ks + 1 < SUB) {
-          if (even) read_frags(slot, ks + 1, C1{}); else read_frags(slot, ks + 1, C0{});
-        } else {
-          read_frags(slot_next, 0, C0{});
-        }
-        if (even) mfmas(C0{}); else mfmas(C1{});
-        if (ks == 0) issue(slot_issue, stage_k(kt + AHEAD));
-        // schedule: the first MFMA (its operands were read a substep ago, so
-        // its wait finds them done), then all fragment reads of the next
-        // substep, then the remaining MFMAs with the stage loads spread
-        // between them
+      for (int q = 1; q < NMFMA; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);
-  #pragma unroll
-        for (int q = 1; q < NMFMA; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (ks == 0 && q <= VM_STAGE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        if (ks == 0 && NMFMA <= VM_STAGE)
-          __builtin_amdgcn_sched_group_barrier(0x020, VM_STAGE - NMFMA + 1, 0);
+        if (ks == 0 && q <= VM_STAGE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      slot = slot_next;
-      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
+      if (ks == 0 && NMFMA <= VM_STAGE)
+        __builtin_amdgcn_sched_group_barrier(0x020, VM_STAGE - NMFMA + 1, 0);
     }
-    // the re-fetches past the end of K landed: nothing of this tile is still
-    // in flight into LDS when the next tile refills the slots
-    PL_WAIT_VM(0);
+    slot = slot_next;
+    slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
   }
-
-  // Epilogue.  The weight fragment is the MFMA's first operand, so an
-  // accumulator is a 32 (weight rows) x 32 (A rows) block: lane L holds A
-  // row L % 32 and weight rows 8*(r/4) + 4*(L/32) + r%4, i.e. four runs of
-  // four adjacent output columns -- 8-byte (h) or 16-byte (y) stores.  N is
-  // a multiple of 32 here, so a run is either wholly inside N or past it.
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int64_t row = row0 + wm * WM + i * 32 + (lane & 31);
-    if (row >= row_end) continue;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (col >= N) continue;
-        const f32x16_t& g = acc[0][i][j];
-        if (GATEUP) {
-          const f32x16_t& u = acc[NMAT - 1][i][j];
-          float2_t h01 = {swiglu_clamped_fast(g[4 * q], u[4 * q], limit),
-                          swiglu_clamped_fast(g[4 * q + 1], u[4 * q + 1], limit)};
-          float2_t h23 = {swiglu_clamped_fast(g[4 * q + 2], u[4 * q + 2], limit),
-                          swiglu_clamped_fast(g[4 * q + 3], u[4 * q + 3], limit)};
-          uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
-                        __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
-          *reinterpret_cast<uint2_t*>(static_cast<uint16_t*>(P.out) + row * N + col) = pk;
-        } else {
-          f32x4_t v = {g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(P.out) + row * N + col) = v;
-        }
-      }
-    }
-  }
-  if constexpr (PP) {
-    if (group == 0) {
-      __builtin_amdgcn_sched_barrier(0);
-      pl_barrier();
-    }
-  }
+  // the re-fetches past the end of K landed: nothing of this tile is still
+  // in flight into LDS when the next tile refills the slots
+  PL_WAIT_VM(0);
+  pipe_store<S>(P, T, acc, limit);
 }
 
 template <int BM>
@@ -635,27 +599,173 @@ __device__ __forceinline__ int pipe_mtiles(const GemmProblem& P) {
   return P.group_offsets ? P.mtile_start[P.G] : (int)((P.M + BM - 1) / BM);
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP>
-__global__ __launch_bounds__(NW * 64, 1) void grouped_pipe_kernel(GemmProblem p0, GemmProblem p1,
-                                                              int has_p1, float limit) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
-  const int mt0 = pipe_mtiles<BM>(p0);
-  const int mt1 = has_p1 ? pipe_mtiles<BM>(p1) : 0;
-  const int tiles0 = mt0 * p0.ntiles;
-  const int total = tiles0 + mt1 * p1.ntiles;
-  // equal contiguous tile ranges per XCD; this XCD's workgroups stride it
+// Persistent: one workgroup per CU.  The real tile count is read on the
+// device (m-tile prefix x n-tiles, routed and shared problems back to back)
+// and split into 8 equal contiguous ranges, one per XCD (workgroup b runs on
+// XCD b % 8); the XCD's workgroups stride its range.
+struct PipeRange {
+  int mt0, mt1, tiles0, t_first, t_end, stride;
+};
+template <int BM>
+__device__ __forceinline__ PipeRange pipe_range(const GemmProblem& p0, const GemmProblem& p1,
+                                                int has_p1) {
+  PipeRange R;
+  R.mt0 = pipe_mtiles<BM>(p0);
+  R.mt1 = has_p1 ? pipe_mtiles<BM>(p1) : 0;
+  R.tiles0 = R.mt0 * p0.ntiles;
+  const int total = R.tiles0 + R.mt1 * p1.ntiles;
   const int nwg = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, lid = b >> 3;
-  const int nwg_x = (nwg - xcd + 7) >> 3;
-  const int t_begin = (int)((int64_t)total * xcd / 8);
-  const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
-  for (int t = t_begin + lid; t < t_end; t += nwg_x) {
-    if (t < tiles0)
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW, PP>(p0, mt0, t, limit, smem_dyn);
+  R.stride = (nwg - xcd + 7) >> 3;
+  R.t_first = (int)((int64_t)total * xcd / 8) + lid;
+  R.t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  return R;
+}
+
+template <class S, int STAGES>
+__global__ __launch_bounds__(S::NW * 64, 1) void grouped_pipe_kernel(GemmProblem p0,
+                                                                     GemmProblem p1, int has_p1,
+                                                                     float limit) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+  const PipeRange R = pipe_range<S::BM>(p0, p1, has_p1);
+  for (int t = R.t_first; t < R.t_end; t += R.stride) {
+    if (t < R.tiles0)
+      pipe_tile<S, STAGES>(p0, R.mt0, t, limit, smem_dyn);
     else
-      pipe_tile<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW, PP>(p1, mt1, t - tiles0, limit,
-                                                                   smem_dyn);
+      pipe_tile<S, STAGES>(p1, R.mt1, t - R.tiles0, limit, smem_dyn);
   }
+}
+
+// Ping-pong schedule of the same tile (eight wavefronts as two groups of
+// four, wave w on SIMD w % 4, so each SIMD holds one wave of each group).
+// Group 0 owns the tile's first BM/2 rows, group 1 the rest.  A step of one
+// group is a memory phase -- read the fragments of one K stage from LDS,
+// issue this wave's share of the stage AHEAD = STAGES-1 ahead, wait for its
+// own loads of the next stage -- then a barrier, then the compute phase (the
+// stage's MFMAs from registers only), then a barrier.  Group 1 runs one
+// barrier behind group 0 for the whole launch, so on every SIMD one wave
+// computes while the other reads and loads.
+//
+// The stage stream runs on across the workgroup's tiles: the last AHEAD
+// steps of a tile issue the first stages of its next tile (whose place is
+// computed at the tile's start), so a new tile starts on landed data and
+// the epilogue of one group overlaps the other group's compute phase.  Stage
+// s of the stream uses slot s % STAGES; stage s+STAGES refills the slot of
+// stage s, and its loads go out in the memory phases of step s+1, after the
+// barrier that ends group 1's memory phase of step s.  Every step issues one
+// stage (past the last tile, the last stage again), so "the next stage
+// landed" is always "at most AHEAD-1 newer stages of this wave's loads in
+// flight" -- epilogue stores between them only make that wait stricter.
+// Needs K >= AHEAD * KB for every problem (the host checks).
+template <class S, int STAGES>
+__global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p0, GemmProblem p1,
+                                                                   int has_p1, float limit) {
+  static_assert(S::NW == 8 && S::WAVES_M == 2, "two row halves, one per group");
+  static_assert(S::KB == 32, "one 32-wide K stage per step");
+  constexpr int KB = S::KB, BM = S::BM, BN = S::BN, STAGE = S::STAGE;
+  constexpr int TM = S::TM, TN = S::TN, NMAT = S::NMAT, WM = S::WM, WN = S::WN;
+  constexpr int AHEAD = STAGES - 1, VM_STAGE = S::PER_WAVE;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+  uint16_t* smem = smem_dyn;
+  const PipeRange R = pipe_range<BM>(p0, p1, has_p1);
+  int t = R.t_first;
+  if (t >= R.t_end) return;  // no tile for this workgroup (uniform)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
+  // the wave's group in a scalar register: barriers are only ever skipped
+  // by whole wavefronts
+  const int group = __builtin_amdgcn_readfirstlane(wave >> 2);
+
+  auto locate = [&](int tt, PipeTile<S>& T) __attribute__((always_inline)) {
+    if (tt < R.tiles0)
+      pipe_locate<S>(p0, R.mt0, tt, T);
+    else
+      pipe_locate<S>(p1, R.mt1, tt - R.tiles0, T);
+  };
+  auto stages_of = [&](int tt) __attribute__((always_inline)) {
+    return (tt < R.tiles0 ? p0.K : p1.K) / KB;
+  };
+
+  f32x16_t acc[NMAT][TM][TN];
+  bf16x8_t fa[2][TM], fb[2][NMAT][TN];
+  auto read_stage = [&](int slot) __attribute__((always_inline)) {
+    const uint16_t* As = smem + slot * STAGE;
+    const uint16_t* Bs = As + BM * KB;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int chunk = s * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 32 + (lane & 31);
+        fa[s][i] = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + pl_swz<KB>(r, chunk) * 8]);
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int r = m * BN + wn * WN + j * 32 + (lane & 31);
+          fb[s][m][j] = *reinterpret_cast<const bf16x8_t*>(&Bs[r * KB + pl_swz<KB>(r, chunk) * 8]);
+        }
+    }
+  };
+  auto compute = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            acc[m][i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][m][j], fa[s][i], acc[m][i][j], 0, 0, 0);
+  };
+  auto pp_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    pl_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  PipeTile<S> cur, nxt;
+  locate(t, cur);
+  int nk = stages_of(t);
+#pragma unroll
+  for (int s0 = 0; s0 < AHEAD; ++s0) pipe_issue<S>(cur, smem, s0, s0 * KB);
+  PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+  pp_barrier();  // stage 0 complete everywhere
+  if (group) pp_barrier();
+  int slot = 0, slot_issue = AHEAD;
+  for (;;) {
+    const int t_next = t + R.stride;
+    const bool more = t_next < R.t_end;
+    if (more) locate(t_next, nxt);
+    pipe_zero<S>(acc);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_stage(slot);
+      const int ka = kt + AHEAD;
+      if (ka < nk)
+        pipe_issue<S>(cur, smem, slot_issue, ka * KB);
+      else if (more)
+        pipe_issue<S>(nxt, smem, slot_issue, (ka - nk) * KB);
+      else
+        pipe_issue<S>(cur, smem, slot_issue, (nk - 1) * KB);
+      PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+      pp_barrier();
+      compute();
+      pp_barrier();
+      slot = slot + 1 == STAGES ? 0 : slot + 1;
+      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
+    }
+    pipe_store<S>(t < R.tiles0 ? p0 : p1, cur, acc, limit);
+    if (!more) break;
+    t = t_next;
+    nk = stages_of(t);
+    cur = nxt;
+  }
+  // pairs with group 1's last barrier
+  if (group == 0) pp_barrier();
 }
 
 // ---------------------------------------------------------------------------
@@ -985,10 +1095,14 @@ int device_cu_count() {
 template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP>
 hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
                        hipStream_t stream) {
-  constexpr int NB = GATEUP ? 2 * BN : BN;
-  const size_t lds = (size_t)STAGES * (BM + NB) * KB * sizeof(uint16_t);
-  static_assert((size_t)STAGES * (BM + NB) * KB * 2 <= 160 * 1024, "LDS");
-  auto kern = grouped_pipe_kernel<BM, BN, GATEUP, KB, STAGES, WAVES_M, NW, PP>;
+  using S = PipeShape<BM, BN, GATEUP, KB, NW, WAVES_M>;
+  const size_t lds = (size_t)STAGES * S::STAGE * sizeof(uint16_t);
+  static_assert((size_t)STAGES * S::STAGE * 2 <= 160 * 1024, "LDS");
+  void (*kern)(GemmProblem, GemmProblem, int, float);
+  if constexpr (PP)
+    kern = grouped_pp_kernel<S, STAGES>;
+  else
+    kern = grouped_pipe_kernel<S, STAGES>;
   static bool attr_set = false;  // raise the dynamic LDS limit once per process
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1109,6 +1223,12 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
     return launch_pipe<256, 256, false, 32, 5, 2, 8, false>(a, b, limit, stream);
   }
   if (v == GemmVariant::kPingPong) {  // eight wavefronts taking turns on each SIMD
+    // the cross-tile stage stream needs at least STAGES-1 = 4 stages per tile;
+    // shorter K takes the interleaved schedule of the same tile
+    if (a.K < 4 * 32 || (b != nullptr && b->K < 4 * 32)) {
+      if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false>(a, b, limit, stream);
+      return launch_pipe<256, 256, false, 32, 5, 2, 8, false>(a, b, limit, stream);
+    }
     if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, true>(a, b, limit, stream);
     return launch_pipe<256, 256, false, 32, 5, 2, 8, true>(a, b, limit, stream);
   }
