@@ -13,12 +13,15 @@ top-8, I=1408, shared I_s=2816), which is bound by HBM bandwidth; the
 prefill, zipf and scmoe workloads (bound by the bf16 matrix cores) can be
 asked for with --workload.
 
-roofline: the dominant kernel is the grouped gate_up launch (routed and
-shared experts in one launch).  Its average duration is measured live with
-HIP events recorded by moe_forward itself on its stream at the boundaries
-of that step, over every timed step.  Algorithmic work per launch:
+roofline: the dominant kernel is the grouped gate_up launch.  With few
+rows per expert (HBM-bound, weight streaming) it holds the routed experts
+only: moe_forward runs the shared expert on a second stream beside the
+routing kernels.  Otherwise routed and shared experts share the launch.
+Its average duration is measured live with HIP events recorded by
+moe_forward itself on its stream at the boundaries of that step, over every
+timed step.  Algorithmic work per launch:
   HBM-bound:  bytes = sum over touched experts of 2*I*H*2 (gate/up weights)
-              + 2*I_s*H*2 (shared) + T*H*2 (x) + (T*k*I + T*I_s)*2 (h out)
+              + T*H*2 (x) + T*k*I*2 (h out)
   MFMA-bound: flops = 2*T*k*H*2I + 2*T*H*2I_s
 traffic: FETCH_SIZE + WRITE_SIZE per launch from the committed rocprofv3
 counter summary of that kernel, when it was taken on the current kernel
@@ -144,12 +147,19 @@ def _is_gate_up(name: str) -> bool:
     return "grouped_" in name and ("<true" in name or ", true" in name)
 
 
-def _counter_means(csv_path: str, counter: str, select) -> tuple[float, int]:
+def _counter_means(csv_path: str, counter: str, select, full_grid: bool = False
+                   ) -> tuple[float, int]:
     """Mean of one rocprofv3 counter (CSV output) over the dispatches of the
-    kernels that `select` accepts by name."""
+    kernels that `select` accepts by name (with full_grid, only those with the
+    largest grid among them: the routed launch, not the shared expert's
+    narrower one on the second stream)."""
     import csv
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+    rows = [r for r in csv.DictReader(open(csv_path))
             if r["Counter_Name"] == counter and select(r["Kernel_Name"])]
+    if full_grid and rows:
+        g = max(int(r["Grid_Size"]) for r in rows)
+        rows = [r for r in rows if int(r["Grid_Size"]) == g]
+    vals = [float(r["Counter_Value"]) for r in rows]
     if not vals:
         raise SystemExit(f"no {counter} rows for the selected kernels in {csv_path}")
     return sum(vals) / len(vals), len(vals)
@@ -165,15 +175,15 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: 
     source hash so that bench.py drops it once the kernel changes."""
     import moe_inputs
     wl = moe_inputs.WORKLOADS[workload]
-    f_kib, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_gate_up)
-    w_kib, nw = _counter_means(write_csv, "WRITE_SIZE", _is_gate_up)
+    f_kib, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_gate_up, full_grid=True)
+    w_kib, nw = _counter_means(write_csv, "WRITE_SIZE", _is_gate_up, full_grid=True)
     cf_kib, _ = _counter_means(cal_fetch_csv, "FETCH_SIZE", lambda n: "neg" in n)
     cw_kib, _ = _counter_means(cal_write_csv, "WRITE_SIZE", lambda n: "neg" in n)
     gib = float(1 << 30)
     f_scale, w_scale = gib / (cf_kib * 1024.0), gib / (cw_kib * 1024.0)
     fetch_b = f_kib * 1024.0 * f_scale
     write_b = w_kib * 1024.0 * w_scale
-    out = {"workload": wl.label(), "kernel": "grouped gate_up + SwiGLU",
+    out = {"workload": wl.label(), "kernel": "grouped gate_up + SwiGLU (routed experts)",
            "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
            "dispatches": [nf, nw],
            "copy_calibration": {"kernel": "torch.neg fp32, 1 GiB in, 1 GiB out",
@@ -282,20 +292,20 @@ def main() -> int:
         hip.destroy(b)
 
     # algorithmic work of the dominant launch and of the whole layer
-    gu_weight_bytes = touched * 2 * I * H * 2 + 2 * Is * H * 2
-    gu_bytes = gu_weight_bytes + T * H * 2 + (T * k * I + T * Is) * 2
+    hbm_bound = wl.T * k <= 64 * E   # about a row tile per expert or less: weight streaming
+    gu_bytes = touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
     gu_flops = 2 * T * k * H * 2 * I + 2 * T * H * 2 * Is
     layer_bytes = (touched * 3 * I * H * 2 + 3 * Is * H * 2 + E * H * 4 + E * 4 + T * H * 2
                    * (2 if wl.scmoe else 1) + T * H * 2)
     layer_flops = 2 * T * k * H * 3 * I + 2 * T * H * 3 * Is
     router_flops = 2 * T * H * E
-    hbm_bound = wl.T * k <= 64 * E   # about a row tile per expert or less: weight streaming
     traffic = committed_traffic(wl.label())
     if hbm_bound:
         achieved = gu_bytes / (gate_up_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": "grouped gate_up + SwiGLU (routed + shared, one launch)",
+                    "kernel": "grouped gate_up + SwiGLU (routed experts; the shared expert "
+                              "runs beside the routing kernels on a second stream)",
                     "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": round(gate_up_ms, 5)}
     else:
         achieved = gu_flops / (gate_up_ms * 1e-3) / 1e12

@@ -51,8 +51,10 @@
  *     floating-point atomics anywhere).
  *   - Device pointers must be 16-byte aligned; H, I and I_shared must be
  *     multiples of 8.  T == 0 is a successful no-op.
- *   - Functions are reentrant; the only library state is the per-thread
- *     error text.
+ *   - Functions are reentrant.  Library state: the per-thread error text,
+ *     and, per thread and device, one extra stream with two events that
+ *     moe_forward creates on its first call that needs them (see there) and
+ *     keeps until the process ends.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -235,6 +237,15 @@ moe_status moe_combine(const moe_params* p, const float* y_perm, const float* to
  *             plain layer; required with ScMoE (the current layer's hidden)
  *   w         weights;  out [T, H] bf16;  probes NULL or optional outputs
  *   ws        >= moe_workspace_size(p) bytes
+ * With a few rows per expert (T*k <= 64*E: the expert GEMMs stream weights)
+ * and a shared expert, the shared expert's two GEMMs run on the calling
+ * thread's second stream for the current device: forked from `stream` at
+ * the start (event record + wait), on 3/4 of the CUs beside the routing
+ * kernels, and joined back into `stream` before the combine.  Work is still
+ * ordered after everything enqueued on `stream` before the call and before
+ * everything enqueued after it, and graph capture on `stream` captures both
+ * branches; make the first such call outside a capture (it creates the
+ * stream and events).
  * Sources: all of the above; "Module glm5next_mlp", Modules forward. */
 moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
                        const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,

@@ -1,6 +1,8 @@
 // Host side of the C ABI declared in include/moe.h: argument validation,
 // workspace carving and launch sequencing.  Nothing here allocates device
-// memory or synchronises; every kernel goes onto the caller's stream.
+// memory or synchronises.  Every kernel goes onto the caller's stream,
+// except that moe_forward runs a weight-streaming shared expert on a second
+// stream of its own, forked from and joined back into the caller's stream.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
@@ -184,6 +186,38 @@ size_t permute_ws_bytes(const moe_params& p) {
   c.take<int32_t>((size_t)tiles * p.E);
   c.take<int32_t>((size_t)tiles * p.E);
   return c.off;
+}
+
+// A second stream and two events per thread and device.  moe_forward runs
+// the shared expert on it beside the routing kernels when the grouped GEMMs
+// stream weights (a few rows per expert): the routing launches are
+// latency-bound and occupy few CUs while the shared weights are a fixed
+// share of the bytes.  Created on first use (so not during a graph capture
+// that starts with the first call), default priority, kept until the
+// process ends.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+
+moe_status side_stream(SideStream** out) {
+  thread_local SideStream per_device[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_DEVICE, "no usable current device (%d)", dev);
+  SideStream& S = per_device[dev];
+  if (S.stream == nullptr) {
+    SideStream n;
+    if (hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) != hipSuccess)
+      return fail(MOE_ERR_DEVICE, "second stream: %s", hipGetErrorString(hipGetLastError()));
+    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess)
+      return fail(MOE_ERR_DEVICE, "stream events: %s", hipGetErrorString(hipGetLastError()));
+    S = n;
+  }
+  *out = &S;
+  return MOE_OK;
 }
 
 moe_status device_status(hipError_t e, const char* what) {
@@ -448,12 +482,32 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
   if (!tiles_fit(gu, shared ? &sgu : nullptr) || !tiles_fit(dn, shared ? &sdn : nullptr))
     return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");
 
+  // Weight streaming (decode-sized batches): the shared expert's two GEMMs
+  // run on the second stream, forked at the start, on 3/4 of the CUs, while
+  // the routing kernels run on the rest; the combine waits for them.
+  const bool beside = shared && v == GemmVariant::kWStream;
+  SideStream* side = nullptr;
+  if (beside && (s = side_stream(&side)) != MOE_OK) return s;
+
   auto mark = [&](int ev) -> moe_status {
     if (probes && probes->events[ev])
       return device_status(hipEventRecord(probes->events[ev], stream), "event record");
     return MOE_OK;
   };
   if ((s = mark(MOE_EV_BEGIN)) != MOE_OK) return s;
+  if (beside) {
+    const int wgs = std::max(8, gemm_cu_count() * 3 / 4 / 8 * 8);
+    if ((s = device_status(hipEventRecord(side->fork, stream), "fork")) != MOE_OK ||
+        (s = device_status(hipStreamWaitEvent(side->stream, side->fork, 0), "fork")) != MOE_OK ||
+        (s = device_status(launch_grouped_gemm(v, true, sgu, nullptr, p->swiglu_limit,
+                                               side->stream, wgs),
+                           "shared gate_up")) != MOE_OK ||
+        (s = device_status(launch_grouped_gemm(v, false, sdn, nullptr, p->swiglu_limit,
+                                               side->stream, wgs),
+                           "shared down")) != MOE_OK ||
+        (s = device_status(hipEventRecord(side->join, side->stream), "join")) != MOE_OK)
+      return s;
+  }
   if (p->scmoe) {
     if ((s = device_status(launch_rmsnorm_bf16(x_routed, w->gamma_pre, L.xr, T, p->H, p->norm_eps,
                                                stream),
@@ -475,16 +529,20 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
                          "permute")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_PERMUTE)) != MOE_OK) return s;
-  if ((s = device_status(launch_grouped_gemm(v, true, gu, shared ? &sgu : nullptr,
+  const bool one_launch = shared && !beside;  // routed and shared problems together
+  if ((s = device_status(launch_grouped_gemm(v, true, gu, one_launch ? &sgu : nullptr,
                                              p->swiglu_limit, stream),
                          "gate_up")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_GATE_UP)) != MOE_OK) return s;
-  if ((s = device_status(launch_grouped_gemm(v, false, dn, shared ? &sdn : nullptr,
+  if ((s = device_status(launch_grouped_gemm(v, false, dn, one_launch ? &sdn : nullptr,
                                              p->swiglu_limit, stream),
                          "down")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_DOWN)) != MOE_OK) return s;
+  if (beside &&
+      (s = device_status(hipStreamWaitEvent(stream, side->join, 0), "join")) != MOE_OK)
+    return s;
   if ((s = device_status(launch_combine(L.y, L.w, L.inv_pos, shared ? L.ys : nullptr,
                                         w->gamma_post, out, T, p->H, p->k, p->scmoe, p->norm_eps,
                                         stream),

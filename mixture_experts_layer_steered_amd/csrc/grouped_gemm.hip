@@ -28,6 +28,7 @@
 // exits when past the end.  Workgroup ids are remapped so each of the 8 XCDs
 // works a contiguous range of tiles, m-tiles fastest: consecutive tiles on an
 // XCD share one weight n-tile in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -1118,7 +1119,7 @@ hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
 
 template <bool GATEUP, int KB, int STAGES>
 hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limit,
-                          hipStream_t stream) {
+                          hipStream_t stream, int max_wgs) {
   const size_t lds = (size_t)STAGES * (WS_BM + WS_NB) * KB * sizeof(uint16_t);
   static_assert((size_t)STAGES * (WS_BM + WS_NB) * KB * 2 <= 160 * 1024, "LDS");
   auto kern = grouped_wstream_kernel<GATEUP, KB, STAGES>;
@@ -1130,8 +1131,9 @@ hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limi
     attr_set = true;
   }
   const GemmProblem pb = b ? *b : a;
-  hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3(256), lds, stream, a, pb, b ? 1 : 0,
-                     limit);
+  // one resident workgroup per CU, or fewer to leave CUs to concurrent work
+  const int grid = max_wgs > 0 ? std::min(max_wgs, device_cu_count()) : device_cu_count();
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a, pb, b ? 1 : 0, limit);
   return hipGetLastError();
 }
 
@@ -1187,6 +1189,8 @@ hipError_t launch_pair(const GemmProblem& a, const GemmProblem* b, float limit, 
 
 }  // namespace
 
+int gemm_cu_count() { return device_cu_count(); }
+
 int gemm_tile_m(GemmVariant v) {
   switch (v) {
     case GemmVariant::kTile32: return 32;
@@ -1212,11 +1216,12 @@ hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, in
 }
 
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
-                               const GemmProblem* b, float limit, hipStream_t stream) {
+                               const GemmProblem* b, float limit, hipStream_t stream,
+                               int max_wgs) {
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
   if (v == GemmVariant::kWStream) {  // 512-byte row pieces, four stages
-    if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream);
-    return launch_wstream<false, 256, 4>(a, b, limit, stream);
+    if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream, max_wgs);
+    return launch_wstream<false, 256, 4>(a, b, limit, stream, max_wgs);
   }
   if (v == GemmVariant::kPipe256W8) {  // eight wavefronts, two per SIMD, interleaved
     if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false>(a, b, limit, stream);

@@ -55,8 +55,12 @@ hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_token, ui
 
 hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
                                 int32_t* start0, int32_t* start1, hipStream_t stream);
+// max_wgs > 0 caps the persistent weight-streaming grid (default: one
+// workgroup per CU), leaving CUs to work on another stream.
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
-                               const GemmProblem* b, float limit, hipStream_t stream);
+                               const GemmProblem* b, float limit, hipStream_t stream,
+                               int max_wgs = 0);
+int gemm_cu_count();  // compute units of the current device
 
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, const float* gamma, uint16_t* out, int64_t T,
                                int H, float eps, hipStream_t stream);

@@ -173,3 +173,34 @@ def test_forward_every_tile_variant(monkeypatch, variant, name):
     if step and (wl.H % step or wl.I % step or wl.I_s % step):
         pytest.skip(f"the pipelined tiles step K in whole {step}-wide stages")
     run_and_check(wl, moe_inputs.generate(wl, seed=1))
+
+
+@pytest.mark.parametrize("name", ["decode_small", "stream_small"])
+def test_forward_graph_replay_matches_eager(name):
+    """moe_forward captured into a HIP graph (the weight-streaming path forks
+    the shared expert onto a second stream and joins it back) replays to the
+    eager result, bit for bit, several times with eager work in between."""
+    torch, moe = gh.torch_and_lib()
+    wl = SMALL[name]
+    gh.note(f"graph replay {wl.label()}")
+    d = gh.Device(wl, moe_inputs.generate(wl, seed=2))
+    d.run()  # eager, outside the capture (also creates the second stream)
+    eager = gh.to_bits(d.out).copy()
+    out_g = torch.empty_like(d.out)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_forward(d.params, d.x, d.x_cur, d.weights, out_g, None, d.ws)  # warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        moe.moe_forward(d.params, d.x, d.x_cur, d.weights, out_g, None, d.ws)
+    for rep in range(3):
+        out_g.fill_(0x7FC0)
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gh.to_bits(out_g), eager, err_msg=f"replay {rep}")
+        d.run()  # eager work between replays
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gh.to_bits(d.out), eager)
