@@ -18,12 +18,19 @@ is synthetic):
   scmoe    T=8192  H=4096 E=128 k=8 I=1024 I_s=2048 rsf=1.0 L=7.0,
            two inputs (preceding-layer and current hidden), RMSNorm
            eps 1e-6 before routing and after the merge
+  decode_w4  the decode shape with W4A16 routed experts (below)
 
 Distributions: activations bf16 N(0,1); expert and shared weights bf16
 N(0,0.02); router weights fp32 N(0,0.02); correction bias fp32
 U(-0.1,0.1); RMSNorm gains 1 (or 1+U(-j,j) when a jitter j is asked).
 bf16 tensors are held as uint16 bit patterns (round-to-nearest-even of
 the fp32 draw).
+
+W4A16 routed experts (workloads with w4): per weight a uniform nibble u in
+[0, 15] (two per byte, low nibble = even column; the value is u - 8), and
+per row and group of 128 columns a bf16 scale weight_std / sqrt(21.5) *
+U(0.5, 1.5) (21.5 is the mean of (u - 8)^2), stored [K/128, rows]; so the
+weights have about the bf16 experts' spread.  The shared expert stays bf16.
 
 Random streams: numpy PCG64 children of SeedSequence(seed), spawned in a
 fixed order: x (x_prev for ScMoE), x_cur, W_r, b, W_gu[e] for e=0..E-1,
@@ -59,6 +66,7 @@ class Workload:
     zipf_s: float = 0.0      # 0 = router rows unscaled
     weight_std: float = WEIGHT_STD
     gamma_jitter: float = 0.0
+    w4: bool = False         # routed experts in W4A16 form
 
     def label(self) -> str:
         s = (f"{self.name}_T{self.T}_H{self.H}_E{self.E}_k{self.k}"
@@ -77,7 +85,11 @@ WORKLOADS = {
                      rsf=2.5, zipf_s=1.1),
     "scmoe": Workload("scmoe", T=8192, H=4096, E=128, k=8, I=1024, I_s=2048,
                       scmoe=True, eps=1e-6),
+    "decode_w4": Workload("decode_w4", T=32, H=4096, E=64, k=8, I=1408, I_s=2816, w4=True),
 }
+
+W4_GROUP = 128
+W4_CODE_RMS = float(np.sqrt(21.5))  # RMS of u - 8 over uniform u in [0, 15]
 
 
 def _threads() -> int:
@@ -112,6 +124,16 @@ def _normal_bf16(seq: np.random.SeedSequence, shape, std: float) -> np.ndarray:
     return f32_to_bf16_bits(v).reshape(shape)
 
 
+def _w4_matrix(g: np.random.Generator, R: int, K: int, std: float) -> tuple[np.ndarray, np.ndarray]:
+    """One W4A16 matrix [R, K]: packed nibbles uint8 [R, K/2] and bf16
+    scale bits [K/128, R]."""
+    q = g.integers(0, 256, size=(R, K // 2), dtype=np.uint8)
+    groups = (K + W4_GROUP - 1) // W4_GROUP
+    sc = g.uniform(0.5, 1.5, size=(groups, R)).astype(np.float32)
+    sc *= np.float32(std / W4_CODE_RMS)
+    return q, f32_to_bf16_bits(sc)
+
+
 def zipf_row_scales(E: int, s: float, perm: np.ndarray) -> np.ndarray:
     """Per-expert router-row scales (pi(e)+1)^-s * sqrt(E / sum_j (j+1)^-2s).
 
@@ -134,6 +156,8 @@ def generate(w: Workload, seed: int = 0, *, T: int | None = None,
       corr_bias    float32 [E]
       w_gate_up    uint16 [E,2I,H]  gate rows [0,I), up rows [I,2I)
       w_down       uint16 [E,H,I]
+        or, with w4: w_gate_up_q uint8 [E,2I,H/2], w_gate_up_scale uint16
+        [E,H/128,2I], w_down_q uint8 [E,H,I/2], w_down_scale uint16 [E,I/128,H]
       ws_gate_up   uint16 [2I_s,H]  (absent when I_s == 0)
       ws_down      uint16 [H,I_s]
       gamma_pre    float32 [H]   (ScMoE only)
@@ -166,7 +190,23 @@ def generate(w: Workload, seed: int = 0, *, T: int | None = None,
     g = np.random.Generator(np.random.PCG64(k_b))
     out["corr_bias"] = g.uniform(-BIAS_RANGE, BIAS_RANGE, E).astype(np.float32)
 
-    if experts:
+    if experts and w.w4:
+        gq = np.empty((E, 2 * I, H // 2), dtype=np.uint8)
+        gs = np.empty((E, (H + W4_GROUP - 1) // W4_GROUP, 2 * I), dtype=np.uint16)
+        dq = np.empty((E, H, I // 2), dtype=np.uint8)
+        ds = np.empty((E, (I + W4_GROUP - 1) // W4_GROUP, H), dtype=np.uint16)
+
+        def one_w4(e):
+            gq[e], gs[e] = _w4_matrix(np.random.Generator(np.random.PCG64(k_gu[e])), 2 * I, H,
+                                      w.weight_std)
+            dq[e], ds[e] = _w4_matrix(np.random.Generator(np.random.PCG64(k_d[e])), H, I,
+                                      w.weight_std)
+
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(one_w4, range(E)))
+        out["w_gate_up_q"], out["w_gate_up_scale"] = gq, gs
+        out["w_down_q"], out["w_down_scale"] = dq, ds
+    elif experts:
         wgu = np.empty((E, 2 * I, H), dtype=np.uint16)
         wd = np.empty((E, H, I), dtype=np.uint16)
 

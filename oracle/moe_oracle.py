@@ -56,6 +56,15 @@ ScMoE pre-norm output and at the final output; bf16(v) of a float64 value
 is round-to-nearest-even of its fp32 rounding; eps is the fp32 value the
 caller passes, widened.
 
+W4A16 routed experts (optional, the next step after the bf16 path): the
+pages name a grouped W4A16 expert GEMM ("Module glm5next_mlp", Modules
+forward_prefill_gemm and Constants MOE_GROUPED_MODULE / W4A16_GEMV_MODULE)
+but not its format.  The reading taken here: signed 4-bit integers in
+offset-binary nibbles (u - 8), two per byte along K (low nibble first),
+one bf16 scale per output row and group of 128 columns, stored group-major
+([K/128, rows]); the weight is exactly (u - 8) * scale and the expert FFN
+then runs as above on those values.  The shared expert stays bf16.
+
 Precision: all sums in float64 (BLAS matmul as a step), single roundings
 at the points named above.  bf16 tensors are uint16 bit patterns.
 """
@@ -194,6 +203,46 @@ def permute(ids: np.ndarray, E: int) -> dict:
                 counts=counts.astype(np.int64))
 
 
+# ------------------------------------------- W4A16 expert weights ----
+
+W4_GROUP = 128
+
+
+def dequant_w4(q: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """W4A16 weights -> float64 values (exact).
+
+    q      uint8 [R, K/2]: byte j holds column 2j (low nibble) and column
+           2j+1 (high nibble); a nibble u stands for the integer u - 8
+    scale  bf16 [ceil(K/128), R]: one scale per row and group of 128 columns
+    Returns w [R, K] with w[r, c] = (u[r, c] - 8) * scale[c // 128, r].
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    R, half = q.shape
+    K = 2 * half
+    u = np.empty((R, K), dtype=np.int64)
+    u[:, 0::2] = q & 0x0F
+    u[:, 1::2] = q >> 4
+    s = bf16_to_f64(np.asarray(scale_bits, dtype=np.uint16))   # [groups, R]
+    per_col = np.repeat(s.T, W4_GROUP, axis=1)[:, :K]
+    return (u - 8).astype(np.float64) * per_col
+
+
+def _weights_f64(w: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or already-widened float64 weights."""
+    w = np.asarray(w)
+    return bf16_to_f64(w) if w.dtype == np.uint16 else w.astype(np.float64)
+
+
+def expert_weights(inp: dict, e: int) -> tuple[np.ndarray, np.ndarray]:
+    """Routed expert e's (gate_up [2I, H], down [H, I]) weights: bf16 bits,
+    or float64 values dequantised from the W4A16 arrays when `inp` holds
+    w_gate_up_q / w_gate_up_scale / w_down_q / w_down_scale."""
+    if "w_gate_up_q" in inp:
+        return (dequant_w4(inp["w_gate_up_q"][e], inp["w_gate_up_scale"][e]),
+                dequant_w4(inp["w_down_q"][e], inp["w_down_scale"][e]))
+    return inp["w_gate_up"][e], inp["w_down"][e]
+
+
 # ---------------------------------------------------------- S4-S6 FFN ----
 
 def swiglu_ffn(a: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
@@ -201,14 +250,15 @@ def swiglu_ffn(a: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
     """S4+S5 for one expert (or S6 for the shared one), fp64.
 
     a          float64 [n, H] (the rows routed to this expert)
-    w_gate_up  bf16 [2I, H]: gate rows [0, I), up rows [I, 2I)
-    w_down     bf16 [H, I]
+    w_gate_up  bf16 [2I, H]: gate rows [0, I), up rows [I, 2I) (or float64
+               weight values, e.g. dequantised W4A16 weights)
+    w_down     bf16 [H, I] (or float64)
     Returns (h float64 [n, I] -- the bf16 value when round_h, y float64
     [n, H], unrounded).
     """
     I = w_gate_up.shape[0] // 2
-    wg = bf16_to_f64(w_gate_up[:I])
-    wu = bf16_to_f64(w_gate_up[I:])
+    wg = _weights_f64(w_gate_up[:I])
+    wu = _weights_f64(w_gate_up[I:])
     g = a @ wg.T
     u = a @ wu.T
     L = float(np.float32(limit))
@@ -218,21 +268,25 @@ def swiglu_ffn(a: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
         h = gc / (1.0 + np.exp(-gc)) * uc
     if round_h:
         h = bf16_to_f64(bf16_round(h))
-    y = h @ bf16_to_f64(w_down).T
+    y = h @ _weights_f64(w_down).T
     return h, y
 
 
-def routed_experts(xr_bits: np.ndarray, perm: dict, w_gate_up: np.ndarray,
-                   w_down: np.ndarray, limit: float, round_h: bool = True,
+def routed_experts(xr_bits: np.ndarray, perm: dict, inp: dict, limit: float,
+                   round_h: bool = True,
                    expert_range: tuple[int, int] | None = None) -> tuple[np.ndarray, np.ndarray]:
     """S4+S5 over all experts: rows of segment e of the permutation go
-    through expert e.  Returns (h_perm [T*k, I], y_perm [T*k, H]) float64
-    in permuted-row order; rows of experts outside `expert_range` stay 0."""
+    through expert e (weights from expert_weights(inp, e)).  Returns
+    (h_perm [T*k, I], y_perm [T*k, H]) float64 in permuted-row order; rows
+    of experts outside `expert_range` stay 0."""
     offsets = perm["offsets"]
     st = perm["sorted_token"]
     E = offsets.shape[0] - 1
-    I = w_gate_up.shape[1] // 2
-    H = w_down.shape[1]
+    H = xr_bits.shape[1]
+    if "w_gate_up_q" in inp:
+        I = inp["w_gate_up_q"].shape[1] // 2
+    else:
+        I = inp["w_gate_up"].shape[1] // 2
     M = st.shape[0]
     h_perm = np.zeros((M, I))
     y_perm = np.zeros((M, H))
@@ -242,7 +296,8 @@ def routed_experts(xr_bits: np.ndarray, perm: dict, w_gate_up: np.ndarray,
         if a1 == a0:
             continue
         a = bf16_to_f64(xr_bits[st[a0:a1]])
-        h, y = swiglu_ffn(a, w_gate_up[e], w_down[e], limit, round_h)
+        wgu, wd = expert_weights(inp, e)
+        h, y = swiglu_ffn(a, wgu, wd, limit, round_h)
         h_perm[a0:a1] = h
         y_perm[a0:a1] = y
     return h_perm, y_perm
@@ -271,8 +326,9 @@ def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
     """The whole layer (S0-S7) on one batch.
 
     `inp` holds the arrays named in moe_inputs.generate (x, x_cur,
-    w_router, corr_bias, w_gate_up, w_down, ws_gate_up, ws_down,
-    gamma_pre, gamma_post).  When `ids` is given, routing uses those
+    w_router, corr_bias, w_gate_up, w_down -- or their W4A16 forms
+    w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale --, ws_gate_up,
+    ws_down, gamma_pre, gamma_post).  When `ids` is given, routing uses those
     expert ids instead of the oracle's own top-k (the weights are still the
     oracle's unbiased scores for those ids); this re-derives the layer for
     tokens whose selection is a near-tie.  `expert_range` keeps only the
@@ -307,8 +363,7 @@ def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
     p = permute(ids, E)
     res.update(offsets=p["offsets"], sorted_token=p["sorted_token"],
                inv_pos=p["inv_pos"], counts=p["counts"])
-    h_perm, y_perm = routed_experts(xr, p, inp["w_gate_up"], inp["w_down"],
-                                    limit, round_h, expert_range)
+    h_perm, y_perm = routed_experts(xr, p, inp, limit, round_h, expert_range)
     res["h_perm"], res["y_perm"] = h_perm, y_perm
     ys = None
     if include_shared and inp.get("ws_gate_up") is not None and inp["ws_gate_up"].shape[0] > 0:

@@ -1,0 +1,99 @@
+"""Pins of the oracle's W4A16 expert weights (the format is this library's
+reading; the pages name the W4A16 expert GEMM but not its layout):
+hand-worked dequantisation, a nibble packer written out here, and the
+special case where every dequantised weight is exact in bf16, in which the
+W4A16 layer must equal the bf16 layer (pinned elsewhere) bit for bit."""
+import numpy as np
+
+import moe_inputs
+from oracle import moe_oracle as mo
+
+
+def _bf16(v):
+    return moe_inputs.f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def _pack(codes):
+    """codes: int array [R, K] of nibbles 0..15 -> bytes [R, K/2], even
+    column in the low nibble (written element by element)."""
+    R, K = codes.shape
+    out = np.zeros((R, K // 2), dtype=np.uint8)
+    for r in range(R):
+        for j in range(K // 2):
+            out[r, j] = int(codes[r, 2 * j]) | (int(codes[r, 2 * j + 1]) << 4)
+    return out
+
+
+def test_dequant_hand_example():
+    # one row, K = 256: two groups of 128 columns
+    q = np.full((1, 128), 0x88, dtype=np.uint8)   # nibble 8 everywhere -> 0
+    q[0, 0] = 0x9F     # columns 0, 1: nibbles 15, 9 -> 7, 1
+    q[0, 64] = 0x70    # columns 128, 129: nibbles 0, 7 -> -8, -1
+    q[0, 127] = 0x0F   # columns 254, 255: nibbles 15, 0 -> 7, -8
+    scale = _bf16([[0.5], [-2.0]])                 # [groups, rows]
+    w = mo.dequant_w4(q, scale)
+    assert w.shape == (1, 256)
+    assert w[0, 0] == 3.5 and w[0, 1] == 0.5
+    assert w[0, 128] == 16.0 and w[0, 129] == 2.0
+    assert w[0, 254] == -14.0 and w[0, 255] == 16.0
+    assert np.count_nonzero(w) == 6
+
+
+def test_dequant_matches_packer_and_scales():
+    rng = np.random.default_rng(5)
+    R, K = 6, 384
+    codes = rng.integers(0, 16, size=(R, K))
+    scale = _bf16(rng.uniform(-1, 1, size=(K // 128, R)))
+    w = mo.dequant_w4(_pack(codes), scale)
+    s = moe_inputs.bf16_bits_to_f32(scale).astype(np.float64)
+    for r in range(R):
+        for c in range(0, K, 7):
+            assert w[r, c] == (codes[r, c] - 8) * s[c // 128, r]
+
+
+def _w4_exact_pair(seed):
+    """A small workload in W4A16 form whose scales are powers of two (so
+    every weight (u - 8) * s is exact in bf16), and the same layer with
+    those weights stored as bf16."""
+    wl = moe_inputs.Workload("w4pin", T=24, H=256, E=6, k=3, I=128, I_s=128, w4=True)
+    inp = moe_inputs.generate(wl, seed)
+    rng = np.random.default_rng(seed)
+    for name in ("w_gate_up_scale", "w_down_scale"):
+        exp = rng.integers(-9, -5, size=inp[name].shape)
+        sign = rng.choice([-1.0, 1.0], size=inp[name].shape)
+        inp[name] = _bf16(sign * np.ldexp(1.0, exp))
+    ref = dict(inp)
+    for name in ("w_gate_up", "w_down"):
+        q, s = ref.pop(name + "_q"), ref.pop(name + "_scale")
+        E, R, half = q.shape
+        bits = np.empty((E, R, 2 * half), dtype=np.uint16)
+        for e in range(E):
+            codes = np.empty((R, 2 * half), dtype=np.int64)
+            codes[:, 0::2] = q[e] & 15
+            codes[:, 1::2] = q[e] >> 4
+            sv = moe_inputs.bf16_bits_to_f32(s[e])           # [groups, R]
+            vals = (codes - 8) * np.repeat(sv.T, 128, axis=1)[:, :2 * half]
+            bits[e] = _bf16(vals)
+            assert np.array_equal(moe_inputs.bf16_bits_to_f32(bits[e]), vals.astype(np.float32))
+        ref[name] = bits
+    return wl, inp, ref
+
+
+def test_w4_layer_equals_bf16_layer_on_exact_weights():
+    wl, inp, ref = _w4_exact_pair(3)
+    a = mo.forward(inp, k=wl.k, rsf=wl.rsf, limit=wl.limit)
+    b = mo.forward(ref, k=wl.k, rsf=wl.rsf, limit=wl.limit)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(a["y_perm"], b["y_perm"])
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_w4_inputs_spread():
+    wl = moe_inputs.WORKLOADS["decode_w4"].with_(E=2, H=512, I=256)
+    inp = moe_inputs.generate(wl, 0)
+    assert inp["w_gate_up_q"].shape == (2, 512, 256)
+    assert inp["w_gate_up_scale"].shape == (2, 4, 512)
+    assert inp["w_down_q"].shape == (2, 512, 128)
+    assert inp["w_down_scale"].shape == (2, 2, 512)
+    w = mo.dequant_w4(inp["w_gate_up_q"][0], inp["w_gate_up_scale"][0])
+    assert 0.015 < w.std() < 0.025   # about the bf16 experts' N(0, 0.02)
