@@ -205,7 +205,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prefill", "zipf", "scmoe"])
+                    choices=["tiny", "decode", "decode_w4", "prefill", "zipf", "scmoe"])
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens the CPU oracle runs on (default: by workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -255,13 +255,20 @@ def main() -> int:
     params = moe.make_params(T, H, E, k, I, Is, wl.rsf, wl.limit, wl.scmoe, wl.eps)
     x = dev_bf16(inp["x"])
     x_cur = dev_bf16(inp["x_cur"]) if wl.scmoe else None
+    w4 = {}
+    if wl.w4:  # W4A16 routed experts: packed codes and bf16 scales
+        w4 = dict(w_gate_up_q=torch.from_numpy(inp["w_gate_up_q"]).to("cuda"),
+                  w_gate_up_scale=dev_bf16(inp["w_gate_up_scale"]),
+                  w_down_q=torch.from_numpy(inp["w_down_q"]).to("cuda"),
+                  w_down_scale=dev_bf16(inp["w_down_scale"]))
     dev = dict(w_router=dev_f32(inp["w_router"]), corr_bias=dev_f32(inp["corr_bias"]),
-               w_gate_up=dev_bf16(inp["w_gate_up"]), w_down=dev_bf16(inp["w_down"]),
+               w_gate_up=None if wl.w4 else dev_bf16(inp["w_gate_up"]),
+               w_down=None if wl.w4 else dev_bf16(inp["w_down"]),
                ws_gate_up=dev_bf16(inp["ws_gate_up"]) if Is else None,
                ws_down=dev_bf16(inp["ws_down"]) if Is else None,
                gamma_pre=dev_f32(inp["gamma_pre"]) if wl.scmoe else None,
                gamma_post=dev_f32(inp["gamma_post"]) if wl.scmoe else None)
-    weights = moe.make_weights(**dev)
+    weights = moe.make_weights(**dev, **w4)
     ws = torch.empty(moe.moe_workspace_size(params), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
@@ -293,10 +300,14 @@ def main() -> int:
 
     # algorithmic work of the dominant launch and of the whole layer
     hbm_bound = wl.T * k <= 64 * E   # about a row tile per expert or less: weight streaming
-    gu_bytes = touched * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+    # bytes of one routed expert's weights of R rows x K: bf16, or W4A16
+    # codes (half a byte each) and one bf16 scale per row and 128 columns
+    def wbytes(R, K):
+        return R * K // 2 + R * (K // 128) * 2 if wl.w4 else R * K * 2
+    gu_bytes = touched * wbytes(2 * I, H) + T * H * 2 + T * k * I * 2
     gu_flops = 2 * T * k * H * 2 * I + 2 * T * H * 2 * Is
-    layer_bytes = (touched * 3 * I * H * 2 + 3 * Is * H * 2 + E * H * 4 + E * 4 + T * H * 2
-                   * (2 if wl.scmoe else 1) + T * H * 2)
+    layer_bytes = (touched * (wbytes(2 * I, H) + wbytes(H, I)) + 3 * Is * H * 2 + E * H * 4 + E * 4
+                   + T * H * 2 * (2 if wl.scmoe else 1) + T * H * 2)
     layer_flops = 2 * T * k * H * 3 * I + 2 * T * H * 3 * Is
     router_flops = 2 * T * H * E
     traffic = committed_traffic(wl.label())

@@ -114,6 +114,20 @@ typedef struct moe_weights {
   const moe_bf16* ws_down;     /* [H, I_s] bf16; unused when I_shared == 0        */
   const float* gamma_pre;      /* [H] fp32 ScMoE pre-norm gain; NULL = ones       */
   const float* gamma_post;     /* [H] fp32 ScMoE post-norm gain; NULL = ones      */
+  /* W4A16 routed experts (the W4A16 expert GEMM named by "Module
+   * glm5next_mlp", Modules forward_prefill_gemm and Constants
+   * MOE_GROUPED_MODULE / W4A16_GEMV_MODULE; the format is this library's):
+   * when w_gate_up_q is set, the routed experts use these four arrays and
+   * w_gate_up / w_down are ignored.  A weight is (u - 8) * scale, u a 4-bit
+   * code, two codes per byte along K (the even column in the low nibble),
+   * one bf16 scale per row and group of 128 columns, scales stored
+   * group-major.  H and I must be multiples of 128, and the batch must be
+   * decode-sized (T*k <= 64*E: the weight-streaming kernels); the shared
+   * expert stays bf16. */
+  const uint8_t* w_gate_up_q;       /* [E, 2I, H/2] codes; NULL = bf16 experts    */
+  const moe_bf16* w_gate_up_scale;  /* [E, H/128, 2I] bf16                        */
+  const uint8_t* w_down_q;          /* [E, H, I/2] codes                          */
+  const moe_bf16* w_down_scale;     /* [E, I/128, H] bf16                         */
 } moe_weights;
 
 /* Step boundaries of moe_forward at which caller-created HIP events can be

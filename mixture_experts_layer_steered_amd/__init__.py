@@ -45,7 +45,8 @@ class moe_params(Structure):
 class moe_weights(Structure):
     _fields_ = [(n, c_void_p) for n in (
         "w_router", "corr_bias", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
-        "gamma_pre", "gamma_post")]
+        "gamma_pre", "gamma_post", "w_gate_up_q", "w_gate_up_scale", "w_down_q",
+        "w_down_scale")]
 
 
 MOE_EV_BEGIN, MOE_EV_PRENORM, MOE_EV_ROUTER, MOE_EV_PERMUTE = 0, 1, 2, 3
@@ -182,9 +183,13 @@ def moe_combine(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, out, stre
 
 
 def make_weights(w_router, corr_bias, w_gate_up, w_down, ws_gate_up=None, ws_down=None,
-                 gamma_pre=None, gamma_post=None) -> moe_weights:
+                 gamma_pre=None, gamma_post=None, w_gate_up_q=None, w_gate_up_scale=None,
+                 w_down_q=None, w_down_scale=None) -> moe_weights:
+    """Weights of one layer; the four *_q / *_scale arrays (W4A16 routed
+    experts) replace w_gate_up / w_down when given."""
     return moe_weights(*[_ptr(t) for t in (w_router, corr_bias, w_gate_up, w_down, ws_gate_up,
-                                           ws_down, gamma_pre, gamma_post)])
+                                           ws_down, gamma_pre, gamma_post, w_gate_up_q,
+                                           w_gate_up_scale, w_down_q, w_down_scale)])
 
 
 def make_probes(topk_ids=None, topk_w=None, expert_offsets=None, sorted_token=None,

@@ -236,6 +236,8 @@ GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int3
   P.mtile_start = mstart;
   P.W = W;
   P.w_stride = w_stride;
+  P.S = nullptr;
+  P.s_stride = 0;
   P.out = out;
   P.M = M;
   P.G = G;
@@ -431,8 +433,19 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
   OPTIONAL_PTR(x_shared);
   REQUIRE_PTR(w->w_router);
   OPTIONAL_PTR(w->corr_bias);
-  REQUIRE_PTR(w->w_gate_up);
-  REQUIRE_PTR(w->w_down);
+  const bool w4 = w->w_gate_up_q != nullptr;
+  if (w4) {
+    REQUIRE_PTR(w->w_gate_up_q);
+    REQUIRE_PTR(w->w_gate_up_scale);
+    REQUIRE_PTR(w->w_down_q);
+    REQUIRE_PTR(w->w_down_scale);
+    if (p->H % 128 != 0 || p->I % 128 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "W4A16 experts need H and I multiples of 128 (H=%d I=%d)",
+                  p->H, p->I);
+  } else {
+    REQUIRE_PTR(w->w_gate_up);
+    REQUIRE_PTR(w->w_down);
+  }
   if (p->I_shared > 0) {
     REQUIRE_PTR(w->ws_gate_up);
     REQUIRE_PTR(w->ws_down);
@@ -450,6 +463,15 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
     OPTIONAL_PTR(probes->xr);
     OPTIONAL_PTR(probes->logits);
   }
+  const int64_t T = p->T, N = T * p->k;
+  const GemmVariant v = pick_variant(
+      N, p->E, std::max<int64_t>(N, T) * std::max(p->H, std::max(p->I, p->I_shared)),
+      (int64_t)2 * std::max(p->I, p->I_shared) * p->H,
+      p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0);
+  if (w4 && v != GemmVariant::kWStream)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "W4A16 experts run on the weight-streaming kernels only (T*k <= 64*E; here "
+                "T*k = %lld, E = %d)", (long long)N, p->E);
   Layout L = carve(*p, ws);
   if (ws_bytes < L.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.bytes);
   if (probes) {
@@ -461,11 +483,6 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
     if (probes->xr && p->scmoe) L.xr = probes->xr;
     if (probes->logits) L.logits = probes->logits;
   }
-  const int64_t T = p->T, N = T * p->k;
-  const GemmVariant v = pick_variant(
-      N, p->E, std::max<int64_t>(N, T) * std::max(p->H, std::max(p->I, p->I_shared)),
-      (int64_t)2 * std::max(p->I, p->I_shared) * p->H,
-      p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0);
   const uint16_t* xr = x_routed;
   const uint16_t* xs = x_shared ? x_shared : x_routed;
   const bool shared = p->I_shared > 0;
@@ -474,6 +491,16 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
                                 (int64_t)2 * p->I * p->H, L.h, N, p->E, p->I, p->H, v, true);
   GemmProblem dn = make_problem(L.h, nullptr, L.offsets, L.mstart, w->w_down,
                                 (int64_t)p->H * p->I, L.y, N, p->E, p->H, p->I, v, false);
+  if (w4) {  // packed codes (uint16 units between experts) and group-major scales
+    gu.W = reinterpret_cast<const uint16_t*>(w->w_gate_up_q);
+    gu.w_stride = (int64_t)2 * p->I * p->H / 4;
+    gu.S = w->w_gate_up_scale;
+    gu.s_stride = (int64_t)(p->H / 128) * 2 * p->I;
+    dn.W = reinterpret_cast<const uint16_t*>(w->w_down_q);
+    dn.w_stride = (int64_t)p->H * p->I / 4;
+    dn.S = w->w_down_scale;
+    dn.s_stride = (int64_t)(p->I / 128) * p->H;
+  }
   GemmProblem sgu = make_problem(xs, nullptr, nullptr, nullptr, w->ws_gate_up, 0, L.hs, T, 1,
                                  p->I_shared, p->H, v, true);
   GemmProblem sdn = make_problem(L.hs, nullptr, nullptr, nullptr, w->ws_down, 0, L.ys, T, 1, p->H,

@@ -1080,6 +1080,235 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight streaming with W4A16 weights (decode; the W4A16 expert GEMM the
+// pages name for GLM-5.3's routed experts, in this library's format).
+//
+// Same tiles, cursors and tile order as the bf16 kernel above; a stage now
+// covers 512 columns of K: A rows in 1 KB pieces (bf16), weight rows in
+// 256-byte pieces of 4-bit codes, and each wave's 16 rows x 4 groups of
+// bf16 scales (128 bytes).  Per 32-wide substep a lane reads 4 bytes of
+// codes (8 nibbles u) and makes the bf16 values 128 + u exactly (bits
+// 0x4300 | u); the MFMA sums x * (128 + u) over a 128-column group, a
+// second MFMA against ones sums x, and the group's contribution
+// scale * (P - 136 * X) = scale * sum x * (u - 8) goes into the fp32
+// accumulator.  Products and the per-group scaling are exact in fp32 up
+// to the sums' rounding; K must be a multiple of 128.
+constexpr int W4_KB = 512;  // K columns per stage
+
+__device__ __forceinline__ bf16x8_t w4_codes_to_bf16(uint32_t d) {
+  // bytes b0..b3 hold columns (2j, 2j+1) in (low, high) nibbles; lane value
+  // of column c: bf16 bits 0x4300 | u_c = 128 + u_c
+  const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+  uint32_t o[4];
+  o[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
+  o[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
+  o[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
+  o[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <bool GATEUP, int STAGES>
+__global__ __launch_bounds__(256, 1) void grouped_wstream_w4_kernel(GemmProblem p0, float limit) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+  constexpr int BM = WS_BM, NB = WS_NB;
+  constexpr int BN = GATEUP ? NB / 2 : NB;       // output columns per tile
+  constexpr int KB = W4_KB;
+  constexpr int A_BYTES = BM * KB * 2;           // 16 rows x 1 KB
+  constexpr int W_ROW = KB / 2;                  // bytes of codes per weight row and stage
+  constexpr int W_BYTES = NB * W_ROW;            // 64 rows x 256 B
+  constexpr int S_WAVE = 128;                    // scale bytes per wave and stage
+  constexpr int STAGE_BYTES = A_BYTES + W_BYTES + 4 * S_WAVE;
+  constexpr int A_PER_WAVE = BM / 4;             // 1 KB A rows per wave
+  constexpr int W_RPI = 1024 / W_ROW;            // weight rows per 1 KB instruction
+  constexpr int W_PER_WAVE = NB / (W_RPI * 4);
+  constexpr int PER_WAVE = A_PER_WAVE + W_PER_WAVE + 1;  // + the scales
+  constexpr int SUB = KB / 32;                   // 32-wide substeps per stage
+  static_assert(W_RPI == 4 && W_PER_WAVE == 4 && (STAGES - 2) * PER_WAVE <= 63, "shape");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* const smem = reinterpret_cast<uint8_t*>(smem_dyn);
+
+  const int mt0 = pipe_mtiles<BM>(p0);
+  const int total = mt0 * p0.ntiles;
+  const int nk = (p0.K + KB - 1) / KB;
+  const int nwg = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, lid = b >> 3;
+  const int nwg_x = (nwg - xcd + 7) >> 3;
+  const int t_begin = (int)((int64_t)total * xcd / 8);
+  const int t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  if (t_begin + lid >= t_end) return;
+  const WsProb P = ws_pick(p0, p0, false, mt0, mt0);
+  const int K = P.K, N = P.N;
+  const int groups = K / 128;
+
+  // ---- load cursor
+  int t_ld = t_begin + lid, kt_ld = 0, slot_ld = 0, g_ld = -1;
+  const uint16_t* ld_A = P.A;
+  const uint8_t* ld_W = nullptr;
+  const uint16_t* ld_S = nullptr;
+  uint32_t offA[A_PER_WAVE], offW[W_PER_WAVE], offS = 0;
+  auto setup_ld = [&]() __attribute__((always_inline)) {
+    int64_t row0, row_end;
+    int n0;
+    ws_locate<BN>(P, t_ld, row0, row_end, n0, g_ld);
+    ld_W = reinterpret_cast<const uint8_t*>(P.W + (int64_t)g_ld * P.w_stride);
+    ld_S = p0.S + (int64_t)g_ld * p0.s_stride;
+    // A: instruction i of wave w fills tile row 4w + i (one 1 KB row piece)
+#pragma unroll
+    for (int i = 0; i < A_PER_WAVE; ++i) {
+      const int64_t gr = row0 + 4 * wave + i;
+      const int64_t r = gr < row_end ? gr : row0;
+      const int64_t src = P.row_index ? (int64_t)ws_sload(P.row_index, r) : r;
+      offA[i] = (uint32_t)(src * K + ws_swz(4 * wave + i, lane) * 8);
+    }
+    // W: instruction i of wave w fills weight rows 4q .. 4q+3, q = w + 4i;
+    // lane L writes row 4q + L/16, 16-byte slot L%16 (logical chunk
+    // ws_swz(row, slot)); in gate_up a wave block's first 8 rows are gate
+    // rows and the next 8 the matching up rows
+#pragma unroll
+    for (int i = 0; i < W_PER_WAVE; ++i) {
+      const int r = 4 * (wave + 4 * i) + lane / 16;
+      int n = GATEUP ? n0 + 8 * (r >> 4) + (r & 7) : n0 + r;
+      const bool up = GATEUP && (r & 8);
+      if (n >= N) n = n0;
+      offW[i] = (uint32_t)((int64_t)(up ? N + n : n) * (K / 2) + ws_swz(r, lane % 16) * 16);
+    }
+    // scales ([K/128, rows] per expert): lane j < 8 of wave w fetches group
+    // j/2 of the stage for the 8 rows of half j%2 of the wave's block (gate
+    // rows, then up rows); offS is the offset of group j/2 of stage 0
+    {
+      const int j = lane & 7;
+      int n = GATEUP ? n0 + 8 * wave : n0 + 16 * wave + 8 * (j & 1);
+      if (n >= N) n = n0;
+      const bool up = GATEUP && (j & 1);
+      offS = (uint32_t)((int64_t)(j >> 1) * (GATEUP ? 2 * N : N) + (up ? N + n : n));
+    }
+  };
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if (t_ld >= t_end) return;
+    uint8_t* base = smem + slot_ld * STAGE_BYTES;
+    const int k0 = kt_ld * KB;
+    // in a partial last stage (K a multiple of 128) lanes past K fetch
+    // column k0 of their row again (never read)
+    const int valid = min(KB, K - k0);
+#pragma unroll
+    for (int i = 0; i < A_PER_WAVE; ++i) {
+      const int chunk = ws_swz(4 * wave + i, lane);  // 8 columns
+      const uint32_t o = offA[i] + k0 - (8 * chunk < valid ? 0 : 8 * chunk);
+      lds_direct_16(ld_A + o, reinterpret_cast<uint16_t*>(base + (4 * wave + i) * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < W_PER_WAVE; ++i) {
+      const int chunk = ws_swz(4 * (wave + 4 * i) + lane / 16, lane % 16);  // 32 columns
+      const uint32_t o = offW[i] + k0 / 2 - (32 * chunk < valid ? 0 : 16 * chunk);
+      lds_direct_16(ld_W + o, reinterpret_cast<uint16_t*>(base + A_BYTES + (wave + 4 * i) * 1024));
+    }
+    if (lane < 8) {  // groups past K fetch the last group again (never read)
+      const int rs = GATEUP ? 2 * N : N;
+      const int gk = min(k0 / 128 + (lane >> 1), groups - 1);
+      const uint32_t o = offS + (uint32_t)(gk - (lane >> 1)) * rs;
+      lds_direct_16(ld_S + o,
+                    reinterpret_cast<uint16_t*>(base + A_BYTES + W_BYTES + wave * S_WAVE));
+    }
+    slot_ld = slot_ld + 1 == STAGES ? 0 : slot_ld + 1;
+    if (++kt_ld == nk) {
+      kt_ld = 0;
+      t_ld += nwg_x;
+      if (t_ld < t_end) setup_ld();
+    }
+  };
+
+  // ---- compute cursor
+  int t_cp = t_begin + lid, kt_cp = 0, slot_cp = 0, g_cp = -1, n0_cp = 0;
+  int64_t row0_cp = 0, row_end_cp = 0;
+  auto setup_cp = [&]() __attribute__((always_inline)) {
+    ws_locate<BN>(P, t_cp, row0_cp, row_end_cp, n0_cp, g_cp);
+  };
+
+  // element (reg r, lane l) of the accumulators: row 4(l/16) + r of the
+  // tile, weight row 16*wave + l%16
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, accP = acc, accX = acc;
+  const int fr = lane & 15;
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u,
+                                                             0x3F803F80u, 0x3F803F80u});
+  auto store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = row0_cp + 4 * (lane >> 4) + r;
+      if (GATEUP) {
+        const float u = __shfl_xor(acc[r], 8, 64);  // lanes j, j+8: g and u of one column
+        const int col = n0_cp + 8 * wave + (fr & 7);
+        if (fr < 8 && row < row_end_cp && col < N)
+          static_cast<uint16_t*>(P.out)[row * N + col] =
+              (uint16_t)f32_to_bf16_bits(swiglu_clamped(acc[r], u, limit));
+      } else {
+        const int col = n0_cp + 16 * wave + fr;
+        if (row < row_end_cp && col < N) static_cast<float*>(P.out)[row * N + col] = acc[r];
+      }
+    }
+  };
+  auto substep = [&](const uint8_t* base, int ks) __attribute__((always_inline)) {
+    const uint16_t* As = reinterpret_cast<const uint16_t*>(base);
+    const uint8_t* Ws = base + A_BYTES;
+    const bf16x8_t a =
+        *reinterpret_cast<const bf16x8_t*>(&As[fr * KB + ws_swz(fr, ks * 4 + (lane >> 4)) * 8]);
+    const int br = 16 * wave + fr;
+    const uint32_t d =
+        *reinterpret_cast<const uint32_t*>(&Ws[br * W_ROW + ws_swz(br, ks) * 16 + 4 * (lane >> 4)]);
+    accP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w4_codes_to_bf16(d), accP, 0, 0, 0);
+    accX = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, accX, 0, 0, 0);
+    if ((ks & 3) == 3) {  // end of a 128-column group: scale and fold in
+      const uint16_t sb = *reinterpret_cast<const uint16_t*>(
+          base + A_BYTES + W_BYTES + wave * S_WAVE + 16 * (2 * (ks >> 2) + (fr >> 3)) + 2 * (fr & 7));
+      const float sc = __uint_as_float((uint32_t)sb << 16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc[r] = fmaf(sc, fmaf(-136.0f, accX[r], accP[r]), acc[r]);
+        accP[r] = 0.f;
+        accX[r] = 0.f;
+      }
+    }
+  };
+
+  setup_ld();
+  setup_cp();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue_next();
+
+  while (true) {
+    // as in the bf16 kernel: own loads of this stage landed, own LDS reads
+    // done, then the barrier
+    if (t_ld < t_end)
+      PL_WAIT_VM_LDS((STAGES - 2) * PER_WAVE);
+    else
+      PL_WAIT_VM_LDS(0);
+    pl_barrier();
+    issue_next();
+    const uint8_t* base = smem + slot_cp * STAGE_BYTES;
+    const int sub_valid = (K - kt_cp * KB) >> 5;  // 32-wide substeps left in K (a multiple of 4)
+    if (sub_valid >= SUB) {
+#pragma unroll
+      for (int ks = 0; ks < SUB; ++ks) substep(base, ks);
+    } else {
+      for (int ks = 0; ks < sub_valid; ++ks) substep(base, ks);
+    }
+    slot_cp = slot_cp + 1 == STAGES ? 0 : slot_cp + 1;
+    if (++kt_cp == nk) {
+      store();
+      t_cp += nwg_x;
+      if (t_cp >= t_end) break;
+      kt_cp = 0;
+      setup_cp();
+      acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
 int device_cu_count() {
   static int cached = 0;  // per process: one device model in a run
   if (cached == 0) {
@@ -1134,6 +1363,24 @@ hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limi
   // one resident workgroup per CU, or fewer to leave CUs to concurrent work
   const int grid = max_wgs > 0 ? std::min(max_wgs, device_cu_count()) : device_cu_count();
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a, pb, b ? 1 : 0, limit);
+  return hipGetLastError();
+}
+
+template <bool GATEUP, int STAGES>
+hipError_t launch_wstream_w4(const GemmProblem& a, float limit, hipStream_t stream, int max_wgs) {
+  constexpr size_t stage = (size_t)WS_BM * W4_KB * 2 + (size_t)WS_NB * W4_KB / 2 + 4 * 128;
+  const size_t lds = STAGES * stage;
+  static_assert(STAGES * stage <= 160 * 1024, "LDS");
+  auto kern = grouped_wstream_w4_kernel<GATEUP, STAGES>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int grid = max_wgs > 0 ? std::min(max_wgs, device_cu_count()) : device_cu_count();
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a, limit);
   return hipGetLastError();
 }
 
@@ -1218,6 +1465,12 @@ hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, in
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                const GemmProblem* b, float limit, hipStream_t stream,
                                int max_wgs) {
+  if (a.S != nullptr) {  // W4A16 weights: weight streaming, one problem per launch
+    if (v != GemmVariant::kWStream || b != nullptr || a.K % 128 != 0)
+      return hipErrorInvalidValue;
+    if (gateup) return launch_wstream_w4<true, 4>(a, limit, stream, max_wgs);
+    return launch_wstream_w4<false, 4>(a, limit, stream, max_wgs);
+  }
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
   if (v == GemmVariant::kWStream) {  // 512-byte row pieces, four stages
     if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream, max_wgs);

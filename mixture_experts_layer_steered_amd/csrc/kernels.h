@@ -16,7 +16,10 @@ struct GemmProblem {
   const int32_t* group_offsets;   // [G+1] device row offsets, or nullptr: one group of M rows
   const int32_t* mtile_start;     // [G+1] device m-tile prefix (with group_offsets)
   const uint16_t* W;              // [G, WR, K] bf16; gate_up: WR = 2N, down: WR = N
-  int64_t w_stride;               // elements between groups of W
+                                  // (W4A16: [G, WR, K/2] bytes of 4-bit codes)
+  int64_t w_stride;               // uint16 elements between groups of W
+  const uint16_t* S;              // W4A16 only: [G, K/128, WR] bf16 scales; nullptr = bf16 W
+  int64_t s_stride;               // elements between groups of S
   void* out;                      // [M, N]: bf16 h (gate_up) or fp32 y (down)
   int64_t M;                      // total rows
   int32_t G;                      // groups

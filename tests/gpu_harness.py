@@ -68,15 +68,22 @@ class Device:
         self.x_cur = dev_bf16(torch, inp["x_cur"]) if wl.scmoe else None
         self.w_router = dev_f32(torch, inp["w_router"])
         self.corr_bias = dev_f32(torch, inp["corr_bias"]) if inp.get("corr_bias") is not None else None
-        self.w_gate_up = dev_bf16(torch, inp["w_gate_up"])
-        self.w_down = dev_bf16(torch, inp["w_down"])
+        w4 = "w_gate_up_q" in inp
+        self.w_gate_up = None if w4 else dev_bf16(torch, inp["w_gate_up"])
+        self.w_down = None if w4 else dev_bf16(torch, inp["w_down"])
+        self.w4 = {}
+        if w4:
+            for n in ("w_gate_up_q", "w_down_q"):
+                self.w4[n] = torch.from_numpy(np.ascontiguousarray(inp[n])).to("cuda")
+            for n in ("w_gate_up_scale", "w_down_scale"):
+                self.w4[n] = dev_bf16(torch, inp[n])
         self.ws_gate_up = dev_bf16(torch, inp["ws_gate_up"]) if wl.I_s else None
         self.ws_down = dev_bf16(torch, inp["ws_down"]) if wl.I_s else None
         self.gamma_pre = dev_f32(torch, inp["gamma_pre"]) if inp.get("gamma_pre") is not None else None
         self.gamma_post = dev_f32(torch, inp["gamma_post"]) if inp.get("gamma_post") is not None else None
         self.weights = moe.make_weights(self.w_router, self.corr_bias, self.w_gate_up, self.w_down,
                                         self.ws_gate_up, self.ws_down, self.gamma_pre,
-                                        self.gamma_post)
+                                        self.gamma_post, **self.w4)
         nbytes = moe.moe_workspace_size(self.params)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         self.out = torch.empty((T, H), dtype=torch.int16, device="cuda")

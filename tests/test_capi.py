@@ -135,6 +135,25 @@ def test_entry_points_reject_before_launch():
     with pytest.raises(moe.MoeError) as ei:   # workspace too small
         moe.moe_forward(P(), 16, None, w, 16, None, 16, stream=0)
     assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    # W4A16 routed experts: all four arrays, K multiples of 128, decode-sized batches
+    w4 = dict(w_gate_up_q=16, w_gate_up_scale=16, w_down_q=16, w_down_scale=16)
+    with pytest.raises(moe.MoeError) as ei:   # a scale array missing
+        moe.moe_forward(P(), 16, None, moe.make_weights(16, None, None, None, 16, 16,
+                                                         **dict(w4, w_down_scale=None)),
+                        16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:   # I not a multiple of 128
+        moe.moe_forward(P(I=192), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
+                        16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:   # more than 64 rows per expert
+        moe.moe_forward(P(T=4096), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
+                        16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:   # decode-sized: reaches the workspace check
+        moe.moe_forward(P(), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
+                        16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
 
 
 def test_empty_batch_is_a_noop_without_pointers():

@@ -204,3 +204,31 @@ def test_forward_graph_replay_matches_eager(name):
         d.run()  # eager work between replays
         torch.cuda.synchronize()
         np.testing.assert_array_equal(gh.to_bits(d.out), eager)
+
+
+# ------------------------------------------------ W4A16 routed experts ----
+
+W4 = {
+    # one whole 512-column stage in gate_up (H = 512); down K = 384: a
+    # partial stage of three 128-column groups; shared expert beside routing
+    "w4_small": Workload("w4_small", T=40, H=512, E=16, k=4, I=384, I_s=256, w4=True),
+    # H = 640: a whole stage then a one-group stage; no shared expert;
+    # several 16-row m-tiles per expert
+    "w4_multi": Workload("w4_multi", T=96, H=640, E=8, k=2, I=256, I_s=0, rsf=1.5, w4=True),
+    # clamp stress with W4 codes (large scales)
+    "w4_clamp": Workload("w4_clamp", T=32, H=256, E=8, k=2, I=128, I_s=128, weight_std=0.3,
+                         w4=True),
+}
+
+
+@pytest.mark.parametrize("name", list(W4))
+def test_forward_w4(name):
+    wl = W4[name]
+    inp = moe_inputs.generate(wl, seed=4)
+    rep, _, _ = run_and_check(wl, inp)
+    assert rep["rows_checked"] == wl.T
+
+
+def test_forward_decode_w4_full():
+    rep = _full("decode_w4", None)
+    assert rep["rows_checked"] == 32
