@@ -119,8 +119,9 @@ typedef struct moe_weights {
    * MOE_GROUPED_MODULE / W4A16_GEMV_MODULE; the format is this library's):
    * when w_gate_up_q is set, the routed experts use these four arrays and
    * w_gate_up / w_down are ignored.  A weight is (u - 8) * scale, u a 4-bit
-   * code, two codes per byte along K (the even column in the low nibble),
-   * one bf16 scale per row and group of 128 columns, scales stored
+   * code, packed along K in 4-byte words of 8 columns (byte j of a word:
+   * column j in the low nibble, column j + 4 in the high nibble), one
+   * bf16 scale per row and group of 128 columns, scales stored
    * group-major.  H and I must be multiples of 128, and the batch must be
    * decode-sized (T*k <= 64*E: the weight-streaming kernels); the shared
    * expert stays bf16. */

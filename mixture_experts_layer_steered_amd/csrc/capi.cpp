@@ -500,6 +500,8 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
     dn.w_stride = (int64_t)p->H * p->I / 4;
     dn.S = w->w_down_scale;
     dn.s_stride = (int64_t)(p->I / 128) * p->H;
+    gu.ntiles = (p->I + gemm_w4_tile_n(true) - 1) / gemm_w4_tile_n(true);
+    dn.ntiles = (p->H + gemm_w4_tile_n(false) - 1) / gemm_w4_tile_n(false);
   }
   GemmProblem sgu = make_problem(xs, nullptr, nullptr, nullptr, w->ws_gate_up, 0, L.hs, T, 1,
                                  p->I_shared, p->H, v, true);

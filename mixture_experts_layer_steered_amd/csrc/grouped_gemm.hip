@@ -1081,52 +1081,92 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
 }
 
 // ---------------------------------------------------------------------------
-// Weight streaming with W4A16 weights (decode; the W4A16 expert GEMM the
-// pages name for GLM-5.3's routed experts, in this library's format).
+// Weight streaming with W4A16 weights (decode; the grouped W4A16 expert GEMM
+// of "Module glm5next_mlp", in this library's format: 4-bit codes u of value
+// u - 8, packed along K in 4-byte words of 8 columns whose byte j holds
+// columns j and j + 4 in its low and high nibble, and one bf16 scale per
+// weight row and 128 columns, stored group-major).
 //
-// Same tiles, cursors and tile order as the bf16 kernel above; a stage now
-// covers 512 columns of K: A rows in 1 KB pieces (bf16), weight rows in
-// 256-byte pieces of 4-bit codes, and each wave's 16 rows x 4 groups of
-// bf16 scales (128 bytes).  Per 32-wide substep a lane reads 4 bytes of
-// codes (8 nibbles u) and makes the bf16 values 128 + u exactly (bits
-// 0x4300 | u); the MFMA sums x * (128 + u) over a 128-column group, a
-// second MFMA against ones sums x, and the group's contribution
-// scale * (P - 136 * X) = scale * sum x * (u - 8) goes into the fp32
-// accumulator.  Products and the per-group scaling are exact in fp32 up
-// to the sums' rounding; K must be a multiple of 128.
-constexpr int W4_KB = 512;  // K columns per stage
+// At a quarter of the bf16 size per weight, a 64-row weight tile would take
+// no more LDS per stage than the 16 gathered A rows and halve the weight bytes
+// in flight.  So a tile here is 16 A rows by NB = 16 * NBLK * NW weight rows:
+// each of the NW wavefronts owns NBLK blocks of 16 weight rows, which share
+// its A fragments; a stage covers KB columns of K (whole 128-column groups).
+// Unlike the bf16 kernel this one has real per-weight ALU work (unpacking
+// the codes), so it runs two wavefronts per SIMD: one's unpacking overlaps
+// the other's MFMAs.  A rows past the segment are not fetched (a lane-0 load
+// keeps each wavefront's count of loads per stage fixed); their products
+// reach only rows that are never stored.
+//
+// Per stage and weight block a lane reads one 16-byte piece of codes: lane
+// group q (lane / 16) takes piece 4s + q of the row's stage span, whose four
+// dwords feed substeps 4s .. 4s+3, and its A fragment in substep 4s + t is
+// columns 32 (4s + q) + 8t .. +7 of its row; a 128-column group is thus four
+// substeps.  A code dword becomes eight bf16 values 128 + u exactly (bits
+// 0x4300 | u: one mask per nibble half, then a byte permute per pair); the
+// MFMA sums
+// x (128 + u) over the group, one more MFMA against ones sums x (shared by
+// the blocks), and scale (P - 136 X) = scale * sum x (u - 8) goes into the
+// fp32 accumulator.  K must be a multiple of 128; a last stage with fewer
+// groups than KB / 128 fetches an earlier group again in place of the
+// missing ones and computes only its own.
+
+// the launched shape: 256 weight rows by 256 columns a stage, eight
+// wavefronts, three stages
+constexpr int W4_NBLK = 2, W4_KB = 256, W4_NW = 8, W4_STAGES = 3;
+
+template <int NBLK, int KB, int NW>
+struct W4Shape {
+  static constexpr int NB = 16 * NBLK * NW;        // weight rows per tile
+  static constexpr int A_BYTES = WS_BM * KB * 2;   // 16 rows of bf16
+  static constexpr int W_ROW = KB / 2;             // code bytes per weight row and stage
+  static constexpr int W_BYTES = NB * W_ROW;
+  static constexpr int S_WAVE = NBLK * KB / 4;     // scale bytes per wavefront and stage
+  static constexpr int STAGE = A_BYTES + W_BYTES + NW * S_WAVE;
+  static constexpr int A_CH = KB / 8;              // 16-byte chunks per A row
+  static constexpr int A_RPI = 64 / A_CH;          // A rows per 1 KB instruction
+  static constexpr int A_PW = WS_BM / (NW * A_RPI);  // A instructions per wavefront
+  static constexpr int W_CH = KB / 32;             // 16-byte pieces per weight row
+  static constexpr int W_RPI = 64 / W_CH;          // weight rows per instruction
+  static constexpr int W_PW = NB / (NW * W_RPI);   // weight instructions per wavefront
+  static constexpr int S_LANES = S_WAVE / 16;      // lanes that fetch the scales
+  static constexpr int PER_WAVE = A_PW + W_PW + 1;
+  static constexpr int GROUPS = KB / 128;          // scale groups per stage
+  static_assert(KB % 128 == 0 && KB <= 512 && A_PW >= 1 && A_PW * NW * A_RPI == WS_BM &&
+                W_PW >= 1 && W_PW * NW * W_RPI == NB && S_LANES >= 1 && S_LANES <= 64,
+                "W4 shape");
+};
+
+// weight row r's 16-byte piece c sits in slot w4_swz: the 16 rows one
+// ds_read_b128 pass touches land in 16 different 16-byte bank groups
+template <int W_CH>
+__device__ __forceinline__ int w4_swz(int r, int c) {
+  return c ^ ((r / (16 / W_CH)) & (W_CH - 1));
+}
 
 __device__ __forceinline__ bf16x8_t w4_codes_to_bf16(uint32_t d) {
-  // bytes b0..b3 hold columns (2j, 2j+1) in (low, high) nibbles; lane value
-  // of column c: bf16 bits 0x4300 | u_c = 128 + u_c
+  // byte j of d holds columns j (low nibble) and j + 4 (high nibble): the
+  // masks give the bytes u of columns 0..3 and 4..7; each permute takes two
+  // of them as the low bytes of a pair and 0x43 as the high bytes
   const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
   uint32_t o[4];
-  o[0] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x43004300u;
-  o[1] = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x43004300u;
-  o[2] = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x43004300u;
-  o[3] = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x43004300u;
+  o[0] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u);  // columns 0, 1
+  o[1] = __builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u);  // columns 2, 3
+  o[2] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u);  // columns 4, 5
+  o[3] = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u);  // columns 6, 7
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const u32x4_t v = {o[0], o[1], o[2], o[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <bool GATEUP, int STAGES>
-__global__ __launch_bounds__(256, 1) void grouped_wstream_w4_kernel(GemmProblem p0, float limit) {
+template <bool GATEUP, int NBLK, int KB, int NW, int STAGES>
+__global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProblem p0,
+                                                                       float limit) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
-  constexpr int BM = WS_BM, NB = WS_NB;
-  constexpr int BN = GATEUP ? NB / 2 : NB;       // output columns per tile
-  constexpr int KB = W4_KB;
-  constexpr int A_BYTES = BM * KB * 2;           // 16 rows x 1 KB
-  constexpr int W_ROW = KB / 2;                  // bytes of codes per weight row and stage
-  constexpr int W_BYTES = NB * W_ROW;            // 64 rows x 256 B
-  constexpr int S_WAVE = 128;                    // scale bytes per wave and stage
-  constexpr int STAGE_BYTES = A_BYTES + W_BYTES + 4 * S_WAVE;
-  constexpr int A_PER_WAVE = BM / 4;             // 1 KB A rows per wave
-  constexpr int W_RPI = 1024 / W_ROW;            // weight rows per 1 KB instruction
-  constexpr int W_PER_WAVE = NB / (W_RPI * 4);
-  constexpr int PER_WAVE = A_PER_WAVE + W_PER_WAVE + 1;  // + the scales
-  constexpr int SUB = KB / 32;                   // 32-wide substeps per stage
-  static_assert(W_RPI == 4 && W_PER_WAVE == 4 && (STAGES - 2) * PER_WAVE <= 63, "shape");
+  using S = W4Shape<NBLK, KB, NW>;
+  constexpr int BM = WS_BM, NB = S::NB;
+  constexpr int BN = GATEUP ? NB / 2 : NB;  // output columns per tile
+  static_assert((STAGES - 2) * S::PER_WAVE <= 63 && STAGES * S::STAGE <= 160 * 1024, "stages");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1144,75 +1184,101 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_w4_kernel(GemmProblem 
   const WsProb P = ws_pick(p0, p0, false, mt0, mt0);
   const int K = P.K, N = P.N;
   const int groups = K / 128;
+  const int rs = GATEUP ? 2 * N : N;  // scale entries per group
 
   // ---- load cursor
-  int t_ld = t_begin + lid, kt_ld = 0, slot_ld = 0, g_ld = -1;
+  int t_ld = t_begin + lid, kt_ld = 0, slot_ld = 0, g_ld = -1, rows_ld = 0;
   const uint16_t* ld_A = P.A;
   const uint8_t* ld_W = nullptr;
   const uint16_t* ld_S = nullptr;
-  uint32_t offA[A_PER_WAVE], offW[W_PER_WAVE], offS = 0;
+  uint32_t offA[S::A_PW], offW[S::W_PW], offS = 0;
   auto setup_ld = [&]() __attribute__((always_inline)) {
     int64_t row0, row_end;
     int n0;
     ws_locate<BN>(P, t_ld, row0, row_end, n0, g_ld);
-    ld_W = reinterpret_cast<const uint8_t*>(P.W + (int64_t)g_ld * P.w_stride);
+    rows_ld = (int)(row_end - row0);
+    ld_W = reinterpret_cast<const uint8_t*>(P.W) + (int64_t)g_ld * P.w_stride * 2;
     ld_S = p0.S + (int64_t)g_ld * p0.s_stride;
-    // A: instruction i of wave w fills tile row 4w + i (one 1 KB row piece)
+    // A: instruction i of wave w fills rows A_RPI q .. A_RPI q + A_RPI - 1,
+    // q = w + NW i; lane L writes row A_RPI q + L / A_CH, slot L % A_CH,
+    // which holds logical chunk slot ^ (row & 15).  Rows past the segment
+    // point at the tile's first row (only lane 0 fetches there).
 #pragma unroll
-    for (int i = 0; i < A_PER_WAVE; ++i) {
-      const int64_t gr = row0 + 4 * wave + i;
-      const int64_t r = gr < row_end ? gr : row0;
-      const int64_t src = P.row_index ? (int64_t)ws_sload(P.row_index, r) : r;
-      offA[i] = (uint32_t)(src * K + ws_swz(4 * wave + i, lane) * 8);
+    for (int i = 0; i < S::A_PW; ++i) {
+      // the instruction's A_RPI row ids are uniform: scalar loads, then each
+      // lane takes its own
+      int64_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < S::A_RPI; ++j) {
+        const int64_t gr = row0 + S::A_RPI * (wave + NW * i) + j;
+        const int64_t rr = gr < row_end ? gr : row0;
+        const int64_t src = P.row_index ? (int64_t)ws_sload(P.row_index, rr) : rr;
+        if (lane / S::A_CH == j) mine = src;
+      }
+      const int r = S::A_RPI * (wave + NW * i) + lane / S::A_CH;
+      offA[i] = (uint32_t)(mine * K + ((lane % S::A_CH) ^ (r & 15)) * 8);
     }
-    // W: instruction i of wave w fills weight rows 4q .. 4q+3, q = w + 4i;
-    // lane L writes row 4q + L/16, 16-byte slot L%16 (logical chunk
-    // ws_swz(row, slot)); in gate_up a wave block's first 8 rows are gate
-    // rows and the next 8 the matching up rows
+    // W: instruction i of wave w fills weight rows W_RPI q .. , q = w + NW i;
+    // lane L writes row W_RPI q + L / W_CH, slot L % W_CH.  Block b (wave
+    // b / NBLK's block b % NBLK) holds tile rows 16 b .. 16 b + 15: in gate_up
+    // 8 gate rows and the matching 8 up rows.  Rows past N fetch row n0.
 #pragma unroll
-    for (int i = 0; i < W_PER_WAVE; ++i) {
-      const int r = 4 * (wave + 4 * i) + lane / 16;
+    for (int i = 0; i < S::W_PW; ++i) {
+      const int r = S::W_RPI * (wave + NW * i) + lane / S::W_CH;
       int n = GATEUP ? n0 + 8 * (r >> 4) + (r & 7) : n0 + r;
       const bool up = GATEUP && (r & 8);
       if (n >= N) n = n0;
-      offW[i] = (uint32_t)((int64_t)(up ? N + n : n) * (K / 2) + ws_swz(r, lane % 16) * 16);
+      const int c = w4_swz<S::W_CH>(r, lane % S::W_CH);
+      offW[i] = (uint32_t)((int64_t)(up ? N + n : n) * (K / 2) + c * 16);
     }
-    // scales ([K/128, rows] per expert): lane j < 8 of wave w fetches group
-    // j/2 of the stage for the 8 rows of half j%2 of the wave's block (gate
-    // rows, then up rows); offS is the offset of group j/2 of stage 0
-    {
-      const int j = lane & 7;
-      int n = GATEUP ? n0 + 8 * wave : n0 + 16 * wave + 8 * (j & 1);
+    // scales of the wave's rows, per group of the stage: in gate_up 8 NBLK
+    // gate columns then the same up columns, in down 16 NBLK rows, in
+    // 16-byte pieces; lane l < S_LANES fetches piece l % (2 NBLK) of stage
+    // group l / (2 NBLK); offS is the piece's offset within a group
+    if (lane < S::S_LANES) {
+      const int pi = lane % (2 * NBLK);
+      int n;
+      bool up = false;
+      if (GATEUP) {
+        up = pi >= NBLK;
+        n = n0 + 8 * NBLK * wave + 8 * (up ? pi - NBLK : pi);
+      } else {
+        n = n0 + 16 * NBLK * wave + 8 * pi;
+      }
       if (n >= N) n = n0;
-      const bool up = GATEUP && (j & 1);
-      offS = (uint32_t)((int64_t)(j >> 1) * (GATEUP ? 2 * N : N) + (up ? N + n : n));
+      offS = (uint32_t)(up ? N + n : n);
     }
   };
   auto issue_next = [&]() __attribute__((always_inline)) {
     if (t_ld >= t_end) return;
-    uint8_t* base = smem + slot_ld * STAGE_BYTES;
+    uint8_t* base = smem + slot_ld * S::STAGE;
     const int k0 = kt_ld * KB;
-    // in a partial last stage (K a multiple of 128) lanes past K fetch
-    // column k0 of their row again (never read)
-    const int valid = min(KB, K - k0);
+    const int gv = min(S::GROUPS, groups - k0 / 128);  // groups of K in this stage
 #pragma unroll
-    for (int i = 0; i < A_PER_WAVE; ++i) {
-      const int chunk = ws_swz(4 * wave + i, lane);  // 8 columns
-      const uint32_t o = offA[i] + k0 - (8 * chunk < valid ? 0 : 8 * chunk);
-      lds_direct_16(ld_A + o, reinterpret_cast<uint16_t*>(base + (4 * wave + i) * 1024));
+    for (int i = 0; i < S::A_PW; ++i) {
+      // chunks past K fetch the chunk 128 columns (or more) back: never read
+      const int r = S::A_RPI * (wave + NW * i) + lane / S::A_CH;
+      const int chunk = (lane % S::A_CH) ^ (r & 15);
+      const int back = chunk / 16 >= gv ? (chunk / 16 - gv + 1) * 128 : 0;
+      const uint32_t o = offA[i] + (uint32_t)k0 - (uint32_t)back;  // >= 0: back <= 8 chunk
+      if (r < rows_ld || lane == 0)
+        lds_direct_16(ld_A + o, reinterpret_cast<uint16_t*>(base + (wave + NW * i) * 1024));
     }
 #pragma unroll
-    for (int i = 0; i < W_PER_WAVE; ++i) {
-      const int chunk = ws_swz(4 * (wave + 4 * i) + lane / 16, lane % 16);  // 32 columns
-      const uint32_t o = offW[i] + k0 / 2 - (32 * chunk < valid ? 0 : 16 * chunk);
-      lds_direct_16(ld_W + o, reinterpret_cast<uint16_t*>(base + A_BYTES + (wave + 4 * i) * 1024));
+    for (int i = 0; i < S::W_PW; ++i) {
+      const int r = S::W_RPI * (wave + NW * i) + lane / S::W_CH;
+      const int c = w4_swz<S::W_CH>(r, lane % S::W_CH);
+      const int back = c / 4 >= gv ? (c / 4 - gv + 1) * 64 : 0;
+      const uint32_t o = offW[i] + (uint32_t)(k0 / 2) - (uint32_t)back;  // >= 0: back <= 16 c
+      lds_direct_16(ld_W + o,
+                    reinterpret_cast<uint16_t*>(base + S::A_BYTES + (wave + NW * i) * 1024));
     }
-    if (lane < 8) {  // groups past K fetch the last group again (never read)
-      const int rs = GATEUP ? 2 * N : N;
-      const int gk = min(k0 / 128 + (lane >> 1), groups - 1);
-      const uint32_t o = offS + (uint32_t)(gk - (lane >> 1)) * rs;
-      lds_direct_16(ld_S + o,
-                    reinterpret_cast<uint16_t*>(base + A_BYTES + W_BYTES + wave * S_WAVE));
+    if (lane < S::S_LANES) {
+      // K group of the piece; groups past K fetch the stage's last one again
+      const int gk = k0 / 128 + min(lane / (2 * NBLK), gv - 1);
+      lds_direct_16(ld_S + (offS + (uint32_t)gk * (uint32_t)rs),
+                    reinterpret_cast<uint16_t*>(base + S::A_BYTES + S::W_BYTES +
+                                                wave * S::S_WAVE));
     }
     slot_ld = slot_ld + 1 == STAGES ? 0 : slot_ld + 1;
     if (++kt_ld == nk) {
@@ -1229,49 +1295,65 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_w4_kernel(GemmProblem 
     ws_locate<BN>(P, t_cp, row0_cp, row_end_cp, n0_cp, g_cp);
   };
 
-  // element (reg r, lane l) of the accumulators: row 4(l/16) + r of the
-  // tile, weight row 16*wave + l%16
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, accP = acc, accX = acc;
-  const int fr = lane & 15;
+  // element (reg r, lane l) of block j's accumulator: row 4(l/16) + r of the
+  // tile, weight row 16 (NBLK wave + j) + l%16
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[NBLK];
+#pragma unroll
+  for (int j = 0; j < NBLK; ++j) acc[j] = zero;
+  const int fr = lane & 15, q = lane >> 4;
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u,
                                                              0x3F803F80u, 0x3F803F80u});
   auto store = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = row0_cp + 4 * (lane >> 4) + r;
-      if (GATEUP) {
-        const float u = __shfl_xor(acc[r], 8, 64);  // lanes j, j+8: g and u of one column
-        const int col = n0_cp + 8 * wave + (fr & 7);
-        if (fr < 8 && row < row_end_cp && col < N)
-          static_cast<uint16_t*>(P.out)[row * N + col] =
-              (uint16_t)f32_to_bf16_bits(swiglu_clamped(acc[r], u, limit));
-      } else {
-        const int col = n0_cp + 16 * wave + fr;
-        if (row < row_end_cp && col < N) static_cast<float*>(P.out)[row * N + col] = acc[r];
+    for (int j = 0; j < NBLK; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = row0_cp + 4 * q + r;
+        if (GATEUP) {
+          const float u = __shfl_xor(acc[j][r], 8, 64);  // lanes i, i+8: g and u of one column
+          const int col = n0_cp + 8 * (NBLK * wave + j) + (fr & 7);
+          if (fr < 8 && row < row_end_cp && col < N)
+            static_cast<uint16_t*>(P.out)[row * N + col] =
+                (uint16_t)f32_to_bf16_bits(swiglu_clamped(acc[j][r], u, limit));
+        } else {
+          const int col = n0_cp + 16 * (NBLK * wave + j) + fr;
+          if (row < row_end_cp && col < N) static_cast<float*>(P.out)[row * N + col] = acc[j][r];
+        }
       }
     }
   };
-  auto substep = [&](const uint8_t* base, int ks) __attribute__((always_inline)) {
+  // one 128-column group s of the stage at base: four substeps (the first
+  // MFMA of each sum starts from zero), then the scaled fold
+  auto group = [&](const uint8_t* base, int s) __attribute__((always_inline)) {
     const uint16_t* As = reinterpret_cast<const uint16_t*>(base);
-    const uint8_t* Ws = base + A_BYTES;
-    const bf16x8_t a =
-        *reinterpret_cast<const bf16x8_t*>(&As[fr * KB + ws_swz(fr, ks * 4 + (lane >> 4)) * 8]);
-    const int br = 16 * wave + fr;
-    const uint32_t d =
-        *reinterpret_cast<const uint32_t*>(&Ws[br * W_ROW + ws_swz(br, ks) * 16 + 4 * (lane >> 4)]);
-    accP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w4_codes_to_bf16(d), accP, 0, 0, 0);
-    accX = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, accX, 0, 0, 0);
-    if ((ks & 3) == 3) {  // end of a 128-column group: scale and fold in
-      const uint16_t sb = *reinterpret_cast<const uint16_t*>(
-          base + A_BYTES + W_BYTES + wave * S_WAVE + 16 * (2 * (ks >> 2) + (fr >> 3)) + 2 * (fr & 7));
-      const float sc = __uint_as_float((uint32_t)sb << 16);
+    const uint8_t* Ws = base + S::A_BYTES;
+    const uint8_t* Ss = base + S::A_BYTES + S::W_BYTES + wave * S::S_WAVE + 32 * NBLK * s;
+    u32x4_t codes[NBLK];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        acc[r] = fmaf(sc, fmaf(-136.0f, accX[r], accP[r]), acc[r]);
-        accP[r] = 0.f;
-        accX[r] = 0.f;
-      }
+    for (int j = 0; j < NBLK; ++j) {
+      const int br = 16 * (NBLK * wave + j) + fr;
+      codes[j] = *reinterpret_cast<const u32x4_t*>(
+          &Ws[br * S::W_ROW + w4_swz<S::W_CH>(br, 4 * s + q) * 16]);
+    }
+    f32x4_t accP[NBLK], accX;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int chunk = 16 * s + 4 * q + t;
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&As[fr * KB + (chunk ^ fr) * 8]);
+#pragma unroll
+      for (int j = 0; j < NBLK; ++j)
+        accP[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w4_codes_to_bf16(codes[j][t]),
+                                                          t == 0 ? zero : accP[j], 0, 0, 0);
+      accX = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, t == 0 ? zero : accX, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+      const int so = GATEUP ? (fr < 8 ? 0 : 16 * NBLK) + 2 * (8 * j + (fr & 7)) : 2 * (16 * j + fr);
+      const float sc = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(Ss + so) << 16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc, fmaf(-136.0f, accX[r], accP[j][r]), acc[j][r]);
     }
   };
 
@@ -1284,18 +1366,18 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_w4_kernel(GemmProblem 
     // as in the bf16 kernel: own loads of this stage landed, own LDS reads
     // done, then the barrier
     if (t_ld < t_end)
-      PL_WAIT_VM_LDS((STAGES - 2) * PER_WAVE);
+      PL_WAIT_VM_LDS((STAGES - 2) * S::PER_WAVE);
     else
       PL_WAIT_VM_LDS(0);
     pl_barrier();
     issue_next();
-    const uint8_t* base = smem + slot_cp * STAGE_BYTES;
-    const int sub_valid = (K - kt_cp * KB) >> 5;  // 32-wide substeps left in K (a multiple of 4)
-    if (sub_valid >= SUB) {
+    const uint8_t* base = smem + slot_cp * S::STAGE;
+    const int gv = groups - kt_cp * S::GROUPS;  // groups of K left
+    if (gv >= S::GROUPS) {
 #pragma unroll
-      for (int ks = 0; ks < SUB; ++ks) substep(base, ks);
+      for (int s = 0; s < S::GROUPS; ++s) group(base, s);
     } else {
-      for (int ks = 0; ks < sub_valid; ++ks) substep(base, ks);
+      for (int s = 0; s < gv; ++s) group(base, s);
     }
     slot_cp = slot_cp + 1 == STAGES ? 0 : slot_cp + 1;
     if (++kt_cp == nk) {
@@ -1304,7 +1386,8 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_w4_kernel(GemmProblem 
       if (t_cp >= t_end) break;
       kt_cp = 0;
       setup_cp();
-      acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NBLK; ++j) acc[j] = zero;
     }
   }
 }
@@ -1366,12 +1449,10 @@ hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limi
   return hipGetLastError();
 }
 
-template <bool GATEUP, int STAGES>
+template <bool GATEUP, int NBLK, int KB, int NW, int STAGES>
 hipError_t launch_wstream_w4(const GemmProblem& a, float limit, hipStream_t stream, int max_wgs) {
-  constexpr size_t stage = (size_t)WS_BM * W4_KB * 2 + (size_t)WS_NB * W4_KB / 2 + 4 * 128;
-  const size_t lds = STAGES * stage;
-  static_assert(STAGES * stage <= 160 * 1024, "LDS");
-  auto kern = grouped_wstream_w4_kernel<GATEUP, STAGES>;
+  const size_t lds = (size_t)STAGES * W4Shape<NBLK, KB, NW>::STAGE;
+  auto kern = grouped_wstream_w4_kernel<GATEUP, NBLK, KB, NW, STAGES>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1380,7 +1461,7 @@ hipError_t launch_wstream_w4(const GemmProblem& a, float limit, hipStream_t stre
     attr_set = true;
   }
   const int grid = max_wgs > 0 ? std::min(max_wgs, device_cu_count()) : device_cu_count();
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, a, limit);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream, a, limit);
   return hipGetLastError();
 }
 
@@ -1455,6 +1536,8 @@ int gemm_tile_n(GemmVariant v, bool gateup) {
   return 128;
 }
 
+int gemm_w4_tile_n(bool gateup) { return gateup ? 8 * W4_NBLK * W4_NW : 16 * W4_NBLK * W4_NW; }
+
 hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
                                 int32_t* start0, int32_t* start1, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, stream, group_offsets, G, bm0,
@@ -1468,8 +1551,9 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
   if (a.S != nullptr) {  // W4A16 weights: weight streaming, one problem per launch
     if (v != GemmVariant::kWStream || b != nullptr || a.K % 128 != 0)
       return hipErrorInvalidValue;
-    if (gateup) return launch_wstream_w4<true, 4>(a, limit, stream, max_wgs);
-    return launch_wstream_w4<false, 4>(a, limit, stream, max_wgs);
+    if (gateup)
+      return launch_wstream_w4<true, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);
+    return launch_wstream_w4<false, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);
   }
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
   if (v == GemmVariant::kWStream) {  // 512-byte row pieces, four stages

@@ -37,6 +37,7 @@ struct GemmProblem {
 enum class GemmVariant { kTile32, kTile128, kWStream, kPipe256W8, kPingPong };
 int gemm_tile_m(GemmVariant v);
 int gemm_tile_n(GemmVariant v, bool gateup);
+int gemm_w4_tile_n(bool gateup);  // output columns of a W4A16 weight-streaming tile
 
 // K-slices of the router GEMM (partials are summed in slice order by the
 // top-k kernel); `partial` needs splits*T*E floats when splits > 1.

@@ -27,7 +27,8 @@ bf16 tensors are held as uint16 bit patterns (round-to-nearest-even of
 the fp32 draw).
 
 W4A16 routed experts (workloads with w4): per weight a uniform nibble u in
-[0, 15] (two per byte, low nibble = even column; the value is u - 8), and
+[0, 15] (the value is u - 8; 4-byte words of 8 columns, byte j holding
+columns j and j + 4 in its low and high nibble), and
 per row and group of 128 columns a bf16 scale weight_std / sqrt(21.5) *
 U(0.5, 1.5) (21.5 is the mean of (u - 8)^2), stored [K/128, rows]; so the
 weights have about the bf16 experts' spread.  The shared expert stays bf16.

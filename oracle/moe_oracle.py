@@ -60,10 +60,13 @@ W4A16 routed experts (optional, the next step after the bf16 path): the
 pages name a grouped W4A16 expert GEMM ("Module glm5next_mlp", Modules
 forward_prefill_gemm and Constants MOE_GROUPED_MODULE / W4A16_GEMV_MODULE)
 but not its format.  The reading taken here: signed 4-bit integers in
-offset-binary nibbles (u - 8), two per byte along K (low nibble first),
-one bf16 scale per output row and group of 128 columns, stored group-major
-([K/128, rows]); the weight is exactly (u - 8) * scale and the expert FFN
-then runs as above on those values.  The shared expert stays bf16.
+offset-binary nibbles (u - 8), packed along K in 4-byte words of 8
+columns, byte j of a word holding its columns j (low nibble) and j + 4
+(high nibble) -- the interleaved order lets a kernel split a word into its
+low and high nibbles with one mask each; one bf16 scale per output row and
+group of 128 columns, stored group-major ([K/128, rows]); the weight is
+exactly (u - 8) * scale and the expert FFN then runs as above on those
+values.  The shared expert stays bf16.
 
 Precision: all sums in float64 (BLAS matmul as a step), single roundings
 at the points named above.  bf16 tensors are uint16 bit patterns.
@@ -211,17 +214,17 @@ W4_GROUP = 128
 def dequant_w4(q: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
     """W4A16 weights -> float64 values (exact).
 
-    q      uint8 [R, K/2]: byte j holds column 2j (low nibble) and column
-           2j+1 (high nibble); a nibble u stands for the integer u - 8
+    q      uint8 [R, K/2]: per 4-byte word w (columns 8w .. 8w+7), byte
+           4w + j holds column 8w + j (low nibble) and column 8w + j + 4
+           (high nibble); a nibble u stands for the integer u - 8
     scale  bf16 [ceil(K/128), R]: one scale per row and group of 128 columns
     Returns w [R, K] with w[r, c] = (u[r, c] - 8) * scale[c // 128, r].
     """
     q = np.asarray(q, dtype=np.uint8)
     R, half = q.shape
     K = 2 * half
-    u = np.empty((R, K), dtype=np.int64)
-    u[:, 0::2] = q & 0x0F
-    u[:, 1::2] = q >> 4
+    words = q.reshape(R, K // 8, 4).astype(np.int64)
+    u = np.concatenate([words & 0x0F, words >> 4], axis=2).reshape(R, K)
     s = bf16_to_f64(np.asarray(scale_bits, dtype=np.uint16))   # [groups, R]
     per_col = np.repeat(s.T, W4_GROUP, axis=1)[:, :K]
     return (u - 8).astype(np.float64) * per_col

@@ -14,28 +14,32 @@ def _bf16(v):
 
 
 def _pack(codes):
-    """codes: int array [R, K] of nibbles 0..15 -> bytes [R, K/2], even
-    column in the low nibble (written element by element)."""
+    """codes: int array [R, K] of nibbles 0..15 -> bytes [R, K/2]: in each
+    4-byte word of 8 columns, byte j holds column j (low nibble) and
+    column j + 4 (high nibble) (written element by element)."""
     R, K = codes.shape
     out = np.zeros((R, K // 2), dtype=np.uint8)
     for r in range(R):
-        for j in range(K // 2):
-            out[r, j] = int(codes[r, 2 * j]) | (int(codes[r, 2 * j + 1]) << 4)
+        for w in range(K // 8):
+            for j in range(4):
+                lo = int(codes[r, 8 * w + j])
+                hi = int(codes[r, 8 * w + j + 4])
+                out[r, 4 * w + j] = lo | (hi << 4)
     return out
 
 
 def test_dequant_hand_example():
     # one row, K = 256: two groups of 128 columns
     q = np.full((1, 128), 0x88, dtype=np.uint8)   # nibble 8 everywhere -> 0
-    q[0, 0] = 0x9F     # columns 0, 1: nibbles 15, 9 -> 7, 1
-    q[0, 64] = 0x70    # columns 128, 129: nibbles 0, 7 -> -8, -1
-    q[0, 127] = 0x0F   # columns 254, 255: nibbles 15, 0 -> 7, -8
+    q[0, 0] = 0x9F     # byte 0 of word 0: columns 0, 4: nibbles 15, 9 -> 7, 1
+    q[0, 65] = 0x70    # byte 1 of word 16: columns 129, 133: nibbles 0, 7 -> -8, -1
+    q[0, 127] = 0x0F   # byte 3 of word 31: columns 251, 255: nibbles 15, 0 -> 7, -8
     scale = _bf16([[0.5], [-2.0]])                 # [groups, rows]
     w = mo.dequant_w4(q, scale)
     assert w.shape == (1, 256)
-    assert w[0, 0] == 3.5 and w[0, 1] == 0.5
-    assert w[0, 128] == 16.0 and w[0, 129] == 2.0
-    assert w[0, 254] == -14.0 and w[0, 255] == 16.0
+    assert w[0, 0] == 3.5 and w[0, 4] == 0.5
+    assert w[0, 129] == 16.0 and w[0, 133] == 2.0
+    assert w[0, 251] == -14.0 and w[0, 255] == 16.0
     assert np.count_nonzero(w) == 6
 
 
@@ -69,8 +73,9 @@ def _w4_exact_pair(seed):
         bits = np.empty((E, R, 2 * half), dtype=np.uint16)
         for e in range(E):
             codes = np.empty((R, 2 * half), dtype=np.int64)
-            codes[:, 0::2] = q[e] & 15
-            codes[:, 1::2] = q[e] >> 4
+            for j in range(4):   # byte j of each 4-byte word: columns j, j + 4
+                codes[:, j::8] = q[e][:, j::4] & 15
+                codes[:, j + 4::8] = q[e][:, j::4] >> 4
             sv = moe_inputs.bf16_bits_to_f32(s[e])           # [groups, R]
             vals = (codes - 8) * np.repeat(sv.T, 128, axis=1)[:, :2 * half]
             bits[e] = _bf16(vals)
