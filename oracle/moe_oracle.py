@@ -46,6 +46,15 @@ What it computes, step by step, and where each step comes from:
      section "One all-reduce for both EP and TP" (shared output and routed
      slots added in one combine); shortcut_block module doc and
      ShortcutMoEBlock._postprocess (post-norm of the merged sum).
+  S8 (optional) finish: the residual add that closes the layer,
+     out = bf16(bf16(o * c0) + bf16(res * c1)) on the layer output o
+     (after the post-norm, which a plain layer may also ask for: Beam's
+     sandwich norm on the MLP output).  Source:
+     "bridge.models.beam.modeling_beam", _beam_bda (bias -> post norm ->
+     dropout -> depth-scaled residual add) and scaled_residual_add (the
+     output times coefs[0] plus the residual times coefs[1], in the
+     residual's dtype); "core.models.hybrid.shortcut_block",
+     ShortcutMoEBlock._postprocess (finish residual/BDA): c0 = c1 = 1.
 
 Readings where the pages are silent (each also listed in the design
 notes): bias added to the sigmoid score, not to the logit; no
@@ -320,12 +329,36 @@ def combine(y_perm: np.ndarray, w: np.ndarray, inv_pos: np.ndarray,
     return z
 
 
+# ------------------------------------------------ S8 finish (optional) ---
+
+def finish(out_bits: np.ndarray, residual_bits: np.ndarray, out_scale: float = 1.0,
+           residual_scale: float = 1.0) -> np.ndarray:
+    """S8: the residual add after the layer output, bf16 bits in and out.
+
+    The pages' scaled_residual_add is output * coefs[0] + residual *
+    coefs[1] in the residual's dtype: bf16 tensor arithmetic, where each
+    product and the sum are computed in fp32 and rounded to bf16.  The
+    layer has no output bias and dropout is the identity at inference, so
+    the bias-dropout-add of the plain (ScMoE) finish is the case
+    c0 = c1 = 1: bf16(o + res).  c0 and c1 are the caller's (the pages give
+    only that their squares sum to one for Beam's depth-scaled add).
+    """
+    o = bf16_to_f64(out_bits).astype(np.float32)
+    r = bf16_to_f64(residual_bits).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        a = bf16_of_f32(o * np.float32(out_scale))
+        b = bf16_of_f32(r * np.float32(residual_scale))
+        return bf16_of_f32(bf16_to_f64(a).astype(np.float32) + bf16_to_f64(b).astype(np.float32))
+
+
 # ------------------------------------------------------------ the layer ---
 
 def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
             eps: float = 1e-6, ids: np.ndarray | None = None,
             round_h: bool = True, expert_range: tuple[int, int] | None = None,
-            include_shared: bool = True) -> dict:
+            include_shared: bool = True, post_norm: bool = False,
+            residual: np.ndarray | None = None, out_scale: float = 1.0,
+            residual_scale: float = 1.0) -> dict:
     """The whole layer (S0-S7) on one batch.
 
     `inp` holds the arrays named in moe_inputs.generate (x, x_cur,
@@ -336,11 +369,15 @@ def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
     oracle's unbiased scores for those ids); this re-derives the layer for
     tokens whose selection is a near-tie.  `expert_range` keeps only the
     routed slots of experts in [lo, hi) (one expert-parallel rank's share);
-    `include_shared` drops the shared expert.
+    `include_shared` drops the shared expert.  `post_norm` applies the
+    post-norm (gamma_post) to a plain layer too; `residual` (bf16 bits
+    [T, H]) adds the finish S8 with the two scales.
 
     Returns a dict with every intermediate: xr, logits, s, s_biased, gap,
-    ids, w, offsets, sorted_token, inv_pos, h_perm, y_perm, hs, ys, z, out
-    (bf16 bits) and out_f64 (the pre-rounding value).
+    ids, w, offsets, sorted_token, inv_pos, h_perm, y_perm, hs, ys, z,
+    out_layer (bf16 bits of the layer output), out (the same, or after the
+    finish when a residual is given) and out_f64 (the value before the
+    layer output's rounding).
     """
     x = inp["x"]
     T, H = x.shape
@@ -376,12 +413,15 @@ def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
     res["ys"] = ys
     z = combine(y_perm, w, p["inv_pos"], ys)
     res["z"] = z
-    if scmoe:
+    if scmoe or post_norm:
         v = rmsnorm_f64(z, inp.get("gamma_post"), eps)
     else:
         v = z
     res["out_f64"] = v
-    res["out"] = bf16_round(v)
+    res["out_layer"] = bf16_round(v)
+    res["out"] = res["out_layer"]
+    if residual is not None:
+        res["out"] = finish(res["out_layer"], residual, out_scale, residual_scale)
     return res
 
 

@@ -89,3 +89,34 @@ def _shared_scaled(y_perm, w, inv_pos, ys):
 def test_planted_mistake_is_caught(monkeypatch, name, attr, fake):
     monkeypatch.setattr(mo, attr, fake)
     assert not _hand_matches(), name
+
+
+# Planted mistakes in the finish step S8: each must fail a pin of
+# test_oracle_finish (run here against the mutated function).
+_real_finish = mo.finish
+
+
+def _finish_one_rounding(o, r, c0=1.0, c1=1.0):
+    v = mo.bf16_to_f64(o) * c0 + mo.bf16_to_f64(r) * c1
+    return mo.bf16_round(v)
+
+
+def _finish_scales_swapped(o, r, c0=1.0, c1=1.0):
+    return _real_finish(o, r, c1, c0)
+
+
+@pytest.mark.parametrize("name,fake", [
+    ("finish rounded once", _finish_one_rounding),
+    ("finish scales swapped", _finish_scales_swapped),
+])
+def test_planted_finish_mistake_is_caught(monkeypatch, name, fake):
+    from tests import test_oracle_finish as pins
+    monkeypatch.setattr(mo, "finish", fake)
+    failed = 0
+    for pin in (pins.test_finish_hand_values, pins.test_finish_is_torch_bf16_arithmetic,
+                pins.test_finish_identities):
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, name
