@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the routed-MoE MLP forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--finish]
 
 One step = one moe_forward call (router, top-k, permute, grouped gate_up
 with the SwiGLU epilogue, grouped down, combine) over one batch of seeded
@@ -10,8 +10,10 @@ steps between two device synchronisations.  Prints one JSON line.
 
 The default workload is the decode-shaped layer (T=32, H=4096, E=64,
 top-8, I=1408, shared I_s=2816), which is bound by HBM bandwidth; the
-prefill, zipf and scmoe workloads (bound by the bf16 matrix cores) can be
-asked for with --workload.
+prefill, zipf and scmoe workloads (bound by the bf16 matrix cores) and
+decode_w4 (the decode shape with W4A16 routed experts) can be asked for
+with --workload.  --finish runs moe_forward_finish instead: the residual
+add after the layer output, fused into the combine.
 
 roofline: the dominant kernel is the grouped gate_up launch.  With few
 rows per expert (HBM-bound, weight streaming) it holds the routed experts
@@ -107,7 +109,7 @@ def cpu_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(wl, inp, sample_tokens: int, min_seconds: float) -> dict:
+def cpu_baseline(wl, inp, sample_tokens: int, min_seconds: float, residual=None) -> dict:
     """The oracle, as it stands, on consecutive chunks of `sample_tokens`
     tokens of the same batch (wrapping around it), one oracle forward per
     chunk, until at least `min_seconds` of CPU time (at most 64 chunks)."""
@@ -118,8 +120,9 @@ def cpu_baseline(wl, inp, sample_tokens: int, min_seconds: float) -> dict:
     while chunks < 64 and (dt < min_seconds or chunks == 0):
         rows = (np.arange(s) + chunks * s) % wl.T
         sub = mo.take_rows(inp, rows)
+        fin = {} if residual is None else dict(residual=residual[rows])
         t0 = time.perf_counter()
-        mo.forward(sub, k=wl.k, rsf=wl.rsf, limit=wl.limit, scmoe=wl.scmoe, eps=wl.eps)
+        mo.forward(sub, k=wl.k, rsf=wl.rsf, limit=wl.limit, scmoe=wl.scmoe, eps=wl.eps, **fin)
         dt += time.perf_counter() - t0
         done += s
         chunks += 1
@@ -211,6 +214,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle time to spend on the baseline sample (at least)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--finish", action="store_true",
+                    help="add the residual after the layer output (moe_forward_finish, "
+                         "coefficients 1: the residual/bias-dropout-add), fused into the combine")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB streaming copy (counter calibration)")
     ap.add_argument("--write-traffic", nargs=4,
@@ -273,8 +279,22 @@ def main() -> int:
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
 
+    residual_bits = None
+    fin = None
+    if args.finish:
+        residual_bits = moe_inputs.f32_to_bf16_bits(
+            np.random.default_rng(1).standard_normal((T, H)).astype(np.float32))
+        residual = dev_bf16(residual_bits)
+        fin = moe.make_finish(residual, 1.0, 1.0)
+
+    def forward(probes):
+        if fin is not None:
+            moe.moe_forward_finish(params, x, x_cur, weights, fin, out, probes, ws)
+        else:
+            moe.moe_forward(params, x, x_cur, weights, out, probes, ws)
+
     # one probed call to learn the routing (touched experts) for the byte count
-    moe.moe_forward(params, x, x_cur, weights, out, moe.make_probes(expert_offsets=offsets), ws)
+    forward(moe.make_probes(expert_offsets=offsets))
     torch.cuda.synchronize()
     counts = np.diff(offsets.cpu().numpy())
     touched = int(np.sum(counts > 0))
@@ -285,11 +305,11 @@ def main() -> int:
 
     print(f"[bench] warmup {warmup}, steps {steps}", file=sys.stderr, flush=True)
     for _ in range(warmup):
-        moe.moe_forward(params, x, x_cur, weights, out, None, ws)
+        forward(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_forward(params, x, x_cur, weights, out, probes[i], ws)
+        forward(probes[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
@@ -307,7 +327,8 @@ def main() -> int:
     gu_bytes = touched * wbytes(2 * I, H) + T * H * 2 + T * k * I * 2
     gu_flops = 2 * T * k * H * 2 * I + 2 * T * H * 2 * Is
     layer_bytes = (touched * (wbytes(2 * I, H) + wbytes(H, I)) + 3 * Is * H * 2 + E * H * 4 + E * 4
-                   + T * H * 2 * (2 if wl.scmoe else 1) + T * H * 2)
+                   + T * H * 2 * (2 if wl.scmoe else 1) + T * H * 2
+                   + (T * H * 2 if args.finish else 0))
     layer_flops = 2 * T * k * H * 3 * I + 2 * T * H * 3 * Is
     router_flops = 2 * T * H * E
     traffic = committed_traffic(wl.label())
@@ -336,7 +357,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle on {sample} tokens", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, inp, sample, args.cpu_seconds)
+        cpu = cpu_baseline(wl, inp, sample, args.cpu_seconds, residual_bits)
 
     line = {
         "metric": METRIC, "value": round(T / s_step, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -345,7 +366,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.label(), "T": T, "H": H, "E": E, "k": k, "I": I, "I_shared": Is,
                    "routed_scaling_factor": wl.rsf, "swiglu_limit": wl.limit,
-                   "scmoe": wl.scmoe, "seed": 0, "parallelism": "ep1_tp1"},
+                   "scmoe": wl.scmoe, "seed": 0, "parallelism": "ep1_tp1",
+                   "finish": "residual_add" if args.finish else None},
         "roofline": roofline, "cpu_baseline": cpu, "layer": layer,
     }
     print(json.dumps(line), flush=True)

@@ -15,6 +15,7 @@
  *   shared:       the same FFN on x (ScMoE: x_cur), width I_s, unscaled
  *   z  = sum_j w[t,j] * y[t,j] + ys[t]                one combine, fp32
  *   out = bf16(z)           [ScMoE] out = bf16(RMSNorm_post(z))
+ *   [finish] out = bf16(bf16(out * c0) + bf16(residual * c1))   (optional)
  *
  * Sources (web pages; cited by title and section):
  *   "Module glm5next_mlp" (metrale_model_arch docs): section "Numerics the
@@ -34,7 +35,11 @@
  *   "core.models.hybrid.shortcut_block" (Megatron-Core API docs): module
  *     doc and ShortcutMoEBlock (ScMoE: the preceding layer's normalised
  *     representation is routed, the shared expert runs on the current one,
- *     the merged sum is normalised again).
+ *     the merged sum is normalised again, _postprocess finishes the
+ *     residual/BDA).
+ *   "bridge.models.beam.modeling_beam": _beam_bda, scaled_residual_add and
+ *     depth_scaled_residual_coefs (post-sublayer norm, then a residual add
+ *     with two scalar coefficients in the residual's dtype).
  *
  * Conventions shared by every entry point:
  *   - bf16 values are passed as uint16_t bit patterns (moe_bf16).
@@ -130,6 +135,31 @@ typedef struct moe_weights {
   const uint8_t* w_down_q;          /* [E, H, I/2] codes                          */
   const moe_bf16* w_down_scale;     /* [E, I/128, H] bf16                         */
 } moe_weights;
+
+/* Finish of the layer, fused into its combine (moe_forward_finish,
+ * moe_combine_finish): the residual add after the layer output,
+ *   out = bf16(bf16(o * out_scale) + bf16(residual * residual_scale)),
+ * each product and the sum computed in fp32 and rounded to bf16 (the add in
+ * the residual's dtype), o the layer output as moe_forward writes it: after
+ * the post-norm, which post_norm = 1 also applies to a plain layer (a
+ * sandwich norm on the MLP output: RMSNorm(z) * gamma_post, eps =
+ * norm_eps).  out_scale = residual_scale = 1 is the ScMoE block's
+ * residual/bias-dropout-add at inference (the layer has no output bias and
+ * dropout is the identity); other values are Beam's depth-scaled residual
+ * add, whose two coefficients the caller computes (their squares sum to one
+ * there; the library does not require it).
+ * Sources: "bridge.models.beam.modeling_beam", _beam_bda,
+ * scaled_residual_add, depth_scaled_residual_coefs,
+ * BeamTransformerLayerSubmodules.post_mlp_layernorm;
+ * "core.models.hybrid.shortcut_block", ShortcutMoEBlock._postprocess. */
+typedef struct moe_finish {
+  const moe_bf16* residual;  /* [T, H] bf16, required; may be the out buffer   */
+                             /* itself (the add is then in place)             */
+  float out_scale;           /* c0, finite                                    */
+  float residual_scale;      /* c1, finite                                    */
+  int32_t post_norm;         /* 1 = RMSNorm_post also without ScMoE (needs     */
+                             /* norm_eps > 0, H <= 8192); 0 = ScMoE's only    */
+} moe_finish;
 
 /* Step boundaries of moe_forward at which caller-created HIP events can be
  * recorded on `stream` (for timing a step on the stream it runs on).
@@ -245,6 +275,14 @@ moe_status moe_combine(const moe_params* p, const float* y_perm, const float* to
                        const int32_t* inv_pos, const float* y_shared, const float* gamma_post,
                        moe_bf16* out, hipStream_t stream);
 
+/* moe_combine followed by the finish *fin (required), in the same kernel:
+ * the post-norm when p->scmoe or fin->post_norm, then the residual add
+ * (moe_finish).  out may be fin->residual (in place). */
+moe_status moe_combine_finish(const moe_params* p, const float* y_perm, const float* topk_w,
+                              const int32_t* inv_pos, const float* y_shared,
+                              const float* gamma_post, const moe_finish* fin, moe_bf16* out,
+                              hipStream_t stream);
+
 /* The whole layer.
  *   x_routed  [T, H] bf16: the layer input (ScMoE: the preceding layer's
  *             hidden, normalised here before routing and the experts)
@@ -265,6 +303,14 @@ moe_status moe_combine(const moe_params* p, const float* y_perm, const float* to
 moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
                        const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward with the finish *fin (required) fused into its combine (see
+ * moe_finish); out may be fin->residual (in place).  Everything else as in
+ * moe_forward. */
+moe_status moe_forward_finish(const moe_params* p, const moe_bf16* x_routed,
+                              const moe_bf16* x_shared, const moe_weights* w,
+                              const moe_finish* fin, moe_bf16* out, const moe_probes* probes,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static text naming a status code. */
 const char* moe_status_string(moe_status s);

@@ -49,6 +49,11 @@ class moe_weights(Structure):
         "w_down_scale")]
 
 
+class moe_finish(Structure):
+    _fields_ = [("residual", c_void_p), ("out_scale", c_float), ("residual_scale", c_float),
+                ("post_norm", c_int32)]
+
+
 MOE_EV_BEGIN, MOE_EV_PRENORM, MOE_EV_ROUTER, MOE_EV_PERMUTE = 0, 1, 2, 3
 MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_COMBINE, MOE_EV_COUNT = 4, 5, 6, 7
 
@@ -86,6 +91,11 @@ def _load() -> ctypes.CDLL:
                              c_void_p]),
         "moe_forward": (st, [P, c_void_p, c_void_p, POINTER(moe_weights), c_void_p,
                              POINTER(moe_probes), c_void_p, c_size_t, c_void_p]),
+        "moe_combine_finish": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    POINTER(moe_finish), c_void_p, c_void_p]),
+        "moe_forward_finish": (st, [P, c_void_p, c_void_p, POINTER(moe_weights),
+                                    POINTER(moe_finish), c_void_p, POINTER(moe_probes), c_void_p,
+                                    c_size_t, c_void_p]),
         "moe_status_string": (c_char_p, [c_int]),
         "moe_last_error": (c_char_p, []),
     }
@@ -99,7 +109,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
             "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
-            "moe_forward", "moe_status_string", "moe_last_error")
+            "moe_combine_finish", "moe_forward", "moe_forward_finish", "moe_status_string",
+            "moe_last_error")
 
 
 def _status_name(s: int) -> str:
@@ -182,6 +193,19 @@ def moe_combine(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, out, stre
                             _ptr(y_shared), _ptr(gamma_post), _ptr(out), _stream(stream)))
 
 
+def make_finish(residual, out_scale=1.0, residual_scale=1.0, post_norm=False) -> moe_finish:
+    """The residual add after the layer output (moe_finish in moe.h)."""
+    return moe_finish(_ptr(residual), out_scale, residual_scale, int(bool(post_norm)))
+
+
+def moe_combine_finish(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, fin, out,
+                       stream=None):
+    f = ctypes.byref(fin) if fin is not None else None
+    _check(_lib.moe_combine_finish(ctypes.byref(params), _ptr(y_perm), _ptr(topk_w),
+                                   _ptr(inv_pos), _ptr(y_shared), _ptr(gamma_post), f, _ptr(out),
+                                   _stream(stream)))
+
+
 def make_weights(w_router, corr_bias, w_gate_up, w_down, ws_gate_up=None, ws_down=None,
                  gamma_pre=None, gamma_post=None, w_gate_up_q=None, w_gate_up_scale=None,
                  w_down_q=None, w_down_scale=None) -> moe_weights:
@@ -208,3 +232,12 @@ def moe_forward(params, x_routed, x_shared, weights: moe_weights, out, probes=No
     _check(_lib.moe_forward(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
                             ctypes.byref(weights), _ptr(out), pr, _ptr(ws), _nbytes(ws),
                             _stream(stream)))
+
+
+def moe_forward_finish(params, x_routed, x_shared, weights: moe_weights, fin, out, probes=None,
+                       ws=None, stream=None):
+    f = ctypes.byref(fin) if fin is not None else None
+    pr = ctypes.byref(probes) if probes is not None else None
+    _check(_lib.moe_forward_finish(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
+                                   ctypes.byref(weights), f, _ptr(out), pr, _ptr(ws), _nbytes(ws),
+                                   _stream(stream)))

@@ -401,32 +401,59 @@ moe_status moe_grouped_swiglu_gemm(int32_t n_groups, int64_t M_total, int32_t H,
   return ok();
 }
 
-moe_status moe_combine(const moe_params* p, const float* y_perm, const float* topk_w,
-                       const int32_t* inv_pos, const float* y_shared, const float* gamma_post,
-                       moe_bf16* out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The finish (NULL = none): residual pointer, finite scales, post-norm flag
+// and, for a plain layer's post-norm, the norm's own limits.
+moe_status check_finish(const moe_params* p, const moe_finish* fin) {
+  if (!fin) return MOE_OK;
+  REQUIRE_PTR(fin->residual);
+  if (!std::isfinite(fin->out_scale) || !std::isfinite(fin->residual_scale))
+    return fail(MOE_ERR_INVALID_ARG, "finish scales must be finite");
+  if (fin->post_norm != 0 && fin->post_norm != 1)
+    return fail(MOE_ERR_INVALID_ARG, "finish post_norm = %d is not 0 or 1", fin->post_norm);
+  if (fin->post_norm && !p->scmoe) {
+    if (!(std::isfinite(p->norm_eps) && p->norm_eps > 0.0f))
+      return fail(MOE_ERR_INVALID_ARG, "norm_eps must be finite and > 0 with a post-norm");
+    if (p->H > kMaxNormH)
+      return fail(MOE_ERR_UNSUPPORTED, "post-norm with H = %d > %d", p->H, kMaxNormH);
+  }
+  return MOE_OK;
+}
+
+moe_status combine_impl(const moe_params* p, const float* y_perm, const float* topk_w,
+                        const int32_t* inv_pos, const float* y_shared, const float* gamma_post,
+                        const moe_finish* fin, moe_bf16* out, hipStream_t stream) {
   moe_status s = check_params(p);
   if (s != MOE_OK) return s;
   if (p->T == 0) return ok();
+  if ((s = check_finish(p, fin)) != MOE_OK) return s;
   REQUIRE_PTR(y_perm);
   REQUIRE_PTR(topk_w);
   REQUIRE_PTR(inv_pos);
   OPTIONAL_PTR(y_shared);
   OPTIONAL_PTR(gamma_post);
   REQUIRE_PTR(out);
-  if ((s = device_status(launch_combine(y_perm, topk_w, inv_pos, y_shared, gamma_post, out, p->T,
-                                        p->H, p->k, p->scmoe, p->norm_eps, stream),
+  const int post = p->scmoe || (fin && fin->post_norm);
+  if ((s = device_status(launch_combine(y_perm, topk_w, inv_pos, y_shared, gamma_post,
+                                        fin ? fin->residual : nullptr, fin ? fin->out_scale : 1.f,
+                                        fin ? fin->residual_scale : 1.f, out, p->T, p->H, p->k,
+                                        post, p->norm_eps, stream),
                          "combine")) != MOE_OK)
     return s;
   return ok();
 }
 
-moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
-                       const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
+                        const moe_weights* w, const moe_finish* fin, moe_bf16* out,
+                        const moe_probes* probes, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status s = check_params(p);
   if (s != MOE_OK) return s;
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   if (p->T == 0) return ok();
+  if ((s = check_finish(p, fin)) != MOE_OK) return s;
   REQUIRE_PTR(x_routed);
   if (p->scmoe && !x_shared)
     return fail(MOE_ERR_INVALID_ARG, "scmoe needs x_shared (the current layer's input)");
@@ -572,13 +599,48 @@ moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_
   if (beside &&
       (s = device_status(hipStreamWaitEvent(stream, side->join, 0), "join")) != MOE_OK)
     return s;
+  const int post = p->scmoe || (fin && fin->post_norm);
   if ((s = device_status(launch_combine(L.y, L.w, L.inv_pos, shared ? L.ys : nullptr,
-                                        w->gamma_post, out, T, p->H, p->k, p->scmoe, p->norm_eps,
-                                        stream),
+                                        w->gamma_post, fin ? fin->residual : nullptr,
+                                        fin ? fin->out_scale : 1.f,
+                                        fin ? fin->residual_scale : 1.f, out, T, p->H, p->k,
+                                        post, p->norm_eps, stream),
                          "combine")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_COMBINE)) != MOE_OK) return s;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_combine(const moe_params* p, const float* y_perm, const float* topk_w,
+                       const int32_t* inv_pos, const float* y_shared, const float* gamma_post,
+                       moe_bf16* out, hipStream_t stream) {
+  return combine_impl(p, y_perm, topk_w, inv_pos, y_shared, gamma_post, nullptr, out, stream);
+}
+
+moe_status moe_combine_finish(const moe_params* p, const float* y_perm, const float* topk_w,
+                              const int32_t* inv_pos, const float* y_shared,
+                              const float* gamma_post, const moe_finish* fin, moe_bf16* out,
+                              hipStream_t stream) {
+  if (!fin) return fail(MOE_ERR_INVALID_ARG, "fin is NULL");
+  return combine_impl(p, y_perm, topk_w, inv_pos, y_shared, gamma_post, fin, out, stream);
+}
+
+moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
+                       const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(p, x_routed, x_shared, w, nullptr, out, probes, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_finish(const moe_params* p, const moe_bf16* x_routed,
+                              const moe_bf16* x_shared, const moe_weights* w,
+                              const moe_finish* fin, moe_bf16* out, const moe_probes* probes,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!fin) return fail(MOE_ERR_INVALID_ARG, "fin is NULL");
+  return forward_impl(p, x_routed, x_shared, w, fin, out, probes, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -9,7 +9,17 @@
 //   out[t] = bf16(z[t])  or, for the ScMoE pairing,
 //   out[t] = bf16(z[t] * gamma_post / sqrt(mean(z[t]^2) + eps))
 // ("core.models.hybrid.shortcut_block", ShortcutMoEBlock._postprocess: the
-// merged routed and shared result is normalised).
+// merged routed and shared result is normalised; a plain layer may ask for
+// the same norm: Beam's sandwich norm on the MLP output).
+//
+// Optional finish, fused into the same pass ("bridge.models.beam.
+// modeling_beam", _beam_bda and scaled_residual_add: output * coefs[0] +
+// residual * coefs[1] in the residual's dtype; ShortcutMoEBlock._postprocess:
+// the residual/BDA, coefficients 1):
+//   out[t] = bf16(bf16(o * c0) + bf16(res[t] * c1))     (fp32 products, sum)
+// with o the bf16 layer output above.  out may be the residual buffer itself:
+// each element's residual is read by the thread that writes it, before it
+// writes it.
 //
 // Pre-norm ("core.models.hybrid.shortcut_block", module doc and
 // _moe_router_preprocess: the shortcut input is normalised before routing):
@@ -41,11 +51,28 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
                     f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16));
 }
 
-template <bool POST>
+// bf16(bf16(o * c0) + bf16(r * c1)) for one bf16 value each (bits)
+__device__ __forceinline__ uint32_t finish_bf16(uint32_t o, uint32_t r, float c0, float c1) {
+  const uint32_t a = f32_to_bf16_bits(bf16_bits_to_f32(o) * c0);
+  const uint32_t b = f32_to_bf16_bits(bf16_bits_to_f32(r) * c1);
+  return f32_to_bf16_bits(bf16_bits_to_f32(a) + bf16_bits_to_f32(b));
+}
+
+// four bf16 outputs (packed) through the finish with four residual values
+__device__ __forceinline__ uint2 finish_bf16x4(uint2 o, uint2 r, float c0, float c1) {
+  return make_uint2(finish_bf16(o.x & 0xffffu, r.x & 0xffffu, c0, c1) |
+                        (finish_bf16(o.x >> 16, r.x >> 16, c0, c1) << 16),
+                    finish_bf16(o.y & 0xffffu, r.y & 0xffffu, c0, c1) |
+                        (finish_bf16(o.y >> 16, r.y >> 16, c0, c1) << 16));
+}
+
+// out and residual may be one buffer (no __restrict__ on either)
+template <bool POST, bool RES>
 __global__ __launch_bounds__(CB_THREADS) void combine_kernel(
     const float* __restrict__ y_perm, const float* __restrict__ w,
     const int32_t* __restrict__ inv_pos, const float* __restrict__ y_shared,
-    const float* __restrict__ gamma, uint16_t* __restrict__ out, int H, int k, float eps) {
+    const float* __restrict__ gamma, const uint16_t* residual, float c0, float c1,
+    uint16_t* out, int H, int k, float eps) {
   __shared__ float ws[MOE_MAX_TOP_K_DEV];
   __shared__ int64_t rows[MOE_MAX_TOP_K_DEV];
   __shared__ double red[CB_THREADS / 64];
@@ -58,6 +85,11 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(
   const int H4 = H >> 2;
   const float4* ys4 = y_shared ? reinterpret_cast<const float4*>(y_shared + t * H) : nullptr;
   uint2* o2 = reinterpret_cast<uint2*>(out + t * H);
+  const uint2* r2 = RES ? reinterpret_cast<const uint2*>(residual + t * H) : nullptr;
+  auto put = [&](int c4, uint2 v) {
+    if (RES) v = finish_bf16x4(v, r2[c4], c0, c1);
+    o2[c4] = v;
+  };
 
   auto zval = [&](int c4) {
     float4 z = ys4 ? ys4[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -75,7 +107,7 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(
   if (!POST) {
     for (int c4 = threadIdx.x; c4 < H4; c4 += CB_THREADS) {
       const float4 z = zval(c4);
-      o2[c4] = pack_bf16x4(z.x, z.y, z.z, z.w);
+      put(c4, pack_bf16x4(z.x, z.y, z.z, z.w));
     }
     return;
   }
@@ -98,10 +130,10 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(
     const int c4 = threadIdx.x + i * CB_THREADS;
     if (c4 < H4) {
       const float4 g = gamma ? g4[c4] : make_float4(1.f, 1.f, 1.f, 1.f);
-      o2[c4] = pack_bf16x4((float)((double)zs[i].x * r * (double)g.x),
-                           (float)((double)zs[i].y * r * (double)g.y),
-                           (float)((double)zs[i].z * r * (double)g.z),
-                           (float)((double)zs[i].w * r * (double)g.w));
+      put(c4, pack_bf16x4((float)((double)zs[i].x * r * (double)g.x),
+                          (float)((double)zs[i].y * r * (double)g.y),
+                          (float)((double)zs[i].z * r * (double)g.z),
+                          (float)((double)zs[i].w * r * (double)g.w)));
     }
   }
 }
@@ -158,15 +190,18 @@ __global__ __launch_bounds__(CB_THREADS) void rmsnorm_bf16_kernel(
 }  // namespace
 
 hipError_t launch_combine(const float* y_perm, const float* w, const int32_t* inv_pos,
-                          const float* y_shared, const float* gamma_post, uint16_t* out,
-                          int64_t T, int H, int k, int post_norm, float eps, hipStream_t stream) {
+                          const float* y_shared, const float* gamma_post, const uint16_t* residual,
+                          float c0, float c1, uint16_t* out, int64_t T, int H, int k,
+                          int post_norm, float eps, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  void (*kern)(const float*, const float*, const int32_t*, const float*, const float*,
+               const uint16_t*, float, float, uint16_t*, int, int, float);
   if (post_norm)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)T), dim3(CB_THREADS), 0, stream,
-                       y_perm, w, inv_pos, y_shared, gamma_post, out, H, k, eps);
+    kern = residual ? combine_kernel<true, true> : combine_kernel<true, false>;
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)T), dim3(CB_THREADS), 0, stream,
-                       y_perm, w, inv_pos, y_shared, gamma_post, out, H, k, eps);
+    kern = residual ? combine_kernel<false, true> : combine_kernel<false, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)T), dim3(CB_THREADS), 0, stream, y_perm, w, inv_pos,
+                     y_shared, gamma_post, residual, c0, c1, out, H, k, eps);
   return hipGetLastError();
 }
 

@@ -69,5 +69,6 @@ int gemm_cu_count();  // compute units of the current device
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, const float* gamma, uint16_t* out, int64_t T,
                                int H, float eps, hipStream_t stream);
 hipError_t launch_combine(const float* y_perm, const float* w, const int32_t* inv_pos,
-                          const float* y_shared, const float* gamma_post, uint16_t* out,
-                          int64_t T, int H, int k, int post_norm, float eps, hipStream_t stream);
+                          const float* y_shared, const float* gamma_post, const uint16_t* residual,
+                          float c0, float c1, uint16_t* out, int64_t T, int H, int k,
+                          int post_norm, float eps, hipStream_t stream);

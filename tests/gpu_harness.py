@@ -56,9 +56,13 @@ def to_bits(t) -> np.ndarray:
 
 
 class Device:
-    """Inputs of one workload resident on the GPU plus the output buffers."""
+    """Inputs of one workload resident on the GPU plus the output buffers.
+    `finish` (optional): dict(residual=bf16 bits [T, H], out_scale,
+    residual_scale, post_norm, in_place) -- the layer then runs through
+    moe_forward_finish; with in_place the output overwrites the residual's
+    device buffer."""
 
-    def __init__(self, wl, inp: dict):
+    def __init__(self, wl, inp: dict, finish: dict | None = None):
         torch, moe = torch_and_lib()
         self.torch, self.moe, self.wl, self.inp = torch, moe, wl, inp
         T, H, E, k = inp["x"].shape[0], wl.H, wl.E, wl.k
@@ -87,6 +91,16 @@ class Device:
         nbytes = moe.moe_workspace_size(self.params)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         self.out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        self.fin = None
+        self.in_place = False
+        if finish is not None:
+            self.residual = dev_bf16(torch, finish["residual"])
+            self.fin = moe.make_finish(self.residual, finish.get("out_scale", 1.0),
+                                       finish.get("residual_scale", 1.0),
+                                       finish.get("post_norm", False))
+            self.in_place = bool(finish.get("in_place", False))
+            if self.in_place:
+                self.out = self.residual
         N = T * k
         self.ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
         self.w = torch.empty((T, k), dtype=torch.float32, device="cuda")
@@ -101,7 +115,8 @@ class Device:
     def canary(self) -> None:
         """Fill every output with NaN / out-of-range bits first, so that an
         element the kernels never write shows up."""
-        self.out.fill_(0x7FC0)
+        if not self.in_place:
+            self.out.fill_(0x7FC0)
         self.ids.fill_(-7)
         self.w.fill_(float("nan"))
         self.offsets.fill_(-7)
@@ -112,8 +127,12 @@ class Device:
             self.xr.fill_(0x7FC0)
 
     def run(self) -> None:
-        self.moe.moe_forward(self.params, self.x, self.x_cur, self.weights, self.out, self.probes,
-                             self.ws)
+        if self.fin is not None:
+            self.moe.moe_forward_finish(self.params, self.x, self.x_cur, self.weights, self.fin,
+                                        self.out, self.probes, self.ws)
+        else:
+            self.moe.moe_forward(self.params, self.x, self.x_cur, self.weights, self.out,
+                                 self.probes, self.ws)
 
     def result(self) -> dict:
         self.torch.cuda.synchronize()
@@ -171,11 +190,12 @@ def check_router(x_bits, w_router, corr_bias, k, rsf, logits_g, ids_g, w_g) -> d
     return rep
 
 
-def check_layer(wl, inp: dict, gpu: dict, rows: np.ndarray | None = None) -> dict:
+def check_layer(wl, inp: dict, gpu: dict, rows: np.ndarray | None = None,
+                finish: dict | None = None) -> dict:
     """Compare one GPU forward with the oracle.  `rows` = token sample for
     the output check (None = all tokens); routing and the permutation are
-    always checked on every token.  Returns a report; raises AssertionError
-    on any violation."""
+    always checked on every token; `finish` as in Device (the oracle then
+    adds S8).  Returns a report; raises AssertionError on any violation."""
     kw = dict(k=wl.k, rsf=wl.rsf, limit=wl.limit, scmoe=wl.scmoe, eps=wl.eps)
     T = inp["x"].shape[0]
     rep: dict = {}
@@ -201,6 +221,11 @@ def check_layer(wl, inp: dict, gpu: dict, rows: np.ndarray | None = None) -> dic
     if rows is None:
         rows = np.arange(T)
     sub = mo.take_rows(inp, rows)
+    if finish is not None:
+        kw.update(post_norm=bool(finish.get("post_norm", False)),
+                  residual=np.asarray(finish["residual"])[rows],
+                  out_scale=finish.get("out_scale", 1.0),
+                  residual_scale=finish.get("residual_scale", 1.0))
     res = mo.forward(sub, ids=ids_g[rows], **kw)
     o_ref = mo.bf16_to_f64(res["out"])
     o_gpu = mo.bf16_to_f64(gpu["out"][rows])

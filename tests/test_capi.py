@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -38,9 +38,9 @@ def test_struct_layout_matches_header(tmp_path):
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
         "int main(void){\n"
-        'printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(moe_params), offsetof(moe_params, norm_eps),'
+        'printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_params), offsetof(moe_params, norm_eps),'
         " offsetof(moe_params, scmoe), sizeof(moe_weights), sizeof(moe_probes),"
-        " offsetof(moe_probes, events));\n"
+        " offsetof(moe_probes, events), sizeof(moe_finish), offsetof(moe_finish, post_norm));\n"
         "return 0;}\n")
     exe = tmp_path / "layout"
     r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
@@ -51,7 +51,8 @@ def test_struct_layout_matches_header(tmp_path):
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     want = [ctypes.sizeof(moe.moe_params), moe.moe_params.norm_eps.offset,
             moe.moe_params.scmoe.offset, ctypes.sizeof(moe.moe_weights),
-            ctypes.sizeof(moe.moe_probes), moe.moe_probes.events.offset]
+            ctypes.sizeof(moe.moe_probes), moe.moe_probes.events.offset,
+            ctypes.sizeof(moe.moe_finish), moe.moe_finish.post_norm.offset]
     assert got == want
 
 
@@ -154,6 +155,37 @@ def test_entry_points_reject_before_launch():
         moe.moe_forward(P(), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
                         16, None, 16, stream=0)
     assert ei.value.status == moe.MOE_ERR_WORKSPACE
+
+
+def test_finish_validation():
+    """moe_forward_finish / moe_combine_finish: the finish is checked on the
+    host like every other argument."""
+    w = moe.make_weights(16, None, 16, 16, 16, 16)
+    cases = [
+        (None, P(), moe.MOE_ERR_INVALID_ARG),                                   # no finish
+        (moe.make_finish(None), P(), moe.MOE_ERR_INVALID_ARG),                  # no residual
+        (moe.make_finish(18), P(), moe.MOE_ERR_UNSUPPORTED),                    # misaligned
+        (moe.make_finish(16, out_scale=math.inf), P(), moe.MOE_ERR_INVALID_ARG),
+        (moe.make_finish(16, residual_scale=math.nan), P(), moe.MOE_ERR_INVALID_ARG),
+        (moe.moe_finish(16, 1.0, 1.0, 2), P(), moe.MOE_ERR_INVALID_ARG),        # flag not 0/1
+        (moe.make_finish(16, post_norm=True), P(norm_eps=0.0), moe.MOE_ERR_INVALID_ARG),
+        (moe.make_finish(16, post_norm=True), P(H=8200), moe.MOE_ERR_UNSUPPORTED),
+        (moe.make_finish(16, 0.6, 0.8, True), P(), moe.MOE_ERR_WORKSPACE),      # valid
+        (moe.make_finish(16), P(scmoe=True, H=8192), moe.MOE_ERR_INVALID_ARG),  # no x_shared
+    ]
+    for fin, p, status in cases:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_forward_finish(p, 16, None, w, fin, 16, None, 16, stream=0)
+        assert ei.value.status == status, (fin, status)
+    for fin, p, status in cases[:8]:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_combine_finish(p, 16, 16, 16, None, None, fin, 16, stream=0)
+        assert ei.value.status == status, (fin, status)
+    # an empty batch needs no buffers, also with a finish
+    moe.moe_forward_finish(P(T=0), None, None, moe.make_weights(None, None, None, None),
+                           moe.make_finish(None), None, None, None, stream=0)
+    moe.moe_combine_finish(P(T=0), None, None, None, None, None, moe.make_finish(None), None,
+                           stream=0)
 
 
 def test_empty_batch_is_a_noop_without_pointers():

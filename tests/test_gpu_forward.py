@@ -232,3 +232,55 @@ def test_forward_w4(name):
 def test_forward_decode_w4_full():
     rep = _full("decode_w4", None)
     assert rep["rows_checked"] == 32
+
+
+# ------------------------------------------------ finish (residual add) ----
+
+FINISH = {
+    # plain layer, the ScMoE-style residual/BDA (coefficients 1)
+    "plain_bda": (Workload("fin_plain", T=96, H=256, E=16, k=3, I=128, I_s=128),
+                  dict(out_scale=1.0, residual_scale=1.0)),
+    # plain layer with the sandwich post-norm and a depth-scaled add
+    "sandwich_scaled": (Workload("fin_sandwich", T=150, H=384, E=24, k=4, I=192, I_s=256,
+                                 gamma_jitter=0.1),
+                        dict(out_scale=0.6, residual_scale=0.8, post_norm=True)),
+    # ScMoE pairing, residual added in place (out is the residual buffer)
+    "scmoe_in_place": (Workload("fin_scmoe", T=120, H=384, E=32, k=4, I=192, I_s=256,
+                                scmoe=True, gamma_jitter=0.1),
+                       dict(out_scale=1.0, residual_scale=1.0, in_place=True)),
+    # decode-sized (weight streaming, shared expert beside routing)
+    "decode_small": (Workload("fin_decode", T=20, H=512, E=40, k=4, I=176, I_s=352),
+                     dict(out_scale=2 ** -0.5, residual_scale=2 ** -0.5)),
+}
+
+
+@pytest.mark.parametrize("name", list(FINISH))
+def test_forward_finish(name):
+    """moe_forward_finish against the oracle with S8, and the fused finish
+    bit for bit against the finish of the GPU's own unfinished output."""
+    wl, fin = FINISH[name]
+    inp = moe_inputs.generate(wl, seed=6)
+    if fin.get("post_norm") and inp.get("gamma_post") is None:
+        inp["gamma_post"] = (1 + 0.1 * np.random.default_rng(7).uniform(-1, 1, wl.H)).astype(np.float32)
+    res_bits = moe_inputs.f32_to_bf16_bits(
+        np.random.default_rng(8).standard_normal((wl.T, wl.H)).astype(np.float32) * 2)
+    fin = dict(fin, residual=res_bits)
+    gh.note(f"forward_finish {name} {wl.label()} {dict((k, v) for k, v in fin.items() if k != 'residual')}")
+    d = gh.Device(wl, inp, finish=fin)
+    d.canary()
+    d.run()
+    gpu = d.result()
+    rep = gh.check_layer(wl, inp, gpu, finish=fin)
+    gh.note(f"  {rep}")
+    # the unfinished output of the same layer on the GPU: a finish that keeps
+    # o (scales 1 and 0, zero residual, the same post-norm setting)
+    keep = dict(residual=np.zeros_like(res_bits), out_scale=1.0, residual_scale=0.0,
+                post_norm=fin.get("post_norm", False))
+    d0 = gh.Device(wl, inp, finish=keep)
+    d0.run()
+    o = d0.result()["out"]
+    want = mo.finish(o, res_bits, fin["out_scale"], fin["residual_scale"])
+    got = gpu["out"]
+    # values, so that -0 and +0 (from o + 0 in the keeping finish) compare equal
+    assert np.array_equal(mo.bf16_to_f64(got), mo.bf16_to_f64(want)), \
+        f"fused finish differs in {int(np.sum(mo.bf16_to_f64(got) != mo.bf16_to_f64(want)))} elements"

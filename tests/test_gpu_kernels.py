@@ -209,3 +209,31 @@ def test_combine_parity(tl, T, H, k, shared, post):
     assert d.max() <= 1.0
     # fp32 accumulation of at most 17 terms: almost every element rounds the same
     assert np.mean(got == ref) > 0.99
+
+
+@pytest.mark.parametrize("post,in_place,c0,c1", [(False, False, 1.0, 1.0), (True, False, 0.6, 0.8),
+                                                  (True, True, 1.0, 1.0), (False, True, 0.25, 1.5)])
+def test_combine_finish_bits(tl, post, in_place, c0, c1):
+    """moe_combine_finish = the finish of moe_combine's own output, bit for
+    bit (the same kernel arithmetic, then S8), also in place."""
+    torch, moe = tl
+    T, H, k = 37, 1032, 5
+    gh.note(f"combine_finish post={post} in_place={in_place} c=({c0},{c1})")
+    rng = np.random.default_rng(41)
+    N = T * k
+    y = gh.dev_f32(torch, (rng.standard_normal((N, H)) * 3).astype(np.float32))
+    w = gh.dev_f32(torch, rng.uniform(0, 2.5, (T, k)).astype(np.float32))
+    inv = torch.from_numpy(rng.permutation(N).astype(np.int32)).cuda()
+    ys = gh.dev_f32(torch, (rng.standard_normal((T, H)) * 2).astype(np.float32))
+    gamma = gh.dev_f32(torch, rng.uniform(0.9, 1.1, H).astype(np.float32))
+    res = moe_inputs.f32_to_bf16_bits((rng.standard_normal((T, H)) * 4).astype(np.float32))
+    p_plain = moe.make_params(T, H, 16, k, 8, 8, 1.0, 7.0, scmoe=False, norm_eps=1e-6)
+    p_o = moe.make_params(T, H, 16, k, 8, 8, 1.0, 7.0, scmoe=post, norm_eps=1e-6)
+    o = torch.full((T, H), 0x7FC0, dtype=torch.int16, device="cuda")
+    moe.moe_combine(p_o, y, w, inv, ys, gamma, o)
+    r_dev = gh.dev_bf16(torch, res)
+    out = r_dev if in_place else torch.full((T, H), 0x7FC0, dtype=torch.int16, device="cuda")
+    moe.moe_combine_finish(p_plain, y, w, inv, ys, gamma, moe.make_finish(r_dev, c0, c1, post), out)
+    torch.cuda.synchronize()
+    want = mo.finish(gh.to_bits(o), res, c0, c1)
+    assert np.array_equal(gh.to_bits(out), want)
