@@ -55,6 +55,12 @@ What it computes, step by step, and where each step comes from:
      output times coefs[0] plus the residual times coefs[1], in the
      residual's dtype); "core.models.hybrid.shortcut_block",
      ShortcutMoEBlock._postprocess (finish residual/BDA): c0 = c1 = 1.
+  Router backward (training; optional): for l = x W_r^T (+ bias) in fp32,
+     grad_x = bf16(fp32(dL W_r)), grad_W = fp32(dL^T x), grad_b =
+     fp32(sum_t dL[t]).  Source: "bridge.models.beam.modeling_beam",
+     _BeamRouterGatingLinear (both GEMM operands in the router dtype, fp32;
+     saved activations keep their dtype, bf16; an expanded stride-0
+     gradient must be read correctly).
 
 Readings where the pages are silent (each also listed in the design
 notes): bias added to the sigmoid score, not to the logit; no
@@ -349,6 +355,29 @@ def finish(out_bits: np.ndarray, residual_bits: np.ndarray, out_scale: float = 1
         a = bf16_of_f32(o * np.float32(out_scale))
         b = bf16_of_f32(r * np.float32(residual_scale))
         return bf16_of_f32(bf16_to_f64(a).astype(np.float32) + bf16_to_f64(b).astype(np.float32))
+
+
+# ----------------------------------------- router backward (optional) ---
+
+def router_backward(grad_logits: np.ndarray, x_bits: np.ndarray, w_router: np.ndarray) -> dict:
+    """Gradients of l = x @ W_r^T (+ b) for the upstream gradient dL [T, E]
+    (fp32; any strides, e.g. a broadcast view).  The GEMMs run in the
+    router dtype (fp32), so their exact values are rounded once to fp32;
+    grad_x is returned in the input's dtype (bf16), as autograd gives a
+    gradient in its input's dtype.
+
+    Returns dict(grad_x bf16 bits [T, H], grad_x_f64 (exact), grad_w fp32
+    [E, H], grad_w_f64, grad_b fp32 [E], grad_b_f64).
+    """
+    dl = np.asarray(grad_logits, dtype=np.float64)
+    x = bf16_to_f64(x_bits)
+    w = np.asarray(w_router, dtype=np.float64)
+    gx = dl @ w
+    gw = dl.T @ x
+    gb = dl.sum(axis=0)
+    return dict(grad_x=bf16_round(gx), grad_x_f64=gx,
+                grad_w=gw.astype(np.float32), grad_w_f64=gw,
+                grad_b=gb.astype(np.float32), grad_b_f64=gb)
 
 
 # ------------------------------------------------------------ the layer ---
