@@ -48,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE fwd tokens/s; % bf16 MFMA peak (prefill), % HBM GB/s (decode)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 KERNEL_SOURCES = ["grouped_gemm.hip", "kernels.h", "common.h"]
 
 
@@ -202,6 +203,80 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: 
     print(json.dumps(out))
 
 
+def router_backward_bench(args) -> int:
+    """Gradients of the router GEMM (moe_router_backward: grad_x, grad_W,
+    grad_b) on the prefill batch (T=8192, H=4096, E=64): one JSON line.
+    Work per call: 2*T*E*H flops for grad_x and as many for grad_W, on the
+    fp32 matrix cores."""
+    import numpy as np
+    import torch
+    import moe_inputs
+    import mixture_experts_layer_steered_amd as moe
+
+    T, H, E = 8192, 4096, 64
+    steps = args.steps if args.steps is not None else 50
+    warmup = args.warmup if args.warmup is not None else 5
+    rng = np.random.default_rng(0)
+    x_bits = moe_inputs.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    dl = (rng.standard_normal((T, E)) * 0.1).astype(np.float32)
+    x = torch.from_numpy(x_bits.view(np.int16)).to("cuda")
+    wd = torch.from_numpy(w).to("cuda")
+    dld = torch.from_numpy(dl).to("cuda")
+    p = moe.make_params(T, H, E, 1, 8, 0, 1.0, 7.0)
+    gx = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    gw = torch.empty((E, H), dtype=torch.float32, device="cuda")
+    gb = torch.empty((E,), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(moe.moe_router_backward_workspace_size(p), 16), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        moe.moe_router_backward(p, dld, x, wd, gx, gw, gb, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        moe.moe_router_backward(p, dld, x, wd, gx, gw, gb, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    ev_ms = e0.elapsed_time(e1) / steps
+    flops = 4 * T * E * H
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as mo
+        n, done, dt = 1024, 0, 0.0
+        while dt < args.cpu_seconds and done < 64 * n:
+            rows = (np.arange(n) + done) % T
+            ts = time.perf_counter()
+            mo.router_backward(dl[rows], x_bits[rows], w)
+            dt += time.perf_counter() - ts
+            done += n
+        cpu = {"value": round(done / dt, 1), "unit": "tokens/s", "cores": cpu_threads(),
+               "kind": "oracle",
+               "sample": f"{done // n} oracle router backwards of {n} tokens of the same batch "
+                         f"({done} tokens, {dt:.1f} s, float64 NumPy)"}
+    line = {
+        "metric": "router backward tokens/s", "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"router_backward_T{T}_H{H}_E{E}", "T": T, "H": H, "E": E,
+                   "outputs": "grad_x bf16, grad_w fp32, grad_b fp32", "parallelism": "ep1_tp1"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "router backward (grad_x and grad_W fp32 GEMMs, grad_b sum), "
+                               "all launches of one call",
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(ev_ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +289,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle time to spend on the baseline sample (at least)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--router-backward", action="store_true",
+                    help="time moe_router_backward (training path) instead of the forward")
     ap.add_argument("--finish", action="store_true",
                     help="add the residual after the layer output (moe_forward_finish, "
                          "coefficients 1: the residual/bias-dropout-add), fused into the combine")
@@ -237,6 +314,8 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy(1 << 30, 5)
         return 0
+    if args.router_backward:
+        return router_backward_bench(args)
 
     import numpy as np
     import torch

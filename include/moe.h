@@ -312,6 +312,31 @@ moe_status moe_forward_finish(const moe_params* p, const moe_bf16* x_routed,
                               const moe_finish* fin, moe_bf16* out, const moe_probes* probes,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of workspace moe_router_backward needs for p->T, H, E (host-only,
+ * pure; 0 is possible). */
+moe_status moe_router_backward_workspace_size(const moe_params* p, size_t* bytes);
+
+/* Backward of the router GEMM l = x @ W_r^T (+ b), fp32 (training path):
+ * for the upstream gradient dL [T, E] (fp32),
+ *   grad_x = bf16(fp32(dL @ W_r))    [T, H] bf16 out, or NULL to skip
+ *   grad_w = fp32(dL^T @ x)          [E, H] fp32 out, or NULL to skip
+ *   grad_b = fp32(sum_t dL[t, :])    [E] fp32 out, or NULL to skip
+ * both GEMMs in fp32 with every product exact (results equal fp32 GEMMs up
+ * to summation order, deterministic); grad_x comes back in the saved
+ * input's dtype.  dL element (t, e) is read at grad_logits[t * g_row_stride
+ * + e * g_col_stride] (strides in elements, >= 0): an expanded gradient
+ * such as that of logits.sum() (both strides 0) is used as it is, without
+ * a contiguous copy.  x [T, H] bf16 (the saved router input), w_router
+ * [E, H] fp32; ws >= moe_router_backward_workspace_size(p) bytes.  With
+ * T == 0, grad_w and grad_b are zero-filled.  Uses p->T, H, E.
+ * Source: "bridge.models.beam.modeling_beam", _BeamRouterGatingLinear
+ * (forward/backward of the fp32 gating GEMM with fp32 weights, bf16 saved
+ * activations, stride-0 gradients). */
+moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
+                               int64_t g_row_stride, int64_t g_col_stride, const moe_bf16* x,
+                               const float* w_router, moe_bf16* grad_x, float* grad_w,
+                               float* grad_b, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static text naming a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -96,6 +96,9 @@ def _load() -> ctypes.CDLL:
         "moe_forward_finish": (st, [P, c_void_p, c_void_p, POINTER(moe_weights),
                                     POINTER(moe_finish), c_void_p, POINTER(moe_probes), c_void_p,
                                     c_size_t, c_void_p]),
+        "moe_router_backward_workspace_size": (st, [P, POINTER(c_size_t)]),
+        "moe_router_backward": (st, [P, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_status_string": (c_char_p, [c_int]),
         "moe_last_error": (c_char_p, []),
     }
@@ -109,7 +112,8 @@ def _load() -> ctypes.CDLL:
 _lib = _load()
 EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
             "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
-            "moe_combine_finish", "moe_forward", "moe_forward_finish", "moe_status_string",
+            "moe_combine_finish", "moe_forward", "moe_forward_finish",
+            "moe_router_backward_workspace_size", "moe_router_backward", "moe_status_string",
             "moe_last_error")
 
 
@@ -241,3 +245,22 @@ def moe_forward_finish(params, x_routed, x_shared, weights: moe_weights, fin, ou
     _check(_lib.moe_forward_finish(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
                                    ctypes.byref(weights), f, _ptr(out), pr, _ptr(ws), _nbytes(ws),
                                    _stream(stream)))
+
+
+def moe_router_backward_workspace_size(params: moe_params) -> int:
+    n = c_size_t(0)
+    _check(_lib.moe_router_backward_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def moe_router_backward(params, grad_logits, x, w_router, grad_x=None, grad_w=None, grad_b=None,
+                        ws=None, stream=None, strides=None):
+    """Gradients of the router GEMM.  `grad_logits` is a float32 tensor
+    [T, E] with any strides (an expanded one is read as it is), or a raw
+    pointer with `strides` = (row, column) in elements."""
+    if strides is None:
+        strides = tuple(grad_logits.stride()) if grad_logits is not None else (0, 0)
+    _check(_lib.moe_router_backward(ctypes.byref(params), _ptr(grad_logits), int(strides[0]),
+                                    int(strides[1]), _ptr(x), _ptr(w_router), _ptr(grad_x),
+                                    _ptr(grad_w), _ptr(grad_b), _ptr(ws), _nbytes(ws),
+                                    _stream(stream)))

@@ -629,6 +629,48 @@ moe_status moe_combine_finish(const moe_params* p, const float* y_perm, const fl
   return combine_impl(p, y_perm, topk_w, inv_pos, y_shared, gamma_post, fin, out, stream);
 }
 
+moe_status moe_router_backward_workspace_size(const moe_params* p, size_t* bytes) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = router_backward_workspace_bytes(p->T, p->H, p->E);
+  return ok();
+}
+
+moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
+                               int64_t g_row_stride, int64_t g_col_stride, const moe_bf16* x,
+                               const float* w_router, moe_bf16* grad_x, float* grad_w,
+                               float* grad_b, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  if (g_row_stride < 0 || g_col_stride < 0)
+    return fail(MOE_ERR_INVALID_ARG, "gradient strides must be >= 0 (%lld, %lld)",
+                (long long)g_row_stride, (long long)g_col_stride);
+  OPTIONAL_PTR(grad_x);
+  OPTIONAL_PTR(grad_w);
+  OPTIONAL_PTR(grad_b);
+  if (p->T > 0) {
+    if (!grad_logits) return fail(MOE_ERR_INVALID_ARG, "grad_logits is NULL");
+    if (reinterpret_cast<uintptr_t>(grad_logits) & 3u)
+      return fail(MOE_ERR_UNSUPPORTED, "grad_logits is not 4-byte aligned");
+    if (grad_x) REQUIRE_PTR(w_router);
+    if (grad_w) REQUIRE_PTR(x);
+    const size_t need = router_backward_workspace_bytes(p->T, p->H, p->E);
+    if (grad_w && need > 0) {
+      REQUIRE_PTR(ws);
+      if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    }
+  }
+  if (!grad_x && !grad_w && !grad_b) return ok();  // nothing asked for
+  if ((s = device_status(launch_router_backward(grad_logits, g_row_stride, g_col_stride, x,
+                                                w_router, grad_x, grad_w, grad_b, p->T, p->H,
+                                                p->E, ws, stream),
+                         "router backward")) != MOE_OK)
+    return s;
+  return ok();
+}
+
 moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
                        const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,
                        size_t ws_bytes, hipStream_t stream) {

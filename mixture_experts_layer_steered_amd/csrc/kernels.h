@@ -66,6 +66,13 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                int max_wgs = 0);
 int gemm_cu_count();  // compute units of the current device
 
+// Router backward (router_bwd.hip): grad_x, grad_w, grad_b each optional
+// (NULL skips it); dL element (t, e) at dl[t * rs + e * cs].
+size_t router_backward_workspace_bytes(int64_t T, int H, int E);
+hipError_t launch_router_backward(const float* dl, int64_t rs, int64_t cs, const uint16_t* x,
+                                  const float* w, uint16_t* gx, float* gw, float* gb, int64_t T,
+                                  int H, int E, void* ws, hipStream_t stream);
+
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, const float* gamma, uint16_t* out, int64_t T,
                                int H, float eps, hipStream_t stream);
 hipError_t launch_combine(const float* y_perm, const float* w, const int32_t* inv_pos,

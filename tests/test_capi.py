@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -186,6 +186,31 @@ def test_finish_validation():
                            moe.make_finish(None), None, None, None, stream=0)
     moe.moe_combine_finish(P(T=0), None, None, None, None, None, moe.make_finish(None), None,
                            stream=0)
+
+
+def test_router_backward_validation():
+    p = P(T=300, H=512, E=24)
+    need = moe.moe_router_backward_workspace_size(p)
+    assert need == moe.moe_router_backward_workspace_size(p) and need > 0
+    cases = [
+        (dict(strides=(-1, 1)), moe.MOE_ERR_INVALID_ARG),                  # negative stride
+        (dict(grad_logits=None), moe.MOE_ERR_INVALID_ARG),
+        (dict(grad_logits=18), moe.MOE_ERR_UNSUPPORTED),                   # misaligned dL
+        (dict(grad_x=16, w_router=None), moe.MOE_ERR_INVALID_ARG),         # grad_x needs W_r
+        (dict(grad_w=16, x=None), moe.MOE_ERR_INVALID_ARG),                # grad_w needs x
+        (dict(grad_w=16), moe.MOE_ERR_INVALID_ARG),                        # no workspace
+        (dict(grad_w=16, ws=16), moe.MOE_ERR_WORKSPACE),                   # 0 bytes of it
+        (dict(grad_x=24), moe.MOE_ERR_UNSUPPORTED),                        # misaligned output
+    ]
+    for kw, status in cases:
+        args = dict(grad_logits=16, x=16, w_router=16, strides=(24, 1))
+        args.update(kw)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_router_backward(p, **args, stream=0)
+        assert ei.value.status == status, (kw, status)
+    # nothing asked for: nothing to do, also without buffers
+    moe.moe_router_backward(p, 16, 16, 16, strides=(24, 1), stream=0)
+    moe.moe_router_backward(P(T=0), None, None, None, stream=0)
 
 
 def test_empty_batch_is_a_noop_without_pointers():
