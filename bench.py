@@ -283,7 +283,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "decode_w4", "prefill", "zipf", "scmoe"])
+                    choices=["tiny", "decode", "decode_w4", "prefill", "prefill_w4", "zipf", "scmoe"])
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens the CPU oracle runs on (default: by workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -337,7 +337,7 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
 
     T, H, E, k, I, Is = wl.T, wl.H, wl.E, wl.k, wl.I, wl.I_s
-    params = moe.make_params(T, H, E, k, I, Is, wl.rsf, wl.limit, wl.scmoe, wl.eps)
+    params = moe.make_params(T, H, E, k, I, Is, wl.rsf, wl.limit, wl.scmoe, wl.eps, w4=wl.w4)
     x = dev_bf16(inp["x"])
     x_cur = dev_bf16(inp["x_cur"]) if wl.scmoe else None
     w4 = {}

@@ -107,6 +107,8 @@ typedef struct moe_params {
   int32_t scmoe;               /* 1 = ScMoE pairing: RMSNorm before routing and   */
                                /*     on the merged output; 0 = plain layer       */
   float norm_eps;              /* RMSNorm epsilon (ScMoE), > 0                    */
+  int32_t w4;                  /* 1 = W4A16 routed experts (moe_weights' *_q and  */
+                               /*     *_scale arrays); 0 = bf16                   */
 } moe_params;
 
 /* Device weights of one layer (all caller-owned, read-only). */
@@ -122,14 +124,19 @@ typedef struct moe_weights {
   /* W4A16 routed experts (the W4A16 expert GEMM named by "Module
    * glm5next_mlp", Modules forward_prefill_gemm and Constants
    * MOE_GROUPED_MODULE / W4A16_GEMV_MODULE; the format is this library's):
-   * when w_gate_up_q is set, the routed experts use these four arrays and
+   * with moe_params.w4 = 1, the routed experts use these four arrays and
    * w_gate_up / w_down are ignored.  A weight is (u - 8) * scale, u a 4-bit
    * code, packed along K in 4-byte words of 8 columns (byte j of a word:
    * column j in the low nibble, column j + 4 in the high nibble), one
    * bf16 scale per row and group of 128 columns, scales stored
-   * group-major.  H and I must be multiples of 128, and the batch must be
-   * decode-sized (T*k <= 64*E: the weight-streaming kernels); the shared
-   * expert stays bf16. */
+   * group-major.  H and I must be multiples of 128; the shared expert stays
+   * bf16.  Decode-sized batches (T*k <= 64*E) stream the codes and unpack
+   * them in registers (exact products: the results equal the dequantised
+   * layer up to fp32 summation order).  Larger batches, bound by the matrix
+   * cores, first dequantise the layer's experts into the workspace (each
+   * weight rounded to bf16, the MFMA operand type: one more rounding than
+   * the exact dequantisation) and run the bf16 grouped GEMMs; their
+   * workspace then holds E * 3 * I * H bf16 more. */
   const uint8_t* w_gate_up_q;       /* [E, 2I, H/2] codes; NULL = bf16 experts    */
   const moe_bf16* w_gate_up_scale;  /* [E, H/128, 2I] bf16                        */
   const uint8_t* w_down_q;          /* [E, H, I/2] codes                          */
@@ -170,7 +177,9 @@ enum {
   MOE_EV_BEGIN = 0,
   MOE_EV_PRENORM = 1,  /* ScMoE pre-norm                                    */
   MOE_EV_ROUTER = 2,   /* router logits + top-k                             */
-  MOE_EV_PERMUTE = 3,  /* permutation + grouped-GEMM tile schedule          */
+  MOE_EV_PERMUTE = 3,  /* permutation + grouped-GEMM tile schedule (and, for */
+                       /* W4A16 experts beyond weight streaming, the wait   */
+                       /* for the gate_up weights' dequantisation)          */
   MOE_EV_GATE_UP = 4,  /* grouped gate_up + SwiGLU (routed and shared)      */
   MOE_EV_DOWN = 5,     /* grouped down projection (routed and shared)       */
   MOE_EV_COMBINE = 6,  /* weighted combine (+ ScMoE post-norm)              */

@@ -38,7 +38,7 @@ class moe_params(Structure):
     _fields_ = [
         ("T", c_int64), ("H", c_int32), ("E", c_int32), ("k", c_int32), ("I", c_int32),
         ("I_shared", c_int32), ("routed_scaling_factor", c_float), ("swiglu_limit", c_float),
-        ("scmoe", c_int32), ("norm_eps", c_float),
+        ("scmoe", c_int32), ("norm_eps", c_float), ("w4", c_int32),
     ]
 
 
@@ -151,10 +151,10 @@ def _nbytes(t) -> int:
 
 
 def make_params(T, H, E, k, I, I_shared, routed_scaling_factor, swiglu_limit, scmoe=False,
-                norm_eps=1e-6) -> moe_params:
+                norm_eps=1e-6, w4=False) -> moe_params:
     return moe_params(int(T), int(H), int(E), int(k), int(I), int(I_shared),
                       float(routed_scaling_factor), float(swiglu_limit), int(bool(scmoe)),
-                      float(norm_eps))
+                      float(norm_eps), int(bool(w4)))
 
 
 def moe_workspace_size(params: moe_params) -> int:

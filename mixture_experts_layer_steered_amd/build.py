@@ -19,8 +19,8 @@ BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["router.hip", "router_bwd.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
-           "capi.cpp"]
+SOURCES = ["router.hip", "router_bwd.hip", "permute.hip", "grouped_gemm.hip", "dequant.hip",
+           "combine.hip", "capi.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -78,6 +78,11 @@ moe_status check_params(const moe_params* p) {
     return fail(MOE_ERR_UNSUPPORTED, "T*k = %lld >= 2^31", (long long)(p->T * p->k));
   if (p->scmoe && p->H > kMaxNormH)
     return fail(MOE_ERR_UNSUPPORTED, "scmoe with H = %d > %d", p->H, kMaxNormH);
+  if (p->w4 != 0 && p->w4 != 1)
+    return fail(MOE_ERR_INVALID_ARG, "w4 = %d is not 0 or 1", p->w4);
+  if (p->w4 && (p->H % 128 != 0 || p->I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "W4A16 experts need H and I multiples of 128 (H=%d I=%d)",
+                p->H, p->I);
   return MOE_OK;
 }
 
@@ -142,8 +147,14 @@ struct Layout {
   uint16_t* hs;
   float* ys;
   uint16_t* xr;
+  uint16_t* deq_gu;  // W4A16 experts dequantised to bf16 (batches beyond weight streaming)
+  uint16_t* deq_dn;
   size_t bytes;
 };
+
+// W4A16 batches with more than 64 rows per expert dequantise the experts
+// first (the same threshold as pick_variant's weight streaming)
+bool w4_dequant_batch(const moe_params& p) { return p.w4 && p.T * p.k > (int64_t)64 * p.E; }
 
 Layout carve(const moe_params& p, void* ws) {
   Carver c;
@@ -167,6 +178,9 @@ Layout carve(const moe_params& p, void* ws) {
   L.hs = c.take<uint16_t>((size_t)T * p.I_shared);
   L.ys = c.take<float>(p.I_shared ? (size_t)T * p.H : 0);
   L.xr = c.take<uint16_t>(p.scmoe ? (size_t)T * p.H : 0);
+  const bool deq = w4_dequant_batch(p);
+  L.deq_gu = deq ? c.take<uint16_t>((size_t)p.E * 2 * p.I * p.H) : nullptr;
+  L.deq_dn = deq ? c.take<uint16_t>((size_t)p.E * p.H * p.I) : nullptr;
   L.bytes = (c.off + 255) & ~size_t(255);
   return L;
 }
@@ -197,7 +211,7 @@ size_t permute_ws_bytes(const moe_params& p) {
 // process ends.
 struct SideStream {
   hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, join2 = nullptr;
 };
 constexpr int kMaxDevices = 64;
 
@@ -212,7 +226,8 @@ moe_status side_stream(SideStream** out) {
     if (hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) != hipSuccess)
       return fail(MOE_ERR_DEVICE, "second stream: %s", hipGetErrorString(hipGetLastError()));
     if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join2, hipEventDisableTiming) != hipSuccess)
       return fail(MOE_ERR_DEVICE, "stream events: %s", hipGetErrorString(hipGetLastError()));
     S = n;
   }
@@ -460,15 +475,12 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   OPTIONAL_PTR(x_shared);
   REQUIRE_PTR(w->w_router);
   OPTIONAL_PTR(w->corr_bias);
-  const bool w4 = w->w_gate_up_q != nullptr;
+  const bool w4 = p->w4 != 0;
   if (w4) {
     REQUIRE_PTR(w->w_gate_up_q);
     REQUIRE_PTR(w->w_gate_up_scale);
     REQUIRE_PTR(w->w_down_q);
     REQUIRE_PTR(w->w_down_scale);
-    if (p->H % 128 != 0 || p->I % 128 != 0)
-      return fail(MOE_ERR_UNSUPPORTED, "W4A16 experts need H and I multiples of 128 (H=%d I=%d)",
-                  p->H, p->I);
   } else {
     REQUIRE_PTR(w->w_gate_up);
     REQUIRE_PTR(w->w_down);
@@ -495,10 +507,14 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
       N, p->E, std::max<int64_t>(N, T) * std::max(p->H, std::max(p->I, p->I_shared)),
       (int64_t)2 * std::max(p->I, p->I_shared) * p->H,
       p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0);
-  if (w4 && v != GemmVariant::kWStream)
+  // W4A16: weight streaming unpacks the codes in its kernel; the tiled
+  // kernels read the experts dequantised into the workspace
+  const bool w4_stream = w4 && v == GemmVariant::kWStream;
+  const bool w4_deq = w4 && !w4_stream;
+  if (w4_deq && !w4_dequant_batch(*p))
     return fail(MOE_ERR_UNSUPPORTED,
-                "W4A16 experts run on the weight-streaming kernels only (T*k <= 64*E; here "
-                "T*k = %lld, E = %d)", (long long)N, p->E);
+                "W4A16 experts with at most 64 rows per expert run on the weight-streaming "
+                "kernels (MOE_GEMM_VARIANT forces another)");
   Layout L = carve(*p, ws);
   if (ws_bytes < L.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.bytes);
   if (probes) {
@@ -518,7 +534,11 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                                 (int64_t)2 * p->I * p->H, L.h, N, p->E, p->I, p->H, v, true);
   GemmProblem dn = make_problem(L.h, nullptr, L.offsets, L.mstart, w->w_down,
                                 (int64_t)p->H * p->I, L.y, N, p->E, p->H, p->I, v, false);
-  if (w4) {  // packed codes (uint16 units between experts) and group-major scales
+  if (w4_deq) {  // bf16 copies [E, 2I, H] and [E, H, I] in the workspace
+    gu.W = L.deq_gu;
+    dn.W = L.deq_dn;
+  }
+  if (w4_stream) {  // packed codes (uint16 units between experts) and group-major scales
     gu.W = reinterpret_cast<const uint16_t*>(w->w_gate_up_q);
     gu.w_stride = (int64_t)2 * p->I * p->H / 4;
     gu.S = w->w_gate_up_scale;
@@ -543,7 +563,7 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   // the routing kernels run on the rest; the combine waits for them.
   const bool beside = shared && v == GemmVariant::kWStream;
   SideStream* side = nullptr;
-  if (beside && (s = side_stream(&side)) != MOE_OK) return s;
+  if ((beside || w4_deq) && (s = side_stream(&side)) != MOE_OK) return s;
 
   auto mark = [&](int ev) -> moe_status {
     if (probes && probes->events[ev])
@@ -562,6 +582,22 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                                                side->stream, wgs),
                            "shared down")) != MOE_OK ||
         (s = device_status(hipEventRecord(side->join, side->stream), "join")) != MOE_OK)
+      return s;
+  }
+  // W4A16 beyond weight streaming: the experts are dequantised on the
+  // second stream, gate_up's while the routing kernels run, down's while the
+  // gate_up GEMM runs; each GEMM waits for its own weights
+  if (w4_deq) {
+    if ((s = device_status(hipEventRecord(side->fork, stream), "fork")) != MOE_OK ||
+        (s = device_status(hipStreamWaitEvent(side->stream, side->fork, 0), "fork")) != MOE_OK ||
+        (s = device_status(launch_w4_dequant(w->w_gate_up_q, w->w_gate_up_scale, L.deq_gu, p->E,
+                                             (int64_t)2 * p->I, p->H, side->stream),
+                           "dequantise gate_up")) != MOE_OK ||
+        (s = device_status(hipEventRecord(side->join, side->stream), "join")) != MOE_OK ||
+        (s = device_status(launch_w4_dequant(w->w_down_q, w->w_down_scale, L.deq_dn, p->E, p->H,
+                                             p->I, side->stream),
+                           "dequantise down")) != MOE_OK ||
+        (s = device_status(hipEventRecord(side->join2, side->stream), "join")) != MOE_OK)
       return s;
   }
   if (p->scmoe) {
@@ -584,6 +620,11 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                                         stream),
                          "permute")) != MOE_OK)
     return s;
+  // (the gate_up weights' dequantisation ends inside the permute step, so
+  // the gate_up step times the GEMM alone)
+  if (w4_deq &&
+      (s = device_status(hipStreamWaitEvent(stream, side->join, 0), "join")) != MOE_OK)
+    return s;
   if ((s = mark(MOE_EV_PERMUTE)) != MOE_OK) return s;
   const bool one_launch = shared && !beside;  // routed and shared problems together
   if ((s = device_status(launch_grouped_gemm(v, true, gu, one_launch ? &sgu : nullptr,
@@ -591,6 +632,9 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                          "gate_up")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_GATE_UP)) != MOE_OK) return s;
+  if (w4_deq &&
+      (s = device_status(hipStreamWaitEvent(stream, side->join2, 0), "join")) != MOE_OK)
+    return s;
   if ((s = device_status(launch_grouped_gemm(v, false, dn, one_launch ? &sdn : nullptr,
                                              p->swiglu_limit, stream),
                          "down")) != MOE_OK)

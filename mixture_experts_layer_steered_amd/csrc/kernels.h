@@ -73,6 +73,11 @@ hipError_t launch_router_backward(const float* dl, int64_t rs, int64_t cs, const
                                   const float* w, uint16_t* gx, float* gw, float* gb, int64_t T,
                                   int H, int E, void* ws, hipStream_t stream);
 
+// W4A16 experts -> bf16 (dequant.hip): G groups of `rows` rows by K
+// columns (K a multiple of 128), codes [G, rows, K/2], scales [G, K/128, rows].
+hipError_t launch_w4_dequant(const uint8_t* q, const uint16_t* scale, uint16_t* out, int G,
+                             int64_t rows, int K, hipStream_t stream);
+
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, const float* gamma, uint16_t* out, int64_t T,
                                int H, float eps, hipStream_t stream);
 hipError_t launch_combine(const float* y_perm, const float* w, const int32_t* inv_pos,

@@ -19,6 +19,7 @@ is synthetic):
            two inputs (preceding-layer and current hidden), RMSNorm
            eps 1e-6 before routing and after the merge
   decode_w4  the decode shape with W4A16 routed experts (below)
+  prefill_w4 the prefill shape with W4A16 routed experts
 
 Distributions: activations bf16 N(0,1); expert and shared weights bf16
 N(0,0.02); router weights fp32 N(0,0.02); correction bias fp32
@@ -87,6 +88,7 @@ WORKLOADS = {
     "scmoe": Workload("scmoe", T=8192, H=4096, E=128, k=8, I=1024, I_s=2048,
                       scmoe=True, eps=1e-6),
     "decode_w4": Workload("decode_w4", T=32, H=4096, E=64, k=8, I=1408, I_s=2816, w4=True),
+    "prefill_w4": Workload("prefill_w4", T=8192, H=4096, E=64, k=8, I=1536, I_s=1536, w4=True),
 }
 
 W4_GROUP = 128

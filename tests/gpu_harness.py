@@ -67,7 +67,8 @@ class Device:
         self.torch, self.moe, self.wl, self.inp = torch, moe, wl, inp
         T, H, E, k = inp["x"].shape[0], wl.H, wl.E, wl.k
         self.T = T
-        self.params = moe.make_params(T, H, E, k, wl.I, wl.I_s, wl.rsf, wl.limit, wl.scmoe, wl.eps)
+        self.params = moe.make_params(T, H, E, k, wl.I, wl.I_s, wl.rsf, wl.limit, wl.scmoe, wl.eps,
+                                      w4="w_gate_up_q" in inp)
         self.x = dev_bf16(torch, inp["x"])
         self.x_cur = dev_bf16(torch, inp["x_cur"]) if wl.scmoe else None
         self.w_router = dev_f32(torch, inp["w_router"])

@@ -38,8 +38,8 @@ def test_struct_layout_matches_header(tmp_path):
     prog.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
         "int main(void){\n"
-        'printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_params), offsetof(moe_params, norm_eps),'
-        " offsetof(moe_params, scmoe), sizeof(moe_weights), sizeof(moe_probes),"
+        'printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_params), offsetof(moe_params, norm_eps),'
+        " offsetof(moe_params, scmoe), offsetof(moe_params, w4), sizeof(moe_weights), sizeof(moe_probes),"
         " offsetof(moe_probes, events), sizeof(moe_finish), offsetof(moe_finish, post_norm));\n"
         "return 0;}\n")
     exe = tmp_path / "layout"
@@ -50,7 +50,7 @@ def test_struct_layout_matches_header(tmp_path):
         pytest.skip("HIP headers unusable from gcc: " + r.stderr[:200])
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     want = [ctypes.sizeof(moe.moe_params), moe.moe_params.norm_eps.offset,
-            moe.moe_params.scmoe.offset, ctypes.sizeof(moe.moe_weights),
+            moe.moe_params.scmoe.offset, moe.moe_params.w4.offset, ctypes.sizeof(moe.moe_weights),
             ctypes.sizeof(moe.moe_probes), moe.moe_probes.events.offset,
             ctypes.sizeof(moe.moe_finish), moe.moe_finish.post_norm.offset]
     assert got == want
@@ -58,7 +58,7 @@ def test_struct_layout_matches_header(tmp_path):
 
 def P(**kw):
     base = dict(T=64, H=128, E=8, k=2, I=256, I_shared=256, routed_scaling_factor=1.0,
-                swiglu_limit=7.0, scmoe=False, norm_eps=1e-6)
+                swiglu_limit=7.0, scmoe=False, norm_eps=1e-6, w4=False)
     base.update(kw)
     return moe.make_params(**base)
 
@@ -84,6 +84,8 @@ def P(**kw):
     (dict(E=1025, k=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 28, k=8), moe.MOE_ERR_UNSUPPORTED),
     (dict(scmoe=True, H=8200), moe.MOE_ERR_UNSUPPORTED),
+    (dict(w4=True, I=192), moe.MOE_ERR_UNSUPPORTED),       # W4A16: H, I multiples of 128
+    (dict(w4=True, H=136), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_param_validation(kw, status):
     with pytest.raises(moe.MoeError) as ei:
@@ -139,22 +141,28 @@ def test_entry_points_reject_before_launch():
     # W4A16 routed experts: all four arrays, K multiples of 128, decode-sized batches
     w4 = dict(w_gate_up_q=16, w_gate_up_scale=16, w_down_q=16, w_down_scale=16)
     with pytest.raises(moe.MoeError) as ei:   # a scale array missing
-        moe.moe_forward(P(), 16, None, moe.make_weights(16, None, None, None, 16, 16,
-                                                         **dict(w4, w_down_scale=None)),
+        moe.moe_forward(P(w4=True), 16, None, moe.make_weights(16, None, None, None, 16, 16,
+                                                                **dict(w4, w_down_scale=None)),
+                        16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:   # W4A16 arrays but params.w4 = 0: bf16 expected
+        moe.moe_forward(P(), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
                         16, None, 16, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
     with pytest.raises(moe.MoeError) as ei:   # I not a multiple of 128
-        moe.moe_forward(P(I=192), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
-                        16, None, 16, stream=0)
+        moe.moe_forward(P(I=192, w4=True), 16, None,
+                        moe.make_weights(16, None, None, None, 16, 16, **w4), 16, None, 16, stream=0)
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
-    with pytest.raises(moe.MoeError) as ei:   # more than 64 rows per expert
-        moe.moe_forward(P(T=4096), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
-                        16, None, 16, stream=0)
-    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
-    with pytest.raises(moe.MoeError) as ei:   # decode-sized: reaches the workspace check
-        moe.moe_forward(P(), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
-                        16, None, 16, stream=0)
-    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    for T in (64, 4096):   # decode-sized and prefill-sized: both reach the workspace check
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_forward(P(T=T, w4=True), 16, None,
+                            moe.make_weights(16, None, None, None, 16, 16, **w4), 16, None, 16,
+                            stream=0)
+        assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    # the prefill-sized W4A16 workspace holds the dequantised experts (E * 3 * I * H bf16)
+    extra = moe.moe_workspace_size(P(T=4096, w4=True)) - moe.moe_workspace_size(P(T=4096))
+    assert extra >= 8 * 3 * 256 * 128 * 2
+    assert moe.moe_workspace_size(P(T=64, w4=True)) == moe.moe_workspace_size(P(T=64))
 
 
 def test_finish_validation():

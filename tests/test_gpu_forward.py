@@ -284,3 +284,43 @@ def test_forward_finish(name):
     # values, so that -0 and +0 (from o + 0 in the keeping finish) compare equal
     assert np.array_equal(mo.bf16_to_f64(got), mo.bf16_to_f64(want)), \
         f"fused finish differs in {int(np.sum(mo.bf16_to_f64(got) != mo.bf16_to_f64(want)))} elements"
+
+
+# ------------------------------- W4A16 experts beyond weight streaming ----
+
+W4_TILED = {
+    # ~300 rows per expert: the LDS-tiled GEMM on the dequantised experts
+    "w4_tiled": Workload("w4_tiled", T=600, H=256, E=4, k=2, I=256, I_s=128, w4=True),
+    # ~2400 rows per expert: the ping-pong GEMM; no shared expert
+    "w4_pingpong": Workload("w4_pingpong", T=2400, H=384, E=4, k=2, I=128, I_s=0, w4=True),
+}
+
+
+def _bf16_rounded_experts(inp):
+    """The same layer with each W4A16 weight rounded to bf16 (what the
+    dequantising path feeds its bf16 GEMMs), as bf16 expert arrays."""
+    ref = {k: v for k, v in inp.items() if not k.endswith("_q") and not k.endswith("_scale")}
+    for name in ("w_gate_up", "w_down"):
+        q, sc = inp[name + "_q"], inp[name + "_scale"]
+        ref[name] = np.stack([mo.bf16_round(mo.dequant_w4(q[e], sc[e])) for e in range(q.shape[0])])
+    return ref
+
+
+@pytest.mark.parametrize("name", list(W4_TILED))
+def test_forward_w4_tiled(name):
+    """Prefill-sized W4A16 batches: parity with the oracle's exact
+    dequantised layer, and bit-for-bit equality with the bf16 path run on
+    the same weights rounded to bf16 on the host."""
+    wl = W4_TILED[name]
+    inp = moe_inputs.generate(wl, seed=5)
+    rep, gpu, _ = run_and_check(wl, inp)
+    ref_inp = _bf16_rounded_experts(inp)
+    wl_bf16 = wl.with_(w4=False)
+    gh.note(f"forward {name} as bf16 on host-rounded weights")
+    d = gh.Device(wl_bf16, ref_inp)
+    d.canary()
+    d.run()
+    g2 = d.result()
+    assert np.array_equal(gpu["ids"], g2["ids"])
+    assert np.array_equal(gpu["out"], g2["out"]), \
+        f"differs from the bf16 path in {int(np.sum(gpu['out'] != g2['out']))} elements"
