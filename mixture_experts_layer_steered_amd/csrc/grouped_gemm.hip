@@ -406,11 +406,61 @@ __device__ __forceinline__ void pipe_issue(const PipeTile<S>& T, uint16_t* smem,
                   base + (wave + S::NW * i) * S::RPI * S::KB);
 }
 
-// Epilogue.  The weight fragment is the MFMA's first operand, so an
-// accumulator is a 32 (weight rows) x 32 (A rows) block: lane L holds A row
-// L % 32 and weight rows 8*(r/4) + 4*(L/32) + r%4, i.e. four runs of four
-// adjacent output columns -- 8-byte (h) or 16-byte (y) stores.  N is a
-// multiple of 32 here, so a run is either wholly inside N or past it.
+// Quad permutation of a float across each group of four lanes (DPP).
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// 4x4 transpose inside each quad of lanes: afterwards register r of lane b
+// (b = lane % 4) holds what register b of lane r held.  Two butterfly steps,
+// each exchanging one bit of the lane index with the same bit of the register
+// index: a lane sends its partner (lane ^ 1, then lane ^ 2) the one register
+// of each pair the partner needs, picked by its own lane bit, so each step
+// takes two DPP moves.  Written out without a loop: the loop form of the same
+// steps was compiled into a single move per step, with wrong results.
+__device__ __forceinline__ void quad_transpose(f32x4_t& v) {
+  const int lane = threadIdx.x & 63;
+  const bool b0 = lane & 1, b1 = lane & 2;
+  const float x0 = quad_dpp<0xB1>(b0 ? v[0] : v[1]);  // lanes 1,0,3,2
+  const float x1 = quad_dpp<0xB1>(b0 ? v[2] : v[3]);
+  const float t0 = b0 ? x0 : v[0], t1 = b0 ? v[1] : x0;
+  const float t2 = b0 ? x1 : v[2], t3 = b0 ? v[3] : x1;
+  const float y0 = quad_dpp<0x4E>(b1 ? t0 : t2);      // lanes 2,3,0,1
+  const float y1 = quad_dpp<0x4E>(b1 ? t1 : t3);
+  v[0] = b1 ? y0 : t0;
+  v[1] = b1 ? y1 : t1;
+  v[2] = b1 ? t2 : y0;
+  v[3] = b1 ? t3 : y1;
+}
+
+// One 32x32x16 MFMA of the tile.  In gate_up the weight fragment is the
+// first operand, so an accumulator is a 32 (weight rows) x 32 (A rows) block
+// and a lane holds one A row: it owns both g and u of four runs of four
+// adjacent output columns, which the clamped SwiGLU pairs up in registers.
+// In down the A fragment goes first: a lane then holds one output column of
+// 16 A rows, so a quad of lanes holds 4x4 blocks of y that a transpose turns
+// into rows; a 16-byte store of the wave then writes 8 whole 128-byte row
+// pieces instead of 32-byte pieces of 32 rows (the fp32 epilogue of this
+// tile writes 256 KB).
+template <class S>
+__device__ __forceinline__ f32x16_t pipe_mfma(const bf16x8_t& w, const bf16x8_t& a,
+                                              const f32x16_t& c) {
+  if constexpr (S::GATEUP)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, a, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w, c, 0, 0, 0);
+}
+
+// Epilogue.  gate_up: lane L holds A row L % 32 and weight rows
+// 8*(r/4) + 4*(L/32) + r%4 of its 32x32 block, i.e. four runs of four
+// adjacent output columns -- 8-byte stores of h.  N is a multiple of 32
+// here, so a run is either wholly inside N or past it.  down: lane L holds
+// output column L % 32 of A rows 8*(r/4) + 4*(L/32) + r%4 -- one dword of y
+// per register, turned into four adjacent columns of one row by a quad
+// transpose (lane 4a+b: row 8*g + 4*(L/32) + b, columns 4a..4a+3 of the
+// block, for each group g of four registers).
 template <class S>
 __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<S>& T,
                                            const f32x16_t (&acc)[S::NMAT][S::TM][S::TN],
@@ -418,18 +468,18 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
   const int N = P.N;
+  if constexpr (S::GATEUP) {
 #pragma unroll
-  for (int i = 0; i < S::TM; ++i) {
-    const int64_t row = T.row0 + wm * S::WM + i * 32 + (lane & 31);
-    if (row >= T.row_end) continue;
+    for (int i = 0; i < S::TM; ++i) {
+      const int64_t row = T.row0 + wm * S::WM + i * 32 + (lane & 31);
+      if (row >= T.row_end) continue;
 #pragma unroll
-    for (int j = 0; j < S::TN; ++j) {
+      for (int j = 0; j < S::TN; ++j) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = T.n0 + wn * S::WN + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (col >= N) continue;
-        const f32x16_t& g = acc[0][i][j];
-        if (S::GATEUP) {
+        for (int q = 0; q < 4; ++q) {
+          const int col = T.n0 + wn * S::WN + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (col >= N) continue;
+          const f32x16_t& g = acc[0][i][j];
           const f32x16_t& u = acc[S::NMAT - 1][i][j];
           float2_t h01 = {swiglu_clamped_fast(g[4 * q], u[4 * q], limit),
                           swiglu_clamped_fast(g[4 * q + 1], u[4 * q + 1], limit)};
@@ -438,12 +488,29 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
           uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
                         __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
           *reinterpret_cast<uint2_t*>(static_cast<uint16_t*>(P.out) + row * N + col) = pk;
-        } else {
-          f32x4_t v = {g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(P.out) + row * N + col) = v;
         }
       }
     }
+  } else {
+    // registers 4g..4g+3 hold a 4 (rows) x 1 (column) piece; the four lanes
+    // of a quad together hold a 4x4 block, which quad_transpose turns into
+    // one row of four adjacent columns per lane
+    float* out = static_cast<float*>(P.out);
+    const int quad = (lane & 31) >> 2;
+#pragma unroll
+    for (int i = 0; i < S::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t v = {acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1], acc[0][i][j][4 * g + 2],
+                       acc[0][i][j][4 * g + 3]};
+          quad_transpose(v);
+          const int64_t row = T.row0 + wm * S::WM + i * 32 + 8 * g + 4 * (lane >> 5) + (lane & 3);
+          const int col = T.n0 + wn * S::WN + j * 32 + 4 * quad;
+          if (row < T.row_end && col < N)
+            *reinterpret_cast<f32x4_t*>(out + row * N + col) = v;
+        }
   }
 }
 
@@ -511,8 +578,7 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[grp][m][j], af[grp][i],
-                                                                acc[m][i][j], 0, 0, 0);
+          acc[m][i][j] = pipe_mfma<S>(bfr[grp][m][j], af[grp][i], acc[m][i][j]);
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
@@ -721,7 +787,7 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
 #pragma unroll
           for (int i = 0; i < TM; ++i)
             acc[m][i][j] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s][m][j], fa[s][i], acc[m][i][j], 0, 0, 0);
+                pipe_mfma<S>(fb[s][m][j], fa[s][i], acc[m][i][j]);
   };
   auto pp_barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
