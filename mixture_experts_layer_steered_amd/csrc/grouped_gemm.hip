@@ -263,6 +263,14 @@ __device__ __forceinline__ void lds_direct_16(const void* g, uint16_t* lds_wave_
                                    0, 0);
 }
 
+// The same for data read exactly once (streamed expert weights): the
+// non-temporal policy keeps the stream from displacing reused lines and lets
+// HBM deliver more of its rate (decode gate_up: 222 -> 211 us for 1.41 GB).
+__device__ __forceinline__ void lds_direct_16_stream(const void* g, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                   0, 2 /* nt */);
+}
+
 // Raw buffer resource over [base, base + 4 GiB): stride 0, the largest record
 // count, and the dword-3 word of CDNA's untyped buffer loads.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pl_rsrc(const void* base) {
@@ -1041,8 +1049,12 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
     const int k0 = kt_ld * KB;
     if (k0 + KB <= K_ld) {
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i)
-        lds_direct_16((i < A_INSTR ? ld_A : ld_W) + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+      for (int i = 0; i < PER_WAVE; ++i) {
+        if (i < A_INSTR)
+          lds_direct_16(ld_A + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+        else
+          lds_direct_16_stream(ld_W + off[i] + k0, base + (wave + 4 * i) * RPI * KB);
+      }
     } else {
       // partial stage: lanes past K fetch the stage's last valid chunk of
       // their row again (same cache line as a valid lane; never read)
@@ -1051,7 +1063,10 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
       for (int i = 0; i < PER_WAVE; ++i) {
         const int chunk = ws_swz(RPI * (wave + 4 * i) + lane / CHUNKS, lane % CHUNKS);
         const uint32_t o = off[i] + k0 - (uint32_t)(chunk > last ? chunk - last : 0) * 8;
-        lds_direct_16((i < A_INSTR ? ld_A : ld_W) + o, base + (wave + 4 * i) * RPI * KB);
+        if (i < A_INSTR)
+          lds_direct_16(ld_A + o, base + (wave + 4 * i) * RPI * KB);
+        else
+          lds_direct_16_stream(ld_W + o, base + (wave + 4 * i) * RPI * KB);
       }
     }
     slot_ld = slot_ld + 1 == STAGES ? 0 : slot_ld + 1;
@@ -1336,15 +1351,15 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
       const int c = w4_swz<S::W_CH>(r, lane % S::W_CH);
       const int back = c / 4 >= gv ? (c / 4 - gv + 1) * 64 : 0;
       const uint32_t o = offW[i] + (uint32_t)(k0 / 2) - (uint32_t)back;  // >= 0: back <= 16 c
-      lds_direct_16(ld_W + o,
-                    reinterpret_cast<uint16_t*>(base + S::A_BYTES + (wave + NW * i) * 1024));
+      lds_direct_16_stream(ld_W + o,
+                           reinterpret_cast<uint16_t*>(base + S::A_BYTES + (wave + NW * i) * 1024));
     }
     if (lane < S::S_LANES) {
       // K group of the piece; groups past K fetch the stage's last one again
       const int gk = k0 / 128 + min(lane / (2 * NBLK), gv - 1);
-      lds_direct_16(ld_S + (offS + (uint32_t)gk * (uint32_t)rs),
-                    reinterpret_cast<uint16_t*>(base + S::A_BYTES + S::W_BYTES +
-                                                wave * S::S_WAVE));
+      lds_direct_16_stream(ld_S + (offS + (uint32_t)gk * (uint32_t)rs),
+                           reinterpret_cast<uint16_t*>(base + S::A_BYTES + S::W_BYTES +
+                                                       wave * S::S_WAVE));
     }
     slot_ld = slot_ld + 1 == STAGES ? 0 : slot_ld + 1;
     if (++kt_ld == nk) {
