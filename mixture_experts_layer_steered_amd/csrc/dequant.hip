@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void w4_dequant_kernel(const uint32_t* __restr
   for (int c8 = threadIdx.x; c8 < wpr; c8 += 256) {
     const float sc = bf16_bits_to_f32(sr[(int64_t)(c8 >> 4) * rows]);
     const float m = -136.0f * sc;  // exact: 136 has 5 significant bits
-    const uint32_t d = qr[c8];
+    const uint32_t d = __builtin_nontemporal_load(qr + c8);  // read once
     // bytes u of columns 0..3 (low nibbles) and 4..7 (high nibbles), then
     // bf16 pairs 128 + u (bits 0x43 over each byte); (128 + u) * sc - 136 sc
     // = (u - 8) * sc is exact in one fma, then one rounding to bf16
