@@ -133,10 +133,12 @@ typedef struct moe_weights {
    * bf16.  Decode-sized batches (T*k <= 64*E) stream the codes and unpack
    * them in registers (exact products: the results equal the dequantised
    * layer up to fp32 summation order).  Larger batches, bound by the matrix
-   * cores, first dequantise the layer's experts into the workspace (each
-   * weight rounded to bf16, the MFMA operand type: one more rounding than
-   * the exact dequantisation) and run the bf16 grouped GEMMs; their
-   * workspace then holds E * 3 * I * H bf16 more. */
+   * cores, first dequantise the layer's experts into the workspace as bf16,
+   * the MFMA operand type, and run the bf16 grouped GEMMs; their workspace
+   * then holds E * 3 * I * H bf16 more.  That dequantisation is exact when
+   * every scale carries at most 4 significant bits (the precision of E4M3
+   * scale factors); finer scales get each weight rounded once to bf16 on
+   * this path. */
   const uint8_t* w_gate_up_q;       /* [E, 2I, H/2] codes; NULL = bf16 experts    */
   const moe_bf16* w_gate_up_scale;  /* [E, H/128, 2I] bf16                        */
   const uint8_t* w_down_q;          /* [E, H, I/2] codes                          */

@@ -9,7 +9,9 @@
 // stored group-major [K/128, rows].  (u - 8) * scale has at most 12
 // significant bits, so it is exact in fp32; each weight is then rounded to
 // bf16 (to nearest, ties to even, by the hardware conversion), the operand
-// type of the MFMAs.
+// type of the MFMAs -- exact when the scale has at most 4 significant bits
+// (4 + 4 bits fit bf16's 8), the scale precision this library's format
+// assumes.
 //
 // One workgroup per weight row (of all groups): its threads walk the row's
 // code words, 4 bytes in and 16 bytes (8 bf16) out each.

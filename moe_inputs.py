@@ -31,8 +31,10 @@ W4A16 routed experts (workloads with w4): per weight a uniform nibble u in
 [0, 15] (the value is u - 8; 4-byte words of 8 columns, byte j holding
 columns j and j + 4 in its low and high nibble), and
 per row and group of 128 columns a bf16 scale weight_std / sqrt(21.5) *
-U(0.5, 1.5) (21.5 is the mean of (u - 8)^2), stored [K/128, rows]; so the
-weights have about the bf16 experts' spread.  The shared expert stays bf16.
+U(0.5, 1.5) (21.5 is the mean of (u - 8)^2) rounded to 4 significant bits
+(nearest, ties to even), stored [K/128, rows]; so the weights have about
+the bf16 experts' spread and each is exact in bf16.  The shared expert
+stays bf16.
 
 Random streams: numpy PCG64 children of SeedSequence(seed), spawned in a
 fixed order: x (x_prev for ScMoE), x_cur, W_r, b, W_gu[e] for e=0..E-1,
@@ -134,6 +136,10 @@ def _w4_matrix(g: np.random.Generator, R: int, K: int, std: float) -> tuple[np.n
     groups = (K + W4_GROUP - 1) // W4_GROUP
     sc = g.uniform(0.5, 1.5, size=(groups, R)).astype(np.float32)
     sc *= np.float32(std / W4_CODE_RMS)
+    # 4 significant bits (the precision of E4M3 scale factors): every weight
+    # (u - 8) * scale then has at most 8 significant bits, exact in bf16
+    m, e = np.frexp(sc)
+    sc = np.ldexp(np.rint(m * 16.0) / 16.0, e).astype(np.float32)
     return q, f32_to_bf16_bits(sc)
 
 

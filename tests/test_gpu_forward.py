@@ -234,6 +234,13 @@ def test_forward_decode_w4_full():
     assert rep["rows_checked"] == 32
 
 
+def test_forward_prefill_w4_full_sampled():
+    # T * k = 65 536 rows over 64 experts: the dequantising path (bf16 GEMMs
+    # on weights rounded once to bf16) against the oracle's exact weights
+    rep = _full("prefill_w4", 96)
+    assert rep["experts_touched"] == 64
+
+
 # ------------------------------------------------ finish (residual add) ----
 
 FINISH = {
@@ -284,6 +291,24 @@ def test_forward_finish(name):
     # values, so that -0 and +0 (from o + 0 in the keeping finish) compare equal
     assert np.array_equal(mo.bf16_to_f64(got), mo.bf16_to_f64(want)), \
         f"fused finish differs in {int(np.sum(mo.bf16_to_f64(got) != mo.bf16_to_f64(want)))} elements"
+
+
+def test_forward_prefill_finish_full_sampled():
+    """The prefill workload with the residual add fused into the combine
+    (coefficients 1), as the bench's --finish runs it, on a token sample."""
+    wl = moe_inputs.WORKLOADS["prefill"]
+    inp = moe_inputs.generate(wl, seed=0)
+    res_bits = moe_inputs.f32_to_bf16_bits(
+        np.random.default_rng(1).standard_normal((wl.T, wl.H)).astype(np.float32))
+    fin = dict(residual=res_bits, out_scale=1.0, residual_scale=1.0)
+    rows = np.sort(np.random.default_rng(7).choice(wl.T, size=64, replace=False))
+    gh.note(f"forward_finish {wl.label()} sampled")
+    d = gh.Device(wl, inp, finish=fin)
+    d.canary()
+    d.run()
+    rep = gh.check_layer(wl, inp, d.result(), rows, finish=fin)
+    gh.note(f"  {rep}")
+    assert rep["rows_checked"] == 64
 
 
 # ------------------------------- W4A16 experts beyond weight streaming ----

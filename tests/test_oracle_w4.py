@@ -93,6 +93,20 @@ def test_w4_layer_equals_bf16_layer_on_exact_weights():
     assert np.array_equal(a["out"], b["out"])
 
 
+def test_w4_scales_make_every_weight_exact_in_bf16():
+    """The synthetic scales carry 4 significant bits, so (u - 8) * scale (at
+    most 4 + 4 bits) is a bf16 value: the tiled path's bf16 operand equals
+    the exact weight."""
+    wl = moe_inputs.WORKLOADS["decode_w4"].with_(E=2, H=512, I=256)
+    inp = moe_inputs.generate(wl, 1)
+    for name in ("w_gate_up", "w_down"):
+        s = inp[name + "_scale"]
+        assert np.all((s & 0xF) == 0) and np.all(s != 0)
+        for e in range(s.shape[0]):
+            w = mo.dequant_w4(inp[name + "_q"][e], s[e])
+            assert np.array_equal(mo.bf16_to_f64(mo.bf16_round(w)), w)
+
+
 def test_w4_inputs_spread():
     wl = moe_inputs.WORKLOADS["decode_w4"].with_(E=2, H=512, I=256)
     inp = moe_inputs.generate(wl, 0)
