@@ -348,6 +348,21 @@ moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
                                const float* w_router, moe_bf16* grad_x, float* grad_w,
                                float* grad_b, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* W4A16 weights -> bf16, for callers whose weights stay fixed across calls:
+ * expand them once, then run the bf16 forward (moe_forward with w4 = 0)
+ * instead of dequantising on every prefill-sized call.  q: [n_groups, rows,
+ * K/2] codes, scale: [n_groups, K/128, rows] bf16, both in the W4A16 layout
+ * of moe_weights; out: [n_groups, rows, K] bf16, out[g][r][c] =
+ * bf16((u - 8) * scale) rounded to nearest, ties to even -- exact when the
+ * scale carries at most 4 significant bits (a zero weight is +0).  K must be a multiple of 128 and
+ * n_groups * rows < 2^31; q, scale and out 16-byte aligned (the caller owns
+ * all three; out must not overlap the inputs).  n_groups, rows or K == 0 is
+ * a successful no-op.  Source: the grouped W4A16 expert GEMM of "Module
+ * glm5next_mlp" (its weights are dequantised to the 16-bit MMA operand type;
+ * the layout is this library's). */
+moe_status moe_w4_dequantize(const uint8_t* q, const moe_bf16* scale, int32_t n_groups,
+                             int64_t rows, int32_t K, moe_bf16* out, hipStream_t stream);
+
 /* Static text naming a status code. */
 const char* moe_status_string(moe_status s);
 

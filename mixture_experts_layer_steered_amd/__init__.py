@@ -99,6 +99,8 @@ def _load() -> ctypes.CDLL:
         "moe_router_backward_workspace_size": (st, [P, POINTER(c_size_t)]),
         "moe_router_backward": (st, [P, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "moe_w4_dequantize": (st, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_void_p,
+                                   c_void_p]),
         "moe_status_string": (c_char_p, [c_int]),
         "moe_last_error": (c_char_p, []),
     }
@@ -113,8 +115,8 @@ _lib = _load()
 EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
             "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
             "moe_combine_finish", "moe_forward", "moe_forward_finish",
-            "moe_router_backward_workspace_size", "moe_router_backward", "moe_status_string",
-            "moe_last_error")
+            "moe_router_backward_workspace_size", "moe_router_backward", "moe_w4_dequantize",
+            "moe_status_string", "moe_last_error")
 
 
 def _status_name(s: int) -> str:
@@ -245,6 +247,13 @@ def moe_forward_finish(params, x_routed, x_shared, weights: moe_weights, fin, ou
     _check(_lib.moe_forward_finish(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
                                    ctypes.byref(weights), f, _ptr(out), pr, _ptr(ws), _nbytes(ws),
                                    _stream(stream)))
+
+
+def moe_w4_dequantize(q, scale, out, n_groups, rows, K, stream=None):
+    """W4A16 codes [n_groups, rows, K/2] and scales [n_groups, K/128, rows]
+    -> bf16 bits [n_groups, rows, K] in `out`."""
+    _check(_lib.moe_w4_dequantize(_ptr(q), _ptr(scale), int(n_groups), int(rows), int(K),
+                                  _ptr(out), _stream(stream)))
 
 
 def moe_router_backward_workspace_size(params: moe_params) -> int:

@@ -715,6 +715,26 @@ moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
   return ok();
 }
 
+moe_status moe_w4_dequantize(const uint8_t* q, const moe_bf16* scale, int32_t n_groups,
+                             int64_t rows, int32_t K, moe_bf16* out, hipStream_t stream) {
+  if (n_groups < 0 || rows < 0 || K < 0)
+    return fail(MOE_ERR_INVALID_ARG, "negative size (n_groups %d, rows %lld, K %d)", n_groups,
+                (long long)rows, K);
+  if (K % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "K = %d is not a multiple of 128", K);
+  if ((int64_t)n_groups * rows >= kMaxPairs)
+    return fail(MOE_ERR_UNSUPPORTED, "n_groups * rows = %lld >= 2^31",
+                (long long)((int64_t)n_groups * rows));
+  if (n_groups == 0 || rows == 0 || K == 0) return ok();
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(scale);
+  REQUIRE_PTR(out);
+  moe_status s;
+  if ((s = device_status(launch_w4_dequant(q, scale, out, n_groups, rows, K, stream),
+                         "dequantise")) != MOE_OK)
+    return s;
+  return ok();
+}
+
 moe_status moe_forward(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
                        const moe_weights* w, moe_bf16* out, const moe_probes* probes, void* ws,
                        size_t ws_bytes, hipStream_t stream) {

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(moe.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -219,6 +219,26 @@ def test_router_backward_validation():
     # nothing asked for: nothing to do, also without buffers
     moe.moe_router_backward(p, 16, 16, 16, strides=(24, 1), stream=0)
     moe.moe_router_backward(P(T=0), None, None, None, stream=0)
+
+
+def test_w4_dequantize_validation():
+    cases = [
+        (dict(rows=-1), moe.MOE_ERR_INVALID_ARG),
+        (dict(K=200), moe.MOE_ERR_UNSUPPORTED),                  # not a multiple of 128
+        (dict(n_groups=1 << 16, rows=1 << 15), moe.MOE_ERR_UNSUPPORTED),  # 2^31 rows
+        (dict(q=None), moe.MOE_ERR_INVALID_ARG),
+        (dict(scale=8), moe.MOE_ERR_UNSUPPORTED),                # misaligned
+        (dict(out=None), moe.MOE_ERR_INVALID_ARG),
+    ]
+    for kw, status in cases:
+        args = dict(q=16, scale=16, out=16, n_groups=2, rows=64, K=256)
+        args.update(kw)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_w4_dequantize(**args, stream=0)
+        assert ei.value.status == status, (kw, status)
+    # empty: nothing to do, also without buffers
+    moe.moe_w4_dequantize(None, None, None, 0, 64, 256, stream=0)
+    moe.moe_w4_dequantize(None, None, None, 2, 64, 0, stream=0)
 
 
 def test_empty_batch_is_a_noop_without_pointers():

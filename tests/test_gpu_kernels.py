@@ -237,3 +237,42 @@ def test_combine_finish_bits(tl, post, in_place, c0, c1):
     torch.cuda.synchronize()
     want = mo.finish(gh.to_bits(o), res, c0, c1)
     assert np.array_equal(gh.to_bits(out), want)
+
+
+# ------------------------------------------------- W4A16 dequantisation ----
+
+@pytest.mark.parametrize("G,R,K,scales", [
+    (3, 70, 384, "synthetic"),   # the generator's 4-significant-bit scales: exact in bf16
+    (2, 33, 256, "fine"),        # arbitrary bf16 scales (8 bits): one rounding per weight
+    (1, 1, 128, "fine"),         # one row, one group
+])
+def test_w4_dequantize_bits(tl, G, R, K, scales):
+    """moe_w4_dequantize = bf16 of the oracle's exact dequantisation (round to
+    nearest even) in value -- bit for bit except the sign of zero weights
+    (u = 8 under a negative scale: the oracle's 0 * (-s) is -0, the kernel's
+    (128 + u) s - 136 s is +0); nothing is written past the output."""
+    torch, moe = tl
+    gh.note(f"w4_dequantize G={G} R={R} K={K} scales={scales}")
+    rng = np.random.default_rng(K + R)
+    q = rng.integers(0, 256, size=(G, R, K // 2), dtype=np.uint8)
+    if scales == "synthetic":
+        inp = moe_inputs.generate(moe_inputs.Workload("dq", T=4, H=K, E=G, k=1, I=128, I_s=0,
+                                                      w4=True), seed=2)
+        sc = inp["w_gate_up_scale"][:, :, :R].copy()
+    else:
+        sc = moe_inputs.f32_to_bf16_bits(
+            rng.uniform(1e-3, 4e-3, size=(G, K // 128, R)).astype(np.float32)
+            * rng.choice([-1.0, 1.0], size=(G, K // 128, R)).astype(np.float32))
+    want = np.stack([mo.bf16_round(mo.dequant_w4(q[g], sc[g])) for g in range(G)])
+    q_d = torch.from_numpy(q).cuda()
+    sc_d = gh.dev_bf16(torch, sc)
+    pad = 1024
+    buf = torch.full((G * R * K + pad,), 0x7FC0, dtype=torch.int16, device="cuda")
+    moe.moe_w4_dequantize(q_d, sc_d, buf, G, R, K)
+    torch.cuda.synchronize()
+    got = gh.to_bits(buf)
+    got_w = got[:G * R * K].reshape(G, R, K)
+    assert np.array_equal(mo.bf16_to_f64(got_w), mo.bf16_to_f64(want))
+    nz = mo.bf16_to_f64(want) != 0
+    assert np.array_equal(got_w[nz], want[nz]) and np.all(got_w[~nz] == 0)
+    assert np.all(got[G * R * K:] == 0x7FC0)
