@@ -187,7 +187,9 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: 
     f_scale, w_scale = gib / (cf_kib * 1024.0), gib / (cw_kib * 1024.0)
     fetch_b = f_kib * 1024.0 * f_scale
     write_b = w_kib * 1024.0 * w_scale
-    out = {"workload": wl.label(), "kernel": "grouped gate_up + SwiGLU (routed experts)",
+    kernel = ("grouped gate_up + SwiGLU (routed experts)" if wl.T * wl.k <= 64 * wl.E
+              else "grouped gate_up + SwiGLU (routed + shared, one launch)")
+    out = {"workload": wl.label(), "kernel": kernel,
            "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
            "dispatches": [nf, nw],
            "copy_calibration": {"kernel": "torch.neg fp32, 1 GiB in, 1 GiB out",
