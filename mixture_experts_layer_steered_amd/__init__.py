@@ -5,8 +5,9 @@ function has the C name, takes torch tensors (device memory) or None for a
 NULL pointer, marshals them to pointers, enqueues on the current (or given)
 HIP stream and raises MoeError on a non-OK status.  All arithmetic happens
 in the library's HIP kernels; there is no other implementation behind
-these names, and importing fails if the library has not been built
-(python -m mixture_experts_layer_steered_amd.build).
+these names.  The library is loaded on the first call (so that the build
+module, python -m mixture_experts_layer_steered_amd.build, can run on a
+fresh checkout); that call raises ImportError if it has not been built.
 
 bf16 tensors may be torch.bfloat16 or torch.int16/uint16 bit patterns.
 """
@@ -111,7 +112,17 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-_lib = _load()
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (loaded on first use; ImportError if missing)."""
+    global _lib_handle
+    if _lib_handle is None:
+        _lib_handle = _load()
+    return _lib_handle
+
+
 EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
             "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
             "moe_combine_finish", "moe_forward", "moe_forward_finish",
@@ -120,12 +131,12 @@ EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
 
 
 def _status_name(s: int) -> str:
-    return _lib.moe_status_string(s).decode()
+    return lib().moe_status_string(s).decode()
 
 
 def _check(s: int) -> None:
     if s != MOE_OK:
-        raise MoeError(s, _lib.moe_last_error().decode())
+        raise MoeError(s, lib().moe_last_error().decode())
 
 
 def _ptr(t):
@@ -161,33 +172,33 @@ def make_params(T, H, E, k, I, I_shared, routed_scaling_factor, swiglu_limit, sc
 
 def moe_workspace_size(params: moe_params) -> int:
     n = c_size_t(0)
-    _check(_lib.moe_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    _check(lib().moe_workspace_size(ctypes.byref(params), ctypes.byref(n)))
     return n.value
 
 
 def moe_router_topk(params, x, w_router, corr_bias, topk_ids, topk_w, ws, stream=None):
-    _check(_lib.moe_router_topk(ctypes.byref(params), _ptr(x), _ptr(w_router), _ptr(corr_bias),
+    _check(lib().moe_router_topk(ctypes.byref(params), _ptr(x), _ptr(w_router), _ptr(corr_bias),
                                 _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws),
                                 _stream(stream)))
 
 
 def moe_permute(params, topk_ids, expert_offsets, sorted_token, inv_pos, ws, stream=None,
                 x=None, x_perm=None):
-    _check(_lib.moe_permute(ctypes.byref(params), _ptr(topk_ids), _ptr(x), _ptr(expert_offsets),
+    _check(lib().moe_permute(ctypes.byref(params), _ptr(topk_ids), _ptr(x), _ptr(expert_offsets),
                             _ptr(sorted_token), _ptr(inv_pos), _ptr(x_perm), _ptr(ws),
                             _nbytes(ws), _stream(stream)))
 
 
 def moe_grouped_gemm_workspace_size(n_groups, M_total, H, I) -> int:
     n = c_size_t(0)
-    _check(_lib.moe_grouped_gemm_workspace_size(int(n_groups), int(M_total), int(H), int(I),
+    _check(lib().moe_grouped_gemm_workspace_size(int(n_groups), int(M_total), int(H), int(I),
                                                 ctypes.byref(n)))
     return n.value
 
 
 def moe_grouped_swiglu_gemm(n_groups, M_total, H, I, swiglu_limit, a, row_index, group_offsets,
                             w_gate_up, w_down, h, y, ws, stream=None):
-    _check(_lib.moe_grouped_swiglu_gemm(int(n_groups), int(M_total), int(H), int(I),
+    _check(lib().moe_grouped_swiglu_gemm(int(n_groups), int(M_total), int(H), int(I),
                                         float(swiglu_limit), _ptr(a), _ptr(row_index),
                                         _ptr(group_offsets), _ptr(w_gate_up), _ptr(w_down),
                                         _ptr(h), _ptr(y), _ptr(ws), _nbytes(ws),
@@ -195,7 +206,7 @@ def moe_grouped_swiglu_gemm(n_groups, M_total, H, I, swiglu_limit, a, row_index,
 
 
 def moe_combine(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, out, stream=None):
-    _check(_lib.moe_combine(ctypes.byref(params), _ptr(y_perm), _ptr(topk_w), _ptr(inv_pos),
+    _check(lib().moe_combine(ctypes.byref(params), _ptr(y_perm), _ptr(topk_w), _ptr(inv_pos),
                             _ptr(y_shared), _ptr(gamma_post), _ptr(out), _stream(stream)))
 
 
@@ -207,7 +218,7 @@ def make_finish(residual, out_scale=1.0, residual_scale=1.0, post_norm=False) ->
 def moe_combine_finish(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, fin, out,
                        stream=None):
     f = ctypes.byref(fin) if fin is not None else None
-    _check(_lib.moe_combine_finish(ctypes.byref(params), _ptr(y_perm), _ptr(topk_w),
+    _check(lib().moe_combine_finish(ctypes.byref(params), _ptr(y_perm), _ptr(topk_w),
                                    _ptr(inv_pos), _ptr(y_shared), _ptr(gamma_post), f, _ptr(out),
                                    _stream(stream)))
 
@@ -235,7 +246,7 @@ def make_probes(topk_ids=None, topk_w=None, expert_offsets=None, sorted_token=No
 def moe_forward(params, x_routed, x_shared, weights: moe_weights, out, probes=None, ws=None,
                 stream=None):
     pr = ctypes.byref(probes) if probes is not None else None
-    _check(_lib.moe_forward(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
+    _check(lib().moe_forward(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
                             ctypes.byref(weights), _ptr(out), pr, _ptr(ws), _nbytes(ws),
                             _stream(stream)))
 
@@ -244,7 +255,7 @@ def moe_forward_finish(params, x_routed, x_shared, weights: moe_weights, fin, ou
                        ws=None, stream=None):
     f = ctypes.byref(fin) if fin is not None else None
     pr = ctypes.byref(probes) if probes is not None else None
-    _check(_lib.moe_forward_finish(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
+    _check(lib().moe_forward_finish(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
                                    ctypes.byref(weights), f, _ptr(out), pr, _ptr(ws), _nbytes(ws),
                                    _stream(stream)))
 
@@ -252,13 +263,13 @@ def moe_forward_finish(params, x_routed, x_shared, weights: moe_weights, fin, ou
 def moe_w4_dequantize(q, scale, out, n_groups, rows, K, stream=None):
     """W4A16 codes [n_groups, rows, K/2] and scales [n_groups, K/128, rows]
     -> bf16 bits [n_groups, rows, K] in `out`."""
-    _check(_lib.moe_w4_dequantize(_ptr(q), _ptr(scale), int(n_groups), int(rows), int(K),
+    _check(lib().moe_w4_dequantize(_ptr(q), _ptr(scale), int(n_groups), int(rows), int(K),
                                   _ptr(out), _stream(stream)))
 
 
 def moe_router_backward_workspace_size(params: moe_params) -> int:
     n = c_size_t(0)
-    _check(_lib.moe_router_backward_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    _check(lib().moe_router_backward_workspace_size(ctypes.byref(params), ctypes.byref(n)))
     return n.value
 
 
@@ -269,7 +280,7 @@ def moe_router_backward(params, grad_logits, x, w_router, grad_x=None, grad_w=No
     pointer with `strides` = (row, column) in elements."""
     if strides is None:
         strides = tuple(grad_logits.stride()) if grad_logits is not None else (0, 0)
-    _check(_lib.moe_router_backward(ctypes.byref(params), _ptr(grad_logits), int(strides[0]),
+    _check(lib().moe_router_backward(ctypes.byref(params), _ptr(grad_logits), int(strides[0]),
                                     int(strides[1]), _ptr(x), _ptr(w_router), _ptr(grad_x),
                                     _ptr(grad_w), _ptr(grad_b), _ptr(ws), _nbytes(ws),
                                     _stream(stream)))

@@ -91,7 +91,7 @@ def test_param_validation(kw, status):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_workspace_size(P(**kw))
     assert ei.value.status == status
-    assert moe._lib.moe_last_error().decode() != ""
+    assert moe.lib().moe_last_error().decode() != ""
 
 
 def test_workspace_size_is_pure_and_grows():
@@ -254,4 +254,4 @@ def test_empty_batch_is_a_noop_without_pointers():
 def test_status_strings():
     for s, name in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARG"), (2, "MOE_ERR_UNSUPPORTED"),
                     (3, "MOE_ERR_WORKSPACE"), (4, "MOE_ERR_DEVICE")]:
-        assert moe._lib.moe_status_string(s).decode() == name
+        assert moe.lib().moe_status_string(s).decode() == name

@@ -185,6 +185,62 @@ def test_rmsnorm_closed_form():
     np.testing.assert_array_equal(got, [[0.84765625, 1.1328125]])
 
 
+def test_rmsnorm_gain_closed_form():
+    """RMSNorm([3, 4]) with gain [2, 1/2], worked by hand: r = 1/sqrt(12.5),
+    so the values are 6r = 1.6970563 and 2r = 0.5656854.  bf16 keeps 8
+    significant bits: in [1, 2) the step is 2^-7, and 1.6970563 lies between
+    1.6953125 (217 steps) and 1.703125 (218), nearer the first; in [1/2, 1)
+    the step is 2^-8, and 0.5656854 lies between 0.5625 (144 steps) and
+    0.56640625 (145), nearer the second.  Ignoring the gain would give
+    [0.84765625, 1.1328125], dividing by it [0.423828125, 2.265625]."""
+    xb = moe_inputs.f32_to_bf16_bits(np.array([[3.0, 4.0]], np.float32))
+    g = np.array([2.0, 0.5], np.float32)
+    got = mo.bf16_to_f64(mo.rmsnorm_bf16(xb, g, 0.0))
+    np.testing.assert_array_equal(got, [[1.6953125, 0.56640625]])
+
+
+def test_scmoe_pre_gain_scales_routed_input_per_channel():
+    """The ScMoE pre-norm gain multiplies each channel of the routed input:
+    a power-of-two gain on one channel scales exactly that column of xr by
+    the same power of two (bf16 rounding commutes with it) and leaves the
+    others and the shared path alone; the post-norm gain does not touch xr."""
+    H = 32
+    inp = tiny_inputs(T=16, H=H, E=6, k=2, I=8, I_s=8, std=0.3, seed=23, scmoe=True)
+    kw = dict(k=2, rsf=1.0, limit=7.0, scmoe=True, eps=1e-6)
+    base = mo.forward(inp, **kw)
+    for ch, c in ((0, 4.0), (7, 0.25), (31, 2.0)):
+        g = np.ones(H, np.float32)
+        g[ch] = c
+        got = mo.forward(dict(inp, gamma_pre=g), **kw)
+        xb, xg = mo.bf16_to_f64(base["xr"]), mo.bf16_to_f64(got["xr"])
+        np.testing.assert_array_equal(xg[:, ch], c * xb[:, ch])
+        others = np.arange(H) != ch
+        np.testing.assert_array_equal(xg[:, others], xb[:, others])
+        np.testing.assert_array_equal(got["ys"], base["ys"])
+    # the post-norm gain leaves the routed input alone
+    gp = np.linspace(0.5, 1.5, H).astype(np.float32)
+    np.testing.assert_array_equal(mo.forward(dict(inp, gamma_post=gp), **kw)["xr"], base["xr"])
+
+
+def test_scmoe_routes_the_gained_input():
+    """With a jittered pre-norm gain the routed half of the ScMoE layer is
+    the plain layer run on the gained, normalised input: a gain of 2^j on
+    every channel gives xr exactly 2^j times the unit-gain xr, and the
+    router then sees logits 2^j times larger."""
+    H = 32
+    inp = tiny_inputs(T=16, H=H, E=6, k=2, I=8, I_s=8, std=0.3, seed=24, scmoe=True)
+    kw = dict(k=2, rsf=1.0, limit=7.0, scmoe=True, eps=1e-6)
+    base = mo.forward(inp, **kw)
+    four = mo.forward(dict(inp, gamma_pre=np.full(H, 4.0, np.float32)), **kw)
+    np.testing.assert_array_equal(mo.bf16_to_f64(four["xr"]), 4.0 * mo.bf16_to_f64(base["xr"]))
+    np.testing.assert_allclose(four["logits"], 4.0 * base["logits"], rtol=1e-6, atol=1e-7)
+    g = (1 + np.random.default_rng(3).uniform(-0.1, 0.1, H)).astype(np.float32)
+    a = mo.forward(dict(inp, gamma_pre=g), **kw)
+    c = mo.forward(dict(inp, x=a["xr"]), k=2, rsf=1.0, limit=7.0, include_shared=False)
+    np.testing.assert_array_equal(a["ids"], c["ids"])
+    np.testing.assert_allclose(a["z"] - a["ys"], c["z"], rtol=1e-12, atol=1e-12)
+
+
 def test_rmsnorm_scale_invariance_exact_for_powers_of_two():
     rng = np.random.default_rng(4)
     x = moe_inputs.f32_to_bf16_bits(rng.standard_normal((5, 64)).astype(np.float32))

@@ -120,3 +120,51 @@ def test_planted_finish_mistake_is_caught(monkeypatch, name, fake):
         except AssertionError:
             failed += 1
     assert failed > 0, name
+
+
+# Planted mistakes in the ScMoE pre-norm gain: each must fail a pin of the
+# pre-norm (the hand-worked gain, the per-channel scaling of the routed
+# input, the gained routing).
+_real_rmsnorm_bf16 = mo.rmsnorm_bf16
+
+
+def _gain_ignored(x_bits, gamma, eps):
+    return _real_rmsnorm_bf16(x_bits, None, eps)
+
+
+def _gain_inverted(x_bits, gamma, eps):
+    inv = None if gamma is None else (1.0 / np.asarray(gamma, np.float64)).astype(np.float32)
+    return _real_rmsnorm_bf16(x_bits, inv, eps)
+
+
+_real_forward = mo.forward
+
+
+def _post_gain_used_before_routing(inp, **kw):
+    # the forward hands the post-norm gain to the pre-norm
+    return _real_forward(dict(inp, gamma_pre=inp.get("gamma_post")), **kw)
+
+
+@pytest.mark.parametrize("name,fake", [
+    ("pre-norm gain ignored", _gain_ignored),
+    ("pre-norm gain inverted", _gain_inverted),
+])
+def test_planted_pre_gain_mistake_is_caught(monkeypatch, name, fake):
+    from tests import test_oracle_layer as pins
+    monkeypatch.setattr(mo, "rmsnorm_bf16", fake)
+    failed = 0
+    for pin in (pins.test_rmsnorm_gain_closed_form,
+                pins.test_scmoe_pre_gain_scales_routed_input_per_channel,
+                pins.test_scmoe_routes_the_gained_input):
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 2, name
+
+
+def test_planted_gain_swap_is_caught(monkeypatch):
+    from tests import test_oracle_layer as pins
+    monkeypatch.setattr(mo, "forward", _post_gain_used_before_routing)
+    with pytest.raises(AssertionError):
+        pins.test_scmoe_pre_gain_scales_routed_input_per_channel()
