@@ -323,6 +323,33 @@ moe_status moe_forward_finish(const moe_params* p, const moe_bf16* x_routed,
                               const moe_finish* fin, moe_bf16* out, const moe_probes* probes,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the fixed device scratch of moe_forward_noalloc (64 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The layer's intermediates live
+ * in a fixed scratch array of MOE_NOALLOC_SCRATCH_BYTES inside the library,
+ * one copy per device, held from the library's first use on that device
+ * until the process ends; its device address is looked up once per device
+ * (the first call on it).  The call allocates and frees nothing and creates
+ * no stream: every kernel runs on `stream` (the shared expert shares the
+ * routed experts' grouped launches instead of running beside the routing
+ * kernels).  Results equal moe_forward's for the same inputs.
+ *   Returns MOE_ERR_WORKSPACE, enqueuing nothing, when
+ *   moe_workspace_size(p) > MOE_NOALLOC_SCRATCH_BYTES (decode-sized
+ *   batches fit: T = 32, H = 4096, E = 64, k = 8, I = 1408, I_shared =
+ *   2816 needs 5.5 MiB, T = 256 of the same layer 44 MiB).
+ *   Every call on one device uses that device's one scratch array, which
+ *   keeps the previous call's contents (nothing in it needs to start at
+ *   zero): calls whose work can overlap on one device -- on different
+ *   streams, or from several threads -- race and corrupt each other's
+ *   results.  Order them on one stream.
+ * Other arguments, validation and errors as in moe_forward. */
+moe_status moe_forward_noalloc(const moe_params* p, const moe_bf16* x_routed,
+                               const moe_bf16* x_shared, const moe_weights* w, moe_bf16* out,
+                               const moe_probes* probes, hipStream_t stream);
+
 /* Bytes of workspace moe_router_backward needs for p->T, H, E (host-only,
  * pure; 0 is possible). */
 moe_status moe_router_backward_workspace_size(const moe_params* p, size_t* bytes);

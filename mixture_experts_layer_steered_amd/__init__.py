@@ -17,6 +17,13 @@ import ctypes
 import os
 from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
+# torch first, at import: its bundled HIP runtime (soname libamdhip64.so.7)
+# is then the one libmoe.so binds to whenever it is loaded in this process,
+# so one runtime serves both (streams and device pointers are objects of
+# that runtime).  A process that loads libmoe.so before importing torch
+# binds the system runtime instead, and torch's tensors are not its own.
+import torch  # noqa: F401,E402
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
@@ -27,6 +34,7 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_DEVICE = 4
 MOE_MAX_TOP_K = 16
 MOE_MAX_EXPERTS = 1024
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -66,10 +74,6 @@ class moe_probes(Structure):
 
 
 def _load() -> ctypes.CDLL:
-    # torch first: its bundled HIP runtime then satisfies libmoe.so's
-    # libamdhip64.so.7 dependency, so one runtime serves both (streams and
-    # device pointers are shared objects of that runtime).
-    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
@@ -97,6 +101,8 @@ def _load() -> ctypes.CDLL:
         "moe_forward_finish": (st, [P, c_void_p, c_void_p, POINTER(moe_weights),
                                     POINTER(moe_finish), c_void_p, POINTER(moe_probes), c_void_p,
                                     c_size_t, c_void_p]),
+        "moe_forward_noalloc": (st, [P, c_void_p, c_void_p, POINTER(moe_weights), c_void_p,
+                                     POINTER(moe_probes), c_void_p]),
         "moe_router_backward_workspace_size": (st, [P, POINTER(c_size_t)]),
         "moe_router_backward": (st, [P, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -125,7 +131,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
             "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
-            "moe_combine_finish", "moe_forward", "moe_forward_finish",
+            "moe_combine_finish", "moe_forward", "moe_forward_finish", "moe_forward_noalloc",
             "moe_router_backward_workspace_size", "moe_router_backward", "moe_w4_dequantize",
             "moe_status_string", "moe_last_error")
 
@@ -258,6 +264,14 @@ def moe_forward_finish(params, x_routed, x_shared, weights: moe_weights, fin, ou
     _check(lib().moe_forward_finish(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
                                    ctypes.byref(weights), f, _ptr(out), pr, _ptr(ws), _nbytes(ws),
                                    _stream(stream)))
+
+
+def moe_forward_noalloc(params, x_routed, x_shared, weights: moe_weights, out, probes=None,
+                        stream=None):
+    """moe_forward on the library's fixed scratch (no workspace argument)."""
+    pr = ctypes.byref(probes) if probes is not None else None
+    _check(lib().moe_forward_noalloc(ctypes.byref(params), _ptr(x_routed), _ptr(x_shared),
+                                     ctypes.byref(weights), _ptr(out), pr, _stream(stream)))
 
 
 def moe_w4_dequantize(q, scale, out, n_groups, rows, K, stream=None):

@@ -461,9 +461,12 @@ moe_status combine_impl(const moe_params* p, const float* y_perm, const float* t
   return ok();
 }
 
+// one_stream: everything on `stream` (no second stream: the shared expert
+// shares the routed experts' launches, W4A16 dequantisation runs in line).
 moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe_bf16* x_shared,
                         const moe_weights* w, const moe_finish* fin, moe_bf16* out,
-                        const moe_probes* probes, void* ws, size_t ws_bytes, hipStream_t stream) {
+                        const moe_probes* probes, void* ws, size_t ws_bytes, hipStream_t stream,
+                        bool one_stream = false) {
   moe_status s = check_params(p);
   if (s != MOE_OK) return s;
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
@@ -561,9 +564,10 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   // Weight streaming (decode-sized batches): the shared expert's two GEMMs
   // run on the second stream, forked at the start, on 3/4 of the CUs, while
   // the routing kernels run on the rest; the combine waits for them.
-  const bool beside = shared && v == GemmVariant::kWStream;
+  const bool beside = shared && v == GemmVariant::kWStream && !one_stream;
+  const bool deq_side = w4_deq && !one_stream;
   SideStream* side = nullptr;
-  if ((beside || w4_deq) && (s = side_stream(&side)) != MOE_OK) return s;
+  if ((beside || deq_side) && (s = side_stream(&side)) != MOE_OK) return s;
 
   auto mark = [&](int ev) -> moe_status {
     if (probes && probes->events[ev])
@@ -587,7 +591,15 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   // W4A16 beyond weight streaming: the experts are dequantised on the
   // second stream, gate_up's while the routing kernels run, down's while the
   // gate_up GEMM runs; each GEMM waits for its own weights
-  if (w4_deq) {
+  if (w4_deq && !deq_side &&
+      ((s = device_status(launch_w4_dequant(w->w_gate_up_q, w->w_gate_up_scale, L.deq_gu, p->E,
+                                            (int64_t)2 * p->I, p->H, stream),
+                          "dequantise gate_up")) != MOE_OK ||
+       (s = device_status(launch_w4_dequant(w->w_down_q, w->w_down_scale, L.deq_dn, p->E, p->H,
+                                            p->I, stream),
+                          "dequantise down")) != MOE_OK))
+    return s;
+  if (deq_side) {
     if ((s = device_status(hipEventRecord(side->fork, stream), "fork")) != MOE_OK ||
         (s = device_status(hipStreamWaitEvent(side->stream, side->fork, 0), "fork")) != MOE_OK ||
         (s = device_status(launch_w4_dequant(w->w_gate_up_q, w->w_gate_up_scale, L.deq_gu, p->E,
@@ -622,7 +634,7 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     return s;
   // (the gate_up weights' dequantisation ends inside the permute step, so
   // the gate_up step times the GEMM alone)
-  if (w4_deq &&
+  if (deq_side &&
       (s = device_status(hipStreamWaitEvent(stream, side->join, 0), "join")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_PERMUTE)) != MOE_OK) return s;
@@ -632,7 +644,7 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                          "gate_up")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_GATE_UP)) != MOE_OK) return s;
-  if (w4_deq &&
+  if (deq_side &&
       (s = device_status(hipStreamWaitEvent(stream, side->join2, 0), "join")) != MOE_OK)
     return s;
   if ((s = device_status(launch_grouped_gemm(v, false, dn, one_launch ? &sdn : nullptr,
@@ -747,6 +759,27 @@ moe_status moe_forward_finish(const moe_params* p, const moe_bf16* x_routed,
                               void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!fin) return fail(MOE_ERR_INVALID_ARG, "fin is NULL");
   return forward_impl(p, x_routed, x_shared, w, fin, out, probes, ws, ws_bytes, stream);
+}
+
+static_assert(MOE_NOALLOC_SCRATCH_BYTES == MOE_NOALLOC_SCRATCH_BYTES_DEV, "scratch size");
+
+moe_status moe_forward_noalloc(const moe_params* p, const moe_bf16* x_routed,
+                               const moe_bf16* x_shared, const moe_weights* w, moe_bf16* out,
+                               const moe_probes* probes, hipStream_t stream) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  const size_t need = carve(*p, nullptr).bytes;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the fixed scratch holds %zu "
+                "(moe_forward takes a workspace of any size)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  size_t bytes = 0;
+  if ((s = device_status(noalloc_scratch(&scratch, &bytes), "fixed scratch address")) != MOE_OK)
+    return s;
+  return forward_impl(p, x_routed, x_shared, w, nullptr, out, probes, scratch, bytes, stream,
+                      /*one_stream=*/true);
 }
 
 }  // extern "C"

@@ -7,6 +7,8 @@
 
 #define MOE_MAX_EXPERTS_DEV 1024
 #define MOE_MAX_TOP_K_DEV 16
+// bytes of the fixed device scratch of moe_forward_noalloc (noalloc.hip)
+#define MOE_NOALLOC_SCRATCH_BYTES_DEV ((size_t)64 << 20)
 
 // One grouped GEMM problem: rows of A (optionally gathered through
 // row_index) grouped by device offsets, each group against its own weight.
@@ -84,3 +86,7 @@ hipError_t launch_combine(const float* y_perm, const float* w, const int32_t* in
                           const float* y_shared, const float* gamma_post, const uint16_t* residual,
                           float c0, float c1, uint16_t* out, int64_t T, int H, int k,
                           int post_norm, float eps, hipStream_t stream);
+
+// Device address and size of the current device's copy of the fixed scratch
+// (looked up once per device, then cached; noalloc.hip).
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);

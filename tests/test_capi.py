@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 14, names
-    lib = ctypes.CDLL(moe.LIB_PATH)
+    assert len(names) == 15, names
+    lib = moe.lib()
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(moe.EXPORTED)
