@@ -343,11 +343,13 @@ def main() -> int:
     x = dev_bf16(inp["x"])
     x_cur = dev_bf16(inp["x_cur"]) if wl.scmoe else None
     w4 = {}
-    if wl.w4:  # W4A16 routed experts: packed codes and bf16 scales
+    if wl.w4:  # W4A16 routed experts: packed codes, E4M3 scales, fp32 tensor scales
         w4 = dict(w_gate_up_q=torch.from_numpy(inp["w_gate_up_q"]).to("cuda"),
-                  w_gate_up_scale=dev_bf16(inp["w_gate_up_scale"]),
+                  w_gate_up_scale=torch.from_numpy(inp["w_gate_up_scale"]).to("cuda"),
                   w_down_q=torch.from_numpy(inp["w_down_q"]).to("cuda"),
-                  w_down_scale=dev_bf16(inp["w_down_scale"]))
+                  w_down_scale=torch.from_numpy(inp["w_down_scale"]).to("cuda"),
+                  w_gate_up_tscale=dev_f32(inp["w_gate_up_tscale"]),
+                  w_down_tscale=dev_f32(inp["w_down_tscale"]))
     dev = dict(w_router=dev_f32(inp["w_router"]), corr_bias=dev_f32(inp["corr_bias"]),
                w_gate_up=None if wl.w4 else dev_bf16(inp["w_gate_up"]),
                w_down=None if wl.w4 else dev_bf16(inp["w_down"]),
@@ -402,9 +404,10 @@ def main() -> int:
     # algorithmic work of the dominant launch and of the whole layer
     hbm_bound = wl.T * k <= 64 * E   # about a row tile per expert or less: weight streaming
     # bytes of one routed expert's weights of R rows x K: bf16, or W4A16
-    # codes (half a byte each) and one bf16 scale per row and 128 columns
+    # codes (half a byte each), one E4M3 scale byte per row and 128 columns
+    # and the fp32 tensor scale
     def wbytes(R, K):
-        return R * K // 2 + R * (K // 128) * 2 if wl.w4 else R * K * 2
+        return R * K // 2 + R * (K // 128) + 4 if wl.w4 else R * K * 2
     gu_bytes = touched * wbytes(2 * I, H) + T * H * 2 + T * k * I * 2
     gu_flops = 2 * T * k * H * 2 * I + 2 * T * H * 2 * Is
     layer_bytes = (touched * (wbytes(2 * I, H) + wbytes(H, I)) + 3 * Is * H * 2 + E * H * 4 + E * 4

@@ -123,26 +123,30 @@ typedef struct moe_weights {
   const float* gamma_post;     /* [H] fp32 ScMoE post-norm gain; NULL = ones      */
   /* W4A16 routed experts (the W4A16 expert GEMM named by "Module
    * glm5next_mlp", Modules forward_prefill_gemm and Constants
-   * MOE_GROUPED_MODULE / W4A16_GEMV_MODULE; the format is this library's):
-   * with moe_params.w4 = 1, the routed experts use these four arrays and
-   * w_gate_up / w_down are ignored.  A weight is (u - 8) * scale, u a 4-bit
-   * code, packed along K in 4-byte words of 8 columns (byte j of a word:
-   * column j in the low nibble, column j + 4 in the high nibble), one
-   * bf16 scale per row and group of 128 columns, scales stored
-   * group-major.  H and I must be multiples of 128; the shared expert stays
-   * bf16.  Decode-sized batches (T*k <= 64*E) stream the codes and unpack
-   * them in registers (exact products: the results equal the dequantised
-   * layer up to fp32 summation order).  Larger batches, bound by the matrix
-   * cores, first dequantise the layer's experts into the workspace as bf16,
-   * the MFMA operand type, and run the bf16 grouped GEMMs; their workspace
-   * then holds E * 3 * I * H bf16 more.  That dequantisation is exact when
-   * every scale carries at most 4 significant bits (the precision of E4M3
-   * scale factors); finer scales get each weight rounded once to bf16 on
-   * this path. */
+   * MOE_GROUPED_MODULE / W4A16_GEMV_MODULE, with the two scale levels of the
+   * NVFP4 routed experts its module doc names; the layout is this
+   * library's): with moe_params.w4 = 1, the routed experts use these arrays
+   * and w_gate_up / w_down are ignored.  A weight is
+   *   (u - 8) * e4m3(scale) * tensor_scale,
+   * u a 4-bit code, packed along K in 4-byte words of 8 columns (byte j of
+   * a word: column j in the low nibble, column j + 4 in the high nibble);
+   * scale one OCP FP8 E4M3 byte per row and group of 128 columns, stored
+   * group-major; tensor_scale one fp32 value per expert and projection.
+   * H and I must be multiples of 128; the shared expert stays bf16.  Every
+   * code and scale byte is accepted (an E4M3 NaN scale, 0x7F or 0xFF, makes
+   * its weights NaN).  (u - 8) * e4m3(scale) is exact in bf16, and the
+   * tensor scale multiplies the fp32 GEMM sums, so on every path the
+   * results equal the exactly dequantised layer up to fp32 summation order.
+   * Decode-sized batches (T*k <= 64*E) stream the codes and unpack them in
+   * registers; larger batches, bound by the matrix cores, first expand the
+   * layer's experts into the workspace as bf16 (exactly; the workspace then
+   * holds E * 3 * I * H bf16 more) and run the bf16 grouped GEMMs. */
   const uint8_t* w_gate_up_q;       /* [E, 2I, H/2] codes; NULL = bf16 experts    */
-  const moe_bf16* w_gate_up_scale;  /* [E, H/128, 2I] bf16                        */
+  const uint8_t* w_gate_up_scale;   /* [E, H/128, 2I] E4M3                        */
   const uint8_t* w_down_q;          /* [E, H, I/2] codes                          */
-  const moe_bf16* w_down_scale;     /* [E, I/128, H] bf16                         */
+  const uint8_t* w_down_scale;      /* [E, I/128, H] E4M3                         */
+  const float* w_gate_up_tscale;    /* [E] fp32 tensor scales; NULL = ones        */
+  const float* w_down_tscale;       /* [E] fp32 tensor scales; NULL = ones        */
 } moe_weights;
 
 /* Finish of the layer, fused into its combine (moe_forward_finish,
@@ -377,18 +381,22 @@ moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
 
 /* W4A16 weights -> bf16, for callers whose weights stay fixed across calls:
  * expand them once, then run the bf16 forward (moe_forward with w4 = 0)
- * instead of dequantising on every prefill-sized call.  q: [n_groups, rows,
- * K/2] codes, scale: [n_groups, K/128, rows] bf16, both in the W4A16 layout
- * of moe_weights; out: [n_groups, rows, K] bf16, out[g][r][c] =
- * bf16((u - 8) * scale) rounded to nearest, ties to even -- exact when the
- * scale carries at most 4 significant bits (a zero weight is +0).  K must be a multiple of 128 and
- * n_groups * rows < 2^31; q, scale and out 16-byte aligned (the caller owns
- * all three; out must not overlap the inputs).  n_groups, rows or K == 0 is
- * a successful no-op.  Source: the grouped W4A16 expert GEMM of "Module
- * glm5next_mlp" (its weights are dequantised to the 16-bit MMA operand type;
- * the layout is this library's). */
-moe_status moe_w4_dequantize(const uint8_t* q, const moe_bf16* scale, int32_t n_groups,
-                             int64_t rows, int32_t K, moe_bf16* out, hipStream_t stream);
+ * instead of expanding on every prefill-sized call.  q: [n_groups, rows,
+ * K/2] codes, scale: [n_groups, K/128, rows] E4M3 bytes, both in the W4A16
+ * layout of moe_weights; tscale: [n_groups] fp32 tensor scales or NULL
+ * (= 1); out: [n_groups, rows, K] bf16,
+ *   out[g][r][c] = bf16((u - 8) * e4m3(scale) * tscale[g]),
+ * rounded to nearest, ties to even -- exact when tscale is NULL or a power
+ * of two ((u - 8) * e4m3(scale) is always a bf16 value); a zero weight is
+ * +0.  K must be a multiple of 128 and n_groups * rows < 2^31; q, scale and
+ * out 16-byte aligned, tscale 4-byte aligned (the caller owns all of them;
+ * out must not overlap the inputs).  n_groups, rows or K == 0 is a
+ * successful no-op.  Source: the grouped W4A16 expert GEMM of "Module
+ * glm5next_mlp" (its weights are dequantised to the 16-bit MMA operand
+ * type; the layout is this library's). */
+moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float* tscale,
+                             int32_t n_groups, int64_t rows, int32_t K, moe_bf16* out,
+                             hipStream_t stream);
 
 /* Static text naming a status code. */
 const char* moe_status_string(moe_status s);

@@ -55,7 +55,7 @@ class moe_weights(Structure):
     _fields_ = [(n, c_void_p) for n in (
         "w_router", "corr_bias", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
         "gamma_pre", "gamma_post", "w_gate_up_q", "w_gate_up_scale", "w_down_q",
-        "w_down_scale")]
+        "w_down_scale", "w_gate_up_tscale", "w_down_tscale")]
 
 
 class moe_finish(Structure):
@@ -106,8 +106,8 @@ def _load() -> ctypes.CDLL:
         "moe_router_backward_workspace_size": (st, [P, POINTER(c_size_t)]),
         "moe_router_backward": (st, [P, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
-        "moe_w4_dequantize": (st, [c_void_p, c_void_p, c_int32, c_int64, c_int32, c_void_p,
-                                   c_void_p]),
+        "moe_w4_dequantize": (st, [c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32,
+                                   c_void_p, c_void_p]),
         "moe_status_string": (c_char_p, [c_int]),
         "moe_last_error": (c_char_p, []),
     }
@@ -231,12 +231,15 @@ def moe_combine_finish(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, fi
 
 def make_weights(w_router, corr_bias, w_gate_up, w_down, ws_gate_up=None, ws_down=None,
                  gamma_pre=None, gamma_post=None, w_gate_up_q=None, w_gate_up_scale=None,
-                 w_down_q=None, w_down_scale=None) -> moe_weights:
-    """Weights of one layer; the four *_q / *_scale arrays (W4A16 routed
-    experts) replace w_gate_up / w_down when given."""
+                 w_down_q=None, w_down_scale=None, w_gate_up_tscale=None,
+                 w_down_tscale=None) -> moe_weights:
+    """Weights of one layer; the W4A16 arrays (*_q codes, *_scale E4M3
+    bytes, *_tscale fp32 tensor scales) replace w_gate_up / w_down when
+    given."""
     return moe_weights(*[_ptr(t) for t in (w_router, corr_bias, w_gate_up, w_down, ws_gate_up,
                                            ws_down, gamma_pre, gamma_post, w_gate_up_q,
-                                           w_gate_up_scale, w_down_q, w_down_scale)])
+                                           w_gate_up_scale, w_down_q, w_down_scale,
+                                           w_gate_up_tscale, w_down_tscale)])
 
 
 def make_probes(topk_ids=None, topk_w=None, expert_offsets=None, sorted_token=None,
@@ -274,11 +277,12 @@ def moe_forward_noalloc(params, x_routed, x_shared, weights: moe_weights, out, p
                                      ctypes.byref(weights), _ptr(out), pr, _stream(stream)))
 
 
-def moe_w4_dequantize(q, scale, out, n_groups, rows, K, stream=None):
-    """W4A16 codes [n_groups, rows, K/2] and scales [n_groups, K/128, rows]
-    -> bf16 bits [n_groups, rows, K] in `out`."""
-    _check(lib().moe_w4_dequantize(_ptr(q), _ptr(scale), int(n_groups), int(rows), int(K),
-                                  _ptr(out), _stream(stream)))
+def moe_w4_dequantize(q, scale, out, n_groups, rows, K, stream=None, tscale=None):
+    """W4A16 codes [n_groups, rows, K/2], E4M3 scales [n_groups, K/128, rows]
+    and optional fp32 tensor scales [n_groups] -> bf16 bits [n_groups, rows,
+    K] in `out`."""
+    _check(lib().moe_w4_dequantize(_ptr(q), _ptr(scale), _ptr(tscale), int(n_groups), int(rows),
+                                   int(K), _ptr(out), _stream(stream)))
 
 
 def moe_router_backward_workspace_size(params: moe_params) -> int:

@@ -253,6 +253,7 @@ GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int3
   P.w_stride = w_stride;
   P.S = nullptr;
   P.s_stride = 0;
+  P.tscale = nullptr;
   P.out = out;
   P.M = M;
   P.G = G;
@@ -484,6 +485,8 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     REQUIRE_PTR(w->w_gate_up_scale);
     REQUIRE_PTR(w->w_down_q);
     REQUIRE_PTR(w->w_down_scale);
+    OPTIONAL_PTR(w->w_gate_up_tscale);
+    OPTIONAL_PTR(w->w_down_tscale);
   } else {
     REQUIRE_PTR(w->w_gate_up);
     REQUIRE_PTR(w->w_down);
@@ -537,6 +540,10 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                                 (int64_t)2 * p->I * p->H, L.h, N, p->E, p->I, p->H, v, true);
   GemmProblem dn = make_problem(L.h, nullptr, L.offsets, L.mstart, w->w_down,
                                 (int64_t)p->H * p->I, L.y, N, p->E, p->H, p->I, v, false);
+  if (w4) {  // the tensor scales multiply the fp32 sums in the epilogues
+    gu.tscale = w->w_gate_up_tscale;
+    dn.tscale = w->w_down_tscale;
+  }
   if (w4_deq) {  // bf16 copies [E, 2I, H] and [E, H, I] in the workspace
     gu.W = L.deq_gu;
     dn.W = L.deq_dn;
@@ -592,21 +599,21 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   // second stream, gate_up's while the routing kernels run, down's while the
   // gate_up GEMM runs; each GEMM waits for its own weights
   if (w4_deq && !deq_side &&
-      ((s = device_status(launch_w4_dequant(w->w_gate_up_q, w->w_gate_up_scale, L.deq_gu, p->E,
+      ((s = device_status(launch_w4_dequant(w->w_gate_up_q, w->w_gate_up_scale, nullptr, L.deq_gu, p->E,
                                             (int64_t)2 * p->I, p->H, stream),
                           "dequantise gate_up")) != MOE_OK ||
-       (s = device_status(launch_w4_dequant(w->w_down_q, w->w_down_scale, L.deq_dn, p->E, p->H,
+       (s = device_status(launch_w4_dequant(w->w_down_q, w->w_down_scale, nullptr, L.deq_dn, p->E, p->H,
                                             p->I, stream),
                           "dequantise down")) != MOE_OK))
     return s;
   if (deq_side) {
     if ((s = device_status(hipEventRecord(side->fork, stream), "fork")) != MOE_OK ||
         (s = device_status(hipStreamWaitEvent(side->stream, side->fork, 0), "fork")) != MOE_OK ||
-        (s = device_status(launch_w4_dequant(w->w_gate_up_q, w->w_gate_up_scale, L.deq_gu, p->E,
+        (s = device_status(launch_w4_dequant(w->w_gate_up_q, w->w_gate_up_scale, nullptr, L.deq_gu, p->E,
                                              (int64_t)2 * p->I, p->H, side->stream),
                            "dequantise gate_up")) != MOE_OK ||
         (s = device_status(hipEventRecord(side->join, side->stream), "join")) != MOE_OK ||
-        (s = device_status(launch_w4_dequant(w->w_down_q, w->w_down_scale, L.deq_dn, p->E, p->H,
+        (s = device_status(launch_w4_dequant(w->w_down_q, w->w_down_scale, nullptr, L.deq_dn, p->E, p->H,
                                              p->I, side->stream),
                            "dequantise down")) != MOE_OK ||
         (s = device_status(hipEventRecord(side->join2, side->stream), "join")) != MOE_OK)
@@ -727,8 +734,9 @@ moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
   return ok();
 }
 
-moe_status moe_w4_dequantize(const uint8_t* q, const moe_bf16* scale, int32_t n_groups,
-                             int64_t rows, int32_t K, moe_bf16* out, hipStream_t stream) {
+moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float* tscale,
+                             int32_t n_groups, int64_t rows, int32_t K, moe_bf16* out,
+                             hipStream_t stream) {
   if (n_groups < 0 || rows < 0 || K < 0)
     return fail(MOE_ERR_INVALID_ARG, "negative size (n_groups %d, rows %lld, K %d)", n_groups,
                 (long long)rows, K);
@@ -740,8 +748,10 @@ moe_status moe_w4_dequantize(const uint8_t* q, const moe_bf16* scale, int32_t n_
   REQUIRE_PTR(q);
   REQUIRE_PTR(scale);
   REQUIRE_PTR(out);
+  if (reinterpret_cast<uintptr_t>(tscale) & 3u)
+    return fail(MOE_ERR_UNSUPPORTED, "tscale is not 4-byte aligned");
   moe_status s;
-  if ((s = device_status(launch_w4_dequant(q, scale, out, n_groups, rows, K, stream),
+  if ((s = device_status(launch_w4_dequant(q, scale, tscale, out, n_groups, rows, K, stream),
                          "dequantise")) != MOE_OK)
     return s;
   return ok();

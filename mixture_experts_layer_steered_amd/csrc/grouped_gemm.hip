@@ -187,7 +187,9 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tile, float 
   }
 
   // epilogue: 32x32 accumulator, lane holds column (lane & 31) and rows
-  // 8*(r/4) + 4*(lane/32) + r%4
+  // 8*(r/4) + 4*(lane/32) + r%4; the group's output scale (1 without one)
+  // multiplies the fp32 sums first
+  const float ts = P.tscale ? P.tscale[g] : 1.0f;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -199,10 +201,11 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tile, float 
         const int64_t row = row0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= row_end) continue;
         if (GATEUP) {
-          const float hv = swiglu_clamped(acc[0][i][j][r], acc[NMAT - 1][i][j][r], limit);
+          const float hv =
+              swiglu_clamped(acc[0][i][j][r] * ts, acc[NMAT - 1][i][j][r] * ts, limit);
           static_cast<uint16_t*>(P.out)[row * N + col] = (uint16_t)f32_to_bf16_bits(hv);
         } else {
-          static_cast<float*>(P.out)[row * N + col] = acc[0][i][j][r];
+          static_cast<float*>(P.out)[row * N + col] = acc[0][i][j][r] * ts;
         }
       }
     }
@@ -343,6 +346,7 @@ template <class S>
 struct PipeTile {
   int64_t row0, row_end;
   int n0;
+  float ts;  // the group's output scale (1 without one)
   __amdgpu_buffer_rsrc_t rs_a, rs_w;
   uint32_t off[S::PER_WAVE];
 };
@@ -380,6 +384,7 @@ __device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, 
   T.row0 = (P.group_offsets ? (int64_t)P.group_offsets[g] : 0) + (int64_t)ml * S::BM;
   T.row_end = P.group_offsets ? (int64_t)P.group_offsets[g + 1] : P.M;
   T.n0 = nt * S::BN;
+  T.ts = P.tscale ? P.tscale[g] : 1.0f;
   T.rs_a = pl_rsrc(P.A);
   T.rs_w = pl_rsrc(P.W + (int64_t)g * P.w_stride);
   const int K = P.K, N = P.N;
@@ -489,10 +494,11 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
           if (col >= N) continue;
           const f32x16_t& g = acc[0][i][j];
           const f32x16_t& u = acc[S::NMAT - 1][i][j];
-          float2_t h01 = {swiglu_clamped_fast(g[4 * q], u[4 * q], limit),
-                          swiglu_clamped_fast(g[4 * q + 1], u[4 * q + 1], limit)};
-          float2_t h23 = {swiglu_clamped_fast(g[4 * q + 2], u[4 * q + 2], limit),
-                          swiglu_clamped_fast(g[4 * q + 3], u[4 * q + 3], limit)};
+          const float ts = T.ts;
+          float2_t h01 = {swiglu_clamped_fast(g[4 * q] * ts, u[4 * q] * ts, limit),
+                          swiglu_clamped_fast(g[4 * q + 1] * ts, u[4 * q + 1] * ts, limit)};
+          float2_t h23 = {swiglu_clamped_fast(g[4 * q + 2] * ts, u[4 * q + 2] * ts, limit),
+                          swiglu_clamped_fast(g[4 * q + 3] * ts, u[4 * q + 3] * ts, limit)};
           uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
                         __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
           *reinterpret_cast<uint2_t*>(static_cast<uint16_t*>(P.out) + row * N + col) = pk;
@@ -511,8 +517,8 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
       for (int j = 0; j < S::TN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4_t v = {acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1], acc[0][i][j][4 * g + 2],
-                       acc[0][i][j][4 * g + 3]};
+          f32x4_t v = {acc[0][i][j][4 * g] * T.ts, acc[0][i][j][4 * g + 1] * T.ts,
+                       acc[0][i][j][4 * g + 2] * T.ts, acc[0][i][j][4 * g + 3] * T.ts};
           quad_transpose(v);
           const int64_t row = T.row0 + wm * S::WM + i * 32 + 8 * g + 4 * (lane >> 5) + (lane & 3);
           const int col = T.n0 + wn * S::WN + j * 32 + 4 * quad;
@@ -893,6 +899,7 @@ struct WsProb {
   const int32_t* mstart;
   const uint16_t* W;
   int64_t w_stride;
+  const float* tscale;
   void* out;
   int64_t M;
   int G, N, K, ntiles, mt_total;
@@ -907,6 +914,7 @@ __device__ __forceinline__ WsProb ws_pick(const GemmProblem& a, const GemmProble
   q.mstart = second ? b.mtile_start : a.mtile_start;
   q.W = second ? b.W : a.W;
   q.w_stride = second ? b.w_stride : a.w_stride;
+  q.tscale = second ? b.tscale : a.tscale;
   q.out = second ? b.out : a.out;
   q.M = second ? b.M : a.M;
   q.G = second ? b.G : a.G;
@@ -1082,6 +1090,7 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
   int64_t row0_cp = 0, row_end_cp = 0;
   int n0_cp = 0;
   void* out_cp = nullptr;
+  float ts_cp = 1.0f;  // the tile's group output scale
   int g_cp = -1;
   bool sec_cp = false;
   auto setup_cp = [&]() __attribute__((always_inline)) {
@@ -1094,6 +1103,7 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
     K_cp = P.K;
     N_cp = P.N;
     out_cp = P.out;
+    ts_cp = P.tscale ? P.tscale[g_cp] : 1.0f;
   };
 
   // element (reg r, lane l) of the wave's accumulator: row 4(l/16) + r of
@@ -1104,15 +1114,16 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t row = row0_cp + 4 * (lane >> 4) + r;
+      const float v = acc[r] * ts_cp;
       if (GATEUP) {
-        const float u = __shfl_xor(acc[r], 8, 64);  // lanes j, j+8: g and u of one column
+        const float u = __shfl_xor(v, 8, 64);  // lanes j, j+8: g and u of one column
         const int col = n0_cp + 8 * wave + (fr & 7);
         if (fr < 8 && row < row_end_cp && col < N_cp)
           static_cast<uint16_t*>(out_cp)[row * N_cp + col] =
-              (uint16_t)f32_to_bf16_bits(swiglu_clamped(acc[r], u, limit));
+              (uint16_t)f32_to_bf16_bits(swiglu_clamped(v, u, limit));
       } else {
         const int col = n0_cp + 16 * wave + fr;
-        if (row < row_end_cp && col < N_cp) static_cast<float*>(out_cp)[row * N_cp + col] = acc[r];
+        if (row < row_end_cp && col < N_cp) static_cast<float*>(out_cp)[row * N_cp + col] = v;
       }
     }
   };
@@ -1165,8 +1176,9 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
 // Weight streaming with W4A16 weights (decode; the grouped W4A16 expert GEMM
 // of "Module glm5next_mlp", in this library's format: 4-bit codes u of value
 // u - 8, packed along K in 4-byte words of 8 columns whose byte j holds
-// columns j and j + 4 in its low and high nibble, and one bf16 scale per
-// weight row and 128 columns, stored group-major).
+// columns j and j + 4 in its low and high nibble, one E4M3 scale byte per
+// weight row and 128 columns, stored group-major, and one fp32 tensor scale
+// per expert, applied to the accumulators before the store).
 //
 // At a quarter of the bf16 size per weight, a 64-row weight tile would take
 // no more LDS per stage than the 16 gathered A rows and halve the weight bytes
@@ -1202,7 +1214,7 @@ struct W4Shape {
   static constexpr int A_BYTES = WS_BM * KB * 2;   // 16 rows of bf16
   static constexpr int W_ROW = KB / 2;             // code bytes per weight row and stage
   static constexpr int W_BYTES = NB * W_ROW;
-  static constexpr int S_WAVE = NBLK * KB / 4;     // scale bytes per wavefront and stage
+  static constexpr int S_WAVE = NBLK * KB / 8;     // scale bytes per wavefront and stage
   static constexpr int STAGE = A_BYTES + W_BYTES + NW * S_WAVE;
   static constexpr int A_CH = KB / 8;              // 16-byte chunks per A row
   static constexpr int A_RPI = 64 / A_CH;          // A rows per 1 KB instruction
@@ -1213,6 +1225,9 @@ struct W4Shape {
   static constexpr int S_LANES = S_WAVE / 16;      // lanes that fetch the scales
   static constexpr int PER_WAVE = A_PW + W_PW + 1;
   static constexpr int GROUPS = KB / 128;          // scale groups per stage
+  // a 16-byte piece of scale bytes covers 16 rows: one block (down) or the
+  // gate or up halves of two blocks (gate_up)
+  static_assert(NBLK % 2 == 0, "whole 16-byte scale pieces");
   static_assert(KB % 128 == 0 && KB <= 512 && A_PW >= 1 && A_PW * NW * A_RPI == WS_BM &&
                 W_PW >= 1 && W_PW * NW * W_RPI == NB && S_LANES >= 1 && S_LANES <= 64,
                 "W4 shape");
@@ -1271,7 +1286,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
   int t_ld = t_begin + lid, kt_ld = 0, slot_ld = 0, g_ld = -1, rows_ld = 0;
   const uint16_t* ld_A = P.A;
   const uint8_t* ld_W = nullptr;
-  const uint16_t* ld_S = nullptr;
+  const uint8_t* ld_S = nullptr;
   uint32_t offA[S::A_PW], offW[S::W_PW], offS = 0;
   auto setup_ld = [&]() __attribute__((always_inline)) {
     int64_t row0, row_end;
@@ -1312,19 +1327,20 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
       const int c = w4_swz<S::W_CH>(r, lane % S::W_CH);
       offW[i] = (uint32_t)((int64_t)(up ? N + n : n) * (K / 2) + c * 16);
     }
-    // scales of the wave's rows, per group of the stage: in gate_up 8 NBLK
-    // gate columns then the same up columns, in down 16 NBLK rows, in
-    // 16-byte pieces; lane l < S_LANES fetches piece l % (2 NBLK) of stage
-    // group l / (2 NBLK); offS is the piece's offset within a group
+    // E4M3 scale bytes of the wave's rows, per group of the stage: in
+    // gate_up 8 NBLK gate rows then the same up rows, in down 16 NBLK rows,
+    // in 16-byte pieces (NBLK per group); lane l < S_LANES fetches piece
+    // l % NBLK of stage group l / NBLK; offS is the piece's byte offset
+    // within a group
     if (lane < S::S_LANES) {
-      const int pi = lane % (2 * NBLK);
+      const int pi = lane % NBLK;
       int n;
       bool up = false;
       if (GATEUP) {
-        up = pi >= NBLK;
-        n = n0 + 8 * NBLK * wave + 8 * (up ? pi - NBLK : pi);
+        up = pi >= NBLK / 2;
+        n = n0 + 8 * NBLK * wave + 16 * (up ? pi - NBLK / 2 : pi);
       } else {
-        n = n0 + 16 * NBLK * wave + 8 * pi;
+        n = n0 + 16 * NBLK * wave + 16 * pi;
       }
       if (n >= N) n = n0;
       offS = (uint32_t)(up ? N + n : n);
@@ -1356,7 +1372,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
     }
     if (lane < S::S_LANES) {
       // K group of the piece; groups past K fetch the stage's last one again
-      const int gk = k0 / 128 + min(lane / (2 * NBLK), gv - 1);
+      const int gk = k0 / 128 + min(lane / NBLK, gv - 1);
       lds_direct_16_stream(ld_S + (offS + (uint32_t)gk * (uint32_t)rs),
                            reinterpret_cast<uint16_t*>(base + S::A_BYTES + S::W_BYTES +
                                                        wave * S::S_WAVE));
@@ -1372,8 +1388,10 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
   // ---- compute cursor
   int t_cp = t_begin + lid, kt_cp = 0, slot_cp = 0, g_cp = -1, n0_cp = 0;
   int64_t row0_cp = 0, row_end_cp = 0;
+  float ts_cp = 1.0f;  // the expert's tensor scale
   auto setup_cp = [&]() __attribute__((always_inline)) {
     ws_locate<BN>(P, t_cp, row0_cp, row_end_cp, n0_cp, g_cp);
+    ts_cp = P.tscale ? P.tscale[g_cp] : 1.0f;
   };
 
   // element (reg r, lane l) of block j's accumulator: row 4(l/16) + r of the
@@ -1392,15 +1410,16 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = row0_cp + 4 * q + r;
+        const float v = acc[j][r] * ts_cp;
         if (GATEUP) {
-          const float u = __shfl_xor(acc[j][r], 8, 64);  // lanes i, i+8: g and u of one column
+          const float u = __shfl_xor(v, 8, 64);  // lanes i, i+8: g and u of one column
           const int col = n0_cp + 8 * (NBLK * wave + j) + (fr & 7);
           if (fr < 8 && row < row_end_cp && col < N)
             static_cast<uint16_t*>(P.out)[row * N + col] =
-                (uint16_t)f32_to_bf16_bits(swiglu_clamped(acc[j][r], u, limit));
+                (uint16_t)f32_to_bf16_bits(swiglu_clamped(v, u, limit));
         } else {
           const int col = n0_cp + 16 * (NBLK * wave + j) + fr;
-          if (row < row_end_cp && col < N) static_cast<float*>(P.out)[row * N + col] = acc[j][r];
+          if (row < row_end_cp && col < N) static_cast<float*>(P.out)[row * N + col] = v;
         }
       }
     }
@@ -1410,7 +1429,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
   auto group = [&](const uint8_t* base, int s) __attribute__((always_inline)) {
     const uint16_t* As = reinterpret_cast<const uint16_t*>(base);
     const uint8_t* Ws = base + S::A_BYTES;
-    const uint8_t* Ss = base + S::A_BYTES + S::W_BYTES + wave * S::S_WAVE + 32 * NBLK * s;
+    const uint8_t* Ss = base + S::A_BYTES + S::W_BYTES + wave * S::S_WAVE + 16 * NBLK * s;
     u32x4_t codes[NBLK];
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
@@ -1431,8 +1450,8 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
     }
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
-      const int so = GATEUP ? (fr < 8 ? 0 : 16 * NBLK) + 2 * (8 * j + (fr & 7)) : 2 * (16 * j + fr);
-      const float sc = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(Ss + so) << 16);
+      const int so = GATEUP ? (fr < 8 ? 0 : 8 * NBLK) + 8 * j + (fr & 7) : 16 * j + fr;
+      const float sc = e4m3_to_f32(Ss[so]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc, fmaf(-136.0f, accX[r], accP[j][r]), acc[j][r]);
     }

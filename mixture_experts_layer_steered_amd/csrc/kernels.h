@@ -20,8 +20,11 @@ struct GemmProblem {
   const uint16_t* W;              // [G, WR, K] bf16; gate_up: WR = 2N, down: WR = N
                                   // (W4A16: [G, WR, K/2] bytes of 4-bit codes)
   int64_t w_stride;               // uint16 elements between groups of W
-  const uint16_t* S;              // W4A16 only: [G, K/128, WR] bf16 scales; nullptr = bf16 W
-  int64_t s_stride;               // elements between groups of S
+  const uint8_t* S;               // W4A16 only: [G, K/128, WR] E4M3 scales; nullptr = bf16 W
+  int64_t s_stride;               // bytes between groups of S
+  const float* tscale;            // [G] fp32 scale of each group's outputs (the W4A16
+                                  // tensor scales, applied to the fp32 accumulators
+                                  // before the epilogue), or nullptr = 1
   void* out;                      // [M, N]: bf16 h (gate_up) or fp32 y (down)
   int64_t M;                      // total rows
   int32_t G;                      // groups
@@ -76,9 +79,10 @@ hipError_t launch_router_backward(const float* dl, int64_t rs, int64_t cs, const
                                   int H, int E, void* ws, hipStream_t stream);
 
 // W4A16 experts -> bf16 (dequant.hip): G groups of `rows` rows by K
-// columns (K a multiple of 128), codes [G, rows, K/2], scales [G, K/128, rows].
-hipError_t launch_w4_dequant(const uint8_t* q, const uint16_t* scale, uint16_t* out, int G,
-                             int64_t rows, int K, hipStream_t stream);
+// columns (K a multiple of 128), codes [G, rows, K/2], E4M3 scales
+// [G, K/128, rows], tensor scales [G] fp32 or nullptr (= 1).
+hipError_t launch_w4_dequant(const uint8_t* q, const uint8_t* scale, const float* tscale,
+                             uint16_t* out, int G, int64_t rows, int K, hipStream_t stream);
 
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, const float* gamma, uint16_t* out, int64_t T,
                                int H, float eps, hipStream_t stream);

@@ -29,12 +29,16 @@ the fp32 draw).
 
 W4A16 routed experts (workloads with w4): per weight a uniform nibble u in
 [0, 15] (the value is u - 8; 4-byte words of 8 columns, byte j holding
-columns j and j + 4 in its low and high nibble), and
-per row and group of 128 columns a bf16 scale weight_std / sqrt(21.5) *
-U(0.5, 1.5) (21.5 is the mean of (u - 8)^2) rounded to 4 significant bits
-(nearest, ties to even), stored [K/128, rows]; so the weights have about
-the bf16 experts' spread and each is exact in bf16.  The shared expert
-stays bf16.
+columns j and j + 4 in its low and high nibble); per row and group of 128
+columns a one-byte OCP E4M3 scale code, stored [K/128, rows]; per expert and
+projection an fp32 tensor scale.  Scale codes: "typical" draws a positive
+code with exponent field 6, 7 or 8 and any mantissa (values 1/2 .. 3.75,
+RMS about 1.94), and the tensor scale weight_std / (sqrt(21.5) * 1.94) *
+U(0.8, 1.25) (21.5 is the mean of (u - 8)^2), so the weights have about the
+bf16 experts' spread; "full" draws every code except the two NaN patterns
+uniformly (both signs, zeros, subnormals, up to 448), with tensor scale
+weight_std / (sqrt(21.5) * 100) * U(0.8, 1.25).  The shared expert stays
+bf16.
 
 Random streams: numpy PCG64 children of SeedSequence(seed), spawned in a
 fixed order: x (x_prev for ScMoE), x_cur, W_r, b, W_gu[e] for e=0..E-1,
@@ -71,6 +75,7 @@ class Workload:
     weight_std: float = WEIGHT_STD
     gamma_jitter: float = 0.0
     w4: bool = False         # routed experts in W4A16 form
+    w4_scales: str = "typical"  # W4A16 scale codes: "typical" or "full" (every E4M3 code)
 
     def label(self) -> str:
         s = (f"{self.name}_T{self.T}_H{self.H}_E{self.E}_k{self.k}"
@@ -129,18 +134,29 @@ def _normal_bf16(seq: np.random.SeedSequence, shape, std: float) -> np.ndarray:
     return f32_to_bf16_bits(v).reshape(shape)
 
 
-def _w4_matrix(g: np.random.Generator, R: int, K: int, std: float) -> tuple[np.ndarray, np.ndarray]:
-    """One W4A16 matrix [R, K]: packed nibbles uint8 [R, K/2] and bf16
-    scale bits [K/128, R]."""
+# the RMS of the scale values each draw gives, for the tensor scale that
+# puts the weights at about weight_std (a property of the code sets below)
+W4_SCALE_RMS = {"typical": 1.94, "full": 100.0}
+
+
+def _w4_matrix(g: np.random.Generator, R: int, K: int, std: float,
+               scales: str) -> tuple[np.ndarray, np.ndarray, np.float32]:
+    """One W4A16 matrix [R, K]: packed nibbles uint8 [R, K/2], E4M3 scale
+    codes uint8 [K/128, R] and its fp32 tensor scale."""
     q = g.integers(0, 256, size=(R, K // 2), dtype=np.uint8)
     groups = (K + W4_GROUP - 1) // W4_GROUP
-    sc = g.uniform(0.5, 1.5, size=(groups, R)).astype(np.float32)
-    sc *= np.float32(std / W4_CODE_RMS)
-    # 4 significant bits (the precision of E4M3 scale factors): every weight
-    # (u - 8) * scale then has at most 8 significant bits, exact in bf16
-    m, e = np.frexp(sc)
-    sc = np.ldexp(np.rint(m * 16.0) / 16.0, e).astype(np.float32)
-    return q, f32_to_bf16_bits(sc)
+    if scales == "typical":
+        field = g.integers(6, 9, size=(groups, R))
+        mant = g.integers(0, 8, size=(groups, R))
+        sc = ((field << 3) | mant).astype(np.uint8)
+    elif scales == "full":
+        # every byte but the NaN patterns 0x7F and 0xFF
+        sc = g.integers(0, 254, size=(groups, R)).astype(np.uint8)
+        sc = np.where(sc >= 0x7F, sc + 1, sc).astype(np.uint8)
+    else:
+        raise ValueError(f"w4_scales {scales!r}")
+    ts = np.float32(std / (W4_CODE_RMS * W4_SCALE_RMS[scales]) * g.uniform(0.8, 1.25))
+    return q, sc, ts
 
 
 def zipf_row_scales(E: int, s: float, perm: np.ndarray) -> np.ndarray:
@@ -165,8 +181,9 @@ def generate(w: Workload, seed: int = 0, *, T: int | None = None,
       corr_bias    float32 [E]
       w_gate_up    uint16 [E,2I,H]  gate rows [0,I), up rows [I,2I)
       w_down       uint16 [E,H,I]
-        or, with w4: w_gate_up_q uint8 [E,2I,H/2], w_gate_up_scale uint16
-        [E,H/128,2I], w_down_q uint8 [E,H,I/2], w_down_scale uint16 [E,I/128,H]
+        or, with w4: w_gate_up_q uint8 [E,2I,H/2], w_gate_up_scale uint8
+        (E4M3) [E,H/128,2I], w_gate_up_tscale float32 [E], w_down_q uint8
+        [E,H,I/2], w_down_scale uint8 [E,I/128,H], w_down_tscale float32 [E]
       ws_gate_up   uint16 [2I_s,H]  (absent when I_s == 0)
       ws_down      uint16 [H,I_s]
       gamma_pre    float32 [H]   (ScMoE only)
@@ -201,20 +218,22 @@ def generate(w: Workload, seed: int = 0, *, T: int | None = None,
 
     if experts and w.w4:
         gq = np.empty((E, 2 * I, H // 2), dtype=np.uint8)
-        gs = np.empty((E, (H + W4_GROUP - 1) // W4_GROUP, 2 * I), dtype=np.uint16)
+        gs = np.empty((E, (H + W4_GROUP - 1) // W4_GROUP, 2 * I), dtype=np.uint8)
+        gt = np.empty(E, dtype=np.float32)
         dq = np.empty((E, H, I // 2), dtype=np.uint8)
-        ds = np.empty((E, (I + W4_GROUP - 1) // W4_GROUP, H), dtype=np.uint16)
+        ds = np.empty((E, (I + W4_GROUP - 1) // W4_GROUP, H), dtype=np.uint8)
+        dt = np.empty(E, dtype=np.float32)
 
         def one_w4(e):
-            gq[e], gs[e] = _w4_matrix(np.random.Generator(np.random.PCG64(k_gu[e])), 2 * I, H,
-                                      w.weight_std)
-            dq[e], ds[e] = _w4_matrix(np.random.Generator(np.random.PCG64(k_d[e])), H, I,
-                                      w.weight_std)
+            gq[e], gs[e], gt[e] = _w4_matrix(np.random.Generator(np.random.PCG64(k_gu[e])),
+                                             2 * I, H, w.weight_std, w.w4_scales)
+            dq[e], ds[e], dt[e] = _w4_matrix(np.random.Generator(np.random.PCG64(k_d[e])),
+                                             H, I, w.weight_std, w.w4_scales)
 
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(one_w4, range(E)))
-        out["w_gate_up_q"], out["w_gate_up_scale"] = gq, gs
-        out["w_down_q"], out["w_down_scale"] = dq, ds
+        out["w_gate_up_q"], out["w_gate_up_scale"], out["w_gate_up_tscale"] = gq, gs, gt
+        out["w_down_q"], out["w_down_scale"], out["w_down_tscale"] = dq, ds, dt
     elif experts:
         wgu = np.empty((E, 2 * I, H), dtype=np.uint16)
         wd = np.empty((E, H, I), dtype=np.uint16)

@@ -74,14 +74,18 @@ caller passes, widened.
 W4A16 routed experts (optional, the next step after the bf16 path): the
 pages name a grouped W4A16 expert GEMM ("Module glm5next_mlp", Modules
 forward_prefill_gemm and Constants MOE_GROUPED_MODULE / W4A16_GEMV_MODULE)
-but not its format.  The reading taken here: signed 4-bit integers in
-offset-binary nibbles (u - 8), packed along K in 4-byte words of 8
-columns, byte j of a word holding its columns j (low nibble) and j + 4
-(high nibble) -- the interleaved order lets a kernel split a word into its
-low and high nibbles with one mask each; one bf16 scale per output row and
-group of 128 columns, stored group-major ([K/128, rows]); the weight is
-exactly (u - 8) * scale and the expert FFN then runs as above on those
-values.  The shared expert stays bf16.
+and call the routed MoE NVFP4 (module doc), but give no layout.  The
+reading taken here keeps NVFP4's two levels of scaling -- a one-byte
+OCP E4M3 scale per block and one fp32 scale per weight tensor -- over
+4-bit integer codes: signed 4-bit integers in offset-binary nibbles
+(u - 8), packed along K in 4-byte words of 8 columns, byte j of a word
+holding its columns j (low nibble) and j + 4 (high nibble) -- the
+interleaved order lets a kernel split a word into its low and high
+nibbles with one mask each; one E4M3 scale per output row and group of
+128 columns, stored group-major ([K/128, rows]); one fp32 scale per
+expert and projection.  The weight is exactly
+(u - 8) * e4m3(scale) * tensor_scale and the expert FFN then runs as
+above on those values.  The shared expert stays bf16.
 
 Precision: all sums in float64 (BLAS matmul as a step), single roundings
 at the points named above.  bf16 tensors are uint16 bit patterns.
@@ -226,23 +230,44 @@ def permute(ids: np.ndarray, E: int) -> dict:
 W4_GROUP = 128
 
 
-def dequant_w4(q: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 bytes -> float64 (exact).
+
+    Bit 7 is the sign, bits 6..3 the exponent field (bias 7), bits 2..0 the
+    mantissa.  Exponent field 0 holds the subnormals m/8 * 2^-6 (and the
+    two zeros); the others (1 + m/8) * 2^(field - 7); the one pattern per
+    sign with every exponent and mantissa bit set is NaN -- the format has
+    no infinities, so its largest value is 1.75 * 2^8 = 448.
+    """
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    field = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    mag = np.where(field == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(field - 7.0))
+    v = np.where(b & 0x80, -mag, mag)
+    return np.where((field == 15) & ((b & 7) == 7), np.nan, v)
+
+
+def dequant_w4(q: np.ndarray, scale_codes: np.ndarray, tensor_scale: float = 1.0) -> np.ndarray:
     """W4A16 weights -> float64 values (exact).
 
-    q      uint8 [R, K/2]: per 4-byte word w (columns 8w .. 8w+7), byte
-           4w + j holds column 8w + j (low nibble) and column 8w + j + 4
-           (high nibble); a nibble u stands for the integer u - 8
-    scale  bf16 [ceil(K/128), R]: one scale per row and group of 128 columns
-    Returns w [R, K] with w[r, c] = (u[r, c] - 8) * scale[c // 128, r].
+    q             uint8 [R, K/2]: per 4-byte word w (columns 8w .. 8w+7), byte
+                  4w + j holds column 8w + j (low nibble) and column 8w + j + 4
+                  (high nibble); a nibble u stands for the integer u - 8
+    scale_codes   uint8 [ceil(K/128), R]: one E4M3 scale per row and group of
+                  128 columns
+    tensor_scale  the fp32 scale of the whole matrix
+    Returns w [R, K] with w[r, c] = (u[r, c] - 8) * e4m3(scale[c // 128, r])
+    * tensor_scale.
     """
     q = np.asarray(q, dtype=np.uint8)
     R, half = q.shape
     K = 2 * half
     words = q.reshape(R, K // 8, 4).astype(np.int64)
     u = np.concatenate([words & 0x0F, words >> 4], axis=2).reshape(R, K)
-    s = bf16_to_f64(np.asarray(scale_bits, dtype=np.uint16))   # [groups, R]
+    s = e4m3_to_f64(scale_codes)                                # [groups, R]
     per_col = np.repeat(s.T, W4_GROUP, axis=1)[:, :K]
-    return (u - 8).astype(np.float64) * per_col
+    ts = float(np.float32(tensor_scale))
+    return (u - 8).astype(np.float64) * per_col * ts
 
 
 def _weights_f64(w: np.ndarray) -> np.ndarray:
@@ -254,10 +279,15 @@ def _weights_f64(w: np.ndarray) -> np.ndarray:
 def expert_weights(inp: dict, e: int) -> tuple[np.ndarray, np.ndarray]:
     """Routed expert e's (gate_up [2I, H], down [H, I]) weights: bf16 bits,
     or float64 values dequantised from the W4A16 arrays when `inp` holds
-    w_gate_up_q / w_gate_up_scale / w_down_q / w_down_scale."""
+    w_gate_up_q / w_gate_up_scale / w_down_q / w_down_scale (and the
+    per-expert tensor scales w_gate_up_tscale / w_down_tscale [E] fp32;
+    absent = 1)."""
     if "w_gate_up_q" in inp:
-        return (dequant_w4(inp["w_gate_up_q"][e], inp["w_gate_up_scale"][e]),
-                dequant_w4(inp["w_down_q"][e], inp["w_down_scale"][e]))
+        def ts(name):
+            t = inp.get(name + "_tscale")
+            return 1.0 if t is None else float(t[e])
+        return (dequant_w4(inp["w_gate_up_q"][e], inp["w_gate_up_scale"][e], ts("w_gate_up")),
+                dequant_w4(inp["w_down_q"][e], inp["w_down_scale"][e], ts("w_down")))
     return inp["w_gate_up"][e], inp["w_down"][e]
 
 

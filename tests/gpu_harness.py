@@ -77,11 +77,12 @@ class Device:
         self.w_gate_up = None if w4 else dev_bf16(torch, inp["w_gate_up"])
         self.w_down = None if w4 else dev_bf16(torch, inp["w_down"])
         self.w4 = {}
-        if w4:
-            for n in ("w_gate_up_q", "w_down_q"):
+        if w4:   # codes and E4M3 scale bytes; fp32 tensor scales when given
+            for n in ("w_gate_up_q", "w_down_q", "w_gate_up_scale", "w_down_scale"):
                 self.w4[n] = torch.from_numpy(np.ascontiguousarray(inp[n])).to("cuda")
-            for n in ("w_gate_up_scale", "w_down_scale"):
-                self.w4[n] = dev_bf16(torch, inp[n])
+            for n in ("w_gate_up_tscale", "w_down_tscale"):
+                if inp.get(n) is not None:
+                    self.w4[n] = dev_f32(torch, inp[n])
         self.ws_gate_up = dev_bf16(torch, inp["ws_gate_up"]) if wl.I_s else None
         self.ws_down = dev_bf16(torch, inp["ws_down"]) if wl.I_s else None
         self.gamma_pre = dev_f32(torch, inp["gamma_pre"]) if inp.get("gamma_pre") is not None else None
@@ -185,7 +186,9 @@ def check_router(x_bits, w_router, corr_bias, k, rsf, logits_g, ids_g, w_g) -> d
     w_ref = (np.float32(rsf) * np.take_along_axis(r["s"], ii, 1)).astype(np.float32)
     wb = abs(rsf) * 0.25 * np.take_along_axis(lbound, ii, 1) + SIG_ULP * np.spacing(np.abs(w_ref))
     dw = np.abs(w_g.astype(np.float64) - w_ref)
-    rep["w_max_ulp_vs_oracle"] = float(ulp_distance(w_g, w_ref).max()) if dw.size else 0.0
+    uw = ulp_distance(w_g, w_ref)
+    rep["w_max_ulp_vs_oracle"] = float(uw.max()) if dw.size else 0.0
+    rep["w_beyond_4ulp"] = int(np.sum(uw > 4))   # reported: the bar is the bound below
     assert np.all(dw <= wb), "weights outside the propagated logit bound"
     rep["route"] = r
     return rep

@@ -145,6 +145,11 @@ def test_entry_points_reject_before_launch():
                                                                 **dict(w4, w_down_scale=None)),
                         16, None, 16, stream=0)
     assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:   # misaligned tensor scales
+        moe.moe_forward(P(w4=True), 16, None,
+                        moe.make_weights(16, None, None, None, 16, 16, **w4, w_down_tscale=20),
+                        16, None, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
     with pytest.raises(moe.MoeError) as ei:   # W4A16 arrays but params.w4 = 0: bf16 expected
         moe.moe_forward(P(), 16, None, moe.make_weights(16, None, None, None, 16, 16, **w4),
                         16, None, 16, stream=0)
@@ -228,6 +233,7 @@ def test_w4_dequantize_validation():
         (dict(n_groups=1 << 16, rows=1 << 15), moe.MOE_ERR_UNSUPPORTED),  # 2^31 rows
         (dict(q=None), moe.MOE_ERR_INVALID_ARG),
         (dict(scale=8), moe.MOE_ERR_UNSUPPORTED),                # misaligned
+        (dict(tscale=18), moe.MOE_ERR_UNSUPPORTED),              # tensor scales misaligned
         (dict(out=None), moe.MOE_ERR_INVALID_ARG),
     ]
     for kw, status in cases:

@@ -147,16 +147,19 @@ def test_forward_decode_full():
     assert rep["rows_checked"] == 32
 
 
-def test_forward_prefill_full_sampled():
-    _full("prefill", 96)
+def test_forward_prefill_full():
+    rep = _full("prefill", None)
+    assert rep["rows_checked"] == 8192
 
 
-def test_forward_scmoe_full_sampled():
-    _full("scmoe", 96)
+def test_forward_scmoe_full():
+    rep = _full("scmoe", None)
+    assert rep["rows_checked"] == 8192
 
 
-def test_forward_zipf_full_sampled():
-    rep = _full("zipf", 48)
+def test_forward_zipf_full():
+    rep = _full("zipf", None)
+    assert rep["rows_checked"] == 16384
     # the Zipf-scaled router leaves the expert load strongly skewed
     assert rep["max_over_mean_count"] > 4
 
@@ -218,6 +221,9 @@ W4 = {
     # clamp stress with W4 codes (large scales)
     "w4_clamp": Workload("w4_clamp", T=32, H=256, E=8, k=2, I=128, I_s=128, weight_std=0.3,
                          w4=True),
+    # every E4M3 scale byte but the NaNs (both signs, zeros, subnormals, 448)
+    "w4_full_range": Workload("w4_full_range", T=40, H=512, E=16, k=4, I=384, I_s=256, w4=True,
+                              w4_scales="full"),
 }
 
 
@@ -234,10 +240,20 @@ def test_forward_decode_w4_full():
     assert rep["rows_checked"] == 32
 
 
-def test_forward_prefill_w4_full_sampled():
-    # T * k = 65 536 rows over 64 experts: the dequantising path (bf16 GEMMs
-    # on weights rounded once to bf16) against the oracle's exact weights
-    rep = _full("prefill_w4", 96)
+@pytest.mark.parametrize("scales", ["typical", "full"])
+def test_forward_prefill_w4_full(scales):
+    # T * k = 65 536 rows over 64 experts: the experts expanded exactly to
+    # bf16, the tensor scales on the fp32 sums, against the oracle's exact
+    # weights; the measured scale draw on every token, every E4M3 scale byte
+    # on a token sample
+    wl = moe_inputs.WORKLOADS["prefill_w4"].with_(w4_scales=scales)
+    gh.note(f"generating {wl.label()} scales={scales}")
+    inp = moe_inputs.generate(wl, seed=0)
+    rows = None
+    if scales == "full":
+        rows = np.sort(np.random.default_rng(7).choice(wl.T, size=256, replace=False))
+    rep, _, dev = run_and_check(wl, inp, rows)
+    del dev
     assert rep["experts_touched"] == 64
 
 
@@ -321,13 +337,16 @@ W4_TILED = {
 }
 
 
-def _bf16_rounded_experts(inp):
-    """The same layer with each W4A16 weight rounded to bf16 (what the
-    dequantising path feeds its bf16 GEMMs), as bf16 expert arrays."""
-    ref = {k: v for k, v in inp.items() if not k.endswith("_q") and not k.endswith("_scale")}
+def _bf16_experts(inp):
+    """The same layer with its W4A16 weights stored as bf16 (exactly: the
+    tensor scales are powers of two here), as bf16 expert arrays."""
+    ref = {k: v for k, v in inp.items()
+           if not k.endswith("_q") and not k.endswith("_scale") and not k.endswith("_tscale")}
     for name in ("w_gate_up", "w_down"):
-        q, sc = inp[name + "_q"], inp[name + "_scale"]
-        ref[name] = np.stack([mo.bf16_round(mo.dequant_w4(q[e], sc[e])) for e in range(q.shape[0])])
+        q, sc, ts = inp[name + "_q"], inp[name + "_scale"], inp[name + "_tscale"]
+        vals = [mo.dequant_w4(q[e], sc[e], ts[e]) for e in range(q.shape[0])]
+        assert all(np.array_equal(mo.bf16_to_f64(mo.bf16_round(v)), v) for v in vals)
+        ref[name] = np.stack([mo.bf16_round(v) for v in vals])
     return ref
 
 
@@ -335,11 +354,15 @@ def _bf16_rounded_experts(inp):
 def test_forward_w4_tiled(name):
     """Prefill-sized W4A16 batches: parity with the oracle's exact
     dequantised layer, and bit-for-bit equality with the bf16 path run on
-    the same weights rounded to bf16 on the host."""
+    the same weights (power-of-two tensor scales make them bf16 values, and
+    scaling an fp32 sum by a power of two commutes with its roundings)."""
     wl = W4_TILED[name]
     inp = moe_inputs.generate(wl, seed=5)
+    rng = np.random.default_rng(9)
+    for n in ("w_gate_up_tscale", "w_down_tscale"):
+        inp[n] = np.ldexp(1.0, rng.integers(-10, -7, size=wl.E)).astype(np.float32)
     rep, gpu, _ = run_and_check(wl, inp)
-    ref_inp = _bf16_rounded_experts(inp)
+    ref_inp = _bf16_experts(inp)
     wl_bf16 = wl.with_(w4=False)
     gh.note(f"forward {name} as bf16 on host-rounded weights")
     d = gh.Device(wl_bf16, ref_inp)

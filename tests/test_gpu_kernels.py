@@ -51,6 +51,38 @@ def test_router_topk_parity(tl, T, H, E, k, rsf):
     gh.note(f"  {rep}")
 
 
+@pytest.mark.parametrize("T,H,E", [(64, 4096, 64), (700, 4096, 256), (37, 520, 24)])
+def test_router_logits_one_hot_exact(tl, T, H, E):
+    """With one-hot activations (one entry +-2^j per token) each logit is a
+    single product, and the three bf16 pieces of an fp32 router weight add
+    up to it exactly in fp32 (8 + 8 + 8 significant bits): the GPU must
+    return +-2^j * W_r[e, i_t] bit for bit, whatever the K slicing and
+    summation order.  A piece left out of the split -- the lowest carries
+    bits 17..24 of each weight -- changes these bits, which the forward-error
+    bound of the general test is too wide to see."""
+    torch, moe = tl
+    gh.note(f"router one-hot T={T} H={H} E={E}")
+    rng = np.random.default_rng(T * 7 + E)
+    pos = rng.integers(0, H, T)
+    val = rng.choice([-1.0, 1.0], T) * np.ldexp(1.0, rng.integers(-3, 4, T))
+    xv = np.zeros((T, H), np.float32)
+    xv[np.arange(T), pos] = val
+    x = moe_inputs.f32_to_bf16_bits(xv)
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    k = min(8, E)
+    p = moe.make_params(T, H, E, k, 8, 0, 1.0, 7.0)
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(p, gh.dev_bf16(torch, x), gh.dev_f32(torch, wr), None, ids, w, ws)
+    torch.cuda.synchronize()
+    logits_g = ws[: T * E * 4].view(torch.float32).cpu().numpy().reshape(T, E)
+    want = (val[:, None] * wr[:, pos].T.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), val[:, None] * wr[:, pos].T.astype(np.float64))
+    bad = np.argwhere(logits_g.view(np.uint32) != want.view(np.uint32))
+    assert bad.size == 0, f"{len(bad)} logits differ, first {bad[:4]}"
+
+
 def test_router_ties_nan_and_no_bias(tl):
     """Exact ties (identical router rows) go to the lower id; a NaN logit
     ranks last; NULL bias means zeros."""
@@ -241,34 +273,37 @@ def test_combine_finish_bits(tl, post, in_place, c0, c1):
 
 # ------------------------------------------------- W4A16 dequantisation ----
 
-@pytest.mark.parametrize("G,R,K,scales", [
-    (3, 70, 384, "synthetic"),   # the generator's 4-significant-bit scales: exact in bf16
-    (2, 33, 256, "fine"),        # arbitrary bf16 scales (8 bits): one rounding per weight
-    (1, 1, 128, "fine"),         # one row, one group
+@pytest.mark.parametrize("G,R,K,ts", [
+    (3, 70, 384, None),     # no tensor scale: the exact expansion
+    (2, 33, 256, "pow2"),   # power-of-two tensor scales: exact as well
+    (2, 40, 256, "fp32"),   # arbitrary fp32 tensor scales: one rounding per weight
+    (1, 1, 128, None),      # one row, one group
 ])
-def test_w4_dequantize_bits(tl, G, R, K, scales):
+def test_w4_dequantize_bits(tl, G, R, K, ts):
     """moe_w4_dequantize = bf16 of the oracle's exact dequantisation (round to
-    nearest even) in value -- bit for bit except the sign of zero weights
-    (u = 8 under a negative scale: the oracle's 0 * (-s) is -0, the kernel's
-    (128 + u) s - 136 s is +0); nothing is written past the output."""
+    nearest even) over every E4M3 scale byte but the NaNs, bit for bit
+    except the sign of zero weights (u = 8 under a negative scale: the
+    oracle's 0 * (-s) is -0, the kernel's (128 + u) s - 136 s is +0);
+    nothing is written past the output."""
     torch, moe = tl
-    gh.note(f"w4_dequantize G={G} R={R} K={K} scales={scales}")
+    gh.note(f"w4_dequantize G={G} R={R} K={K} tscale={ts}")
     rng = np.random.default_rng(K + R)
     q = rng.integers(0, 256, size=(G, R, K // 2), dtype=np.uint8)
-    if scales == "synthetic":
-        inp = moe_inputs.generate(moe_inputs.Workload("dq", T=4, H=K, E=G, k=1, I=128, I_s=0,
-                                                      w4=True), seed=2)
-        sc = inp["w_gate_up_scale"][:, :, :R].copy()
-    else:
-        sc = moe_inputs.f32_to_bf16_bits(
-            rng.uniform(1e-3, 4e-3, size=(G, K // 128, R)).astype(np.float32)
-            * rng.choice([-1.0, 1.0], size=(G, K // 128, R)).astype(np.float32))
-    want = np.stack([mo.bf16_round(mo.dequant_w4(q[g], sc[g])) for g in range(G)])
+    sc = rng.integers(0, 254, size=(G, K // 128, R)).astype(np.uint8)
+    sc = np.where(sc >= 0x7F, sc + 1, sc).astype(np.uint8)     # no NaN codes
+    tsv = None
+    if ts == "pow2":
+        tsv = np.ldexp(1.0, rng.integers(-12, 3, size=G)).astype(np.float32)
+    elif ts == "fp32":
+        tsv = rng.uniform(1e-3, 3e-3, size=G).astype(np.float32)
+    want = np.stack([mo.bf16_round(mo.dequant_w4(q[g], sc[g], 1.0 if tsv is None else tsv[g]))
+                     for g in range(G)])
     q_d = torch.from_numpy(q).cuda()
-    sc_d = gh.dev_bf16(torch, sc)
+    sc_d = torch.from_numpy(sc).cuda()
+    ts_d = None if tsv is None else gh.dev_f32(torch, tsv)
     pad = 1024
     buf = torch.full((G * R * K + pad,), 0x7FC0, dtype=torch.int16, device="cuda")
-    moe.moe_w4_dequantize(q_d, sc_d, buf, G, R, K)
+    moe.moe_w4_dequantize(q_d, sc_d, buf, G, R, K, tscale=ts_d)
     torch.cuda.synchronize()
     got = gh.to_bits(buf)
     got_w = got[:G * R * K].reshape(G, R, K)

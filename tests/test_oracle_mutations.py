@@ -168,3 +168,40 @@ def test_planted_gain_swap_is_caught(monkeypatch):
     monkeypatch.setattr(mo, "forward", _post_gain_used_before_routing)
     with pytest.raises(AssertionError):
         pins.test_scmoe_pre_gain_scales_routed_input_per_channel()
+
+
+# Planted mistakes in the W4A16 dequantisation: each must fail a W4 pin.
+_real_e4m3 = mo.e4m3_to_f64
+_real_dequant_w4 = mo.dequant_w4
+
+
+def _e4m3_bias_8(codes):
+    return _real_e4m3(codes) / 2.0
+
+
+def _e4m3_no_subnormals(codes):
+    b = np.asarray(codes, np.uint8)
+    v = _real_e4m3(b)
+    return np.where(((b >> 3) & 0xF) == 0, np.sign(v) * (1 + (b & 7) / 8.0) * 2.0 ** -7, v)
+
+
+def _tensor_scale_ignored(q, scale_codes, tensor_scale=1.0):
+    return _real_dequant_w4(q, scale_codes, 1.0)
+
+
+@pytest.mark.parametrize("name,attr,fake", [
+    ("E4M3 exponent bias 8", "e4m3_to_f64", _e4m3_bias_8),
+    ("E4M3 subnormals read as normals", "e4m3_to_f64", _e4m3_no_subnormals),
+    ("tensor scale ignored", "dequant_w4", _tensor_scale_ignored),
+])
+def test_planted_w4_mistake_is_caught(monkeypatch, name, attr, fake):
+    from tests import test_oracle_w4 as pins
+    monkeypatch.setattr(mo, attr, fake)
+    failed = 0
+    for pin in (pins.test_e4m3_hand_values, pins.test_e4m3_every_byte_matches_torch,
+                pins.test_dequant_hand_example, pins.test_dequant_matches_packer_and_scales):
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, name
