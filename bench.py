@@ -29,8 +29,16 @@ traffic: FETCH_SIZE + WRITE_SIZE per launch from the committed rocprofv3
 counter summary of that kernel, when it was taken on the current kernel
 source (else null).
 
+measured peaks: before the workload, two diagnostic kernels of the library
+measure what this GPU delivers -- bf16 MFMA throughput (four independent
+32x32x16 MFMA chains per wavefront, two workgroups of four wavefronts per
+CU, varied non-zero operands) and HBM read bandwidth (a 4 GiB read stream,
+non-temporal 16-byte loads) -- and the roofline record carries the
+fraction against that measured peak beside the one against the published
+peak (--no-probe-peaks skips them).
+
 cpu_baseline: the CPU oracle (float64 NumPy, untuned) timed on this host on
-a bounded sample of the same batch.
+a bounded sample of the same batch, with the host's CPU model and BLAS.
 """
 from __future__ import annotations
 
@@ -110,6 +118,77 @@ def cpu_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def blas_backend() -> str:
+    try:
+        from threadpoolctl import threadpool_info
+        b = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '?')})"
+             for i in threadpool_info() if i.get("user_api") == "blas"]
+        if b:
+            return "; ".join(b)
+    except Exception:
+        pass
+    return "unknown"
+
+
+def measure_peaks(moe, torch) -> dict:
+    """Measured bf16 MFMA throughput and HBM read bandwidth of this GPU (the
+    library's probe kernels, timed with events on the stream they run on;
+    the median of several launches)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    wgs, iters = 2 * cus, 40000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    moe.moe_probe_mfma_bf16(wgs, 1000, sink)
+    mfma = []
+    for _ in range(5):
+        a, b = ev(), ev()
+        a.record()
+        flops = moe.moe_probe_mfma_bf16(wgs, iters, sink)
+        b.record()
+        torch.cuda.synchronize()
+        mfma.append(flops / (a.elapsed_time(b) * 1e-3) / 1e12)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = None
+    for per_cu in (1, 2, 4, 8):   # workgroups per CU: the best median
+        rwgs = per_cu * cus
+        rsink = torch.empty(rwgs * 256, dtype=torch.int32, device="cuda")
+        moe.moe_probe_hbm_read(buf, nbytes, rwgs, rsink)
+        hbm = []
+        for _ in range(7):
+            a, b = ev(), ev()
+            a.record()
+            moe.moe_probe_hbm_read(buf, nbytes, rwgs, rsink)
+            b.record()
+            torch.cuda.synchronize()
+            hbm.append(nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+        hbm.sort()
+        if best is None or hbm[len(hbm) // 2] > best[0]:
+            best = (hbm[len(hbm) // 2], hbm[-1], rwgs)
+    del buf
+    mfma.sort()
+    return {"mfma_bf16_tflops": round(mfma[len(mfma) // 2], 1),
+            "mfma_bf16_tflops_max": round(mfma[-1], 1),
+            "hbm_read_gbs": round(best[0], 1), "hbm_read_gbs_max": round(best[1], 1),
+            "method": f"moe_probe_mfma_bf16: {wgs} workgroups x {iters} rounds of four "
+                      f"32x32x16 bf16 MFMA chains per wavefront (median of 5); "
+                      f"moe_probe_hbm_read: 4 GiB read once, each workgroup streaming one "
+                      f"contiguous block in 16 KB steps of non-temporal 16-byte loads, the best "
+                      f"median of 7 over 1, 2, 4 and 8 workgroups per CU ({best[2]} workgroups)"}
+
+
 def cpu_baseline(wl, inp, sample_tokens: int, min_seconds: float, residual=None) -> dict:
     """The oracle, as it stands, on consecutive chunks of `sample_tokens`
     tokens of the same batch (wrapping around it), one oracle forward per
@@ -128,7 +207,7 @@ def cpu_baseline(wl, inp, sample_tokens: int, min_seconds: float, residual=None)
         done += s
         chunks += 1
     return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": cpu_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "blas": blas_backend(),
             "sample": f"{chunks} oracle forwards of {s} consecutive tokens of the same batch of "
                       f"{wl.T} ({done} tokens, {dt:.1f} s, float64 NumPy)"}
 
@@ -205,6 +284,53 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: 
     print(json.dumps(out))
 
 
+def _grouped_kind(name: str) -> str | None:
+    if "grouped_" not in name:
+        return None
+    return "gate_up" if ("<true" in name or ", true" in name) else "down"
+
+
+def write_mfma(workload: str, csv_path: str, command: str) -> None:
+    """MFMA counters of the grouped GEMM launches from one rocprofv3 --pmc
+    run (counters MfmaUtil, MfmaFlopsBF16, GRBM_GUI_ACTIVE): per
+    projection, the mean MFMA-busy share of the SIMDs' active cycles and the
+    bf16 MFMA flops the hardware executed per launch against the algorithmic
+    flops (the excess is the padding of partly filled row tiles).  Writes
+    profiles/mfma_<workload>.json."""
+    import csv
+    import moe_inputs
+    wl = moe_inputs.WORKLOADS[workload]
+    T, H, k, I, Is = wl.T, wl.H, wl.k, wl.I, wl.I_s
+    algo = {"gate_up": 2 * T * k * H * 2 * I + 2 * T * H * 2 * Is,
+            "down": 2 * T * k * I * H + 2 * T * Is * H}
+    vals: dict = {}
+    for r in csv.DictReader(open(csv_path)):
+        kind = _grouped_kind(r["Kernel_Name"])
+        if kind is None:
+            continue
+        vals.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    out = {"workload": wl.label(), "command": command, "kernel_source_sha256": kernel_source_sha(),
+           "projections": {}}
+    for kind in ("gate_up", "down"):
+        util = vals.get((kind, "MfmaUtil"), [])
+        flops = vals.get((kind, "MfmaFlopsBF16"), [])
+        gui = vals.get((kind, "GRBM_GUI_ACTIVE"), [])
+        if not util:
+            continue
+        mean = lambda v: sum(v) / len(v) if v else None  # noqa: E731
+        f = mean(flops)
+        out["projections"][kind] = {
+            "dispatches": len(util), "mfma_util_percent": round(mean(util), 2),
+            "mfma_flops_executed_per_launch": f, "algorithmic_flops_per_launch": algo[kind],
+            "executed_over_algorithmic": round(f / algo[kind], 4) if f else None,
+            "grbm_gui_active_per_launch": mean(gui)}
+    path = os.path.join(ROOT, "profiles", f"mfma_{wl.label()}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def router_backward_bench(args) -> int:
     """Gradients of the router GEMM (moe_router_backward: grad_x, grad_W,
     grad_b) on the prefill batch (T=8192, H=4096, E=64): one JSON line.
@@ -257,7 +383,7 @@ def router_backward_bench(args) -> int:
             dt += time.perf_counter() - ts
             done += n
         cpu = {"value": round(done / dt, 1), "unit": "tokens/s", "cores": cpu_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(), "blas": blas_backend(),
                "sample": f"{done // n} oracle router backwards of {n} tokens of the same batch "
                          f"({done} tokens, {dt:.1f} s, float64 NumPy)"}
     line = {
@@ -291,6 +417,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle time to spend on the baseline sample (at least)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe-peaks", action="store_true",
+                    help="skip measuring this GPU's MFMA and HBM peaks")
     ap.add_argument("--router-backward", action="store_true",
                     help="time moe_router_backward (training path) instead of the forward")
     ap.add_argument("--finish", action="store_true",
@@ -303,10 +431,16 @@ def main() -> int:
                     help="summarise rocprofv3 counter runs into profiles/ (no GPU work)")
     ap.add_argument("--traffic-command", default="",
                     help="the command lines that produced the counter runs (recorded)")
+    ap.add_argument("--write-mfma", metavar="COUNTER_CSV",
+                    help="summarise a rocprofv3 --pmc run of MfmaUtil, MfmaFlopsBF16 and "
+                         "GRBM_GUI_ACTIVE into profiles/ (no GPU work)")
     args = ap.parse_args()
 
     if args.write_traffic:
         write_traffic(args.workload, *args.write_traffic, args.traffic_command)
+        return 0
+    if args.write_mfma:
+        write_mfma(args.workload, args.write_mfma, args.traffic_command)
         return 0
 
     if args.gpus != 1:
@@ -327,7 +461,9 @@ def main() -> int:
     wl = moe_inputs.WORKLOADS[args.workload]
     steps = args.steps if args.steps is not None else (300 if wl.T <= 64 else 20)
     warmup = args.warmup if args.warmup is not None else (30 if wl.T <= 64 else 3)
-    sample = args.cpu_sample if args.cpu_sample is not None else (wl.T if wl.T <= 64 else 8)
+    # the oracle widens every touched expert's weights once per forward, so it
+    # runs on whole batches (up to 8192 tokens), not on small chunks
+    sample = args.cpu_sample if args.cpu_sample is not None else min(wl.T, 8192)
 
     print(f"[bench] generating {wl.label()}", file=sys.stderr, flush=True)
     inp = moe_inputs.generate(wl, seed=0)
@@ -382,6 +518,11 @@ def main() -> int:
     counts = np.diff(offsets.cpu().numpy())
     touched = int(np.sum(counts > 0))
 
+    peaks = None
+    if not args.no_probe_peaks:
+        print("[bench] measuring this GPU's MFMA and HBM peaks", file=sys.stderr, flush=True)
+        peaks = measure_peaks(moe, torch)
+
     hip = HipEvents()
     evs = [(hip.create(), hip.create()) for _ in range(steps)]
     probes = [moe.make_probes(events={moe.MOE_EV_PERMUTE: a, moe.MOE_EV_GATE_UP: b}) for a, b in evs]
@@ -430,6 +571,10 @@ def main() -> int:
                     "traffic": traffic,
                     "kernel": "grouped gate_up + SwiGLU (routed + shared, one launch)",
                     "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(gate_up_ms, 5)}
+    if peaks is not None:
+        mp = peaks["hbm_read_gbs"] if hbm_bound else peaks["mfma_bf16_tflops"]
+        roofline["measured_peak"] = mp
+        roofline["frac_measured"] = round(achieved / mp, 4)
     s_step = ms_per_step * 1e-3
     layer = {"tokens_per_s": round(T / s_step, 1),
              "GB_per_s": round(layer_bytes / s_step / 1e9, 1),
@@ -437,6 +582,10 @@ def main() -> int:
              "TFLOP_per_s": round((layer_flops + router_flops) / s_step / 1e12, 1),
              "mfma_frac": round((layer_flops + router_flops) / s_step / 1e12 / BF16_PEAK_TFLOPS, 4),
              "experts_touched": touched, "max_over_mean_count": round(float(counts.max() / counts.mean()), 2)}
+    if peaks is not None:
+        layer["hbm_frac_measured"] = round(layer_bytes / s_step / 1e9 / peaks["hbm_read_gbs"], 4)
+        layer["mfma_frac_measured"] = round((layer_flops + router_flops) / s_step / 1e12
+                                            / peaks["mfma_bf16_tflops"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -452,7 +601,7 @@ def main() -> int:
                    "routed_scaling_factor": wl.rsf, "swiglu_limit": wl.limit,
                    "scmoe": wl.scmoe, "seed": 0, "parallelism": "ep1_tp1",
                    "finish": "residual_add" if args.finish else None},
-        "roofline": roofline, "cpu_baseline": cpu, "layer": layer,
+        "roofline": roofline, "cpu_baseline": cpu, "layer": layer, "measured_peaks": peaks,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -178,7 +178,9 @@ typedef struct moe_finish {
  * recorded on `stream` (for timing a step on the stream it runs on).
  * events[MOE_EV_BEGIN] is recorded before the first kernel, events[s] right
  * after step s; a step the layer does not run records at the same point as
- * the one before it. */
+ * the one before it.  For batches of at most 4096 (token, slot) pairs and
+ * T*E <= 16384 the top-k and the permutation are one launch: MOE_EV_ROUTER
+ * then follows both and MOE_EV_PERMUTE is recorded at the same point. */
 enum {
   MOE_EV_BEGIN = 0,
   MOE_EV_PRENORM = 1,  /* ScMoE pre-norm                                    */
@@ -204,6 +206,10 @@ typedef struct moe_probes {
   int32_t* inv_pos;            /* [T * k]                                         */
   moe_bf16* xr;                /* [T, H] ScMoE routed input after the pre-norm    */
   float* logits;               /* [T, E] fp32 router logits                       */
+  moe_bf16* h;                 /* [T * k, I] routed SwiGLU outputs (permuted rows) */
+  float* y;                    /* [T * k, H] routed down outputs (permuted rows)  */
+  moe_bf16* h_shared;          /* [T, I_shared] shared expert's SwiGLU outputs    */
+  float* y_shared;             /* [T, H] shared expert's output                   */
   hipEvent_t events[MOE_EV_COUNT];
 } moe_probes;
 
@@ -397,6 +403,25 @@ moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
 moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float* tscale,
                              int32_t n_groups, int64_t rows, int32_t K, moe_bf16* out,
                              hipStream_t stream);
+
+/* Diagnostics, not on the layer's path: what the current device delivers,
+ * for reporting the layer's rates against measured peaks beside the
+ * published ones.
+ * moe_probe_mfma_bf16: `workgroups` workgroups of four wavefronts, each
+ *   running `iters` rounds of four independent 32x32x16 bf16 MFMAs on
+ *   varied non-zero operands (workgroups, iters >= 1); sink [workgroups *
+ *   256] fp32 device scratch the kernel writes (16-byte aligned);
+ *   *flops (host) receives the floating-point operations enqueued.
+ * moe_probe_hbm_read: reads `bytes` of src once (each of `workgroups`
+ *   workgroups of 256 threads streams one contiguous block, 16 KB per step
+ *   in non-temporal 16-byte loads; bytes a positive multiple of 16, src
+ *   16-byte aligned); sink [workgroups * 256] uint32 device scratch the
+ *   kernel writes.
+ * Time them with events on `stream`. */
+moe_status moe_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, double* flops,
+                               hipStream_t stream);
+moe_status moe_probe_hbm_read(const void* src, int64_t bytes, int32_t workgroups,
+                              uint32_t* sink, hipStream_t stream);
 
 /* Static text naming a status code. */
 const char* moe_status_string(moe_status s);

@@ -15,7 +15,8 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import (POINTER, Structure, c_char_p, c_double, c_float, c_int, c_int32, c_int64,
+                    c_size_t, c_void_p)
 
 # torch first, at import: its bundled HIP runtime (soname libamdhip64.so.7)
 # is then the one libmoe.so binds to whenever it is loaded in this process,
@@ -69,8 +70,8 @@ MOE_EV_GATE_UP, MOE_EV_DOWN, MOE_EV_COMBINE, MOE_EV_COUNT = 4, 5, 6, 7
 
 class moe_probes(Structure):
     _fields_ = [(n, c_void_p) for n in (
-        "topk_ids", "topk_w", "expert_offsets", "sorted_token", "inv_pos", "xr", "logits")] + [
-        ("events", c_void_p * MOE_EV_COUNT)]
+        "topk_ids", "topk_w", "expert_offsets", "sorted_token", "inv_pos", "xr", "logits", "h",
+        "y", "h_shared", "y_shared")] + [("events", c_void_p * MOE_EV_COUNT)]
 
 
 def _load() -> ctypes.CDLL:
@@ -108,6 +109,9 @@ def _load() -> ctypes.CDLL:
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_w4_dequantize": (st, [c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32,
                                    c_void_p, c_void_p]),
+        "moe_probe_mfma_bf16": (st, [c_int32, c_int32, c_void_p, POINTER(c_double),
+                                     c_void_p]),
+        "moe_probe_hbm_read": (st, [c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
         "moe_status_string": (c_char_p, [c_int]),
         "moe_last_error": (c_char_p, []),
     }
@@ -133,7 +137,7 @@ EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
             "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
             "moe_combine_finish", "moe_forward", "moe_forward_finish", "moe_forward_noalloc",
             "moe_router_backward_workspace_size", "moe_router_backward", "moe_w4_dequantize",
-            "moe_status_string", "moe_last_error")
+            "moe_probe_mfma_bf16", "moe_probe_hbm_read", "moe_status_string", "moe_last_error")
 
 
 def _status_name(s: int) -> str:
@@ -243,10 +247,11 @@ def make_weights(w_router, corr_bias, w_gate_up, w_down, ws_gate_up=None, ws_dow
 
 
 def make_probes(topk_ids=None, topk_w=None, expert_offsets=None, sorted_token=None,
-                inv_pos=None, xr=None, logits=None, events=None) -> moe_probes:
+                inv_pos=None, xr=None, logits=None, events=None, h=None, y=None,
+                h_shared=None, y_shared=None) -> moe_probes:
     """`events`: dict {MOE_EV_*: raw hipEvent_t handle (int)}."""
     pr = moe_probes(*[_ptr(t) for t in (topk_ids, topk_w, expert_offsets, sorted_token,
-                                        inv_pos, xr, logits)])
+                                        inv_pos, xr, logits, h, y, h_shared, y_shared)])
     for i, ev in (events or {}).items():
         pr.events[i] = ev
     return pr
@@ -301,4 +306,18 @@ def moe_router_backward(params, grad_logits, x, w_router, grad_x=None, grad_w=No
     _check(lib().moe_router_backward(ctypes.byref(params), _ptr(grad_logits), int(strides[0]),
                                     int(strides[1]), _ptr(x), _ptr(w_router), _ptr(grad_x),
                                     _ptr(grad_w), _ptr(grad_b), _ptr(ws), _nbytes(ws),
+                                    _stream(stream)))
+
+
+def moe_probe_mfma_bf16(workgroups, iters, sink, stream=None) -> float:
+    """Enqueue the bf16 MFMA throughput probe; returns the flops enqueued."""
+    f = c_double(0.0)
+    _check(lib().moe_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), ctypes.byref(f),
+                                     _stream(stream)))
+    return f.value
+
+
+def moe_probe_hbm_read(src, nbytes, workgroups, sink, stream=None) -> None:
+    """Enqueue the HBM read-stream probe over nbytes of src."""
+    _check(lib().moe_probe_hbm_read(_ptr(src), int(nbytes), int(workgroups), _ptr(sink),
                                     _stream(stream)))

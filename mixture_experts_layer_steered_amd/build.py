@@ -20,7 +20,8 @@ LIB = os.path.join(HERE, "libmoe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["router.hip", "router_bwd.hip", "permute.hip", "grouped_gemm.hip", "dequant.hip",
-           "combine.hip", "noalloc.hip", "capi.cpp"]
+           "combine.hip", "noalloc.hip", "probe.hip",
+           "capi.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

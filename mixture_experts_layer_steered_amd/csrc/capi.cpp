@@ -507,6 +507,10 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     OPTIONAL_PTR(probes->inv_pos);
     OPTIONAL_PTR(probes->xr);
     OPTIONAL_PTR(probes->logits);
+    OPTIONAL_PTR(probes->h);
+    OPTIONAL_PTR(probes->y);
+    OPTIONAL_PTR(probes->h_shared);
+    OPTIONAL_PTR(probes->y_shared);
   }
   const int64_t T = p->T, N = T * p->k;
   const GemmVariant v = pick_variant(
@@ -531,6 +535,10 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     if (probes->inv_pos) L.inv_pos = probes->inv_pos;
     if (probes->xr && p->scmoe) L.xr = probes->xr;
     if (probes->logits) L.logits = probes->logits;
+    if (probes->h) L.h = probes->h;
+    if (probes->y) L.y = probes->y;
+    if (probes->h_shared && p->I_shared > 0) L.hs = probes->h_shared;
+    if (probes->y_shared && p->I_shared > 0) L.ys = probes->y_shared;
   }
   const uint16_t* xr = x_routed;
   const uint16_t* xs = x_shared ? x_shared : x_routed;
@@ -571,7 +579,11 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   // Weight streaming (decode-sized batches): the shared expert's two GEMMs
   // run on the second stream, forked at the start, on 3/4 of the CUs, while
   // the routing kernels run on the rest; the combine waits for them.
-  const bool beside = shared && v == GemmVariant::kWStream && !one_stream;
+  // MOE_SHARED_BESIDE=0 keeps the shared expert in the routed launches (a
+  // tuning lever; the results are the same)
+  const char* beside_env = std::getenv("MOE_SHARED_BESIDE");
+  const bool beside = shared && v == GemmVariant::kWStream && !one_stream &&
+                      !(beside_env && !std::strcmp(beside_env, "0"));
   const bool deq_side = w4_deq && !one_stream;
   SideStream* side = nullptr;
   if ((beside || deq_side) && (s = side_stream(&side)) != MOE_OK) return s;
@@ -627,18 +639,32 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     xr = L.xr;
   }
   if ((s = mark(MOE_EV_PRENORM)) != MOE_OK) return s;
-  if ((s = device_status(launch_router(xr, w->w_router, w->corr_bias, L.logits, L.partial, L.ids,
-                                       L.w, T, p->H, p->E, p->k, p->routed_scaling_factor, stream),
-                         "router")) != MOE_OK)
-    return s;
-  if ((s = mark(MOE_EV_ROUTER)) != MOE_OK) return s;
-  // the permutation and the grouped GEMM's m-tile prefix (one launch for a
-  // decode-sized batch)
-  if ((s = device_status(launch_permute(L.ids, L.counts, L.starts, L.offsets, L.sorted_token,
-                                        L.inv_pos, N, p->E, p->k, gemm_tile_m(v), L.mstart,
-                                        stream),
-                         "permute")) != MOE_OK)
-    return s;
+  if (route_small_fits(T, p->E, p->k)) {
+    // decode-sized: the router GEMM, then top-k, permutation and the GEMM's
+    // m-tile prefix in one launch (the router event follows both)
+    if ((s = device_status(launch_route_small(xr, w->w_router, w->corr_bias, L.logits, L.partial,
+                                              L.ids, L.w, T, p->H, p->E, p->k,
+                                              p->routed_scaling_factor, L.offsets,
+                                              L.sorted_token, L.inv_pos, gemm_tile_m(v), L.mstart,
+                                              stream),
+                           "routing")) != MOE_OK)
+      return s;
+    if ((s = mark(MOE_EV_ROUTER)) != MOE_OK) return s;
+  } else {
+    if ((s = device_status(launch_router(xr, w->w_router, w->corr_bias, L.logits, L.partial,
+                                         L.ids, L.w, T, p->H, p->E, p->k,
+                                         p->routed_scaling_factor, stream),
+                           "router")) != MOE_OK)
+      return s;
+    if ((s = mark(MOE_EV_ROUTER)) != MOE_OK) return s;
+    // the permutation and the grouped GEMM's m-tile prefix (one launch for a
+    // batch of at most 4096 pairs)
+    if ((s = device_status(launch_permute(L.ids, L.counts, L.starts, L.offsets, L.sorted_token,
+                                          L.inv_pos, N, p->E, p->k, gemm_tile_m(v), L.mstart,
+                                          stream),
+                           "permute")) != MOE_OK)
+      return s;
+  }
   // (the gate_up weights' dequantisation ends inside the permute step, so
   // the gate_up step times the GEMM alone)
   if (deq_side &&
@@ -753,6 +779,35 @@ moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float
   moe_status s;
   if ((s = device_status(launch_w4_dequant(q, scale, tscale, out, n_groups, rows, K, stream),
                          "dequantise")) != MOE_OK)
+    return s;
+  return ok();
+}
+
+moe_status moe_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, double* flops,
+                               hipStream_t stream) {
+  if (workgroups < 1 || iters < 1)
+    return fail(MOE_ERR_INVALID_ARG, "workgroups = %d, iters = %d must be >= 1", workgroups,
+                iters);
+  REQUIRE_PTR(sink);
+  if (!flops) return fail(MOE_ERR_INVALID_ARG, "flops is NULL");
+  moe_status s;
+  if ((s = device_status(launch_probe_mfma(workgroups, iters, sink, stream), "mfma probe")) !=
+      MOE_OK)
+    return s;
+  *flops = probe_mfma_flops(workgroups, iters);
+  return ok();
+}
+
+moe_status moe_probe_hbm_read(const void* src, int64_t bytes, int32_t workgroups,
+                              uint32_t* sink, hipStream_t stream) {
+  if (workgroups < 1 || bytes < 16 || bytes % 16)
+    return fail(MOE_ERR_INVALID_ARG, "bytes = %lld must be a positive multiple of 16, "
+                "workgroups = %d >= 1", (long long)bytes, workgroups);
+  REQUIRE_PTR(src);
+  REQUIRE_PTR(sink);
+  moe_status s;
+  if ((s = device_status(launch_probe_read(src, bytes, workgroups, sink, stream), "read probe")) !=
+      MOE_OK)
     return s;
   return ok();
 }

@@ -51,6 +51,18 @@ hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, f
                          float* partial, int32_t* ids, float* wts, int64_t T, int H, int E, int k,
                          float rsf, hipStream_t stream);
 
+// Routing of a batch small enough for one workgroup (T*k <= 4096 pairs and
+// T*E <= 16384 logits, decode): the router GEMM, then one kernel that sums
+// the logits' K-slice partials into LDS, ranks every token from them (wave
+// top-k), permutes the pairs and writes the grouped GEMM's m-tile prefix
+// for tiles of bm rows.  Results equal launch_router + launch_permute bit
+// for bit.
+bool route_small_fits(int64_t T, int E, int k);
+hipError_t launch_route_small(const uint16_t* x, const float* w, const float* bias, float* logits,
+                              float* partial, int32_t* ids, float* wts, int64_t T, int H, int E,
+                              int k, float rsf, int32_t* offsets, int32_t* sorted_token,
+                              int32_t* inv_pos, int bm, int32_t* mstart, hipStream_t stream);
+
 int permute_tiles(int64_t N);
 // mstart (optional): also write the grouped GEMM's m-tile prefix over the
 // expert counts for tiles of bm rows (as launch_gemm_schedule does).
@@ -94,3 +106,11 @@ hipError_t launch_combine(const float* y_perm, const float* w, const int32_t* in
 // Device address and size of the current device's copy of the fixed scratch
 // (looked up once per device, then cached; noalloc.hip).
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
+// Peak probes (probe.hip): a bf16 MFMA throughput kernel (wgs workgroups of
+// four wavefronts; sink [wgs * 256] fp32) with its flop count, and an HBM
+// read stream over `bytes` (a multiple of 16) of src (sink [wgs * 256]).
+hipError_t launch_probe_mfma(int wgs, int iters, float* sink, hipStream_t stream);
+double probe_mfma_flops(int wgs, int iters);
+hipError_t launch_probe_read(const void* src, int64_t bytes, int wgs, uint32_t* sink,
+                             hipStream_t stream);

@@ -19,14 +19,9 @@
 // never shows in a result.
 #include "common.h"
 #include "kernels.h"
+#include "permute_small.h"
 
 namespace {
-
-constexpr int PM_THREADS = 1024;
-constexpr int PM_WAVES = PM_THREADS / 64;
-constexpr int PM_PER_WAVE = 256;
-constexpr int PM_TILE = PM_WAVES * PM_PER_WAVE;  // 4096 pairs
-constexpr int PM_STEPS = PM_PER_WAVE / 64;
 
 __global__ __launch_bounds__(PM_THREADS) void permute_hist_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ counts, int64_t N, int E) {
@@ -141,85 +136,9 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_token, int32_t* __restrict__ inv_pos, int64_t N, int E, int k,
     int bm, int32_t* __restrict__ mstart) {
-  __shared__ int32_t whist[PM_WAVES][MOE_MAX_EXPERTS_DEV];
-  __shared__ int32_t wsum[2][PM_WAVES];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) whist[i / E][i % E] = 0;
-  __syncthreads();
-  const int64_t wbase = (int64_t)wave * PM_PER_WAVE;
-  int my_e[PM_STEPS];
-#pragma unroll
-  for (int s = 0; s < PM_STEPS; ++s) {
-    const int64_t p = wbase + s * 64 + lane;
-    my_e[s] = (p < N) ? ids[p] : MOE_MAX_EXPERTS_DEV;  // sentinel: matches no expert
-    if (p < N) atomicAdd(&whist[wave][my_e[s]], 1);
-  }
-  __syncthreads();
-  // thread e: expert e's count, then exclusive scans over experts of the
-  // counts (offsets) and of the m-tiles ceil(count / bm) (GEMM schedule)
-  const int e = threadIdx.x;
-  int32_t cnt = 0;
-  if (e < E)
-    for (int w = 0; w < PM_WAVES; ++w) cnt += whist[w][e];
-  int32_t v[2] = {cnt, (cnt + bm - 1) / bm};
-  int32_t incl[2] = {v[0], v[1]};
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int32_t o = __shfl_up(incl[q], off, 64);
-      if (lane >= off) incl[q] += o;
-    }
-  }
-  if (lane == 63) {
-    wsum[0][wave] = incl[0];
-    wsum[1][wave] = incl[1];
-  }
-  __syncthreads();
-  int32_t before[2] = {0, 0};
-  for (int w = 0; w < wave; ++w) {
-    before[0] += wsum[0][w];
-    before[1] += wsum[1][w];
-  }
-  const int32_t start = before[0] + incl[0] - v[0];
-  if (e < E) {
-    offsets[e] = start;
-    if (mstart) mstart[e] = before[1] + incl[1] - v[1];
-    // each wave's run of expert e starts after the earlier waves' pairs
-    int32_t run = start;
-    for (int w = 0; w < PM_WAVES; ++w) {
-      const int32_t c = whist[w][e];
-      whist[w][e] = run;
-      run += c;
-    }
-  }
-  if (e == E - 1) {
-    offsets[E] = (int32_t)N;
-    if (mstart) mstart[E] = before[1] + incl[1];
-  }
-  __syncthreads();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-  for (int s = 0; s < PM_STEPS; ++s) {
-    const int ee = my_e[s];
-    uint64_t same = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 11; ++b) {
-      const bool bit = (ee >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      same &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(same & lt_mask);
-    const int n_same = __popcll(same);
-    if (ee < E) {
-      const int64_t p = wbase + s * 64 + lane;
-      const int32_t pos = whist[wave][ee] + rank;
-      sorted_token[pos] = (int32_t)(p / k);
-      inv_pos[p] = pos;
-      if (rank == 0) whist[wave][ee] += n_same;
-    }
-  }
+  __shared__ int32_t whist[PM_WAVES * MOE_MAX_EXPERTS_DEV];
+  __shared__ int32_t wsum[2 * PM_WAVES];
+  permute_small_body(ids, offsets, sorted_token, inv_pos, N, E, k, bm, mstart, whist, wsum);
 }
 
 // Optional materialised gather of the permuted activations: 16 bytes per

@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "permute_small.h"
 #include "topk.h"
 
 namespace {
@@ -162,9 +163,73 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  int id, slot;
-  topk_token<TK_PER_LANE>(partial, splits, logits, bias, ids, wts, t, T, E, k, rsf, lane, id,
-                          slot);
+  topk_token<TK_PER_LANE>(partial, splits, logits, bias, ids, wts, t, T, E, k, rsf, lane);
+}
+
+// Routing of a batch small enough for one workgroup (decode): the logits'
+// K-slice partials are summed (in slice order, as the top-k kernel sums
+// them) into LDS, each wavefront ranks tokens from those LDS-staged logits,
+// the picks go to LDS as well, and the same workgroup then permutes the
+// pairs and writes the grouped GEMM's m-tile prefix -- one launch after the
+// router GEMM instead of two.  The LDS of the logits is reused for the
+// permute's histograms.
+constexpr int RS_MAX_LOGITS = 16384;  // T * E staged in LDS
+constexpr int RS_LDS_WORDS =
+    RS_MAX_LOGITS > PM_WAVES * MOE_MAX_EXPERTS_DEV ? RS_MAX_LOGITS : PM_WAVES * MOE_MAX_EXPERTS_DEV;
+
+template <int TK_PER_LANE>
+__global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
+    const float* __restrict__ partial, int splits, float* __restrict__ logits,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ wts, int T,
+    int E, int k, float rsf, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token,
+    int32_t* __restrict__ inv_pos, int bm, int32_t* __restrict__ mstart) {
+  __shared__ __attribute__((aligned(16))) int32_t lds[RS_LDS_WORDS];
+  __shared__ int32_t ids_lds[PM_TILE];
+  __shared__ int32_t wsum[2 * PM_WAVES];
+  float* lg_lds = reinterpret_cast<float*>(lds);
+  const int TE = T * E;
+  // logits: slice partials summed in slice order; two elements per thread
+  // and pass, their 2 x 16 loads in flight together
+  for (int i0 = threadIdx.x; i0 < TE; i0 += 2 * PM_THREADS) {
+    const int i1 = i0 + PM_THREADS;
+    float l0 = 0.f, l1 = 0.f;
+    for (int sp0 = 0; sp0 < splits; sp0 += 16) {
+      float p0[16], p1[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const bool in = sp0 + u < splits;
+        p0[u] = in ? partial[(int64_t)(sp0 + u) * TE + i0] : 0.f;
+        p1[u] = in && i1 < TE ? partial[(int64_t)(sp0 + u) * TE + i1] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (sp0 + u < splits) {
+          l0 = sp0 + u == 0 ? p0[u] : l0 + p0[u];
+          l1 = sp0 + u == 0 ? p1[u] : l1 + p1[u];
+        }
+      }
+    }
+    lg_lds[i0] = l0;
+    if (splits > 1) logits[i0] = l0;
+    if (i1 < TE) {
+      lg_lds[i1] = l1;
+      if (splits > 1) logits[i1] = l1;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += PM_WAVES) {
+    float lg[TK_PER_LANE];
+#pragma unroll
+    for (int i = 0; i < TK_PER_LANE; ++i) {
+      const int e = lane + 64 * i;
+      lg[i] = e < E ? lg_lds[t * E + e] : 0.f;
+    }
+    topk_select<TK_PER_LANE>(lg, bias, ids, wts, ids_lds, t, E, k, rsf, lane);
+  }
+  __syncthreads();
+  permute_small_body(ids_lds, offsets, sorted_token, inv_pos, (int64_t)T * k, E, k, bm, mstart,
+                     lds, wsum);
 }
 
 }  // namespace
@@ -212,5 +277,37 @@ hipError_t launch_router(const uint16_t* x, const float* w, const float* bias, f
     hipLaunchKernelGGL(router_topk_kernel<8>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
   else
     hipLaunchKernelGGL(router_topk_kernel<16>, g, b, 0, stream, part, splits, logits, bias, ids, wts, T, E, k, rsf);
+  return hipGetLastError();
+}
+
+bool route_small_fits(int64_t T, int E, int k) {
+  return T * k <= PM_TILE && T * E <= RS_MAX_LOGITS;
+}
+
+hipError_t launch_route_small(const uint16_t* x, const float* w, const float* bias, float* logits,
+                              float* partial, int32_t* ids, float* wts, int64_t T, int H, int E,
+                              int k, float rsf, int32_t* offsets, int32_t* sorted_token,
+                              int32_t* inv_pos, int bm, int32_t* mstart, hipStream_t stream) {
+  hipError_t e = launch_router_logits(x, w, logits, partial, T, H, E, stream);
+  if (e != hipSuccess) return e;
+  const int splits = router_splits(T, H, E);
+  float* part = splits > 1 ? partial : logits;
+  const int bmv = bm > 0 ? bm : 1;
+  const int Ti = (int)T;
+#define MOE_ROUTE_SMALL(TK)                                                                      \
+  hipLaunchKernelGGL(route_small_kernel<TK>, dim3(1), dim3(PM_THREADS), 0, stream, part, splits, \
+                     logits, bias, ids, wts, Ti, E, k, rsf, offsets, sorted_token, inv_pos, bmv,  \
+                     mstart)
+  if (E <= 64)
+    MOE_ROUTE_SMALL(1);
+  else if (E <= 128)
+    MOE_ROUTE_SMALL(2);
+  else if (E <= 256)
+    MOE_ROUTE_SMALL(4);
+  else if (E <= 512)
+    MOE_ROUTE_SMALL(8);
+  else
+    MOE_ROUTE_SMALL(16);
+#undef MOE_ROUTE_SMALL
   return hipGetLastError();
 }

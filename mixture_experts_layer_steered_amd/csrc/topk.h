@@ -27,27 +27,121 @@ __device__ __forceinline__ uint64_t topk_key(float sb, int e) {
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
 }
 
-// One wavefront ranks token t.  The logit of expert e is the sum of the
-// `splits` K-slice partials partial[s][t][e] in slice order (fixed, so
-// reruns repeat); with splits > 1 it is also written to logits[t][e].
-// TK_PER_LANE = ceil(E/64) experts per lane, as 64-bit keys; k wave-wide
-// arg-max rounds pick the winners.  TK_SLICES partial loads are in flight
-// per expert (registers against round trips).  Lanes j < k write pick j's rank-ordered
-// id and weight; the function returns the id (lane < k) and its slot.
+// The selection of one token by one wavefront from its logits in
+// registers: lane L holds experts L + 64 i (i < TK_PER_LANE) as lg[i] (lanes
+// past E hold anything; only e < E ranks).  k wave-wide arg-max rounds over
+// 64-bit keys pick the winners; the picks' ids and weights go to ids / wts
+// of token t in ascending id order, the ids also to ids_copy when it is
+// not null (the same layout, e.g. in LDS).
+//
+// With at most two experts per lane (E <= 128) the selection is a count
+// instead: every key is compared with all E keys (read across the wave
+// with readlane, uniform indices), an expert is picked iff fewer than k
+// keys exceed its own, and a pick's slot is the number of picks with a
+// lower id (one ballot per half).  The keys are distinct (the id is part
+// of them), so both forms pick the same experts.
+template <int TK_PER_LANE>
+__device__ __forceinline__ void topk_select(const float (&lg)[TK_PER_LANE],
+                                            const float* __restrict__ bias,
+                                            int32_t* __restrict__ ids, float* __restrict__ wts,
+                                            int32_t* ids_copy, int64_t t, int E, int k, float rsf,
+                                            int lane) {
+  uint64_t key[TK_PER_LANE];
+  float sg[TK_PER_LANE];  // the unbiased scores: the emitted weights reuse them
+#pragma unroll
+  for (int i = 0; i < TK_PER_LANE; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = 0;
+    sg[i] = 0.f;
+    if (e < E) {
+      sg[i] = topk_sigmoid(lg[i]);
+      const float b = bias ? bias[e] : 0.0f;
+      key[i] = topk_key(sg[i] + b, e);
+    }
+  }
+  if constexpr (TK_PER_LANE <= 2) {
+    int above[TK_PER_LANE];
+#pragma unroll
+    for (int i = 0; i < TK_PER_LANE; ++i) above[i] = 0;
+#pragma unroll
+    for (int h = 0; h < TK_PER_LANE; ++h) {
+      const uint32_t klo = (uint32_t)key[h], khi = (uint32_t)(key[h] >> 32);
+      for (int j = 0; j < 64; ++j) {
+        const uint64_t other = ((uint64_t)__builtin_amdgcn_readlane(khi, j) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane(klo, j);
+#pragma unroll
+        for (int i = 0; i < TK_PER_LANE; ++i) above[i] += other > key[i] ? 1 : 0;
+      }
+    }
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int before = 0;   // picks in the halves of lower ids
+#pragma unroll
+    for (int i = 0; i < TK_PER_LANE; ++i) {
+      const int e = lane + 64 * i;
+      const bool pick = e < E && above[i] < k;
+      const uint64_t picks = __ballot(pick);
+      if (pick) {
+        const int slot = before + __popcll(picks & lower);
+        ids[t * k + slot] = e;
+        wts[t * k + slot] = rsf * sg[i];
+        if (ids_copy) ids_copy[t * k + slot] = e;
+      }
+      before += __popcll(picks);
+    }
+    return;
+  }
+  int mine = -1;       // lane j < k ends up holding the j-th pick
+  float mine_s = 0.f;  // and its unbiased score
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < TK_PER_LANE; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(~(uint32_t)best);
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < TK_PER_LANE; ++i) {
+      if (key[i] == best) {
+        key[i] = 0;  // taken: 0 is below every real key
+        se = sg[i];
+      }
+    }
+    se = __shfl(se, e & 63, MOE_WAVE);  // the owner lane of expert e holds its score
+    if (lane == j) {
+      mine = e;
+      mine_s = se;
+    }
+  }
+  // ascending order: rank of each pick among the k picks
+  int rank = 0;
+  for (int i = 0; i < k; ++i) {
+    const int other = __shfl(mine, i, MOE_WAVE);
+    rank += (lane < k && other < mine) ? 1 : 0;
+  }
+  if (lane < k) {
+    ids[t * k + rank] = mine;
+    wts[t * k + rank] = rsf * mine_s;
+    if (ids_copy) ids_copy[t * k + rank] = mine;
+  }
+}
+
+// One wavefront ranks token t from the router GEMM's K-slice partials: the
+// logit of expert e is the sum of the `splits` partials partial[s][t][e] in
+// slice order (fixed, so reruns repeat); with splits > 1 it is also written
+// to logits[t][e].  TK_SLICES partial loads are in flight per expert
+// (registers against round trips).
 template <int TK_PER_LANE, int TK_SLICES = (TK_PER_LANE <= 4 ? 16 : 64 / TK_PER_LANE)>
 __device__ __forceinline__ void topk_token(const float* __restrict__ partial, int splits,
                                            float* __restrict__ logits,
                                            const float* __restrict__ bias,
                                            int32_t* __restrict__ ids, float* __restrict__ wts,
                                            int64_t t, int64_t T, int E, int k, float rsf,
-                                           int lane, int& out_id, int& out_slot) {
+                                           int lane) {
   const int64_t TE = T * E;
-  uint64_t key[TK_PER_LANE];
   float lg[TK_PER_LANE];
 #pragma unroll
   for (int i = 0; i < TK_PER_LANE; ++i) {
     const int e = lane + 64 * i;
-    key[i] = 0;
     lg[i] = 0.f;
     if (e < E) {
       // the K-slice partials, TK_SLICES loads in flight (one round trip for
@@ -64,43 +158,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ partial, in
       }
       if (splits > 1) logits[t * E + e] = l;
       lg[i] = l;
-      const float s = topk_sigmoid(l);
-      const float b = bias ? bias[e] : 0.0f;
-      key[i] = topk_key(s + b, e);
     }
   }
-  int mine = -1;       // lane j < k ends up holding the j-th pick
-  float mine_l = 0.f;  // and its logit
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < TK_PER_LANE; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(~(uint32_t)best);
-    float le = 0.f;
-#pragma unroll
-    for (int i = 0; i < TK_PER_LANE; ++i) {
-      if (key[i] == best) {
-        key[i] = 0;  // taken: 0 is below every real key
-        le = lg[i];
-      }
-    }
-    le = __shfl(le, e & 63, MOE_WAVE);  // the owner lane of expert e holds its logit
-    if (lane == j) {
-      mine = e;
-      mine_l = le;
-    }
-  }
-  // ascending order: rank of each pick among the k picks
-  int rank = 0;
-  for (int i = 0; i < k; ++i) {
-    const int other = __shfl(mine, i, MOE_WAVE);
-    rank += (lane < k && other < mine) ? 1 : 0;
-  }
-  if (lane < k) {
-    ids[t * k + rank] = mine;
-    wts[t * k + rank] = rsf * topk_sigmoid(mine_l);
-  }
-  out_id = mine;
-  out_slot = rank;
+  topk_select<TK_PER_LANE>(lg, bias, ids, wts, nullptr, t, E, k, rsf, lane);
 }

@@ -293,20 +293,20 @@ def expert_weights(inp: dict, e: int) -> tuple[np.ndarray, np.ndarray]:
 
 # ---------------------------------------------------------- S4-S6 FFN ----
 
-def swiglu_ffn(a: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
-               limit: float, round_h: bool = True) -> tuple[np.ndarray, np.ndarray]:
-    """S4+S5 for one expert (or S6 for the shared one), fp64.
+def swiglu_pre(a: np.ndarray, w_gate_up: np.ndarray, limit: float,
+               cols: np.ndarray | None = None) -> dict:
+    """The SwiGLU of S4 (S6) before its bf16 rounding, fp64, for the output
+    columns `cols` (all when None): g = a Wg^T and u = a Wu^T, the clamped
+    h = silu(min(g, L)) * clamp(u, -L, L), and sum_i |a_i| |w_i| of the gate
+    and up dot products (the scale of their rounding errors in any fp32
+    evaluation).
 
-    a          float64 [n, H] (the rows routed to this expert)
-    w_gate_up  bf16 [2I, H]: gate rows [0, I), up rows [I, 2I) (or float64
-               weight values, e.g. dequantised W4A16 weights)
-    w_down     bf16 [H, I] (or float64)
-    Returns (h float64 [n, I] -- the bf16 value when round_h, y float64
-    [n, H], unrounded).
+    a          float64 [n, H];  w_gate_up bf16 [2I, H] (or float64 values)
+    Returns dict(g, u, h, gabs, uabs), each [n, len(cols)] (or [n, I]).
     """
     I = w_gate_up.shape[0] // 2
-    wg = _weights_f64(w_gate_up[:I])
-    wu = _weights_f64(w_gate_up[I:])
+    wg = _weights_f64(w_gate_up[:I] if cols is None else w_gate_up[:I][cols])
+    wu = _weights_f64(w_gate_up[I:] if cols is None else w_gate_up[I:][cols])
     g = a @ wg.T
     u = a @ wu.T
     L = float(np.float32(limit))
@@ -314,19 +314,53 @@ def swiglu_ffn(a: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
     uc = np.clip(u, -L, L)                # up: bounded on both sides
     with np.errstate(over="ignore", invalid="ignore"):
         h = gc / (1.0 + np.exp(-gc)) * uc
-    if round_h:
-        h = bf16_to_f64(bf16_round(h))
+    aa = np.abs(a)
+    return dict(g=g, u=u, h=h, gabs=aa @ np.abs(wg).T, uabs=aa @ np.abs(wu).T)
+
+
+def swiglu_ffn(a: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
+               limit: float, round_h: bool = True,
+               h_given: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """S4+S5 for one expert (or S6 for the shared one), fp64.
+
+    a          float64 [n, H] (the rows routed to this expert)
+    w_gate_up  bf16 [2I, H]: gate rows [0, I), up rows [I, 2I) (or float64
+               weight values, e.g. dequantised W4A16 weights)
+    w_down     bf16 [H, I] (or float64)
+    h_given    float64 [n, I] or None: bf16 values of h to use instead of
+               this function's own rounding (a valid rounding chosen by
+               another evaluation: the layer is then re-derived from it)
+    Returns (h float64 [n, I] -- the bf16 value when round_h, y float64
+    [n, H], unrounded).
+    """
+    if h_given is not None:
+        h = np.asarray(h_given, dtype=np.float64)
+    else:
+        I = w_gate_up.shape[0] // 2
+        wg = _weights_f64(w_gate_up[:I])
+        wu = _weights_f64(w_gate_up[I:])
+        g = a @ wg.T
+        u = a @ wu.T
+        L = float(np.float32(limit))
+        gc = np.minimum(g, L)                 # gate: bounded above only
+        uc = np.clip(u, -L, L)                # up: bounded on both sides
+        with np.errstate(over="ignore", invalid="ignore"):
+            h = gc / (1.0 + np.exp(-gc)) * uc
+        if round_h:
+            h = bf16_to_f64(bf16_round(h))
     y = h @ _weights_f64(w_down).T
     return h, y
 
 
 def routed_experts(xr_bits: np.ndarray, perm: dict, inp: dict, limit: float,
                    round_h: bool = True,
-                   expert_range: tuple[int, int] | None = None) -> tuple[np.ndarray, np.ndarray]:
+                   expert_range: tuple[int, int] | None = None,
+                   h_given: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
     """S4+S5 over all experts: rows of segment e of the permutation go
     through expert e (weights from expert_weights(inp, e)).  Returns
     (h_perm [T*k, I], y_perm [T*k, H]) float64 in permuted-row order; rows
-    of experts outside `expert_range` stay 0."""
+    of experts outside `expert_range` stay 0.  h_given [T*k, I] (permuted
+    rows) replaces the rounded h, as in swiglu_ffn."""
     offsets = perm["offsets"]
     st = perm["sorted_token"]
     E = offsets.shape[0] - 1
@@ -345,7 +379,8 @@ def routed_experts(xr_bits: np.ndarray, perm: dict, inp: dict, limit: float,
             continue
         a = bf16_to_f64(xr_bits[st[a0:a1]])
         wgu, wd = expert_weights(inp, e)
-        h, y = swiglu_ffn(a, wgu, wd, limit, round_h)
+        hg = None if h_given is None else h_given[a0:a1]
+        h, y = swiglu_ffn(a, wgu, wd, limit, round_h, hg)
         h_perm[a0:a1] = h
         y_perm[a0:a1] = y
     return h_perm, y_perm
@@ -417,7 +452,8 @@ def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
             round_h: bool = True, expert_range: tuple[int, int] | None = None,
             include_shared: bool = True, post_norm: bool = False,
             residual: np.ndarray | None = None, out_scale: float = 1.0,
-            residual_scale: float = 1.0) -> dict:
+            residual_scale: float = 1.0, h_given: np.ndarray | None = None,
+            hs_given: np.ndarray | None = None) -> dict:
     """The whole layer (S0-S7) on one batch.
 
     `inp` holds the arrays named in moe_inputs.generate (x, x_cur,
@@ -430,7 +466,13 @@ def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
     routed slots of experts in [lo, hi) (one expert-parallel rank's share);
     `include_shared` drops the shared expert.  `post_norm` applies the
     post-norm (gamma_post) to a plain layer too; `residual` (bf16 bits
-    [T, H]) adds the finish S8 with the two scales.
+    [T, H]) adds the finish S8 with the two scales.  `h_given` (routed h,
+    [T*k, I] in the permuted-row order of the routing used) and `hs_given`
+    (shared h, [T, I_s]) replace the oracle's own bf16 rounding of h: an h
+    within one bf16 step of the exact value is a valid result wherever the
+    exact value lies within the rounding error of fp32 arithmetic of a
+    rounding midpoint, and the rest of the layer is then re-derived from the
+    rounding another evaluation chose, as for near-tie ids.
 
     Returns a dict with every intermediate: xr, logits, s, s_biased, gap,
     ids, w, offsets, sorted_token, inv_pos, h_perm, y_perm, hs, ys, z,
@@ -462,12 +504,12 @@ def forward(inp: dict, *, k: int, rsf: float, limit: float, scmoe: bool = False,
     p = permute(ids, E)
     res.update(offsets=p["offsets"], sorted_token=p["sorted_token"],
                inv_pos=p["inv_pos"], counts=p["counts"])
-    h_perm, y_perm = routed_experts(xr, p, inp, limit, round_h, expert_range)
+    h_perm, y_perm = routed_experts(xr, p, inp, limit, round_h, expert_range, h_given)
     res["h_perm"], res["y_perm"] = h_perm, y_perm
     ys = None
     if include_shared and inp.get("ws_gate_up") is not None and inp["ws_gate_up"].shape[0] > 0:
         hs, ys = swiglu_ffn(bf16_to_f64(x_sh), inp["ws_gate_up"], inp["ws_down"],
-                            limit, round_h)
+                            limit, round_h, hs_given)
         res["hs"] = hs
     res["ys"] = ys
     z = combine(y_perm, w, p["inv_pos"], ys)

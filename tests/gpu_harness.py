@@ -16,7 +16,17 @@ Parity bar (the layer's tolerances):
     (|d sigma/dl| <= 1/4) plus SIG_ULP ulp of the oracle's weight;
   * offsets, sorted_token and inv_pos bit-exact (against the oracle's
     permutation of the GPU's ids);
-  * outputs |gpu - oracle| <= 2e-2 * max(1, |oracle|) elementwise.
+  * the SwiGLU outputs h (routed and shared, read through the forward's
+    probes) equal the oracle's bf16 rounding, except elements where another
+    rounding is as correct: the GPU's value must be a rounding of a value
+    within the fp32 error bound of the exact one (K u sum|x w| for each
+    K-term dot product carried through the SwiGLU, plus 2^-19 |h| for its
+    exp and reciprocal), and at most 1 % of the elements may differ (count
+    reported);
+  * outputs |gpu - oracle| <= 2e-2 * max(1, |oracle|) elementwise, the
+    oracle re-deriving y, ys and the output from the GPU's validated h (as
+    for near-tie ids); the distance to the oracle's own rounding of h is
+    reported beside it.
 """
 from __future__ import annotations
 
@@ -111,8 +121,12 @@ class Device:
         self.inv_pos = torch.empty(max(N, 1), dtype=torch.int32, device="cuda")
         self.xr = torch.empty((T, H), dtype=torch.int16, device="cuda") if wl.scmoe else None
         self.logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        self.h = torch.empty((max(N, 1), wl.I), dtype=torch.int16, device="cuda")
+        self.hs = (torch.empty((T, wl.I_s), dtype=torch.int16, device="cuda")
+                   if wl.I_s else None)
         self.probes = moe.make_probes(self.ids, self.w, self.offsets, self.sorted_token,
-                                      self.inv_pos, self.xr, self.logits)
+                                      self.inv_pos, self.xr, self.logits, h=self.h,
+                                      h_shared=self.hs)
 
     def canary(self) -> None:
         """Fill every output with NaN / out-of-range bits first, so that an
@@ -142,7 +156,10 @@ class Device:
         r = dict(out=to_bits(self.out), ids=self.ids.cpu().numpy(), w=self.w.cpu().numpy(),
                  offsets=self.offsets.cpu().numpy(),
                  sorted_token=self.sorted_token.cpu().numpy()[:N],
-                 inv_pos=self.inv_pos.cpu().numpy()[:N], logits=self.logits.cpu().numpy())
+                 inv_pos=self.inv_pos.cpu().numpy()[:N], logits=self.logits.cpu().numpy(),
+                 h=to_bits(self.h)[:N])
+        if self.hs is not None:
+            r["hs"] = to_bits(self.hs)
         if self.xr is not None:
             r["xr"] = to_bits(self.xr)
         return r
@@ -194,6 +211,54 @@ def check_router(x_bits, w_router, corr_bias, k, rsf, logits_g, ids_g, w_g) -> d
     return rep
 
 
+H_FAST = 2.0 ** -19   # relative error allowed for the SwiGLU's exp and reciprocal
+
+
+H_FLIP_SHARE = 1e-2   # at most this share of h elements may differ from the oracle's rounding
+
+
+def validate_h(h_gpu: np.ndarray, h_ora: np.ndarray, pre_fn, limit: float, K: int) -> dict:
+    """The GPU's bf16 h against the oracle's rounding (both bit patterns of
+    one [n, I] block).  An element that differs must be a correct rounding of
+    a value within the fp32 error bound of the exact one: |h_gpu - h| <=
+    bound + half a bf16 step of h_gpu, the bound being K u sum|x w| on each
+    dot product carried through the SwiGLU (|silu'| <= 1.1) plus H_FAST |h|
+    (near a rounding midpoint that allows the other neighbour; where the
+    dot products cancel, several steps).  And the share of differing
+    elements must stay below H_FLIP_SHARE (or 16 elements): a systematic
+    defect (a K stage lost, a wrong row) moves most elements by a step or
+    more.  pre_fn(rows,
+    cols) returns the oracle's swiglu_pre for those rows and columns.
+    Returns the count and the largest (distance - half step) / bound."""
+    diff = np.argwhere(h_gpu != h_ora)
+    rep = {"flips": int(len(diff)), "flip_max_over_bound": 0.0}
+    if len(diff) == 0:
+        return rep
+    assert len(diff) <= max(16, H_FLIP_SHARE * h_gpu.size), (
+        f"h differs from the oracle's rounding in {len(diff)} of {h_gpu.size} elements")
+    r, c = diff[:, 0], diff[:, 1]
+    ur, ri = np.unique(r, return_inverse=True)
+    uc, ci = np.unique(c, return_inverse=True)
+    pre = pre_fn(ur, uc)
+    g, u, h = pre["g"][ri, ci], pre["u"][ri, ci], pre["h"][ri, ci]
+    L = float(np.float32(limit))
+    gc, uc_ = np.minimum(g, L), np.clip(u, -L, L)
+    silu = gc / (1.0 + np.exp(-gc))
+    eps = K * U32
+    bound = (1.1 * np.abs(uc_) * eps * pre["gabs"][ri, ci] + np.abs(silu) * eps * pre["uabs"][ri, ci]
+             + H_FAST * np.abs(h))
+    vg = mo.bf16_to_f64(h_gpu[r, c])
+    half_step = np.spacing(np.abs(vg).astype(np.float32)).astype(np.float64) * 2.0 ** 15
+    ratio = (np.abs(vg - h) - half_step) / np.maximum(bound, 1e-300)
+    ok = np.isfinite(vg) & (ratio <= 1.0)
+    rep["flip_max_over_bound"] = float(ratio.max())
+    bad = np.nonzero(~ok)[0]
+    assert bad.size == 0, (
+        f"h differs beyond a valid rounding at {bad.size} of {len(diff)} elements, e.g. "
+        f"{[(int(r[i]), int(c[i]), float(vg[i]), float(h[i]), float(bound[i])) for i in bad[:3]]}")
+    return rep
+
+
 def check_layer(wl, inp: dict, gpu: dict, rows: np.ndarray | None = None,
                 finish: dict | None = None) -> dict:
     """Compare one GPU forward with the oracle.  `rows` = token sample for
@@ -230,10 +295,53 @@ def check_layer(wl, inp: dict, gpu: dict, rows: np.ndarray | None = None,
                   residual=np.asarray(finish["residual"])[rows],
                   out_scale=finish.get("out_scale", 1.0),
                   residual_scale=finish.get("residual_scale", 1.0))
-    res = mo.forward(sub, ids=ids_g[rows], **kw)
-    o_ref = mo.bf16_to_f64(res["out"])
+    ids_sub = ids_g[rows]
+    res = mo.forward(sub, ids=ids_sub, **kw)
     o_gpu = mo.bf16_to_f64(gpu["out"][rows])
     assert np.all(np.isfinite(o_gpu)), "non-finite output (unwritten element?)"
+    o_own = mo.bf16_to_f64(res["out"])
+    d_own = np.abs(o_gpu - o_own) / (OUT_TOL * np.maximum(1.0, np.abs(o_own)))
+    rep["out_max_d_over_tol_oracle_h"] = float(d_own.max()) if d_own.size else 0.0
+    given = {}
+    if "h" in gpu:
+        # the GPU's h rows in the oracle's permuted order for the checked tokens
+        k = wl.k
+        ps = mo.permute(ids_sub, wl.E)
+        src = gpu["inv_pos"].reshape(T, k)[rows].reshape(-1)       # GPU row of (token, slot)
+        h_sub = np.empty((len(rows) * k, wl.I), dtype=np.uint16)
+        h_sub[ps["inv_pos"]] = gpu["h"][src]
+        h_ora = mo.bf16_round(res["h_perm"])
+        xr_sub = res["xr"]
+        offs = ps["offsets"]
+
+        def pre_routed(prow, cols):
+            out = {n: np.zeros((len(prow), len(cols))) for n in ("g", "u", "h", "gabs", "uabs")}
+            e_of = np.searchsorted(offs, prow, side="right") - 1
+            for e in np.unique(e_of):
+                sel = np.nonzero(e_of == e)[0]
+                a = mo.bf16_to_f64(xr_sub[ps["sorted_token"][prow[sel]]])
+                pe = mo.swiglu_pre(a, mo.expert_weights(inp, int(e))[0], wl.limit, cols)
+                for n in out:
+                    out[n][sel] = pe[n]
+            return out
+
+        hv = validate_h(h_sub, h_ora, pre_routed, wl.limit, wl.H)
+        rep["h_flips"], rep["h_flip_max_over_bound"] = hv["flips"], hv["flip_max_over_bound"]
+        given["h_given"] = mo.bf16_to_f64(h_sub)
+        if "hs" in gpu and res.get("hs") is not None:
+            hs_sub = gpu["hs"][rows]
+            x_sh = sub["x_cur"] if wl.scmoe else sub["x"]
+
+            def pre_shared(prow, cols):
+                return mo.swiglu_pre(mo.bf16_to_f64(x_sh[prow]), inp["ws_gate_up"], wl.limit, cols)
+
+            hv = validate_h(hs_sub, mo.bf16_round(res["hs"]), pre_shared, wl.limit, wl.H)
+            rep["hs_flips"] = hv["flips"]
+            rep["hs_flip_max_over_bound"] = hv["flip_max_over_bound"]
+            given["hs_given"] = mo.bf16_to_f64(hs_sub)
+        if rep["h_flips"] or rep.get("hs_flips"):
+            res = mo.forward(sub, ids=ids_sub, **kw, **given)
+    o_ref = mo.bf16_to_f64(res["out"])
     d = np.abs(o_gpu - o_ref) / (OUT_TOL * np.maximum(1.0, np.abs(o_ref)))
     rep["out_max_d_over_tol"] = float(d.max()) if d.size else 0.0
     rep["out_exact_frac"] = float(np.mean(o_gpu == o_ref)) if d.size else 1.0

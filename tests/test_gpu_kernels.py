@@ -108,6 +108,46 @@ def test_router_ties_nan_and_no_bias(tl):
     assert np.all(np.isnan(logits_g[:, 7]))
 
 
+@pytest.mark.parametrize("T,H,E,k", [
+    (32, 4096, 64, 8),     # the decode workload's routing
+    (64, 128, 8, 2),       # tiny
+    (64, 256, 256, 8),     # T * E at the LDS bound, four experts per lane
+    (16, 520, 1024, 16),   # E and k at their bounds, ragged K
+    (1, 64, 3, 3),         # one token, k == E
+])
+def test_fused_routing_matches_separate_calls(tl, T, H, E, k):
+    """moe_forward routes decode-sized batches with one kernel after the
+    router GEMM (partials summed into LDS, wave top-k over the LDS logits,
+    permutation, GEMM schedule); its ids, weights, logits and permutation
+    equal those of moe_router_topk followed by moe_permute bit for bit."""
+    torch, moe = tl
+    gh.note(f"fused routing T={T} H={H} E={E} k={k}")
+    wl = moe_inputs.Workload("route", T=T, H=H, E=E, k=k, I=64, I_s=0, rsf=1.5)
+    inp = moe_inputs.generate(wl, seed=T + E)
+    d = gh.Device(wl, inp)
+    d.canary()
+    d.run()
+    g = d.result()
+    p = d.params
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(p, d.x, d.w_router, d.corr_bias, ids, w, ws)
+    logits = ws[: T * E * 4].view(torch.float32).clone()
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    st = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    ip = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    moe.moe_permute(p, ids, offs, st, ip, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(g["ids"], ids.cpu().numpy())
+    assert np.array_equal(g["w"].view(np.uint32), w.cpu().numpy().view(np.uint32))
+    assert np.array_equal(g["logits"].view(np.uint32),
+                          logits.cpu().numpy().reshape(T, E).view(np.uint32))
+    assert np.array_equal(g["offsets"], offs.cpu().numpy())
+    assert np.array_equal(g["sorted_token"], st.cpu().numpy())
+    assert np.array_equal(g["inv_pos"], ip.cpu().numpy())
+
+
 # ----------------------------------------------------------- permute ----
 
 @pytest.mark.parametrize("T,E,k,skew", [

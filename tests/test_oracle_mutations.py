@@ -22,7 +22,7 @@ def test_unmutated_oracle_matches():
     assert _hand_matches()
 
 
-def _symmetric_clamp(a, w_gate_up, w_down, limit, round_h=True):
+def _symmetric_clamp(a, w_gate_up, w_down, limit, round_h=True, h_given=None):
     I = w_gate_up.shape[0] // 2
     g = a @ mo.bf16_to_f64(w_gate_up[:I]).T
     u = a @ mo.bf16_to_f64(w_gate_up[I:]).T
@@ -33,10 +33,10 @@ def _symmetric_clamp(a, w_gate_up, w_down, limit, round_h=True):
     return h, h @ mo.bf16_to_f64(w_down).T
 
 
-def _swapped_gate_up(a, w_gate_up, w_down, limit, round_h=True):
+def _swapped_gate_up(a, w_gate_up, w_down, limit, round_h=True, h_given=None):
     I = w_gate_up.shape[0] // 2
     sw = np.concatenate([w_gate_up[I:], w_gate_up[:I]])
-    return _real_ffn(a, sw, w_down, limit, round_h)
+    return _real_ffn(a, sw, w_down, limit, round_h, h_given)
 
 
 _real_ffn = mo.swiglu_ffn
