@@ -20,8 +20,9 @@ rows per expert (HBM-bound, weight streaming) it holds the routed experts
 only: moe_forward runs the shared expert on a second stream beside the
 routing kernels.  Otherwise routed and shared experts share the launch.
 Its average duration is measured live with HIP events recorded by
-moe_forward itself on its stream at the boundaries of that step, over every
-timed step.  Algorithmic work per launch:
+moe_forward itself on its stream at the boundaries of that step, on every
+8th timed step (--event-every; an event is a packet in the stream that
+delays the next launch by microseconds, so the other steps run without).  Algorithmic work per launch:
   HBM-bound:  bytes = sum over touched experts of 2*I*H*2 (gate/up weights)
               + T*H*2 (x) + T*k*I*2 (h out)
   MFMA-bound: flops = 2*T*k*H*2I + 2*T*H*2I_s
@@ -80,18 +81,24 @@ def committed_traffic(workload_label: str):
 
 
 class HipEvents:
-    """Raw hipEvent_t handles (the library records them on its own stream)."""
+    """Raw hipEvent_t handles (the library records them on its own stream).
+    They only time: created without the system-scope fence of a default
+    event, whose cache writeback and invalidation at every record would
+    stall the stream between the kernels being timed."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self) -> int:
         ev = ctypes.c_void_p()
-        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed ({rc})")
         return ev.value
@@ -417,6 +424,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle time to spend on the baseline sample (at least)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="time the dominant launch with events on every N-th timed step")
     ap.add_argument("--no-probe-peaks", action="store_true",
                     help="skip measuring this GPU's MFMA and HBM peaks")
     ap.add_argument("--router-backward", action="store_true",
@@ -523,9 +532,16 @@ def main() -> int:
         print("[bench] measuring this GPU's MFMA and HBM peaks", file=sys.stderr, flush=True)
         peaks = measure_peaks(moe, torch)
 
+    # the dominant launch is timed by events that moe_forward records around
+    # it on every `every`-th timed step (each event is a packet in the
+    # stream, which costs the next launch a few microseconds: sampling keeps
+    # them out of most steps); at least one step is timed
+    every = max(1, args.event_every)
+    timed = list(range(0, steps, every))
     hip = HipEvents()
-    evs = [(hip.create(), hip.create()) for _ in range(steps)]
-    probes = [moe.make_probes(events={moe.MOE_EV_PERMUTE: a, moe.MOE_EV_GATE_UP: b}) for a, b in evs]
+    evs = {i: (hip.create(), hip.create()) for i in timed}
+    probes = {i: moe.make_probes(events={moe.MOE_EV_PERMUTE: a, moe.MOE_EV_GATE_UP: b})
+              for i, (a, b) in evs.items()}
 
     print(f"[bench] warmup {warmup}, steps {steps}", file=sys.stderr, flush=True)
     for _ in range(warmup):
@@ -533,12 +549,12 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        forward(probes[i])
+        forward(probes.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
-    gate_up_ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / steps
-    for a, b in evs:
+    gate_up_ms = sum(hip.elapsed_ms(a, b) for a, b in evs.values()) / len(evs)
+    for a, b in evs.values():
         hip.destroy(a)
         hip.destroy(b)
 
@@ -563,14 +579,16 @@ def main() -> int:
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "grouped gate_up + SwiGLU (routed experts; the shared expert "
                               "runs beside the routing kernels on a second stream)",
-                    "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": round(gate_up_ms, 5)}
+                    "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": round(gate_up_ms, 5),
+                    "launches_timed": len(evs)}
     else:
         achieved = gu_flops / (gate_up_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                     "traffic": traffic,
                     "kernel": "grouped gate_up + SwiGLU (routed + shared, one launch)",
-                    "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(gate_up_ms, 5)}
+                    "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(gate_up_ms, 5),
+                    "launches_timed": len(evs)}
     if peaks is not None:
         mp = peaks["hbm_read_gbs"] if hbm_bound else peaks["mfma_bf16_tflops"]
         roofline["measured_peak"] = mp

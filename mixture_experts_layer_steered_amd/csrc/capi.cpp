@@ -225,9 +225,13 @@ moe_status side_stream(SideStream** out) {
     SideStream n;
     if (hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) != hipSuccess)
       return fail(MOE_ERR_DEVICE, "second stream: %s", hipGetErrorString(hipGetLastError()));
-    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join2, hipEventDisableTiming) != hipSuccess)
+    // the events only order work of one device: a device-scope release
+    // (the default system-scope one writes back and invalidates caches for
+    // the host's sake and stalls the queue for microseconds)
+    const unsigned flags = hipEventDisableTiming | hipEventReleaseToDevice;
+    if (hipEventCreateWithFlags(&n.fork, flags) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, flags) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join2, flags) != hipSuccess)
       return fail(MOE_ERR_DEVICE, "stream events: %s", hipGetErrorString(hipGetLastError()));
     S = n;
   }
