@@ -586,7 +586,10 @@ def main() -> int:
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                     "traffic": traffic,
-                    "kernel": "grouped gate_up + SwiGLU (routed + shared, one launch)",
+                    "kernel": ("grouped gate_up + SwiGLU (routed W4A16 experts unpacked in "
+                               "the tile, then the bf16 shared expert: two launches)"
+                               if wl.w4 else
+                               "grouped gate_up + SwiGLU (routed + shared, one launch)"),
                     "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(gate_up_ms, 5),
                     "launches_timed": len(evs)}
     if peaks is not None:

@@ -138,9 +138,12 @@ typedef struct moe_weights {
    * tensor scale multiplies the fp32 GEMM sums, so on every path the
    * results equal the exactly dequantised layer up to fp32 summation order.
    * Decode-sized batches (T*k <= 64*E) stream the codes and unpack them in
-   * registers; larger batches, bound by the matrix cores, first expand the
-   * layer's experts into the workspace as bf16 (exactly; the workspace then
-   * holds E * 3 * I * H bf16 more) and run the bf16 grouped GEMMs. */
+   * registers; prefill-sized ones (T*k >= 512*E) stage the codes and scales
+   * in LDS and unpack them there, a stage ahead of the MFMAs, inside the
+   * grouped GEMM; batches in between (or a tile variant forced through
+   * MOE_GEMM_VARIANT) first expand the layer's experts into the workspace
+   * as bf16 (exactly; the workspace then holds E * 3 * I * H bf16 more) and
+   * run the bf16 grouped GEMMs. */
   const uint8_t* w_gate_up_q;       /* [E, 2I, H/2] codes; NULL = bf16 experts    */
   const uint8_t* w_gate_up_scale;   /* [E, H/128, 2I] E4M3                        */
   const uint8_t* w_down_q;          /* [E, H, I/2] codes                          */
@@ -186,7 +189,7 @@ enum {
   MOE_EV_PRENORM = 1,  /* ScMoE pre-norm                                    */
   MOE_EV_ROUTER = 2,   /* router logits + top-k                             */
   MOE_EV_PERMUTE = 3,  /* permutation + grouped-GEMM tile schedule (and, for */
-                       /* W4A16 experts beyond weight streaming, the wait   */
+                       /* W4A16 experts expanded in the workspace, the wait */
                        /* for the gate_up weights' dequantisation)          */
   MOE_EV_GATE_UP = 4,  /* grouped gate_up + SwiGLU (routed and shared)      */
   MOE_EV_DOWN = 5,     /* grouped down projection (routed and shared)       */

@@ -152,9 +152,23 @@ struct Layout {
   size_t bytes;
 };
 
-// W4A16 batches with more than 64 rows per expert dequantise the experts
-// first (the same threshold as pick_variant's weight streaming)
-bool w4_dequant_batch(const moe_params& p) { return p.w4 && p.T * p.k > (int64_t)64 * p.E; }
+// The tile variant of the layer's expert GEMMs (routed and shared).
+GemmVariant layer_variant(const moe_params& p) {
+  const int64_t N = p.T * p.k;
+  return pick_variant(N, p.E, std::max<int64_t>(N, p.T) * std::max(p.H, std::max(p.I, p.I_shared)),
+                      (int64_t)2 * std::max(p.I, p.I_shared) * p.H,
+                      p.H % 32 == 0 && p.I % 32 == 0 && p.I_shared % 32 == 0);
+}
+
+// W4A16 routed experts are read as codes by the weight-streaming and
+// ping-pong kernels; the other tile variants (forced by MOE_GEMM_VARIANT, or
+// the 128-row tiles of mid-sized batches) read them dequantised to bf16 in
+// the workspace.
+bool w4_dequant_batch(const moe_params& p) {
+  if (!p.w4) return false;
+  const GemmVariant v = layer_variant(p);
+  return v != GemmVariant::kWStream && v != GemmVariant::kPingPong;
+}
 
 Layout carve(const moe_params& p, void* ws) {
   Carver c;
@@ -517,18 +531,11 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     OPTIONAL_PTR(probes->y_shared);
   }
   const int64_t T = p->T, N = T * p->k;
-  const GemmVariant v = pick_variant(
-      N, p->E, std::max<int64_t>(N, T) * std::max(p->H, std::max(p->I, p->I_shared)),
-      (int64_t)2 * std::max(p->I, p->I_shared) * p->H,
-      p->H % 32 == 0 && p->I % 32 == 0 && p->I_shared % 32 == 0);
-  // W4A16: weight streaming unpacks the codes in its kernel; the tiled
-  // kernels read the experts dequantised into the workspace
-  const bool w4_stream = w4 && v == GemmVariant::kWStream;
-  const bool w4_deq = w4 && !w4_stream;
-  if (w4_deq && !w4_dequant_batch(*p))
-    return fail(MOE_ERR_UNSUPPORTED,
-                "W4A16 experts with at most 64 rows per expert run on the weight-streaming "
-                "kernels (MOE_GEMM_VARIANT forces another)");
+  const GemmVariant v = layer_variant(*p);
+  // W4A16: weight streaming and the ping-pong tile unpack the codes in their
+  // kernels; the other tiles read the experts dequantised into the workspace
+  const bool w4_codes = w4 && (v == GemmVariant::kWStream || v == GemmVariant::kPingPong);
+  const bool w4_deq = w4 && !w4_codes;
   Layout L = carve(*p, ws);
   if (ws_bytes < L.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.bytes);
   if (probes) {
@@ -560,7 +567,7 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     gu.W = L.deq_gu;
     dn.W = L.deq_dn;
   }
-  if (w4_stream) {  // packed codes (uint16 units between experts) and group-major scales
+  if (w4_codes) {  // packed codes (uint16 units between experts) and group-major scales
     gu.W = reinterpret_cast<const uint16_t*>(w->w_gate_up_q);
     gu.w_stride = (int64_t)2 * p->I * p->H / 4;
     gu.S = w->w_gate_up_scale;
@@ -569,8 +576,10 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     dn.w_stride = (int64_t)p->H * p->I / 4;
     dn.S = w->w_down_scale;
     dn.s_stride = (int64_t)(p->I / 128) * p->H;
-    gu.ntiles = (p->I + gemm_w4_tile_n(true) - 1) / gemm_w4_tile_n(true);
-    dn.ntiles = (p->H + gemm_w4_tile_n(false) - 1) / gemm_w4_tile_n(false);
+    if (v == GemmVariant::kWStream) {  // its own tile width; the ping-pong tile keeps the bf16 one
+      gu.ntiles = (p->I + gemm_w4_tile_n(true) - 1) / gemm_w4_tile_n(true);
+      dn.ntiles = (p->H + gemm_w4_tile_n(false) - 1) / gemm_w4_tile_n(false);
+    }
   }
   GemmProblem sgu = make_problem(xs, nullptr, nullptr, nullptr, w->ws_gate_up, 0, L.hs, T, 1,
                                  p->I_shared, p->H, v, true);
@@ -675,10 +684,17 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
       (s = device_status(hipStreamWaitEvent(stream, side->join, 0), "join")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_PERMUTE)) != MOE_OK) return s;
-  const bool one_launch = shared && !beside;  // routed and shared problems together
+  // routed and shared problems in one launch; W4A16 routed experts read as
+  // codes take a launch of their own, and the bf16 shared expert follows
+  const bool one_launch = shared && !beside && !w4_codes;
+  const bool after = shared && !beside && w4_codes;
   if ((s = device_status(launch_grouped_gemm(v, true, gu, one_launch ? &sgu : nullptr,
                                              p->swiglu_limit, stream),
                          "gate_up")) != MOE_OK)
+    return s;
+  if (after && (s = device_status(launch_grouped_gemm(v, true, sgu, nullptr, p->swiglu_limit,
+                                                      stream),
+                                  "shared gate_up")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_GATE_UP)) != MOE_OK) return s;
   if (deq_side &&
@@ -687,6 +703,10 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   if ((s = device_status(launch_grouped_gemm(v, false, dn, one_launch ? &sdn : nullptr,
                                              p->swiglu_limit, stream),
                          "down")) != MOE_OK)
+    return s;
+  if (after && (s = device_status(launch_grouped_gemm(v, false, sdn, nullptr, p->swiglu_limit,
+                                                      stream),
+                                  "shared down")) != MOE_OK)
     return s;
   if ((s = mark(MOE_EV_DOWN)) != MOE_OK) return s;
   if (beside &&

@@ -29,12 +29,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 // OCP FP8 E4M3 byte -> fp32 (exact).  Bit 7 sign, bits 6..3 exponent field
 // (bias 7), bits 2..0 mantissa; field 0 holds the subnormals m * 2^-9; the
-// all-ones magnitude 0x7F is NaN (the format has no infinities).
+// all-ones magnitude 0x7F is NaN (the format has no infinities).  One
+// formula for both kinds, without branches: (8 [field > 0] + m) *
+// 2^(max(field, 1) - 10), the integer converted exactly and scaled by ldexp.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   const uint32_t field = (b >> 3) & 15u, m = b & 7u;
-  float mag = field == 0 ? (float)m * 0x1p-9f : __uint_as_float(((field + 120u) << 23) | (m << 20));
-  if ((b & 0x7Fu) == 0x7Fu) mag = __uint_as_float(0x7FC00000u);
-  return (b & 0x80u) ? -mag : mag;
+  const float mag = __builtin_amdgcn_ldexpf((float)(m + 8u * min(field, 1u)),
+                                            (int)max(field, 1u) - 10);
+  const uint32_t bits = (b & 0x7Fu) == 0x7Fu ? 0x7FC00000u : __float_as_uint(mag);
+  return __uint_as_float(bits | ((b & 0x80u) << 24));
 }
 
 // Clamped SwiGLU on fp32 pre-activations: the gate is bounded from above

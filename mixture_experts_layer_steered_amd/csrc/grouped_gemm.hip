@@ -293,6 +293,8 @@ __device__ __forceinline__ void lds_buffer_16(__amdgpu_buffer_rsrc_t rsrc, uint3
 // its LDS reads and writes have completed.
 #define PL_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0070)
 #define PL_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+// lgkmcnt(0) alone: this wave's LDS reads and writes have completed
+#define PL_WAIT_LDS() __builtin_amdgcn_s_waitcnt(0xC07F)
 // vmcnt(n) with lgkmcnt(m), m < 16: all but this wave's m newest LDS
 // operations have completed (they complete in order)
 #define PL_WAIT_VM_LDS_N(n, m) \
@@ -360,10 +362,12 @@ struct PipeTile {
 // fetch the tile's first row (their products reach only outputs never
 // stored).  Offsets are 32-bit: A and one group's weights hold fewer than
 // 2^31 elements (the host checks).
+//
+// pipe_coords: the tile's rows, first column, output scale and A resource;
+// returns its group.
 template <class S>
-__device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, int tile,
-                                            PipeTile<S>& T) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int pipe_coords(const GemmProblem& P, int mt_total, int tile,
+                                           PipeTile<S>& T) {
   int g = 0, ms = 0, mc = mt_total;
   if (P.group_offsets != nullptr) {
     int lo = 0, hi = P.G - 1;  // last g with mtile_start[g] * ntiles <= tile
@@ -386,6 +390,26 @@ __device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, 
   T.n0 = nt * S::BN;
   T.ts = P.tscale ? P.tscale[g] : 1.0f;
   T.rs_a = pl_rsrc(P.A);
+  return g;
+}
+
+// Byte offset of the A piece that lane `lane` of load instruction i of wave
+// `wave` fetches (its row clamped to the tile's first row past the segment).
+template <class S>
+__device__ __forceinline__ uint32_t pipe_a_off(const GemmProblem& P, const PipeTile<S>& T, int i,
+                                               int wave, int lane) {
+  const int row = S::RPI * (wave + S::NW * i) + lane / S::CHUNKS;
+  const int chunk = pl_swz<S::KB>(row, lane % S::CHUNKS);
+  const int64_t gr = T.row0 + row < T.row_end ? T.row0 + row : T.row0;
+  const int64_t a_row = P.row_index ? (int64_t)P.row_index[gr] : gr;
+  return (uint32_t)((a_row * P.K + chunk * 8) * 2);
+}
+
+template <class S>
+__device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, int tile,
+                                            PipeTile<S>& T) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = pipe_coords<S>(P, mt_total, tile, T);
   T.rs_w = pl_rsrc(P.W + (int64_t)g * P.w_stride);
   const int K = P.K, N = P.N;
 #pragma unroll
@@ -393,9 +417,7 @@ __device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, 
     const int row = S::RPI * (wave + S::NW * i) + lane / S::CHUNKS;
     const int chunk = pl_swz<S::KB>(row, lane % S::CHUNKS);
     if (i < S::A_INSTR) {
-      const int64_t gr = T.row0 + row < T.row_end ? T.row0 + row : T.row0;
-      const int64_t a_row = P.row_index ? (int64_t)P.row_index[gr] : gr;
-      T.off[i] = (uint32_t)((a_row * K + chunk * 8) * 2);
+      T.off[i] = pipe_a_off<S>(P, T, i, wave, lane);
     } else {
       const int r = row - S::BM;
       int n = S::GATEUP ? T.n0 + (r < S::BN ? r : r - S::BN) : T.n0 + r;
@@ -474,12 +496,12 @@ __device__ __forceinline__ f32x16_t pipe_mfma(const bf16x8_t& w, const bf16x8_t&
 // per register, turned into four adjacent columns of one row by a quad
 // transpose (lane 4a+b: row 8*g + 4*(L/32) + b, columns 4a..4a+3 of the
 // block, for each group g of four registers).
+// (wm, wn): the wave's row half and column block of the tile.
 template <class S>
 __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<S>& T,
                                            const f32x16_t (&acc)[S::NMAT][S::TM][S::TN],
-                                           float limit) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
+                                           float limit, int wm, int wn) {
+  const int lane = threadIdx.x & 63;
   const int N = P.N;
   if constexpr (S::GATEUP) {
 #pragma unroll
@@ -672,7 +694,7 @@ __device__ __forceinline__ void pipe_tile(const GemmProblem& P, int mt_total, in
   // the re-fetches past the end of K landed: nothing of this tile is still
   // in flight into LDS when the next tile refills the slots
   PL_WAIT_VM(0);
-  pipe_store<S>(P, T, acc, limit);
+  pipe_store<S>(P, T, acc, limit, wm, wn);
 }
 
 template <int BM>
@@ -839,10 +861,296 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
       slot = slot + 1 == STAGES ? 0 : slot + 1;
       slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
     }
-    pipe_store<S>(t < R.tiles0 ? p0 : p1, cur, acc, limit);
+    pipe_store<S>(t < R.tiles0 ? p0 : p1, cur, acc, limit, wm, wn);
     if (!more) break;
     t = t_next;
     nk = stages_of(t);
+    cur = nxt;
+  }
+  // pairs with group 1's last barrier
+  if (group == 0) pp_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong tile with W4A16 weights (long expert segments: the grouped
+// W4A16 expert GEMM of "Module glm5next_mlp", in this library's format --
+// see the weight-streaming W4A16 kernel below for the code and scale
+// layout).
+//
+// The bf16 ping-pong above with the weights read as 4-bit codes and
+// dequantised inside the tile.  A stage slot holds the stage's A rows, the
+// tile's NB weight rows of codes (16 bytes per row: the stage's 32 columns)
+// and one E4M3 scale byte per weight row (its 128-column group), about a
+// quarter of the bf16 weight bytes.  The two wave groups split the tile by
+// columns here, not by rows: group g owns output columns
+// [g BN/2, (g+1) BN/2) (wave w: column block 2 (w/4) + w%2 of four, row half
+// (w/2)%2), so it needs only its own half of the weight rows.  In its compute
+// phase of stage s a group dequantises its half of stage s+1 into a two-slot
+// bf16 ring -- one fma per weight, (128 + u) s - 136 s = (u - 8) s, exact in
+// fp32 and, with at most 8 significant bits, exact as the bf16 that its
+// upper half is -- between its MFMAs; the barrier that ends the phase makes
+// the ring slot visible to the group's memory phase of stage s+1, which reads
+// the weight fragments from the ring.  A ring slot is written in the compute
+// phase of stage s-1 and read in the memory phase of stage s, both by the
+// same group, and rewritten only after the next memory phase has read the
+// other slot, so two slots suffice.  Every wave issues three load
+// instructions per stage: two of A, and one of its group's codes (waves
+// 4g, 4g+1: 64 weight rows each) or scales (waves 4g+2, 4g+3: four lanes,
+// 64 weight rows each).  The tensor scale multiplies the accumulators in the
+// epilogue.  K must be a multiple of 128.
+template <class S>
+struct PpW4Layout {
+  static constexpr int A_BYTES = S::BM * S::KB * 2;
+  static constexpr int C_ROW = S::KB / 2;  // code bytes per weight row and stage
+  static constexpr int C_BYTES = S::NB * C_ROW;
+  static constexpr int STAGE = A_BYTES + C_BYTES + S::NB;  // + a scale byte per weight row
+  static constexpr int RING = S::NB * S::KB * 2;           // one stage of bf16 weights
+  static constexpr int HALF = S::NB / 2;                   // weight rows per wave group
+  static constexpr int VM_STAGE = S::A_INSTR + 1;          // load instructions per wave and stage
+  static_assert(S::KB == 32 && C_ROW == 16, "one 16-byte code piece per weight row and stage");
+  static_assert(HALF == 128 && STAGE % 16 == 0, "two waves x 64 code rows per group");
+};
+
+// Wave w's tile position in the column split: (row half, column block).
+__device__ __forceinline__ int pp_w4_wm(int wave) { return (wave >> 1) & 1; }
+__device__ __forceinline__ int pp_w4_wn(int wave) { return 2 * (wave >> 2) + (wave & 1); }
+
+// Tile t: the A offsets as in the bf16 tile; off[A_INSTR] is the byte offset
+// of this wave's codes (one 16-byte piece per lane: weight row 64 (w%2) +
+// lane of its group's half) or scales (lane < 4: the 16 bytes of rows
+// 16 lane .. +15 of the same 64), from rs_w; rows past N read row n0.
+template <class S>
+__device__ __forceinline__ void pp_w4_locate(const GemmProblem& P, int mt_total, int tile,
+                                             int wave, PipeTile<S>& T) {
+  using L = PpW4Layout<S>;
+  const int lane = threadIdx.x & 63;
+  const int g = pipe_coords<S>(P, mt_total, tile, T);
+#pragma unroll
+  for (int i = 0; i < S::A_INSTR; ++i) T.off[i] = pipe_a_off<S>(P, T, i, wave, lane);
+  const int grp = wave >> 2, q = wave & 3, hq = q & 1;
+  const int r_in = q < 2 ? lane : 16 * lane;
+  // gate_up: a group's half is BN/2 gate rows (hq = 0) and the matching up
+  // rows (hq = 1); down: 128 consecutive rows
+  int n = S::GATEUP ? T.n0 + (S::BN / 2) * grp + r_in : T.n0 + L::HALF * grp + 64 * hq + r_in;
+  if (n >= P.N) n = T.n0;
+  const int64_t wr = S::GATEUP && hq ? (int64_t)P.N + n : n;
+  if (q < 2) {
+    T.rs_w = pl_rsrc(reinterpret_cast<const uint8_t*>(P.W) + (int64_t)g * P.w_stride * 2);
+    T.off[S::A_INSTR] = (uint32_t)(wr * (P.K / 2));
+  } else {
+    T.rs_w = pl_rsrc(P.S + (int64_t)g * P.s_stride);
+    T.off[S::A_INSTR] = (uint32_t)wr;
+  }
+}
+
+// This wave's loads of stage k0 of tile T into stage slot `slot`; wr_total
+// is the weight rows of one group (gate_up 2N, down N): the scale rows of
+// one 128-column group.
+template <class S>
+__device__ __forceinline__ void pp_w4_issue(const PipeTile<S>& T, uint8_t* smem, int slot, int k0,
+                                            int wave, int wr_total) {
+  using L = PpW4Layout<S>;
+  const int lane = threadIdx.x & 63;
+  uint8_t* base = smem + slot * L::STAGE;
+#pragma unroll
+  for (int i = 0; i < S::A_INSTR; ++i)
+    lds_buffer_16(T.rs_a, T.off[i], (uint32_t)k0 * 2,
+                  reinterpret_cast<uint16_t*>(base + (wave + S::NW * i) * S::RPI * S::KB * 2));
+  const int grp = wave >> 2, q = wave & 3;
+  const int crow = L::HALF * grp + 64 * (q & 1);  // the wave's first row in the slot's order
+  if (q < 2)
+    lds_buffer_16(T.rs_w, T.off[S::A_INSTR], (uint32_t)k0 / 2,
+                  reinterpret_cast<uint16_t*>(base + L::A_BYTES + crow * L::C_ROW));
+  else if (lane < 4)
+    lds_buffer_16(T.rs_w, T.off[S::A_INSTR], (uint32_t)(k0 / 128) * (uint32_t)wr_total,
+                  reinterpret_cast<uint16_t*>(base + L::A_BYTES + L::C_BYTES + crow));
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Two weights (u - 8) s as one bf16 pair, from bytes j and j+1 of `nib`
+// (a code in the low nibble of each; sel0 and sel1 pick them): each code
+// becomes the fp32 128 + u (0x43 high byte, the code in the next byte), one
+// fma with c = -136 s gives (u - 8) s exactly, and its upper half is the
+// bf16 value; the pack takes the two upper halves.
+__device__ __forceinline__ uint32_t w4_dequant2(uint32_t nib, uint32_t sel0, uint32_t sel1,
+                                                float s, float c) {
+  const float f0 = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x43434343u, nib, sel0)), s, c);
+  const float f1 = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x43434343u, nib, sel1)), s, c);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0),
+                               0x07060302u);
+}
+// byte j of a nibble word into byte 2 of an fp32 whose byte 3 is 0x43
+constexpr uint32_t W4_SEL0 = 0x04000C0Cu, W4_SEL1 = 0x04010C0Cu, W4_SEL2 = 0x04020C0Cu,
+                   W4_SEL3 = 0x04030C0Cu;
+
+// MFMAs LO .. HI-1 of a stage, numbered in the order (substep, matrix,
+// column block, row block): the two substeps' products into one accumulator
+// are eight apart.
+template <class S, int LO, int HI>
+__device__ __forceinline__ void pp_mfma_range(f32x16_t (&acc)[S::NMAT][S::TM][S::TN],
+                                              const bf16x8_t (&fa)[2][S::TM],
+                                              const bf16x8_t (&fb)[2][S::NMAT][S::TN]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int m = 0; m < S::NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < S::TN; ++j)
+#pragma unroll
+        for (int i = 0; i < S::TM; ++i) {
+          const int n = ((s * S::NMAT + m) * S::TN + j) * S::TM + i;
+          if (n >= LO && n < HI) acc[m][i][j] = pipe_mfma<S>(fb[s][m][j], fa[s][i], acc[m][i][j]);
+        }
+}
+
+template <class S, int STAGES>
+__global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProblem p0,
+                                                                      float limit) {
+  static_assert(S::NW == 8 && S::WAVES_M == 2 && S::KB == 32, "ping-pong shape");
+  using L = PpW4Layout<S>;
+  constexpr int KB = S::KB, BN = S::BN;
+  constexpr int TM = S::TM, TN = S::TN, NMAT = S::NMAT, WM = S::WM, WN = S::WN;
+  constexpr int AHEAD = STAGES - 1;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
+  uint8_t* smem = reinterpret_cast<uint8_t*>(smem_dyn);
+  uint16_t* ring = reinterpret_cast<uint16_t*>(smem + STAGES * L::STAGE);
+  GemmProblem unused = p0;
+  const PipeRange R = pipe_range<S::BM>(p0, unused, 0);
+  int t = R.t_first;
+  if (t >= R.t_end) return;  // no tile for this workgroup (uniform)
+
+  const int lane = threadIdx.x & 63;
+  // the wave index and group in scalar registers: barriers are only ever
+  // skipped by whole wavefronts, and the LDS bases of the loads are uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = wave >> 2;
+  const int wm = pp_w4_wm(wave), wn = pp_w4_wn(wave);
+  const int wr_total = S::GATEUP ? 2 * p0.N : p0.N;
+  const int nk = p0.K / KB;
+
+  // this lane's share of its group's dequantisation: weight row rho of the
+  // half (slot order), columns 16 h .. 16 h + 15 of the stage
+  const int gl = (wave & 3) * 64 + lane;
+  const int rho = gl >> 1, h = gl & 1;
+  const int crow = L::HALF * group + rho;
+  const int rrow = S::GATEUP ? (rho >> 6) * BN + (BN / 2) * group + (rho & 63)
+                             : L::HALF * group + rho;
+  const int rpos0 = rrow * KB + pl_swz<KB>(rrow, 2 * h) * 8;
+  const int rpos1 = rrow * KB + pl_swz<KB>(rrow, 2 * h + 1) * 8;
+
+  f32x16_t acc[NMAT][TM][TN];
+  bf16x8_t fa[2][TM], fb[2][NMAT][TN];
+  auto read_stage = [&](int slot, int rslot) __attribute__((always_inline)) {
+    const uint16_t* As = reinterpret_cast<const uint16_t*>(smem + slot * L::STAGE);
+    const uint16_t* Bs = ring + rslot * (L::RING / 2);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int chunk = s * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 32 + (lane & 31);
+        fa[s][i] = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + pl_swz<KB>(r, chunk) * 8]);
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int r = m * BN + wn * WN + j * 32 + (lane & 31);
+          fb[s][m][j] = *reinterpret_cast<const bf16x8_t*>(&Bs[r * KB + pl_swz<KB>(r, chunk) * 8]);
+        }
+    }
+  };
+  // Dequantise this group's half of the stage in `slot` into ring slot
+  // `rslot`.  In a compute phase (mfma set) the stage's 16 MFMAs go around
+  // it in a fixed order of issue: the two LDS reads, three MFMAs while they
+  // land, then one piece of the unpacking after each MFMA -- the scale, then
+  // two columns at a time (five VALU instructions), a ring write after each
+  // eight columns.  An MFMA holds the matrix pipe for 32 cycles, longer than
+  // a piece takes to issue, so the pipe is never left waiting for the ALU.
+  auto dequant = [&](int slot, int rslot, bool mfma) __attribute__((always_inline)) {
+    static_assert(2 * NMAT * TM * TN == 16, "16 MFMAs per stage");
+    const uint8_t* st = smem + slot * L::STAGE;
+    const uint2_t cw = *reinterpret_cast<const uint2_t*>(st + L::A_BYTES + crow * L::C_ROW + 8 * h);
+    const uint32_t sb = st[L::A_BYTES + L::C_BYTES + crow];
+    uint16_t* rs = ring + rslot * (L::RING / 2);
+#define PPW4_MFMA(lo, hi)                          \
+    if (mfma) {                                    \
+      __builtin_amdgcn_sched_barrier(0);           \
+      pp_mfma_range<S, lo, hi>(acc, fa, fb);       \
+      __builtin_amdgcn_sched_barrier(0);           \
+    }
+    PPW4_MFMA(0, 3)
+    const float sc = e4m3_to_f32(sb);
+    PPW4_MFMA(3, 4)
+    const float cc = -136.0f * sc;
+    const uint32_t n0 = cw[0] & 0x0F0F0F0Fu;
+    const uint32_t p0 = w4_dequant2(n0, W4_SEL0, W4_SEL1, sc, cc);
+    PPW4_MFMA(4, 5)
+    const uint32_t p1 = w4_dequant2(n0, W4_SEL2, W4_SEL3, sc, cc);
+    const uint32_t n1 = (cw[0] >> 4) & 0x0F0F0F0Fu;
+    PPW4_MFMA(5, 6)
+    const uint32_t p2 = w4_dequant2(n1, W4_SEL0, W4_SEL1, sc, cc);
+    PPW4_MFMA(6, 7)
+    const uint32_t p3 = w4_dequant2(n1, W4_SEL2, W4_SEL3, sc, cc);
+    *reinterpret_cast<u32x4_t*>(rs + rpos0) = u32x4_t{p0, p1, p2, p3};
+    PPW4_MFMA(7, 8)
+    const uint32_t n2 = cw[1] & 0x0F0F0F0Fu;
+    const uint32_t p4 = w4_dequant2(n2, W4_SEL0, W4_SEL1, sc, cc);
+    PPW4_MFMA(8, 9)
+    const uint32_t p5 = w4_dequant2(n2, W4_SEL2, W4_SEL3, sc, cc);
+    const uint32_t n3 = (cw[1] >> 4) & 0x0F0F0F0Fu;
+    PPW4_MFMA(9, 10)
+    const uint32_t p6 = w4_dequant2(n3, W4_SEL0, W4_SEL1, sc, cc);
+    PPW4_MFMA(10, 11)
+    const uint32_t p7 = w4_dequant2(n3, W4_SEL2, W4_SEL3, sc, cc);
+    *reinterpret_cast<u32x4_t*>(rs + rpos1) = u32x4_t{p4, p5, p6, p7};
+    PPW4_MFMA(11, 16)
+#undef PPW4_MFMA
+  };
+  auto pp_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    pl_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  PipeTile<S> cur, nxt;
+  pp_w4_locate<S>(p0, R.mt0, t, wave, cur);
+#pragma unroll
+  for (int s0 = 0; s0 < AHEAD; ++s0) pp_w4_issue<S>(cur, smem, s0, s0 * KB, wave, wr_total);
+  PL_WAIT_VM_LDS((AHEAD - 1) * L::VM_STAGE);
+  pp_barrier();  // stage 0 landed everywhere
+  dequant(0, 0, false);
+  PL_WAIT_LDS();
+  pp_barrier();  // its weights in ring slot 0
+  if (group) pp_barrier();
+  int slot = 0, slot_issue = AHEAD, rslot = 0;
+  for (;;) {
+    const int t_next = t + R.stride;
+    const bool more = t_next < R.t_end;
+    if (more) pp_w4_locate<S>(p0, R.mt0, t_next, wave, nxt);
+    pipe_zero<S>(acc);
+    for (int kt = 0; kt < nk; ++kt) {
+      read_stage(slot, rslot);
+      const int ka = kt + AHEAD;
+      if (ka < nk)
+        pp_w4_issue<S>(cur, smem, slot_issue, ka * KB, wave, wr_total);
+      else if (more)
+        pp_w4_issue<S>(nxt, smem, slot_issue, (ka - nk) * KB, wave, wr_total);
+      else
+        pp_w4_issue<S>(cur, smem, slot_issue, (nk - 1) * KB, wave, wr_total);
+      PL_WAIT_VM_LDS((AHEAD - 1) * L::VM_STAGE);
+      pp_barrier();
+      slot = slot + 1 == STAGES ? 0 : slot + 1;
+      rslot ^= 1;
+      dequant(slot, rslot, true);  // the next stage of the stream, beside this one's MFMAs
+      PL_WAIT_LDS();
+      pp_barrier();
+      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
+    }
+    pipe_store<S>(p0, cur, acc, limit, wm, wn);
+    if (!more) break;
+    t = t_next;
     cur = nxt;
   }
   // pairs with group 1's last barrier
@@ -1207,6 +1515,8 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
 // the launched shape: 256 weight rows by 256 columns a stage, eight
 // wavefronts, three stages
 constexpr int W4_NBLK = 2, W4_KB = 256, W4_NW = 8, W4_STAGES = 3;
+// stage slots of the W4A16 ping-pong tile
+constexpr int W4_PP_STAGES = 5;
 
 template <int NBLK, int KB, int NW>
 struct W4Shape {
@@ -1529,6 +1839,24 @@ hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
   return hipGetLastError();
 }
 
+template <bool GATEUP, int STAGES>
+hipError_t launch_pp_w4(const GemmProblem& a, float limit, hipStream_t stream) {
+  using S = PipeShape<256, GATEUP ? 128 : 256, GATEUP, 32, 8, 2>;
+  const size_t lds = (size_t)STAGES * PpW4Layout<S>::STAGE + 2 * PpW4Layout<S>::RING;
+  static_assert((size_t)STAGES * PpW4Layout<S>::STAGE + 2 * PpW4Layout<S>::RING <= 160 * 1024,
+                "LDS");
+  auto kern = grouped_pp_w4_kernel<S, STAGES>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3(S::NW * 64), lds, stream, a, limit);
+  return hipGetLastError();
+}
+
 template <bool GATEUP, int KB, int STAGES>
 hipError_t launch_wstream(const GemmProblem& a, const GemmProblem* b, float limit,
                           hipStream_t stream, int max_wgs) {
@@ -1648,9 +1976,14 @@ hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, in
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                const GemmProblem* b, float limit, hipStream_t stream,
                                int max_wgs) {
-  if (a.S != nullptr) {  // W4A16 weights: weight streaming, one problem per launch
-    if (v != GemmVariant::kWStream || b != nullptr || a.K % 128 != 0)
-      return hipErrorInvalidValue;
+  if (a.S != nullptr) {  // W4A16 weights: one problem per launch
+    if (b != nullptr || a.K % 128 != 0) return hipErrorInvalidValue;
+    if (v == GemmVariant::kPingPong) {  // long segments: the ping-pong tile, 5 stages
+      if (a.K < 4 * 32 || a.N % 32 != 0) return hipErrorInvalidValue;
+      if (gateup) return launch_pp_w4<true, W4_PP_STAGES>(a, limit, stream);
+      return launch_pp_w4<false, W4_PP_STAGES>(a, limit, stream);
+    }
+    if (v != GemmVariant::kWStream) return hipErrorInvalidValue;
     if (gateup)
       return launch_wstream_w4<true, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);
     return launch_wstream_w4<false, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);

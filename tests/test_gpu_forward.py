@@ -235,6 +235,19 @@ def test_forward_w4(name):
     assert rep["rows_checked"] == wl.T
 
 
+@pytest.mark.parametrize("variant", ["pingpong", "tile128", "pipe256w8"])
+@pytest.mark.parametrize("name", ["w4_small", "w4_multi", "w4_clamp"])
+def test_forward_w4_tile_variant(monkeypatch, variant, name):
+    """W4A16 layers on the tiled variants, forced on decode-sized batches:
+    the ping-pong tile unpacks the codes itself (mostly empty 256-row tiles,
+    one or two n-tiles), the others read the experts dequantised in the
+    workspace."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT", variant)
+    wl = W4[name]
+    rep, _, _ = run_and_check(wl, moe_inputs.generate(wl, seed=4))
+    assert rep["rows_checked"] == wl.T
+
+
 def test_forward_decode_w4_full():
     rep = _full("decode_w4", None)
     assert rep["rows_checked"] == 32
@@ -332,8 +345,14 @@ def test_forward_prefill_finish_full_sampled():
 W4_TILED = {
     # ~300 rows per expert: the LDS-tiled GEMM on the dequantised experts
     "w4_tiled": Workload("w4_tiled", T=600, H=256, E=4, k=2, I=256, I_s=128, w4=True),
-    # ~2400 rows per expert: the ping-pong GEMM; no shared expert
+    # ~2400 rows per expert: the ping-pong GEMM on the codes; no shared
+    # expert; down K = 128 (four stages, the fewest it takes), down N = 384
+    # (a half-empty last column tile)
     "w4_pingpong": Workload("w4_pingpong", T=2400, H=384, E=4, k=2, I=128, I_s=0, w4=True),
+    # 4096 rows per expert: two or more tiles per workgroup in both
+    # projections (the stage stream runs across tiles), shared expert after
+    "w4_pingpong_multi": Workload("w4_pingpong_multi", T=8192, H=512, E=8, k=4, I=512, I_s=256,
+                                  w4=True),
 }
 
 
