@@ -164,10 +164,11 @@ GemmVariant layer_variant(const moe_params& p) {
 // ping-pong kernels; the other tile variants (forced by MOE_GEMM_VARIANT, or
 // the 128-row tiles of mid-sized batches) read them dequantised to bf16 in
 // the workspace.
+bool w4_codes_variant(const moe_params&, GemmVariant v) {
+  return v == GemmVariant::kWStream || v == GemmVariant::kPingPong;
+}
 bool w4_dequant_batch(const moe_params& p) {
-  if (!p.w4) return false;
-  const GemmVariant v = layer_variant(p);
-  return v != GemmVariant::kWStream && v != GemmVariant::kPingPong;
+  return p.w4 && !w4_codes_variant(p, layer_variant(p));
 }
 
 Layout carve(const moe_params& p, void* ws) {
@@ -534,7 +535,7 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   const GemmVariant v = layer_variant(*p);
   // W4A16: weight streaming and the ping-pong tile unpack the codes in their
   // kernels; the other tiles read the experts dequantised into the workspace
-  const bool w4_codes = w4 && (v == GemmVariant::kWStream || v == GemmVariant::kPingPong);
+  const bool w4_codes = w4 && w4_codes_variant(*p, v);
   const bool w4_deq = w4 && !w4_codes;
   Layout L = carve(*p, ws);
   if (ws_bytes < L.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.bytes);

@@ -47,6 +47,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// Uniform loads through the scalar data cache (waited on with lgkmcnt, so
+// they never wait behind the direct-to-LDS stage loads and stores the way
+// a vector load's vmcnt wait does).
+__device__ __forceinline__ int32_t ws_sload(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+__device__ __forceinline__ float ws_sloadf(const float* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
 __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tile, float limit) {
   constexpr int THREADS = WAVES_M * WAVES_N * 64;
@@ -189,7 +199,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProblem& P, int tile, float 
   // epilogue: 32x32 accumulator, lane holds column (lane & 31) and rows
   // 8*(r/4) + 4*(lane/32) + r%4; the group's output scale (1 without one)
   // multiplies the fp32 sums first
-  const float ts = P.tscale ? P.tscale[g] : 1.0f;
+  const float ts = P.tscale ? ws_sloadf(P.tscale, g) : 1.0f;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -373,11 +383,11 @@ __device__ __forceinline__ int pipe_coords(const GemmProblem& P, int mt_total, i
     int lo = 0, hi = P.G - 1;  // last g with mtile_start[g] * ntiles <= tile
     while (lo < hi) {
       int mid = (lo + hi + 1) >> 1;
-      if (P.mtile_start[mid] * P.ntiles <= tile) lo = mid; else hi = mid - 1;
+      if (ws_sload(P.mtile_start, mid) * P.ntiles <= tile) lo = mid; else hi = mid - 1;
     }
     g = lo;
-    ms = P.mtile_start[g];
-    mc = P.mtile_start[g + 1] - ms;
+    ms = ws_sload(P.mtile_start, g);
+    mc = ws_sload(P.mtile_start, g + 1) - ms;
   }
   const int local = tile - ms * P.ntiles;
   const int blk = local / (PL_MBLK * P.ntiles);
@@ -385,16 +395,20 @@ __device__ __forceinline__ int pipe_coords(const GemmProblem& P, int mt_total, i
   const int width = min(PL_MBLK, mc - blk * PL_MBLK);
   const int nt = rem / width;
   const int ml = blk * PL_MBLK + rem % width;
-  T.row0 = (P.group_offsets ? (int64_t)P.group_offsets[g] : 0) + (int64_t)ml * S::BM;
-  T.row_end = P.group_offsets ? (int64_t)P.group_offsets[g + 1] : P.M;
+  T.row0 = (P.group_offsets ? (int64_t)ws_sload(P.group_offsets, g) : 0) + (int64_t)ml * S::BM;
+  T.row_end = P.group_offsets ? (int64_t)ws_sload(P.group_offsets, g + 1) : P.M;
   T.n0 = nt * S::BN;
-  T.ts = P.tscale ? P.tscale[g] : 1.0f;
+  T.ts = P.tscale ? ws_sloadf(P.tscale, g) : 1.0f;
   T.rs_a = pl_rsrc(P.A);
   return g;
 }
 
 // Byte offset of the A piece that lane `lane` of load instruction i of wave
 // `wave` fetches (its row clamped to the tile's first row past the segment).
+// The gathered source rows are per-lane vector loads; their wait, once per
+// tile, finds the stage loads in flight mostly landed (measured: reading
+// them through the scalar cache instead, 16 loads and selects per
+// instruction, was slower).
 template <class S>
 __device__ __forceinline__ uint32_t pipe_a_off(const GemmProblem& P, const PipeTile<S>& T, int i,
                                                int wave, int lane) {
@@ -408,7 +422,8 @@ __device__ __forceinline__ uint32_t pipe_a_off(const GemmProblem& P, const PipeT
 template <class S>
 __device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, int tile,
                                             PipeTile<S>& T) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = pipe_coords<S>(P, mt_total, tile, T);
   T.rs_w = pl_rsrc(P.W + (int64_t)g * P.w_stride);
   const int K = P.K, N = P.N;
@@ -878,92 +893,144 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
 // layout).
 //
 // The bf16 ping-pong above with the weights read as 4-bit codes and
-// dequantised inside the tile.  A stage slot holds the stage's A rows, the
-// tile's NB weight rows of codes (16 bytes per row: the stage's 32 columns)
-// and one E4M3 scale byte per weight row (its 128-column group), about a
-// quarter of the bf16 weight bytes.  The two wave groups split the tile by
-// columns here, not by rows: group g owns output columns
-// [g BN/2, (g+1) BN/2) (wave w: column block 2 (w/4) + w%2 of four, row half
-// (w/2)%2), so it needs only its own half of the weight rows.  In its compute
-// phase of stage s a group dequantises its half of stage s+1 into a two-slot
-// bf16 ring -- one fma per weight, (128 + u) s - 136 s = (u - 8) s, exact in
-// fp32 and, with at most 8 significant bits, exact as the bf16 that its
-// upper half is -- between its MFMAs; the barrier that ends the phase makes
-// the ring slot visible to the group's memory phase of stage s+1, which reads
-// the weight fragments from the ring.  A ring slot is written in the compute
-// phase of stage s-1 and read in the memory phase of stage s, both by the
-// same group, and rewritten only after the next memory phase has read the
-// other slot, so two slots suffice.  Every wave issues three load
-// instructions per stage: two of A, and one of its group's codes (waves
-// 4g, 4g+1: 64 weight rows each) or scales (waves 4g+2, 4g+3: four lanes,
-// 64 weight rows each).  The tensor scale multiplies the accumulators in the
-// epilogue.  K must be a multiple of 128.
+// dequantised inside the tile.  A stages keep only the A rows (16 KB, five
+// slots, four in flight); the weights arrive per 128-column group (four
+// stages): each weight row's 64 code bytes and its E4M3 scale byte, two
+// groups resident.  The two wave groups split the tile by columns here, not
+// by rows: group g owns output columns [g BN/2, (g+1) BN/2) (wave w: column
+// block 2 (w/4) + w%2 of four, row half (w/2)%2), so it needs only its own
+// half of the weight rows -- and loads only that half, so that everything a
+// group reads from a code slot was loaded, and waited for, by its own
+// waves.  In its compute phase of stage s a group dequantises its half of
+// stage s+1 into a two-slot bf16 ring -- one fma per weight,
+// (128 + u) s - 136 s = (u - 8) s, exact in fp32 and, with at most 8
+// significant bits, exact as the bf16 that its upper half is -- between its
+// MFMAs; the barrier that ends the phase makes the ring slot visible to the
+// group's memory phase of stage s+1, which reads the weight fragments from
+// the ring.  The scale bytes are decoded through a 256-entry table of
+// (s, -136 s) built in LDS at the start.
+//
+// Loads: every wave issues two A instructions per stage (the stage AHEAD
+// ahead) and, at the first stage of each code group, first three more: its
+// group's share of the next code group (two of 16 rows x 64 contiguous
+// bytes each, the four 16-byte pieces of a row in XOR-swizzled positions so
+// that a stage's reads of 16 consecutive rows hit 64 banks, and the group's
+// 128 scale bytes).  That group's slot was last read in the compute phase
+// two steps earlier, and its first stage is dequantised three steps later,
+// after the wait that sees the A stage issued behind it land.  The wait for
+// "the next A stage landed" leaves 9 loads in flight, or 6 when no code
+// group was issued in the last three steps (stage index 3 mod 4).  The
+// tensor scale multiplies the accumulators in the epilogue.  K must be a
+// multiple of 128.
 template <class S>
 struct PpW4Layout {
-  static constexpr int A_BYTES = S::BM * S::KB * 2;
-  static constexpr int C_ROW = S::KB / 2;  // code bytes per weight row and stage
-  static constexpr int C_BYTES = S::NB * C_ROW;
-  static constexpr int STAGE = A_BYTES + C_BYTES + S::NB;  // + a scale byte per weight row
-  static constexpr int RING = S::NB * S::KB * 2;           // one stage of bf16 weights
+  static constexpr int STAGES = 5;                         // A slots
+  static constexpr int AHEAD = STAGES - 1;
+  static constexpr int A_BYTES = S::BM * S::KB * 2;        // one A stage
+  static constexpr int G_COLS = 128;                       // K columns of a code group
+  static constexpr int G_STAGES = G_COLS / S::KB;          // stages per code group
+  static constexpr int C_ROW = G_COLS / 2;                 // code bytes per row and group
   static constexpr int HALF = S::NB / 2;                   // weight rows per wave group
-  static constexpr int VM_STAGE = S::A_INSTR + 1;          // load instructions per wave and stage
-  static_assert(S::KB == 32 && C_ROW == 16, "one 16-byte code piece per weight row and stage");
-  static_assert(HALF == 128 && STAGE % 16 == 0, "two waves x 64 code rows per group");
+  static constexpr int C_BYTES = S::NB * C_ROW;
+  static constexpr int C_SLOT = C_BYTES + S::NB;           // + a scale byte per weight row
+  static constexpr int C_SLOTS = 2;
+  static constexpr int RING = S::NB * S::KB * 2;           // one stage of bf16 weights
+  static constexpr int C_OFF = STAGES * A_BYTES;           // code slots
+  static constexpr int R_OFF = C_OFF + C_SLOTS * C_SLOT;   // bf16 ring
+  static constexpr int T_OFF = R_OFF + 2 * RING;           // scale table
+  static constexpr int BYTES = T_OFF + 256 * 8;
+  static constexpr int A_VM = S::A_INSTR;                  // A loads per wave and stage
+  static constexpr int C_VM = 3;                           // code-group loads per wave
+  static_assert(S::KB == 32 && G_STAGES == 4 && C_ROW == 64, "four 16-byte pieces per row");
+  static_assert(S::NB == 256 && S::NW == 8 && S::A_INSTR == 2 && HALF == 128,
+                "two code instructions of 16 rows per wave");
+  static_assert(C_SLOT % 16 == 0 && BYTES <= 160 * 1024, "LDS");
 };
 
 // Wave w's tile position in the column split: (row half, column block).
 __device__ __forceinline__ int pp_w4_wm(int wave) { return (wave >> 1) & 1; }
 __device__ __forceinline__ int pp_w4_wn(int wave) { return 2 * (wave >> 2) + (wave & 1); }
 
-// Tile t: the A offsets as in the bf16 tile; off[A_INSTR] is the byte offset
-// of this wave's codes (one 16-byte piece per lane: weight row 64 (w%2) +
-// lane of its group's half) or scales (lane < 4: the 16 bytes of rows
-// 16 lane .. +15 of the same 64), from rs_w; rows past N read row n0.
+// Local row l of wave group g's half (gate_up: its BN/2 gate rows, then the
+// matching up rows; down: 128 consecutive rows) as a global weight row of
+// tile column n0 (columns past N read column n0).
 template <class S>
-__device__ __forceinline__ void pp_w4_locate(const GemmProblem& P, int mt_total, int tile,
-                                             int wave, PipeTile<S>& T) {
-  using L = PpW4Layout<S>;
-  const int lane = threadIdx.x & 63;
-  const int g = pipe_coords<S>(P, mt_total, tile, T);
-#pragma unroll
-  for (int i = 0; i < S::A_INSTR; ++i) T.off[i] = pipe_a_off<S>(P, T, i, wave, lane);
-  const int grp = wave >> 2, q = wave & 3, hq = q & 1;
-  const int r_in = q < 2 ? lane : 16 * lane;
-  // gate_up: a group's half is BN/2 gate rows (hq = 0) and the matching up
-  // rows (hq = 1); down: 128 consecutive rows
-  int n = S::GATEUP ? T.n0 + (S::BN / 2) * grp + r_in : T.n0 + L::HALF * grp + 64 * hq + r_in;
-  if (n >= P.N) n = T.n0;
-  const int64_t wr = S::GATEUP && hq ? (int64_t)P.N + n : n;
-  if (q < 2) {
-    T.rs_w = pl_rsrc(reinterpret_cast<const uint8_t*>(P.W) + (int64_t)g * P.w_stride * 2);
-    T.off[S::A_INSTR] = (uint32_t)(wr * (P.K / 2));
-  } else {
-    T.rs_w = pl_rsrc(P.S + (int64_t)g * P.s_stride);
-    T.off[S::A_INSTR] = (uint32_t)wr;
-  }
+__device__ __forceinline__ int64_t pp_w4_wrow(const GemmProblem& P, int n0, int g, int l) {
+  constexpr int Q = S::GATEUP ? S::BN / 2 : PpW4Layout<S>::HALF;
+  const bool up = S::GATEUP && l >= Q;
+  int n = n0 + Q * g + (up ? l - Q : l);
+  if (n >= P.N) n = n0;
+  return up ? (int64_t)P.N + n : n;
 }
 
-// This wave's loads of stage k0 of tile T into stage slot `slot`; wr_total
-// is the weight rows of one group (gate_up 2N, down N): the scale rows of
-// one 128-column group.
+// XOR swizzle of a code row's four 16-byte pieces
+__device__ __forceinline__ int pp_w4_cswz(int r) { return (r >> 2) & 3; }
+
+// A tile as one wave of the W4A16 tile sees it: the bf16 tile's fields (A
+// offsets in t.off[0..1]), this expert's code and scale resources, and the
+// byte offsets of the wave's two code pieces (local rows 16 (q + 4 i) +
+// lane/4 of its group's half, q = w % 4; piece lane%4 swizzled) and scale
+// piece (lane < 8: local rows 16 lane .. +15).
 template <class S>
-__device__ __forceinline__ void pp_w4_issue(const PipeTile<S>& T, uint8_t* smem, int slot, int k0,
-                                            int wave, int wr_total) {
+struct PpW4Tile {
+  PipeTile<S> t;
+  __amdgpu_buffer_rsrc_t rs_s;
+  uint32_t off_c0, off_c1, off_s;
+};
+
+template <class S>
+__device__ __forceinline__ void pp_w4_locate(const GemmProblem& P, int mt_total, int tile,
+                                             int wave, PpW4Tile<S>& T) {
   using L = PpW4Layout<S>;
   const int lane = threadIdx.x & 63;
-  uint8_t* base = smem + slot * L::STAGE;
+  const int g = pipe_coords<S>(P, mt_total, tile, T.t);
+#pragma unroll
+  for (int i = 0; i < S::A_INSTR; ++i) T.t.off[i] = pipe_a_off<S>(P, T.t, i, wave, lane);
+  T.t.rs_w = pl_rsrc(reinterpret_cast<const uint8_t*>(P.W) + (int64_t)g * P.w_stride * 2);
+  T.rs_s = pl_rsrc(P.S + (int64_t)g * P.s_stride);
+  const int grp = wave >> 2, q = wave & 3;
+  uint32_t off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int l = 16 * (q + 4 * i) + lane / 4;
+    const int piece = (lane % 4) ^ pp_w4_cswz(L::HALF * grp + l);
+    off[i] = (uint32_t)(pp_w4_wrow<S>(P, T.t.n0, grp, l) * (P.K / 2) + piece * 16);
+  }
+  T.off_c0 = off[0];
+  T.off_c1 = off[1];
+  T.off_s = (uint32_t)pp_w4_wrow<S>(P, T.t.n0, grp, 16 * (lane & 7));
+}
+
+// This wave's share of code group `cg` (local to tile T) into code slot
+// `cslot`; wr_total is the weight rows of one expert (gate_up 2N, down N):
+// the scale rows of one group.  The slot holds the rows in local order, wave
+// group g's half at rows 128 g ..; its scale bytes likewise.
+template <class S>
+__device__ __forceinline__ void pp_w4_issue_c(const PpW4Tile<S>& T, uint8_t* smem, int cslot,
+                                              int cg, int wave, int wr_total) {
+  using L = PpW4Layout<S>;
+  const int lane = threadIdx.x & 63;
+  const int grp = wave >> 2, q = wave & 3;
+  uint8_t* base = smem + L::C_OFF + cslot * L::C_SLOT;
+  lds_buffer_16(T.t.rs_w, T.off_c0, (uint32_t)cg * L::C_ROW,
+                reinterpret_cast<uint16_t*>(base + (L::HALF * grp + 16 * q) * L::C_ROW));
+  lds_buffer_16(T.t.rs_w, T.off_c1, (uint32_t)cg * L::C_ROW,
+                reinterpret_cast<uint16_t*>(base + (L::HALF * grp + 16 * (q + 4)) * L::C_ROW));
+  if (lane < 8)  // the group's four waves write the same 128 scale bytes
+    lds_buffer_16(T.rs_s, T.off_s, (uint32_t)cg * (uint32_t)wr_total,
+                  reinterpret_cast<uint16_t*>(base + L::C_BYTES + L::HALF * grp));
+}
+
+// This wave's A loads of stage k0 of tile T into A slot `slot`.
+template <class S>
+__device__ __forceinline__ void pp_w4_issue_a(const PpW4Tile<S>& T, uint8_t* smem, int slot,
+                                              int k0, int wave) {
+  using L = PpW4Layout<S>;
+  uint8_t* base = smem + slot * L::A_BYTES;
 #pragma unroll
   for (int i = 0; i < S::A_INSTR; ++i)
-    lds_buffer_16(T.rs_a, T.off[i], (uint32_t)k0 * 2,
+    lds_buffer_16(T.t.rs_a, T.t.off[i], (uint32_t)k0 * 2,
                   reinterpret_cast<uint16_t*>(base + (wave + S::NW * i) * S::RPI * S::KB * 2));
-  const int grp = wave >> 2, q = wave & 3;
-  const int crow = L::HALF * grp + 64 * (q & 1);  // the wave's first row in the slot's order
-  if (q < 2)
-    lds_buffer_16(T.rs_w, T.off[S::A_INSTR], (uint32_t)k0 / 2,
-                  reinterpret_cast<uint16_t*>(base + L::A_BYTES + crow * L::C_ROW));
-  else if (lane < 4)
-    lds_buffer_16(T.rs_w, T.off[S::A_INSTR], (uint32_t)(k0 / 128) * (uint32_t)wr_total,
-                  reinterpret_cast<uint16_t*>(base + L::A_BYTES + L::C_BYTES + crow));
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -1004,17 +1071,17 @@ __device__ __forceinline__ void pp_mfma_range(f32x16_t (&acc)[S::NMAT][S::TM][S:
         }
 }
 
-template <class S, int STAGES>
+template <class S>
 __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProblem p0,
                                                                       float limit) {
   static_assert(S::NW == 8 && S::WAVES_M == 2 && S::KB == 32, "ping-pong shape");
   using L = PpW4Layout<S>;
-  constexpr int KB = S::KB, BN = S::BN;
+  constexpr int KB = S::KB, BN = S::BN, STAGES = L::STAGES, AHEAD = L::AHEAD;
   constexpr int TM = S::TM, TN = S::TN, NMAT = S::NMAT, WM = S::WM, WN = S::WN;
-  constexpr int AHEAD = STAGES - 1;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
   uint8_t* smem = reinterpret_cast<uint8_t*>(smem_dyn);
-  uint16_t* ring = reinterpret_cast<uint16_t*>(smem + STAGES * L::STAGE);
+  uint16_t* ring = reinterpret_cast<uint16_t*>(smem + L::R_OFF);
+  float2_t* table = reinterpret_cast<float2_t*>(smem + L::T_OFF);
   GemmProblem unused = p0;
   const PipeRange R = pipe_range<S::BM>(p0, unused, 0);
   int t = R.t_first;
@@ -1027,22 +1094,29 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   const int group = wave >> 2;
   const int wm = pp_w4_wm(wave), wn = pp_w4_wn(wave);
   const int wr_total = S::GATEUP ? 2 * p0.N : p0.N;
-  const int nk = p0.K / KB;
+  const int nk = p0.K / KB;          // stages per tile (a multiple of 4)
+  const int ng = nk / L::G_STAGES;   // code groups per tile
 
-  // this lane's share of its group's dequantisation: weight row rho of the
-  // half (slot order), columns 16 h .. 16 h + 15 of the stage
+  // the scale table: (s, -136 s) for every E4M3 byte
+  if (threadIdx.x < 256) {
+    const float sc = e4m3_to_f32(threadIdx.x);
+    table[threadIdx.x] = float2_t{sc, -136.0f * sc};
+  }
+
+  // this lane's share of its group's dequantisation: local row rho of the
+  // group's half (code slot row crow), columns 16 h .. 16 h + 15 of the stage
   const int gl = (wave & 3) * 64 + lane;
   const int rho = gl >> 1, h = gl & 1;
   const int crow = L::HALF * group + rho;
-  const int rrow = S::GATEUP ? (rho >> 6) * BN + (BN / 2) * group + (rho & 63)
-                             : L::HALF * group + rho;
+  const int cswz = pp_w4_cswz(crow);
+  const int rrow = S::GATEUP ? (rho >> 6) * BN + (BN / 2) * group + (rho & 63) : crow;
   const int rpos0 = rrow * KB + pl_swz<KB>(rrow, 2 * h) * 8;
   const int rpos1 = rrow * KB + pl_swz<KB>(rrow, 2 * h + 1) * 8;
 
   f32x16_t acc[NMAT][TM][TN];
   bf16x8_t fa[2][TM], fb[2][NMAT][TN];
   auto read_stage = [&](int slot, int rslot) __attribute__((always_inline)) {
-    const uint16_t* As = reinterpret_cast<const uint16_t*>(smem + slot * L::STAGE);
+    const uint16_t* As = reinterpret_cast<const uint16_t*>(smem + slot * L::A_BYTES);
     const uint16_t* Bs = ring + rslot * (L::RING / 2);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -1061,18 +1135,20 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
         }
     }
   };
-  // Dequantise this group's half of the stage in `slot` into ring slot
-  // `rslot`.  In a compute phase (mfma set) the stage's 16 MFMAs go around
-  // it in a fixed order of issue: the two LDS reads, three MFMAs while they
-  // land, then one piece of the unpacking after each MFMA -- the scale, then
-  // two columns at a time (five VALU instructions), a ring write after each
-  // eight columns.  An MFMA holds the matrix pipe for 32 cycles, longer than
-  // a piece takes to issue, so the pipe is never left waiting for the ALU.
-  auto dequant = [&](int slot, int rslot, bool mfma) __attribute__((always_inline)) {
+  // Dequantise this group's half of stream stage `ss` (code slot of its
+  // group, piece ss % 4 of each row) into ring slot `rslot`.  In a compute
+  // phase (mfma set) the stage's 16 MFMAs go around it in a fixed order of
+  // issue: the two LDS reads, two MFMAs while they land, the table read, two
+  // more, then one piece of the unpacking after each MFMA (two columns at a
+  // time, five VALU instructions; a ring write after each eight columns).
+  // An MFMA holds the matrix pipe for 32 cycles, longer than a piece takes to
+  // issue.
+  auto dequant = [&](int ss, int rslot, bool mfma) __attribute__((always_inline)) {
     static_assert(2 * NMAT * TM * TN == 16, "16 MFMAs per stage");
-    const uint8_t* st = smem + slot * L::STAGE;
-    const uint2_t cw = *reinterpret_cast<const uint2_t*>(st + L::A_BYTES + crow * L::C_ROW + 8 * h);
-    const uint32_t sb = st[L::A_BYTES + L::C_BYTES + crow];
+    const uint8_t* cs = smem + L::C_OFF + ((ss >> 2) & 1) * L::C_SLOT;
+    const uint2_t cw = *reinterpret_cast<const uint2_t*>(
+        cs + crow * L::C_ROW + (((ss & 3) ^ cswz) << 4) + 8 * h);
+    const uint32_t sb = cs[L::C_BYTES + crow];
     uint16_t* rs = ring + rslot * (L::RING / 2);
 #define PPW4_MFMA(lo, hi)                          \
     if (mfma) {                                    \
@@ -1080,30 +1156,29 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
       pp_mfma_range<S, lo, hi>(acc, fa, fb);       \
       __builtin_amdgcn_sched_barrier(0);           \
     }
-    PPW4_MFMA(0, 3)
-    const float sc = e4m3_to_f32(sb);
-    PPW4_MFMA(3, 4)
-    const float cc = -136.0f * sc;
+    PPW4_MFMA(0, 2)
+    const float2_t sc = table[sb];
+    PPW4_MFMA(2, 4)
     const uint32_t n0 = cw[0] & 0x0F0F0F0Fu;
-    const uint32_t p0 = w4_dequant2(n0, W4_SEL0, W4_SEL1, sc, cc);
+    const uint32_t p0 = w4_dequant2(n0, W4_SEL0, W4_SEL1, sc[0], sc[1]);
     PPW4_MFMA(4, 5)
-    const uint32_t p1 = w4_dequant2(n0, W4_SEL2, W4_SEL3, sc, cc);
+    const uint32_t p1 = w4_dequant2(n0, W4_SEL2, W4_SEL3, sc[0], sc[1]);
     const uint32_t n1 = (cw[0] >> 4) & 0x0F0F0F0Fu;
     PPW4_MFMA(5, 6)
-    const uint32_t p2 = w4_dequant2(n1, W4_SEL0, W4_SEL1, sc, cc);
+    const uint32_t p2 = w4_dequant2(n1, W4_SEL0, W4_SEL1, sc[0], sc[1]);
     PPW4_MFMA(6, 7)
-    const uint32_t p3 = w4_dequant2(n1, W4_SEL2, W4_SEL3, sc, cc);
+    const uint32_t p3 = w4_dequant2(n1, W4_SEL2, W4_SEL3, sc[0], sc[1]);
     *reinterpret_cast<u32x4_t*>(rs + rpos0) = u32x4_t{p0, p1, p2, p3};
     PPW4_MFMA(7, 8)
     const uint32_t n2 = cw[1] & 0x0F0F0F0Fu;
-    const uint32_t p4 = w4_dequant2(n2, W4_SEL0, W4_SEL1, sc, cc);
+    const uint32_t p4 = w4_dequant2(n2, W4_SEL0, W4_SEL1, sc[0], sc[1]);
     PPW4_MFMA(8, 9)
-    const uint32_t p5 = w4_dequant2(n2, W4_SEL2, W4_SEL3, sc, cc);
+    const uint32_t p5 = w4_dequant2(n2, W4_SEL2, W4_SEL3, sc[0], sc[1]);
     const uint32_t n3 = (cw[1] >> 4) & 0x0F0F0F0Fu;
     PPW4_MFMA(9, 10)
-    const uint32_t p6 = w4_dequant2(n3, W4_SEL0, W4_SEL1, sc, cc);
+    const uint32_t p6 = w4_dequant2(n3, W4_SEL0, W4_SEL1, sc[0], sc[1]);
     PPW4_MFMA(10, 11)
-    const uint32_t p7 = w4_dequant2(n3, W4_SEL2, W4_SEL3, sc, cc);
+    const uint32_t p7 = w4_dequant2(n3, W4_SEL2, W4_SEL3, sc[0], sc[1]);
     *reinterpret_cast<u32x4_t*>(rs + rpos1) = u32x4_t{p4, p5, p6, p7};
     PPW4_MFMA(11, 16)
 #undef PPW4_MFMA
@@ -1114,41 +1189,65 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  PipeTile<S> cur, nxt;
+  PpW4Tile<S> cur, nxt;
   pp_w4_locate<S>(p0, R.mt0, t, wave, cur);
+  // The stream: stage ss of the workgroup's stage stream (ss counts across
+  // tiles; every tile has nk stages, a multiple of 4) sits in A slot
+  // ss % STAGES and ring slot ss % 2; code group ss / 4 in code slot
+  // (ss / 4) % 2.  The prologue loads code group 0, then A stages
+  // 0..AHEAD-1.
+  pp_w4_issue_c<S>(cur, smem, 0, 0, wave, wr_total);
 #pragma unroll
-  for (int s0 = 0; s0 < AHEAD; ++s0) pp_w4_issue<S>(cur, smem, s0, s0 * KB, wave, wr_total);
-  PL_WAIT_VM_LDS((AHEAD - 1) * L::VM_STAGE);
-  pp_barrier();  // stage 0 landed everywhere
+  for (int s0 = 0; s0 < AHEAD; ++s0) pp_w4_issue_a<S>(cur, smem, s0, s0 * KB, wave);
+  PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM);
+  pp_barrier();  // code group 0, A stage 0 and the table everywhere
   dequant(0, 0, false);
   PL_WAIT_LDS();
-  pp_barrier();  // its weights in ring slot 0
+  pp_barrier();  // stage 0's weights in ring slot 0
   if (group) pp_barrier();
-  int slot = 0, slot_issue = AHEAD, rslot = 0;
+  int ss = 0;  // stream index of the stage being read
   for (;;) {
     const int t_next = t + R.stride;
     const bool more = t_next < R.t_end;
     if (more) pp_w4_locate<S>(p0, R.mt0, t_next, wave, nxt);
     pipe_zero<S>(acc);
-    for (int kt = 0; kt < nk; ++kt) {
-      read_stage(slot, rslot);
+    for (int kt = 0; kt < nk; ++kt, ++ss) {
+      read_stage(ss % STAGES, ss & 1);
+      // at a code group's first stage: this group's half of the next code
+      // group (of this tile, else of the next one; past the last tile, the
+      // last group again, into a slot nothing reads any more) ...
+      if ((kt & 3) == 0) {
+        const int cg = kt / L::G_STAGES + 1;
+        const int cslot = (ss / L::G_STAGES + 1) & 1;
+        if (cg < ng)
+          pp_w4_issue_c<S>(cur, smem, cslot, cg, wave, wr_total);
+        else if (more)
+          pp_w4_issue_c<S>(nxt, smem, cslot, 0, wave, wr_total);
+        else
+          pp_w4_issue_c<S>(cur, smem, cslot, ng - 1, wave, wr_total);
+      }
+      // ... then A stage kt + AHEAD of this tile (or of the next one; past
+      // the last tile, the last stage again)
       const int ka = kt + AHEAD;
+      const int sa = (ss + AHEAD) % STAGES;
       if (ka < nk)
-        pp_w4_issue<S>(cur, smem, slot_issue, ka * KB, wave, wr_total);
+        pp_w4_issue_a<S>(cur, smem, sa, ka * KB, wave);
       else if (more)
-        pp_w4_issue<S>(nxt, smem, slot_issue, (ka - nk) * KB, wave, wr_total);
+        pp_w4_issue_a<S>(nxt, smem, sa, (ka - nk) * KB, wave);
       else
-        pp_w4_issue<S>(cur, smem, slot_issue, (nk - 1) * KB, wave, wr_total);
-      PL_WAIT_VM_LDS((AHEAD - 1) * L::VM_STAGE);
+        pp_w4_issue_a<S>(cur, smem, sa, (nk - 1) * KB, wave);
+      // own loads of A stage ss+1 landed (and, with them, every code load
+      // issued before it)
+      if ((kt & 3) == 3)
+        PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM);
+      else
+        PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM + L::C_VM);
       pp_barrier();
-      slot = slot + 1 == STAGES ? 0 : slot + 1;
-      rslot ^= 1;
-      dequant(slot, rslot, true);  // the next stage of the stream, beside this one's MFMAs
+      dequant(ss + 1, (ss + 1) & 1, true);  // the next stage of the stream, beside this one's MFMAs
       PL_WAIT_LDS();
       pp_barrier();
-      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
     }
-    pipe_store<S>(p0, cur, acc, limit, wm, wn);
+    pipe_store<S>(p0, cur.t, acc, limit, wm, wn);
     if (!more) break;
     t = t_next;
     cur = nxt;
@@ -1192,11 +1291,6 @@ __device__ __forceinline__ int ws_swz(int row, int chunk) {
   // rows are a multiple of 256 bytes long: the 16 rows one ds_read_b128 pass
   // touches must sit in 16 different 16-byte bank groups
   return chunk ^ (row & 15);
-}
-
-// Uniform load through the scalar data cache (waited on with lgkmcnt).
-__device__ __forceinline__ int32_t ws_sload(const int32_t* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
 // One problem's fields, selected between the two problems of the launch.
@@ -1411,7 +1505,7 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
     K_cp = P.K;
     N_cp = P.N;
     out_cp = P.out;
-    ts_cp = P.tscale ? P.tscale[g_cp] : 1.0f;
+    ts_cp = P.tscale ? ws_sloadf(P.tscale, g_cp) : 1.0f;
   };
 
   // element (reg r, lane l) of the wave's accumulator: row 4(l/16) + r of
@@ -1515,8 +1609,6 @@ __global__ __launch_bounds__(256, 1) void grouped_wstream_kernel(GemmProblem p0,
 // the launched shape: 256 weight rows by 256 columns a stage, eight
 // wavefronts, three stages
 constexpr int W4_NBLK = 2, W4_KB = 256, W4_NW = 8, W4_STAGES = 3;
-// stage slots of the W4A16 ping-pong tile
-constexpr int W4_PP_STAGES = 5;
 
 template <int NBLK, int KB, int NW>
 struct W4Shape {
@@ -1701,7 +1793,7 @@ __global__ __launch_bounds__(NW * 64, 1) void grouped_wstream_w4_kernel(GemmProb
   float ts_cp = 1.0f;  // the expert's tensor scale
   auto setup_cp = [&]() __attribute__((always_inline)) {
     ws_locate<BN>(P, t_cp, row0_cp, row_end_cp, n0_cp, g_cp);
-    ts_cp = P.tscale ? P.tscale[g_cp] : 1.0f;
+    ts_cp = P.tscale ? ws_sloadf(P.tscale, g_cp) : 1.0f;
   };
 
   // element (reg r, lane l) of block j's accumulator: row 4(l/16) + r of the
@@ -1839,13 +1931,11 @@ hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
   return hipGetLastError();
 }
 
-template <bool GATEUP, int STAGES>
+template <bool GATEUP>
 hipError_t launch_pp_w4(const GemmProblem& a, float limit, hipStream_t stream) {
   using S = PipeShape<256, GATEUP ? 128 : 256, GATEUP, 32, 8, 2>;
-  const size_t lds = (size_t)STAGES * PpW4Layout<S>::STAGE + 2 * PpW4Layout<S>::RING;
-  static_assert((size_t)STAGES * PpW4Layout<S>::STAGE + 2 * PpW4Layout<S>::RING <= 160 * 1024,
-                "LDS");
-  auto kern = grouped_pp_w4_kernel<S, STAGES>;
+  const size_t lds = PpW4Layout<S>::BYTES;
+  auto kern = grouped_pp_w4_kernel<S>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1978,10 +2068,10 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                int max_wgs) {
   if (a.S != nullptr) {  // W4A16 weights: one problem per launch
     if (b != nullptr || a.K % 128 != 0) return hipErrorInvalidValue;
-    if (v == GemmVariant::kPingPong) {  // long segments: the ping-pong tile, 5 stages
-      if (a.K < 4 * 32 || a.N % 32 != 0) return hipErrorInvalidValue;
-      if (gateup) return launch_pp_w4<true, W4_PP_STAGES>(a, limit, stream);
-      return launch_pp_w4<false, W4_PP_STAGES>(a, limit, stream);
+    if (v == GemmVariant::kPingPong) {  // long segments: the ping-pong tile
+      if (a.K < 128 || a.N % 32 != 0) return hipErrorInvalidValue;
+      if (gateup) return launch_pp_w4<true>(a, limit, stream);
+      return launch_pp_w4<false>(a, limit, stream);
     }
     if (v != GemmVariant::kWStream) return hipErrorInvalidValue;
     if (gateup)

@@ -345,10 +345,14 @@ def test_forward_prefill_finish_full_sampled():
 W4_TILED = {
     # ~300 rows per expert: the LDS-tiled GEMM on the dequantised experts
     "w4_tiled": Workload("w4_tiled", T=600, H=256, E=4, k=2, I=256, I_s=128, w4=True),
-    # ~2400 rows per expert: the ping-pong GEMM on the codes; no shared
-    # expert; down K = 128 (four stages, the fewest it takes), down N = 384
-    # (a half-empty last column tile)
+    # ~2400 rows per expert: the W4A16 ping-pong tile; no shared expert;
+    # down K = 128 (one code group per tile: the stream fetches the next
+    # tile's first group during the only one) and N = 384 (a half-empty last
+    # column tile)
     "w4_pingpong": Workload("w4_pingpong", T=2400, H=384, E=4, k=2, I=128, I_s=0, w4=True),
+    # two code groups per tile in down
+    "w4_pingpong_k256": Workload("w4_pingpong_k256", T=2400, H=384, E=4, k=2, I=256, I_s=0,
+                                 w4=True),
     # 4096 rows per expert: two or more tiles per workgroup in both
     # projections (the stage stream runs across tiles), shared expert after
     "w4_pingpong_multi": Workload("w4_pingpong_multi", T=8192, H=512, E=8, k=4, I=512, I_s=256,
