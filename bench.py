@@ -308,29 +308,39 @@ def write_mfma(workload: str, csv_path: str, command: str) -> None:
     import moe_inputs
     wl = moe_inputs.WORKLOADS[workload]
     T, H, k, I, Is = wl.T, wl.H, wl.k, wl.I, wl.I_s
-    algo = {"gate_up": 2 * T * k * H * 2 * I + 2 * T * H * 2 * Is,
-            "down": 2 * T * k * I * H + 2 * T * Is * H}
+    routed = {"gate_up": 2 * T * k * H * 2 * I, "down": 2 * T * k * I * H}
+    shared = {"gate_up": 2 * T * H * 2 * Is, "down": 2 * T * Is * H}
+    # W4A16 routed experts run in launches of their own (grouped_pp_w4_*),
+    # the bf16 shared expert in the bf16 tile's launches; otherwise one launch
+    # per projection carries both
+    split = wl.w4
     vals: dict = {}
     for r in csv.DictReader(open(csv_path)):
         kind = _grouped_kind(r["Kernel_Name"])
         if kind is None:
             continue
-        vals.setdefault((kind, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        part = ("routed" if "_w4_" in r["Kernel_Name"] else "shared") if split else "all"
+        vals.setdefault((kind, part, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     out = {"workload": wl.label(), "command": command, "kernel_source_sha256": kernel_source_sha(),
            "projections": {}}
+    parts = ("routed", "shared") if split else ("all",)
     for kind in ("gate_up", "down"):
-        util = vals.get((kind, "MfmaUtil"), [])
-        flops = vals.get((kind, "MfmaFlopsBF16"), [])
-        gui = vals.get((kind, "GRBM_GUI_ACTIVE"), [])
-        if not util:
-            continue
-        mean = lambda v: sum(v) / len(v) if v else None  # noqa: E731
-        f = mean(flops)
-        out["projections"][kind] = {
-            "dispatches": len(util), "mfma_util_percent": round(mean(util), 2),
-            "mfma_flops_executed_per_launch": f, "algorithmic_flops_per_launch": algo[kind],
-            "executed_over_algorithmic": round(f / algo[kind], 4) if f else None,
-            "grbm_gui_active_per_launch": mean(gui)}
+        for part in parts:
+            util = vals.get((kind, part, "MfmaUtil"), [])
+            flops = vals.get((kind, part, "MfmaFlopsBF16"), [])
+            gui = vals.get((kind, part, "GRBM_GUI_ACTIVE"), [])
+            if not util:
+                continue
+            algo = {"routed": routed[kind], "shared": shared[kind],
+                    "all": routed[kind] + shared[kind]}[part]
+            mean = lambda v: sum(v) / len(v) if v else None  # noqa: E731
+            f = mean(flops)
+            key = kind if part == "all" else f"{kind}_{part}"
+            out["projections"][key] = {
+                "dispatches": len(util), "mfma_util_percent": round(mean(util), 2),
+                "mfma_flops_executed_per_launch": f, "algorithmic_flops_per_launch": algo,
+                "executed_over_algorithmic": round(f / algo, 4) if f else None,
+                "grbm_gui_active_per_launch": mean(gui)}
     path = os.path.join(ROOT, "profiles", f"mfma_{wl.label()}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)

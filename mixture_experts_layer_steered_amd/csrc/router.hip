@@ -188,6 +188,11 @@ __global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
   __shared__ int32_t wsum[2 * PM_WAVES];
   float* lg_lds = reinterpret_cast<float*>(lds);
   const int TE = T * E;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the biases of this lane's experts, loaded once (in flight with the
+  // partials) for every token the wave ranks
+  float bv[TK_PER_LANE];
+  topk_bias<TK_PER_LANE>(bias, E, lane, bv);
   // logits: slice partials summed in slice order; two elements per thread
   // and pass, their 2 x 16 loads in flight together
   for (int i0 = threadIdx.x; i0 < TE; i0 += 2 * PM_THREADS) {
@@ -217,7 +222,6 @@ __global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
     }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int t = wave; t < T; t += PM_WAVES) {
     float lg[TK_PER_LANE];
 #pragma unroll
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
       const int e = lane + 64 * i;
       lg[i] = e < E ? lg_lds[t * E + e] : 0.f;
     }
-    topk_select<TK_PER_LANE>(lg, bias, ids, wts, ids_lds, t, E, k, rsf, lane);
+    topk_select<TK_PER_LANE>(lg, bv, ids, wts, ids_lds, t, E, k, rsf, lane);
   }
   __syncthreads();
   permute_small_body(ids_lds, offsets, sorted_token, inv_pos, (int64_t)T * k, E, k, bm, mstart,

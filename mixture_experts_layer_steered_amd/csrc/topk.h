@@ -27,9 +27,21 @@ __device__ __forceinline__ uint64_t topk_key(float sb, int e) {
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
 }
 
+// The correction bias of lane L's experts L + 64 i (0 past E or without a
+// bias), loaded once and kept in registers across tokens.
+template <int TK_PER_LANE>
+__device__ __forceinline__ void topk_bias(const float* __restrict__ bias, int E, int lane,
+                                          float (&bv)[TK_PER_LANE]) {
+#pragma unroll
+  for (int i = 0; i < TK_PER_LANE; ++i) {
+    const int e = lane + 64 * i;
+    bv[i] = (bias && e < E) ? bias[e] : 0.0f;
+  }
+}
+
 // The selection of one token by one wavefront from its logits in
 // registers: lane L holds experts L + 64 i (i < TK_PER_LANE) as lg[i] (lanes
-// past E hold anything; only e < E ranks).  k wave-wide arg-max rounds over
+// past E hold anything; only e < E ranks) and their biases as bv[i].  k wave-wide arg-max rounds over
 // 64-bit keys pick the winners; the picks' ids and weights go to ids / wts
 // of token t in ascending id order, the ids also to ids_copy when it is
 // not null (the same layout, e.g. in LDS).
@@ -42,7 +54,7 @@ __device__ __forceinline__ uint64_t topk_key(float sb, int e) {
 // of them), so both forms pick the same experts.
 template <int TK_PER_LANE>
 __device__ __forceinline__ void topk_select(const float (&lg)[TK_PER_LANE],
-                                            const float* __restrict__ bias,
+                                            const float (&bv)[TK_PER_LANE],
                                             int32_t* __restrict__ ids, float* __restrict__ wts,
                                             int32_t* ids_copy, int64_t t, int E, int k, float rsf,
                                             int lane) {
@@ -55,8 +67,7 @@ __device__ __forceinline__ void topk_select(const float (&lg)[TK_PER_LANE],
     sg[i] = 0.f;
     if (e < E) {
       sg[i] = topk_sigmoid(lg[i]);
-      const float b = bias ? bias[e] : 0.0f;
-      key[i] = topk_key(sg[i] + b, e);
+      key[i] = topk_key(sg[i] + bv[i], e);
     }
   }
   if constexpr (TK_PER_LANE <= 2) {
@@ -138,6 +149,8 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ partial, in
                                            int64_t t, int64_t T, int E, int k, float rsf,
                                            int lane) {
   const int64_t TE = T * E;
+  float bv[TK_PER_LANE];
+  topk_bias<TK_PER_LANE>(bias, E, lane, bv);  // in flight with the partials
   float lg[TK_PER_LANE];
 #pragma unroll
   for (int i = 0; i < TK_PER_LANE; ++i) {
@@ -160,5 +173,5 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ partial, in
       lg[i] = l;
     }
   }
-  topk_select<TK_PER_LANE>(lg, bias, ids, wts, nullptr, t, E, k, rsf, lane);
+  topk_select<TK_PER_LANE>(lg, bv, ids, wts, nullptr, t, E, k, rsf, lane);
 }
