@@ -18,6 +18,16 @@ constexpr int PM_PER_WAVE = 256;
 constexpr int PM_TILE = PM_WAVES * PM_PER_WAVE;  // 4096 pairs
 constexpr int PM_STEPS = PM_PER_WAVE / 64;
 
+// Workgroup barrier for LDS only: this thread's LDS operations have completed
+// (lgkmcnt(0)), and global stores still in flight are not waited for (the
+// results go to later launches).
+__device__ __forceinline__ void pm_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Every thread of the workgroup calls it (it synchronises the workgroup).
 // ids: the N <= PM_TILE expert ids (global or LDS memory); whist: LDS of
 // PM_WAVES * MOE_MAX_EXPERTS_DEV ints; wsum: LDS of 2 * PM_WAVES ints.
@@ -30,16 +40,21 @@ __device__ __forceinline__ void permute_small_body(const int32_t* ids, int32_t* 
   const int wave = threadIdx.x >> 6;
   constexpr int MX = MOE_MAX_EXPERTS_DEV;
   for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) whist[(i / E) * MX + i % E] = 0;
-  __syncthreads();
-  const int64_t wbase = (int64_t)wave * PM_PER_WAVE;
+  pm_lds_barrier();
+  // each wave takes a contiguous run of the pairs in order, as few 64-pair
+  // steps as spread the batch over all the waves (one step each up to 1024
+  // pairs); the order of the runs is the order of the waves
+  const int steps = (int)((N + PM_WAVES * 64 - 1) / (PM_WAVES * 64));
+  const int64_t wbase = (int64_t)wave * steps * 64;
   int my_e[PM_STEPS];
 #pragma unroll
   for (int s = 0; s < PM_STEPS; ++s) {
     const int64_t p = wbase + s * 64 + lane;
-    my_e[s] = (p < N) ? ids[p] : MX;  // sentinel: matches no expert
-    if (p < N) atomicAdd(&whist[wave * MX + my_e[s]], 1);
+    const bool in = s < steps && p < N;
+    my_e[s] = in ? ids[p] : MX;  // sentinel: matches no expert
+    if (in) atomicAdd(&whist[wave * MX + my_e[s]], 1);
   }
-  __syncthreads();
+  pm_lds_barrier();
   // thread e: expert e's count, then exclusive scans over experts of the
   // counts (offsets) and of the m-tiles ceil(count / bm) (GEMM schedule)
   const int e = threadIdx.x;
@@ -60,7 +75,7 @@ __device__ __forceinline__ void permute_small_body(const int32_t* ids, int32_t* 
     wsum[wave] = incl[0];
     wsum[PM_WAVES + wave] = incl[1];
   }
-  __syncthreads();
+  pm_lds_barrier();
   int32_t before[2] = {0, 0};
   for (int w = 0; w < wave; ++w) {
     before[0] += wsum[w];
@@ -82,10 +97,11 @@ __device__ __forceinline__ void permute_small_body(const int32_t* ids, int32_t* 
     offsets[E] = (int32_t)N;
     if (mstart) mstart[E] = before[1] + incl[1];
   }
-  __syncthreads();
+  pm_lds_barrier();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int s = 0; s < PM_STEPS; ++s) {
+    if (s >= steps) break;  // uniform
     const int ee = my_e[s];
     uint64_t same = ~0ull;
 #pragma unroll

@@ -177,6 +177,15 @@ constexpr int RS_MAX_LOGITS = 16384;  // T * E staged in LDS
 constexpr int RS_LDS_WORDS =
     RS_MAX_LOGITS > PM_WAVES * MOE_MAX_EXPERTS_DEV ? RS_MAX_LOGITS : PM_WAVES * MOE_MAX_EXPERTS_DEV;
 
+// Workgroup barrier without a memory fence: LDS visibility comes from the
+// lgkmcnt(0) wait before it, and global stores still in flight are not
+// waited for (nothing in the workgroup reads them back).
+__device__ __forceinline__ void rs_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int TK_PER_LANE>
 __global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
     const float* __restrict__ partial, int splits, float* __restrict__ logits,
@@ -194,34 +203,37 @@ __global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
   float bv[TK_PER_LANE];
   topk_bias<TK_PER_LANE>(bias, E, lane, bv);
   // logits: slice partials summed in slice order; two elements per thread
-  // and pass, their 2 x 16 loads in flight together
+  // and pass, their 2 x RT_MAX_SPLITS loads in flight together.  The loads
+  // are unconditional (indices past the slices or past T*E are clamped to
+  // valid ones and their values dropped), so they issue back to back.
+  static_assert(RT_MAX_SPLITS == 16, "one pass over the slices");
   for (int i0 = threadIdx.x; i0 < TE; i0 += 2 * PM_THREADS) {
-    const int i1 = i0 + PM_THREADS;
-    float l0 = 0.f, l1 = 0.f;
-    for (int sp0 = 0; sp0 < splits; sp0 += 16) {
-      float p0[16], p1[16];
+    const int i1 = i0 + PM_THREADS < TE ? i0 + PM_THREADS : i0;
+    float p0[RT_MAX_SPLITS], p1[RT_MAX_SPLITS];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const bool in = sp0 + u < splits;
-        p0[u] = in ? partial[(int64_t)(sp0 + u) * TE + i0] : 0.f;
-        p1[u] = in && i1 < TE ? partial[(int64_t)(sp0 + u) * TE + i1] : 0.f;
-      }
+    for (int u = 0; u < RT_MAX_SPLITS; ++u) {
+      const int64_t su = u < splits ? u : splits - 1;
+      p0[u] = partial[su * TE + i0];
+      p1[u] = partial[su * TE + i1];
+    }
+    float l0 = p0[0], l1 = p1[0];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (sp0 + u < splits) {
-          l0 = sp0 + u == 0 ? p0[u] : l0 + p0[u];
-          l1 = sp0 + u == 0 ? p1[u] : l1 + p1[u];
-        }
+    for (int u = 1; u < RT_MAX_SPLITS; ++u) {
+      if (u < splits) {
+        l0 += p0[u];
+        l1 += p1[u];
       }
     }
     lg_lds[i0] = l0;
     if (splits > 1) logits[i0] = l0;
-    if (i1 < TE) {
+    if (i0 + PM_THREADS < TE) {
       lg_lds[i1] = l1;
       if (splits > 1) logits[i1] = l1;
     }
   }
-  __syncthreads();
+  // the logits in LDS everywhere (the global copies need not have landed)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  rs_barrier();
   for (int t = wave; t < T; t += PM_WAVES) {
     float lg[TK_PER_LANE];
 #pragma unroll
@@ -231,7 +243,9 @@ __global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
     }
     topk_select<TK_PER_LANE>(lg, bv, ids, wts, ids_lds, t, E, k, rsf, lane);
   }
-  __syncthreads();
+  // the picks in LDS everywhere (their global copies need not have landed)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  rs_barrier();
   permute_small_body(ids_lds, offsets, sorted_token, inv_pos, (int64_t)T * k, E, k, bm, mstart,
                      lds, wsum);
 }

@@ -46,12 +46,12 @@ __device__ __forceinline__ void topk_bias(const float* __restrict__ bias, int E,
 // of token t in ascending id order, the ids also to ids_copy when it is
 // not null (the same layout, e.g. in LDS).
 //
-// With at most two experts per lane (E <= 128) the selection is a count
-// instead: every key is compared with all E keys (read across the wave
-// with readlane, uniform indices), an expert is picked iff fewer than k
-// keys exceed its own, and a pick's slot is the number of picks with a
-// lower id (one ballot per half).  The keys are distinct (the id is part
-// of them), so both forms pick the same experts.
+// With at most two experts per lane (E <= 128) the selection is a
+// threshold search instead: the k-th largest score is found bit by bit with
+// one ballot per bit (and per half), the experts above it are picked, and
+// ties at it go to the lowest ids; a pick's slot is the number of picks
+// with a lower id (one ballot per half).  The keys order scores first and
+// ids second, so both forms pick the same experts.
 template <int TK_PER_LANE>
 __device__ __forceinline__ void topk_select(const float (&lg)[TK_PER_LANE],
                                             const float (&bv)[TK_PER_LANE],
@@ -71,25 +71,42 @@ __device__ __forceinline__ void topk_select(const float (&lg)[TK_PER_LANE],
     }
   }
   if constexpr (TK_PER_LANE <= 2) {
-    int above[TK_PER_LANE];
+    // the high words of the keys (the orderable scores; 0 for NaN), lanes
+    // past E excluded: the k-th largest score thr is the largest value with
+    // at least k scores >= it, found bit by bit from the top with one ballot
+    // per bit; the picks are every score above thr and, of those equal to
+    // it, the lowest ids (the order of the full keys)
+    uint32_t kv[TK_PER_LANE];
+    bool valid[TK_PER_LANE];
 #pragma unroll
-    for (int i = 0; i < TK_PER_LANE; ++i) above[i] = 0;
+    for (int i = 0; i < TK_PER_LANE; ++i) {
+      valid[i] = lane + 64 * i < E;
+      kv[i] = (uint32_t)(key[i] >> 32);
+    }
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-    for (int h = 0; h < TK_PER_LANE; ++h) {
-      const uint32_t klo = (uint32_t)key[h], khi = (uint32_t)(key[h] >> 32);
-      for (int j = 0; j < 64; ++j) {
-        const uint64_t other = ((uint64_t)__builtin_amdgcn_readlane(khi, j) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane(klo, j);
+      for (int i = 0; i < TK_PER_LANE; ++i) cnt += __popcll(__ballot(valid[i] && kv[i] >= cand));
+      if (cnt >= k) thr = cand;
+    }
+    uint64_t above[TK_PER_LANE], eq[TK_PER_LANE];
+    int need = k;  // picks still to make among the scores equal to thr
 #pragma unroll
-        for (int i = 0; i < TK_PER_LANE; ++i) above[i] += other > key[i] ? 1 : 0;
-      }
+    for (int i = 0; i < TK_PER_LANE; ++i) {
+      above[i] = __ballot(valid[i] && kv[i] > thr);
+      eq[i] = __ballot(valid[i] && kv[i] == thr);
+      need -= __popcll(above[i]);
     }
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int before = 0;   // picks in the halves of lower ids
+    int before = 0, eq_before = 0;  // picks and ties in the halves of lower ids
 #pragma unroll
     for (int i = 0; i < TK_PER_LANE; ++i) {
       const int e = lane + 64 * i;
-      const bool pick = e < E && above[i] < k;
+      const bool is_above = (above[i] >> lane) & 1ull;
+      const bool is_eq = (eq[i] >> lane) & 1ull;
+      const bool pick = is_above || (is_eq && eq_before + __popcll(eq[i] & lower) < need);
       const uint64_t picks = __ballot(pick);
       if (pick) {
         const int slot = before + __popcll(picks & lower);
@@ -98,6 +115,7 @@ __device__ __forceinline__ void topk_select(const float (&lg)[TK_PER_LANE],
         if (ids_copy) ids_copy[t * k + slot] = e;
       }
       before += __popcll(picks);
+      eq_before += __popcll(eq[i]);
     }
     return;
   }
