@@ -591,7 +591,7 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");
 
   // Weight streaming (decode-sized batches): the shared expert's two GEMMs
-  // run on the second stream, forked at the start, on 3/4 of the CUs, while
+  // run on the second stream, forked at the start, on half of the CUs, while
   // the routing kernels run on the rest; the combine waits for them.
   // MOE_SHARED_BESIDE=0 keeps the shared expert in the routed launches (a
   // tuning lever; the results are the same)
@@ -609,7 +609,7 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   };
   if ((s = mark(MOE_EV_BEGIN)) != MOE_OK) return s;
   if (beside) {
-    const int wgs = std::max(8, gemm_cu_count() * 3 / 4 / 8 * 8);
+    const int wgs = std::max(8, gemm_cu_count() / 2 / 8 * 8);
     if ((s = device_status(hipEventRecord(side->fork, stream), "fork")) != MOE_OK ||
         (s = device_status(hipStreamWaitEvent(side->stream, side->fork, 0), "fork")) != MOE_OK ||
         (s = device_status(launch_grouped_gemm(v, true, sgu, nullptr, p->swiglu_limit,

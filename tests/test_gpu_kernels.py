@@ -108,6 +108,59 @@ def test_router_ties_nan_and_no_bias(tl):
     assert np.all(np.isnan(logits_g[:, 7]))
 
 
+TIED = [3, 20, 40, 50, 63, 64, 70, 77, 90, 99]
+
+
+@pytest.mark.parametrize("case", ["nan_majority", "all_equal", "ties_across_halves"])
+def test_router_selection_edges(tl, case):
+    """Selections decided at the k-th score: more NaN logits than E - k (the
+    threshold falls to NaN, whose experts then go by lowest id), every
+    expert tied (ids 0..k-1), and ties at the k-th score that span both
+    halves of a 100-expert lane layout; against the oracle's selection, with
+    the separate top-k kernel and the fused decode routing."""
+    torch, moe = tl
+    rng = np.random.default_rng(11)
+    T, H = 24, 64
+    E, k = (12, 5) if case == "nan_majority" else (100, 8)
+    x = moe_inputs.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    bias = (rng.uniform(-0.1, 0.1, E)).astype(np.float32)
+    if case == "nan_majority":
+        wr[[0, 1, 3, 4, 6, 7, 8, 10, 11]] = np.nan   # 3 finite experts, k = 5
+    elif case == "all_equal":
+        wr[:] = wr[0]
+        bias[:] = 0.0
+    else:
+        # ten experts share the best row and bias: the picks are the eight
+        # lowest ids among them, across both 64-expert halves
+        for e in TIED:
+            wr[e] = wr[3]
+            bias[e] = 0.5
+    r = mo.topk_route(mo.router_logits(x, wr), bias, k, 1.0)
+    p = moe.make_params(T, H, E, k, 8, 0, 1.0, 7.0)
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(p, gh.dev_bf16(torch, x), gh.dev_f32(torch, wr), gh.dev_f32(torch, bias),
+                        ids, w, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), r["ids"])
+    if case == "all_equal":
+        np.testing.assert_array_equal(r["ids"], np.tile(np.arange(k), (T, 1)))
+    if case == "nan_majority":
+        assert np.all(np.isin([2, 5, 9], r["ids"]))
+    if case == "ties_across_halves":
+        np.testing.assert_array_equal(r["ids"], np.tile(TIED[:k], (T, 1)))
+    # the fused decode routing (top-k and permutation in one launch)
+    d = gh.Device(moe_inputs.Workload("edge", T=T, H=H, E=E, k=k, I=128, I_s=0),
+                  dict(x=x, w_router=wr, corr_bias=bias, w_gate_up=np.zeros((E, 256, H), np.uint16),
+                       w_down=np.zeros((E, H, 128), np.uint16), gamma_pre=None, gamma_post=None,
+                       x_cur=None, ws_gate_up=None, ws_down=None))
+    d.run()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d.result()["ids"], r["ids"])
+
+
 @pytest.mark.parametrize("T,H,E,k", [
     (32, 4096, 64, 8),     # the decode workload's routing
     (64, 128, 8, 2),       # tiny
