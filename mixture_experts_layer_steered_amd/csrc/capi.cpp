@@ -118,16 +118,19 @@ GemmVariant pick_variant_raw(int64_t rows, int64_t groups) {
 }
 
 // The pipelined and streaming variants address A rows and one group's
-// weights with 32-bit element offsets and step K in 32-wide units; other
-// operands fall back to the LDS-staged tiles.
+// weights with 32-bit element offsets and step K in 32-wide units, and the
+// pipelined tiles address a tile's output with 32-bit byte offsets (output
+// widths up to 2^20); other operands fall back to the LDS-staged tiles.
 GemmVariant pick_variant(int64_t rows, int64_t groups, int64_t a_elems, int64_t w_group_elems,
-                         bool k_multiple_of_32) {
+                         bool k_multiple_of_32, int64_t max_width) {
   GemmVariant v = pick_variant_raw(rows, groups);
   const int64_t lim = (int64_t)1 << 31;
   if (v == GemmVariant::kWStream && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32))
     v = GemmVariant::kTile32;
   const bool pipe = v == GemmVariant::kPipe256W8 || v == GemmVariant::kPingPong;
-  if (pipe && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32)) v = GemmVariant::kTile128;
+  if (pipe && (a_elems >= lim || w_group_elems >= lim || !k_multiple_of_32 ||
+               max_width > ((int64_t)1 << 20)))
+    v = GemmVariant::kTile128;
   return v;
 }
 
@@ -157,7 +160,8 @@ GemmVariant layer_variant(const moe_params& p) {
   const int64_t N = p.T * p.k;
   return pick_variant(N, p.E, std::max<int64_t>(N, p.T) * std::max(p.H, std::max(p.I, p.I_shared)),
                       (int64_t)2 * std::max(p.I, p.I_shared) * p.H,
-                      p.H % 32 == 0 && p.I % 32 == 0 && p.I_shared % 32 == 0);
+                      p.H % 32 == 0 && p.I % 32 == 0 && p.I_shared % 32 == 0,
+                      std::max(p.H, std::max(p.I, p.I_shared)));
 }
 
 // W4A16 routed experts are read as codes by the weight-streaming and
@@ -414,7 +418,7 @@ moe_status moe_grouped_swiglu_gemm(int32_t n_groups, int64_t M_total, int32_t H,
   // gathered rows can repeat, the routed case), the down A is h [M_total, I].
   const GemmVariant v =
       pick_variant(M_total, n_groups, std::max<int64_t>(M_total, 1) * std::max(H, I),
-                   (int64_t)2 * I * H, H % 32 == 0 && I % 32 == 0);
+                   (int64_t)2 * I * H, H % 32 == 0 && I % 32 == 0, std::max(H, I));
   int32_t* mstart = static_cast<int32_t*>(ws);
   GemmProblem gu = make_problem(a, row_index, group_offsets, mstart, w_gate_up,
                                 (int64_t)2 * I * H, h, M_total, n_groups, I, H, v, true);

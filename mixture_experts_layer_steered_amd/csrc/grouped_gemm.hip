@@ -346,6 +346,7 @@ struct PipeShape {
   static constexpr int NMAT = GATEUP ? 2 : 1;
   static constexpr int SUB = KB / 16;              // MFMA K substeps per stage
   static constexpr int A_INSTR = BM / (NW * RPI);  // instructions of each wave that fill A rows
+  static constexpr int STORES = TM * TN * 4;       // epilogue stores per wave
   static_assert(INSTR % NW == 0 && SUB % 2 == 0, "shape");
   static_assert(BM % (NW * RPI) == 0, "A rows fill whole instructions of every wave");
 };
@@ -403,25 +404,43 @@ __device__ __forceinline__ int pipe_coords(const GemmProblem& P, int mt_total, i
   return g;
 }
 
-// Byte offset of the A piece that lane `lane` of load instruction i of wave
-// `wave` fetches (its row clamped to the tile's first row past the segment).
-// The gathered source rows are per-lane vector loads; their wait, once per
-// tile, finds the stage loads in flight mostly landed (measured: reading
-// them through the scalar cache instead, 16 loads and selects per
-// instruction, was slower).
+// Row of the A piece that lane `lane` of load instruction i of wave `wave`
+// fetches, in the problem's row space (clamped to the tile's first row past
+// the segment).
 template <class S>
-__device__ __forceinline__ uint32_t pipe_a_off(const GemmProblem& P, const PipeTile<S>& T, int i,
-                                               int wave, int lane) {
+__device__ __forceinline__ int32_t pipe_a_row(const PipeTile<S>& T, int i, int wave, int lane) {
+  const int row = S::RPI * (wave + S::NW * i) + lane / S::CHUNKS;
+  return (int32_t)(T.row0 + row < T.row_end ? T.row0 + row : T.row0);
+}
+
+// Byte offset of that piece, from its source row in A.
+template <class S>
+__device__ __forceinline__ uint32_t pipe_a_off_of(int K, int32_t a_row, int i, int wave,
+                                                  int lane) {
   const int row = S::RPI * (wave + S::NW * i) + lane / S::CHUNKS;
   const int chunk = pl_swz<S::KB>(row, lane % S::CHUNKS);
-  const int64_t gr = T.row0 + row < T.row_end ? T.row0 + row : T.row0;
-  const int64_t a_row = P.row_index ? (int64_t)P.row_index[gr] : gr;
-  return (uint32_t)((a_row * P.K + chunk * 8) * 2);
+  return (uint32_t)(((int64_t)a_row * K + chunk * 8) * 2);
 }
 
 template <class S>
-__device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, int tile,
-                                            PipeTile<S>& T) {
+__device__ __forceinline__ uint32_t pipe_a_off(const GemmProblem& P, const PipeTile<S>& T, int i,
+                                               int wave, int lane) {
+  const int32_t r = pipe_a_row<S>(T, i, wave, lane);
+  return pipe_a_off_of<S>(P.K, P.row_index ? P.row_index[r] : r, i, wave, lane);
+}
+
+// Tile T's place in three parts.  pipe_locate_coords: coordinates, weight
+// offsets, and the A rows in the problem's row space (in T.off[i <
+// A_INSTR]); pipe_locate_rows: those rows through row_index when A is
+// gathered (per-lane vector loads, which may still be in flight after it;
+// measured: reading the rows through the scalar cache instead, 16 loads and
+// selects per instruction, was slower); pipe_locate_end: the rows to byte
+// offsets.  Between the last two the caller can run steps whose waits see
+// the row loads land, so that no wait for them drains the stage loads and
+// stores issued before them.
+template <class S>
+__device__ __forceinline__ void pipe_locate_coords(const GemmProblem& P, int mt_total, int tile,
+                                                   PipeTile<S>& T) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = pipe_coords<S>(P, mt_total, tile, T);
@@ -432,7 +451,7 @@ __device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, 
     const int row = S::RPI * (wave + S::NW * i) + lane / S::CHUNKS;
     const int chunk = pl_swz<S::KB>(row, lane % S::CHUNKS);
     if (i < S::A_INSTR) {
-      T.off[i] = pipe_a_off<S>(P, T, i, wave, lane);
+      T.off[i] = (uint32_t)pipe_a_row<S>(T, i, wave, lane);
     } else {
       const int r = row - S::BM;
       int n = S::GATEUP ? T.n0 + (r < S::BN ? r : r - S::BN) : T.n0 + r;
@@ -441,6 +460,31 @@ __device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, 
       T.off[i] = (uint32_t)(((int64_t)(up ? N + n : n) * K + chunk * 8) * 2);
     }
   }
+}
+
+template <class S>
+__device__ __forceinline__ void pipe_locate_rows(const int32_t* row_index, PipeTile<S>& T) {
+  if (row_index != nullptr) {
+#pragma unroll
+    for (int i = 0; i < S::A_INSTR; ++i) T.off[i] = (uint32_t)row_index[T.off[i]];
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void pipe_locate_end(int K, PipeTile<S>& T) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < S::A_INSTR; ++i)
+    T.off[i] = pipe_a_off_of<S>(K, (int32_t)T.off[i], i, wave, lane);
+}
+
+template <class S>
+__device__ __forceinline__ void pipe_locate(const GemmProblem& P, int mt_total, int tile,
+                                            PipeTile<S>& T) {
+  pipe_locate_coords<S>(P, mt_total, tile, T);
+  pipe_locate_rows<S>(P.row_index, T);
+  pipe_locate_end<S>(P.K, T);
 }
 
 // This wave's loads of the K columns [k0, k0 + KB) of tile T into LDS slot
@@ -511,24 +555,40 @@ __device__ __forceinline__ f32x16_t pipe_mfma(const bf16x8_t& w, const bf16x8_t&
 // per register, turned into four adjacent columns of one row by a quad
 // transpose (lane 4a+b: row 8*g + 4*(L/32) + b, columns 4a..4a+3 of the
 // block, for each group g of four registers).
-// (wm, wn): the wave's row half and column block of the tile.
+//
+// The stores are buffer stores through a resource that spans exactly the
+// tile's rows of the output ([row0, min(row_end, row0 + BM)) x N): lanes
+// past the segment fall outside it, lanes past N are sent outside it, and
+// the buffer range check drops both.  So every wave issues exactly
+// S::STORES stores for every tile, and the stage waits right after an
+// epilogue can count them (pipe offsets stay below 2^31: N <= 2^20, which
+// the host checks).  (wm, wn): the wave's row half and column block.
+template <class S>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pipe_out_rsrc(const GemmProblem& P,
+                                                                const PipeTile<S>& T) {
+  constexpr int ES = S::GATEUP ? 2 : 4;  // bytes per output element
+  const int64_t rows = T.row_end - T.row0 < S::BM ? T.row_end - T.row0 : S::BM;
+  char* base = static_cast<char*>(P.out) + T.row0 * P.N * ES;
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)(rows * P.N * ES), 0x00020000);
+}
+
 template <class S>
 __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<S>& T,
                                            const f32x16_t (&acc)[S::NMAT][S::TM][S::TN],
                                            float limit, int wm, int wn) {
   const int lane = threadIdx.x & 63;
   const int N = P.N;
+  const __amdgpu_buffer_rsrc_t rs = pipe_out_rsrc<S>(P, T);
+  constexpr uint32_t kOut = 0x80000000u;  // past every tile's resource
   if constexpr (S::GATEUP) {
 #pragma unroll
     for (int i = 0; i < S::TM; ++i) {
-      const int64_t row = T.row0 + wm * S::WM + i * 32 + (lane & 31);
-      if (row >= T.row_end) continue;
+      const int r = wm * S::WM + i * 32 + (lane & 31);
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int col = T.n0 + wn * S::WN + j * 32 + 8 * q + 4 * (lane >> 5);
-          if (col >= N) continue;
           const f32x16_t& g = acc[0][i][j];
           const f32x16_t& u = acc[S::NMAT - 1][i][j];
           const float ts = T.ts;
@@ -538,7 +598,8 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
                           swiglu_clamped_fast(g[4 * q + 3] * ts, u[4 * q + 3] * ts, limit)};
           uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
                         __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
-          *reinterpret_cast<uint2_t*>(static_cast<uint16_t*>(P.out) + row * N + col) = pk;
+          const uint32_t off = col < N ? (uint32_t)(r * N + col) * 2u : kOut;
+          __builtin_amdgcn_raw_buffer_store_b64(pk, rs, off, 0, 0);
         }
       }
     }
@@ -546,7 +607,6 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
     // registers 4g..4g+3 hold a 4 (rows) x 1 (column) piece; the four lanes
     // of a quad together hold a 4x4 block, which quad_transpose turns into
     // one row of four adjacent columns per lane
-    float* out = static_cast<float*>(P.out);
     const int quad = (lane & 31) >> 2;
 #pragma unroll
     for (int i = 0; i < S::TM; ++i)
@@ -557,11 +617,27 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
           f32x4_t v = {acc[0][i][j][4 * g] * T.ts, acc[0][i][j][4 * g + 1] * T.ts,
                        acc[0][i][j][4 * g + 2] * T.ts, acc[0][i][j][4 * g + 3] * T.ts};
           quad_transpose(v);
-          const int64_t row = T.row0 + wm * S::WM + i * 32 + 8 * g + 4 * (lane >> 5) + (lane & 3);
+          const int r = wm * S::WM + i * 32 + 8 * g + 4 * (lane >> 5) + (lane & 3);
           const int col = T.n0 + wn * S::WN + j * 32 + 4 * quad;
-          if (row < T.row_end && col < N)
-            *reinterpret_cast<f32x4_t*>(out + row * N + col) = v;
+          const uint32_t off = col < N ? (uint32_t)(r * N + col) * 4u : kOut;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
         }
+  }
+}
+
+// The same number of stores as pipe_store, all dropped (an empty resource):
+// stands in for the epilogue of the tile before a workgroup's first, so that
+// the first tile's stage waits count the same queue as every later tile's.
+template <class S>
+__device__ __forceinline__ void pipe_store_none(const GemmProblem& P) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(P.out, (short)0, 0, 0x00020000);
+#pragma unroll
+  for (int q = 0; q < S::STORES; ++q) {
+    if constexpr (S::GATEUP)
+      __builtin_amdgcn_raw_buffer_store_b64(uint2_t{0u, 0u}, rs, 0u, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{0.f, 0.f, 0.f, 0.f}, rs, 0u, 0, 0);
   }
 }
 
@@ -773,8 +849,9 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pipe_kernel(GemmProblem
 // barrier that ends group 1's memory phase of step s.  Every step issues one
 // stage (past the last tile, the last stage again), so "the next stage
 // landed" is always "at most AHEAD-1 newer stages of this wave's loads in
-// flight" -- epilogue stores between them only make that wait stricter.
-// Needs K >= AHEAD * KB for every problem (the host checks).
+// flight" (the first AHEAD-1 steps of a tile also allow for the previous
+// tile's epilogue stores, see `step`).  Needs K >= 2 AHEAD KB for every
+// problem (the host checks).
 template <class S, int STAGES>
 __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p0, GemmProblem p1,
                                                                    int has_p1, float limit) {
@@ -796,11 +873,20 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
   // by whole wavefronts
   const int group = __builtin_amdgcn_readfirstlane(wave >> 2);
 
-  auto locate = [&](int tt, PipeTile<S>& T) __attribute__((always_inline)) {
-    if (tt < R.tiles0)
-      pipe_locate<S>(p0, R.mt0, tt, T);
-    else
-      pipe_locate<S>(p1, R.mt1, tt - R.tiles0, T);
+  // (the compiler merges the two branches' row loads into one; passing the
+  // selected problem's row_index to a single call instead made it keep the
+  // tiles in scratch memory)
+  auto locate_begin = [&](int tt, PipeTile<S>& T) __attribute__((always_inline)) {
+    if (tt < R.tiles0) {
+      pipe_locate_coords<S>(p0, R.mt0, tt, T);
+      pipe_locate_rows<S>(p0.row_index, T);
+    } else {
+      pipe_locate_coords<S>(p1, R.mt1, tt - R.tiles0, T);
+      pipe_locate_rows<S>(p1.row_index, T);
+    }
+  };
+  auto locate_end = [&](int tt, PipeTile<S>& T) __attribute__((always_inline)) {
+    pipe_locate_end<S>(tt < R.tiles0 ? p0.K : p1.K, T);
   };
   auto stages_of = [&](int tt) __attribute__((always_inline)) {
     return (tt < R.tiles0 ? p0.K : p1.K) / KB;
@@ -847,35 +933,61 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
   };
 
   PipeTile<S> cur, nxt;
-  locate(t, cur);
+  locate_begin(t, cur);
+  locate_end(t, cur);
   int nk = stages_of(t);
 #pragma unroll
   for (int s0 = 0; s0 < AHEAD; ++s0) pipe_issue<S>(cur, smem, s0, s0 * KB);
   PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
   pp_barrier();  // stage 0 complete everywhere
   if (group) pp_barrier();
+  pipe_store_none<S>(p0);
   int slot = 0, slot_issue = AHEAD;
+  // One step: read stage kt's fragments, issue this wave's loads of the
+  // stage AHEAD ahead into the slot read in the step before (from tile src
+  // at K offset k0), wait for its loads of stage kt+1, barrier, MFMAs,
+  // barrier.  The waits of the first AHEAD-1 steps of
+  // a tile (RELAXED) let the previous epilogue's S::STORES stores stay in
+  // flight: they were issued after stages 0..AHEAD-1 of this tile and
+  // before stage AHEAD, so "stage kt+1 landed" is "at most (AHEAD-1)
+  // VM_STAGE + STORES newer operations in flight" (the A row loads of the
+  // next tile, issued after the stores, only make that stricter); from step
+  // AHEAD-1 on, the stage waited for is younger than the stores.
+  auto step = [&](const PipeTile<S>& src, int k0, auto relaxed_c) __attribute__((always_inline)) {
+    read_stage(slot);
+    pipe_issue<S>(src, smem, slot_issue, k0);
+    if constexpr (decltype(relaxed_c)::value)
+      PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE + S::STORES);
+    else
+      PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
+    pp_barrier();
+    compute();
+    pp_barrier();
+    slot = slot + 1 == STAGES ? 0 : slot + 1;
+    slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
+  };
+  using T0 = std::integral_constant<bool, false>;
+  using T1 = std::integral_constant<bool, true>;
   for (;;) {
     const int t_next = t + R.stride;
     const bool more = t_next < R.t_end;
-    if (more) locate(t_next, nxt);
+    // the next tile's A rows load while this tile's first AHEAD steps run
+    // (their stages are this tile's: nk >= 2 AHEAD); the offsets are formed
+    // after step AHEAD-1, whose wait has seen the rows land.  The last AHEAD
+    // steps issue the next tile's first stages -- past the last tile, this
+    // tile's first stages again, into slots nothing reads any more.
+    if (more) locate_begin(t_next, nxt);
     pipe_zero<S>(acc);
-    for (int kt = 0; kt < nk; ++kt) {
-      read_stage(slot);
-      const int ka = kt + AHEAD;
-      if (ka < nk)
-        pipe_issue<S>(cur, smem, slot_issue, ka * KB);
-      else if (more)
-        pipe_issue<S>(nxt, smem, slot_issue, (ka - nk) * KB);
-      else
-        pipe_issue<S>(cur, smem, slot_issue, (nk - 1) * KB);
-      PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
-      pp_barrier();
-      compute();
-      pp_barrier();
-      slot = slot + 1 == STAGES ? 0 : slot + 1;
-      slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
-    }
+#pragma unroll
+    for (int kt = 0; kt < AHEAD - 1; ++kt) step(cur, (kt + AHEAD) * KB, T1{});
+    step(cur, (2 * AHEAD - 1) * KB, T0{});
+    if (more)
+      locate_end(t_next, nxt);
+    else
+      nxt = cur;
+    for (int kt = AHEAD; kt < nk - AHEAD; ++kt) step(cur, (kt + AHEAD) * KB, T0{});
+#pragma unroll 1
+    for (int q = 0; q < AHEAD; ++q) step(nxt, q * KB, T0{});
     pipe_store<S>(t < R.tiles0 ? p0 : p1, cur, acc, limit, wm, wn);
     if (!more) break;
     t = t_next;
@@ -2088,9 +2200,9 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
     return launch_pipe<256, 256, false, 32, 5, 2, 8, false>(a, b, limit, stream);
   }
   if (v == GemmVariant::kPingPong) {  // eight wavefronts taking turns on each SIMD
-    // the cross-tile stage stream needs at least STAGES-1 = 4 stages per tile;
-    // shorter K takes the interleaved schedule of the same tile
-    if (a.K < 4 * 32 || (b != nullptr && b->K < 4 * 32)) {
+    // the cross-tile stage stream needs at least 2 (STAGES-1) = 8 stages per
+    // tile; shorter K takes the interleaved schedule of the same tile
+    if (a.K < 8 * 32 || (b != nullptr && b->K < 8 * 32)) {
       if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false>(a, b, limit, stream);
       return launch_pipe<256, 256, false, 32, 5, 2, 8, false>(a, b, limit, stream);
     }
