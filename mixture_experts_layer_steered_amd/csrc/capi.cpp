@@ -165,11 +165,13 @@ GemmVariant layer_variant(const moe_params& p) {
 }
 
 // W4A16 routed experts are read as codes by the weight-streaming and
-// ping-pong kernels; the other tile variants (forced by MOE_GEMM_VARIANT, or
-// the 128-row tiles of mid-sized batches) read them dequantised to bf16 in
-// the workspace.
-bool w4_codes_variant(const moe_params&, GemmVariant v) {
-  return v == GemmVariant::kWStream || v == GemmVariant::kPingPong;
+// ping-pong kernels (the latter for K >= 256 in both projections: H, I >=
+// 256); the other tile variants (forced by MOE_GEMM_VARIANT, or the 128-row
+// tiles of mid-sized batches) read them dequantised to bf16 in the
+// workspace.
+bool w4_codes_variant(const moe_params& p, GemmVariant v) {
+  return v == GemmVariant::kWStream ||
+         (v == GemmVariant::kPingPong && p.H >= 256 && p.I >= 256);
 }
 bool w4_dequant_batch(const moe_params& p) {
   return p.w4 && !w4_codes_variant(p, layer_variant(p));

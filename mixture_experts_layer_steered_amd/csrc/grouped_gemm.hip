@@ -1031,9 +1031,10 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
 // two steps earlier, and its first stage is dequantised three steps later,
 // after the wait that sees the A stage issued behind it land.  The wait for
 // "the next A stage landed" leaves 9 loads in flight, or 6 when no code
-// group was issued in the last three steps (stage index 3 mod 4).  The
-// tensor scale multiplies the accumulators in the epilogue.  K must be a
-// multiple of 128.
+// group was issued in the last three steps (stage index 3 mod 4), plus the
+// previous epilogue's stores in a tile's first three steps.  The tensor
+// scale multiplies the accumulators in the epilogue.  K must be a multiple
+// of 128 and at least 256.
 template <class S>
 struct PpW4Layout {
   static constexpr int STAGES = 5;                         // A slots
@@ -1090,14 +1091,18 @@ struct PpW4Tile {
   uint32_t off_c0, off_c1, off_s;
 };
 
+// Everything but the A offsets, as pipe_locate_coords + pipe_locate_rows (the
+// A source rows in T.t.off[i < A_INSTR], loads possibly in flight); then
+// pipe_locate_end turns them into offsets.
 template <class S>
-__device__ __forceinline__ void pp_w4_locate(const GemmProblem& P, int mt_total, int tile,
-                                             int wave, PpW4Tile<S>& T) {
+__device__ __forceinline__ void pp_w4_locate_begin(const GemmProblem& P, int mt_total, int tile,
+                                                   int wave, PpW4Tile<S>& T) {
   using L = PpW4Layout<S>;
   const int lane = threadIdx.x & 63;
   const int g = pipe_coords<S>(P, mt_total, tile, T.t);
 #pragma unroll
-  for (int i = 0; i < S::A_INSTR; ++i) T.t.off[i] = pipe_a_off<S>(P, T.t, i, wave, lane);
+  for (int i = 0; i < S::A_INSTR; ++i) T.t.off[i] = (uint32_t)pipe_a_row<S>(T.t, i, wave, lane);
+  pipe_locate_rows<S>(P.row_index, T.t);
   T.t.rs_w = pl_rsrc(reinterpret_cast<const uint8_t*>(P.W) + (int64_t)g * P.w_stride * 2);
   T.rs_s = pl_rsrc(P.S + (int64_t)g * P.s_stride);
   const int grp = wave >> 2, q = wave & 3;
@@ -1302,7 +1307,8 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   };
 
   PpW4Tile<S> cur, nxt;
-  pp_w4_locate<S>(p0, R.mt0, t, wave, cur);
+  pp_w4_locate_begin<S>(p0, R.mt0, t, wave, cur);
+  pipe_locate_end<S>(p0.K, cur.t);
   // The stream: stage ss of the workgroup's stage stream (ss counts across
   // tiles; every tile has nk stages, a multiple of 4) sits in A slot
   // ss % STAGES and ring slot ss % 2; code group ss / 4 in code slot
@@ -1317,48 +1323,57 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   PL_WAIT_LDS();
   pp_barrier();  // stage 0's weights in ring slot 0
   if (group) pp_barrier();
+  pipe_store_none<S>(p0);
   int ss = 0;  // stream index of the stage being read
+  // Step kt of a tile: read stream stage ss; at a code group's first stage,
+  // this group's half of code group cg of tile src (the next group: of this
+  // tile, else group 0 of the next one), then A stage k0 of src (AHEAD
+  // ahead); wait for this wave's loads of A stage ss+1 (and, with them,
+  // every code load issued before it); dequantise stage ss+1 beside this
+  // stage's MFMAs.  As in the bf16 tile, the first AHEAD-1 steps of a tile
+  // (RELAXED) also let the previous epilogue's S::STORES stores stay in
+  // flight (issued after this tile's A stages 0..AHEAD-1 and code group 0,
+  // before its code group 1 and A stage AHEAD).
+  auto step = [&](int kt, const PpW4Tile<S>& src, int cg, int k0, auto relaxed_c)
+                  __attribute__((always_inline)) {
+    constexpr int EXTRA = decltype(relaxed_c)::value ? S::STORES : 0;
+    read_stage(ss % STAGES, ss & 1);
+    if ((kt & 3) == 0)
+      pp_w4_issue_c<S>(src, smem, (ss / L::G_STAGES + 1) & 1, cg, wave, wr_total);
+    pp_w4_issue_a<S>(src, smem, (ss + AHEAD) % STAGES, k0, wave);
+    if ((kt & 3) == 3)
+      PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM + EXTRA);
+    else
+      PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM + L::C_VM + EXTRA);
+    pp_barrier();
+    dequant(ss + 1, (ss + 1) & 1, true);  // the next stage of the stream, beside this one's MFMAs
+    PL_WAIT_LDS();
+    pp_barrier();
+    ++ss;
+  };
+  using T0 = std::integral_constant<bool, false>;
+  using T1 = std::integral_constant<bool, true>;
+  static_assert(AHEAD == L::G_STAGES, "the first AHEAD steps issue code group 1 only");
   for (;;) {
     const int t_next = t + R.stride;
     const bool more = t_next < R.t_end;
-    if (more) pp_w4_locate<S>(p0, R.mt0, t_next, wave, nxt);
+    // as in the bf16 tile: the next tile's A rows load during the first
+    // AHEAD steps (whose stages are all this tile's: nk >= 2 AHEAD), and
+    // the last AHEAD steps issue the next tile's first code group and A
+    // stages (past the last tile, this tile's again, into free slots)
+    if (more) pp_w4_locate_begin<S>(p0, R.mt0, t_next, wave, nxt);
     pipe_zero<S>(acc);
-    for (int kt = 0; kt < nk; ++kt, ++ss) {
-      read_stage(ss % STAGES, ss & 1);
-      // at a code group's first stage: this group's half of the next code
-      // group (of this tile, else of the next one; past the last tile, the
-      // last group again, into a slot nothing reads any more) ...
-      if ((kt & 3) == 0) {
-        const int cg = kt / L::G_STAGES + 1;
-        const int cslot = (ss / L::G_STAGES + 1) & 1;
-        if (cg < ng)
-          pp_w4_issue_c<S>(cur, smem, cslot, cg, wave, wr_total);
-        else if (more)
-          pp_w4_issue_c<S>(nxt, smem, cslot, 0, wave, wr_total);
-        else
-          pp_w4_issue_c<S>(cur, smem, cslot, ng - 1, wave, wr_total);
-      }
-      // ... then A stage kt + AHEAD of this tile (or of the next one; past
-      // the last tile, the last stage again)
-      const int ka = kt + AHEAD;
-      const int sa = (ss + AHEAD) % STAGES;
-      if (ka < nk)
-        pp_w4_issue_a<S>(cur, smem, sa, ka * KB, wave);
-      else if (more)
-        pp_w4_issue_a<S>(nxt, smem, sa, (ka - nk) * KB, wave);
-      else
-        pp_w4_issue_a<S>(cur, smem, sa, (nk - 1) * KB, wave);
-      // own loads of A stage ss+1 landed (and, with them, every code load
-      // issued before it)
-      if ((kt & 3) == 3)
-        PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM);
-      else
-        PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM + L::C_VM);
-      pp_barrier();
-      dequant(ss + 1, (ss + 1) & 1, true);  // the next stage of the stream, beside this one's MFMAs
-      PL_WAIT_LDS();
-      pp_barrier();
-    }
+#pragma unroll
+    for (int kt = 0; kt < AHEAD - 1; ++kt) step(kt, cur, 1, (kt + AHEAD) * KB, T1{});
+    step(AHEAD - 1, cur, 1, (2 * AHEAD - 1) * KB, T0{});
+    if (more)
+      pipe_locate_end<S>(p0.K, nxt.t);
+    else
+      nxt = cur;
+    for (int kt = AHEAD; kt < nk - AHEAD; ++kt)
+      step(kt, cur, kt / L::G_STAGES + 1, (kt + AHEAD) * KB, T0{});
+#pragma unroll 1
+    for (int q = 0; q < AHEAD; ++q) step(nk - AHEAD + q, nxt, 0, q * KB, T0{});
     pipe_store<S>(p0, cur.t, acc, limit, wm, wn);
     if (!more) break;
     t = t_next;
@@ -2181,7 +2196,7 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
   if (a.S != nullptr) {  // W4A16 weights: one problem per launch
     if (b != nullptr || a.K % 128 != 0) return hipErrorInvalidValue;
     if (v == GemmVariant::kPingPong) {  // long segments: the ping-pong tile
-      if (a.K < 128 || a.N % 32 != 0) return hipErrorInvalidValue;
+      if (a.K < 256 || a.N % 32 != 0) return hipErrorInvalidValue;
       if (gateup) return launch_pp_w4<true>(a, limit, stream);
       return launch_pp_w4<false>(a, limit, stream);
     }

@@ -166,12 +166,16 @@ def test_entry_points_reject_before_launch():
         assert ei.value.status == moe.MOE_ERR_WORKSPACE
     # mid-sized W4A16 batches (the 128-row tiles) read the experts dequantised
     # in the workspace (E * 3 * I * H bf16); prefill-sized ones (the
-    # ping-pong tile) and decode-sized ones unpack the codes in the kernel
+    # ping-pong tile, K >= 256 in both projections) and decode-sized ones
+    # unpack the codes in the kernel
     extra = moe.moe_workspace_size(P(T=1024, w4=True)) - moe.moe_workspace_size(P(T=1024))
     assert extra >= 8 * 3 * 256 * 128 * 2
-    for T in (64, 4096):
-        assert moe.moe_workspace_size(P(T=T, w4=True)) == moe.moe_workspace_size(P(T=T))
     assert moe.moe_workspace_size(P(T=64, w4=True)) == moe.moe_workspace_size(P(T=64))
+    assert (moe.moe_workspace_size(P(T=4096, H=256, w4=True))
+            == moe.moe_workspace_size(P(T=4096, H=256)))
+    # prefill-sized with H = 128 < 256: dequantised as well
+    extra = moe.moe_workspace_size(P(T=4096, w4=True)) - moe.moe_workspace_size(P(T=4096))
+    assert extra >= 8 * 3 * 256 * 128 * 2
 
 
 def test_finish_validation():

@@ -345,12 +345,14 @@ def test_forward_prefill_finish_full_sampled():
 W4_TILED = {
     # ~300 rows per expert: the LDS-tiled GEMM on the dequantised experts
     "w4_tiled": Workload("w4_tiled", T=600, H=256, E=4, k=2, I=256, I_s=128, w4=True),
-    # ~2400 rows per expert: the W4A16 ping-pong tile; no shared expert;
-    # down K = 128 (one code group per tile: the stream fetches the next
-    # tile's first group during the only one) and N = 384 (a half-empty last
-    # column tile)
-    "w4_pingpong": Workload("w4_pingpong", T=2400, H=384, E=4, k=2, I=128, I_s=0, w4=True),
-    # two code groups per tile in down
+    # ~2400 rows per expert, but I = 128: the W4A16 ping-pong tile needs
+    # K >= 256 in both projections, so the experts are dequantised and run
+    # through the bf16 tiles (down, K = 128, in the interleaved schedule)
+    "w4_prefill_k128": Workload("w4_prefill_k128", T=2400, H=384, E=4, k=2, I=128, I_s=0,
+                                w4=True),
+    # the W4A16 ping-pong tile at its shortest K: down K = 256, two code
+    # groups per tile (every step is one of a tile's first or last four);
+    # N = 384 (a half-empty last column tile); no shared expert
     "w4_pingpong_k256": Workload("w4_pingpong_k256", T=2400, H=384, E=4, k=2, I=256, I_s=0,
                                  w4=True),
     # 4096 rows per expert: two or more tiles per workgroup in both
