@@ -563,16 +563,35 @@ __device__ __forceinline__ f32x16_t pipe_mfma(const bf16x8_t& w, const bf16x8_t&
 // S::STORES stores for every tile, and the stage waits right after an
 // epilogue can count them (pipe offsets stay below 2^31: N <= 2^20, which
 // the host checks).  (wm, wn): the wave's row half and column block.
+// (The resource's fields go through readfirstlane: they are uniform, and a
+// resource the compiler cannot prove uniform costs a loop around every
+// store.)
 template <class S>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pipe_out_rsrc(const GemmProblem& P,
                                                                 const PipeTile<S>& T) {
   constexpr int ES = S::GATEUP ? 2 : 4;  // bytes per output element
   const int64_t rows = T.row_end - T.row0 < S::BM ? T.row_end - T.row0 : S::BM;
-  char* base = static_cast<char*>(P.out) + T.row0 * P.N * ES;
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)(rows * P.N * ES), 0x00020000);
+  const uint64_t base = reinterpret_cast<uint64_t>(static_cast<char*>(P.out) + T.row0 * P.N * ES);
+  const uint64_t b = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+  const int nrec = __builtin_amdgcn_readfirstlane((int)(rows * P.N * ES));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(b), (short)0, nrec, 0x00020000);
 }
 
-template <class S>
+// One epilogue store at byte offset `off` of resource rs.  The offset passes
+// through an empty asm statement so that the compiler can neither merge nor
+// drop stores (several go to the same dropped offset): the stage waits after
+// an epilogue count exactly S::STORES of them.
+__device__ __forceinline__ void pipe_st64(uint2_t v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+}
+__device__ __forceinline__ void pipe_st128(f32x4_t v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+}
+
+template <class S, bool HALF = false>
 __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<S>& T,
                                            const f32x16_t (&acc)[S::NMAT][S::TM][S::TN],
                                            float limit, int wm, int wn) {
@@ -580,10 +599,14 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
   const int N = P.N;
   const __amdgpu_buffer_rsrc_t rs = pipe_out_rsrc<S>(P, T);
   constexpr uint32_t kOut = 0x80000000u;  // past every tile's resource
+  // a half-height tile (HALF): the wave's rows start at wm WM/2 and only
+  // its first TM/2 row blocks hold sums; the others' stores are dropped
+  constexpr int WROWS = HALF ? S::WM / 2 : S::WM;
+  auto live = [](int i) { return !HALF || i < S::TM / 2; };
   if constexpr (S::GATEUP) {
 #pragma unroll
     for (int i = 0; i < S::TM; ++i) {
-      const int r = wm * S::WM + i * 32 + (lane & 31);
+      const int r = wm * WROWS + i * 32 + (lane & 31);
 #pragma unroll
       for (int j = 0; j < S::TN; ++j) {
 #pragma unroll
@@ -598,8 +621,7 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
                           swiglu_clamped_fast(g[4 * q + 3] * ts, u[4 * q + 3] * ts, limit)};
           uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
                         __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
-          const uint32_t off = col < N ? (uint32_t)(r * N + col) * 2u : kOut;
-          __builtin_amdgcn_raw_buffer_store_b64(pk, rs, off, 0, 0);
+          pipe_st64(pk, rs, live(i) && col < N ? (uint32_t)(r * N + col) * 2u : kOut);
         }
       }
     }
@@ -617,10 +639,9 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
           f32x4_t v = {acc[0][i][j][4 * g] * T.ts, acc[0][i][j][4 * g + 1] * T.ts,
                        acc[0][i][j][4 * g + 2] * T.ts, acc[0][i][j][4 * g + 3] * T.ts};
           quad_transpose(v);
-          const int r = wm * S::WM + i * 32 + 8 * g + 4 * (lane >> 5) + (lane & 3);
+          const int r = wm * WROWS + i * 32 + 8 * g + 4 * (lane >> 5) + (lane & 3);
           const int col = T.n0 + wn * S::WN + j * 32 + 4 * quad;
-          const uint32_t off = col < N ? (uint32_t)(r * N + col) * 4u : kOut;
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+          pipe_st128(v, rs, live(i) && col < N ? (uint32_t)(r * N + col) * 4u : kOut);
         }
   }
 }
@@ -635,9 +656,9 @@ __device__ __forceinline__ void pipe_store_none(const GemmProblem& P) {
 #pragma unroll
   for (int q = 0; q < S::STORES; ++q) {
     if constexpr (S::GATEUP)
-      __builtin_amdgcn_raw_buffer_store_b64(uint2_t{0u, 0u}, rs, 0u, 0, 0);
+      pipe_st64(uint2_t{0u, 0u}, rs, 0u);
     else
-      __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{0.f, 0.f, 0.f, 0.f}, rs, 0u, 0, 0);
+      pipe_st128(f32x4_t{0.f, 0.f, 0.f, 0.f}, rs, 0u);
   }
 }
 
@@ -894,15 +915,22 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
 
   f32x16_t acc[NMAT][TM][TN];
   bf16x8_t fa[2][TM], fb[2][NMAT][TN];
-  auto read_stage = [&](int slot) __attribute__((always_inline)) {
+  // A tile of at most BM/2 rows (an expert's last m-tile, often) runs as a
+  // half-height tile: group g takes rows [g BM/4, (g+1) BM/4), each wave
+  // its first TM/2 row blocks, so both groups' compute phases halve instead
+  // of one group's going idle.  Its stage loads, waits and stores are those
+  // of a full tile; every output sums its products in the same order.
+  auto read_stage = [&](int slot, auto half_c) __attribute__((always_inline)) {
+    constexpr bool HALF = decltype(half_c)::value;
+    constexpr int TMH = HALF ? TM / 2 : TM, WMH = HALF ? WM / 2 : WM;
     const uint16_t* As = smem + slot * STAGE;
     const uint16_t* Bs = As + BM * KB;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int chunk = s * 2 + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + (lane & 31);
+      for (int i = 0; i < TMH; ++i) {
+        const int r = wm * WMH + i * 32 + (lane & 31);
         fa[s][i] = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + pl_swz<KB>(r, chunk) * 8]);
       }
 #pragma unroll
@@ -914,7 +942,8 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
         }
     }
   };
-  auto compute = [&]() __attribute__((always_inline)) {
+  auto compute = [&](auto half_c) __attribute__((always_inline)) {
+    constexpr int TMH = decltype(half_c)::value ? TM / 2 : TM;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -922,7 +951,7 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
+          for (int i = 0; i < TMH; ++i)
             acc[m][i][j] =
                 pipe_mfma<S>(fb[s][m][j], fa[s][i], acc[m][i][j]);
   };
@@ -953,15 +982,16 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
   // VM_STAGE + STORES newer operations in flight" (the A row loads of the
   // next tile, issued after the stores, only make that stricter); from step
   // AHEAD-1 on, the stage waited for is younger than the stores.
-  auto step = [&](const PipeTile<S>& src, int k0, auto relaxed_c) __attribute__((always_inline)) {
-    read_stage(slot);
+  auto step = [&](const PipeTile<S>& src, int k0, auto relaxed_c, auto half_c)
+                  __attribute__((always_inline)) {
+    read_stage(slot, half_c);
     pipe_issue<S>(src, smem, slot_issue, k0);
     if constexpr (decltype(relaxed_c)::value)
       PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE + S::STORES);
     else
       PL_WAIT_VM_LDS((AHEAD - 1) * VM_STAGE);
     pp_barrier();
-    compute();
+    compute(half_c);
     pp_barrier();
     slot = slot + 1 == STAGES ? 0 : slot + 1;
     slot_issue = slot_issue + 1 == STAGES ? 0 : slot_issue + 1;
@@ -978,17 +1008,23 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
     // tile's first stages again, into slots nothing reads any more.
     if (more) locate_begin(t_next, nxt);
     pipe_zero<S>(acc);
+    auto run = [&](auto half_c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < AHEAD - 1; ++kt) step(cur, (kt + AHEAD) * KB, T1{});
-    step(cur, (2 * AHEAD - 1) * KB, T0{});
-    if (more)
-      locate_end(t_next, nxt);
-    else
-      nxt = cur;
-    for (int kt = AHEAD; kt < nk - AHEAD; ++kt) step(cur, (kt + AHEAD) * KB, T0{});
+      for (int kt = 0; kt < AHEAD - 1; ++kt) step(cur, (kt + AHEAD) * KB, T1{}, half_c);
+      step(cur, (2 * AHEAD - 1) * KB, T0{}, half_c);
+      if (more)
+        locate_end(t_next, nxt);
+      else
+        nxt = cur;
+      for (int kt = AHEAD; kt < nk - AHEAD; ++kt) step(cur, (kt + AHEAD) * KB, T0{}, half_c);
 #pragma unroll 1
-    for (int q = 0; q < AHEAD; ++q) step(nxt, q * KB, T0{});
-    pipe_store<S>(t < R.tiles0 ? p0 : p1, cur, acc, limit, wm, wn);
+      for (int q = 0; q < AHEAD; ++q) step(nxt, q * KB, T0{}, half_c);
+      pipe_store<S, decltype(half_c)::value>(t < R.tiles0 ? p0 : p1, cur, acc, limit, wm, wn);
+    };
+    if (cur.row_end - cur.row0 <= BM / 2)
+      run(T1{});
+    else
+      run(T0{});
     if (!more) break;
     t = t_next;
     nk = stages_of(t);
