@@ -252,6 +252,29 @@ def test_permute_parity(tl, T, E, k, skew):
     ([2, 3, 4, 1] * 16, 512, 1408, 0.02),                # short groups (weight streaming tiles)
 ])
 def test_grouped_swiglu_gemm_parity(tl, counts, H, I, std):
+    check_grouped_gemm(tl, counts, H, I, std)
+
+
+@pytest.mark.parametrize("counts,H,I", [
+    # the 256-row ping-pong tile with every kind of last m-tile: exactly 128
+    # rows and 1 row (half-height), 129 and 256 rows (full), 384 = 256 + 128
+    # and 640 = 2 x 256 + 128 (full tiles, then a half-height one), an empty
+    # group; K = 512 / 384 (both >= 256), down N = 512 (two column tiles)
+    ([128, 129, 1, 384, 0, 640, 256, 513], 512, 384),
+    # K = 256 in down (the shortest the tile takes)
+    ([130, 100, 700], 288, 256),
+    # K = 256 in gate_up, and a ragged gate_up N (288: a last column tile
+    # with 32 of its 128 columns)
+    ([130, 100, 700], 256, 288),
+])
+def test_grouped_gemm_pingpong_tiles(tl, counts, H, I, monkeypatch):
+    """The ping-pong tile forced on groups whose last m-tiles are full or
+    half-height (at most 128 rows), against the same forward-error bounds."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT", "pingpong")
+    check_grouped_gemm(tl, counts, H, I, 0.05)
+
+
+def check_grouped_gemm(tl, counts, H, I, std):
     torch, moe = tl
     gh.note(f"grouped gemm counts={counts[:8]} H={H} I={I}")
     rng = np.random.default_rng(sum(counts) + H + I)
