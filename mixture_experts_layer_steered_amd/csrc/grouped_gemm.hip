@@ -975,13 +975,13 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
   // One step: read stage kt's fragments, issue this wave's loads of the
   // stage AHEAD ahead into the slot read in the step before (from tile src
   // at K offset k0), wait for its loads of stage kt+1, barrier, MFMAs,
-  // barrier.  The waits of the first AHEAD-1 steps of
-  // a tile (RELAXED) let the previous epilogue's S::STORES stores stay in
-  // flight: they were issued after stages 0..AHEAD-1 of this tile and
-  // before stage AHEAD, so "stage kt+1 landed" is "at most (AHEAD-1)
-  // VM_STAGE + STORES newer operations in flight" (the A row loads of the
-  // next tile, issued after the stores, only make that stricter); from step
-  // AHEAD-1 on, the stage waited for is younger than the stores.
+  // barrier.  The waits of the first AHEAD-1 steps of a tile (RELAXED) let
+  // the previous epilogue's S::STORES stores stay in flight: they were
+  // issued after stages 0..AHEAD-1 of this tile and before stage AHEAD, so
+  // "stage kt+1 landed" is "at most (AHEAD-1) VM_STAGE + STORES newer
+  // operations in flight" (the A row loads of the next tile, issued after
+  // the stores, only make that stricter); from step AHEAD-1 on, the stage
+  // waited for is younger than the stores.
   auto step = [&](const PipeTile<S>& src, int k0, auto relaxed_c, auto half_c)
                   __attribute__((always_inline)) {
     read_stage(slot, half_c);
