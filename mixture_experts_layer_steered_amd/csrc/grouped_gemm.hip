@@ -816,8 +816,12 @@ __device__ __forceinline__ int pipe_mtiles(const GemmProblem& P) {
 
 // Persistent: one workgroup per CU.  The real tile count is read on the
 // device (m-tile prefix x n-tiles, routed and shared problems back to back)
-// and split into 8 equal contiguous ranges, one per XCD (workgroup b runs on
-// XCD b % 8); the XCD's workgroups stride its range.
+// and split into 8 contiguous ranges of equal cost, one per XCD (workgroup b
+// runs on XCD b % 8); the XCD's workgroups stride its range.  A tile costs
+// its K stages: the two problems' K differ where the shared expert's width
+// differs from the routed experts' (the down projection of ScMoE: 64 stages
+// against 32), and equal tile counts would give the XCD that holds the
+// shared tiles most of the work.
 struct PipeRange {
   int mt0, mt1, tiles0, t_first, t_end, stride;
 };
@@ -829,11 +833,17 @@ __device__ __forceinline__ PipeRange pipe_range(const GemmProblem& p0, const Gem
   R.mt1 = has_p1 ? pipe_mtiles<BM>(p1) : 0;
   R.tiles0 = R.mt0 * p0.ntiles;
   const int total = R.tiles0 + R.mt1 * p1.ntiles;
+  const int64_t k0 = p0.K, k1 = has_p1 ? p1.K : p0.K;  // cost per tile (K in any unit)
+  const int64_t c0 = (int64_t)R.tiles0 * k0;
+  const int64_t ctot = c0 + (int64_t)(total - R.tiles0) * k1;
+  auto first_tile_from = [&](int64_t c) {  // first tile starting at cost >= c
+    return c <= c0 ? (int)((c + k0 - 1) / k0) : R.tiles0 + (int)((c - c0 + k1 - 1) / k1);
+  };
   const int nwg = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, lid = b >> 3;
   R.stride = (nwg - xcd + 7) >> 3;
-  R.t_first = (int)((int64_t)total * xcd / 8) + lid;
-  R.t_end = (int)((int64_t)total * (xcd + 1) / 8);
+  R.t_first = first_tile_from(ctot * xcd / 8) + lid;
+  R.t_end = first_tile_from(ctot * (xcd + 1) / 8);
   return R;
 }
 
