@@ -814,16 +814,19 @@ __device__ __forceinline__ int pipe_mtiles(const GemmProblem& P) {
   return P.group_offsets ? P.mtile_start[P.G] : (int)((P.M + BM - 1) / BM);
 }
 
-// Persistent: one workgroup per CU.  The real tile count is read on the
-// device (m-tile prefix x n-tiles, routed and shared problems back to back)
-// and split into 8 contiguous ranges of equal cost, one per XCD (workgroup b
-// runs on XCD b % 8); the XCD's workgroups stride its range.  A tile costs
-// its K stages: the two problems' K differ where the shared expert's width
-// differs from the routed experts' (the down projection of ScMoE: 64 stages
-// against 32), and equal tile counts would give the XCD that holds the
-// shared tiles most of the work.
+// Persistent: one workgroup per CU.  The real tile counts are read on the
+// device (m-tile prefix x n-tiles; routed problem, then shared problem) and
+// each problem is split into 8 equal contiguous ranges, one per XCD
+// (workgroup b runs on XCD b % 8): an XCD takes its share of the routed
+// tiles, then its share of the shared expert's.  Its workgroups stride that
+// sequence (virtual index v, tile(v) the real tile).  Splitting the
+// concatenated tile list instead gave one XCD all of the shared expert's
+// tiles, which differ in cost (ScMoE: twice the K in down, no partly filled
+// m-tiles), and that XCD ended last by up to half the launch.
 struct PipeRange {
   int mt0, mt1, tiles0, t_first, t_end, stride;
+  int base0, n0, base1;  // this XCD's first routed tile and count, first shared tile
+  __device__ __forceinline__ int tile(int v) const { return v < n0 ? base0 + v : base1 + (v - n0); }
 };
 template <int BM>
 __device__ __forceinline__ PipeRange pipe_range(const GemmProblem& p0, const GemmProblem& p1,
@@ -832,18 +835,16 @@ __device__ __forceinline__ PipeRange pipe_range(const GemmProblem& p0, const Gem
   R.mt0 = pipe_mtiles<BM>(p0);
   R.mt1 = has_p1 ? pipe_mtiles<BM>(p1) : 0;
   R.tiles0 = R.mt0 * p0.ntiles;
-  const int total = R.tiles0 + R.mt1 * p1.ntiles;
-  const int64_t k0 = p0.K, k1 = has_p1 ? p1.K : p0.K;  // cost per tile (K in any unit)
-  const int64_t c0 = (int64_t)R.tiles0 * k0;
-  const int64_t ctot = c0 + (int64_t)(total - R.tiles0) * k1;
-  auto first_tile_from = [&](int64_t c) {  // first tile starting at cost >= c
-    return c <= c0 ? (int)((c + k0 - 1) / k0) : R.tiles0 + (int)((c - c0 + k1 - 1) / k1);
-  };
+  const int tiles1 = R.mt1 * p1.ntiles;
   const int nwg = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, lid = b >> 3;
   R.stride = (nwg - xcd + 7) >> 3;
-  R.t_first = first_tile_from(ctot * xcd / 8) + lid;
-  R.t_end = first_tile_from(ctot * (xcd + 1) / 8);
+  R.base0 = (int)((int64_t)R.tiles0 * xcd / 8);
+  R.n0 = (int)((int64_t)R.tiles0 * (xcd + 1) / 8) - R.base0;
+  R.base1 = R.tiles0 + (int)((int64_t)tiles1 * xcd / 8);
+  const int n1 = R.tiles0 + (int)((int64_t)tiles1 * (xcd + 1) / 8) - R.base1;
+  R.t_first = lid;
+  R.t_end = R.n0 + n1;
   return R;
 }
 
@@ -853,7 +854,8 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pipe_kernel(GemmProblem
                                                                      float limit) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
   const PipeRange R = pipe_range<S::BM>(p0, p1, has_p1);
-  for (int t = R.t_first; t < R.t_end; t += R.stride) {
+  for (int v = R.t_first; v < R.t_end; v += R.stride) {
+    const int t = R.tile(v);
     if (t < R.tiles0)
       pipe_tile<S, STAGES>(p0, R.mt0, t, limit, smem_dyn);
     else
@@ -894,8 +896,9 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
   extern __shared__ __attribute__((aligned(16))) uint16_t smem_dyn[];
   uint16_t* smem = smem_dyn;
   const PipeRange R = pipe_range<BM>(p0, p1, has_p1);
-  int t = R.t_first;
-  if (t >= R.t_end) return;  // no tile for this workgroup (uniform)
+  int v = R.t_first;  // position in this XCD's tile sequence
+  if (v >= R.t_end) return;  // no tile for this workgroup (uniform)
+  int t = R.tile(v);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1009,8 +1012,8 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
   using T0 = std::integral_constant<bool, false>;
   using T1 = std::integral_constant<bool, true>;
   for (;;) {
-    const int t_next = t + R.stride;
-    const bool more = t_next < R.t_end;
+    const bool more = v + R.stride < R.t_end;
+    const int t_next = more ? R.tile(v + R.stride) : t;
     // the next tile's A rows load while this tile's first AHEAD steps run
     // (their stages are this tile's: nk >= 2 AHEAD); the offsets are formed
     // after step AHEAD-1, whose wait has seen the rows land.  The last AHEAD
@@ -1036,6 +1039,7 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_kernel(GemmProblem p
     else
       run(T0{});
     if (!more) break;
+    v += R.stride;
     t = t_next;
     nk = stages_of(t);
     cur = nxt;
@@ -1247,8 +1251,9 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   float2_t* table = reinterpret_cast<float2_t*>(smem + L::T_OFF);
   GemmProblem unused = p0;
   const PipeRange R = pipe_range<S::BM>(p0, unused, 0);
-  int t = R.t_first;
-  if (t >= R.t_end) return;  // no tile for this workgroup (uniform)
+  int v = R.t_first;  // position in this XCD's tile sequence
+  if (v >= R.t_end) return;  // no tile for this workgroup (uniform)
+  int t = R.tile(v);
 
   const int lane = threadIdx.x & 63;
   // the wave index and group in scalar registers: barriers are only ever
@@ -1401,8 +1406,8 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   using T1 = std::integral_constant<bool, true>;
   static_assert(AHEAD == L::G_STAGES, "the first AHEAD steps issue code group 1 only");
   for (;;) {
-    const int t_next = t + R.stride;
-    const bool more = t_next < R.t_end;
+    const bool more = v + R.stride < R.t_end;
+    const int t_next = more ? R.tile(v + R.stride) : t;
     // as in the bf16 tile: the next tile's A rows load during the first
     // AHEAD steps (whose stages are all this tile's: nk >= 2 AHEAD), and
     // the last AHEAD steps issue the next tile's first code group and A
@@ -1422,6 +1427,7 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
     for (int q = 0; q < AHEAD; ++q) step(nk - AHEAD + q, nxt, 0, q * KB, T0{});
     pipe_store<S>(p0, cur.t, acc, limit, wm, wn);
     if (!more) break;
+    v += R.stride;
     t = t_next;
     cur = nxt;
   }
