@@ -1220,8 +1220,9 @@ constexpr uint32_t W4_SEL0 = 0x04000C0Cu, W4_SEL1 = 0x04010C0Cu, W4_SEL2 = 0x040
 
 // MFMAs LO .. HI-1 of a stage, numbered in the order (substep, matrix,
 // column block, row block): the two substeps' products into one accumulator
-// are eight apart.
-template <class S, int LO, int HI>
+// are eight apart.  HALF: only those of the first TM/2 row blocks (a
+// half-height tile).
+template <class S, int LO, int HI, bool HALF = false>
 __device__ __forceinline__ void pp_mfma_range(f32x16_t (&acc)[S::NMAT][S::TM][S::TN],
                                               const bf16x8_t (&fa)[2][S::TM],
                                               const bf16x8_t (&fb)[2][S::NMAT][S::TN]) {
@@ -1234,7 +1235,8 @@ __device__ __forceinline__ void pp_mfma_range(f32x16_t (&acc)[S::NMAT][S::TM][S:
 #pragma unroll
         for (int i = 0; i < S::TM; ++i) {
           const int n = ((s * S::NMAT + m) * S::TN + j) * S::TM + i;
-          if (n >= LO && n < HI) acc[m][i][j] = pipe_mfma<S>(fb[s][m][j], fa[s][i], acc[m][i][j]);
+          if (n >= LO && n < HI && (!HALF || i < S::TM / 2))
+            acc[m][i][j] = pipe_mfma<S>(fb[s][m][j], fa[s][i], acc[m][i][j]);
         }
 }
 
@@ -1283,15 +1285,20 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
 
   f32x16_t acc[NMAT][TM][TN];
   bf16x8_t fa[2][TM], fb[2][NMAT][TN];
-  auto read_stage = [&](int slot, int rslot) __attribute__((always_inline)) {
+  // HALF: a gate_up tile of at most BM/2 rows, run half-height as in the
+  // bf16 tile (row half wm takes rows [wm BM/4, (wm+1) BM/4), its first
+  // TM/2 row blocks); the dequantisation is a full tile's
+  auto read_stage = [&](int slot, int rslot, auto half_c) __attribute__((always_inline)) {
+    constexpr bool HALF = decltype(half_c)::value;
+    constexpr int TMH = HALF ? TM / 2 : TM, WMH = HALF ? WM / 2 : WM;
     const uint16_t* As = reinterpret_cast<const uint16_t*>(smem + slot * L::A_BYTES);
     const uint16_t* Bs = ring + rslot * (L::RING / 2);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int chunk = s * 2 + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + (lane & 31);
+      for (int i = 0; i < TMH; ++i) {
+        const int r = wm * WMH + i * 32 + (lane & 31);
         fa[s][i] = *reinterpret_cast<const bf16x8_t*>(&As[r * KB + pl_swz<KB>(r, chunk) * 8]);
       }
 #pragma unroll
@@ -1311,7 +1318,8 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   // time, five VALU instructions; a ring write after each eight columns).
   // An MFMA holds the matrix pipe for 32 cycles, longer than a piece takes to
   // issue.
-  auto dequant = [&](int ss, int rslot, bool mfma) __attribute__((always_inline)) {
+  auto dequant = [&](int ss, int rslot, bool mfma, auto half_c) __attribute__((always_inline)) {
+    constexpr bool HALF = decltype(half_c)::value;
     static_assert(2 * NMAT * TM * TN == 16, "16 MFMAs per stage");
     const uint8_t* cs = smem + L::C_OFF + ((ss >> 2) & 1) * L::C_SLOT;
     const uint2_t cw = *reinterpret_cast<const uint2_t*>(
@@ -1321,7 +1329,7 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
 #define PPW4_MFMA(lo, hi)                          \
     if (mfma) {                                    \
       __builtin_amdgcn_sched_barrier(0);           \
-      pp_mfma_range<S, lo, hi>(acc, fa, fb);       \
+      pp_mfma_range<S, lo, hi, HALF>(acc, fa, fb); \
       __builtin_amdgcn_sched_barrier(0);           \
     }
     PPW4_MFMA(0, 2)
@@ -1370,7 +1378,7 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   for (int s0 = 0; s0 < AHEAD; ++s0) pp_w4_issue_a<S>(cur, smem, s0, s0 * KB, wave);
   PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM);
   pp_barrier();  // code group 0, A stage 0 and the table everywhere
-  dequant(0, 0, false);
+  dequant(0, 0, false, std::false_type{});
   PL_WAIT_LDS();
   pp_barrier();  // stage 0's weights in ring slot 0
   if (group) pp_barrier();
@@ -1385,10 +1393,10 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
   // (RELAXED) also let the previous epilogue's S::STORES stores stay in
   // flight (issued after this tile's A stages 0..AHEAD-1 and code group 0,
   // before its code group 1 and A stage AHEAD).
-  auto step = [&](int kt, const PpW4Tile<S>& src, int cg, int k0, auto relaxed_c)
+  auto step = [&](int kt, const PpW4Tile<S>& src, int cg, int k0, auto relaxed_c, auto half_c)
                   __attribute__((always_inline)) {
     constexpr int EXTRA = decltype(relaxed_c)::value ? S::STORES : 0;
-    read_stage(ss % STAGES, ss & 1);
+    read_stage(ss % STAGES, ss & 1, half_c);
     if ((kt & 3) == 0)
       pp_w4_issue_c<S>(src, smem, (ss / L::G_STAGES + 1) & 1, cg, wave, wr_total);
     pp_w4_issue_a<S>(src, smem, (ss + AHEAD) % STAGES, k0, wave);
@@ -1397,7 +1405,7 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
     else
       PL_WAIT_VM_LDS((AHEAD - 1) * L::A_VM + L::C_VM + EXTRA);
     pp_barrier();
-    dequant(ss + 1, (ss + 1) & 1, true);  // the next stage of the stream, beside this one's MFMAs
+    dequant(ss + 1, (ss + 1) & 1, true, half_c);  // the next stage, beside this one's MFMAs
     PL_WAIT_LDS();
     pp_barrier();
     ++ss;
@@ -1414,18 +1422,25 @@ __global__ __launch_bounds__(S::NW * 64, 1) void grouped_pp_w4_kernel(GemmProble
     // stages (past the last tile, this tile's again, into free slots)
     if (more) pp_w4_locate_begin<S>(p0, R.mt0, t_next, wave, nxt);
     pipe_zero<S>(acc);
+    auto run = [&](auto h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < AHEAD - 1; ++kt) step(kt, cur, 1, (kt + AHEAD) * KB, T1{});
-    step(AHEAD - 1, cur, 1, (2 * AHEAD - 1) * KB, T0{});
-    if (more)
-      pipe_locate_end<S>(p0.K, nxt.t);
-    else
-      nxt = cur;
-    for (int kt = AHEAD; kt < nk - AHEAD; ++kt)
-      step(kt, cur, kt / L::G_STAGES + 1, (kt + AHEAD) * KB, T0{});
+      for (int kt = 0; kt < AHEAD - 1; ++kt) step(kt, cur, 1, (kt + AHEAD) * KB, T1{}, h);
+      step(AHEAD - 1, cur, 1, (2 * AHEAD - 1) * KB, T0{}, h);
+      if (more)
+        pipe_locate_end<S>(p0.K, nxt.t);
+      else
+        nxt = cur;
+      for (int kt = AHEAD; kt < nk - AHEAD; ++kt)
+        step(kt, cur, kt / L::G_STAGES + 1, (kt + AHEAD) * KB, T0{}, h);
 #pragma unroll 1
-    for (int q = 0; q < AHEAD; ++q) step(nk - AHEAD + q, nxt, 0, q * KB, T0{});
-    pipe_store<S>(p0, cur.t, acc, limit, wm, wn);
+      for (int q = 0; q < AHEAD; ++q) step(nk - AHEAD + q, nxt, 0, q * KB, T0{}, h);
+      pipe_store<S, decltype(h)::value>(p0, cur.t, acc, limit, wm, wn);
+    };
+    // (down keeps full tiles: the half-height copy of its steps spills)
+    if (S::GATEUP && cur.t.row_end - cur.t.row0 <= S::BM / 2)
+      run(std::integral_constant<bool, S::GATEUP>{});
+    else
+      run(T0{});
     if (!more) break;
     v += R.stride;
     t = t_next;

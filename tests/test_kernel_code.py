@@ -44,11 +44,11 @@ def kernel_body(asm, pattern):
 
 # (kernel: gate_up Lb1E or down Lb0E, STORES, epilogue copies).  bf16
 # ping-pong: full tile, half-height tile, and the stand-in before the first
-# tile; W4A16 ping-pong: full tile and the stand-in
+# tile; W4A16 ping-pong: the same in gate_up, no half-height tile in down
 CASES = [
     (r"17grouped_pp_kernel.*Lb1E", 16, 3),
     (r"17grouped_pp_kernel.*Lb0E", 32, 3),
-    (r"20grouped_pp_w4_kernel.*Lb1E", 16, 2),
+    (r"20grouped_pp_w4_kernel.*Lb1E", 16, 3),
     (r"20grouped_pp_w4_kernel.*Lb0E", 32, 2),
 ]
 
