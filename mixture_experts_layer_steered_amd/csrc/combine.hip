@@ -186,20 +186,26 @@ __global__ __launch_bounds__(RN_THREADS) void rmsnorm_bf16_kernel(
   const double sum = block_sum_f64<RN_THREADS>(ss, red);
   const double r = 1.0 / sqrt(sum / (double)H + (double)eps);
   uint4* o8 = reinterpret_cast<uint4*>(out + t * H);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
 #pragma unroll
   for (int i = 0; i < RN_MAXV; ++i) {
     const int c = threadIdx.x + i * RN_THREADS;
     if (c < H8) {
       const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      float g[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+      if (gamma) {  // the row's 8 gains in two 16-byte loads
+        const float4 g0 = g4[2 * c], g1 = g4[2 * c + 1];
+        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      }
       uint32_t o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = c * 8 + 2 * q;
         double a = (double)bf16_bits_to_f32(u[q] & 0xffffu) * r;
         double b = (double)bf16_bits_to_f32(u[q] >> 16) * r;
         if (gamma) {
-          a *= (double)gamma[col];
-          b *= (double)gamma[col + 1];
+          a *= (double)g[2 * q];
+          b *= (double)g[2 * q + 1];
         }
         o[q] = f32_to_bf16_bits((float)a) | (f32_to_bf16_bits((float)b) << 16);
       }
