@@ -48,6 +48,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -232,9 +233,26 @@ def calibrate_copy(nbytes: int, reps: int) -> None:
                       "reps": reps}))
 
 
+# where the grouped GEMM kernels carry their gate_up flag: the third argument
+# of the pipelined tiles' shape, the last of the LDS-staged tiles', the first
+# of the weight-streaming tiles'
+_GATEUP_FLAG = (re.compile(r"PipeShape<\d+, \d+, (true|false)"),
+                re.compile(r"grouped_gemm_kernel<(?:\d+, ){4}(true|false)"),
+                re.compile(r"grouped_\w+_kernel<(true|false)"))
+
+
+def _grouped_kind(name: str) -> str | None:
+    if "grouped_" not in name:
+        return None
+    for rx in _GATEUP_FLAG:
+        m = rx.search(name)
+        if m:
+            return "gate_up" if m.group(1) == "true" else "down"
+    return None
+
+
 def _is_gate_up(name: str) -> bool:
-    # grouped GEMM kernels carry the gate_up flag as a `true` template argument
-    return "grouped_" in name and ("<true" in name or ", true" in name)
+    return _grouped_kind(name) == "gate_up"
 
 
 def _counter_means(csv_path: str, counter: str, select, full_grid: bool = False
@@ -289,12 +307,6 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: 
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
-
-
-def _grouped_kind(name: str) -> str | None:
-    if "grouped_" not in name:
-        return None
-    return "gate_up" if ("<true" in name or ", true" in name) else "down"
 
 
 def write_mfma(workload: str, csv_path: str, command: str) -> None:
@@ -434,6 +446,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle time to spend on the baseline sample (at least)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row-major-experts", action="store_true",
+                    help="do not give the layer the tile-blocked copies of the bf16 experts")
     ap.add_argument("--event-every", type=int, default=8,
                     help="time the dominant launch with events on every N-th timed step")
     ap.add_argument("--no-probe-peaks", action="store_true",
@@ -512,6 +526,25 @@ def main() -> int:
                ws_down=dev_bf16(inp["ws_down"]) if Is else None,
                gamma_pre=dev_f32(inp["gamma_pre"]) if wl.scmoe else None,
                gamma_post=dev_f32(inp["gamma_post"]) if wl.scmoe else None)
+    # bf16 experts: their tile-blocked copies are written once here, before
+    # any timing, as a weight-loading step (moe_pack_experts); the 256-row
+    # tiles read them, the other tiles the row-major weights
+    layout = "row_major"
+    if not wl.w4 and not args.row_major_experts and H % 32 == 0 and I % 32 == 0 and Is % 32 == 0:
+        gu_n, dn_n = moe.moe_packed_experts_size(params)
+        dev["w_gate_up_packed"] = torch.empty(gu_n, dtype=torch.int16, device="cuda")
+        dev["w_down_packed"] = torch.empty(dn_n, dtype=torch.int16, device="cuda")
+        moe.moe_pack_experts(params, dev["w_gate_up"], dev["w_down"], dev["w_gate_up_packed"],
+                             dev["w_down_packed"])
+        if Is:
+            ps = moe.make_params(T, H, 1, 1, Is, 0, wl.rsf, wl.limit, False, wl.eps)
+            sgu_n, sdn_n = moe.moe_packed_experts_size(ps)
+            dev["ws_gate_up_packed"] = torch.empty(sgu_n, dtype=torch.int16, device="cuda")
+            dev["ws_down_packed"] = torch.empty(sdn_n, dtype=torch.int16, device="cuda")
+            moe.moe_pack_experts(ps, dev["ws_gate_up"], dev["ws_down"],
+                                 dev["ws_gate_up_packed"], dev["ws_down_packed"])
+        torch.cuda.synchronize()
+        layout = "row_major+tile_blocked"
     weights = moe.make_weights(**dev, **w4)
     ws = torch.empty(moe.moe_workspace_size(params), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
@@ -631,7 +664,8 @@ def main() -> int:
         "config": {"workload": wl.label(), "T": T, "H": H, "E": E, "k": k, "I": I, "I_shared": Is,
                    "routed_scaling_factor": wl.rsf, "swiglu_limit": wl.limit,
                    "scmoe": wl.scmoe, "seed": 0, "parallelism": "ep1_tp1",
-                   "finish": "residual_add" if args.finish else None},
+                   "finish": "residual_add" if args.finish else None,
+                   "expert_layout": layout},
         "roofline": roofline, "cpu_baseline": cpu, "layer": layer, "measured_peaks": peaks,
     }
     print(json.dumps(line), flush=True)

@@ -150,6 +150,19 @@ typedef struct moe_weights {
   const uint8_t* w_down_scale;      /* [E, I/128, H] E4M3                         */
   const float* w_gate_up_tscale;    /* [E] fp32 tensor scales; NULL = ones        */
   const float* w_down_tscale;       /* [E] fp32 tensor scales; NULL = ones        */
+  /* Optional tile-blocked copies of the bf16 experts, written once by
+   * moe_pack_experts (NULL = not given; not with W4A16): the routed pair
+   * both or neither, and with them the shared expert's pair when
+   * I_shared > 0 (moe_pack_experts with E = 1 and I = I_shared).
+   * Prefill-sized batches (the 256-row tiles) then read each 32-column K
+   * stage of a 256-row weight tile as one contiguous 16 KB block instead of
+   * 256 pieces of 64 bytes, half as many requests to the caches; the
+   * results are the same bits.  The row-major weights stay required (the
+   * other batch sizes read them). */
+  const moe_bf16* w_gate_up_packed;
+  const moe_bf16* w_down_packed;
+  const moe_bf16* ws_gate_up_packed;
+  const moe_bf16* ws_down_packed;
 } moe_weights;
 
 /* Finish of the layer, fused into its combine (moe_forward_finish,
@@ -406,6 +419,31 @@ moe_status moe_router_backward(const moe_params* p, const float* grad_logits,
 moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float* tscale,
                              int32_t n_groups, int64_t rows, int32_t K, moe_bf16* out,
                              hipStream_t stream);
+
+/* Tile-blocked copies of bf16 routed experts for moe_weights' *_packed
+ * fields: a one-time preparation of the weights, like loading them, not a
+ * step of the layer (the layout is this library's: the loads of its
+ * 256-row tiles, not a format of the pages).
+ * gate_up_packed: for expert e, column tile b (output columns [128 b,
+ *   128 b + 128), b < ceil(I/128)) and K stage s (columns [32 s, 32 s + 32)
+ *   of H, s < H/32), one block of 256 rows x 32 values, each row's 32
+ *   values contiguous: rows 0..127 the gate rows 128 b + r of w_gate_up[e],
+ *   rows 128..255 the up rows I + 128 b + r; rows past I are zeros.  Blocks
+ *   in the order (e, b, s).
+ * down_packed: for expert e, row tile b (rows [256 b, 256 b + 256) of
+ *   w_down[e], b < ceil(H/256)) and K stage s (s < I/32), the 256 x 32
+ *   block of those rows; rows past H are zeros.  Blocks in the order
+ *   (e, b, s).
+ * moe_packed_experts_size gives the element counts (E * ceil(I/128) * 256
+ * * H and E * ceil(H/256) * 256 * I bf16).  The shared expert's copies are
+ * the same with E = 1 and I = I_shared (ws_gate_up, ws_down as w_gate_up,
+ * w_down).  H and I must be multiples of 32 (else MOE_ERR_UNSUPPORTED);
+ * pointers device, 16-byte aligned; the outputs must not overlap the
+ * inputs.  Asynchronous on stream. */
+moe_status moe_packed_experts_size(const moe_params* p, int64_t* gate_up_elems,
+                                   int64_t* down_elems);
+moe_status moe_pack_experts(const moe_params* p, const moe_bf16* w_gate_up, const moe_bf16* w_down,
+                            moe_bf16* gate_up_packed, moe_bf16* down_packed, hipStream_t stream);
 
 /* Diagnostics, not on the layer's path: what the current device delivers,
  * for reporting the layer's rates against measured peaks beside the

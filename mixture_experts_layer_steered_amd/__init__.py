@@ -56,7 +56,8 @@ class moe_weights(Structure):
     _fields_ = [(n, c_void_p) for n in (
         "w_router", "corr_bias", "w_gate_up", "w_down", "ws_gate_up", "ws_down",
         "gamma_pre", "gamma_post", "w_gate_up_q", "w_gate_up_scale", "w_down_q",
-        "w_down_scale", "w_gate_up_tscale", "w_down_tscale")]
+        "w_down_scale", "w_gate_up_tscale", "w_down_tscale", "w_gate_up_packed",
+        "w_down_packed", "ws_gate_up_packed", "ws_down_packed")]
 
 
 class moe_finish(Structure):
@@ -109,6 +110,8 @@ def _load() -> ctypes.CDLL:
                                      c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_w4_dequantize": (st, [c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32,
                                    c_void_p, c_void_p]),
+        "moe_packed_experts_size": (st, [P, POINTER(c_int64), POINTER(c_int64)]),
+        "moe_pack_experts": (st, [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "moe_probe_mfma_bf16": (st, [c_int32, c_int32, c_void_p, POINTER(c_double),
                                      c_void_p]),
         "moe_probe_hbm_read": (st, [c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
@@ -137,7 +140,7 @@ EXPORTED = ("moe_workspace_size", "moe_router_topk", "moe_permute",
             "moe_grouped_gemm_workspace_size", "moe_grouped_swiglu_gemm", "moe_combine",
             "moe_combine_finish", "moe_forward", "moe_forward_finish", "moe_forward_noalloc",
             "moe_router_backward_workspace_size", "moe_router_backward", "moe_w4_dequantize",
-            "moe_probe_mfma_bf16", "moe_probe_hbm_read", "moe_status_string", "moe_last_error")
+            "moe_packed_experts_size", "moe_pack_experts", "moe_probe_mfma_bf16", "moe_probe_hbm_read", "moe_status_string", "moe_last_error")
 
 
 def _status_name(s: int) -> str:
@@ -236,14 +239,16 @@ def moe_combine_finish(params, y_perm, topk_w, inv_pos, y_shared, gamma_post, fi
 def make_weights(w_router, corr_bias, w_gate_up, w_down, ws_gate_up=None, ws_down=None,
                  gamma_pre=None, gamma_post=None, w_gate_up_q=None, w_gate_up_scale=None,
                  w_down_q=None, w_down_scale=None, w_gate_up_tscale=None,
-                 w_down_tscale=None) -> moe_weights:
+                 w_down_tscale=None, w_gate_up_packed=None, w_down_packed=None,
+                 ws_gate_up_packed=None, ws_down_packed=None) -> moe_weights:
     """Weights of one layer; the W4A16 arrays (*_q codes, *_scale E4M3
     bytes, *_tscale fp32 tensor scales) replace w_gate_up / w_down when
-    given."""
+    given; *_packed are the tile-blocked copies of moe_pack_experts."""
     return moe_weights(*[_ptr(t) for t in (w_router, corr_bias, w_gate_up, w_down, ws_gate_up,
                                            ws_down, gamma_pre, gamma_post, w_gate_up_q,
                                            w_gate_up_scale, w_down_q, w_down_scale,
-                                           w_gate_up_tscale, w_down_tscale)])
+                                           w_gate_up_tscale, w_down_tscale, w_gate_up_packed,
+                                           w_down_packed, ws_gate_up_packed, ws_down_packed)])
 
 
 def make_probes(topk_ids=None, topk_w=None, expert_offsets=None, sorted_token=None,
@@ -288,6 +293,21 @@ def moe_w4_dequantize(q, scale, out, n_groups, rows, K, stream=None, tscale=None
     K] in `out`."""
     _check(lib().moe_w4_dequantize(_ptr(q), _ptr(scale), _ptr(tscale), int(n_groups), int(rows),
                                    int(K), _ptr(out), _stream(stream)))
+
+
+def moe_packed_experts_size(params: moe_params):
+    """(gate_up, down) element counts of the tile-blocked expert copies."""
+    gu, dn = c_int64(0), c_int64(0)
+    _check(lib().moe_packed_experts_size(ctypes.byref(params), ctypes.byref(gu),
+                                         ctypes.byref(dn)))
+    return gu.value, dn.value
+
+
+def moe_pack_experts(params, w_gate_up, w_down, gate_up_packed, down_packed, stream=None):
+    """Write the tile-blocked copies of the bf16 routed experts (sizes from
+    moe_packed_experts_size) for moe_weights' *_packed fields."""
+    _check(lib().moe_pack_experts(ctypes.byref(params), _ptr(w_gate_up), _ptr(w_down),
+                                  _ptr(gate_up_packed), _ptr(down_packed), _stream(stream)))
 
 
 def moe_router_backward_workspace_size(params: moe_params) -> int:

@@ -286,6 +286,7 @@ GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int3
   P.K = K;
   P.ntiles = (N + bn - 1) / bn;
   P.max_mtiles = (int32_t)((M + bm - 1) / bm + (offsets ? G : 0));
+  P.packed = 0;
   return P;
 }
 
@@ -516,6 +517,20 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     REQUIRE_PTR(w->w_gate_up);
     REQUIRE_PTR(w->w_down);
   }
+  const bool packed = w->w_gate_up_packed != nullptr;
+  if ((w->w_down_packed != nullptr) != packed)
+    return fail(MOE_ERR_INVALID_ARG, "w_gate_up_packed and w_down_packed go together");
+  if (packed && w4) return fail(MOE_ERR_INVALID_ARG, "packed experts are bf16 (params.w4 = 0)");
+  if (packed && (p->H % 32 || p->I % 32 || p->I_shared % 32))
+    return fail(MOE_ERR_UNSUPPORTED, "packed experts need H, I and I_shared multiples of 32");
+  if (packed && p->I_shared > 0) {  // the 256-row tiles run both in one launch
+    REQUIRE_PTR(w->ws_gate_up_packed);
+    REQUIRE_PTR(w->ws_down_packed);
+  }
+  OPTIONAL_PTR(w->w_gate_up_packed);
+  OPTIONAL_PTR(w->w_down_packed);
+  OPTIONAL_PTR(w->ws_gate_up_packed);
+  OPTIONAL_PTR(w->ws_down_packed);
   if (p->I_shared > 0) {
     REQUIRE_PTR(w->ws_gate_up);
     REQUIRE_PTR(w->ws_down);
@@ -592,6 +607,25 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                                  p->I_shared, p->H, v, true);
   GemmProblem sdn = make_problem(L.hs, nullptr, nullptr, nullptr, w->ws_down, 0, L.ys, T, 1, p->H,
                                  p->I_shared, v, false);
+  // tile-blocked copies of the bf16 experts, for the 256-row tiles (their
+  // K stages then are contiguous 16 KB blocks, byte offsets within 4 GiB
+  // per expert); other tiles read the rows
+  if (packed && (v == GemmVariant::kPingPong || v == GemmVariant::kPipe256W8) &&
+      2 * pack_experts_elems(1, p->I, p->H, true) <= UINT32_MAX &&
+      2 * pack_experts_elems(1, p->H, p->I, false) <= UINT32_MAX &&
+      2 * pack_experts_elems(1, p->I_shared, p->H, true) <= UINT32_MAX &&
+      2 * pack_experts_elems(1, p->H, p->I_shared, false) <= UINT32_MAX) {
+    gu.W = w->w_gate_up_packed;
+    gu.w_stride = pack_experts_elems(1, p->I, p->H, true);
+    gu.packed = 1;
+    dn.W = w->w_down_packed;
+    dn.w_stride = pack_experts_elems(1, p->H, p->I, false);
+    dn.packed = 1;
+    sgu.W = w->ws_gate_up_packed;
+    sgu.packed = 1;
+    sdn.W = w->ws_down_packed;
+    sdn.packed = 1;
+  }
   if (p->scmoe) gu.A = L.xr;
   if (!tiles_fit(gu, shared ? &sgu : nullptr) || !tiles_fit(dn, shared ? &sdn : nullptr))
     return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");
@@ -810,6 +844,37 @@ moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float
   moe_status s;
   if ((s = device_status(launch_w4_dequant(q, scale, tscale, out, n_groups, rows, K, stream),
                          "dequantise")) != MOE_OK)
+    return s;
+  return ok();
+}
+
+moe_status moe_packed_experts_size(const moe_params* p, int64_t* gate_up_elems,
+                                   int64_t* down_elems) {
+  moe_status s = check_params(p);
+  if (s != MOE_OK) return s;
+  if (!gate_up_elems || !down_elems) return fail(MOE_ERR_INVALID_ARG, "output pointer is NULL");
+  if (p->H % 32 || p->I % 32)
+    return fail(MOE_ERR_UNSUPPORTED, "packed experts need H and I multiples of 32");
+  *gate_up_elems = pack_experts_elems(p->E, p->I, p->H, true);
+  *down_elems = pack_experts_elems(p->E, p->H, p->I, false);
+  return ok();
+}
+
+moe_status moe_pack_experts(const moe_params* p, const moe_bf16* w_gate_up, const moe_bf16* w_down,
+                            moe_bf16* gate_up_packed, moe_bf16* down_packed, hipStream_t stream) {
+  int64_t gu = 0, dn = 0;
+  moe_status s = moe_packed_experts_size(p, &gu, &dn);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(w_gate_up);
+  REQUIRE_PTR(w_down);
+  REQUIRE_PTR(gate_up_packed);
+  REQUIRE_PTR(down_packed);
+  if ((s = device_status(launch_pack_experts(w_gate_up, gate_up_packed, p->E, p->I, p->H, true,
+                                             stream),
+                         "pack gate_up")) != MOE_OK ||
+      (s = device_status(launch_pack_experts(w_down, down_packed, p->E, p->H, p->I, false,
+                                             stream),
+                         "pack down")) != MOE_OK)
     return s;
   return ok();
 }

@@ -328,11 +328,12 @@ __device__ __forceinline__ int pl_swz(int row, int chunk) {
   return KB == 32 ? chunk ^ ((row >> 2) & 3) : chunk ^ ((row >> 1) & 7);
 }
 
-// Compile-time shape of the pipelined tile.
-template <int BM_, int BN_, bool GATEUP_, int KB_, int NW_, int WAVES_M_>
+// Compile-time shape of the pipelined tile; PACKED: the weights in the
+// tile-blocked layout of launch_pack_experts.
+template <int BM_, int BN_, bool GATEUP_, int KB_, int NW_, int WAVES_M_, bool PACKED_ = false>
 struct PipeShape {
   static constexpr int BM = BM_, BN = BN_, KB = KB_, NW = NW_, WAVES_M = WAVES_M_;
-  static constexpr bool GATEUP = GATEUP_;
+  static constexpr bool GATEUP = GATEUP_, PACKED = PACKED_;
   static constexpr int NB = GATEUP ? 2 * BN : BN;  // weight rows per tile
   static constexpr int ROWS = BM + NB;             // LDS rows per stage
   static constexpr int CHUNKS = KB / 8;            // 16-byte chunks per row
@@ -349,6 +350,10 @@ struct PipeShape {
   static constexpr int STORES = TM * TN * 4;       // epilogue stores per wave
   static_assert(INSTR % NW == 0 && SUB % 2 == 0, "shape");
   static_assert(BM % (NW * RPI) == 0, "A rows fill whole instructions of every wave");
+  static_assert(!PACKED || (KB == 32 && NB == 256), "the tile-blocked layout: 256 x 32 blocks");
+  // bytes between the K stages of one weight row: 64 in rows of K, one
+  // 256 x 32 block tile-blocked
+  static constexpr uint32_t W_STAGE = PACKED ? NB * KB * 2 : KB * 2;
 };
 
 // One output tile as one wavefront sees it: rows [row0, row_end) of its
@@ -452,6 +457,12 @@ __device__ __forceinline__ void pipe_locate_coords(const GemmProblem& P, int mt_
     const int chunk = pl_swz<S::KB>(row, lane % S::CHUNKS);
     if (i < S::A_INSTR) {
       T.off[i] = (uint32_t)pipe_a_row<S>(T, i, wave, lane);
+    } else if constexpr (S::PACKED) {
+      // tile-blocked weights: tile row r's 32 values of stage s at byte
+      // ((tile * K/32 + s) * NB + r) * 64; the stage part goes in the
+      // scalar offset (pipe_issue)
+      const int r = row - S::BM;
+      T.off[i] = (uint32_t)((int64_t)(T.n0 / S::BN) * S::NB * K * 2 + r * 64 + chunk * 16);
     } else {
       const int r = row - S::BM;
       int n = S::GATEUP ? T.n0 + (r < S::BN ? r : r - S::BN) : T.n0 + r;
@@ -496,7 +507,8 @@ __device__ __forceinline__ void pipe_issue(const PipeTile<S>& T, uint16_t* smem,
   uint16_t* base = smem + slot * S::STAGE;
 #pragma unroll
   for (int i = 0; i < S::PER_WAVE; ++i)
-    lds_buffer_16(i < S::A_INSTR ? T.rs_a : T.rs_w, T.off[i], (uint32_t)k0 * 2,
+    lds_buffer_16(i < S::A_INSTR ? T.rs_a : T.rs_w, T.off[i],
+                  i < S::A_INSTR ? (uint32_t)k0 * 2 : (uint32_t)(k0 / S::KB) * S::W_STAGE,
                   base + (wave + S::NW * i) * S::RPI * S::KB);
 }
 
@@ -2101,10 +2113,11 @@ int device_cu_count() {
   return cached;
 }
 
-template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP>
+template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP,
+          bool PACKED>
 hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
                        hipStream_t stream) {
-  using S = PipeShape<BM, BN, GATEUP, KB, NW, WAVES_M>;
+  using S = PipeShape<BM, BN, GATEUP, KB, NW, WAVES_M, PACKED>;
   const size_t lds = (size_t)STAGES * S::STAGE * sizeof(uint16_t);
   static_assert((size_t)STAGES * S::STAGE * 2 <= 160 * 1024, "LDS");
   void (*kern)(GemmProblem, GemmProblem, int, float);
@@ -2175,6 +2188,41 @@ hipError_t launch_wstream_w4(const GemmProblem& a, float limit, hipStream_t stre
   const int grid = max_wgs > 0 ? std::min(max_wgs, device_cu_count()) : device_cu_count();
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, stream, a, limit);
   return hipGetLastError();
+}
+
+// Tile-blocked copy of expert weights (launch_pack_experts): one workgroup
+// of 256 threads per block (group, tile b, K stage s); thread r copies tile
+// row r's 32 values (64 bytes, four 16-byte loads and stores).
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void pack_experts_kernel(const uint16_t* __restrict__ w,
+                                                           uint16_t* __restrict__ packed, int N,
+                                                           int K, int ntiles) {
+  const int nk = K / 32;
+  const int64_t blk = blockIdx.x;  // (g * ntiles + b) * nk + s
+  const int s = (int)(blk % nk);
+  const int64_t gb = blk / nk;
+  const int b = (int)(gb % ntiles);
+  const int64_t g = gb / ntiles;
+  const int r = threadIdx.x;
+  int n;
+  bool up = false;
+  if (GATEUP) {
+    up = r >= 128;
+    n = 128 * b + (r & 127);
+  } else {
+    n = 256 * b + r;
+  }
+  const int64_t rows = GATEUP ? 2 * (int64_t)N : N;
+  uint4* dst = reinterpret_cast<uint4*>(packed + (blk * 256 + r) * 32);
+  if (n < N) {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        w + (g * rows + (up ? N + n : n)) * (int64_t)K + (int64_t)s * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = src[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
 // m-tile prefix of up to two tile heights over one set of group offsets.
@@ -2250,6 +2298,25 @@ int gemm_tile_n(GemmVariant v, bool gateup) {
 
 int gemm_w4_tile_n(bool gateup) { return gateup ? 8 * W4_NBLK * W4_NW : 16 * W4_NBLK * W4_NW; }
 
+int64_t pack_experts_elems(int G, int N, int K, bool gateup) {
+  const int64_t tiles = gateup ? (N + 127) / 128 : (N + 255) / 256;
+  return (int64_t)G * tiles * 256 * K;
+}
+
+hipError_t launch_pack_experts(const uint16_t* w, uint16_t* packed, int G, int N, int K,
+                               bool gateup, hipStream_t stream) {
+  const int ntiles = gateup ? (N + 127) / 128 : (N + 255) / 256;
+  const int64_t blocks = (int64_t)G * ntiles * (K / 32);
+  if (blocks == 0) return hipSuccess;
+  if (gateup)
+    hipLaunchKernelGGL(pack_experts_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                       packed, N, K, ntiles);
+  else
+    hipLaunchKernelGGL(pack_experts_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, w,
+                       packed, N, K, ntiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
                                 int32_t* start0, int32_t* start1, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_schedule_kernel, dim3(1), dim3(1024), 0, stream, group_offsets, G, bm0,
@@ -2257,11 +2324,28 @@ hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, in
   return hipGetLastError();
 }
 
+// The 256-row tiles over weights in rows of K or tile-blocked (PACKED).
+template <bool PACKED>
+hipError_t launch_pipe_layout(GemmVariant v, bool gateup, const GemmProblem& a,
+                              const GemmProblem* b, float limit, hipStream_t stream) {
+  // ping-pong: eight wavefronts taking turns on each SIMD; its cross-tile
+  // stage stream needs at least 2 (STAGES-1) = 8 stages per tile, so
+  // shorter K takes the interleaved schedule of the same tile (eight
+  // wavefronts, two per SIMD)
+  const bool pp = v == GemmVariant::kPingPong && a.K >= 8 * 32 && (b == nullptr || b->K >= 8 * 32);
+  if (pp) {
+    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, true, PACKED>(a, b, limit, stream);
+    return launch_pipe<256, 256, false, 32, 5, 2, 8, true, PACKED>(a, b, limit, stream);
+  }
+  if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false, PACKED>(a, b, limit, stream);
+  return launch_pipe<256, 256, false, 32, 5, 2, 8, false, PACKED>(a, b, limit, stream);
+}
+
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                const GemmProblem* b, float limit, hipStream_t stream,
                                int max_wgs) {
   if (a.S != nullptr) {  // W4A16 weights: one problem per launch
-    if (b != nullptr || a.K % 128 != 0) return hipErrorInvalidValue;
+    if (b != nullptr || a.K % 128 != 0 || a.packed) return hipErrorInvalidValue;
     if (v == GemmVariant::kPingPong) {  // long segments: the ping-pong tile
       if (a.K < 256 || a.N % 32 != 0) return hipErrorInvalidValue;
       if (gateup) return launch_pp_w4<true>(a, limit, stream);
@@ -2272,24 +2356,18 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
       return launch_wstream_w4<true, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);
     return launch_wstream_w4<false, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);
   }
+  // the tile-blocked weight layout is read by the 256-row tiles only, and
+  // the problems of one launch share their layout
+  if (b != nullptr && b->packed != a.packed) return hipErrorInvalidValue;
+  if (a.packed && v != GemmVariant::kPingPong && v != GemmVariant::kPipe256W8)
+    return hipErrorInvalidValue;
+  if (a.packed) return launch_pipe_layout<true>(v, gateup, a, b, limit, stream);
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
   if (v == GemmVariant::kWStream) {  // 512-byte row pieces, four stages
     if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream, max_wgs);
     return launch_wstream<false, 256, 4>(a, b, limit, stream, max_wgs);
   }
-  if (v == GemmVariant::kPipe256W8) {  // eight wavefronts, two per SIMD, interleaved
-    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false>(a, b, limit, stream);
-    return launch_pipe<256, 256, false, 32, 5, 2, 8, false>(a, b, limit, stream);
-  }
-  if (v == GemmVariant::kPingPong) {  // eight wavefronts taking turns on each SIMD
-    // the cross-tile stage stream needs at least 2 (STAGES-1) = 8 stages per
-    // tile; shorter K takes the interleaved schedule of the same tile
-    if (a.K < 8 * 32 || (b != nullptr && b->K < 8 * 32)) {
-      if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false>(a, b, limit, stream);
-      return launch_pipe<256, 256, false, 32, 5, 2, 8, false>(a, b, limit, stream);
-    }
-    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, true>(a, b, limit, stream);
-    return launch_pipe<256, 256, false, 32, 5, 2, 8, true>(a, b, limit, stream);
-  }
+  if (v == GemmVariant::kPipe256W8 || v == GemmVariant::kPingPong)
+    return launch_pipe_layout<false>(v, gateup, a, b, limit, stream);
   return launch_pair<128, 128, 2, 2>(a, b, limit, gateup, stream);
 }

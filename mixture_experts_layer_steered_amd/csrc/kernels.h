@@ -32,6 +32,8 @@ struct GemmProblem {
   int32_t K;                      // reduction length
   int32_t ntiles;                 // ceil(N / BN) (BN of the variant and projection)
   int32_t max_mtiles;             // host bound: ceil(M / BM) + G (or ceil(M / BM) for one group)
+  int32_t packed;                 // 1: W in the tile-blocked layout of launch_pack_experts
+                                  // (256-row tiles only; w_stride its padded expert size)
 };
 
 // Tile variants of the grouped GEMM: persistent weight streaming in long
@@ -73,6 +75,16 @@ hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, 
 // x_perm[r] = x[sorted_token[r]] for r < N (rows of H bf16, H a multiple of 8).
 hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_token, uint16_t* x_perm,
                               int64_t N, int H, hipStream_t stream);
+
+// Tile-blocked copy of G experts' weights for the 256-row tiles: for each
+// group, tile b of 256 weight rows and K stage s of 32 columns, one block of
+// 256 rows x 32 values (row-contiguous), blocks in the order (group, b, s).
+// gate_up (gateup, W [G, 2N, K]): tile b's rows are gate rows 128 b .. + 127
+// then the up rows N + 128 b ..; down (W [G, N, K]): rows 256 b .. + 255.
+// Rows past N are zeros.  K a multiple of 32.
+int64_t pack_experts_elems(int G, int N, int K, bool gateup);
+hipError_t launch_pack_experts(const uint16_t* w, uint16_t* packed, int G, int N, int K,
+                               bool gateup, hipStream_t stream);
 
 hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, int bm1,
                                 int32_t* start0, int32_t* start1, hipStream_t stream);

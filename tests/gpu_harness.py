@@ -128,6 +128,28 @@ class Device:
                                       self.inv_pos, self.xr, self.logits, h=self.h,
                                       h_shared=self.hs)
 
+    def pack(self) -> None:
+        """Write the tile-blocked copies of the bf16 experts (routed, and the
+        shared expert with E = 1, I = I_shared) and hand them to the layer."""
+        torch, moe, wl = self.torch, self.moe, self.wl
+        gu_n, dn_n = moe.moe_packed_experts_size(self.params)
+        self.gu_packed = torch.full((gu_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+        self.dn_packed = torch.full((dn_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+        moe.moe_pack_experts(self.params, self.w_gate_up, self.w_down, self.gu_packed,
+                             self.dn_packed)
+        extra = dict(w_gate_up_packed=self.gu_packed, w_down_packed=self.dn_packed)
+        if wl.I_s:
+            ps = moe.make_params(self.T, wl.H, 1, 1, wl.I_s, 0, wl.rsf, wl.limit, False, wl.eps)
+            sgu_n, sdn_n = moe.moe_packed_experts_size(ps)
+            self.sgu_packed = torch.full((sgu_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+            self.sdn_packed = torch.full((sdn_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+            moe.moe_pack_experts(ps, self.ws_gate_up, self.ws_down, self.sgu_packed,
+                                 self.sdn_packed)
+            extra.update(ws_gate_up_packed=self.sgu_packed, ws_down_packed=self.sdn_packed)
+        self.weights = moe.make_weights(self.w_router, self.corr_bias, self.w_gate_up,
+                                        self.w_down, self.ws_gate_up, self.ws_down,
+                                        self.gamma_pre, self.gamma_post, **extra)
+
     def canary(self) -> None:
         """Fill every output with NaN / out-of-range bits first, so that an
         element the kernels never write shows up."""

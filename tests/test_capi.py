@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     lib = moe.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -176,6 +176,44 @@ def test_entry_points_reject_before_launch():
     # prefill-sized with H = 128 < 256: dequantised as well
     extra = moe.moe_workspace_size(P(T=4096, w4=True)) - moe.moe_workspace_size(P(T=4096))
     assert extra >= 8 * 3 * 256 * 128 * 2
+
+
+def test_packed_experts_validation():
+    """The tile-blocked expert copies: sizes (E * ceil(I/128) * 256 * H for
+    gate_up, E * ceil(H/256) * 256 * I for down), H and I multiples of 32,
+    and the forward's host checks of the *_packed fields."""
+    assert moe.moe_packed_experts_size(P(H=4096, E=64, I=1536)) == (
+        64 * 12 * 256 * 4096, 64 * 16 * 256 * 1536)
+    # ragged: I = 160 -> two gate_up tiles; H = 288 -> two down tiles
+    assert moe.moe_packed_experts_size(P(H=288, E=3, I=160)) == (
+        3 * 2 * 256 * 288, 3 * 2 * 256 * 160)
+    for kw in (dict(H=136), dict(I=200)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_packed_experts_size(P(**kw))
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as ei:   # a NULL source
+        moe.moe_pack_experts(P(), 16, None, 16, 16, stream=0)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:   # misaligned output
+        moe.moe_pack_experts(P(), 16, 16, 16, 24, stream=0)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    base = dict(w_router=16, corr_bias=None, w_gate_up=16, w_down=16, ws_gate_up=16, ws_down=16)
+    full = dict(w_gate_up_packed=16, w_down_packed=16, ws_gate_up_packed=16, ws_down_packed=16)
+    w4 = dict(w_gate_up_q=16, w_gate_up_scale=16, w_down_q=16, w_down_scale=16)
+    cases = [
+        (P(), dict(full, w_down_packed=None), moe.MOE_ERR_INVALID_ARG),    # routed pair split
+        (P(), dict(full, ws_down_packed=None), moe.MOE_ERR_INVALID_ARG),   # shared pair missing
+        (P(), dict(full, ws_gate_up_packed=24), moe.MOE_ERR_UNSUPPORTED),  # misaligned
+        (P(I_shared=0), dict(w_gate_up_packed=16, w_down_packed=16), moe.MOE_ERR_WORKSPACE),
+        (P(I_shared=136), full, moe.MOE_ERR_UNSUPPORTED),                  # not 32-multiple
+        (P(w4=True), dict(full, **w4), moe.MOE_ERR_INVALID_ARG),           # W4A16 + packed
+        (P(), full, moe.MOE_ERR_WORKSPACE),                                # valid
+    ]
+    for p, extra, status in cases:
+        w = moe.make_weights(**dict(base, **extra))
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_forward(p, 16, None, w, 16, None, 16, stream=0)
+        assert ei.value.status == status, (extra, status)
 
 
 def test_finish_validation():

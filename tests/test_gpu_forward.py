@@ -209,6 +209,99 @@ def test_forward_graph_replay_matches_eager(name):
         np.testing.assert_array_equal(gh.to_bits(d.out), eager)
 
 
+# ------------------------------------------ tile-blocked expert copies ----
+
+def packed_layout(w: np.ndarray, N: int, K: int, gateup: bool) -> np.ndarray:
+    """The tile-blocked layout of moe_pack_experts as the header defines it,
+    built by indexing: blocks (e, b, s) of 256 rows x 32 values; gate_up tile
+    b holds gate rows 128 b + r then up rows N + 128 b + r, down tile b rows
+    256 b + r; rows past N zero."""
+    E = w.shape[0]
+    tile = 128 if gateup else 256
+    nt = -(-N // tile)
+    out = np.zeros((E, nt, K // 32, 256, 32), dtype=w.dtype)
+    for b in range(nt):
+        for r in range(256):
+            n = tile * b + (r % 128 if gateup else r)
+            if n < N:
+                src = N + n if gateup and r >= 128 else n
+                out[:, b, :, r, :] = w[:, src, :].reshape(E, K // 32, 32)
+    return out.reshape(-1)
+
+
+def test_pack_experts_layout():
+    """moe_pack_experts writes every element of the layout, bit for bit:
+    ragged tiles in both projections (I = 160 < 2 x 128, H = 288 < 2 x 256)."""
+    torch, moe = gh.torch_and_lib()
+    E, H, I = 3, 288, 160
+    rng = np.random.default_rng(11)
+    wgu = rng.integers(0, 1 << 16, size=(E, 2 * I, H), dtype=np.uint16)
+    wdn = rng.integers(0, 1 << 16, size=(E, H, I), dtype=np.uint16)
+    p = moe.make_params(64, H, E, 2, I, 0, 1.0, 7.0, False, 1e-6)
+    gu_n, dn_n = moe.moe_packed_experts_size(p)
+    gu = torch.full((gu_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+    dn = torch.full((dn_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+    gh.note(f"pack E={E} H={H} I={I}")
+    moe.moe_pack_experts(p, gh.dev_bf16(torch, wgu), gh.dev_bf16(torch, wdn), gu, dn)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gh.to_bits(gu), packed_layout(wgu, I, H, True))
+    np.testing.assert_array_equal(gh.to_bits(dn), packed_layout(wdn, H, I, False))
+
+
+PACKED = {
+    # K >= 256 in both projections (the ping-pong schedule), ragged N tiles in
+    # both (I = 288, H = 288), a shared expert whose width is ragged too
+    "pp_ragged": Workload("pp_ragged", T=700, H=288, E=4, k=2, I=288, I_s=320, rsf=1.3),
+    "pipe_small": SMALL["pipe_small"],      # K = 160 in down: the interleaved schedule
+    "scmoe_gamma": SMALL["scmoe_gamma"],
+    "no_shared": SMALL["no_shared"],
+}
+
+
+@pytest.mark.parametrize("variant", ["pingpong", "pipe256w8"])
+@pytest.mark.parametrize("name", list(PACKED))
+def test_forward_packed_experts(monkeypatch, variant, name):
+    """The 256-row tiles over the tile-blocked copies give the same bits as
+    over the row-major experts (only the addresses differ), and the layer
+    stays parity-green against the oracle."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT", variant)
+    wl = PACKED[name]
+    inp = moe_inputs.generate(wl, seed=6)
+    gh.note(f"packed {variant} {wl.label()}")
+    d = gh.Device(wl, inp)
+    d.canary()
+    d.run()
+    rows = d.result()
+    d.pack()
+    d.canary()
+    d.run()
+    tiled = d.result()
+    for key in ("out", "h", "hs"):
+        if key in rows:
+            np.testing.assert_array_equal(tiled[key], rows[key], err_msg=key)
+    gh.check_layer(wl, inp, tiled)
+
+
+def test_forward_prefill_packed_full():
+    """The measured prefill workload with the tile-blocked copies: every
+    output bit equal to the row-major run, a sample of tokens against the
+    oracle."""
+    wl = moe_inputs.WORKLOADS["prefill"]
+    gh.note(f"generating {wl.label()}")
+    inp = moe_inputs.generate(wl, seed=0)
+    d = gh.Device(wl, inp)
+    d.run()
+    rows = d.result()
+    d.pack()
+    d.canary()
+    d.run()
+    tiled = d.result()
+    np.testing.assert_array_equal(tiled["out"], rows["out"])
+    np.testing.assert_array_equal(tiled["h"], rows["h"])
+    sample = np.sort(np.random.default_rng(7).choice(wl.T, size=64, replace=False))
+    gh.note(f"  {gh.check_layer(wl, inp, tiled, sample)}")
+
+
 # ------------------------------------------------ W4A16 routed experts ----
 
 W4 = {
