@@ -287,6 +287,7 @@ GemmProblem make_problem(const uint16_t* A, const int32_t* row_index, const int3
   P.ntiles = (N + bn - 1) / bn;
   P.max_mtiles = (int32_t)((M + bm - 1) / bm + (offsets ? G : 0));
   P.packed = 0;
+  P.hblk = 0;
   return P;
 }
 
@@ -626,6 +627,12 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     sdn.W = w->ws_down_packed;
     sdn.packed = 1;
   }
+  // the 256-row tiles pass h (and the shared expert's) from gate_up to down
+  // stage-blocked within each tile, so that down reads a K stage of a tile as
+  // one contiguous block; a caller who reads h or h_shared gets them in rows
+  if ((v == GemmVariant::kPingPong || v == GemmVariant::kPipe256W8) && !w4 &&
+      !(probes && (probes->h || probes->h_shared)))
+    gu.hblk = dn.hblk = sgu.hblk = sdn.hblk = 1;
   if (p->scmoe) gu.A = L.xr;
   if (!tiles_fit(gu, shared ? &sgu : nullptr) || !tiles_fit(dn, shared ? &sdn : nullptr))
     return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");

@@ -329,11 +329,16 @@ __device__ __forceinline__ int pl_swz(int row, int chunk) {
 }
 
 // Compile-time shape of the pipelined tile; PACKED: the weights in the
-// tile-blocked layout of launch_pack_experts.
-template <int BM_, int BN_, bool GATEUP_, int KB_, int NW_, int WAVES_M_, bool PACKED_ = false>
+// tile-blocked layout of launch_pack_experts; HBLK: h stage-blocked within
+// each tile (gate_up writes it so, down reads it so as its A): the tile's
+// rows [row0, row0 + rows) of K columns keep their row-major footprint,
+// holding stage s (columns [32 s, 32 s + 32)) of row r at element
+// row0 * K + (s * rows + r) * 32.
+template <int BM_, int BN_, bool GATEUP_, int KB_, int NW_, int WAVES_M_, bool PACKED_ = false,
+          bool HBLK_ = false>
 struct PipeShape {
   static constexpr int BM = BM_, BN = BN_, KB = KB_, NW = NW_, WAVES_M = WAVES_M_;
-  static constexpr bool GATEUP = GATEUP_, PACKED = PACKED_;
+  static constexpr bool GATEUP = GATEUP_, PACKED = PACKED_, HBLK = HBLK_;
   static constexpr int NB = GATEUP ? 2 * BN : BN;  // weight rows per tile
   static constexpr int ROWS = BM + NB;             // LDS rows per stage
   static constexpr int CHUNKS = KB / 8;            // 16-byte chunks per row
@@ -351,6 +356,7 @@ struct PipeShape {
   static_assert(INSTR % NW == 0 && SUB % 2 == 0, "shape");
   static_assert(BM % (NW * RPI) == 0, "A rows fill whole instructions of every wave");
   static_assert(!PACKED || (KB == 32 && NB == 256), "the tile-blocked layout: 256 x 32 blocks");
+  static_assert(!HBLK || KB == 32, "h blocks of 32 columns");
   // bytes between the K stages of one weight row: 64 in rows of K, one
   // 256 x 32 block tile-blocked
   static constexpr uint32_t W_STAGE = PACKED ? NB * KB * 2 : KB * 2;
@@ -368,6 +374,12 @@ struct PipeTile {
   __amdgpu_buffer_rsrc_t rs_a, rs_w;
   uint32_t off[S::PER_WAVE];
 };
+
+// Rows of tile T (BM, fewer in a segment's last tile).
+template <class S>
+__device__ __forceinline__ int64_t pipe_rows(const PipeTile<S>& T) {
+  return T.row_end - T.row0 < S::BM ? T.row_end - T.row0 : S::BM;
+}
 
 // Tile t of a problem with mt_total m-tiles.  Tile order: group (expert)
 // major, then blocks of up to PL_MBLK m-tiles, n-tile, m-tile (the last
@@ -427,13 +439,6 @@ __device__ __forceinline__ uint32_t pipe_a_off_of(int K, int32_t a_row, int i, i
   return (uint32_t)(((int64_t)a_row * K + chunk * 8) * 2);
 }
 
-template <class S>
-__device__ __forceinline__ uint32_t pipe_a_off(const GemmProblem& P, const PipeTile<S>& T, int i,
-                                               int wave, int lane) {
-  const int32_t r = pipe_a_row<S>(T, i, wave, lane);
-  return pipe_a_off_of<S>(P.K, P.row_index ? P.row_index[r] : r, i, wave, lane);
-}
-
 // Tile T's place in three parts.  pipe_locate_coords: coordinates, weight
 // offsets, and the A rows in the problem's row space (in T.off[i <
 // A_INSTR]); pipe_locate_rows: those rows through row_index when A is
@@ -486,8 +491,17 @@ __device__ __forceinline__ void pipe_locate_end(int K, PipeTile<S>& T) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < S::A_INSTR; ++i)
-    T.off[i] = pipe_a_off_of<S>(K, (int32_t)T.off[i], i, wave, lane);
+  for (int i = 0; i < S::A_INSTR; ++i) {
+    if constexpr (S::HBLK && !S::GATEUP) {
+      // A stage-blocked within the tile: the row's 64 bytes of stage 0 at
+      // row0 * K * 2 + r * 64; the stage part goes in the scalar offset
+      const int row = S::RPI * (wave + S::NW * i) + lane / S::CHUNKS;
+      const int chunk = pl_swz<S::KB>(row, lane % S::CHUNKS);
+      T.off[i] = (uint32_t)(T.row0 * K * 2 + ((int64_t)T.off[i] - T.row0) * 64 + chunk * 16);
+    } else {
+      T.off[i] = pipe_a_off_of<S>(K, (int32_t)T.off[i], i, wave, lane);
+    }
+  }
 }
 
 template <class S>
@@ -505,10 +519,14 @@ __device__ __forceinline__ void pipe_issue(const PipeTile<S>& T, uint16_t* smem,
                                            int k0) {
   const int wave = threadIdx.x >> 6;
   uint16_t* base = smem + slot * S::STAGE;
+  // bytes between A's K stages: 64 in rows of K; the tile's rows x 64 when
+  // stage-blocked
+  uint32_t a_soff = (uint32_t)k0 * 2;
+  if constexpr (S::HBLK && !S::GATEUP) a_soff = (uint32_t)(k0 / S::KB) * (uint32_t)pipe_rows(T) * 64u;
 #pragma unroll
   for (int i = 0; i < S::PER_WAVE; ++i)
     lds_buffer_16(i < S::A_INSTR ? T.rs_a : T.rs_w, T.off[i],
-                  i < S::A_INSTR ? (uint32_t)k0 * 2 : (uint32_t)(k0 / S::KB) * S::W_STAGE,
+                  i < S::A_INSTR ? a_soff : (uint32_t)(k0 / S::KB) * S::W_STAGE,
                   base + (wave + S::NW * i) * S::RPI * S::KB);
 }
 
@@ -582,7 +600,7 @@ template <class S>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pipe_out_rsrc(const GemmProblem& P,
                                                                 const PipeTile<S>& T) {
   constexpr int ES = S::GATEUP ? 2 : 4;  // bytes per output element
-  const int64_t rows = T.row_end - T.row0 < S::BM ? T.row_end - T.row0 : S::BM;
+  const int64_t rows = pipe_rows(T);
   const uint64_t base = reinterpret_cast<uint64_t>(static_cast<char*>(P.out) + T.row0 * P.N * ES);
   const uint64_t b = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
@@ -616,6 +634,7 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
   constexpr int WROWS = HALF ? S::WM / 2 : S::WM;
   auto live = [](int i) { return !HALF || i < S::TM / 2; };
   if constexpr (S::GATEUP) {
+    const uint32_t rows = (uint32_t)pipe_rows(T);
 #pragma unroll
     for (int i = 0; i < S::TM; ++i) {
       const int r = wm * WROWS + i * 32 + (lane & 31);
@@ -633,7 +652,12 @@ __device__ __forceinline__ void pipe_store(const GemmProblem& P, const PipeTile<
                           swiglu_clamped_fast(g[4 * q + 3] * ts, u[4 * q + 3] * ts, limit)};
           uint2_t pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(h01, bf16x2_t)),
                         __builtin_bit_cast(uint32_t, __builtin_convertvector(h23, bf16x2_t))};
-          pipe_st64(pk, rs, live(i) && col < N ? (uint32_t)(r * N + col) * 2u : kOut);
+          // stage-blocked h: row r of stage col / 32 at (col / 32 * rows + r) * 64
+          // bytes (rows past the segment would land in other rows: dropped)
+          const uint32_t off = S::HBLK ? ((uint32_t)(col >> 5) * rows + r) * 64u + (col & 31) * 2u
+                                       : (uint32_t)(r * N + col) * 2u;
+          pipe_st64(pk, rs,
+                    live(i) && col < N && (!S::HBLK || (uint32_t)r < rows) ? off : kOut);
         }
       }
     }
@@ -2114,10 +2138,10 @@ int device_cu_count() {
 }
 
 template <int BM, int BN, bool GATEUP, int KB, int STAGES, int WAVES_M, int NW, bool PP,
-          bool PACKED>
+          bool PACKED, bool HBLK>
 hipError_t launch_pipe(const GemmProblem& a, const GemmProblem* b, float limit,
                        hipStream_t stream) {
-  using S = PipeShape<BM, BN, GATEUP, KB, NW, WAVES_M, PACKED>;
+  using S = PipeShape<BM, BN, GATEUP, KB, NW, WAVES_M, PACKED, HBLK>;
   const size_t lds = (size_t)STAGES * S::STAGE * sizeof(uint16_t);
   static_assert((size_t)STAGES * S::STAGE * 2 <= 160 * 1024, "LDS");
   void (*kern)(GemmProblem, GemmProblem, int, float);
@@ -2324,8 +2348,9 @@ hipError_t launch_gemm_schedule(const int32_t* group_offsets, int G, int bm0, in
   return hipGetLastError();
 }
 
-// The 256-row tiles over weights in rows of K or tile-blocked (PACKED).
-template <bool PACKED>
+// The 256-row tiles over weights in rows of K or tile-blocked (PACKED), h
+// in rows or stage-blocked (HBLK).
+template <bool PACKED, bool HBLK>
 hipError_t launch_pipe_layout(GemmVariant v, bool gateup, const GemmProblem& a,
                               const GemmProblem* b, float limit, hipStream_t stream) {
   // ping-pong: eight wavefronts taking turns on each SIMD; its cross-tile
@@ -2334,18 +2359,18 @@ hipError_t launch_pipe_layout(GemmVariant v, bool gateup, const GemmProblem& a,
   // wavefronts, two per SIMD)
   const bool pp = v == GemmVariant::kPingPong && a.K >= 8 * 32 && (b == nullptr || b->K >= 8 * 32);
   if (pp) {
-    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, true, PACKED>(a, b, limit, stream);
-    return launch_pipe<256, 256, false, 32, 5, 2, 8, true, PACKED>(a, b, limit, stream);
+    if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, true, PACKED, HBLK>(a, b, limit, stream);
+    return launch_pipe<256, 256, false, 32, 5, 2, 8, true, PACKED, HBLK>(a, b, limit, stream);
   }
-  if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false, PACKED>(a, b, limit, stream);
-  return launch_pipe<256, 256, false, 32, 5, 2, 8, false, PACKED>(a, b, limit, stream);
+  if (gateup) return launch_pipe<256, 128, true, 32, 5, 2, 8, false, PACKED, HBLK>(a, b, limit, stream);
+  return launch_pipe<256, 256, false, 32, 5, 2, 8, false, PACKED, HBLK>(a, b, limit, stream);
 }
 
 hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
                                const GemmProblem* b, float limit, hipStream_t stream,
                                int max_wgs) {
   if (a.S != nullptr) {  // W4A16 weights: one problem per launch
-    if (b != nullptr || a.K % 128 != 0 || a.packed) return hipErrorInvalidValue;
+    if (b != nullptr || a.K % 128 != 0 || a.packed || a.hblk) return hipErrorInvalidValue;
     if (v == GemmVariant::kPingPong) {  // long segments: the ping-pong tile
       if (a.K < 256 || a.N % 32 != 0) return hipErrorInvalidValue;
       if (gateup) return launch_pp_w4<true>(a, limit, stream);
@@ -2356,18 +2381,20 @@ hipError_t launch_grouped_gemm(GemmVariant v, bool gateup, const GemmProblem& a,
       return launch_wstream_w4<true, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);
     return launch_wstream_w4<false, W4_NBLK, W4_KB, W4_NW, W4_STAGES>(a, limit, stream, max_wgs);
   }
-  // the tile-blocked weight layout is read by the 256-row tiles only, and
-  // the problems of one launch share their layout
-  if (b != nullptr && b->packed != a.packed) return hipErrorInvalidValue;
-  if (a.packed && v != GemmVariant::kPingPong && v != GemmVariant::kPipe256W8)
+  // the blocked weight and h layouts are read by the 256-row tiles only,
+  // and the problems of one launch share their layouts
+  if (b != nullptr && (b->packed != a.packed || b->hblk != a.hblk)) return hipErrorInvalidValue;
+  if ((a.packed || a.hblk) && v != GemmVariant::kPingPong && v != GemmVariant::kPipe256W8)
     return hipErrorInvalidValue;
-  if (a.packed) return launch_pipe_layout<true>(v, gateup, a, b, limit, stream);
+  if (a.packed && a.hblk) return launch_pipe_layout<true, true>(v, gateup, a, b, limit, stream);
+  if (a.packed) return launch_pipe_layout<true, false>(v, gateup, a, b, limit, stream);
+  if (a.hblk) return launch_pipe_layout<false, true>(v, gateup, a, b, limit, stream);
   if (v == GemmVariant::kTile32) return launch_pair<32, 128, 1, 4>(a, b, limit, gateup, stream);
   if (v == GemmVariant::kWStream) {  // 512-byte row pieces, four stages
     if (gateup) return launch_wstream<true, 256, 4>(a, b, limit, stream, max_wgs);
     return launch_wstream<false, 256, 4>(a, b, limit, stream, max_wgs);
   }
   if (v == GemmVariant::kPipe256W8 || v == GemmVariant::kPingPong)
-    return launch_pipe_layout<false>(v, gateup, a, b, limit, stream);
+    return launch_pipe_layout<false, false>(v, gateup, a, b, limit, stream);
   return launch_pair<128, 128, 2, 2>(a, b, limit, gateup, stream);
 }

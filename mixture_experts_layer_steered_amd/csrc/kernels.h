@@ -34,6 +34,11 @@ struct GemmProblem {
   int32_t max_mtiles;             // host bound: ceil(M / BM) + G (or ceil(M / BM) for one group)
   int32_t packed;                 // 1: W in the tile-blocked layout of launch_pack_experts
                                   // (256-row tiles only; w_stride its padded expert size)
+  int32_t hblk;                   // 1 (256-row tiles only): gate_up writes `out`, down reads
+                                  // A, stage-blocked within each 256-row tile: the tile's
+                                  // rows [r0, r0 + n) keep their row-major footprint, with
+                                  // columns [32 s, 32 s + 32) of row r0 + r at element
+                                  // r0 * K + (s * n + r) * 32 (K: h's width)
 };
 
 // Tile variants of the grouped GEMM: persistent weight streaming in long

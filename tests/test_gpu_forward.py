@@ -282,10 +282,45 @@ def test_forward_packed_experts(monkeypatch, variant, name):
     gh.check_layer(wl, inp, tiled)
 
 
+def unprobe_h(d) -> None:
+    """Probe everything but h and h_shared: the forward then hands h from
+    gate_up to down in its own layout (stage-blocked within each 256-row
+    tile on those tiles)."""
+    d.probes = d.moe.make_probes(d.ids, d.w, d.offsets, d.sorted_token, d.inv_pos, d.xr,
+                                 d.logits)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("variant", ["pingpong", "pipe256w8"])
+@pytest.mark.parametrize("name", list(PACKED))
+def test_forward_blocked_h(monkeypatch, variant, name, packed):
+    """h stage-blocked between the 256-row tiles gives the same output bits
+    as h in rows (the run that probes it, checked against the oracle):
+    partial and half-height tiles, experts with no rows, the shared expert
+    with T not a multiple of 256, either weight layout."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT", variant)
+    wl = PACKED[name]
+    inp = moe_inputs.generate(wl, seed=8)
+    gh.note(f"blocked h {variant} packed={packed} {wl.label()}")
+    d = gh.Device(wl, inp)
+    if packed:
+        d.pack()
+    d.canary()
+    d.run()
+    rows = d.result()
+    gh.check_layer(wl, inp, rows)
+    unprobe_h(d)
+    d.canary()
+    d.run()
+    blk = d.result()
+    for key in ("out", "ids", "offsets", "sorted_token", "inv_pos"):
+        np.testing.assert_array_equal(blk[key], rows[key], err_msg=key)
+
+
 def test_forward_prefill_packed_full():
-    """The measured prefill workload with the tile-blocked copies: every
-    output bit equal to the row-major run, a sample of tokens against the
-    oracle."""
+    """The measured prefill workload with the tile-blocked expert copies and
+    with h stage-blocked (the bench's configuration): every output bit equal
+    to the row-major run, a sample of tokens against the oracle."""
     wl = moe_inputs.WORKLOADS["prefill"]
     gh.note(f"generating {wl.label()}")
     inp = moe_inputs.generate(wl, seed=0)
@@ -300,6 +335,10 @@ def test_forward_prefill_packed_full():
     np.testing.assert_array_equal(tiled["h"], rows["h"])
     sample = np.sort(np.random.default_rng(7).choice(wl.T, size=64, replace=False))
     gh.note(f"  {gh.check_layer(wl, inp, tiled, sample)}")
+    unprobe_h(d)
+    d.canary()
+    d.run()
+    np.testing.assert_array_equal(d.result()["out"], rows["out"])
 
 
 # ------------------------------------------------ W4A16 routed experts ----

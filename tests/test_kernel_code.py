@@ -42,16 +42,14 @@ def kernel_body(asm, pattern):
     return asm[start:end]
 
 
-# (kernel: PipeShape<256, BN, GATEUP, 32, 8, 2, PACKED> with gate_up Lb1E or
-# down Lb0E, then the weight layout Lb0E rows / Lb1E tile-blocked; STORES,
-# epilogue copies).  bf16 ping-pong: full tile, half-height tile, and the
-# stand-in before the first tile; W4A16 ping-pong: the same in gate_up, no
-# half-height tile in down
-CASES = [
-    (r"17grouped_pp_kernel.*Lb1ELi32ELi8ELi2ELb0E", 16, 3),
-    (r"17grouped_pp_kernel.*Lb1ELi32ELi8ELi2ELb1E", 16, 3),
-    (r"17grouped_pp_kernel.*Lb0ELi32ELi8ELi2ELb0E", 32, 3),
-    (r"17grouped_pp_kernel.*Lb0ELi32ELi8ELi2ELb1E", 32, 3),
+# (kernel: PipeShape<256, BN, GATEUP, 32, 8, 2, PACKED, HBLK> with gate_up
+# Lb1E or down Lb0E, then the weight layout and the h layout, each Lb0E rows
+# / Lb1E blocked; STORES, epilogue copies).  bf16 ping-pong: full tile,
+# half-height tile, and the stand-in before the first tile; W4A16
+# ping-pong: the same in gate_up, no half-height tile in down
+CASES = [(rf"17grouped_pp_kernel.*{proj}ELi32ELi8ELi2E{w}E{h}E", stores, 3)
+         for proj, stores in (("Lb1", 16), ("Lb0", 32))
+         for w in ("Lb0", "Lb1") for h in ("Lb0", "Lb1")] + [
     (r"20grouped_pp_w4_kernel.*Lb1ELi32", 16, 3),
     (r"20grouped_pp_w4_kernel.*Lb0ELi32", 32, 2),
 ]
