@@ -397,9 +397,14 @@ def test_forward_prefill_w4_full(scales):
     rows = None
     if scales == "full":
         rows = np.sort(np.random.default_rng(7).choice(wl.T, size=256, replace=False))
-    rep, _, dev = run_and_check(wl, inp, rows)
-    del dev
+    rep, gpu, dev = run_and_check(wl, inp, rows)
     assert rep["experts_touched"] == 64
+    # without h probes (as the bench runs it): the same output bits
+    unprobe_h(dev)
+    dev.canary()
+    dev.run()
+    np.testing.assert_array_equal(dev.result()["out"], gpu["out"])
+    del dev
 
 
 # ------------------------------------------------ finish (residual add) ----
@@ -518,7 +523,7 @@ def test_forward_w4_tiled(name):
     rng = np.random.default_rng(9)
     for n in ("w_gate_up_tscale", "w_down_tscale"):
         inp[n] = np.ldexp(1.0, rng.integers(-10, -7, size=wl.E)).astype(np.float32)
-    rep, gpu, _ = run_and_check(wl, inp)
+    rep, gpu, dw = run_and_check(wl, inp)
     ref_inp = _bf16_experts(inp)
     wl_bf16 = wl.with_(w4=False)
     gh.note(f"forward {name} as bf16 on host-rounded weights")
@@ -529,3 +534,8 @@ def test_forward_w4_tiled(name):
     assert np.array_equal(gpu["ids"], g2["ids"])
     assert np.array_equal(gpu["out"], g2["out"]), \
         f"differs from the bf16 path in {int(np.sum(gpu['out'] != g2['out']))} elements"
+    # without h probes (as the bench runs it): the same output bits
+    unprobe_h(dw)
+    dw.canary()
+    dw.run()
+    np.testing.assert_array_equal(dw.result()["out"], gpu["out"])
