@@ -38,6 +38,12 @@ non-temporal 16-byte loads) -- and the roofline record carries the
 fraction against that measured peak beside the one against the published
 peak (--no-probe-peaks skips them).
 
+expert layout: the bf16 experts' tile-blocked copies (moe_pack_experts) are
+written once before any timing, like a weight load, and handed to the layer
+beside the row-major weights (config.expert_layout); the 256-row tiles of
+prefill-sized batches read them, the other tiles the row-major weights.
+--row-major-experts leaves them out.
+
 cpu_baseline: the CPU oracle (float64 NumPy, untuned) timed on this host on
 a bounded sample of the same batch, with the host's CPU model and BLAS.
 """

@@ -255,6 +255,9 @@ PACKED = {
     "pipe_small": SMALL["pipe_small"],      # K = 160 in down: the interleaved schedule
     "scmoe_gamma": SMALL["scmoe_gamma"],
     "no_shared": SMALL["no_shared"],
+    # three tokens: one partial half-height tile per touched expert, most
+    # experts empty, the shared expert a single 3-row tile
+    "tiny_pp": Workload("tiny_pp", T=3, H=256, E=8, k=2, I=256, I_s=256),
 }
 
 
