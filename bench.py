@@ -536,12 +536,14 @@ def main() -> int:
     # any timing, as a weight-loading step (moe_pack_experts); the 256-row
     # tiles read them, the other tiles the row-major weights
     layout = "row_major"
-    if not wl.w4 and not args.row_major_experts and H % 32 == 0 and I % 32 == 0 and Is % 32 == 0:
-        gu_n, dn_n = moe.moe_packed_experts_size(params)
-        dev["w_gate_up_packed"] = torch.empty(gu_n, dtype=torch.int16, device="cuda")
-        dev["w_down_packed"] = torch.empty(dn_n, dtype=torch.int16, device="cuda")
-        moe.moe_pack_experts(params, dev["w_gate_up"], dev["w_down"], dev["w_gate_up_packed"],
-                             dev["w_down_packed"])
+    if not args.row_major_experts and H % 32 == 0 and I % 32 == 0 and Is % 32 == 0 and (
+            Is or not wl.w4):
+        if not wl.w4:  # W4A16 routed experts: the shared expert's copies only
+            gu_n, dn_n = moe.moe_packed_experts_size(params)
+            dev["w_gate_up_packed"] = torch.empty(gu_n, dtype=torch.int16, device="cuda")
+            dev["w_down_packed"] = torch.empty(dn_n, dtype=torch.int16, device="cuda")
+            moe.moe_pack_experts(params, dev["w_gate_up"], dev["w_down"],
+                                 dev["w_gate_up_packed"], dev["w_down_packed"])
         if Is:
             ps = moe.make_params(T, H, 1, 1, Is, 0, wl.rsf, wl.limit, False, wl.eps)
             sgu_n, sdn_n = moe.moe_packed_experts_size(ps)
@@ -550,7 +552,7 @@ def main() -> int:
             moe.moe_pack_experts(ps, dev["ws_gate_up"], dev["ws_down"],
                                  dev["ws_gate_up_packed"], dev["ws_down_packed"])
         torch.cuda.synchronize()
-        layout = "row_major+tile_blocked"
+        layout = "row_major+tile_blocked" if not wl.w4 else "w4a16_codes+shared_tile_blocked"
     weights = moe.make_weights(**dev, **w4)
     ws = torch.empty(moe.moe_workspace_size(params), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")

@@ -151,9 +151,12 @@ typedef struct moe_weights {
   const float* w_gate_up_tscale;    /* [E] fp32 tensor scales; NULL = ones        */
   const float* w_down_tscale;       /* [E] fp32 tensor scales; NULL = ones        */
   /* Optional tile-blocked copies of the bf16 experts, written once by
-   * moe_pack_experts (NULL = not given; not with W4A16): the routed pair
-   * both or neither, and with them the shared expert's pair when
-   * I_shared > 0 (moe_pack_experts with E = 1 and I = I_shared).
+   * moe_pack_experts (NULL = not given), each pair both or neither: the
+   * routed pair (bf16 routed experts only, not with W4A16) and the shared
+   * expert's (moe_pack_experts with E = 1 and I = I_shared).  With bf16
+   * routed experts and I_shared > 0 the two pairs come together (the tiles
+   * run both in one launch); with W4A16 routed experts the shared pair
+   * alone may be given.
    * Prefill-sized batches (the 256-row tiles) then read each 32-column K
    * stage of a 256-row weight tile as one contiguous 16 KB block instead of
    * 256 pieces of 64 bytes, half as many requests to the caches; the

@@ -519,15 +519,18 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
     REQUIRE_PTR(w->w_down);
   }
   const bool packed = w->w_gate_up_packed != nullptr;
+  const bool packed_s = w->ws_gate_up_packed != nullptr;
   if ((w->w_down_packed != nullptr) != packed)
     return fail(MOE_ERR_INVALID_ARG, "w_gate_up_packed and w_down_packed go together");
-  if (packed && w4) return fail(MOE_ERR_INVALID_ARG, "packed experts are bf16 (params.w4 = 0)");
-  if (packed && (p->H % 32 || p->I % 32 || p->I_shared % 32))
+  if ((w->ws_down_packed != nullptr) != packed_s)
+    return fail(MOE_ERR_INVALID_ARG, "ws_gate_up_packed and ws_down_packed go together");
+  if (packed && w4)
+    return fail(MOE_ERR_INVALID_ARG, "packed routed experts are bf16 (params.w4 = 0)");
+  if ((packed || packed_s) && (p->H % 32 || p->I_shared % 32 || (packed && p->I % 32)))
     return fail(MOE_ERR_UNSUPPORTED, "packed experts need H, I and I_shared multiples of 32");
-  if (packed && p->I_shared > 0) {  // the 256-row tiles run both in one launch
-    REQUIRE_PTR(w->ws_gate_up_packed);
-    REQUIRE_PTR(w->ws_down_packed);
-  }
+  if (!w4 && p->I_shared > 0 && packed != packed_s)  // the 256-row tiles run both in one launch
+    return fail(MOE_ERR_INVALID_ARG,
+                "bf16 routed and shared experts: both packed pairs or neither");
   OPTIONAL_PTR(w->w_gate_up_packed);
   OPTIONAL_PTR(w->w_down_packed);
   OPTIONAL_PTR(w->ws_gate_up_packed);
@@ -610,18 +613,25 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
                                  p->I_shared, v, false);
   // tile-blocked copies of the bf16 experts, for the 256-row tiles (their
   // K stages then are contiguous 16 KB blocks, byte offsets within 4 GiB
-  // per expert); other tiles read the rows
-  if (packed && (v == GemmVariant::kPingPong || v == GemmVariant::kPipe256W8) &&
-      2 * pack_experts_elems(1, p->I, p->H, true) <= UINT32_MAX &&
-      2 * pack_experts_elems(1, p->H, p->I, false) <= UINT32_MAX &&
-      2 * pack_experts_elems(1, p->I_shared, p->H, true) <= UINT32_MAX &&
-      2 * pack_experts_elems(1, p->H, p->I_shared, false) <= UINT32_MAX) {
+  // per expert); other tiles read the rows.  The problems of one launch
+  // share their layout: bf16 routed and shared experts take theirs
+  // together, a shared expert after the W4A16 code tiles alone
+  const bool pipe_tiles = v == GemmVariant::kPingPong || v == GemmVariant::kPipe256W8;
+  const bool routed_fits = 2 * pack_experts_elems(1, p->I, p->H, true) <= UINT32_MAX &&
+                           2 * pack_experts_elems(1, p->H, p->I, false) <= UINT32_MAX;
+  const bool shared_fits = 2 * pack_experts_elems(1, p->I_shared, p->H, true) <= UINT32_MAX &&
+                           2 * pack_experts_elems(1, p->H, p->I_shared, false) <= UINT32_MAX;
+  const bool shared_alone = shared && w4_codes && v == GemmVariant::kPingPong;
+  const bool use_packed = pipe_tiles && packed && routed_fits && shared_fits;
+  if (use_packed) {
     gu.W = w->w_gate_up_packed;
     gu.w_stride = pack_experts_elems(1, p->I, p->H, true);
     gu.packed = 1;
     dn.W = w->w_down_packed;
     dn.w_stride = pack_experts_elems(1, p->H, p->I, false);
     dn.packed = 1;
+  }
+  if (pipe_tiles && packed_s && shared_fits && (use_packed || shared_alone)) {
     sgu.W = w->ws_gate_up_packed;
     sgu.packed = 1;
     sdn.W = w->ws_down_packed;
@@ -629,10 +639,12 @@ moe_status forward_impl(const moe_params* p, const moe_bf16* x_routed, const moe
   }
   // the 256-row tiles pass h (and the shared expert's) from gate_up to down
   // stage-blocked within each tile, so that down reads a K stage of a tile as
-  // one contiguous block; a caller who reads h or h_shared gets them in rows
-  if ((v == GemmVariant::kPingPong || v == GemmVariant::kPipe256W8) && !w4 &&
-      !(probes && (probes->h || probes->h_shared)))
-    gu.hblk = dn.hblk = sgu.hblk = sdn.hblk = 1;
+  // one contiguous block (the W4A16 code tiles keep h in rows); a caller who
+  // reads h or h_shared gets them in rows
+  if (pipe_tiles && !(probes && (probes->h || probes->h_shared))) {
+    if (!w4_codes) gu.hblk = dn.hblk = 1;
+    sgu.hblk = sdn.hblk = 1;
+  }
   if (p->scmoe) gu.A = L.xr;
   if (!tiles_fit(gu, shared ? &sgu : nullptr) || !tiles_fit(dn, shared ? &sdn : nullptr))
     return fail(MOE_ERR_UNSUPPORTED, "too many tiles for one launch");

@@ -129,15 +129,18 @@ class Device:
                                       h_shared=self.hs)
 
     def pack(self) -> None:
-        """Write the tile-blocked copies of the bf16 experts (routed, and the
-        shared expert with E = 1, I = I_shared) and hand them to the layer."""
+        """Write the tile-blocked copies of the bf16 experts (the routed ones
+        unless they are W4A16, and the shared expert with E = 1, I = I_shared)
+        and hand them to the layer."""
         torch, moe, wl = self.torch, self.moe, self.wl
-        gu_n, dn_n = moe.moe_packed_experts_size(self.params)
-        self.gu_packed = torch.full((gu_n,), 0x7FC0, dtype=torch.int16, device="cuda")
-        self.dn_packed = torch.full((dn_n,), 0x7FC0, dtype=torch.int16, device="cuda")
-        moe.moe_pack_experts(self.params, self.w_gate_up, self.w_down, self.gu_packed,
-                             self.dn_packed)
-        extra = dict(w_gate_up_packed=self.gu_packed, w_down_packed=self.dn_packed)
+        extra = {}
+        if not self.w4:  # W4A16 routed experts: the shared expert's copies only
+            gu_n, dn_n = moe.moe_packed_experts_size(self.params)
+            self.gu_packed = torch.full((gu_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+            self.dn_packed = torch.full((dn_n,), 0x7FC0, dtype=torch.int16, device="cuda")
+            moe.moe_pack_experts(self.params, self.w_gate_up, self.w_down, self.gu_packed,
+                                 self.dn_packed)
+            extra = dict(w_gate_up_packed=self.gu_packed, w_down_packed=self.dn_packed)
         if wl.I_s:
             ps = moe.make_params(self.T, wl.H, 1, 1, wl.I_s, 0, wl.rsf, wl.limit, False, wl.eps)
             sgu_n, sdn_n = moe.moe_packed_experts_size(ps)
@@ -148,7 +151,7 @@ class Device:
             extra.update(ws_gate_up_packed=self.sgu_packed, ws_down_packed=self.sdn_packed)
         self.weights = moe.make_weights(self.w_router, self.corr_bias, self.w_gate_up,
                                         self.w_down, self.ws_gate_up, self.ws_down,
-                                        self.gamma_pre, self.gamma_post, **extra)
+                                        self.gamma_pre, self.gamma_post, **self.w4, **extra)
 
     def canary(self) -> None:
         """Fill every output with NaN / out-of-range bits first, so that an

@@ -202,11 +202,14 @@ def test_packed_experts_validation():
     w4 = dict(w_gate_up_q=16, w_gate_up_scale=16, w_down_q=16, w_down_scale=16)
     cases = [
         (P(), dict(full, w_down_packed=None), moe.MOE_ERR_INVALID_ARG),    # routed pair split
-        (P(), dict(full, ws_down_packed=None), moe.MOE_ERR_INVALID_ARG),   # shared pair missing
+        (P(), dict(full, ws_down_packed=None), moe.MOE_ERR_INVALID_ARG),   # shared pair split
         (P(), dict(full, ws_gate_up_packed=24), moe.MOE_ERR_UNSUPPORTED),  # misaligned
         (P(I_shared=0), dict(w_gate_up_packed=16, w_down_packed=16), moe.MOE_ERR_WORKSPACE),
         (P(I_shared=136), full, moe.MOE_ERR_UNSUPPORTED),                  # not 32-multiple
         (P(w4=True), dict(full, **w4), moe.MOE_ERR_INVALID_ARG),           # W4A16 + packed
+        (P(), dict(ws_gate_up_packed=16, ws_down_packed=16), moe.MOE_ERR_INVALID_ARG),
+        (P(w4=True), dict(ws_gate_up_packed=16, ws_down_packed=16, **w4),  # shared alone
+         moe.MOE_ERR_WORKSPACE),
         (P(), full, moe.MOE_ERR_WORKSPACE),                                # valid
     ]
     for p, extra, status in cases:

@@ -402,8 +402,10 @@ def test_forward_prefill_w4_full(scales):
         rows = np.sort(np.random.default_rng(7).choice(wl.T, size=256, replace=False))
     rep, gpu, dev = run_and_check(wl, inp, rows)
     assert rep["experts_touched"] == 64
-    # without h probes (as the bench runs it): the same output bits
+    # without h probes and with the shared expert's tile-blocked copies (as
+    # the bench runs it): the same output bits
     unprobe_h(dev)
+    dev.pack()
     dev.canary()
     dev.run()
     np.testing.assert_array_equal(dev.result()["out"], gpu["out"])
@@ -537,8 +539,14 @@ def test_forward_w4_tiled(name):
     assert np.array_equal(gpu["ids"], g2["ids"])
     assert np.array_equal(gpu["out"], g2["out"]), \
         f"differs from the bf16 path in {int(np.sum(gpu['out'] != g2['out']))} elements"
-    # without h probes (as the bench runs it): the same output bits
+    # without h probes (as the bench runs it), then also with the shared
+    # expert's tile-blocked copies: the same output bits
     unprobe_h(dw)
     dw.canary()
     dw.run()
     np.testing.assert_array_equal(dw.result()["out"], gpu["out"])
+    if wl.I_s:
+        dw.pack()
+        dw.canary()
+        dw.run()
+        np.testing.assert_array_equal(dw.result()["out"], gpu["out"])
