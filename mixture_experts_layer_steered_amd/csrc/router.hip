@@ -30,10 +30,10 @@ namespace {
 
 constexpr int RT_BT = 64;       // tokens per workgroup tile
 constexpr int RT_BE = 64;       // experts per workgroup tile
-constexpr int RT_BK = 32;       // K per LDS stage
-constexpr int RT_LD = RT_BK + 8;  // padded LDS row (bf16 elements): 80 bytes
+constexpr int RT_BK = 64;       // K per LDS stage
+constexpr int RT_LD = RT_BK + 8;  // padded LDS row (bf16 elements): 144 bytes
 constexpr int RT_MAX_SPLITS = 16; // K slices of the router GEMM at most
-constexpr int RT_DEPTH = 4;       // K steps in flight per workgroup
+constexpr int RT_DEPTH = 2;       // K steps in flight per workgroup
 
 __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   uint32_t u = __float_as_uint(w);
@@ -66,15 +66,22 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  // x tile: 64 rows x 32 k = 256 chunks of 8 bf16, one per thread
-  const int xr = tid >> 2, xc = (tid & 3) * 8;
-  // w tile: 64 rows x 32 k = 512 float4, two per thread
-  int wr_[2], wc_[2];
+  // x tile: 64 rows x 64 k = 512 chunks of 8 bf16, two per thread
+  constexpr int XQ = RT_BT * RT_BK / 8 / 256, WQ = RT_BE * RT_BK / 4 / 256;
+  int xr_[XQ], xc_[XQ];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < XQ; ++q) {
     const int idx = tid + q * 256;
-    wr_[q] = idx >> 3;
-    wc_[q] = (idx & 7) * 4;
+    xr_[q] = idx / (RT_BK / 8);
+    xc_[q] = (idx % (RT_BK / 8)) * 8;
+  }
+  // w tile: 64 rows x 64 k = 1024 float4, four per thread
+  int wr_[WQ], wc_[WQ];
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int idx = tid + q * 256;
+    wr_[q] = idx / (RT_BK / 4);
+    wc_[q] = (idx % (RT_BK / 4)) * 4;
   }
   const int k_begin = blockIdx.z * k_slice;
   const int k_end = min(H, k_begin + k_slice);
@@ -84,16 +91,19 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   // K steps go through a ring of RT_DEPTH register buffers: the loads of
   // step it + RT_DEPTH are issued as soon as step it is in LDS, so a slice
   // pays about one memory round trip instead of one per step
-  uint4 xv[RT_DEPTH];
-  float4 wv[RT_DEPTH][2];
+  uint4 xv[RT_DEPTH][XQ];
+  float4 wv[RT_DEPTH][WQ];
   auto load = [&](int it, auto d_c) __attribute__((always_inline)) {
     constexpr int d = decltype(d_c)::value;
     const int k0 = k_begin + it * RT_BK;
-    xv[d] = make_uint4(0, 0, 0, 0);
-    if (t0 + xr < T && k0 + xc < k_end)
-      xv[d] = *reinterpret_cast<const uint4*>(x + (t0 + xr) * (int64_t)H + k0 + xc);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < XQ; ++q) {
+      xv[d][q] = make_uint4(0, 0, 0, 0);
+      if (t0 + xr_[q] < T && k0 + xc_[q] < k_end)
+        xv[d][q] = *reinterpret_cast<const uint4*>(x + (t0 + xr_[q]) * (int64_t)H + k0 + xc_[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
       wv[d][q] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e0 + wr_[q] < E && k0 + wc_[q] < k_end)
         wv[d][q] = *reinterpret_cast<const float4*>(w + (int64_t)(e0 + wr_[q]) * H + k0 + wc_[q]);
@@ -102,9 +112,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   auto step = [&](int it, auto d_c) __attribute__((always_inline)) {
     constexpr int d = decltype(d_c)::value;
     __syncthreads();
-    *reinterpret_cast<uint4*>(&xs[xr * RT_LD + xc]) = xv[d];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < XQ; ++q) *reinterpret_cast<uint4*>(&xs[xr_[q] * RT_LD + xc_[q]]) = xv[d][q];
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
       uint32_t h[4], m[4], l[4];
       split3(wv[d][q].x, h[0], m[0], l[0]);
       split3(wv[d][q].y, h[1], m[1], l[1]);
@@ -132,18 +143,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   };
   using D0 = std::integral_constant<int, 0>;
   using D1 = std::integral_constant<int, 1>;
-  using D2 = std::integral_constant<int, 2>;
-  using D3 = std::integral_constant<int, 3>;
-  static_assert(RT_DEPTH == 4, "the ring below is unrolled for four buffers");
+  static_assert(RT_DEPTH == 2, "the ring below is unrolled for two buffers");
   if (0 < nit) load(0, D0{});
   if (1 < nit) load(1, D1{});
-  if (2 < nit) load(2, D2{});
-  if (3 < nit) load(3, D3{});
   for (int it0 = 0; it0 < nit; it0 += RT_DEPTH) {
     step(it0, D0{});
     if (it0 + 1 < nit) step(it0 + 1, D1{});
-    if (it0 + 2 < nit) step(it0 + 2, D2{});
-    if (it0 + 3 < nit) step(it0 + 3, D3{});
   }
   // 32x32 accumulator: lane holds column (lane & 31), rows 8*(r/4) + 4*(lane/32) + r%4
   const int col = e0 + wn * 32 + (lane & 31);
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(PM_THREADS) void route_small_kernel(
 
 int router_splits(int64_t T, int H, int E) {
   // enough workgroups to cover the chip (about two per CU), each slice a
-  // multiple of the 32-wide K step and at least 64 wide
+  // multiple of the 64-wide K step
   const int64_t tiles = ((T + RT_BT - 1) / RT_BT) * ((E + RT_BE - 1) / RT_BE);
   if (tiles == 0) return 1;
   int64_t s = (512 + tiles - 1) / tiles;
