@@ -159,7 +159,7 @@ typedef struct moe_weights {
    * alone may be given.
    * Prefill-sized batches (the 256-row tiles) then read each 32-column K
    * stage of a 256-row weight tile as one contiguous 16 KB block instead of
-   * 256 pieces of 64 bytes, half as many requests to the caches; the
+   * 256 pieces of 64 bytes, in fewer and larger requests to the caches; the
    * results are the same bits.  The row-major weights stay required (the
    * other batch sizes read them). */
   const moe_bf16* w_gate_up_packed;
@@ -423,10 +423,11 @@ moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float
                              int32_t n_groups, int64_t rows, int32_t K, moe_bf16* out,
                              hipStream_t stream);
 
-/* Tile-blocked copies of bf16 routed experts for moe_weights' *_packed
- * fields: a one-time preparation of the weights, like loading them, not a
- * step of the layer (the layout is this library's: the loads of its
- * 256-row tiles, not a format of the pages).
+/* Tile-blocked copies of bf16 experts for moe_weights' *_packed fields: a
+ * one-time preparation of the weights, like loading them, not a step of the
+ * layer (the layout is this library's: the loads of its 256-row tiles, not
+ * a format of the pages).  p is checked as in every call; only its E, H
+ * and I shape the copies.
  * gate_up_packed: for expert e, column tile b (output columns [128 b,
  *   128 b + 128), b < ceil(I/128)) and K stage s (columns [32 s, 32 s + 32)
  *   of H, s < H/32), one block of 256 rows x 32 values, each row's 32
@@ -441,7 +442,8 @@ moe_status moe_w4_dequantize(const uint8_t* q, const uint8_t* scale, const float
  * * H and E * ceil(H/256) * 256 * I bf16).  The shared expert's copies are
  * the same with E = 1 and I = I_shared (ws_gate_up, ws_down as w_gate_up,
  * w_down).  H and I must be multiples of 32 (else MOE_ERR_UNSUPPORTED);
- * pointers device, 16-byte aligned; the outputs must not overlap the
+ * pointers device and 16-byte aligned (NULL: MOE_ERR_INVALID_ARG,
+ * misaligned: MOE_ERR_UNSUPPORTED); the outputs must not overlap the
  * inputs.  Asynchronous on stream. */
 moe_status moe_packed_experts_size(const moe_params* p, int64_t* gate_up_elems,
                                    int64_t* down_elems);

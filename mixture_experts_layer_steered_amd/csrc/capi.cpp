@@ -888,6 +888,9 @@ moe_status moe_pack_experts(const moe_params* p, const moe_bf16* w_gate_up, cons
   REQUIRE_PTR(w_down);
   REQUIRE_PTR(gate_up_packed);
   REQUIRE_PTR(down_packed);
+  // one workgroup per 256 x 32 block: the grid's x dimension bounds the count
+  if (gu / (256 * 32) > INT32_MAX || dn / (256 * 32) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "experts too large to pack in one launch");
   if ((s = device_status(launch_pack_experts(w_gate_up, gate_up_packed, p->E, p->I, p->H, true,
                                              stream),
                          "pack gate_up")) != MOE_OK ||
