@@ -153,6 +153,13 @@ class Device:
                                         self.w_down, self.ws_gate_up, self.ws_down,
                                         self.gamma_pre, self.gamma_post, **self.w4, **extra)
 
+    def unprobe_h(self) -> None:
+        """Probe everything but h and h_shared: the forward then hands h from
+        gate_up to down in its own layout (stage-blocked within each 256-row
+        tile on those tiles)."""
+        self.probes = self.moe.make_probes(self.ids, self.w, self.offsets, self.sorted_token,
+                                           self.inv_pos, self.xr, self.logits)
+
     def canary(self) -> None:
         """Fill every output with NaN / out-of-range bits first, so that an
         element the kernels never write shows up."""

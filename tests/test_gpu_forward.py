@@ -285,14 +285,6 @@ def test_forward_packed_experts(monkeypatch, variant, name):
     gh.check_layer(wl, inp, tiled)
 
 
-def unprobe_h(d) -> None:
-    """Probe everything but h and h_shared: the forward then hands h from
-    gate_up to down in its own layout (stage-blocked within each 256-row
-    tile on those tiles)."""
-    d.probes = d.moe.make_probes(d.ids, d.w, d.offsets, d.sorted_token, d.inv_pos, d.xr,
-                                 d.logits)
-
-
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("variant", ["pingpong", "pipe256w8"])
 @pytest.mark.parametrize("name", list(PACKED))
@@ -312,7 +304,7 @@ def test_forward_blocked_h(monkeypatch, variant, name, packed):
     d.run()
     rows = d.result()
     gh.check_layer(wl, inp, rows)
-    unprobe_h(d)
+    d.unprobe_h()
     d.canary()
     d.run()
     blk = d.result()
@@ -338,7 +330,7 @@ def test_forward_prefill_packed_full():
     np.testing.assert_array_equal(tiled["h"], rows["h"])
     sample = np.sort(np.random.default_rng(7).choice(wl.T, size=64, replace=False))
     gh.note(f"  {gh.check_layer(wl, inp, tiled, sample)}")
-    unprobe_h(d)
+    d.unprobe_h()
     d.canary()
     d.run()
     np.testing.assert_array_equal(d.result()["out"], rows["out"])
@@ -404,7 +396,7 @@ def test_forward_prefill_w4_full(scales):
     assert rep["experts_touched"] == 64
     # without h probes and with the shared expert's tile-blocked copies (as
     # the bench runs it): the same output bits
-    unprobe_h(dev)
+    dev.unprobe_h()
     dev.pack()
     dev.canary()
     dev.run()
@@ -541,7 +533,7 @@ def test_forward_w4_tiled(name):
         f"differs from the bf16 path in {int(np.sum(gpu['out'] != g2['out']))} elements"
     # without h probes (as the bench runs it), then also with the shared
     # expert's tile-blocked copies: the same output bits
-    unprobe_h(dw)
+    dw.unprobe_h()
     dw.canary()
     dw.run()
     np.testing.assert_array_equal(dw.result()["out"], gpu["out"])
