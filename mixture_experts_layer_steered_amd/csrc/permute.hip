@@ -38,12 +38,16 @@ __global__ __launch_bounds__(PM_THREADS) void permute_hist_kernel(
 }
 
 // Single workgroup.  counts[tiles][E] -> starts[tiles][E] (exclusive start of
-// each (expert, tile) run in expert-major order) and offsets[E+1].
+// each (expert, tile) run in expert-major order) and offsets[E+1]; with
+// mstart, also the grouped GEMM's m-tile prefix for tiles of bm rows
+// (mstart[e] = sum over e' < e of ceil(n_e' / bm), mstart[E] the total).
 __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(
     const int32_t* __restrict__ counts, int32_t* __restrict__ starts,
-    int32_t* __restrict__ offsets, int tiles, int E, int64_t N) {
+    int32_t* __restrict__ offsets, int tiles, int E, int64_t N, int bm,
+    int32_t* __restrict__ mstart) {
   __shared__ int32_t tot[MOE_MAX_EXPERTS_DEV];
   __shared__ int32_t wsum[PM_WAVES];
+  __shared__ int32_t msum[PM_WAVES];
   const int e = threadIdx.x;
   int32_t run = 0;
   if (e < E) {
@@ -72,6 +76,21 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(
     tot[e] = excl;
   }
   if (e == 0) offsets[E] = (int32_t)N;
+  if (mstart != nullptr) {  // the same block scan over the experts' m-tile counts
+    const int32_t mv = (v + bm - 1) / bm;
+    int32_t mincl = mv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int32_t o = __shfl_up(mincl, off, 64);
+      if (lane >= off) mincl += o;
+    }
+    if (lane == 63) msum[wave] = mincl;
+    __syncthreads();
+    int32_t mbefore = 0;
+    for (int w = 0; w < wave; ++w) mbefore += msum[w];
+    if (e < E) mstart[e] = mbefore + mincl - mv;
+    if (e == E - 1) mstart[E] = mbefore + mincl;
+  }
   __syncthreads();
   if (e < E) {
     for (int t = 0; t < tiles; ++t) starts[(int64_t)t * E + e] += tot[e];
@@ -186,15 +205,14 @@ hipError_t launch_permute(const int32_t* ids, int32_t* counts, int32_t* starts, 
   if (tiles == 0) {
     // no pairs: offsets are all zero
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, stream, counts, starts,
-                       offsets, 0, E, (int64_t)0);
+                       offsets, 0, E, (int64_t)0, bm > 0 ? bm : 1, mstart);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(permute_hist_kernel, dim3(tiles), dim3(PM_THREADS), 0, stream, ids, counts,
                      N, E);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, stream, counts, starts,
-                     offsets, tiles, E, N);
+                     offsets, tiles, E, N, bm > 0 ? bm : 1, mstart);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(tiles), dim3(PM_THREADS), 0, stream, ids,
                      starts, sorted_token, inv_pos, N, E, k);
-  if (mstart) return launch_gemm_schedule(offsets, E, bm, bm, mstart, nullptr, stream);
   return hipGetLastError();
 }
