@@ -312,6 +312,39 @@ def test_forward_blocked_h(monkeypatch, variant, name, packed):
         np.testing.assert_array_equal(blk[key], rows[key], err_msg=key)
 
 
+def test_forward_graph_replay_blocked_layouts(monkeypatch):
+    """A forward on the 256-row tiles with the tile-blocked copies and h
+    stage-blocked, captured into a HIP graph, replays to the eager result bit
+    for bit, several times with eager work in between."""
+    monkeypatch.setenv("MOE_GEMM_VARIANT", "pingpong")
+    torch, moe = gh.torch_and_lib()
+    wl = PACKED["pp_ragged"]
+    gh.note(f"graph replay, blocked layouts {wl.label()}")
+    d = gh.Device(wl, moe_inputs.generate(wl, seed=9))
+    d.pack()
+    d.unprobe_h()
+    d.run()
+    eager = gh.to_bits(d.out).copy()
+    out_g = torch.empty_like(d.out)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_forward(d.params, d.x, d.x_cur, d.weights, out_g, None, d.ws)  # warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        moe.moe_forward(d.params, d.x, d.x_cur, d.weights, out_g, None, d.ws)
+    for rep in range(3):
+        out_g.fill_(0x7FC0)
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gh.to_bits(out_g), eager, err_msg=f"replay {rep}")
+        d.run()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gh.to_bits(d.out), eager)
+
+
 def test_forward_prefill_packed_full():
     """The measured prefill workload with the tile-blocked expert copies and
     with h stage-blocked (the bench's configuration): every output bit equal
