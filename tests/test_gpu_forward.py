@@ -1,8 +1,9 @@
 """Whole-layer parity on the GPU (moe_forward through the C ABI) against
 the oracle: small and medium shapes compared on every element, the
-measured workloads at full size on every token's routing and permutation
-and on a sample of tokens' outputs (the layer is row-independent, so the
-oracle computes those rows alone), plus the layer's degenerate cases."""
+measured workloads at full size on every token's routing, permutation and
+output (a few variant runs check a sample of tokens' outputs: the layer is
+row-independent, so the oracle computes those rows alone), plus the layer's
+degenerate cases."""
 import numpy as np
 import pytest
 
